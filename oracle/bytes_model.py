@@ -1,0 +1,35 @@
+"""KV-cache byte counts (the unit of the HBM roofline).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The IndexMem page (technical summary, section 1, problem statement) estimates
+about 320 GB of KV cache for a 70B-parameter model at a one-million-token
+context.  K and V each hold head_dim values per KV head per layer per token,
+which with an 80-layer, 8-KV-head, head_dim-128 model in 2-byte storage gives
+exactly 320 GiB at 2^20 tokens; that architecture is an assumption consistent
+with the figure (the page does not give it).
+"""
+from __future__ import annotations
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """Bytes of K plus V for one token across all layers and KV heads."""
+    return 2 * layers * kv_heads * head_dim * elem_bytes
+
+
+def attention_layer_bytes(units: int, n: int, head_dim: int, elem_bytes: int,
+                          retention: bool, batch: int, hq: int, moved: int = 0,
+                          evict: bool = False) -> int:
+    """Algorithmic bytes of one layer's decode step (each byte touched once).
+
+    units = B * Hkv heads each read n K rows and n V rows; the retention array
+    (4 B) and positions (4 B) are read once per slot when the bias or eviction
+    needs them; each moved row (K, V, log beta, pos) is read and written once;
+    q is read and (out, lse) written once.
+    """
+    A = units * n * 2 * head_dim * elem_bytes
+    if retention or evict:
+        A += units * n * 8
+    A += moved * 2 * (2 * head_dim * elem_bytes + 8)
+    A += batch * hq * head_dim * elem_bytes + batch * hq * (head_dim + 1) * 4
+    return A

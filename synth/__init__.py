@@ -1,0 +1,297 @@
+"""Seeded synthetic inputs for bounded decode attention.
+
+This module is shared by the float64 oracle's tests and by the HIP path's tests
+and benchmark.  It only *draws* inputs: it holds none of the method's arithmetic
+(no attention, no retention keys, no eviction, no merge, no lookup).
+
+Distributions follow the five workloads:
+
+* K, V, q ~ N(0, 1); bf16 values are rounded to nearest-even from float64.
+* retention: beta = sigmoid(x), x ~ N(2, 1.5) (1.5 is the standard deviation),
+  stored as log beta in float32, because the kernels take log beta.
+* token positions: 0..n-1 for a fresh cache; the decode token sits at t = n.
+* ASM codebooks: centroids ~ N(0,1)^D normalised to unit L2 length in float64,
+  then rounded to bf16; stored states abar ~ N(0,1)^D in bf16; log Zbar ~ U(0, 12).
+* MEMENTO layout: thinking blocks of uniform integer length in [2048, 16384], each
+  followed by a 200-token memento, filling the cache; the last block is the one
+  still being written and has no memento.
+
+Host generation uses numpy's PCG64.  Large workloads are drawn on the device
+with torch's seeded generator (``device_*`` helpers); their parity checks read
+the drawn bits back before any kernel runs.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "bf16_bits", "bf16_to_f64", "f32_bits",
+    "host_cache", "host_queries", "host_new_tokens", "host_codebook",
+    "memento_layout", "device_cache", "device_queries", "device_codebook",
+]
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: str            # "f32" or "bf16"
+    ctx: int              # tokens in the cache before the decode token
+    budget: int           # M, live slots per KV head after eviction
+    layers: int
+    seed: int
+    steps: int = 1        # decode steps (the tiny workload runs 16)
+    retention: bool = True   # False: beta == 1 (no log beta array)
+    codebook: int = 0     # ASM centroids per KV head (0: no ASM)
+
+    @property
+    def group(self) -> int:
+        return self.hq // self.hkv
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.hkv
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", batch=1, hq=8, hkv=2, head_dim=64, dtype="f32",
+                     ctx=512, budget=256, layers=1, seed=1001, steps=16),
+    "qwen3_8b_32k": Workload("qwen3_8b_32k", batch=16, hq=32, hkv=8, head_dim=128,
+                             dtype="bf16", ctx=32768, budget=4096, layers=36,
+                             seed=1002),
+    "qwen3_32b_128k": Workload("qwen3_32b_128k", batch=8, hq=64, hkv=8, head_dim=128,
+                               dtype="bf16", ctx=131072, budget=8192, layers=64,
+                               seed=1003),
+    "asm_lookup": Workload("asm_lookup", batch=32, hq=32, hkv=8, head_dim=128,
+                           dtype="bf16", ctx=2048, budget=1 << 30, layers=36,
+                           seed=1004, retention=False, codebook=4096),
+    "memento_1m": Workload("memento_1m", batch=1, hq=64, hkv=8, head_dim=128,
+                           dtype="bf16", ctx=1 << 20, budget=65536, layers=1,
+                           seed=1005, retention=False),
+}
+
+
+# --------------------------------------------------------------------------
+# dtype helpers (bit-exact, shared by both sides)
+# --------------------------------------------------------------------------
+def bf16_bits(x) -> np.ndarray:
+    """Round float64 values to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Works on the float64 value directly (no float32 detour, so no double rounding).
+    Only finite values within bf16's normal range are expected.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2**e, 0.5 <= |m| < 1
+    r = np.rint(m * 256.0)                   # 8 significant bits, half-to-even
+    v = np.ldexp(r, e - 8)                   # exact in float64 and in float32
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_bits(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32)
+
+
+def _log_sigmoid_f32(x: np.ndarray) -> np.ndarray:
+    # log(1/(1+e^-x)) evaluated stably in float64, stored as float32
+    x = np.asarray(x, dtype=np.float64)
+    out = np.where(x >= 0, -np.log1p(np.exp(-np.abs(x))), x - np.log1p(np.exp(-np.abs(x))))
+    return out.astype(np.float32)
+
+
+def _draw_values(rng, shape, dtype):
+    z = rng.standard_normal(size=shape)
+    if dtype == "bf16":
+        return bf16_bits(z)
+    return z.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# host generators (numpy PCG64)
+# --------------------------------------------------------------------------
+def host_cache(w: Workload, n: int | None = None, cap: int | None = None,
+               seed: int | None = None, units: tuple[int, int] | None = None):
+    """A fresh cache with n live tokens per KV head at positions 0..n-1.
+
+    Returns a dict of numpy arrays (uint16 bf16 bits or float32 values):
+    k, v [B][Hkv][cap][D]; log_beta [B][Hkv][cap] float32 (or None);
+    pos [B][Hkv][cap] int32; len [B][Hkv] int32.
+    Slots at and beyond n hold zeros.
+    """
+    n = w.ctx if n is None else n
+    cap = n + w.steps if cap is None else cap
+    B, H = (w.batch, w.hkv) if units is None else units
+    D = w.head_dim
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    vd = np.uint16 if w.dtype == "bf16" else np.float32
+    k = np.zeros((B, H, cap, D), vd)
+    v = np.zeros((B, H, cap, D), vd)
+    k[:, :, :n] = _draw_values(rng, (B, H, n, D), w.dtype)
+    v[:, :, :n] = _draw_values(rng, (B, H, n, D), w.dtype)
+    log_beta = None
+    if w.retention:
+        log_beta = np.zeros((B, H, cap), np.float32)
+        log_beta[:, :, :n] = _log_sigmoid_f32(rng.normal(2.0, 1.5, size=(B, H, n)))
+    pos = np.zeros((B, H, cap), np.int32)
+    pos[:, :, :n] = np.arange(n, dtype=np.int32)
+    length = np.full((B, H), n, np.int32)
+    return {"k": k, "v": v, "log_beta": log_beta, "pos": pos, "len": length}
+
+
+def host_queries(w: Workload, steps: int | None = None, seed_offset: int = 7,
+                 batch: int | None = None):
+    """q [steps][B][Hq][D] (bf16 bits or float32)."""
+    steps = w.steps if steps is None else steps
+    B = w.batch if batch is None else batch
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    return _draw_values(rng, (steps, B, w.hq, w.head_dim), w.dtype)
+
+
+def host_new_tokens(w: Workload, steps: int | None = None, seed_offset: int = 13,
+                    batch: int | None = None):
+    """Per decode step: k_new, v_new [steps][B][Hkv][D], log_beta_new [steps][B][Hkv]."""
+    steps = w.steps if steps is None else steps
+    B = w.batch if batch is None else batch
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    k = _draw_values(rng, (steps, B, w.hkv, w.head_dim), w.dtype)
+    v = _draw_values(rng, (steps, B, w.hkv, w.head_dim), w.dtype)
+    lb = None
+    if w.retention:
+        lb = _log_sigmoid_f32(rng.normal(2.0, 1.5, size=(steps, B, w.hkv)))
+    return k, v, lb
+
+
+def host_codebook(w: Workload, K: int | None = None, seed_offset: int = 29):
+    """ASM codebook per KV head: centroids, abar [Hkv][K][D] bf16 bits; log_zbar [Hkv][K] f32."""
+    K = w.codebook if K is None else K
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    c = rng.standard_normal(size=(w.hkv, K, w.head_dim))
+    c = c / np.sqrt((c * c).sum(axis=-1, keepdims=True))
+    centroids = bf16_bits(c)
+    abar = bf16_bits(rng.standard_normal(size=(w.hkv, K, w.head_dim)))
+    log_zbar = rng.uniform(0.0, 12.0, size=(w.hkv, K)).astype(np.float32)
+    return centroids, abar, log_zbar
+
+
+def memento_layout(total: int = 1 << 20, seed: int = 1005, memento: int = 200,
+                   lo: int = 2048, hi: int = 16384):
+    """Block/memento layout of a reasoning trace filling ``total`` slots.
+
+    Returns (blocks, ranges): blocks is a list of (start, block_len, memento_len);
+    ranges is an int32 array [R][2] of half-open position ranges covering every
+    completed thinking block (those followed by a memento).  The last block is
+    the current one; it has no memento and is not erased.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    blocks = []
+    p = 0
+    while p < total:
+        L = int(rng.integers(lo, hi + 1))
+        if p + L + memento >= total:          # current block: runs to the end
+            blocks.append((p, total - p, 0))
+            break
+        blocks.append((p, L, memento))
+        p += L + memento
+    ranges = np.array([(s, s + L) for (s, L, mlen) in blocks if mlen > 0], np.int32)
+    return blocks, ranges.reshape(-1, 2)
+
+
+# --------------------------------------------------------------------------
+# device generators (torch, seeded); used for workloads too large for the host
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def device_cache(w: Workload, layer: int, n: int | None = None, cap: int | None = None,
+                 device: str = "cuda", out: dict | None = None):
+    """Draw one layer's cache on the device.  Deterministic in (seed, layer).
+
+    Returns a dict of torch tensors: k, v [B][Hkv][cap][D] (bfloat16 or float32),
+    log_beta [B][Hkv][cap] float32 or None, pos int32, len int32.
+    If ``out`` is given its tensors are filled in place.
+    """
+    torch = _torch()
+    n = w.ctx if n is None else n
+    cap = n + w.steps if cap is None else cap
+    B, H, D = w.batch, w.hkv, w.head_dim
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 1000003 + layer)
+    if out is None:
+        out = {
+            "k": torch.empty((B, H, cap, D), dtype=tdt, device=device),
+            "v": torch.empty((B, H, cap, D), dtype=tdt, device=device),
+            "log_beta": (torch.empty((B, H, cap), dtype=torch.float32, device=device)
+                         if w.retention else None),
+            "pos": torch.empty((B, H, cap), dtype=torch.int32, device=device),
+            "len": torch.empty((B, H), dtype=torch.int32, device=device),
+        }
+    # bf16 values: draw float32 normals and round to nearest-even bf16
+    for name in ("k", "v"):
+        t = out[name]
+        for b in range(B):      # per batch row bounds the float32 staging buffer
+            z = torch.randn((H, n, D), generator=g, device=device, dtype=torch.float32)
+            t[b, :, :n].copy_(z.to(tdt))
+            del z
+        if cap > n:
+            t[:, :, n:].zero_()
+    if w.retention:
+        x = torch.randn((B, H, n), generator=g, device=device, dtype=torch.float32)
+        x = x * 1.5 + 2.0
+        out["log_beta"][:, :, :n] = torch.nn.functional.logsigmoid(x)
+        if cap > n:
+            out["log_beta"][:, :, n:].zero_()
+    out["pos"][:, :, :n] = torch.arange(n, dtype=torch.int32, device=device)
+    if cap > n:
+        out["pos"][:, :, n:].zero_()
+    out["len"].fill_(n)
+    return out
+
+
+def device_queries(w: Workload, layer: int, device: str = "cuda", step: int = 0):
+    torch = _torch()
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 7919 + layer * 131 + step)
+    q = torch.randn((w.batch, w.hq, w.head_dim), generator=g, device=device)
+    k = torch.randn((w.batch, w.hkv, w.head_dim), generator=g, device=device)
+    v = torch.randn((w.batch, w.hkv, w.head_dim), generator=g, device=device)
+    lb = None
+    if w.retention:
+        x = torch.randn((w.batch, w.hkv), generator=g, device=device) * 1.5 + 2.0
+        lb = torch.nn.functional.logsigmoid(x)
+    return q.to(tdt), k.to(tdt), v.to(tdt), lb
+
+
+def device_codebook(w: Workload, layer: int, device: str = "cuda"):
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 104729 + layer)
+    c = torch.randn((w.hkv, w.codebook, w.head_dim), generator=g, device=device,
+                    dtype=torch.float64)
+    c = c / c.square().sum(-1, keepdim=True).sqrt()
+    abar = torch.randn((w.hkv, w.codebook, w.head_dim), generator=g, device=device)
+    lz = torch.rand((w.hkv, w.codebook), generator=g, device=device) * 12.0
+    return c.to(torch.bfloat16), abar.to(torch.bfloat16), lz.float()
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)

@@ -1,0 +1,318 @@
+"""Pin checks that tie the float64 oracle to something other than itself.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with an
+independent statement of what the pages fix: a library routine (torch's scaled
+dot-product attention, scipy's logsumexp), a closed form written without logs
+(beta_i ** (t - i)), an identity (online softmax, lossless merge), or brute
+force over every subset on tiny inputs.  The functions are looked up through
+the oracle's modules at call time, so tests/test_oracle_mutations.py can plant
+mistakes in the oracle and show each one fails a pin.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle.asm as OA
+import oracle.attn as OT
+import oracle.bytes_model as OB
+import oracle.evict as OE
+
+TOL = 1e-11
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _sdpa(q, K, V, scale, mask=None):
+    """torch's scaled dot-product attention in float64 on the CPU (one query)."""
+    qt = torch.tensor(q, dtype=torch.float64).reshape(1, 1, 1, -1)
+    Kt = torch.tensor(K, dtype=torch.float64).reshape(1, 1, K.shape[0], -1)
+    Vt = torch.tensor(V, dtype=torch.float64).reshape(1, 1, V.shape[0], -1)
+    m = None if mask is None else torch.tensor(mask, dtype=torch.float64).reshape(1, 1, 1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=m, scale=scale)
+    return o.reshape(-1).numpy()
+
+
+# ---------------------------------------------------------------- P1
+def check_attention_library(seed=0):
+    """beta == 1 reduces to textbook softmax attention: torch SDPA + scipy logsumexp."""
+    r = _rng(seed)
+    for n, D in ((1, 8), (7, 16), (37, 32), (130, 64)):
+        q = r.standard_normal(D)
+        K = r.standard_normal((n, D)) * 2.0
+        V = r.standard_normal((n, D))
+        scale = 1.0 / math.sqrt(D)
+        pos = np.arange(n) * 3 + 5
+        out, lse = OT.attention(q, K, V, None, pos, int(pos[-1]) + 1, scale)
+        ref = _sdpa(q, K, V, scale)
+        assert np.max(np.abs(out - ref)) < TOL * 10, "attention != SDPA"
+        ref_lse = scipy.special.logsumexp(scale * (K @ q))
+        assert abs(lse - ref_lse) < TOL * 10, "lse != logsumexp"
+        # a non-default scale reaches the dot product
+        out2, _ = OT.attention(q, K, V, None, pos, int(pos[-1]) + 1, 0.37)
+        assert np.max(np.abs(out2 - _sdpa(q, K, V, 0.37))) < TOL * 10
+
+
+# ---------------------------------------------------------------- P2
+def check_bias_closed_form(seed=1):
+    """Weights e^{scale q.k_i} * beta_i^(t - pos_i), renormalised, with no logs.
+
+    Positions are gapped (slot != position) and include the decode token at
+    distance 0 with beta = 0 (beta^0 = 1).
+    """
+    r = _rng(seed)
+    for n in (1, 2, 5, 9):
+        D = 8
+        q = r.standard_normal(D)
+        K = r.standard_normal((n, D))
+        V = r.standard_normal((n, D))
+        scale = 1.0 / math.sqrt(D)
+        pos = np.sort(r.choice(40, size=n, replace=False)).astype(np.int64)
+        t = int(pos[-1])                       # the newest token is the query token
+        lb32 = np.log(r.uniform(0.4, 1.0, size=n)).astype(np.float32)
+        lb32[-1] = -np.inf                     # beta = 0 at distance 0
+        beta = np.exp(lb32.astype(np.float64))
+        w = np.array([math.exp(scale * float(q @ K[i])) * (beta[i] ** int(t - pos[i]))
+                      for i in range(n)])
+        ref = (w @ V) / w.sum()
+        out, lse = OT.attention(q, K, V, lb32, pos, t, scale)
+        assert np.max(np.abs(out - ref)) < 1e-12, "biased attention != closed form"
+        assert abs(lse - math.log(w.sum())) < 1e-12, "biased lse != closed form"
+
+
+# ---------------------------------------------------------------- P3
+def _rand_state(r, D, empty=False):
+    if empty:
+        return (np.zeros(D), -np.inf, 0.0)
+    return (r.standard_normal(D), float(r.normal(0, 30)), float(r.uniform(0.5, 50)))
+
+
+def check_split_merge(seed=2):
+    """Online-softmax identity: any partition (empty blocks included), merged, equals
+    full attention; merge is associative, commutative, and (0,-inf,0) is its identity."""
+    r = _rng(seed)
+    for n, D in ((1, 4), (33, 8), (200, 16)):
+        q = r.standard_normal(D)
+        K = r.standard_normal((n, D)) * 1.5
+        V = r.standard_normal((n, D))
+        pos = np.arange(n)
+        t = n
+        lb = np.log(r.uniform(0.8, 1.0, size=n)).astype(np.float32)
+        full_o, full_l = OT.attention(q, K, V, lb, pos, t, 0.5)
+        for _ in range(5):
+            cuts = np.sort(r.integers(0, n + 1, size=r.integers(0, 6)))
+            bounds = [0] + [int(c) for c in cuts] + [n]
+            o, l, _ = OT.split_attention(q, K, V, lb, pos, t, 0.5, bounds)
+            assert np.max(np.abs(o - full_o)) < TOL * 10, "split+merge != full"
+            assert abs(l - full_l) < TOL * 10, "split+merge lse != full"
+    D = 6
+    for _ in range(20):
+        A, Bs, C = (_rand_state(r, D, empty=(r.uniform() < 0.2)) for _ in range(3))
+        ab_c = OT.state_to_out_lse(OT.merge_states([OT.merge_states([A, Bs]), C]))
+        a_bc = OT.state_to_out_lse(OT.merge_states([A, OT.merge_states([Bs, C])]))
+        ba = OT.state_to_out_lse(OT.merge_states([Bs, A]))
+        ab = OT.state_to_out_lse(OT.merge_states([A, Bs]))
+        assert np.allclose(ab_c[0], a_bc[0], atol=1e-12) and \
+            (ab_c[1] == a_bc[1] or abs(ab_c[1] - a_bc[1]) < 1e-12), "merge not associative"
+        assert np.allclose(ab[0], ba[0], atol=1e-12), "merge not commutative"
+        ident = OT.state_to_out_lse(OT.merge_states([A, (np.zeros(D), -np.inf, 0.0)]))
+        a_only = OT.state_to_out_lse(OT.merge_states([A]))
+        assert np.allclose(ident[0], a_only[0]) and \
+            (ident[1] == a_only[1]), "empty state is not the identity"
+    # two explicit states against the page's formula (Z_A a_A + Z_B a_B)/(Z_A + Z_B)
+    aA, aB = r.standard_normal(D), r.standard_normal(D)
+    ZA, ZB = 3.0, 5.0
+    o, l = OT.state_to_out_lse(OT.merge_states([(aA, 0.0, ZA), (aB, 0.0, ZB)]))
+    assert np.allclose(o, (ZA * aA + ZB * aB) / (ZA + ZB), atol=1e-14)
+    assert abs(l - math.log(ZA + ZB)) < 1e-14
+
+
+# ---------------------------------------------------------------- P4
+def check_asm_lossless(seed=3):
+    """Merging a query's own state with the prefix state equals attention over
+    [prefix; own tokens] (torch SDPA); log Zbar = -inf leaves the own state."""
+    r = _rng(seed)
+    D = 16
+    scale = 1.0 / math.sqrt(D)
+    for npre, nself in ((5, 3), (64, 17), (1, 1)):
+        q = r.standard_normal(D)
+        Kp, Vp = r.standard_normal((npre, D)), r.standard_normal((npre, D))
+        Ks, Vs = r.standard_normal((nself, D)), r.standard_normal((nself, D))
+        abar, lzbar = OT.attention(q, Kp, Vp, None, np.arange(npre), npre, scale)
+        so, sl = OT.attention(q, Ks, Vs, None, np.arange(nself), nself, scale)
+        mo, ml = OA.asm_merge(so, sl, abar, lzbar)
+        ref = _sdpa(q, np.vstack([Kp, Ks]), np.vstack([Vp, Vs]), scale)
+        ref_l = scipy.special.logsumexp(scale * (np.vstack([Kp, Ks]) @ q))
+        assert np.max(np.abs(mo - ref)) < 1e-12, "ASM merge is not lossless"
+        assert abs(ml - ref_l) < 1e-12, "ASM merge lse is not lossless"
+        mo2, ml2 = OA.asm_merge(so, sl, abar, -np.inf)
+        assert np.allclose(mo2, so, atol=1e-15) and abs(ml2 - sl) < 1e-15
+        mo3, ml3 = OA.asm_merge(np.zeros(D), -np.inf, abar, lzbar)
+        assert np.allclose(mo3, abar, atol=1e-15) and abs(ml3 - lzbar) < 1e-15
+
+
+# ---------------------------------------------------------------- P5
+def _score_order_key(beta, d, p):
+    return (beta ** d, p)
+
+
+def check_evict_bruteforce(seed=4, trials=40):
+    """For n <= 10 exactly one M-subset has every kept token above every evicted one
+    in (beta^(t-i), position) order, scores taken as the plain power; it must be the
+    oracle's kept set."""
+    r = _rng(seed)
+    for _ in range(trials):
+        n = int(r.integers(1, 11))
+        M = int(r.integers(0, n + 1))
+        pos = np.sort(r.choice(30, size=n, replace=False)).astype(np.int64)
+        t = int(pos[-1]) + int(r.integers(0, 3))
+        lb32 = np.log(r.uniform(0.3, 1.0, size=n)).astype(np.float32)
+        if r.uniform() < 0.3:       # force ties in the score
+            lb32[:] = lb32[0]
+        beta = np.exp(lb32.astype(np.float64))
+        keys = [_score_order_key(float(beta[i]), int(t - pos[i]), int(pos[i])) for i in range(n)]
+        m_keep = min(n, M)
+        good = []
+        for kept in itertools.combinations(range(n), m_keep):
+            ks = set(kept)
+            ev = [keys[i] for i in range(n) if i not in ks]
+            kp = [keys[i] for i in kept]
+            if not ev or not kp or min(kp) > max(ev):
+                good.append(ks)
+        assert len(good) == 1, "brute force: separating subset not unique"
+        keep, gone = OE.evict_plan(lb32, pos, n, t, M)
+        assert set(np.nonzero(keep)[0].tolist()) == good[0], "eviction != brute force"
+        assert list(gone) == sorted(pos[~keep].tolist()), "evicted positions"
+
+
+def check_evict_sliding_window(seed=5):
+    """beta == 1 (no array) or one shared beta: the newest M tokens stay."""
+    r = _rng(seed)
+    for n, M in ((10, 3), (50, 49), (7, 0), (5, 5), (5, 9), (300, 17)):
+        pos = np.sort(r.choice(10 * n + 10, size=n, replace=False)).astype(np.int64)
+        t = int(pos[-1]) + 1
+        for lb in (None, np.full(n, np.float32(np.log(0.9)), np.float32),
+                   np.zeros(n, np.float32)):
+            keep, gone = OE.evict_plan(lb, pos, n, t, M)
+            want = np.zeros(n, bool)
+            want[max(0, n - M):] = True
+            assert np.array_equal(keep, want), "sliding window"
+            assert len(gone) == max(0, n - M)
+
+
+def check_evict_invariants(seed=6):
+    """len = min(n, M); the decode token (distance 0) stays when M >= 1; kept and
+    evicted partition the live tokens; -0.0 and +0.0 are one key."""
+    r = _rng(seed)
+    for _ in range(30):
+        n = int(r.integers(1, 200))
+        M = int(r.integers(0, n + 5))
+        pos = np.arange(n, dtype=np.int64)
+        t = n - 1
+        lb = np.log(1.0 / (1.0 + np.exp(-r.normal(2, 1.5, size=n)))).astype(np.float32)
+        keep, gone = OE.evict_plan(lb, pos, n, t, M)
+        assert keep.sum() == min(n, M)
+        if M >= 1:
+            assert keep[-1], "decode token evicted"
+        assert sorted(np.concatenate([pos[keep], gone]).tolist()) == pos.tolist()
+    k = OE.retention_keys(np.array([-0.5, 0.0, -0.0], np.float32), np.array([3, 1, 2]), 3)
+    assert not np.signbit(k).any() and np.all(k == 0.0), "-0.0 not canonical"
+    k2 = OE.retention_keys(np.array([-0.5, -0.25], np.float32), np.array([1, 2]), 3)
+    assert k2.tolist() == [-1.0, -0.25], "key = (t - pos) * log beta"
+    assert OE.retention_keys(None, np.array([0, 5]), 9).tolist() == [0.0, 0.0]
+
+
+# ---------------------------------------------------------------- P6
+def check_compaction(seed=7):
+    """Compaction keeps each kept row bit for bit, in slot order; positions stay
+    strictly increasing; rows are moved as raw storage values."""
+    r = _rng(seed)
+    B, H, cap, D = 2, 3, 40, 4
+    c = OE.Cache(r.integers(0, 65535, size=(B, H, cap, D)).astype(np.uint16),
+                 r.integers(0, 65535, size=(B, H, cap, D)).astype(np.uint16),
+                 r.standard_normal((B, H, cap)).astype(np.float32),
+                 np.tile(np.arange(cap, dtype=np.int32) * 2, (B, H, 1)),
+                 np.full((B, H), 33, np.int32))
+    for b in range(B):
+        for g in range(H):
+            keep = r.uniform(size=33) < 0.4
+            before = c.copy()
+            kept = OE.compact_unit(c, b, g, keep)
+            idx = np.nonzero(keep)[0]
+            assert kept == idx.size and c.length[b, g] == kept
+            for j, s in enumerate(idx):
+                assert np.array_equal(c.k[b, g, j], before.k[b, g, s])
+                assert np.array_equal(c.v[b, g, j], before.v[b, g, s])
+                assert c.log_beta[b, g, j].tobytes() == before.log_beta[b, g, s].tobytes()
+                assert c.pos[b, g, j] == before.pos[b, g, s]
+            assert np.all(np.diff(c.pos[b, g, :kept]) > 0)
+
+
+# ---------------------------------------------------------------- P7
+def check_erase_bruteforce(seed=8):
+    """Set filter written as a plain loop; empty range list is the identity."""
+    r = _rng(seed)
+    for _ in range(30):
+        n = int(r.integers(0, 60))
+        pos = np.sort(r.choice(200, size=n, replace=False)).astype(np.int64)
+        edges = np.sort(r.choice(210, size=2 * int(r.integers(0, 5)), replace=False))
+        ranges = edges.reshape(-1, 2)
+        keep = OE.erase_plan(pos, n, ranges)
+        for i in range(n):
+            inside = False
+            for s, e in ranges:
+                if s <= pos[i] and pos[i] < e:
+                    inside = True
+            assert keep[i] == (not inside), "erase != set filter"
+        assert OE.erase_plan(pos, n, np.zeros((0, 2), np.int64)).all()
+
+
+# ---------------------------------------------------------------- P8
+def check_lookup_bruteforce(seed=9):
+    """Cosine argmax written as a loop with math.sqrt; ties to the lowest index;
+    q = lambda * c_j finds j; centroids of unequal length."""
+    r = _rng(seed)
+    for K, D in ((1, 4), (9, 8), (64, 16)):
+        C = r.standard_normal((K, D)) * r.uniform(0.2, 3.0, size=(K, 1))
+        if K > 3:
+            C[K - 1] = C[1]                                    # duplicate: tie
+        q = r.standard_normal(D)
+        best, bk = -2.0, -1
+        qn = math.sqrt(sum(x * x for x in q))
+        for k in range(K):
+            dot = sum(float(C[k, d]) * float(q[d]) for d in range(D))
+            cn = math.sqrt(sum(float(x) * float(x) for x in C[k]))
+            cs = dot / (cn * qn)
+            if cs > best:
+                best, bk = cs, k
+        assert OA.cosine_lookup(q, C) == bk, "lookup != brute force"
+        j = int(r.integers(0, K))
+        if K > 3 and j == K - 1:
+            j = 1
+        assert OA.cosine_lookup(2.5 * C[j], C) == j, "q = lambda c_j"
+    # a long centroid at a wider angle: the raw dot product prefers it, cosine does not
+    C = np.array([[1.0, 0.0, 0.0], [10.0, 10.0, 0.0], [0.0, 0.0, 1.0]])
+    assert OA.cosine_lookup(np.array([1.0, 0.1, 0.0]), C) == 0, "cosine, not dot product"
+    # equal similarities: the lowest index wins
+    C = np.array([[0.0, 1.0], [2.0, 0.0], [0.0, 3.0], [5.0, 0.0]])
+    assert OA.cosine_lookup(np.array([1.0, 0.0]), C) == 1, "ties go to the lowest index"
+    assert OA.cosine_lookup(np.array([0.0, 0.5]), C) == 0, "ties go to the lowest index"
+
+
+# ---------------------------------------------------------------- P9
+def check_bytes_model():
+    """IndexMem's memory-wall estimate: ~320 GB of KV for a 70B model at 1M tokens."""
+    per_tok = OB.kv_bytes_per_token(80, 8, 128, 2)
+    assert per_tok * (1 << 20) == 320 * (1 << 30)
+
+
+ALL = [check_attention_library, check_bias_closed_form, check_split_merge,
+       check_asm_lossless, check_evict_bruteforce, check_evict_sliding_window,
+       check_evict_invariants, check_compaction, check_erase_bruteforce,
+       check_lookup_bruteforce, check_bytes_model]

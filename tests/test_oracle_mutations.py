@@ -1,0 +1,184 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail a pin.
+
+Every mutant below is a plausible slip -- a dropped term, a wrong sign or
+index, a transposed operand, a reversed tie-break -- patched into the oracle
+module for the duration of one test.  The test passes only if at least one pin
+raises, which shows the pins can tell a wrong oracle from a right one.
+"""
+import numpy as np
+import pytest
+
+import oracle.asm as OA
+import oracle.attn as OT
+import oracle.evict as OE
+import pins
+
+_orig_bias = OT.retention_bias
+_orig_state = OT.attention_state
+_orig_merge = OT.merge_states
+_orig_keys = OE.retention_keys
+_orig_plan = OE.evict_plan
+
+
+def bias_sign_flipped(log_beta, pos, t):
+    return -_orig_bias(log_beta, pos, t)
+
+
+def bias_dropped(log_beta, pos, t):
+    return _orig_bias(None, pos, t)
+
+
+def bias_uses_slot(log_beta, pos, t):
+    slots = np.arange(np.asarray(pos).shape[0]) + (int(t) - int(np.asarray(pos)[-1]) if
+                                                   np.asarray(pos).size else 0)
+    return _orig_bias(log_beta, slots, t)
+
+
+def bias_ignores_zero_distance(log_beta, pos, t):
+    pos = np.asarray(pos, dtype=np.int64)
+    if log_beta is None:
+        return np.zeros(pos.shape)
+    with np.errstate(invalid="ignore"):
+        return (t - pos).astype(np.float64) * np.asarray(log_beta, np.float64)
+
+
+def state_bias_scaled(q, K, V, bias, scale):
+    return _orig_state(q, K, V, np.asarray(bias) * scale, scale)
+
+
+def state_no_scale(q, K, V, bias, scale):
+    return _orig_state(q, K, V, bias, 1.0)
+
+
+def state_k_for_v(q, K, V, bias, scale):
+    return _orig_state(q, K, K, bias, scale)
+
+
+def merge_weights_swapped(states):
+    a, m, Z = None, -np.inf, 0.0
+    for a2, m2, Z2 in states:
+        a2 = np.asarray(a2, dtype=np.float64)
+        if Z2 == 0.0:
+            a = np.zeros_like(a2) if a is None else a
+            continue
+        if Z == 0.0:
+            a, m, Z = a2.copy(), float(m2), float(Z2)
+            continue
+        M = max(m, float(m2))
+        wa, wb = Z * np.exp(m - M), Z2 * np.exp(float(m2) - M)
+        a = (wb * a + wa * a2) / (wa + wb)
+        m, Z = M, wa + wb
+    return a, m, Z
+
+
+def merge_no_rescale(states):
+    a, m, Z = None, -np.inf, 0.0
+    for a2, m2, Z2 in states:
+        a2 = np.asarray(a2, dtype=np.float64)
+        if Z2 == 0.0:
+            a = np.zeros_like(a2) if a is None else a
+            continue
+        if Z == 0.0:
+            a, m, Z = a2.copy(), float(m2), float(Z2)
+            continue
+        a = (Z * a + Z2 * a2) / (Z + Z2)
+        m, Z = max(m, float(m2)), Z + Z2
+    return a, m, Z
+
+
+def keys_negated(log_beta, pos, t):
+    return -_orig_keys(log_beta, pos, t)
+
+
+def keys_no_distance(log_beta, pos, t):
+    pos = np.asarray(pos)
+    if log_beta is None:
+        return np.zeros(pos.shape)
+    return np.asarray(log_beta, np.float64) + 0.0
+
+
+def plan_ties_high_first(log_beta, pos, n, t, M):
+    keep = np.ones(n, dtype=bool)
+    if n <= M:
+        return keep, np.zeros(0, np.int32)
+    p = np.asarray(pos)[:n].astype(np.int64)
+    lb = None if log_beta is None else np.asarray(log_beta)[:n]
+    key = OE.retention_keys(lb, p, t)
+    order = np.lexsort((-p, key))
+    keep[order[: n - M]] = False
+    return keep, np.sort(p[~keep]).astype(np.int32)
+
+
+def plan_off_by_one(log_beta, pos, n, t, M):
+    return _orig_plan(log_beta, pos, n, t, M + 1)
+
+
+def erase_closed(pos, n, ranges):
+    p = np.asarray(pos)[:n].astype(np.int64)
+    keep = np.ones(n, dtype=bool)
+    for s, e in np.asarray(ranges, dtype=np.int64).reshape(-1, 2):
+        keep &= ~((p >= s) & (p <= e))
+    return keep
+
+
+def lookup_raw_dot(q, centroids):
+    return int(np.argmax(np.asarray(centroids, np.float64) @ np.asarray(q, np.float64)))
+
+
+def lookup_last_tie(q, centroids):
+    cos = OA.cosine_similarities(q, centroids)
+    return int(len(cos) - 1 - np.argmax(cos[::-1]))
+
+
+def asm_merge_linear(out, lse, abar, log_zbar):
+    w1, w2 = lse, log_zbar
+    if not np.isfinite(w1):
+        return np.asarray(abar, np.float64), log_zbar
+    if not np.isfinite(w2):
+        return np.asarray(out, np.float64), lse
+    return (w1 * np.asarray(out) + w2 * np.asarray(abar)) / (w1 + w2), np.logaddexp(lse, log_zbar)
+
+
+def compact_reversed(cache, b, g, keep):
+    n = keep.shape[0]
+    idx = np.nonzero(keep)[0][::-1]
+    kept = idx.shape[0]
+    for arr in (cache.k, cache.v, cache.pos) + (() if cache.log_beta is None
+                                                  else (cache.log_beta,)):
+        arr[b, g, :kept] = arr[b, g, :n][idx].copy()
+    cache.length[b, g] = kept
+    return kept
+
+
+MUTANTS = [
+    (OT, "retention_bias", bias_sign_flipped),
+    (OT, "retention_bias", bias_dropped),
+    (OT, "retention_bias", bias_uses_slot),
+    (OT, "retention_bias", bias_ignores_zero_distance),
+    (OT, "attention_state", state_bias_scaled),
+    (OT, "attention_state", state_no_scale),
+    (OT, "attention_state", state_k_for_v),
+    (OT, "merge_states", merge_weights_swapped),
+    (OT, "merge_states", merge_no_rescale),
+    (OE, "retention_keys", keys_negated),
+    (OE, "retention_keys", keys_no_distance),
+    (OE, "evict_plan", plan_ties_high_first),
+    (OE, "evict_plan", plan_off_by_one),
+    (OE, "erase_plan", erase_closed),
+    (OA, "cosine_lookup", lookup_raw_dot),
+    (OA, "cosine_lookup", lookup_last_tie),
+    (OA, "asm_merge", asm_merge_linear),
+    (OE, "compact_unit", compact_reversed),
+]
+
+
+@pytest.mark.parametrize("mod,name,mutant", MUTANTS, ids=lambda x: getattr(x, "__name__", ""))
+def test_mutant_fails_a_pin(monkeypatch, mod, name, mutant):
+    monkeypatch.setattr(mod, name, mutant)
+    failed = []
+    for check in pins.ALL:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(check.__name__)
+    assert failed, f"no pin caught the planted mistake {mutant.__name__}"
