@@ -1,0 +1,22 @@
+"""Python binding of libkvbound (decode attention over a memory-bounded KV cache).
+
+Argument marshalling only: every step runs in the HIP library's kernels.  Torch
+tensors supply device memory and the current stream.  The library must be built
+(``python -m bounded_decode_attention_amd.build``); importing this module does
+not build it, and every call fails loudly if it is missing.
+
+Entry points (same names as the C ABI in include/kvbound.h):
+    kv_attn_decode, kv_evict_to_budget, kv_erase_ranges, asm_lookup_merge
+plus the workspace-size helpers and ``KVCache``, a holder of one layer's tensors.
+"""
+from ._lib import (KVBError, KVCache, asm_lookup_merge, asm_lookup_merge_workspace,
+                   kv_attn_decode, kv_attn_decode_splits, kv_attn_decode_workspace,
+                   kv_erase_ranges, kv_erase_workspace, kv_evict_to_budget,
+                   kv_evict_workspace, library, library_path, strerror)
+
+__all__ = [
+    "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
+    "asm_lookup_merge", "kv_attn_decode_workspace", "kv_attn_decode_splits",
+    "kv_evict_workspace", "kv_erase_workspace", "asm_lookup_merge_workspace",
+    "library", "library_path", "strerror",
+]

@@ -1,0 +1,255 @@
+"""ctypes marshalling for libkvbound.so (see include/kvbound.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvbound.so")
+_lib = None
+
+KVB_F32, KVB_BF16 = 0, 1
+
+
+class KVBError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("log_beta", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("len", ctypes.c_void_p), ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("cap", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """The loaded shared library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"libkvbound.so is not built ({_LIB_PATH}); run "
+                              "python -m bounded_decode_attention_amd.build")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        CP = ctypes.POINTER(_Cache)
+        sigs = {
+            "kvb_strerror": (ctypes.c_char_p, [I32]),
+            "kv_attn_decode_splits": (I32, [CP, I32]),
+            "kv_attn_decode_workspace": (SZ, [CP, I32, I32]),
+            "kv_evict_workspace": (SZ, [CP, I32]),
+            "kv_erase_workspace": (SZ, [CP]),
+            "asm_lookup_merge_workspace": (SZ, [I32, I32, I32, I32, I32]),
+            "kv_attn_decode": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P]),
+            "kv_evict_to_budget": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
+            "kv_erase_ranges": (I32, [CP, P, P, I32, P, P, SZ, P]),
+            "asm_lookup_merge": (I32, [P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, P, P,
+                                       SZ, P]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return library().kvb_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, where):
+    if status != 0:
+        raise KVBError(status, where)
+
+
+def _need(t, name, dtype=None, device=True):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+class KVCache:
+    """One layer's cache tensors (all on the same device, contiguous).
+
+    k, v      [B][Hkv][cap][D] bfloat16 or float32
+    log_beta  [B][Hkv][cap] float32, or None (beta == 1)
+    pos       [B][Hkv][cap] int32
+    length    [B][Hkv] int32 (device)
+    """
+
+    def __init__(self, k, v, log_beta, pos, length):
+        _need(k, "k")
+        _need(v, "v", k.dtype)
+        if k.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("k/v dtype must be bfloat16 or float32")
+        if k.shape != v.shape or k.dim() != 4:
+            raise ValueError("k, v must both be [B][Hkv][cap][D]")
+        B, H, cap, D = k.shape
+        if log_beta is not None:
+            _need(log_beta, "log_beta", torch.float32)
+            if tuple(log_beta.shape) != (B, H, cap):
+                raise ValueError("log_beta must be [B][Hkv][cap]")
+        _need(pos, "pos", torch.int32)
+        _need(length, "length", torch.int32)
+        if tuple(pos.shape) != (B, H, cap) or tuple(length.shape) != (B, H):
+            raise ValueError("pos must be [B][Hkv][cap], length [B][Hkv]")
+        self.k, self.v, self.log_beta, self.pos, self.length = k, v, log_beta, pos, length
+        self.B, self.Hkv, self.cap, self.D = B, H, cap, D
+        self.dtype = KVB_BF16 if k.dtype == torch.bfloat16 else KVB_F32
+        self._desc = _Cache(k.data_ptr(), v.data_ptr(),
+                            None if log_beta is None else log_beta.data_ptr(),
+                            pos.data_ptr(), length.data_ptr(), B, H, cap, D, self.dtype)
+
+    @classmethod
+    def from_dict(cls, d):
+        return cls(d["k"], d["v"], d.get("log_beta"), d["pos"], d["len"])
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+
+def _ws(ws, nbytes, device):
+    """The caller's workspace (uint8 device tensor), or a new one of the needed size.
+    A caller workspace that is too small is passed through; the library rejects it."""
+    if ws is None:
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def kv_attn_decode_splits(cache: KVCache, Hq: int) -> int:
+    return int(library().kv_attn_decode_splits(cache.desc, Hq))
+
+
+def kv_attn_decode_workspace(cache: KVCache, Hq: int, num_splits: int = 0) -> int:
+    return int(library().kv_attn_decode_workspace(cache.desc, Hq, num_splits))
+
+
+def kv_evict_workspace(cache: KVCache, M: int) -> int:
+    return int(library().kv_evict_workspace(cache.desc, M))
+
+
+def kv_erase_workspace(cache: KVCache) -> int:
+    return int(library().kv_erase_workspace(cache.desc))
+
+
+def asm_lookup_merge_workspace(B, Hq, Hkv, D, K) -> int:
+    return int(library().asm_lookup_merge_workspace(B, Hq, Hkv, D, K))
+
+
+def kv_attn_decode(cache: KVCache, q, t, scale: float = 0.0, k_new=None, v_new=None,
+                   log_beta_new=None, num_splits: int = 0, out=None, lse=None, ws=None,
+                   stream=None):
+    """Append (optional) + retention-biased GQA decode attention.  Returns (out, lse)."""
+    _need(q, "q", cache.k.dtype)
+    _need(t, "t", torch.int32)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x is not None:
+            _need(x, name, cache.k.dtype)
+    if log_beta_new is not None:
+        _need(log_beta_new, "log_beta_new", torch.float32)
+    ws = _ws(ws, kv_attn_decode_workspace(cache, Hq, num_splits), q.device)
+    st = library().kv_attn_decode(cache.desc, _ptr(q), Hq, _ptr(t), float(scale), _ptr(k_new),
+                                  _ptr(v_new), _ptr(log_beta_new), int(num_splits), _ptr(out),
+                                  _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_attn_decode")
+    return out, lse
+
+
+def kv_evict_to_budget(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=None, ws=None,
+                       stream=None):
+    """Evict every head over budget to M slots and compact in place.
+
+    evicted_pos: optional int32 [B][Hkv][max_evict] tensor (ascending positions).
+    Returns n_evicted [B][Hkv] int32 (allocated if not given).
+    """
+    _need(t, "t", torch.int32)
+    if n_evicted is None:
+        n_evicted = torch.empty((cache.B, cache.Hkv), dtype=torch.int32, device=t.device)
+    _need(n_evicted, "n_evicted", torch.int32)
+    max_evict = 0
+    if evicted_pos is not None:
+        _need(evicted_pos, "evicted_pos", torch.int32)
+        max_evict = evicted_pos.shape[-1]
+    ws = _ws(ws, kv_evict_workspace(cache, M), t.device)
+    st = library().kv_evict_to_budget(cache.desc, _ptr(t), int(M), _ptr(evicted_pos), max_evict,
+                                      _ptr(n_evicted), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_evict_to_budget")
+    return n_evicted
+
+
+def kv_erase_ranges(cache: KVCache, ranges, n_ranges, n_erased=None, ws=None, stream=None):
+    """Erase half-open position ranges ([B][R][2] int32) from every head; compact in place."""
+    _need(ranges, "ranges", torch.int32)
+    _need(n_ranges, "n_ranges", torch.int32)
+    if ranges.dim() != 3 or ranges.shape[-1] != 2:
+        raise ValueError("ranges must be [B][R][2]")
+    if n_erased is None:
+        n_erased = torch.empty((cache.B, cache.Hkv), dtype=torch.int32, device=ranges.device)
+    ws = _ws(ws, kv_erase_workspace(cache), ranges.device)
+    st = library().kv_erase_ranges(cache.desc, _ptr(ranges), _ptr(n_ranges), ranges.shape[1],
+                                   _ptr(n_erased), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_erase_ranges")
+    return n_erased
+
+
+def asm_lookup_merge(q, centroids, abar, log_zbar, self_out, self_lse, out=None, out_lse=None,
+                     idx=None, ws=None, stream=None):
+    """Cosine-argmax codebook lookup + merge with the query's own state.
+
+    Returns (out, out_lse, idx).
+    """
+    _need(q, "q", torch.bfloat16)
+    _need(centroids, "centroids", torch.bfloat16)
+    _need(abar, "abar", torch.bfloat16)
+    _need(log_zbar, "log_zbar", torch.float32)
+    _need(self_out, "self_out", torch.float32)
+    _need(self_lse, "self_lse", torch.float32)
+    B, Hq, D = q.shape
+    Hkv, K, D2 = centroids.shape
+    if D2 != D or tuple(abar.shape) != (Hkv, K, D) or tuple(log_zbar.shape) != (Hkv, K):
+        raise ValueError("codebook shapes must be [Hkv][K][D] and [Hkv][K]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
+    ws = _ws(ws, asm_lookup_merge_workspace(B, Hq, Hkv, D, K), q.device)
+    st = library().asm_lookup_merge(_ptr(q), B, Hq, Hkv, D, _ptr(centroids), _ptr(abar),
+                                    _ptr(log_zbar), K, _ptr(self_out), _ptr(self_lse), _ptr(out),
+                                    _ptr(out_lse), _ptr(idx), _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    _check(st, "asm_lookup_merge")
+    return out, out_lse, idx

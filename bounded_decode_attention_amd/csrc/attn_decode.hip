@@ -1,0 +1,540 @@
+// Decode-step GQA attention with the retention bias, split over the KV axis.
+//
+// Logit of token i for a decode query at position t ("Cache What Lasts", section
+// 2.1, retention-gated attention):  s_i = scale * q.k_i + (t - pos_i) * log beta_i.
+// Each split emits an attention state (a, m, Z) and the states are combined with
+// the merge operator of "Context Memorization for Efficient Long Context
+// Generation" (method step 2; online-softmax identity in its background section).
+//
+// Kernels
+//   kv_append          one new token per KV head at slot len; len += 1.
+//   attn_split_mfma    bf16, D in {64,128}, group G in {1,2,4,8}: one wave per
+//                      (KV head, split).  QK^T and PV run on v_mfma_f32_16x16x32_bf16.
+//   attn_split_generic any dtype / D <= 256 / G <= 16; one wave per split, one
+//                      token at a time (used for float32 caches and odd shapes).
+//   attn_merge         merge of the splits' states, in split order.
+//
+// MFMA tile layout (32 tokens per iteration, one wave).  The 16 MFMA columns hold
+// the G query heads (columns 0..G-1) and the same G heads again (G..2G-1); the
+// second copy carries the low-order bf16 part of the probabilities in PV, so
+// P ~= P_hi + P_lo is applied with ~16 significant bits while V stays bf16.
+//   QK^T: A = K rows (lane l: token row l%16, dims 8*(l/16) + 32*kk .. +8), read
+//         straight from HBM (each instruction covers 16 rows x 64 contiguous B);
+//         B = q columns.  Output lane (g=l/16, c=l%16) holds S[token 4g+r][head c].
+//   PV:   O^T[dim][col] += V^T[dim][token] * P^T[token][col].  P^T is consumed in
+//         place: lane (g, c) already holds column c's probabilities of tokens
+//         {4g..4g+3, 16+4g..16+4g+3}, which become its 8 k-slots.  V^T is read from
+//         an LDS copy of the V tile (written with coalesced 16-byte stores); LDS rows
+//         are permuted and padded so that the four lane groups read four disjoint
+//         32-byte bank groups.
+#include "common.h"
+
+namespace kvb {
+
+struct AttnArgs {
+  const void* k;
+  const void* v;
+  const float* log_beta;
+  const int32_t* pos;
+  const int32_t* len;
+  const void* q;
+  const int32_t* t;
+  float* part_a;   // [B][Hq][P][D]
+  float* part_ml;  // [B][Hq][P][2]  (m, Z)
+  int32_t B, Hkv, cap, D, Hq, G, P;
+  float scale_log2;  // scale * log2(e)
+};
+
+// ------------------------------------------------------------------ append
+__global__ __launch_bounds__(64) void kv_append(void* k, void* v, float* log_beta, int32_t* pos,
+                                                int32_t* len, int32_t cap, int32_t row_words,
+                                                const void* k_new, const void* v_new,
+                                                const float* lb_new, const int32_t* t,
+                                                int32_t Hkv, int32_t* status) {
+  const int u = blockIdx.x;
+  const int s = len[u];
+  if (s >= cap) {
+    if (threadIdx.x == 0) status[0] = KVB_ECAPACITY;
+    return;
+  }
+  const size_t dst = ((size_t)u * cap + s) * row_words;
+  const uint32_t* kn = (const uint32_t*)k_new + (size_t)u * row_words;
+  const uint32_t* vn = (const uint32_t*)v_new + (size_t)u * row_words;
+  for (int w = threadIdx.x; w < row_words; w += 64) {
+    ((uint32_t*)k)[dst + w] = kn[w];
+    ((uint32_t*)v)[dst + w] = vn[w];
+  }
+  if (threadIdx.x == 0) {
+    pos[(size_t)u * cap + s] = t[u / Hkv];
+    if (log_beta) log_beta[(size_t)u * cap + s] = lb_new[u];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) len[u] = s + 1;
+}
+
+// Token range of split p of a head with n live tokens: whole 32-token tiles,
+// spread as evenly as possible over the P splits.
+__device__ __forceinline__ void split_range(int n, int p, int P, int& lo, int& hi) {
+  const int tiles = (n + 31) >> 5;
+  const int t0 = (int)(((long long)tiles * p) / P);
+  const int t1 = (int)(((long long)tiles * (p + 1)) / P);
+  lo = t0 * 32;
+  hi = min(t1 * 32, n);
+}
+
+// LDS row of tile token tt (0..31): transposes (tt/4)%4 with tt%4 so that the
+// tokens one PV k-slot reads across the four lane groups sit in adjacent rows.
+__device__ __forceinline__ int lds_row(int tt) {
+  return ((tt >> 2) & 3) + ((tt & 3) << 2) + (tt & 16);
+}
+
+// ------------------------------------------------------------------ MFMA split
+template <int D, int G>
+__global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
+  constexpr int KK = D / 32;     // QK k-steps
+  constexpr int NB = D / 16;     // PV output dim blocks
+  constexpr int CH = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;   // rows per V load instruction
+  constexpr int NV = 32 / RPI;   // V load instructions per tile
+  constexpr int RS = 2 * D + 32; // LDS row stride (bytes)
+  static_assert(2 * G <= 16, "group too large for the hi/lo column split");
+
+  __shared__ __attribute__((aligned(16))) unsigned char vtile[32 * RS];
+
+  const int u = blockIdx.y;
+  const int p = blockIdx.x;
+  const int b = u / a.Hkv;
+  const int g = u - b * a.Hkv;
+  const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int lc = lane & 15;
+
+  const int n = min(a.len[u], a.cap);
+  int lo, end;
+  split_range(n, p, a.P, lo, end);
+  // 16-byte loads of log beta / pos need a 4-slot aligned head base
+  const bool vec_ok = ((size_t)u * a.cap & 3) == 0;
+
+  // q as the B operand: column lc is head lc (lc < G), head lc-G (G <= lc < 2G), or 0.
+  const int hcol = lc < G ? lc : (lc < 2 * G ? lc - G : -1);
+  u32x4 qv[KK];
+  {
+    const uint16_t* qp =
+        (const uint16_t*)a.q + ((size_t)(b * a.Hq + g * G + (hcol < 0 ? 0 : hcol))) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qv[kk] = hcol >= 0 ? *(const u32x4*)(qp + 32 * kk + 8 * lg) : z;
+    }
+  }
+
+  const uint16_t* kb = (const uint16_t*)a.k + (size_t)u * a.cap * D;
+  const uint16_t* vb = (const uint16_t*)a.v + (size_t)u * a.cap * D;
+  const float* lbb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
+  const int32_t* pb = a.pos + (size_t)u * a.cap;
+  const int qpos = a.t[b];
+  const float sc = a.scale_log2;
+
+  float m2 = kNegInf;  // running max of this column's logits (log2 units)
+  float lsum = 0.f;    // this lane's share of Z (its 8 tokens per tile)
+  f32x4 acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int tb = lo; tb < end; tb += 32) {
+    const bool full = tb + 32 <= end;
+    const int last = end - 1;
+
+    // ---- global loads: K (MFMA A layout), V (coalesced rows), bias inputs
+    u32x4 kr[2][KK];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int row = tb + 16 * j + lc;
+      if (!full) row = min(row, last);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kr[j][kk] = *(const u32x4*)(kb + (size_t)row * D + 32 * kk + 8 * lg);
+    }
+    u32x4 vr[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int row = tb + RPI * i + lane / CH;
+      if (!full) row = min(row, last);
+      vr[i] = *(const u32x4*)(vb + (size_t)row * D + 8 * (lane % CH));
+    }
+    float lbv[2][4];
+    int pv[2][4];
+    if (lbb) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r0 = tb + 16 * j + 4 * lg;
+        if (full && vec_ok) {
+          const f32x4 l4 = *(const f32x4*)(lbb + r0);
+          const i32x4 p4 = *(const i32x4*)(pb + r0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            lbv[j][r] = l4[r];
+            pv[j][r] = p4[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = min(r0 + r, last);
+            lbv[j][r] = lbb[row];
+            pv[j][r] = pb[row];
+          }
+        }
+      }
+    }
+
+    // ---- V tile to LDS (row-permuted)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int tt = RPI * i + lane / CH;
+      *(u32x4*)(vtile + lds_row(tt) * RS + 16 * (lane % CH)) = vr[i];
+    }
+
+    // ---- S = K q^T on MFMA
+    f32x4 S[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) S[j] = mfma_16x16x32_bf16(kr[j][kk], qv[kk], S[j]);
+    }
+
+    // ---- logits (log2 units), online max
+    float s[2][4];
+    float mt = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tb + 16 * j + 4 * lg + r;
+        float bias = 0.f;
+        if (lbb) {
+          const int d = qpos - pv[j][r];
+          bias = d != 0 ? (float)d * lbv[j][r] : 0.f;
+        }
+        float x = fmaf(S[j][r], sc, bias * kLog2e);
+        if (tok >= end) x = kNegInf;
+        s[j][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    if (mt > m2) {
+      const float alpha = (m2 == kNegInf) ? 0.f : exp2_fast(m2 - mt);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] *= alpha;
+      lsum *= alpha;
+      m2 = mt;
+    }
+    const float mref = (m2 == kNegInf) ? 0.f : m2;
+
+    // ---- probabilities -> bf16 hi (columns < G) / lo (columns G..2G-1) B operand
+    uint32_t pw[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t h[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int e = 2 * e2 + w;
+        const float x = exp2_fast((e < 4 ? s[0][e] : s[1][e - 4]) - mref);
+        lsum += x;
+        const uint32_t xb = __float_as_uint(x);
+        const uint32_t hi = xb >> 16;
+        const uint32_t lo16 = f32_to_bf16_rne(x - __uint_as_float(xb & 0xFFFF0000u));
+        h[w] = lc < G ? hi : lo16;
+      }
+      pw[e2] = h[0] | (h[1] << 16);
+    }
+    const u32x4 pb4 = {pw[0], pw[1], pw[2], pw[3]};
+
+    // ---- O^T += V^T P^T on MFMA; V^T gathered from LDS
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const unsigned char* col = vtile + 2 * (16 * nb + lc);
+      uint32_t vw[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int e0 = 2 * e2, e1 = 2 * e2 + 1;
+        const int t0 = e0 < 4 ? 4 * lg + e0 : 16 + 4 * lg + e0 - 4;
+        const int t1 = e1 < 4 ? 4 * lg + e1 : 16 + 4 * lg + e1 - 4;
+        const uint32_t v0 = *(const uint16_t*)(col + lds_row(t0) * RS);
+        const uint32_t v1 = *(const uint16_t*)(col + lds_row(t1) * RS);
+        vw[e2] = v0 | (v1 << 16);
+      }
+      const u32x4 va = {vw[0], vw[1], vw[2], vw[3]};
+      acc[nb] = mfma_16x16x32_bf16(va, pb4, acc[nb]);
+    }
+  }
+
+  // ---- epilogue: Z over the four lane groups; hi + lo columns; normalise; store
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // lane (g, c < G) adds the low-part column c + G held by lane + G; the shuffles
+  // run with every lane active (ds_bpermute only reads active lanes)
+  const int src = lane + G < 64 ? lane + G : lane;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nb][i] = (acc[nb][i] + __shfl(acc[nb][i], src, 64)) * inv;
+  if (lc < G) {
+    const int h = g * G + lc;
+    const size_t sidx = ((size_t)(b * a.Hq + h)) * a.P + p;
+    float* pa = a.part_a + sidx * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) *(f32x4*)(pa + 16 * nb + 4 * lg) = acc[nb];
+    if (lg == 0) {
+      a.part_ml[2 * sidx] = m2 == kNegInf ? kNegInf : m2 * kLn2;
+      a.part_ml[2 * sidx + 1] = lsum;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ generic split
+template <typename T, int DPL, int MAXG>
+__global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
+  const int u = blockIdx.y;
+  const int p = blockIdx.x;
+  const int b = u / a.Hkv;
+  const int g = u - b * a.Hkv;
+  const int lane = threadIdx.x;
+  const int D = a.D, G = a.G;
+  const int n = min(a.len[u], a.cap);
+  int lo, end;
+  split_range(n, p, a.P, lo, end);
+
+  auto ld = [](const T* ptr) -> float {
+    if constexpr (sizeof(T) == 2) return bf16_bits_to_f32(*(const uint16_t*)ptr);
+    else return *(const float*)ptr;
+  };
+
+  float qf[MAXG][DPL];
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h)
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      const int d = lane + 64 * j;
+      qf[h][j] = (h < G && d < D)
+                     ? ld((const T*)a.q + ((size_t)(b * a.Hq + g * G + h)) * D + d)
+                     : 0.f;
+    }
+  float m[MAXG], Z[MAXG], acc[MAXG][DPL];
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) {
+    m[h] = kNegInf;
+    Z[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) acc[h][j] = 0.f;
+  }
+  const T* kb = (const T*)a.k + (size_t)u * a.cap * D;
+  const T* vb = (const T*)a.v + (size_t)u * a.cap * D;
+  const float* lbb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
+  const int32_t* pb = a.pos + (size_t)u * a.cap;
+  const int qpos = a.t[b];
+
+  for (int tok = lo; tok < end; ++tok) {
+    float kf[DPL], vf[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      const int d = lane + 64 * j;
+      kf[j] = d < D ? ld(kb + (size_t)tok * D + d) : 0.f;
+      vf[j] = d < D ? ld(vb + (size_t)tok * D + d) : 0.f;
+    }
+    float bias = 0.f;
+    if (lbb) {
+      const int dd = qpos - pb[tok];
+      bias = dd != 0 ? (float)dd * lbb[tok] : 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) {
+      if (h < G) {
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) part = fmaf(qf[h][j], kf[j], part);
+        const float s = fmaf(wave_sum(part), a.scale_log2, bias * kLog2e);
+        const float mn = fmaxf(m[h], s);
+        if (mn != kNegInf) {
+          const float alpha = m[h] == kNegInf ? 0.f : exp2_fast(m[h] - mn);
+          const float pr = exp2_fast(s - mn);
+          Z[h] = Z[h] * alpha + pr;
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) acc[h][j] = fmaf(acc[h][j], alpha, pr * vf[j]);
+          m[h] = mn;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) {
+    if (h < G) {
+      const size_t sidx = ((size_t)(b * a.Hq + g * G + h)) * a.P + p;
+      const float inv = Z[h] > 0.f ? 1.f / Z[h] : 0.f;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) {
+        const int d = lane + 64 * j;
+        if (d < D) a.part_a[sidx * D + d] = acc[h][j] * inv;
+      }
+      if (lane == 0) {
+        a.part_ml[2 * sidx] = m[h] == kNegInf ? kNegInf : m[h] * kLn2;
+        a.part_ml[2 * sidx + 1] = Z[h];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ merge
+// One wave per (b, h): fold the P states in split order with the merge operator.
+__global__ __launch_bounds__(64) void attn_merge(const float* part_a, const float* part_ml, int P,
+                                                 int D, float* out, float* lse) {
+  const int bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* ml = part_ml + (size_t)bh * P * 2;
+  const float* pa = part_a + (size_t)bh * P * D;
+  float M = kNegInf;
+  for (int p = lane; p < P; p += 64)
+    if (ml[2 * p + 1] > 0.f) M = fmaxf(M, ml[2 * p]);
+  M = wave_max(M);
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  float W = 0.f;
+  if (M != kNegInf) {
+    for (int p = 0; p < P; ++p) {
+      const float Zp = ml[2 * p + 1];
+      if (Zp > 0.f) {
+        const float w = Zp * __expf(ml[2 * p] - M);
+        W += w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = lane + 64 * j;
+          if (d < D) o[j] = fmaf(w, pa[(size_t)p * D + d], o[j]);
+        }
+      }
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = lane + 64 * j;
+    if (d < D) out[(size_t)bh * D + d] = o[j] * inv;
+  }
+  if (lane == 0) lse[bh] = W > 0.f ? M + __logf(W) : kNegInf;
+}
+
+// ------------------------------------------------------------------ host
+static bool mfma_supported(const kvb_cache* c, int G) {
+  return c->dtype == KVB_BF16 && (c->D == 64 || c->D == 128) &&
+         (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+template <int D, int G>
+static void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_split_mfma<D, G>), grid, dim3(64), 0, s, a);
+}
+
+static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.P, c->B * c->Hkv);
+  if (mfma_supported(c, a.G)) {
+#define KVB_MFMA_CASE(DD, GG) \
+  if (c->D == DD && a.G == GG) { launch_mfma<DD, GG>(a, grid, s); return KVB_OK; }
+    KVB_MFMA_CASE(128, 1) KVB_MFMA_CASE(128, 2) KVB_MFMA_CASE(128, 4) KVB_MFMA_CASE(128, 8)
+    KVB_MFMA_CASE(64, 1) KVB_MFMA_CASE(64, 2) KVB_MFMA_CASE(64, 4) KVB_MFMA_CASE(64, 8)
+#undef KVB_MFMA_CASE
+  }
+  const int dpl = (c->D + 63) / 64;
+#define KVB_GEN_CASE(TT, DPL)                                                           \
+  if (dpl == DPL) {                                                                     \
+    hipLaunchKernelGGL((attn_split_generic<TT, DPL, 16>), grid, dim3(64), 0, s, a);    \
+    return KVB_OK;                                                                      \
+  }
+  if (c->dtype == KVB_F32) {
+    KVB_GEN_CASE(float, 1) KVB_GEN_CASE(float, 2) KVB_GEN_CASE(float, 3) KVB_GEN_CASE(float, 4)
+  } else {
+    KVB_GEN_CASE(__bf16, 1) KVB_GEN_CASE(__bf16, 2) KVB_GEN_CASE(__bf16, 3)
+    KVB_GEN_CASE(__bf16, 4)
+  }
+#undef KVB_GEN_CASE
+  return KVB_EUNSUPPORTED;
+}
+
+static int32_t auto_splits(const kvb_cache* c) {
+  const long long units = (long long)c->B * c->Hkv;
+  const long long tiles = (c->cap + 31) / 32;
+  long long P = (8192 + units - 1) / units;
+  if (P > tiles) P = tiles;
+  if (P > 1024) P = 1024;
+  if (P < 1) P = 1;
+  return (int32_t)P;
+}
+
+}  // namespace kvb
+
+using namespace kvb;
+
+extern "C" int32_t kv_attn_decode_splits(const kvb_cache* cache, int32_t Hq) {
+  (void)Hq;
+  if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1) return 0;
+  return auto_splits(cache);
+}
+
+extern "C" size_t kv_attn_decode_workspace(const kvb_cache* cache, int32_t Hq, int32_t num_splits) {
+  if (!cache || Hq < 1 || cache->B < 1 || cache->D < 1) return 0;
+  const size_t P = num_splits > 0 ? (size_t)num_splits : (size_t)auto_splits(cache);
+  const size_t S = (size_t)cache->B * Hq * P;
+  return kWsHeader + align_up(S * cache->D * sizeof(float), 256) + align_up(S * 2 * sizeof(float), 256);
+}
+
+extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq,
+                                  const int32_t* t, float scale, const void* k_new,
+                                  const void* v_new, const float* log_beta_new,
+                                  int32_t num_splits, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVB_EINVAL;
+  if (k_new && cache->log_beta && !log_beta_new) return KVB_EINVAL;
+  if (num_splits < 0 || num_splits > 4096) return KVB_EINVAL;
+  const int G = Hq / cache->Hkv;
+  if (!mfma_supported(cache, G) && (G > 16 || cache->D > 256)) return KVB_EUNSUPPORTED;
+  const int P = num_splits > 0 ? num_splits : auto_splits(cache);
+  const size_t need = kv_attn_decode_workspace(cache, Hq, P);
+  if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
+  if ((st = check_device())) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  const size_t S = (size_t)cache->B * Hq * P;
+  AttnArgs a;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.log_beta = cache->log_beta;
+  a.pos = cache->pos;
+  a.len = cache->len;
+  a.q = q;
+  a.t = t;
+  a.part_a = (float*)((char*)ws + kWsHeader);
+  a.part_ml = (float*)((char*)ws + kWsHeader + align_up(S * cache->D * sizeof(float), 256));
+  a.B = cache->B;
+  a.Hkv = cache->Hkv;
+  a.cap = cache->cap;
+  a.D = cache->D;
+  a.Hq = Hq;
+  a.G = G;
+  a.P = P;
+  a.scale_log2 = (scale > 0.f ? scale : 1.0f / sqrtf((float)cache->D)) * kLog2e;
+
+  if (k_new) {
+    const int elem = cache->dtype == KVB_BF16 ? 2 : 4;
+    hipLaunchKernelGGL(kv_append, dim3(cache->B * cache->Hkv), dim3(64), 0, s, cache->k,
+                       cache->v, cache->log_beta, cache->pos, cache->len, cache->cap,
+                       cache->D * elem / 4, k_new, v_new, log_beta_new, t, cache->Hkv,
+                       (int32_t*)ws);
+  }
+  if ((st = launch_split(cache, a, s))) return st;
+  hipLaunchKernelGGL(attn_merge, dim3(cache->B * Hq), dim3(64), 0, s, a.part_a, a.part_ml, P,
+                     cache->D, out, lse);
+  return launch_status();
+}

@@ -1,0 +1,604 @@
+// Retention-score eviction to a budget, MEMENTO range erasure, and the stable
+// in-place compaction both share.
+//
+// Eviction ("Cache What Lasts", section 2.2, inference): a head holding n > M
+// tokens loses the n - M with the lowest retention score beta_i^(t-i).  Tokens
+// are ranked by kappa_i = (t - pos_i) * log beta_i (the log of that score,
+// computed exactly in double: a <= 30-bit integer times a 24-bit significand),
+// ties broken by lower position first.  Erasure ("MEMENTO: Teaching LLMs to
+// Manage Their Own Context", blocks and compression; system engineering) drops
+// every slot whose position lies in one of the sequence's half-open ranges.
+//
+// Kernels
+//   evict_select   one 1024-thread workgroup per head: finds the threshold
+//                  element (kappa*, slot*) -- the (n-M)-th in (kappa, slot) order --
+//                  by a 3-pass radix select on the float32-rounded key (a monotone
+//                  map of kappa), then an exact pass on the 64-bit key among the
+//                  float32 ties, then the slot among exact ties.
+//   keep_count     per 4096-slot chunk: number of kept slots.
+//   keep_emit      per chunk: exclusive scan -> destination slot of every kept
+//                  row (keep_src[dst] = src); evicted positions; rows whose source
+//                  would be overwritten by another workgroup's writes are copied
+//                  to scratch first (see compact_move).
+//   compact_move   per group of MOVE_ROWS destination rows: read every source row
+//                  (from the cache, or from scratch for staged rows), barrier, write.
+//
+// In-place safety: kept row j moves from src_j >= j to j.  A workgroup owns the
+// destination rows [j0, j0 + R); the only rows it writes are its own.  A source
+// row can be clobbered only if it lies below `kept` (nothing is written at or
+// beyond kept) and inside another workgroup's destination range; those sources
+// (src_j >= j0 + R of their own group) are staged by keep_emit, before any move
+// starts.  Sources inside the group's own range are read before the barrier.
+#include <string.h>
+
+#include "common.h"
+
+namespace kvb {
+
+enum { MODE_NOOP = 0, MODE_EVICT = 1, MODE_ERASE = 2 };
+
+struct UnitInfo {
+  uint64_t kstar;  // ordered 64-bit key of the threshold element
+  int32_t sstar;   // its slot
+  int32_t mode;
+  int32_t n;       // live slots before
+  int32_t kept;    // live slots after
+  int32_t pad[2];
+};
+static_assert(sizeof(UnitInfo) == 32, "UnitInfo layout");
+
+constexpr int kChunk = 4096;      // slots per keep_count / keep_emit workgroup
+constexpr int kChunkThreads = 256;
+constexpr int kPerThread = kChunk / kChunkThreads;
+constexpr int kSelThreads = 1024;
+
+// ---------------------------------------------------------------- keys
+__device__ __forceinline__ double retention_key(const float* lb, const int32_t* ps, int i,
+                                                int tq) {
+  if (!lb) return 0.0;
+  const int d = tq - ps[i];
+  if (d == 0) return 0.0;
+  return (double)d * (double)lb[i];
+}
+
+// Order-preserving maps of a double / float to unsigned integers (+0 and -0
+// map to the same value).
+__device__ __forceinline__ uint64_t ord64(double k) {
+  uint64_t b = (uint64_t)__double_as_longlong(k);
+  if ((b << 1) == 0) b = 0;
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+__device__ __forceinline__ uint32_t ord32(double k) {
+  uint32_t b = __float_as_uint((float)k);  // round to nearest: monotone in k
+  if ((b << 1) == 0) b = 0;
+  return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- block helpers
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int x, int* smem, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) smem[w] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int i = 0; i < NT / 64; ++i) {
+      s += smem[i];
+      smem[i] = s;
+    }
+  }
+  __syncthreads();
+  const int off = w > 0 ? smem[w - 1] : 0;
+  total = smem[NT / 64 - 1];
+  __syncthreads();
+  return off + v - x;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_sum(int x, int* smem) {
+  int total;
+  (void)block_excl_scan<NT>(x, smem, total);
+  return total;
+}
+
+// Find the histogram bucket holding the r-th (1-based) element; returns the bucket
+// and replaces r by the rank inside it.  hist has nb bins (nb <= 2 * NT).
+template <int NT>
+__device__ __forceinline__ int select_bucket(const uint32_t* hist, int nb, int& r, int* smem,
+                                             int* out) {
+  const int per = (nb + NT - 1) / NT;
+  const int b0 = threadIdx.x * per;
+  int c = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < nb) c += (int)hist[b0 + i];
+  int total;
+  const int excl = block_excl_scan<NT>(c, smem, total);
+  if (r > excl && r <= excl + c) {
+    int acc = excl;
+    for (int i = 0; i < per; ++i) {
+      const int h = (int)hist[b0 + i];
+      if (r <= acc + h) {
+        out[0] = b0 + i;
+        out[1] = r - acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+  const int bucket = min(max(out[0], 0), nb - 1);  // always found when r <= count
+  r = out[1];
+  __syncthreads();
+  return bucket;
+}
+
+// ---------------------------------------------------------------- select
+__global__ __launch_bounds__(kSelThreads) void evict_select(const float* lb_all,
+                                                            const int32_t* pos_all,
+                                                            const int32_t* len, int cap,
+                                                            int Hkv, const int32_t* tq, int M,
+                                                            UnitInfo* info, int32_t* n_out) {
+  __shared__ uint32_t hist[2048];
+  __shared__ unsigned long long bmin[1024];
+  __shared__ unsigned long long bmax[1024];
+  __shared__ int smem[kSelThreads / 64];
+  __shared__ int out[4];
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = min(len[u], cap);
+  if (tid == 0) {
+    out[0] = 0;
+    out[1] = 1;
+    out[2] = -1;
+  }
+  if (n <= M) {
+    if (tid == 0) {
+      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, {0, 0}};
+      info[u] = z;
+      if (n_out) n_out[u] = 0;
+    }
+    return;
+  }
+  const float* lb = lb_all ? lb_all + (size_t)u * cap : nullptr;
+  const int32_t* ps = pos_all + (size_t)u * cap;
+  const int tpos = tq[u / Hkv];
+  int r = n - M;  // 1-based rank of the last evicted element
+
+  // ---- radix select on the float32-rounded key: 11 + 11 + 10 bits
+  uint32_t prefix = 0;
+  int bucket = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int i = tid; i < nb; i += kSelThreads) {
+      hist[i] = 0;
+      if (pass == 2) {
+        bmin[i] = ~0ull;
+        bmax[i] = 0ull;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const double k = retention_key(lb, ps, i, tpos);
+      const uint32_t k32 = ord32(k);
+      const bool match = pass == 0 || (k32 >> (shift + (pass == 2 ? 10 : 11))) == prefix;
+      if (match) {
+        const uint32_t d = (k32 >> shift) & (uint32_t)(nb - 1);
+        atomicAdd(&hist[d], 1u);
+        if (pass == 2) {
+          const unsigned long long k64 = ord64(k);
+          atomicMin(&bmin[d], k64);
+          atomicMax(&bmax[d], k64);
+        }
+      }
+    }
+    __syncthreads();
+    bucket = select_bucket<kSelThreads>(hist, nb, r, smem, out);
+    prefix = (prefix << (pass == 2 ? 10 : 11)) | (uint32_t)bucket;
+  }
+  const uint32_t t32 = prefix;
+  unsigned long long K = bmin[bucket];
+  const unsigned long long kmax = bmax[bucket];
+  __syncthreads();
+
+  // ---- exact 64-bit key among the float32 ties (only when they differ)
+  if (K != kmax) {
+    unsigned long long pfx = 0;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kSelThreads) {
+        const double k = retention_key(lb, ps, i, tpos);
+        if (ord32(k) != t32) continue;
+        const unsigned long long k64 = ord64(k);
+        if (pass == 0 || (k64 >> (shift + 8)) == pfx)
+          atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      const int bk = select_bucket<kSelThreads>(hist, 256, r, smem, out);
+      pfx = (pfx << 8) | (unsigned long long)bk;
+    }
+    K = pfx;
+  }
+
+  // ---- slot of the r-th element (slot order) whose exact key is K
+  int sstar = -1;
+  int seen = 0;
+  for (int base = 0; base < n; base += kSelThreads) {
+    const int i = base + tid;
+    bool f = false;
+    if (i < n) {
+      const double k = retention_key(lb, ps, i, tpos);
+      f = ord64(k) == K;
+    }
+    int total;
+    const int excl = block_excl_scan<kSelThreads>(f ? 1 : 0, smem, total);
+    if (f && seen + excl + 1 == r) out[2] = i;
+    __syncthreads();
+    if (seen + total >= r) {
+      sstar = out[2];
+      break;
+    }
+    seen += total;
+  }
+  if (tid == 0) {
+    UnitInfo v = {K, sstar, MODE_EVICT, n, M, {0, 0}};
+    info[u] = v;
+  }
+}
+
+// ---------------------------------------------------------------- keep predicate
+struct KeepArgs {
+  const float* log_beta;
+  const int32_t* pos;
+  int32_t* len;
+  const int32_t* tq;
+  const int32_t* ranges;    // erase: [B][R][2]
+  const int32_t* n_ranges;  // erase: [B]
+  UnitInfo* info;
+  int32_t* counts;          // [U][C]
+  int32_t* keep_src;        // [U][Mk]
+  unsigned char* scratch;   // [U][Mk][srow]
+  int32_t* evicted_pos;     // [U][max_evict] or null
+  int32_t* n_out;           // [U] or null
+  const void* k;
+  const void* v;
+  int32_t cap, Hkv, R, C, Mk, max_evict, row_bytes, srow, move_rows;
+};
+
+__device__ __forceinline__ bool in_ranges(const int32_t* rg, int nr, int p) {
+  // last range with start <= p
+  int lo = 0, hi = nr - 1, found = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rg[2 * mid] <= p) {
+      found = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return found >= 0 && p < rg[2 * found + 1];
+}
+
+template <int MODE>
+__device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int n, bool* f) {
+  const int32_t* ps = a.pos + (size_t)u * a.cap;
+  if (MODE == MODE_EVICT) {
+    const UnitInfo inf = a.info[u];
+    const float* lb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
+    const int tpos = a.tq[u / a.Hkv];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e;
+      if (i < n) {
+        const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+        f[e] = k64 > inf.kstar || (k64 == inf.kstar && i > inf.sstar);
+      } else {
+        f[e] = false;
+      }
+    }
+  } else {
+    const int b = u / a.Hkv;
+    const int32_t* rg = a.ranges + (size_t)b * a.R * 2;
+    const int nr = a.n_ranges[b];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e;
+      f[e] = i < n && !in_ranges(rg, nr, ps[i]);
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kChunkThreads) void keep_count(KeepArgs a) {
+  __shared__ int smem[kChunkThreads / 64];
+  const int u = blockIdx.y, c = blockIdx.x;
+  if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
+  const int n = min(a.len[u], a.cap);
+  const int base = c * kChunk;
+  int cnt = 0;
+  if (base < n) {
+    bool f[kPerThread];
+    keep_flags<MODE>(a, u, base + threadIdx.x * kPerThread, n, f);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) cnt += f[e] ? 1 : 0;
+  }
+  const int tot = block_sum<kChunkThreads>(cnt, smem);
+  if (threadIdx.x == 0) a.counts[(size_t)u * a.C + c] = tot;
+}
+
+__device__ __forceinline__ void copy_row_to_scratch(const KeepArgs& a, int u, int src, int dst) {
+  unsigned char* s = a.scratch + ((size_t)u * a.Mk + dst) * a.srow;
+  const size_t off = ((size_t)u * a.cap + src) * a.row_bytes;
+  const u32x4* kp = (const u32x4*)((const unsigned char*)a.k + off);
+  const u32x4* vp = (const u32x4*)((const unsigned char*)a.v + off);
+  const int pieces = a.row_bytes / 16;
+  for (int i = 0; i < pieces; ++i) {
+    ((u32x4*)s)[i] = kp[i];
+    ((u32x4*)(s + a.row_bytes))[i] = vp[i];
+  }
+  int32_t* tail = (int32_t*)(s + 2 * a.row_bytes);
+  tail[0] = a.log_beta ? __float_as_int(a.log_beta[(size_t)u * a.cap + src]) : 0;
+  tail[1] = a.pos[(size_t)u * a.cap + src];
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
+  __shared__ int smem[kChunkThreads / 64];
+  const int u = blockIdx.y, c = blockIdx.x;
+  if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
+  const int n = min(a.len[u], a.cap);
+  // kept rows before this chunk, and in total
+  int before = 0, all = 0;
+  for (int j = threadIdx.x; j < a.C; j += kChunkThreads) {
+    const int x = a.counts[(size_t)u * a.C + j];
+    all += x;
+    if (j < c) before += x;
+  }
+  before = block_sum<kChunkThreads>(before, smem);
+  all = block_sum<kChunkThreads>(all, smem);
+  if (c == 0 && threadIdx.x == 0) {
+    a.info[u].kept = all;
+    if (MODE == MODE_ERASE) a.info[u].mode = MODE_ERASE;
+    if (a.n_out) a.n_out[u] = n - all;
+  }
+  const int base = c * kChunk;
+  if (base >= n) return;
+  const int i0 = base + threadIdx.x * kPerThread;
+  bool f[kPerThread];
+  keep_flags<MODE>(a, u, i0, n, f);
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) cnt += f[e] ? 1 : 0;
+  int total;
+  int dst = before + block_excl_scan<kChunkThreads>(cnt, smem, total);
+  const int32_t* ps = a.pos + (size_t)u * a.cap;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = i0 + e;
+    if (i >= n) break;
+    if (f[e]) {
+      if (dst < a.Mk) {  // always true when the threshold is consistent
+        a.keep_src[(size_t)u * a.Mk + dst] = i;
+        if (i != dst && i < all && i >= (dst / a.move_rows + 1) * a.move_rows)
+          copy_row_to_scratch(a, u, i, dst);
+      }
+      ++dst;
+    } else if (MODE == MODE_EVICT && a.evicted_pos) {
+      const int ev = i - dst;  // evicted slots before i
+      if (ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- move
+constexpr int kMoveThreads = 256;
+constexpr int kMovePieces = 8;  // 16-byte pieces per thread per group
+
+__global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, int check_mode) {
+  const int cpu = (a.Mk + a.move_rows - 1) / a.move_rows;
+  const int ppr = a.row_bytes / 16;  // pieces per row per tensor
+  const int tid = threadIdx.x;
+  for (int w = blockIdx.x; w < U * cpu; w += gridDim.x) {
+    const int u = w / cpu, ch = w - u * cpu;
+    const UnitInfo inf = a.info[u];
+    if (check_mode && inf.mode == MODE_NOOP) continue;
+    const int kept = min(inf.kept, a.Mk);
+    if (ch == 0 && tid == 0) a.len[u] = kept;
+    const int j0 = ch * a.move_rows;
+    if (j0 >= kept) continue;
+    const int rows = min(a.move_rows, kept - j0);
+    const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
+    const unsigned char* scr = a.scratch + (size_t)u * a.Mk * a.srow;
+    unsigned char* kb = (unsigned char*)a.k + (size_t)u * a.cap * a.row_bytes;
+    unsigned char* vb = (unsigned char*)a.v + (size_t)u * a.cap * a.row_bytes;
+    float* lbb = a.log_beta ? (float*)a.log_beta + (size_t)u * a.cap : nullptr;
+    int32_t* pb = (int32_t*)a.pos + (size_t)u * a.cap;
+
+    u32x4 buf[kMovePieces];
+    bool live[kMovePieces];
+    int32_t tail_lb = 0, tail_pos = 0, tail_dst = -1;
+    // ---- read phase
+#pragma unroll
+    for (int q = 0; q < kMovePieces; ++q) {
+      live[q] = false;
+      const int pidx = tid + q * kMoveThreads;
+      const int row = pidx / (2 * ppr);
+      if (row >= rows) continue;
+      const int part = pidx - row * 2 * ppr;  // [0, ppr): K, [ppr, 2ppr): V
+      const int j = j0 + row;
+      const int src = ks[j];
+      if (src == j) continue;
+      const bool isv = part >= ppr;
+      const int pc = isv ? part - ppr : part;
+      const bool staged = src < kept && src >= j0 + a.move_rows;
+      const unsigned char* from;
+      if (staged)
+        from = scr + (size_t)j * a.srow + (isv ? a.row_bytes : 0) + 16 * pc;
+      else
+        from = (isv ? vb : kb) + (size_t)src * a.row_bytes + 16 * pc;
+      buf[q] = *(const u32x4*)from;
+      live[q] = true;
+    }
+    if (tid < rows) {
+      const int j = j0 + tid;
+      const int src = ks[j];
+      if (src != j) {
+        const bool staged = src < kept && src >= j0 + a.move_rows;
+        if (staged) {
+          const int32_t* tl = (const int32_t*)(scr + (size_t)j * a.srow + 2 * a.row_bytes);
+          tail_lb = tl[0];
+          tail_pos = tl[1];
+        } else {
+          tail_lb = lbb ? __float_as_int(lbb[src]) : 0;
+          tail_pos = pb[src];
+        }
+        tail_dst = j;
+      }
+    }
+    __syncthreads();
+    // ---- write phase
+#pragma unroll
+    for (int q = 0; q < kMovePieces; ++q) {
+      if (!live[q]) continue;
+      const int pidx = tid + q * kMoveThreads;
+      const int row = pidx / (2 * ppr);
+      const int part = pidx - row * 2 * ppr;
+      const bool isv = part >= ppr;
+      const int pc = isv ? part - ppr : part;
+      *(u32x4*)((isv ? vb : kb) + (size_t)(j0 + row) * a.row_bytes + 16 * pc) = buf[q];
+    }
+    if (tail_dst >= 0) {
+      if (lbb) lbb[tail_dst] = __int_as_float(tail_lb);
+      pb[tail_dst] = tail_pos;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- host
+struct CompactLayout {
+  size_t info, counts, keep_src, scratch, total;
+  int C, Mk, srow, move_rows, row_bytes;
+};
+
+static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
+  CompactLayout L;
+  const size_t U = (size_t)c->B * c->Hkv;
+  L.row_bytes = c->D * (c->dtype == KVB_BF16 ? 2 : 4);
+  L.srow = 2 * L.row_bytes + 16;
+  L.C = (c->cap + kChunk - 1) / kChunk;
+  L.Mk = Mk < 1 ? 1 : Mk;
+  L.move_rows = kMoveThreads * kMovePieces / (2 * (L.row_bytes / 16));
+  if (L.move_rows > kMoveThreads) L.move_rows = kMoveThreads;  // one thread per row tail
+  L.info = kWsHeader;
+  L.counts = L.info + align_up(U * sizeof(UnitInfo), 256);
+  L.keep_src = L.counts + align_up(U * L.C * sizeof(int32_t), 256);
+  L.scratch = L.keep_src + align_up(U * L.Mk * sizeof(int32_t), 256);
+  L.total = L.scratch + align_up(U * L.Mk * (size_t)L.srow, 256);
+  return L;
+}
+
+static KeepArgs keep_args(const kvb_cache* c, const CompactLayout& L, void* ws) {
+  KeepArgs a;
+  memset(&a, 0, sizeof(a));
+  char* w = (char*)ws;
+  a.log_beta = c->log_beta;
+  a.pos = c->pos;
+  a.len = c->len;
+  a.info = (UnitInfo*)(w + L.info);
+  a.counts = (int32_t*)(w + L.counts);
+  a.keep_src = (int32_t*)(w + L.keep_src);
+  a.scratch = (unsigned char*)(w + L.scratch);
+  a.k = c->k;
+  a.v = c->v;
+  a.cap = c->cap;
+  a.Hkv = c->Hkv;
+  a.C = L.C;
+  a.Mk = L.Mk;
+  a.row_bytes = L.row_bytes;
+  a.srow = L.srow;
+  a.move_rows = L.move_rows;
+  return a;
+}
+
+static int32_t launch_compaction(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s) {
+  const int U = c->B * c->Hkv;
+  dim3 grid(a.C, U);
+  if (mode == MODE_EVICT) {
+    hipLaunchKernelGGL(keep_count<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL(keep_emit<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(keep_count<MODE_ERASE>, grid, dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL(keep_emit<MODE_ERASE>, grid, dim3(kChunkThreads), 0, s, a);
+  }
+  const long long items = (long long)U * ((a.Mk + a.move_rows - 1) / a.move_rows);
+  const int blocks = (int)(items < 4096 ? items : 4096);
+  hipLaunchKernelGGL(compact_move, dim3(blocks), dim3(kMoveThreads), 0, s, a, U,
+                     mode == MODE_EVICT ? 1 : 0);
+  return launch_status();
+}
+
+}  // namespace kvb
+
+using namespace kvb;
+
+extern "C" size_t kv_evict_workspace(const kvb_cache* cache, int32_t M) {
+  if (!cache || M < 0 || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1 || cache->D < 8)
+    return 0;
+  return compact_layout(cache, M < cache->cap ? M : cache->cap).total;
+}
+
+extern "C" size_t kv_erase_workspace(const kvb_cache* cache) {
+  if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1 || cache->D < 8) return 0;
+  return compact_layout(cache, cache->cap).total;
+}
+
+extern "C" int32_t kv_evict_to_budget(const kvb_cache* cache, const int32_t* t, int32_t M,
+                                      int32_t* evicted_pos, int32_t max_evict,
+                                      int32_t* n_evicted, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!t || M < 0 || max_evict < 0 || (evicted_pos && max_evict == 0)) return KVB_EINVAL;
+  const CompactLayout L = compact_layout(cache, M < cache->cap ? M : cache->cap);
+  if (!ws || ws_bytes < L.total) return KVB_EWORKSPACE;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  KeepArgs a = keep_args(cache, L, ws);
+  a.tq = t;
+  a.evicted_pos = evicted_pos;
+  a.max_evict = max_evict;
+  a.n_out = n_evicted;
+  hipLaunchKernelGGL(evict_select, dim3(cache->B * cache->Hkv), dim3(kSelThreads), 0, s,
+                     cache->log_beta, cache->pos, cache->len, cache->cap, cache->Hkv, t, M,
+                     a.info, n_evicted);
+  return launch_compaction(cache, a, MODE_EVICT, s);
+}
+
+extern "C" int32_t kv_erase_ranges(const kvb_cache* cache, const int32_t* ranges,
+                                   const int32_t* n_ranges, int32_t R, int32_t* n_erased,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (R < 0 || !n_ranges || (R > 0 && !ranges)) return KVB_EINVAL;
+  const CompactLayout L = compact_layout(cache, cache->cap);
+  if (!ws || ws_bytes < L.total) return KVB_EWORKSPACE;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  KeepArgs a = keep_args(cache, L, ws);
+  a.ranges = ranges;
+  a.n_ranges = n_ranges;
+  a.R = R;
+  a.n_out = n_erased;
+  return launch_compaction(cache, a, MODE_ERASE, s);
+}

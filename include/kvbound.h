@@ -1,0 +1,194 @@
+/*
+ * kvbound -- decode-step attention over a memory-bounded KV cache, for MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a DEVICE pointer unless the comment says
+ * "host".  Every call is asynchronous on `stream` (a hipStream_t passed as
+ * void*; NULL means the default stream), performs no host synchronisation, and
+ * allocates nothing: scratch memory is the caller's workspace `ws` of at least
+ * the size the matching *_workspace() function returns.  The library keeps no
+ * state between calls; calls on different streams must not share a workspace
+ * or a cache.
+ *
+ * Errors: arguments are validated on the host before anything is launched; a
+ * failed check returns a negative kvb_status and leaves all memory untouched.
+ * Conditions that live in device memory (e.g. `len`) cannot be checked on the
+ * host without a synchronisation; their handling is stated per call.
+ *
+ * Sources of the operations (web pages, cited by title and section):
+ *  [TRIM]  "Cache What Lasts: Token Retention for Memory-Bounded KV Cache in LLMs",
+ *          section 2.1 (retention-gated attention: logit q.k + (t-i) log beta_i)
+ *          and section 2.2 (inference: over budget M, evict the lowest beta_i^(t-i)).
+ *  [ASM]   "Context Memorization for Efficient Long Context Generation",
+ *          background (online-softmax identity), method steps 1-4 (attention state
+ *          (a, Z), merge operator, cosine-argmax retrieval, merge with the query's
+ *          own state), technical novelty (GQA: centroids per KV head).
+ *  [MEM]   "MEMENTO: Teaching LLMs to Manage Their Own Context", blocks and
+ *          compression (a finished thinking block's KV entries are removed once its
+ *          memento exists) and system engineering (entries physically removed
+ *          within one generate call).
+ */
+#ifndef KVBOUND_H
+#define KVBOUND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVB_OK = 0,
+  KVB_EINVAL = -1,       /* a NULL pointer, a size out of range, Hq % Hkv != 0 ... */
+  KVB_EUNSUPPORTED = -2, /* dtype / head_dim / group size combination not built */
+  KVB_ECAPACITY = -3,    /* cache capacity too small for the request            */
+  KVB_EWORKSPACE = -4,   /* ws is NULL or ws_bytes below the required size       */
+  KVB_EDEVICE = -5,      /* no usable HIP device, or the device is not gfx950    */
+  KVB_ELAUNCH = -6       /* a kernel launch failed (hipGetLastError)            */
+} kvb_status;
+
+typedef enum { KVB_F32 = 0, KVB_BF16 = 1 } kvb_dtype;
+
+/*
+ * One layer's KV cache; a plain descriptor, read during the call, not retained.
+ *   k, v      [B][Hkv][cap][D] elements of `dtype`, dense row-major (one row = one
+ *             token of one KV head, D contiguous values).
+ *   log_beta  [B][Hkv][cap] float32 natural log of the retention score beta_i of
+ *             each slot ([TRIM] 2.1), values in [-inf, 0]; NULL means beta == 1
+ *             (no retention bias; eviction then keeps the newest tokens).
+ *   pos       [B][Hkv][cap] int32 absolute token position of each slot.  Within
+ *             the live slots of a head positions must be strictly increasing.
+ *   len       [B][Hkv] int32 live slots per head, device resident; slots at and
+ *             beyond len are unspecified.
+ * The caller owns all of it.  Requires 1 <= B, Hkv; 1 <= cap < 2^30;
+ * D in {64, 128} for KVB_BF16 (any 1 <= D <= 256 for KVB_F32); D % 8 == 0.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  float* log_beta;
+  int32_t* pos;
+  int32_t* len;
+  int32_t B, Hkv, cap, D;
+  int32_t dtype; /* kvb_dtype */
+} kvb_cache;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* kvb_strerror(int32_t status);
+
+/* Number of KV splits kv_attn_decode uses for num_splits == 0 (host only). */
+int32_t kv_attn_decode_splits(const kvb_cache* cache, int32_t Hq);
+
+/* Workspace sizes in bytes (host only; no device access). */
+size_t kv_attn_decode_workspace(const kvb_cache* cache, int32_t Hq, int32_t num_splits);
+size_t kv_evict_workspace(const kvb_cache* cache, int32_t M);
+size_t kv_erase_workspace(const kvb_cache* cache);
+size_t asm_lookup_merge_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t K);
+
+/*
+ * Decode-step grouped-query attention with the retention bias, split over the KV
+ * axis ([TRIM] 2.1; [ASM] background and method steps 1-2).
+ *
+ * Optional append first: if k_new != NULL, each head (b, g) writes k_new[b][g],
+ * v_new[b][g] (and log_beta_new[b][g] when the cache has log_beta) at slot
+ * len[b][g] with pos = t[b], then len[b][g] += 1.  A head whose len already equals
+ * cap is not appended to (its len stays; the caller must keep cap > len).
+ *
+ * Then for every query head h of sequence b (KV head g = h / (Hq/Hkv)) over the
+ * live slots i < len[b][g]:
+ *   s_i   = scale * (q[b][h] . k_i) + (t[b] - pos_i) * log_beta_i
+ *           (the bias term is 0 when t[b] == pos_i or log_beta is NULL)
+ *   out   = sum_i e^{s_i} v_i / sum_i e^{s_i},   lse = log sum_i e^{s_i}.
+ * The live slots are cut into num_splits contiguous blocks; each block yields a
+ * partial state (a, m, Z) (a normalised over the block, m its max logit,
+ * Z = sum e^{s-m}), and the states are combined with the merge operator
+ * ((Z_A a_A + Z_B a_B)/(Z_A + Z_B), Z_A + Z_B) in split order (deterministic).
+ * An empty head (len == 0, or every weight 0) gives out = 0, lse = -inf.
+ *
+ *   q          [B][Hq][D] in the cache dtype
+ *   Hq         query heads; Hq % Hkv == 0
+ *   t          [B] int32 position of each sequence's decode token
+ *   scale      dot-product scale; <= 0 selects 1/sqrt(D)
+ *   k_new, v_new [B][Hkv][D] cache dtype, or both NULL (no append)
+ *   log_beta_new [B][Hkv] float32; required with k_new iff cache->log_beta != NULL
+ *   num_splits 0 = kv_attn_decode_splits(); else 1..4096
+ *   out        [B][Hq][D] float32;  lse [B][Hq] float32
+ *   ws         workspace of kv_attn_decode_workspace(cache, Hq, num_splits) bytes;
+ *              after the call it holds the partial states
+ *              [B][Hq][num_splits][D + 2] float32 (a[D], m, Z) at byte offset 256.
+ */
+int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq, const int32_t* t,
+                       float scale, const void* k_new, const void* v_new,
+                       const float* log_beta_new, int32_t num_splits, float* out, float* lse,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Evict every head over budget to exactly M live slots, then compact in place
+ * ([TRIM] 2.2).
+ *
+ * For a head with n = len > M the key of slot i is
+ *   kappa_i = (t[b] - pos_i) * log_beta_i   (exact in double; +0 when t[b] == pos_i
+ *                                            or log_beta is NULL; -0 equals +0),
+ * the logarithm of the retention score beta_i^(t-i).  The n - M slots that come
+ * first in (kappa, pos) ascending order are evicted (ties: lower position first).
+ * The surviving rows (k, v, log_beta, pos) move, in their slot order, to slots
+ * [0, M) and len becomes M.  Heads with len <= M are untouched.
+ *
+ *   t          [B] int32 current token position of each sequence
+ *   M          budget, >= 0
+ *   evicted_pos [B][Hkv][max_evict] int32 or NULL: the evicted positions of each
+ *              head in ascending order; only the first max_evict are written.
+ *   n_evicted  [B][Hkv] int32 or NULL: number evicted per head.
+ *   ws         workspace of kv_evict_workspace(cache, M) bytes.
+ * Preconditions (not checked): positions strictly increasing over live slots,
+ * pos <= t, no NaN in log_beta.
+ */
+int32_t kv_evict_to_budget(const kvb_cache* cache, const int32_t* t, int32_t M,
+                           int32_t* evicted_pos, int32_t max_evict, int32_t* n_evicted,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Erase position ranges from every KV head of a sequence and compact in place
+ * ([MEM] blocks and compression; system engineering).
+ *
+ *   ranges     [B][R][2] int32 half-open position ranges [s, e) per sequence,
+ *              sorted by s, pairwise disjoint, s < e.
+ *   n_ranges   [B] int32 ranges used per sequence (0..R).
+ *   R          row stride of `ranges` (>= 0).
+ *   n_erased   [B][Hkv] int32 or NULL: slots removed per head.
+ * A slot is kept iff its position lies in none of its sequence's ranges; kept
+ * rows keep their slot order and fill slots [0, kept); len becomes kept.
+ *   ws         workspace of kv_erase_workspace(cache) bytes.
+ */
+int32_t kv_erase_ranges(const kvb_cache* cache, const int32_t* ranges, const int32_t* n_ranges,
+                        int32_t R, int32_t* n_erased, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * Attention-state memory lookup and merge ([ASM] method steps 3 and 4; GQA
+ * extension).  For every query head h of sequence b (KV head g = h / (Hq/Hkv)):
+ *   idx = argmax_k cos(q[b][h], centroids[g][k])   (ties: lowest k; the stored
+ *         centroid values are used as they are; a zero query gives idx 0)
+ *   (out, out_lse) = merge((self_out, self_lse), (abar[g][idx], log_zbar[g][idx]))
+ * where merge weights each output by its normaliser: with Z = e^self_lse and
+ * Zbar = e^log_zbar, out = (Z self_out + Zbar abar) / (Z + Zbar),
+ * out_lse = log(Z + Zbar).  self_lse = -inf means no own tokens.
+ *
+ *   q          [B][Hq][D] bf16;  centroids, abar [Hkv][K][D] bf16;  log_zbar [Hkv][K] f32
+ *   self_out   [B][Hq][D] f32;   self_lse [B][Hq] f32 (e.g. kv_attn_decode's out, lse)
+ *   out        [B][Hq][D] f32;   out_lse [B][Hq] f32 (may alias self_out / self_lse)
+ *   idx        [B][Hq] int32 or NULL
+ *   D == 128 or 64; 1 <= K < 2^24; (Hq / Hkv) * B <= 65536.
+ *   ws         workspace of asm_lookup_merge_workspace(B, Hq, Hkv, D, K) bytes.
+ */
+int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         const void* centroids, const void* abar, const float* log_zbar,
+                         int32_t K, const float* self_out, const float* self_lse, float* out,
+                         float* out_lse, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVBOUND_H */

@@ -1,0 +1,110 @@
+"""The C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bounded_decode_attention_amd as kvb
+from bounded_decode_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvbound.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(kvb.library_path()),
+                               reason="libkvbound.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges", "asm_lookup_merge"):
+        assert n in names
+
+
+@needs_lib
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(kvb.library_path())
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+@needs_lib
+def test_strerror():
+    assert kvb.strerror(0) == "ok"
+    for s in range(-6, 0):
+        assert kvb.strerror(s) not in ("", "unknown status")
+    assert kvb.strerror(-99) == "unknown status"
+
+
+def _desc(**kw):
+    d = dict(k=8, v=8, log_beta=None, pos=16, len=24, B=2, Hkv=2, cap=100, D=128, dtype=1)
+    d.update(kw)
+    return _lib._Cache(d["k"], d["v"], d["log_beta"], d["pos"], d["len"], d["B"], d["Hkv"],
+                       d["cap"], d["D"], d["dtype"])
+
+
+@needs_lib
+def test_workspace_sizes_host_only():
+    L = kvb.library()
+    c = _desc()
+    P = L.kv_attn_decode_splits(ctypes.byref(c), 8)
+    assert 1 <= P <= 4  # 100-slot cache: 4 tiles
+    assert L.kv_attn_decode_workspace(ctypes.byref(c), 8, 0) >= 256 + 2 * 8 * P * 130 * 4
+    assert L.kv_evict_workspace(ctypes.byref(c), 10) > 256
+    assert L.kv_erase_workspace(ctypes.byref(c)) >= L.kv_evict_workspace(ctypes.byref(c), 10)
+    assert L.asm_lookup_merge_workspace(32, 32, 8, 128, 4096) > 256
+    assert L.kv_evict_workspace(ctypes.byref(c), -1) == 0
+    assert L.asm_lookup_merge_workspace(1, 3, 2, 128, 16) == 0
+
+
+@needs_lib
+def test_invalid_arguments_rejected_before_launch():
+    """Fake (never dereferenced) pointers: validation fails first, nothing runs."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    ws = P(4096)
+    good = _desc()
+    # kv_attn_decode
+    args = [P(64), 8, P(72), 0.0, None, None, None, 0, P(80), P(88), ws, 1 << 30, None]
+    assert L.kv_attn_decode(None, *args) == -1
+    assert L.kv_attn_decode(ctypes.byref(good), P(64), 7, *args[2:]) == -1      # Hq % Hkv
+    assert L.kv_attn_decode(ctypes.byref(_desc(D=96)), *args) == -2            # bf16 D=96
+    assert L.kv_attn_decode(ctypes.byref(_desc(dtype=5)), *args) == -2
+    assert L.kv_attn_decode(ctypes.byref(_desc(cap=0)), *args) == -1
+    assert L.kv_attn_decode(ctypes.byref(_desc(pos=None)), *args) == -1
+    a2 = list(args)
+    a2[4] = P(8)                                                              # k_new w/o v_new
+    assert L.kv_attn_decode(ctypes.byref(good), *a2) == -1
+    a3 = list(args)
+    a3[7] = 5000                                                              # num_splits
+    assert L.kv_attn_decode(ctypes.byref(good), *a3) == -1
+    a4 = list(args)
+    a4[11] = 16                                                               # ws too small
+    assert L.kv_attn_decode(ctypes.byref(good), *a4) == -4
+    # kv_evict_to_budget
+    assert L.kv_evict_to_budget(ctypes.byref(good), P(8), -1, None, 0, None, ws, 1 << 30, None) == -1
+    assert L.kv_evict_to_budget(ctypes.byref(good), None, 5, None, 0, None, ws, 1 << 30, None) == -1
+    assert L.kv_evict_to_budget(ctypes.byref(good), P(8), 5, None, 0, None, ws, 8, None) == -4
+    # kv_erase_ranges
+    assert L.kv_erase_ranges(ctypes.byref(good), None, P(8), 3, None, ws, 1 << 30, None) == -1
+    assert L.kv_erase_ranges(ctypes.byref(good), P(8), None, 3, None, ws, 1 << 30, None) == -1
+    # asm_lookup_merge
+    base = [P(8), 2, 8, 2, 128, P(8), P(8), P(8), 64, P(8), P(8), P(8), P(8), None, ws, 1 << 30, None]
+    bad = list(base)
+    bad[4] = 96
+    assert L.asm_lookup_merge(*bad) == -2
+    bad = list(base)
+    bad[2] = 7
+    assert L.asm_lookup_merge(*bad) == -1
+    bad = list(base)
+    bad[0] = None
+    assert L.asm_lookup_merge(*bad) == -1

@@ -1,0 +1,185 @@
+"""kv_attn_decode on the GPU against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import bounded_decode_attention_amd as kvb
+import oracle
+import synth
+from gpu_util import (check_attention, dev_cache, host_dict, oracle_attention, say, to_dev,
+                      to_host, values)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_cache(seed, B, Hkv, n, cap, D, dtype, retention=True, lens=None):
+    w = synth.Workload("t", batch=B, hq=Hkv, hkv=Hkv, head_dim=D, dtype=dtype, ctx=n,
+                       budget=0, layers=1, seed=seed, retention=retention)
+    d = synth.host_cache(w, n=n, cap=cap)
+    if lens is not None:
+        d["len"] = np.asarray(lens, np.int32).reshape(B, Hkv)
+    return d
+
+
+def _queries(seed, B, Hq, D, dtype):
+    w = synth.Workload("t", batch=B, hq=Hq, hkv=1, head_dim=D, dtype=dtype, ctx=1, budget=0,
+                       layers=1, seed=seed)
+    return synth.host_queries(w, steps=1)[0]
+
+
+CASES = [
+    # B, Hq, Hkv, D, n, dtype, splits
+    (1, 4, 1, 128, 1, "bf16", 0),
+    (2, 8, 2, 128, 31, "bf16", 0),
+    (2, 8, 2, 128, 33, "bf16", 1),
+    (1, 32, 8, 128, 1000, "bf16", 0),
+    (2, 16, 2, 128, 4097, "bf16", 7),
+    (1, 64, 8, 128, 2050, "bf16", 3),     # G = 8
+    (2, 4, 2, 128, 300, "bf16", 0),       # G = 2
+    (2, 2, 2, 128, 257, "bf16", 0),       # G = 1
+    (1, 8, 2, 64, 700, "bf16", 0),        # D = 64
+    (1, 16, 2, 64, 129, "bf16", 5),       # D = 64, G = 8
+    (1, 6, 2, 128, 200, "bf16", 0),       # G = 3: generic kernel
+    (1, 8, 2, 64, 513, "f32", 0),         # float32 generic kernel
+    (1, 8, 2, 96, 77, "f32", 3),          # float32, D = 96
+]
+
+
+@pytest.mark.parametrize("retention", [True, False])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_D{}_n{}_{}_P{}".format(*c))
+def test_attention_vs_oracle(case, retention):
+    B, Hq, Hkv, D, n, dtype, P = case
+    say("case", case, retention)
+    d = _rand_cache(100 + n, B, Hkv, n, n + 5, D, dtype, retention)
+    q = _queries(200 + n, B, Hq, D, dtype)
+    t = np.full(B, n + 3, np.int32)       # decode token 3 positions past the last
+    c = dev_cache(d)
+    out, lse = kvb.kv_attn_decode(c, to_dev(q), to_dev(t), num_splits=P)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_attention(d, q, t)
+    check_attention(to_host(out), to_host(lse), ref_out, ref_lse, str(case))
+
+
+def test_attention_append_then_attend():
+    """k_new/v_new/log_beta_new land at slot len with pos = t, then are attended."""
+    B, Hq, Hkv, D, n = 2, 8, 2, 128, 100
+    d = _rand_cache(7, B, Hkv, n, n + 2, D, "bf16")
+    q = _queries(8, B, Hq, D, "bf16")
+    kn = synth.bf16_bits(np.random.default_rng(1).standard_normal((B, Hkv, D)))
+    vn = synth.bf16_bits(np.random.default_rng(2).standard_normal((B, Hkv, D)))
+    lbn = np.full((B, Hkv), -0.5, np.float32)
+    t = np.array([n, n + 10], np.int32)
+    c = dev_cache(d)
+    out, lse = kvb.kv_attn_decode(c, to_dev(q), to_dev(t), k_new=to_dev(kn), v_new=to_dev(vn),
+                                  log_beta_new=to_dev(lbn))
+    torch.cuda.synchronize()
+    ref = oracle.Cache.from_arrays(d)
+    oracle.append_tokens(ref, kn, vn, lbn, t)
+    got = host_dict(c)
+    assert got["len"].tolist() == [[n + 1] * Hkv] * B
+    for b in range(B):
+        for g in range(Hkv):
+            assert np.array_equal(got["k"][b, g, n], kn[b, g])
+            assert np.array_equal(got["v"][b, g, n], vn[b, g])
+            assert got["pos"][b, g, n] == t[b] and got["log_beta"][b, g, n] == lbn[b, g]
+    rd = {"k": ref.k, "v": ref.v, "log_beta": ref.log_beta, "pos": ref.pos, "len": ref.length}
+    ref_out, ref_lse = oracle_attention(rd, q, t)
+    check_attention(to_host(out), to_host(lse), ref_out, ref_lse, "append")
+
+
+def test_attention_edges():
+    """Empty heads, a single live token, all-but-newest weights zero (log beta = -inf),
+    a decode token at the same position as a live slot, more splits than tiles."""
+    B, Hq, Hkv, D, n = 2, 8, 4, 128, 70
+    d = _rand_cache(9, B, Hkv, n, n, D, "bf16", lens=[[0, 1, 70, 33], [70, 0, 2, 64]])
+    d["log_beta"][0, 2, :] = -np.inf                  # only distance-0 tokens keep weight
+    d["log_beta"][1, 3, :] = -np.inf                  # every weight zero -> empty
+    q = _queries(10, B, Hq, D, "bf16")
+    t = np.array([69, 75], np.int32)                  # b=0: t equals the last live position
+    c = dev_cache(d)
+    for P in (1, 2, 64, 300):
+        out, lse = kvb.kv_attn_decode(c, to_dev(q), to_dev(t), num_splits=P)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle_attention(d, q, t)
+        check_attention(to_host(out), to_host(lse), ref_out, ref_lse, f"edges P={P}")
+
+
+def test_attention_deterministic():
+    d = _rand_cache(11, 2, 2, 5000, 5000, 128, "bf16")
+    q = _queries(12, 2, 8, 128, "bf16")
+    t = np.full(2, 5000, np.int32)
+    c = dev_cache(d)
+    o1, l1 = kvb.kv_attn_decode(c, to_dev(q), to_dev(t))
+    o2, l2 = kvb.kv_attn_decode(c, to_dev(q), to_dev(t))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_attention_scale_and_errors():
+    d = _rand_cache(13, 1, 2, 64, 64, 128, "bf16")
+    q = _queries(14, 1, 8, 128, "bf16")
+    t = np.full(1, 64, np.int32)
+    c = dev_cache(d)
+    out, lse = kvb.kv_attn_decode(c, to_dev(q), to_dev(t), scale=0.3)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_attention(d, q, t, scale=0.3)
+    check_attention(to_host(out), to_host(lse), ref_out, ref_lse, "scale")
+    with pytest.raises(kvb.KVBError):   # Hq not a multiple of Hkv
+        kvb.kv_attn_decode(c, to_dev(q[:, :7].copy()), to_dev(t))
+    with pytest.raises(kvb.KVBError):   # workspace too small
+        kvb.kv_attn_decode(c, to_dev(q), to_dev(t),
+                           ws=torch.empty(300, dtype=torch.uint8, device="cuda"))
+
+
+def _sampled_full_size(w, units, splits_list, layer=0):
+    say("full-size", w.name, "units", units)
+    dc = synth.device_cache(w, layer)
+    q, kn, vn, lbn = synth.device_queries(w, layer)
+    t = torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda")
+    # read back the exact input bits of the sampled heads before any kernel runs
+    G = w.group
+    sub = {}
+    for (b, g) in units:
+        sub[(b, g)] = {k: to_host(dc[k][b:b + 1, g:g + 1]) if dc[k] is not None else None
+                       for k in ("k", "v", "log_beta", "pos")}
+    qh = to_host(q)
+    knh, vnh = to_host(kn), to_host(vn)
+    lbh = to_host(lbn) if lbn is not None else None
+    c = kvb.KVCache.from_dict(dc)
+    for i, P in enumerate(splits_list):
+        if i == 0:
+            out, lse = kvb.kv_attn_decode(c, q, t, k_new=kn, v_new=vn, log_beta_new=lbn,
+                                          num_splits=P)
+        else:
+            out, lse = kvb.kv_attn_decode(c, q, t, num_splits=P)
+        torch.cuda.synchronize()
+        oh, lh = to_host(out), to_host(lse)
+        for (b, g), s in sub.items():
+            # append the decode token to the host copy, as the call did
+            n = w.ctx
+            dd = {"k": s["k"].copy(), "v": s["v"].copy(),
+                  "log_beta": None if s["log_beta"] is None else s["log_beta"].copy(),
+                  "pos": s["pos"].copy(), "len": np.array([[n + 1]], np.int32)}
+            dd["k"][0, 0, n] = knh[b, g]
+            dd["v"][0, 0, n] = vnh[b, g]
+            dd["pos"][0, 0, n] = w.ctx
+            if dd["log_beta"] is not None:
+                dd["log_beta"][0, 0, n] = lbh[b, g]
+            qs = qh[b:b + 1, g * G:(g + 1) * G]
+            ref_out, ref_lse = oracle.decode_attention(
+                values(dd["k"]), values(dd["v"]), dd["log_beta"], dd["pos"], dd["len"],
+                values(qs), np.array([w.ctx]))
+            check_attention(oh[b:b + 1, g * G:(g + 1) * G], lh[b:b + 1, g * G:(g + 1) * G],
+                            ref_out, ref_lse, f"{w.name} ({b},{g}) P={P}")
+    del dc, c
+    torch.cuda.empty_cache()
+
+
+def test_attention_full_size_qwen3_8b_32k():
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    _sampled_full_size(w, [(0, 0), (7, 3), (15, 7)], [0, 128])
+
+
+def test_attention_full_size_qwen3_32b_128k():
+    w = synth.WORKLOADS["qwen3_32b_128k"]
+    _sampled_full_size(w, [(0, 0), (5, 6)], [64, 128, 256])

@@ -1,0 +1,224 @@
+"""kv_evict_to_budget / kv_erase_ranges on the GPU: bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import bounded_decode_attention_amd as kvb
+import oracle
+import synth
+from gpu_util import (check_attention, check_compacted, check_layout, dev_cache, host_dict, say,
+                      snapshot_rows, to_dev, to_host, values)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache(seed, B, Hkv, n, cap, D, dtype="bf16", retention=True, lens=None):
+    w = synth.Workload("t", batch=B, hq=Hkv, hkv=Hkv, head_dim=D, dtype=dtype, ctx=n,
+                       budget=0, layers=1, seed=seed, retention=retention)
+    d = synth.host_cache(w, n=n, cap=cap)
+    if lens is not None:
+        d["len"] = np.asarray(lens, np.int32).reshape(B, Hkv)
+    return d
+
+
+def _evict_and_check(d, t, M, what, max_evict=None):
+    B, H = d["len"].shape
+    n_max = int(d["len"].max())
+    c = dev_cache(d)
+    me = max_evict if max_evict is not None else max(1, n_max)
+    ev = torch.full((B, H, me), -7, dtype=torch.int32, device="cuda")
+    n_ev = kvb.kv_evict_to_budget(c, to_dev(np.asarray(t, np.int32)), M, evicted_pos=ev)
+    torch.cuda.synchronize()
+    ref, ref_ev, ref_n = oracle.evict_to_budget(oracle.Cache.from_arrays(d), t, M)
+    check_layout(host_dict(c), ref, what)
+    assert np.array_equal(to_host(n_ev), ref_n), f"{what} n_evicted"
+    evh = to_host(ev)
+    for b in range(B):
+        for g in range(H):
+            k = min(int(ref_n[b, g]), me)
+            assert np.array_equal(evh[b, g, :k], ref_ev[b][g][:k]), f"{what} ({b},{g}) evicted_pos"
+    return c, ref
+
+
+@pytest.mark.parametrize("n,M", [(1, 0), (1, 1), (5, 3), (33, 32), (100, 0), (100, 99),
+                                 (513, 256), (4097, 4096), (5000, 64), (10000, 9000),
+                                 (20000, 17)])
+@pytest.mark.parametrize("retention", [True, False])
+def test_evict_vs_oracle(n, M, retention):
+    say("evict", n, M, retention)
+    d = _cache(n * 7 + M, 2, 3, n, n + 3, 128, retention=retention)
+    t = np.array([n, n + 5], np.int32)
+    _evict_and_check(d, t, M, f"n={n} M={M} r={retention}")
+
+
+def test_evict_ties_and_special_keys():
+    """Equal keys (ties by position), log beta = -inf, log beta = 0 and -0.0,
+    a live slot at the decode position, n <= M heads left untouched."""
+    B, H, n = 1, 6, 300
+    d = _cache(3, B, H, n, n, 128, lens=[[300, 300, 300, 300, 300, 100]])
+    lb = d["log_beta"]
+    lb[0, 0, :] = np.float32(-0.25)               # one shared beta: sliding window
+    lb[0, 1, ::3] = -np.inf                        # weight-zero tokens go first
+    lb[0, 2, :] = np.where(np.arange(n) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+    lb[0, 3, 50:60] = np.float32(-1e-30)           # tiny keys
+    lb[0, 4, :] = np.float32(-0.001)
+    lb[0, 4, 100:200] = lb[0, 4, 99]               # long run of equal log beta
+    t = np.array([299], np.int32)                  # pos 299 sits at distance 0
+    for M in (0, 1, 50, 150, 299):
+        _evict_and_check(d, t, M, f"ties M={M}")
+
+
+def test_evict_float32_tiny_workload_steps():
+    """The tiny workload: 16 decode steps of append + attention + eviction."""
+    w = synth.WORKLOADS["tiny"]
+    d = synth.host_cache(w)
+    qs = synth.host_queries(w)
+    kn, vn, lbn = synth.host_new_tokens(w)
+    c = dev_cache(d)
+    ref = oracle.Cache.from_arrays(d)
+    for s in range(w.steps):
+        say("tiny step", s)
+        t = np.full(w.batch, w.ctx + s, np.int32)
+        out, lse = kvb.kv_attn_decode(c, to_dev(qs[s]), to_dev(t), k_new=to_dev(kn[s]),
+                                      v_new=to_dev(vn[s]), log_beta_new=to_dev(lbn[s]))
+        n_ev = kvb.kv_evict_to_budget(c, to_dev(t), w.budget)
+        torch.cuda.synchronize()
+        oracle.append_tokens(ref, kn[s], vn[s], lbn[s], t)
+        ref_out, ref_lse = oracle.decode_attention(ref.values("k"), ref.values("v"), ref.log_beta,
+                                                   ref.pos, ref.length, qs[s].astype(np.float64), t)
+        check_attention(to_host(out), to_host(lse), ref_out, ref_lse, f"tiny step {s}")
+        ref, _, ref_n = oracle.evict_to_budget(ref, t, w.budget)
+        check_layout(host_dict(c), ref, f"tiny step {s}")
+        assert np.array_equal(to_host(n_ev), ref_n)
+
+
+def test_evict_steady_state_shift():
+    """Budget M with one token over: each step evicts one and shifts the rest down
+    (the compaction's cross-workgroup staging path)."""
+    B, H, D, M = 2, 2, 128, 1000
+    d = _cache(21, B, H, M, M + 40, D)
+    c = dev_cache(d)
+    ref = oracle.Cache.from_arrays(d)
+    rng = np.random.default_rng(5)
+    for s in range(6):
+        t = np.full(B, M + s, np.int32)
+        kn = synth.bf16_bits(rng.standard_normal((B, H, D)))
+        vn = synth.bf16_bits(rng.standard_normal((B, H, D)))
+        lbn = np.log(rng.uniform(0.5, 1.0, (B, H))).astype(np.float32)
+        qn = synth.bf16_bits(rng.standard_normal((B, 4 * H, D)))
+        kvb.kv_attn_decode(c, to_dev(qn), to_dev(t), k_new=to_dev(kn), v_new=to_dev(vn),
+                           log_beta_new=to_dev(lbn))
+        kvb.kv_evict_to_budget(c, to_dev(t), M)
+        torch.cuda.synchronize()
+        oracle.append_tokens(ref, kn, vn, lbn, t)
+        ref, _, _ = oracle.evict_to_budget(ref, t, M)
+        check_layout(host_dict(c), ref, f"steady step {s}")
+
+
+def test_evict_float32_and_d64():
+    for dtype, D in (("f32", 64), ("bf16", 64), ("f32", 128)):
+        d = _cache(31, 1, 2, 3000, 3001, D, dtype=dtype)
+        _evict_and_check(d, np.array([3000], np.int32), 700, f"{dtype} D={D}")
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_32k", "qwen3_32b_128k"])
+def test_evict_full_size(name):
+    """One full layer: append the decode token, evict every head to M.  The oracle's
+    plan (from the downloaded retention arrays and positions) names the kept slots;
+    every head's compacted rows must be exactly those rows, in order."""
+    w = synth.WORKLOADS[name]
+    say("evict full size", name)
+    dc = synth.device_cache(w, layer=0)
+    q, kn, vn, lbn = synth.device_queries(w, 0)
+    t = torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda")
+    c = kvb.KVCache.from_dict(dc)
+    kvb.kv_attn_decode(c, q, t, k_new=kn, v_new=vn, log_beta_new=lbn)
+    torch.cuda.synchronize()
+    n = w.ctx + 1
+    lbh = to_host(c.log_beta[:, :, :n])
+    ph = to_host(c.pos[:, :, :n])
+    keep, ref_ev = {}, {}
+    for b in range(w.batch):
+        for g in range(w.hkv):
+            k, e = oracle.evict_plan(lbh[b, g], ph[b, g], n, w.ctx, w.budget)
+            keep[(b, g)] = np.nonzero(k)[0]
+            ref_ev[(b, g)] = e
+    snap = snapshot_rows(c, keep)
+    ev = torch.empty((w.batch, w.hkv, 64), dtype=torch.int32, device="cuda")
+    n_ev = kvb.kv_evict_to_budget(c, t, w.budget, evicted_pos=ev)
+    torch.cuda.synchronize()
+    check_compacted(c, snap, name)
+    assert (to_host(n_ev) == n - w.budget).all()
+    evh = to_host(ev)
+    for (b, g), e in ref_ev.items():
+        assert np.array_equal(evh[b, g], e[:64]), f"evicted_pos ({b},{g})"
+    del dc, c
+    torch.cuda.empty_cache()
+
+
+def test_erase_vs_oracle():
+    rng = np.random.default_rng(9)
+    for trial in range(6):
+        B, H, n = 2, 3, int(rng.integers(1, 9000))
+        d = _cache(40 + trial, B, H, n, n + 1, 128, retention=trial % 2 == 0)
+        R = int(rng.integers(0, 40))
+        ranges = np.zeros((B, R, 2), np.int32)
+        nr = np.zeros(B, np.int32)
+        for b in range(B):
+            k = int(rng.integers(0, R + 1))
+            edges = np.sort(rng.choice(n + 50, size=2 * k, replace=False)).astype(np.int32)
+            ranges[b, :k] = edges.reshape(k, 2)
+            nr[b] = k
+        say("erase trial", trial, n, R)
+        c = dev_cache(d)
+        n_er = kvb.kv_erase_ranges(c, to_dev(ranges), to_dev(nr))
+        torch.cuda.synchronize()
+        ref, ref_n = oracle.erase_ranges(oracle.Cache.from_arrays(d),
+                                         [ranges[b, :nr[b]] for b in range(B)])
+        check_layout(host_dict(c), ref, f"erase {trial}")
+        assert np.array_equal(to_host(n_er), ref_n)
+
+
+def test_memento_full_size():
+    """1M-token cache laid out as thinking blocks + 200-token mementos: erase all
+    completed blocks, append the decode token, attend with beta == 1, evict to M
+    (a no-op here)."""
+    w = synth.WORKLOADS["memento_1m"]
+    blocks, ranges = synth.memento_layout(total=w.ctx, seed=w.seed)
+    say("memento blocks", len(blocks), "ranges", ranges.shape)
+    dc = synth.device_cache(w, layer=0)
+    q, kn, vn, _ = synth.device_queries(w, 0)
+    c = kvb.KVCache.from_dict(dc)
+    ph = to_host(c.pos[:, :, :w.ctx])
+    keep = {(0, g): np.nonzero(oracle.erase_plan(ph[0, g], w.ctx, ranges))[0]
+            for g in range(w.hkv)}
+    kept = 200 * (len(blocks) - 1) + blocks[-1][1]
+    assert all(v.size == kept for v in keep.values())
+    snap = snapshot_rows(c, keep)
+    rg = torch.from_numpy(ranges[None].copy()).cuda()
+    nr = torch.tensor([ranges.shape[0]], dtype=torch.int32, device="cuda")
+    n_er = kvb.kv_erase_ranges(c, rg, nr)
+    torch.cuda.synchronize()
+    check_compacted(c, snap, "memento erase")
+    assert (to_host(n_er) == w.ctx - kept).all()
+    t = torch.full((1,), w.ctx, dtype=torch.int32, device="cuda")
+    out, lse = kvb.kv_attn_decode(c, q, t, k_new=kn, v_new=vn)
+    n_ev = kvb.kv_evict_to_budget(c, t, w.budget)
+    torch.cuda.synchronize()
+    assert to_host(n_ev).tolist() == [[0] * w.hkv]
+    assert (to_host(c.length) == kept + 1).all()
+    G = w.group
+    oh, lh, qh = to_host(out), to_host(lse), to_host(q)
+    knh, vnh = to_host(kn), to_host(vn)
+    for g in (0, 5):
+        s = snap[(0, g)]
+        kk = np.concatenate([s["k"], knh[0, g][None]])[None, None]
+        vv = np.concatenate([s["v"], vnh[0, g][None]])[None, None]
+        pp = np.concatenate([s["pos"], [w.ctx]])[None, None]
+        ro, rl = oracle.decode_attention(values(kk), values(vv), None, pp,
+                                         np.array([[kept + 1]]),
+                                         values(qh[:, g * G:(g + 1) * G]), np.array([w.ctx]))
+        check_attention(oh[:, g * G:(g + 1) * G], lh[:, g * G:(g + 1) * G], ro, rl,
+                        f"memento attention g={g}")
+    del dc, c
+    torch.cuda.empty_cache()
