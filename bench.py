@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: bounded-KV decode attention + eviction at 32K context.
+
+One step = one decode step of a 36-layer Qwen3-8B-like stack (batch 16, 32 query
+heads / 8 KV heads, head_dim 128, bf16 K/V/q, fp32 accumulation) over a 32768-
+token cache per sequence: per layer, append the decode token (t = 32768), run
+retention-biased GQA attention over all 32769 live tokens, evict every KV head
+to the budget M = 4096 and compact the cache in place.  Inputs are seeded and
+synthetic (K, V, q ~ N(0,1) in bf16; beta = sigmoid(N(2, 1.5))) and resident in
+HBM before the timed region.  Eviction is destructive, so the first M slots of
+every layer (the only ones compaction writes) are restored from a pristine copy
+between steps, outside the timed region.
+
+Prints one JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bounded-KV decode attn: KV GB/s vs HBM peak; decode steps/s at 32K ctx"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_qwen3_8b_32k_traffic.json")
+
+
+def algorithmic_bytes(w, n, moved_rows):
+    """Bytes the step must touch once: K and V rows, log beta and positions of
+    every live slot, moved rows (read + write of K, V, log beta, pos), q in,
+    out + lse out.  Split-K partial states are overhead and not counted."""
+    U, D, e = w.units, w.head_dim, w.elem_bytes
+    attn = U * n * 2 * D * e + U * n * 8 + w.batch * w.hq * D * e + w.batch * w.hq * (D + 1) * 4
+    moves = moved_rows * 2 * (2 * D * e + 8)
+    return attn, moves
+
+
+def source_digest(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def cpu_baseline(w, host_units, t, M, budget_s=12.0):
+    """The float64 oracle, as it stands, on whole heads of one layer (append +
+    attention for the head's query group + eviction + compaction), timed until
+    ``budget_s`` of CPU work; extrapolated to the full step (units x layers)."""
+    import numpy as np
+
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done = 0
+    elapsed = 0.0
+    for (k, v, lb, pos, n, q, kn, vn, lbn) in host_units:
+        t0 = time.perf_counter()
+        c = oracle.Cache(k[None, None].copy(), v[None, None].copy(), lb[None, None].copy(),
+                         pos[None, None].copy(), np.array([[n]], np.int32))
+        oracle.append_tokens(c, kn[None, None], vn[None, None], np.array([[lbn]], np.float32),
+                             np.array([t]))
+        oracle.decode_attention(c.values("k"), c.values("v"), c.log_beta, c.pos, c.length,
+                                ((q.astype(np.uint32) << 16).view(np.float32)
+                                 .astype(np.float64))[None], np.array([t]))
+        oracle.evict_to_budget(c, np.array([t]), M)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    unit_s = elapsed / done
+    step_s = unit_s * w.units * w.layers
+    return {"value": 1.0 / step_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} whole KV heads of layer 0 ({w.ctx + 1} tokens, {w.group} query "
+                      f"heads each: append + attention + eviction to {M} + compaction), "
+                      f"{elapsed:.1f} s, extrapolated x{w.units} heads x{w.layers} layers",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_8b_32k")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (testing)")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--serial", action="store_true",
+                    help="run each layer's eviction on the attention stream (no overlap)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path shards by KV head with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.layers:
+        w = dataclasses.replace(w, layers=args.layers)
+    L, M, B = w.layers, w.budget, w.batch
+    n = w.ctx + 1
+    dev = "cuda"
+    print(f"# generating {L} layers of {w.name} on the device", file=sys.stderr, flush=True)
+    caches, kvs, qs, prist = [], [], [], []
+    for layer in range(L):
+        d = synth.device_cache(w, layer)
+        caches.append(d)
+        kvs.append(kvb.KVCache.from_dict(d))
+        qs.append(synth.device_queries(w, layer))
+        prist.append({k: d[k][:, :, :M].clone() for k in ("k", "v", "log_beta", "pos")})
+    torch.cuda.synchronize()
+    t = torch.full((B,), w.ctx, dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, w.hq, w.head_dim), dtype=torch.float32, device=dev) for _ in range(L)]
+    lses = [torch.empty((B, w.hq), dtype=torch.float32, device=dev) for _ in range(L)]
+    nev = [torch.empty((B, w.hkv), dtype=torch.int32, device=dev) for _ in range(L)]
+    first_ev = [torch.empty((B, w.hkv, 1), dtype=torch.int32, device=dev) for _ in range(L)]
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, args.splits), dtype=torch.uint8,
+                       device=dev)
+    ws_e = torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device=dev)
+    splits = args.splits or kvb.kv_attn_decode_splits(kvs[0], w.hq)
+
+    def restore():
+        for d, p in zip(caches, prist):
+            for k in ("k", "v", "log_beta", "pos"):
+                d[k][:, :, :M].copy_(p[k])
+            d["len"].fill_(w.ctx)
+
+    # Per layer: append the decode token, then attention over the whole cache.
+    # Eviction planning only reads log beta and positions, so it starts as soon as
+    # the token is appended and runs beside the attention; the row moves rewrite
+    # the cache and wait for that layer's attention.  Layer l+1's attention waits
+    # for neither.  The side stream has default priority and is joined at the end.
+    main = torch.cuda.current_stream()
+    side = main if args.serial else torch.cuda.Stream()
+    appended = [torch.cuda.Event() for _ in range(L)]
+    attended = [torch.cuda.Event() for _ in range(L)]
+
+    def step():
+        for layer in range(L):
+            q, kn, vn, lb = qs[layer]
+            kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
+            if side is not main:
+                appended[layer].record(main)
+                side.wait_event(appended[layer])
+            kvb.kv_evict_plan(kvs[layer], t, M, evicted_pos=first_ev[layer],
+                              n_evicted=nev[layer], ws=ws_e, stream=side)
+            kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=outs[layer],
+                               lse=lses[layer], ws=ws_a, stream=main)
+            if side is not main:
+                attended[layer].record(main)
+                side.wait_event(attended[layer])
+            kvb.kv_evict_apply(kvs[layer], M, ws_e, stream=side)
+        if side is not main:
+            main.wait_stream(side)
+
+    for _ in range(args.warmup):
+        restore()
+        step()
+    torch.cuda.synchronize()
+
+    # CPU baseline inputs: whole heads of layer 0 as drawn (read before the timed run)
+    host_units = []
+    if not args.no_cpu:
+        restore()
+        torch.cuda.synchronize()
+        d0 = caches[0]
+        q0, kn0, vn0, lb0 = (x.cpu() for x in qs[0])
+        for u in range(w.units):
+            b, g = divmod(u, w.hkv)
+            host_units.append((
+                d0["k"][b, g, :n].view(torch.int16).cpu().numpy().view(np.uint16),
+                d0["v"][b, g, :n].view(torch.int16).cpu().numpy().view(np.uint16),
+                d0["log_beta"][b, g, :n].cpu().numpy(), d0["pos"][b, g, :n].cpu().numpy(),
+                w.ctx,
+                q0[b, g * w.group:(g + 1) * w.group].view(torch.int16).numpy().view(np.uint16),
+                kn0[b, g].view(torch.int16).numpy().view(np.uint16),
+                vn0[b, g].view(torch.int16).numpy().view(np.uint16), float(lb0[b, g])))
+
+    kvb.trace_enable(args.steps * L + 16, ("attn_split",))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(args.steps):
+        restore()
+        torch.cuda.synchronize()
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    split_ms = [ms for name, ms in kvb.trace_read() if name == "attn_split"]
+    kvb.trace_disable()
+
+    # sanity: every head evicted to M; moved rows from the first evicted position
+    moved = 0
+    for layer in range(L):
+        assert bool((nev[layer] == n - M).all()), "eviction count"
+        p0 = first_ev[layer].clamp(max=M).sum().item()
+        moved += w.units * M - p0
+    attn_b, move_b = algorithmic_bytes(w, n, 0)
+    total_b = L * attn_b + algorithmic_bytes(w, n, moved)[1]
+    ms_per_step = sum(times) / len(times)
+    gbps = total_b / (ms_per_step * 1e-3) / 1e9
+    split_avg = sum(split_ms) / len(split_ms)
+    split_gbps = attn_b / (split_avg * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        src = os.path.join(ROOT, "bounded_decode_attention_amd", "csrc", "attn_decode.hip")
+        if tr.get("source_sha") == source_digest(src) and tr.get("splits") == splits:
+            traffic = tr.get("traffic_bytes")
+
+    line = {
+        "metric": METRIC, "value": round(1000.0 / ms_per_step, 3), "unit": "decode steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.head_dim, "ctx": w.ctx, "budget": M, "layers": L,
+                   "kv_splits": splits,
+                   "eviction_stream": "serial" if args.serial else "overlapped"},
+        "kv_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": total_b, "moved_rows_per_step": moved,
+        "roofline": {"bound": "hbm", "kernel": "attn_split_mfma<D=128,G=4>",
+                     "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "bytes_per_launch": attn_b, "avg_launch_ms": round(split_avg, 5),
+                     "launches": len(split_ms)},
+        "cpu_baseline": None,
+    }
+    if host_units:
+        line["cpu_baseline"] = cpu_baseline(w, host_units, w.ctx, M, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

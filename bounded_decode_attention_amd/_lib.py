@@ -49,9 +49,16 @@ def library():
             "asm_lookup_merge_workspace": (SZ, [I32, I32, I32, I32, I32]),
             "kv_attn_decode": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P]),
             "kv_evict_to_budget": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
+            "kv_evict_plan": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
+            "kv_evict_apply": (I32, [CP, I32, P, SZ, P]),
+            "kv_append": (I32, [CP, P, P, P, P, P, SZ, P]),
             "kv_erase_ranges": (I32, [CP, P, P, I32, P, P, SZ, P]),
             "asm_lookup_merge": (I32, [P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, P, P,
                                        SZ, P]),
+            "kvb_trace_enable": (I32, [I32, I32]),
+            "kvb_trace_read": (I32, [P, P, I32]),
+            "kvb_trace_reset": (None, []),
+            "kvb_trace_disable": (None, []),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -209,6 +216,44 @@ def kv_evict_to_budget(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=No
     return n_evicted
 
 
+def kv_append(cache: KVCache, k_new, v_new, log_beta_new, t, ws=None, stream=None):
+    """Append one token per KV head (slot len, pos = t[b]); len += 1."""
+    _need(k_new, "k_new", cache.k.dtype)
+    _need(v_new, "v_new", cache.k.dtype)
+    _need(t, "t", torch.int32)
+    if log_beta_new is not None:
+        _need(log_beta_new, "log_beta_new", torch.float32)
+    ws = _ws(ws, 256, t.device)
+    st = library().kv_append(cache.desc, _ptr(k_new), _ptr(v_new), _ptr(log_beta_new), _ptr(t),
+                             _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_append")
+
+
+def kv_evict_plan(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=None, ws=None,
+                  stream=None):
+    """Phase 1 of eviction (reads the cache only).  Returns (n_evicted, ws); pass the
+    same ws to kv_evict_apply."""
+    _need(t, "t", torch.int32)
+    if n_evicted is None:
+        n_evicted = torch.empty((cache.B, cache.Hkv), dtype=torch.int32, device=t.device)
+    max_evict = 0
+    if evicted_pos is not None:
+        _need(evicted_pos, "evicted_pos", torch.int32)
+        max_evict = evicted_pos.shape[-1]
+    ws = _ws(ws, kv_evict_workspace(cache, M), t.device)
+    st = library().kv_evict_plan(cache.desc, _ptr(t), int(M), _ptr(evicted_pos), max_evict,
+                                 _ptr(n_evicted), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_evict_plan")
+    return n_evicted, ws
+
+
+def kv_evict_apply(cache: KVCache, M: int, ws, stream=None):
+    """Phase 2 of eviction: move the kept rows and set len."""
+    _need(ws, "ws", torch.uint8)
+    st = library().kv_evict_apply(cache.desc, int(M), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_evict_apply")
+
+
 def kv_erase_ranges(cache: KVCache, ranges, n_ranges, n_erased=None, ws=None, stream=None):
     """Erase half-open position ranges ([B][R][2] int32) from every head; compact in place."""
     _need(ranges, "ranges", torch.int32)
@@ -253,3 +298,35 @@ def asm_lookup_merge(q, centroids, abar, log_zbar, self_out, self_lse, out=None,
                                     _stream(stream))
     _check(st, "asm_lookup_merge")
     return out, out_lse, idx
+
+
+TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
+              "keep_count": 16, "keep_emit": 32, "compact_move": 64, "asm_lookup": 128,
+              "asm_finalize": 256}
+
+
+def trace_enable(capacity: int, kernels=("attn_split",)):
+    """Record HIP event pairs around the named kernels' launches (see kvb_trace_enable)."""
+    mask = 0
+    for k in kernels:
+        mask |= TRACE_BITS[k]
+    _check(library().kvb_trace_enable(int(capacity), mask), "kvb_trace_enable")
+
+
+def trace_read(max_entries: int = 1 << 16):
+    """[(kernel name, milliseconds)] for every recorded launch (waits for them)."""
+    import numpy as np
+    ids = np.zeros(max_entries, np.int32)
+    ms = np.zeros(max_entries, np.float32)
+    n = library().kvb_trace_read(ids.ctypes.data_as(ctypes.c_void_p),
+                                 ms.ctypes.data_as(ctypes.c_void_p), max_entries)
+    names = {v: k for k, v in TRACE_BITS.items()}
+    return [(names.get(int(i), str(int(i))), float(m)) for i, m in zip(ids[:n], ms[:n])]
+
+
+def trace_reset():
+    library().kvb_trace_reset()
+
+
+def trace_disable():
+    library().kvb_trace_disable()

@@ -2,9 +2,32 @@
 // cache descriptor validation.
 #include <string.h>
 
+#include <vector>
+
 #include "common.h"
 
 namespace kvb {
+
+namespace {
+struct TraceState {
+  int mask = 0;
+  int used = 0;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int> kernel;
+};
+TraceState g_trace;
+}  // namespace
+
+TraceScope::TraceScope(int k, hipStream_t s) : slot(-1), stream(s) {
+  if (!(g_trace.mask & k) || g_trace.used >= (int)g_trace.start.size()) return;
+  slot = g_trace.used++;
+  g_trace.kernel[slot] = k;
+  hipEventRecord(g_trace.start[slot], s);
+}
+
+TraceScope::~TraceScope() {
+  if (slot >= 0) hipEventRecord(g_trace.stop[slot], stream);
+}
 
 int32_t check_device() {
   static int cached[64];  // 0 unknown, 1 ok, -1 not gfx950
@@ -31,6 +54,52 @@ int32_t check_cache(const kvb_cache* c, bool need_kv) {
 }
 
 }  // namespace kvb
+
+using namespace kvb;
+
+extern "C" void kvb_trace_disable(void) {
+  for (size_t i = 0; i < g_trace.start.size(); ++i) {
+    hipEventDestroy(g_trace.start[i]);
+    hipEventDestroy(g_trace.stop[i]);
+  }
+  g_trace = TraceState();
+}
+
+extern "C" int32_t kvb_trace_enable(int32_t capacity, int32_t kernel_mask) {
+  kvb_trace_disable();
+  if (capacity < 0 || capacity > (1 << 20)) return KVB_EINVAL;
+  if (capacity == 0 || kernel_mask == 0) return KVB_OK;
+  int32_t st = check_device();
+  if (st) return st;
+  g_trace.start.resize(capacity);
+  g_trace.stop.resize(capacity);
+  g_trace.kernel.assign(capacity, 0);
+  for (int i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&g_trace.start[i]) != hipSuccess ||
+        hipEventCreate(&g_trace.stop[i]) != hipSuccess) {
+      g_trace.start.resize(i);
+      g_trace.stop.resize(i);
+      kvb_trace_disable();
+      return KVB_EDEVICE;
+    }
+  }
+  g_trace.mask = kernel_mask;
+  return KVB_OK;
+}
+
+extern "C" int32_t kvb_trace_read(int32_t* kernel_ids, float* ms, int32_t max) {
+  const int n = g_trace.used < max ? g_trace.used : max;
+  for (int i = 0; i < n; ++i) {
+    float e = -1.f;
+    if (hipEventSynchronize(g_trace.stop[i]) == hipSuccess)
+      hipEventElapsedTime(&e, g_trace.start[i], g_trace.stop[i]);
+    if (kernel_ids) kernel_ids[i] = g_trace.kernel[i];
+    if (ms) ms[i] = e;
+  }
+  return n;
+}
+
+extern "C" void kvb_trace_reset(void) { g_trace.used = 0; }
 
 extern "C" const char* kvb_strerror(int32_t status) {
   switch (status) {

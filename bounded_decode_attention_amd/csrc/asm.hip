@@ -256,10 +256,14 @@ extern "C" int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_
   a.cand_idx = (int32_t*)((char*)ws + kWsHeader + align_up(n * 4, 256));
   hipStream_t s = (hipStream_t)stream;
   dim3 grid(a.KC, Hkv, a.QB);
-  if (D == 128)
-    hipLaunchKernelGGL(asm_lookup_partial<128>, grid, dim3(64 * kAsmWaves), 0, s, a);
-  else
-    hipLaunchKernelGGL(asm_lookup_partial<64>, grid, dim3(64 * kAsmWaves), 0, s, a);
+  {
+    TraceScope tr(kTrAsmLookup, s);
+    if (D == 128)
+      hipLaunchKernelGGL(asm_lookup_partial<128>, grid, dim3(64 * kAsmWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(asm_lookup_partial<64>, grid, dim3(64 * kAsmWaves), 0, s, a);
+  }
+  TraceScope tr(kTrAsmFinalize, s);
   hipLaunchKernelGGL(asm_finalize, dim3(B * Hq), dim3(64), 0, s, a);
   return launch_status();
 }

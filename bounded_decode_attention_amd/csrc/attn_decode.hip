@@ -295,6 +295,234 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ pipelined split (D = 128)
+// Same math and MFMA layout as attn_split_mfma, in a two-stage pipeline: while
+// tile i is computed, tile i+1's K rows are in flight into a second register set
+// and its V rows into a second LDS buffer.  V goes HBM -> LDS directly
+// (global_load_lds_dwordx4: lane l of DMA instruction i lands at byte 16*l of that
+// instruction's 1 KB block), so it needs no VGPRs and no ds_write.  Instruction i
+// carries tile rows 4i..4i+3 and its block starts at i*1056 bytes: the 32-byte
+// pad puts the four lane groups of every transposed read in disjoint bank groups.
+// The two buffers are distinct arrays and the loop is unrolled by two, so each
+// stage's LDS reads wait only on that stage's own loads.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+constexpr int kVBlk = 1056;  // bytes per V DMA instruction block (1 KB + pad)
+
+struct KTile {
+  u32x4 k[2][4];
+  float lb[2][4];
+  int ps[2][4];
+};
+
+// Issues every load of one tile with no branches (the waitcnt pass then keeps the
+// other stage's loads in flight).  Rows past the split end are clamped to its last
+// row (cache hits); with VEC (capacity % 4 == 0) log beta and pos are read four at
+// a time from base min(r0, cap - 4), which equals r0 for every slot below cap.
+template <bool VEC>
+__device__ __forceinline__ void issue_tile128(const uint16_t* kb, const uint16_t* vb,
+                                              const float* lbb, const int32_t* pb, int tb,
+                                              int end, int cap, int lane, KTile& t,
+                                              lds_u8* __restrict__ vlds) {
+  const int lg = lane >> 4, lc = lane & 15;
+  const int last = end - 1;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = min(tb + 16 * j + lc, last);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t.k[j][kk] = *(const u32x4*)(kb + (size_t)row * 128 + 32 * kk + 8 * lg);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = min(tb + 4 * i + lg, last);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (size_t)row * 128 + 8 * lc),
+                                     (lds_void_t*)(vlds + i * kVBlk), 16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r0 = tb + 16 * j + 4 * lg;
+    if constexpr (VEC) {
+      const int rb = min(r0, cap - 4);
+      const f32x4 l4 = *(const f32x4*)(lbb + rb);
+      const i32x4 p4 = *(const i32x4*)(pb + rb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        t.lb[j][r] = l4[r];
+        t.ps[j][r] = p4[r];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(r0 + r, last);
+        t.lb[j][r] = lbb[row];
+        t.ps[j][r] = pb[row];
+      }
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void compute_tile128(const KTile& t, const lds_u8* __restrict__ vlds, int tb,
+                                                int end, int lane, const u32x4* qv, float sc,
+                                                int qpos, bool has_lb, float& m2, float& lsum,
+                                                f32x4* acc) {
+  const int lg = lane >> 4, lc = lane & 15;
+  f32x4 S[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) S[j] = mfma_16x16x32_bf16(t.k[j][kk], qv[kk], S[j]);
+  }
+  float s[2][4];
+  float mt = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tb + 16 * j + 4 * lg + r;
+      float bias = 0.f;
+      if (has_lb) {
+        const int d = qpos - t.ps[j][r];
+        bias = d != 0 ? (float)d * t.lb[j][r] : 0.f;
+      }
+      float x = fmaf(S[j][r], sc, bias * kLog2e);
+      if (tok >= end) x = kNegInf;
+      s[j][r] = x;
+      mt = fmaxf(mt, x);
+    }
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  if (mt > m2) {
+    const float alpha = (m2 == kNegInf) ? 0.f : exp2_fast(m2 - mt);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    lsum *= alpha;
+    m2 = mt;
+  }
+  const float mref = (m2 == kNegInf) ? 0.f : m2;
+  uint32_t pw[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    uint32_t h[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int e = 2 * e2 + w;
+      const float x = exp2_fast((e < 4 ? s[0][e] : s[1][e - 4]) - mref);
+      lsum += x;
+      const uint32_t xb = __float_as_uint(x);
+      const uint32_t hi = xb >> 16;
+      const uint32_t lo16 = f32_to_bf16_rne(x - __uint_as_float(xb & 0xFFFF0000u));
+      h[w] = lc < G ? hi : lo16;
+    }
+    pw[e2] = h[0] | (h[1] << 16);
+  }
+  const u32x4 pb4 = {pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const lds_u8* col = vlds + 2 * (16 * nb + lc);
+    uint32_t vw[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int e0 = 2 * e2, e1 = 2 * e2 + 1;
+      const int t0 = e0 < 4 ? 4 * lg + e0 : 16 + 4 * lg + e0 - 4;
+      const int t1 = e1 < 4 ? 4 * lg + e1 : 16 + 4 * lg + e1 - 4;
+      typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+      const uint32_t v0 = *(lds_u16*)(col + (t0 >> 2) * kVBlk + (t0 & 3) * 256);
+      const uint32_t v1 = *(lds_u16*)(col + (t1 >> 2) * kVBlk + (t1 & 3) * 256);
+      vw[e2] = v0 | (v1 << 16);
+    }
+    const u32x4 va = {vw[0], vw[1], vw[2], vw[3]};
+    acc[nb] = mfma_16x16x32_bf16(va, pb4, acc[nb]);
+  }
+}
+
+template <int G, bool LB, bool VEC>
+__global__ __launch_bounds__(64) void attn_split_pipe128(AttnArgs a) {
+  static_assert(2 * G <= 16, "group too large for the hi/lo column split");
+  __shared__ __attribute__((aligned(16))) unsigned char vbufA_[8 * kVBlk];
+  __shared__ __attribute__((aligned(16))) unsigned char vbufB_[8 * kVBlk];
+  lds_u8* vbufA = (lds_u8*)vbufA_;
+  lds_u8* vbufB = (lds_u8*)vbufB_;
+  const int u = blockIdx.y;
+  const int p = blockIdx.x;
+  const int b = u / a.Hkv;
+  const int g = u - b * a.Hkv;
+  const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int lc = lane & 15;
+  const int n = min(a.len[u], a.cap);
+  const int end = n;
+
+  const int hcol = lc < G ? lc : (lc < 2 * G ? lc - G : -1);
+  u32x4 qv[4];
+  {
+    const uint16_t* qp =
+        (const uint16_t*)a.q + ((size_t)(b * a.Hq + g * G + (hcol < 0 ? 0 : hcol))) * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qv[kk] = hcol >= 0 ? *(const u32x4*)(qp + 32 * kk + 8 * lg) : z;
+    }
+  }
+  const uint16_t* kb = (const uint16_t*)a.k + (size_t)u * a.cap * 128;
+  const uint16_t* vb = (const uint16_t*)a.v + (size_t)u * a.cap * 128;
+  // without a retention array the bias loads read pos twice (harmless, unused)
+  const int32_t* pb = a.pos + (size_t)u * a.cap;
+  const float* lbb = LB ? a.log_beta + (size_t)u * a.cap : (const float*)pb;
+  const int qpos = a.t[b];
+  const float sc = a.scale_log2;
+
+  float m2 = kNegInf, lsum = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Tiles in pairs (A, B) with one loop exit, so each register set keeps its
+  // registers and the waitcnt pass can leave the other stage's loads pending.
+  KTile tA, tB;
+  // Split p takes tiles p, p + P, p + 2P, ... of the head (round-robin), so the
+  // waves of one head read neighbouring tiles at the same time.
+  const int T = (n + 31) >> 5;
+  const int ntiles = p < T ? (T - p + a.P - 1) / a.P : 0;
+  const int step = 32 * a.P;
+  if (ntiles > 0) {
+    int tb = 32 * p;
+    issue_tile128<VEC>(kb, vb, lbb, pb, tb, end, a.cap, lane, tA, vbufA);
+    for (int k = 0; k < (ntiles >> 1); ++k) {
+      issue_tile128<VEC>(kb, vb, lbb, pb, tb + step, end, a.cap, lane, tB, vbufB);
+      compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      issue_tile128<VEC>(kb, vb, lbb, pb, tb + 2 * step, end, a.cap, lane, tA, vbufA);
+      compute_tile128<G>(tB, vbufB, tb + step, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      tb += 2 * step;
+    }
+    if (ntiles & 1) compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+  }
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int src = lane + G < 64 ? lane + G : lane;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nb][i] = (acc[nb][i] + __shfl(acc[nb][i], src, 64)) * inv;
+  if (lc < G) {
+    const int h = g * G + lc;
+    const size_t sidx = ((size_t)(b * a.Hq + h)) * a.P + p;
+    float* pa = a.part_a + sidx * 128;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) *(f32x4*)(pa + 16 * nb + 4 * lg) = acc[nb];
+    if (lg == 0) {
+      a.part_ml[2 * sidx] = m2 == kNegInf ? kNegInf : m2 * kLn2;
+      a.part_ml[2 * sidx + 1] = lsum;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ generic split
 template <typename T, int DPL, int MAXG>
 __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
@@ -388,40 +616,73 @@ __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ merge
-// One wave per (b, h): fold the P states in split order with the merge operator.
-__global__ __launch_bounds__(64) void attn_merge(const float* part_a, const float* part_ml, int P,
-                                                 int D, float* out, float* lse) {
+// One 256-thread workgroup per (b, h) folds the P split states with the merge
+// operator.  Weights w_p = Z_p e^{m_p - M} are staged in LDS; thread group q
+// (256 / D groups) sums w_p a_p over its contiguous share of the splits with 8
+// loads in flight, and the groups' sums are added in group order, so the result
+// does not depend on timing.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxP = 4096;
+
+__global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
+                                                            const float* part_ml, int P, int D,
+                                                            float* out, float* lse) {
+  __shared__ float w[kMergeMaxP];
+  __shared__ float red[kMergeThreads];
+  __shared__ float gsum[kMergeThreads];
   const int bh = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const float* ml = part_ml + (size_t)bh * P * 2;
   const float* pa = part_a + (size_t)bh * P * D;
-  float M = kNegInf;
-  for (int p = lane; p < P; p += 64)
-    if (ml[2 * p + 1] > 0.f) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-  float W = 0.f;
-  if (M != kNegInf) {
-    for (int p = 0; p < P; ++p) {
-      const float Zp = ml[2 * p + 1];
-      if (Zp > 0.f) {
-        const float w = Zp * __expf(ml[2 * p] - M);
-        W += w;
+  const int NG = kMergeThreads / D;  // thread groups over the splits
+  const int q = tid / D, d = tid - q * D;
+  const int p0 = q < NG ? (int)((long long)P * q / NG) : 0;
+  const int p1 = q < NG ? (int)((long long)P * (q + 1) / NG) : 0;
+  // the split outputs do not depend on the weights: load the first batch now
+  constexpr int kB = 16;
+  float x[kB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = lane + 64 * j;
-          if (d < D) o[j] = fmaf(w, pa[(size_t)p * D + d], o[j]);
-        }
-      }
-    }
+  for (int e = 0; e < kB; ++e) x[e] = p0 + e < p1 ? pa[(size_t)(p0 + e) * D + d] : 0.f;
+  float mx = kNegInf;
+  for (int p = tid; p < P; p += kMergeThreads)
+    if (ml[2 * p + 1] > 0.f) mx = fmaxf(mx, ml[2 * p]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
   }
-  const float inv = W > 0.f ? 1.f / W : 0.f;
+  const float M = red[0];
+  for (int p = tid; p < P; p += kMergeThreads) {
+    const float Zp = ml[2 * p + 1];
+    w[p] = (Zp > 0.f && M != kNegInf) ? Zp * __expf(ml[2 * p] - M) : 0.f;
+  }
+  __syncthreads();
+  float o = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = lane + 64 * j;
-    if (d < D) out[(size_t)bh * D + d] = o[j] * inv;
+  for (int e = 0; e < kB; ++e)
+    if (p0 + e < p1) o = fmaf(w[p0 + e], x[e], o);
+  for (int pb = p0 + kB; pb < p1; pb += kB) {
+#pragma unroll
+    for (int e = 0; e < kB; ++e) x[e] = pb + e < p1 ? pa[(size_t)(pb + e) * D + d] : 0.f;
+#pragma unroll
+    for (int e = 0; e < kB; ++e)
+      if (pb + e < p1) o = fmaf(w[pb + e], x[e], o);
   }
-  if (lane == 0) lse[bh] = W > 0.f ? M + __logf(W) : kNegInf;
+  gsum[tid] = o;
+  if (tid == 0) {
+    float W = 0.f;
+    for (int p = 0; p < P; ++p) W += w[p];
+    red[0] = W;
+  }
+  __syncthreads();
+  const float W = red[0];
+  if (tid < D) {
+    float acc = 0.f;
+    for (int g = 0; g < NG; ++g) acc += gsum[g * D + tid];
+    out[(size_t)bh * D + tid] = W > 0.f ? acc / W : 0.f;
+  }
+  if (tid == 0) lse[bh] = W > 0.f ? M + __logf(W) : kNegInf;
 }
 
 // ------------------------------------------------------------------ host
@@ -438,9 +699,19 @@ static void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
 static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.P, c->B * c->Hkv);
   if (mfma_supported(c, a.G)) {
+#define KVB_PIPE_CASE(GG)                                                                  \
+  if (c->D == 128 && a.G == GG) {                                                          \
+    const bool lb = c->log_beta != nullptr, vec = c->cap % 4 == 0 && c->cap >= 4;         \
+    if (lb && vec) hipLaunchKernelGGL((attn_split_pipe128<GG, true, true>), grid, dim3(64), 0, s, a);   \
+    else if (lb) hipLaunchKernelGGL((attn_split_pipe128<GG, true, false>), grid, dim3(64), 0, s, a);   \
+    else if (vec) hipLaunchKernelGGL((attn_split_pipe128<GG, false, true>), grid, dim3(64), 0, s, a);  \
+    else hipLaunchKernelGGL((attn_split_pipe128<GG, false, false>), grid, dim3(64), 0, s, a);          \
+    return KVB_OK;                                                                         \
+  }
+    KVB_PIPE_CASE(1) KVB_PIPE_CASE(2) KVB_PIPE_CASE(4) KVB_PIPE_CASE(8)
+#undef KVB_PIPE_CASE
 #define KVB_MFMA_CASE(DD, GG) \
   if (c->D == DD && a.G == GG) { launch_mfma<DD, GG>(a, grid, s); return KVB_OK; }
-    KVB_MFMA_CASE(128, 1) KVB_MFMA_CASE(128, 2) KVB_MFMA_CASE(128, 4) KVB_MFMA_CASE(128, 8)
     KVB_MFMA_CASE(64, 1) KVB_MFMA_CASE(64, 2) KVB_MFMA_CASE(64, 4) KVB_MFMA_CASE(64, 8)
 #undef KVB_MFMA_CASE
   }
@@ -460,10 +731,12 @@ static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s
   return KVB_EUNSUPPORTED;
 }
 
+// About two rounds of resident waves (2 per SIMD): fewer, longer splits stream
+// better than many short ones, and keep the merged partial states small.
 static int32_t auto_splits(const kvb_cache* c) {
   const long long units = (long long)c->B * c->Hkv;
   const long long tiles = (c->cap + 31) / 32;
-  long long P = (8192 + units - 1) / units;
+  long long P = (4096 + units - 1) / units;
   if (P > tiles) P = tiles;
   if (P > 1024) P = 1024;
   if (P < 1) P = 1;
@@ -485,6 +758,23 @@ extern "C" size_t kv_attn_decode_workspace(const kvb_cache* cache, int32_t Hq, i
   const size_t P = num_splits > 0 ? (size_t)num_splits : (size_t)auto_splits(cache);
   const size_t S = (size_t)cache->B * Hq * P;
   return kWsHeader + align_up(S * cache->D * sizeof(float), 256) + align_up(S * 2 * sizeof(float), 256);
+}
+
+extern "C" int32_t kv_append(const kvb_cache* cache, const void* k_new, const void* v_new,
+                             const float* log_beta_new, const int32_t* t, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!k_new || !v_new || !t || (cache->log_beta && !log_beta_new)) return KVB_EINVAL;
+  if (!ws || ws_bytes < kWsHeader) return KVB_EWORKSPACE;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int elem = cache->dtype == KVB_BF16 ? 2 : 4;
+  TraceScope tr(kTrAppend, s);
+  hipLaunchKernelGGL(kv_append, dim3(cache->B * cache->Hkv), dim3(64), 0, s, cache->k, cache->v,
+                     cache->log_beta, cache->pos, cache->len, cache->cap, cache->D * elem / 4,
+                     k_new, v_new, log_beta_new, t, cache->Hkv, (int32_t*)ws);
+  return launch_status();
 }
 
 extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq,
@@ -527,14 +817,19 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   a.scale_log2 = (scale > 0.f ? scale : 1.0f / sqrtf((float)cache->D)) * kLog2e;
 
   if (k_new) {
+    TraceScope tr(kTrAppend, s);
     const int elem = cache->dtype == KVB_BF16 ? 2 : 4;
     hipLaunchKernelGGL(kv_append, dim3(cache->B * cache->Hkv), dim3(64), 0, s, cache->k,
                        cache->v, cache->log_beta, cache->pos, cache->len, cache->cap,
                        cache->D * elem / 4, k_new, v_new, log_beta_new, t, cache->Hkv,
                        (int32_t*)ws);
   }
-  if ((st = launch_split(cache, a, s))) return st;
-  hipLaunchKernelGGL(attn_merge, dim3(cache->B * Hq), dim3(64), 0, s, a.part_a, a.part_ml, P,
-                     cache->D, out, lse);
+  {
+    TraceScope tr(kTrAttnSplit, s);
+    if ((st = launch_split(cache, a, s))) return st;
+  }
+  TraceScope tr(kTrAttnMerge, s);
+  hipLaunchKernelGGL(attn_merge, dim3(cache->B * Hq), dim3(kMergeThreads), 0, s, a.part_a,
+                     a.part_ml, P, cache->D, out, lse);
   return launch_status();
 }

@@ -61,6 +61,19 @@ int32_t check_device();
 // Host: validate a cache descriptor (pointers, sizes, dtype/D support).
 int32_t check_cache(const kvb_cache* c, bool need_kv);
 
+// Kernel-launch tracing (see kvb_trace_enable): records a HIP event pair on the
+// launch stream around each traced kernel while enabled.
+enum TraceKernel {
+  kTrAttnSplit = 1, kTrAttnMerge = 2, kTrAppend = 4, kTrEvictSelect = 8, kTrKeepCount = 16,
+  kTrKeepEmit = 32, kTrCompactMove = 64, kTrAsmLookup = 128, kTrAsmFinalize = 256
+};
+struct TraceScope {
+  TraceScope(int kernel, hipStream_t s);
+  ~TraceScope();
+  int slot;
+  hipStream_t stream;
+};
+
 inline int32_t launch_status() {
   return hipGetLastError() == hipSuccess ? KVB_OK : KVB_ELAUNCH;
 }

@@ -255,6 +255,236 @@ __global__ __launch_bounds__(kSelThreads) void evict_select(const float* lb_all,
   }
 }
 
+// ---------------------------------------------------------------- fused LDS planner
+// One 1024-thread workgroup per head, for heads whose float32-rounded keys fit in
+// LDS (gfx950: 160 KB).  Same selection as evict_select, then the head's own scan:
+// keep flags in slot order -> destination of every kept row (keep_src), evicted
+// positions, and staging of cross-workgroup hazard rows -- no chunk kernels needed.
+// Keys sit at LDS index i + i/32 so that both the strided passes and the
+// per-thread contiguous ranges of the scan are free of bank conflicts.
+__device__ __forceinline__ int skew(int i) { return i + (i >> 5); }
+
+struct PlanArgs {
+  const float* log_beta;
+  const int32_t* pos;
+  const int32_t* len;
+  const int32_t* tq;
+  UnitInfo* info;
+  int32_t* keep_src;
+  int32_t* evicted_pos;
+  int32_t* n_out;
+  unsigned char* scratch;
+  const void* k;
+  const void* v;
+  int32_t cap, Hkv, M, Mk, max_evict, row_bytes, srow, move_rows;
+};
+
+__device__ void stage_row(const PlanArgs& a, int u, int src, int dst) {
+  unsigned char* s = a.scratch + ((size_t)u * a.Mk + dst) * a.srow;
+  const size_t off = ((size_t)u * a.cap + src) * a.row_bytes;
+  const u32x4* kp = (const u32x4*)((const unsigned char*)a.k + off);
+  const u32x4* vp = (const u32x4*)((const unsigned char*)a.v + off);
+  const int pieces = a.row_bytes / 16;
+  for (int i = 0; i < pieces; ++i) {
+    ((u32x4*)s)[i] = kp[i];
+    ((u32x4*)(s + a.row_bytes))[i] = vp[i];
+  }
+  int32_t* tail = (int32_t*)(s + 2 * a.row_bytes);
+  tail[0] = a.log_beta ? __float_as_int(a.log_beta[(size_t)u * a.cap + src]) : 0;
+  tail[1] = a.pos[(size_t)u * a.cap + src];
+}
+
+constexpr int kStageList = 1024;  // staged rows copied cooperatively per head
+
+__global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
+  extern __shared__ uint32_t keys[];  // ord32 keys at skew(i)
+  __shared__ uint32_t hist[2048];
+  __shared__ int smem[kSelThreads / 64];
+  __shared__ int out[4];
+  __shared__ unsigned long long mm[2];
+  __shared__ int2 stage[kStageList];
+  __shared__ int nstage;
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = min(a.len[u], a.cap);
+  const int M = a.M;
+  if (tid == 0) {
+    out[0] = 0;
+    out[1] = 1;
+    out[2] = -1;
+    mm[0] = ~0ull;
+    mm[1] = 0ull;
+    nstage = 0;
+  }
+  if (n <= M) {
+    if (tid == 0) {
+      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, {0, 0}};
+      a.info[u] = z;
+      if (a.n_out) a.n_out[u] = 0;
+    }
+    return;
+  }
+  const float* lb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
+  const int32_t* ps = a.pos + (size_t)u * a.cap;
+  const int tpos = a.tq[u / a.Hkv];
+  int r = n - M;
+
+  // ---- pass 0: keys to LDS + histogram of the top 11 bits.  Sixteen rounds' loads
+  // are issued before any key is formed (the loop is latency bound otherwise).
+  for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  constexpr int kRounds = 16;
+  for (int i0 = tid; i0 < n; i0 += kRounds * kSelThreads) {
+    float lv[kRounds];
+    int pv[kRounds];
+#pragma unroll
+    for (int e = 0; e < kRounds; ++e) {
+      const int i = min(i0 + e * kSelThreads, n - 1);
+      lv[e] = lb ? lb[i] : 0.f;
+      pv[e] = ps[i];
+    }
+#pragma unroll
+    for (int e = 0; e < kRounds; ++e) {
+      const int i = i0 + e * kSelThreads;
+      if (i < n) {
+        const int d = tpos - pv[e];
+        const double k = (!lb || d == 0) ? 0.0 : (double)d * (double)lv[e];
+        const uint32_t k32 = ord32(k);
+        keys[skew(i)] = k32;
+        atomicAdd(&hist[k32 >> 21], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  int bucket = select_bucket<kSelThreads>(hist, 2048, r, smem, out);
+  uint32_t prefix = (uint32_t)bucket;
+  // ---- passes 1, 2 over LDS
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 10 : 0;
+    const int bits = pass == 1 ? 11 : 10;
+    const int nb = 1 << bits;
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint32_t k32 = keys[skew(i)];
+      if ((k32 >> (shift + bits)) == prefix) atomicAdd(&hist[(k32 >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    bucket = select_bucket<kSelThreads>(hist, nb, r, smem, out);
+    prefix = (prefix << bits) | (uint32_t)bucket;
+  }
+  const uint32_t t32 = prefix;
+
+  // ---- exact keys of the float32 ties: min and max
+  for (int i = tid; i < n; i += kSelThreads) {
+    if (keys[skew(i)] != t32) continue;
+    const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+    atomicMin(&mm[0], k64);
+    atomicMax(&mm[1], k64);
+  }
+  __syncthreads();
+  unsigned long long K = mm[0];
+  if (K != mm[1]) {
+    // distinct exact keys among the ties: radix over the 64-bit key (rare)
+    unsigned long long pfx = 0;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kSelThreads) {
+        if (keys[skew(i)] != t32) continue;
+        const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+        if (pass == 0 || (k64 >> (shift + 8)) == pfx) atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      const int bk = select_bucket<kSelThreads>(hist, 256, r, smem, out);
+      pfx = (pfx << 8) | (unsigned long long)bk;
+    }
+    K = pfx;
+  }
+
+  // ---- slot of the r-th tie (slot order) with exact key K: contiguous ranges
+  const int ipt = (n + kSelThreads - 1) / kSelThreads;
+  const int lo = min(n, tid * ipt), hi = min(n, lo + ipt);
+  int c = 0;
+  for (int i = lo; i < hi; ++i)
+    if (keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K) ++c;
+  int tot;
+  const int before = block_excl_scan<kSelThreads>(c, smem, tot);
+  if (r > before && r <= before + c) {
+    int seen = before;
+    for (int i = lo; i < hi; ++i)
+      if (keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K && ++seen == r) {
+        out[2] = i;
+        break;
+      }
+  }
+  __syncthreads();
+  const int sstar = out[2];
+
+  // ---- keep flags, scan, emit
+  auto keep = [&](int i) -> bool {
+    const uint32_t k32 = keys[skew(i)];
+    if (k32 != t32) return k32 > t32;
+    const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+    return k64 > K || (k64 == K && i > sstar);
+  };
+  int kc = 0;
+  for (int i = lo; i < hi; ++i) kc += keep(i) ? 1 : 0;
+  int kept_all;
+  int dst = block_excl_scan<kSelThreads>(kc, smem, kept_all);
+  int ev = lo - dst;
+  const int kept = min(kept_all, a.Mk);
+  for (int i = lo; i < hi; ++i) {
+    if (keep(i)) {
+      if (dst < a.Mk) {
+        a.keep_src[(size_t)u * a.Mk + dst] = i;
+        if (i != dst && i < kept && i >= (dst / a.move_rows + 1) * a.move_rows) {
+          const int slot = atomicAdd(&nstage, 1);
+          if (slot < kStageList)
+            stage[slot] = make_int2(i, dst);
+          else
+            stage_row(a, u, i, dst);  // list full: copy it here
+        }
+      }
+      ++dst;
+    } else {
+      if (a.evicted_pos && ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
+      ++ev;
+    }
+  }
+  __syncthreads();
+  // ---- staged rows: all threads copy 16-byte pieces (K, V) and the row tails
+  {
+    const int ns = min(nstage, kStageList);
+    const int ppr = a.row_bytes / 16;
+    const int per = 2 * ppr + 1;
+    const unsigned char* kb = (const unsigned char*)a.k + (size_t)u * a.cap * a.row_bytes;
+    const unsigned char* vb = (const unsigned char*)a.v + (size_t)u * a.cap * a.row_bytes;
+    for (int q = tid; q < ns * per; q += kSelThreads) {
+      const int e = q / per, part = q - e * per;
+      const int src = stage[e].x, dst2 = stage[e].y;
+      unsigned char* sp = a.scratch + ((size_t)u * a.Mk + dst2) * a.srow;
+      if (part < 2 * ppr) {
+        const bool isv = part >= ppr;
+        const int pc = isv ? part - ppr : part;
+        *(u32x4*)(sp + (isv ? a.row_bytes : 0) + 16 * pc) =
+            *(const u32x4*)((isv ? vb : kb) + (size_t)src * a.row_bytes + 16 * pc);
+      } else {
+        int32_t* tail = (int32_t*)(sp + 2 * a.row_bytes);
+        tail[0] = lb ? __float_as_int(lb[src]) : 0;
+        tail[1] = ps[src];
+      }
+    }
+  }
+  if (tid == 0) {
+    UnitInfo v = {K, sstar, MODE_EVICT, n, kept, {0, 0}};
+    a.info[u] = v;
+    if (a.n_out) a.n_out[u] = n - kept_all;
+  }
+}
+
 // ---------------------------------------------------------------- keep predicate
 struct KeepArgs {
   const float* log_beta;
@@ -404,10 +634,20 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
 constexpr int kMoveThreads = 256;
 constexpr int kMovePieces = 8;  // 16-byte pieces per thread per group
 
+// Thread layout: piece column pc = tid % (2*ppr) (K chunks, then V chunks) is fixed
+// per thread; the thread moves that column of rows tid / (2*ppr) + q * rpp,
+// q < kMovePieces (rpp = rows per pass).  All reads of the group are issued
+// before the barrier, all writes after it.
 __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, int check_mode) {
   const int cpu = (a.Mk + a.move_rows - 1) / a.move_rows;
-  const int ppr = a.row_bytes / 16;  // pieces per row per tensor
+  const int ppr = a.row_bytes / 16;   // 16-byte pieces per row per tensor
+  const int cols = 2 * ppr;
+  const int rpp = kMoveThreads / cols; // rows per pass
   const int tid = threadIdx.x;
+  const int col = tid % cols;
+  const int r0 = tid / cols;
+  const bool isv = col >= ppr;
+  const int pc = isv ? col - ppr : col;
   for (int w = blockIdx.x; w < U * cpu; w += gridDim.x) {
     const int u = w / cpu, ch = w - u * cpu;
     const UnitInfo inf = a.info[u];
@@ -419,63 +659,52 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
     const int rows = min(a.move_rows, kept - j0);
     const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
     const unsigned char* scr = a.scratch + (size_t)u * a.Mk * a.srow;
-    unsigned char* kb = (unsigned char*)a.k + (size_t)u * a.cap * a.row_bytes;
-    unsigned char* vb = (unsigned char*)a.v + (size_t)u * a.cap * a.row_bytes;
+    unsigned char* tb = (unsigned char*)(isv ? a.v : a.k) + (size_t)u * a.cap * a.row_bytes;
     float* lbb = a.log_beta ? (float*)a.log_beta + (size_t)u * a.cap : nullptr;
     int32_t* pb = (int32_t*)a.pos + (size_t)u * a.cap;
 
-    u32x4 buf[kMovePieces];
-    bool live[kMovePieces];
-    int32_t tail_lb = 0, tail_pos = 0, tail_dst = -1;
-    // ---- read phase
+    int src[kMovePieces];
 #pragma unroll
     for (int q = 0; q < kMovePieces; ++q) {
-      live[q] = false;
-      const int pidx = tid + q * kMoveThreads;
-      const int row = pidx / (2 * ppr);
-      if (row >= rows) continue;
-      const int part = pidx - row * 2 * ppr;  // [0, ppr): K, [ppr, 2ppr): V
-      const int j = j0 + row;
-      const int src = ks[j];
-      if (src == j) continue;
-      const bool isv = part >= ppr;
-      const int pc = isv ? part - ppr : part;
-      const bool staged = src < kept && src >= j0 + a.move_rows;
-      const unsigned char* from;
-      if (staged)
-        from = scr + (size_t)j * a.srow + (isv ? a.row_bytes : 0) + 16 * pc;
-      else
-        from = (isv ? vb : kb) + (size_t)src * a.row_bytes + 16 * pc;
-      buf[q] = *(const u32x4*)from;
-      live[q] = true;
+      const int row = r0 + q * rpp;
+      src[q] = (r0 < rpp && row < rows) ? ks[j0 + row] : -1;
     }
+    u32x4 buf[kMovePieces];
+#pragma unroll
+    for (int q = 0; q < kMovePieces; ++q) {
+      const int j = j0 + r0 + q * rpp;
+      if (src[q] < 0 || src[q] == j) {
+        src[q] = -1;
+        continue;
+      }
+      const bool staged = src[q] < kept && src[q] >= j0 + a.move_rows;
+      const unsigned char* from =
+          staged ? scr + (size_t)j * a.srow + (isv ? a.row_bytes : 0) + 16 * pc
+                 : tb + (size_t)src[q] * a.row_bytes + 16 * pc;
+      buf[q] = *(const u32x4*)from;
+    }
+    int32_t tail_lb = 0, tail_pos = 0, tail_dst = -1;
     if (tid < rows) {
       const int j = j0 + tid;
-      const int src = ks[j];
-      if (src != j) {
-        const bool staged = src < kept && src >= j0 + a.move_rows;
-        if (staged) {
+      const int s = ks[j];
+      if (s != j) {
+        if (s < kept && s >= j0 + a.move_rows) {
           const int32_t* tl = (const int32_t*)(scr + (size_t)j * a.srow + 2 * a.row_bytes);
           tail_lb = tl[0];
           tail_pos = tl[1];
         } else {
-          tail_lb = lbb ? __float_as_int(lbb[src]) : 0;
-          tail_pos = pb[src];
+          tail_lb = lbb ? __float_as_int(lbb[s]) : 0;
+          tail_pos = pb[s];
         }
         tail_dst = j;
       }
     }
     __syncthreads();
-    // ---- write phase
 #pragma unroll
     for (int q = 0; q < kMovePieces; ++q) {
-      if (!live[q]) continue;
-      const int pidx = tid + q * kMoveThreads;
-      const int row = pidx / (2 * ppr);
-      const int part = pidx - row * 2 * ppr;
-      const bool isv = part >= ppr;
-      const int pc = isv ? part - ppr : part;
-      *(u32x4*)((isv ? vb : kb) + (size_t)(j0 + row) * a.row_bytes + 16 * pc) = buf[q];
+      if (src[q] < 0) continue;
+      const int j = j0 + r0 + q * rpp;
+      *(u32x4*)(tb + (size_t)j * a.row_bytes + 16 * pc) = buf[q];
     }
     if (tail_dst >= 0) {
       if (lbb) lbb[tail_dst] = __int_as_float(tail_lb);
@@ -486,6 +715,28 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
 }
 
 // ---------------------------------------------------------------- host
+// Dynamic LDS available to evict_plan_lds (static LDS of the kernel excluded).
+static size_t plan_lds_limit() {
+  static size_t limit = 0;
+  if (limit == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        v > 0) {
+      hipFuncAttributes fa;
+      size_t static_lds = 64 * 1024;  // conservative if the query fails
+      if (hipFuncGetAttributes(&fa, (const void*)evict_plan_lds) == hipSuccess)
+        static_lds = fa.sharedSizeBytes;
+      limit = (size_t)v > static_lds + 256 ? (size_t)v - static_lds - 256 : 1;
+      hipFuncSetAttribute((const void*)evict_plan_lds,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit);
+    } else {
+      limit = 1;
+    }
+  }
+  return limit;
+}
+
 struct CompactLayout {
   size_t info, counts, keep_src, scratch, total;
   int C, Mk, srow, move_rows, row_bytes;
@@ -498,8 +749,12 @@ static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
   L.srow = 2 * L.row_bytes + 16;
   L.C = (c->cap + kChunk - 1) / kChunk;
   L.Mk = Mk < 1 ? 1 : Mk;
-  L.move_rows = kMoveThreads * kMovePieces / (2 * (L.row_bytes / 16));
-  if (L.move_rows > kMoveThreads) L.move_rows = kMoveThreads;  // one thread per row tail
+  {
+    const int cols = 2 * (L.row_bytes / 16);
+    const int rpp = kMoveThreads / cols;
+    L.move_rows = rpp * kMovePieces;
+    if (L.move_rows > kMoveThreads) L.move_rows = kMoveThreads;  // one thread per row tail
+  }
   L.info = kWsHeader;
   L.counts = L.info + align_up(U * sizeof(UnitInfo), 256);
   L.keep_src = L.counts + align_up(U * L.C * sizeof(int32_t), 256);
@@ -531,21 +786,86 @@ static KeepArgs keep_args(const kvb_cache* c, const CompactLayout& L, void* ws) 
   return a;
 }
 
-static int32_t launch_compaction(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s) {
+static void launch_keep_chunks(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s) {
   const int U = c->B * c->Hkv;
   dim3 grid(a.C, U);
   if (mode == MODE_EVICT) {
-    hipLaunchKernelGGL(keep_count<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a);
-    hipLaunchKernelGGL(keep_emit<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a);
+    { TraceScope tr(kTrKeepCount, s);
+      hipLaunchKernelGGL(keep_count<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a); }
+    { TraceScope tr(kTrKeepEmit, s);
+      hipLaunchKernelGGL(keep_emit<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a); }
   } else {
-    hipLaunchKernelGGL(keep_count<MODE_ERASE>, grid, dim3(kChunkThreads), 0, s, a);
-    hipLaunchKernelGGL(keep_emit<MODE_ERASE>, grid, dim3(kChunkThreads), 0, s, a);
+    { TraceScope tr(kTrKeepCount, s);
+      hipLaunchKernelGGL(keep_count<MODE_ERASE>, grid, dim3(kChunkThreads), 0, s, a); }
+    { TraceScope tr(kTrKeepEmit, s);
+      hipLaunchKernelGGL(keep_emit<MODE_ERASE>, grid, dim3(kChunkThreads), 0, s, a); }
   }
+}
+
+static void launch_move(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s) {
+  const int U = c->B * c->Hkv;
   const long long items = (long long)U * ((a.Mk + a.move_rows - 1) / a.move_rows);
-  const int blocks = (int)(items < 4096 ? items : 4096);
+  const int blocks = (int)(items < 1024 ? items : 1024);  // persistent: 4 per CU
+  TraceScope tr(kTrCompactMove, s);
   hipLaunchKernelGGL(compact_move, dim3(blocks), dim3(kMoveThreads), 0, s, a, U,
                      mode == MODE_EVICT ? 1 : 0);
+}
+
+// Eviction plan: selection, destinations, evicted positions, staging.  Reads the
+// cache, writes only the workspace and the caller's outputs.
+static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const int32_t* t,
+                          int32_t M, int32_t* evicted_pos, int32_t max_evict,
+                          int32_t* n_evicted, void* ws, hipStream_t s) {
+  KeepArgs a = keep_args(cache, L, ws);
+  a.tq = t;
+  a.evicted_pos = evicted_pos;
+  a.max_evict = max_evict;
+  a.n_out = n_evicted;
+  const size_t lds_keys = ((size_t)cache->cap + cache->cap / 32 + 1) * sizeof(uint32_t);
+  if (lds_keys <= plan_lds_limit()) {
+    PlanArgs pa;
+    pa.log_beta = cache->log_beta;
+    pa.pos = cache->pos;
+    pa.len = cache->len;
+    pa.tq = t;
+    pa.info = a.info;
+    pa.keep_src = a.keep_src;
+    pa.evicted_pos = evicted_pos;
+    pa.n_out = n_evicted;
+    pa.scratch = a.scratch;
+    pa.k = cache->k;
+    pa.v = cache->v;
+    pa.cap = cache->cap;
+    pa.Hkv = cache->Hkv;
+    pa.M = M;
+    pa.Mk = a.Mk;
+    pa.max_evict = max_evict;
+    pa.row_bytes = a.row_bytes;
+    pa.srow = a.srow;
+    pa.move_rows = a.move_rows;
+    TraceScope tr(kTrEvictSelect, s);
+    hipLaunchKernelGGL(evict_plan_lds, dim3(cache->B * cache->Hkv), dim3(kSelThreads), lds_keys, s,
+                       pa);
+  } else {
+    {
+      TraceScope tr(kTrEvictSelect, s);
+      hipLaunchKernelGGL(evict_select, dim3(cache->B * cache->Hkv), dim3(kSelThreads), 0, s,
+                         cache->log_beta, cache->pos, cache->len, cache->cap, cache->Hkv, t, M,
+                         a.info, n_evicted);
+    }
+    launch_keep_chunks(cache, a, MODE_EVICT, s);
+  }
   return launch_status();
+}
+
+static int32_t evict_validate(const kvb_cache* cache, int32_t M, size_t ws_bytes, const void* ws,
+                              CompactLayout& L) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (M < 0) return KVB_EINVAL;
+  L = compact_layout(cache, M < cache->cap ? M : cache->cap);
+  if (!ws || ws_bytes < L.total) return KVB_EWORKSPACE;
+  return KVB_OK;
 }
 
 }  // namespace kvb
@@ -563,26 +883,34 @@ extern "C" size_t kv_erase_workspace(const kvb_cache* cache) {
   return compact_layout(cache, cache->cap).total;
 }
 
+extern "C" int32_t kv_evict_plan(const kvb_cache* cache, const int32_t* t, int32_t M,
+                                 int32_t* evicted_pos, int32_t max_evict, int32_t* n_evicted,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  CompactLayout L;
+  int32_t st = evict_validate(cache, M, ws_bytes, ws, L);
+  if (st) return st;
+  if (!t || max_evict < 0 || (evicted_pos && max_evict == 0)) return KVB_EINVAL;
+  if ((st = check_device())) return st;
+  return evict_plan(cache, L, t, M, evicted_pos, max_evict, n_evicted, ws, (hipStream_t)stream);
+}
+
+extern "C" int32_t kv_evict_apply(const kvb_cache* cache, int32_t M, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  CompactLayout L;
+  int32_t st = evict_validate(cache, M, ws_bytes, ws, L);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  launch_move(cache, keep_args(cache, L, ws), MODE_EVICT, (hipStream_t)stream);
+  return launch_status();
+}
+
 extern "C" int32_t kv_evict_to_budget(const kvb_cache* cache, const int32_t* t, int32_t M,
                                       int32_t* evicted_pos, int32_t max_evict,
                                       int32_t* n_evicted, void* ws, size_t ws_bytes,
                                       void* stream) {
-  int32_t st = check_cache(cache, true);
+  int32_t st = kv_evict_plan(cache, t, M, evicted_pos, max_evict, n_evicted, ws, ws_bytes, stream);
   if (st) return st;
-  if (!t || M < 0 || max_evict < 0 || (evicted_pos && max_evict == 0)) return KVB_EINVAL;
-  const CompactLayout L = compact_layout(cache, M < cache->cap ? M : cache->cap);
-  if (!ws || ws_bytes < L.total) return KVB_EWORKSPACE;
-  if ((st = check_device())) return st;
-  hipStream_t s = (hipStream_t)stream;
-  KeepArgs a = keep_args(cache, L, ws);
-  a.tq = t;
-  a.evicted_pos = evicted_pos;
-  a.max_evict = max_evict;
-  a.n_out = n_evicted;
-  hipLaunchKernelGGL(evict_select, dim3(cache->B * cache->Hkv), dim3(kSelThreads), 0, s,
-                     cache->log_beta, cache->pos, cache->len, cache->cap, cache->Hkv, t, M,
-                     a.info, n_evicted);
-  return launch_compaction(cache, a, MODE_EVICT, s);
+  return kv_evict_apply(cache, M, ws, ws_bytes, stream);
 }
 
 extern "C" int32_t kv_erase_ranges(const kvb_cache* cache, const int32_t* ranges,
@@ -600,5 +928,7 @@ extern "C" int32_t kv_erase_ranges(const kvb_cache* cache, const int32_t* ranges
   a.n_ranges = n_ranges;
   a.R = R;
   a.n_out = n_erased;
-  return launch_compaction(cache, a, MODE_ERASE, s);
+  launch_keep_chunks(cache, a, MODE_ERASE, s);
+  launch_move(cache, a, MODE_ERASE, s);
+  return launch_status();
 }

@@ -99,9 +99,10 @@ size_t asm_lookup_merge_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *   s_i   = scale * (q[b][h] . k_i) + (t[b] - pos_i) * log_beta_i
  *           (the bias term is 0 when t[b] == pos_i or log_beta is NULL)
  *   out   = sum_i e^{s_i} v_i / sum_i e^{s_i},   lse = log sum_i e^{s_i}.
- * The live slots are cut into num_splits contiguous blocks; each block yields a
- * partial state (a, m, Z) (a normalised over the block, m its max logit,
- * Z = sum e^{s-m}), and the states are combined with the merge operator
+ * The live slots are cut into 32-slot tiles dealt to num_splits splits (round
+ * robin for D = 128, contiguous runs otherwise); each split yields a partial
+ * state (a, m, Z) (a normalised over its tiles, m its max logit, Z = sum e^{s-m}),
+ * and the states are combined with the merge operator
  * ((Z_A a_A + Z_B a_B)/(Z_A + Z_B), Z_A + Z_B) in split order (deterministic).
  * An empty head (len == 0, or every weight 0) gives out = 0, lse = -inf.
  *
@@ -114,13 +115,26 @@ size_t asm_lookup_merge_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *   num_splits 0 = kv_attn_decode_splits(); else 1..4096
  *   out        [B][Hq][D] float32;  lse [B][Hq] float32
  *   ws         workspace of kv_attn_decode_workspace(cache, Hq, num_splits) bytes;
- *              after the call it holds the partial states
- *              [B][Hq][num_splits][D + 2] float32 (a[D], m, Z) at byte offset 256.
+ *              after the call it holds the split states: a [B][Hq][num_splits][D]
+ *              float32 at byte offset 256, then (m, Z) [B][Hq][num_splits][2]
+ *              float32 at the next 256-byte boundary.
  */
 int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq, const int32_t* t,
                        float scale, const void* k_new, const void* v_new,
                        const float* log_beta_new, int32_t num_splits, float* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Append one token per KV head: the same append kv_attn_decode performs when
+ * given k_new (slot len, pos = t[b], len += 1; a full head is skipped).  For
+ * callers that start eviction planning (kv_evict_plan) as soon as the token is in
+ * the cache, concurrently with the attention that follows.
+ *   k_new, v_new [B][Hkv][D] cache dtype; log_beta_new [B][Hkv] f32 (required iff
+ *   cache->log_beta != NULL); t [B] int32; ws: at least 256 bytes (status word).
+ */
+int32_t kv_append(const kvb_cache* cache, const void* k_new, const void* v_new,
+                  const float* log_beta_new, const int32_t* t, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /*
  * Evict every head over budget to exactly M live slots, then compact in place
@@ -146,6 +160,20 @@ int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq, const 
 int32_t kv_evict_to_budget(const kvb_cache* cache, const int32_t* t, int32_t M,
                            int32_t* evicted_pos, int32_t max_evict, int32_t* n_evicted,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_evict_to_budget in two phases, so that eviction can overlap attention.
+ * kv_evict_plan selects the evicted slots and the destination of every kept row,
+ * writes evicted_pos / n_evicted, and copies into ws the few kept rows whose
+ * source a later move would overwrite; it reads the cache and does not modify it.
+ * kv_evict_apply then moves the rows and sets len.  Use the same cache, M and ws
+ * for both, apply ordered after plan; between them the cache may be read (e.g. by
+ * kv_attn_decode without k_new) but not written.
+ */
+int32_t kv_evict_plan(const kvb_cache* cache, const int32_t* t, int32_t M, int32_t* evicted_pos,
+                      int32_t max_evict, int32_t* n_evicted, void* ws, size_t ws_bytes,
+                      void* stream);
+int32_t kv_evict_apply(const kvb_cache* cache, int32_t M, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Erase position ranges from every KV head of a sequence and compact in place
@@ -186,6 +214,24 @@ int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int3
                          int32_t K, const float* self_out, const float* self_lse, float* out,
                          float* out_lse, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * Kernel timing (a measurement aid; off by default; not thread-safe).
+ * kvb_trace_enable(capacity, mask) creates `capacity` HIP event pairs; from then
+ * on every launch of a kernel selected by `mask` records one pair on the launch
+ * stream around that launch, until the pairs run out.  mask bits: 1 attention
+ * split kernel, 2 split merge, 4 append, 8 eviction select, 16 keep count,
+ * 32 keep emit, 64 compaction move, 128 ASM lookup, 256 ASM finalize.
+ * kvb_trace_read waits for the recorded pairs and writes, for the first `max`,
+ * the kernel bit and the elapsed milliseconds (-1 if unavailable); it returns
+ * how many it wrote (host arrays).  kvb_trace_reset reuses the pairs from the
+ * start; kvb_trace_disable destroys them.  Returns KVB_OK, KVB_EINVAL
+ * (capacity outside 0..2^20) or KVB_EDEVICE.
+ */
+int32_t kvb_trace_enable(int32_t capacity, int32_t kernel_mask);
+int32_t kvb_trace_read(int32_t* kernel_ids, float* ms, int32_t max);
+void kvb_trace_reset(void);
+void kvb_trace_disable(void);
 
 #ifdef __cplusplus
 }

@@ -224,13 +224,15 @@ def device_cache(w: Workload, layer: int, n: int | None = None, cap: int | None 
                  device: str = "cuda", out: dict | None = None):
     """Draw one layer's cache on the device.  Deterministic in (seed, layer).
 
+    The default capacity is n + steps rounded up to a multiple of 32 slots.
+
     Returns a dict of torch tensors: k, v [B][Hkv][cap][D] (bfloat16 or float32),
     log_beta [B][Hkv][cap] float32 or None, pos int32, len int32.
     If ``out`` is given its tensors are filled in place.
     """
     torch = _torch()
     n = w.ctx if n is None else n
-    cap = n + w.steps if cap is None else cap
+    cap = ceil_div(n + w.steps, 32) * 32 if cap is None else cap
     B, H, D = w.batch, w.hkv, w.head_dim
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     g = torch.Generator(device=device)
