@@ -94,7 +94,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--serial", action="store_true",
                     help="run each layer's eviction on the attention stream (no overlap)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy kernel 5 times (scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(5):
+            torch.mul(x, 1.0, out=y)        # elementwise kernel: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "elementwise copy", "bytes_read": 1 << 30,
+                          "bytes_written": 1 << 30, "launches": 5}))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path shards by KV head with no exchange; see DESIGN.md).",
