@@ -93,7 +93,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--serial", action="store_true",
-                    help="run each layer's eviction on the attention stream (no overlap)")
+                    help="run each layer's eviction planning on the attention stream (no overlap)")
+    ap.add_argument("--fused", action="store_true",
+                    help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
+                         "of attention followed by a separate compaction pass")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy kernel 5 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -153,15 +156,21 @@ def main():
                 d[k][:, :, :M].copy_(p[k])
             d["len"].fill_(w.ctx)
 
-    # Per layer: append the decode token, then attention over the whole cache.
-    # Eviction planning only reads log beta and positions, so it starts as soon as
-    # the token is appended and runs beside the attention; the row moves rewrite
-    # the cache and wait for that layer's attention.  Layer l+1's attention waits
-    # for neither.  The side stream has default priority and is joined at the end.
+    # Per layer: append the decode token, then plan the eviction (reads log beta and
+    # positions only) on a side stream.  Default: attention over the whole cache
+    # beside the planner; the compaction pass (re-reads the kept rows) follows on
+    # the side stream, beside the next layer's attention.  --fused: attention over
+    # the tiles below the destination boundary runs beside the planner; the rest
+    # waits for the plan and writes every kept row to its compacted slot from the
+    # data it has loaded.  Layer l+1's
+    # work starts after layer l's attention (its inputs would come from it).  The
+    # side stream has default priority and is joined at the end.
     main = torch.cuda.current_stream()
     side = main if args.serial else torch.cuda.Stream()
     appended = [torch.cuda.Event() for _ in range(L)]
+    planned = [torch.cuda.Event() for _ in range(L)]
     attended = [torch.cuda.Event() for _ in range(L)]
+    fused = args.fused
 
     def step():
         for layer in range(L):
@@ -172,6 +181,17 @@ def main():
                 side.wait_event(appended[layer])
             kvb.kv_evict_plan(kvs[layer], t, M, evicted_pos=first_ev[layer],
                               n_evicted=nev[layer], ws=ws_e, stream=side)
+            if fused:
+                kvb.kv_attn_decode_compact(kvs[layer], q, t, M, ws_e, num_splits=args.splits,
+                                           phase=1, out=outs[layer], lse=lses[layer], ws=ws_a,
+                                           stream=main)
+                if side is not main:
+                    planned[layer].record(side)
+                    main.wait_event(planned[layer])
+                kvb.kv_attn_decode_compact(kvs[layer], q, t, M, ws_e, num_splits=args.splits,
+                                           phase=2, out=outs[layer], lse=lses[layer], ws=ws_a,
+                                           stream=main)
+                continue
             kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=outs[layer],
                                lse=lses[layer], ws=ws_a, stream=main)
             if side is not main:
@@ -204,7 +224,7 @@ def main():
                 kn0[b, g].view(torch.int16).numpy().view(np.uint16),
                 vn0[b, g].view(torch.int16).numpy().view(np.uint16), float(lb0[b, g])))
 
-    kvb.trace_enable(args.steps * L + 16, ("attn_split",))
+    kvb.trace_enable(2 * args.steps * L + 16, ("attn_split", "attn_fused"))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     times = []
@@ -216,8 +236,11 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
-    split_ms = [ms for name, ms in kvb.trace_read() if name == "attn_split"]
+    trace = kvb.trace_read()
     kvb.trace_disable()
+    # per layer: the attention split launch(es) of that layer (fused: both phases)
+    split_ms = [ms for name, ms in trace if name == "attn_split"]
+    fused_ms = [ms for name, ms in trace if name == "attn_fused"]
 
     # sanity: every head evicted to M; moved rows from the first evicted position
     moved = 0
@@ -229,14 +252,25 @@ def main():
     total_b = L * attn_b + algorithmic_bytes(w, n, moved)[1]
     ms_per_step = sum(times) / len(times)
     gbps = total_b / (ms_per_step * 1e-3) / 1e9
-    split_avg = sum(split_ms) / len(split_ms)
-    split_gbps = attn_b / (split_avg * 1e-3) / 1e9
+    if fused:
+        # the fused pair reads every row once and writes the moved rows once
+        assert len(split_ms) == len(fused_ms)
+        unit_b = attn_b + (moved // L) * (2 * w.head_dim * w.elem_bytes + 8)
+        pair = [a + b for a, b in zip(split_ms, fused_ms)]
+        split_avg = sum(pair) / len(pair)
+        kernel = "attn_split_pipe128<G=4> phases 1+2 (attention + compaction writes)"
+    else:
+        unit_b = attn_b
+        split_avg = sum(split_ms) / len(split_ms)
+        kernel = "attn_split_pipe128<G=4>"
+    split_gbps = unit_b / (split_avg * 1e-3) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         src = os.path.join(ROOT, "bounded_decode_attention_amd", "csrc", "attn_decode.hip")
-        if tr.get("source_sha") == source_digest(src) and tr.get("splits") == splits:
+        if (tr.get("source_sha") == source_digest(src) and tr.get("splits") == splits
+                and tr.get("fused", False) == fused):
             traffic = tr.get("traffic_bytes")
 
     line = {
@@ -247,16 +281,20 @@ def main():
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "ctx": w.ctx, "budget": M, "layers": L,
                    "kv_splits": splits,
-                   "eviction_stream": "serial" if args.serial else "overlapped"},
+                   "eviction_stream": "serial" if args.serial else "overlapped",
+                   "compaction": "fused" if fused else "separate pass"},
         "kv_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": total_b, "moved_rows_per_step": moved,
-        "roofline": {"bound": "hbm", "kernel": "attn_split_mfma<D=128,G=4>",
+        "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "bytes_per_launch": attn_b, "avg_launch_ms": round(split_avg, 5),
+                     "bytes_per_launch": unit_b, "avg_launch_ms": round(split_avg, 5),
                      "launches": len(split_ms)},
         "cpu_baseline": None,
     }
+    if fused:
+        line["roofline"]["phase_ms"] = [round(sum(split_ms) / len(split_ms), 5),
+                                        round(sum(fused_ms) / len(fused_ms), 5)]
     if host_units:
         line["cpu_baseline"] = cpu_baseline(w, host_units, w.ctx, M, args.cpu_seconds)
     print(json.dumps(line), flush=True)

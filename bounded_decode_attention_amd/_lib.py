@@ -52,6 +52,8 @@ def library():
             "kv_evict_plan": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
             "kv_evict_apply": (I32, [CP, I32, P, SZ, P]),
             "kv_append": (I32, [CP, P, P, P, P, P, SZ, P]),
+            "kv_attn_decode_compact": (I32, [CP, P, I32, P, F, I32, I32, I32, P, P, P, SZ, P, SZ,
+                                             P]),
             "kv_erase_ranges": (I32, [CP, P, P, I32, P, P, SZ, P]),
             "asm_lookup_merge": (I32, [P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, P, P,
                                        SZ, P]),
@@ -254,6 +256,29 @@ def kv_evict_apply(cache: KVCache, M: int, ws, stream=None):
     _check(st, "kv_evict_apply")
 
 
+def kv_attn_decode_compact(cache: KVCache, q, t, M: int, ws_evict, scale: float = 0.0,
+                           num_splits: int = 0, phase: int = 0, out=None, lse=None, ws=None,
+                           stream=None):
+    """Attention + the planned compaction in one pass (plan: kv_evict_plan with the
+    same M and ws_evict).  phase 0 = all; 1 = first tiles only; 2 = the rest.
+    Returns (out, lse)."""
+    _need(q, "q", cache.k.dtype)
+    _need(t, "t", torch.int32)
+    _need(ws_evict, "ws_evict", torch.uint8)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = _ws(ws, kv_attn_decode_workspace(cache, Hq, num_splits), q.device)
+    st = library().kv_attn_decode_compact(cache.desc, _ptr(q), Hq, _ptr(t), float(scale), int(M),
+                                          int(num_splits), int(phase), _ptr(out), _ptr(lse),
+                                          _ptr(ws), ws.numel(), _ptr(ws_evict), ws_evict.numel(),
+                                          _stream(stream))
+    _check(st, "kv_attn_decode_compact")
+    return out, lse
+
+
 def kv_erase_ranges(cache: KVCache, ranges, n_ranges, n_erased=None, ws=None, stream=None):
     """Erase half-open position ranges ([B][R][2] int32) from every head; compact in place."""
     _need(ranges, "ranges", torch.int32)
@@ -302,7 +327,7 @@ def asm_lookup_merge(q, centroids, abar, log_zbar, self_out, self_lse, out=None,
 
 TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "keep_count": 16, "keep_emit": 32, "compact_move": 64, "asm_lookup": 128,
-              "asm_finalize": 256}
+              "asm_finalize": 256, "attn_fused": 512}
 
 
 def trace_enable(capacity: int, kernels=("attn_split",)):

@@ -27,6 +27,8 @@
 //         an LDS copy of the V tile (written with coalesced 16-byte stores); LDS rows
 //         are permuted and padded so that the four lane groups read four disjoint
 //         32-byte bank groups.
+#include <string.h>
+
 #include "common.h"
 
 namespace kvb {
@@ -43,6 +45,15 @@ struct AttnArgs {
   float* part_ml;  // [B][Hq][P][2]  (m, Z)
   int32_t B, Hkv, cap, D, Hq, G, P;
   float scale_log2;  // scale * log2(e)
+  // tile range of this launch and its first split index (pipelined kernel): splits
+  // p_off .. p_off + gridDim.x - 1 take tiles tile_lo, tile_lo + 1, ... round robin
+  int32_t tile_lo, tile_hi, p_off;
+  // fused compaction (MOVE launches only)
+  FusedPlan plan;
+  void* kw;  // K, V written through these (the same buffers as k, v)
+  void* vw;
+  float* lbw;
+  int32_t* posw;
 };
 
 // ------------------------------------------------------------------ append
@@ -315,19 +326,28 @@ struct KTile {
   u32x4 k[2][4];
   float lb[2][4];
   int ps[2][4];
+  uint32_t mk;  // fused compaction: the tile's keep mask and first destination
+  int bs;
 };
 
 // Issues every load of one tile with no branches (the waitcnt pass then keeps the
 // other stage's loads in flight).  Rows past the split end are clamped to its last
 // row (cache hits); with VEC (capacity % 4 == 0) log beta and pos are read four at
 // a time from base min(r0, cap - 4), which equals r0 for every slot below cap.
-template <bool VEC>
+template <bool VEC, bool MOVE>
 __device__ __forceinline__ void issue_tile128(const uint16_t* kb, const uint16_t* vb,
                                               const float* lbb, const int32_t* pb, int tb,
                                               int end, int cap, int lane, KTile& t,
-                                              lds_u8* __restrict__ vlds) {
+                                              lds_u8* __restrict__ vlds, const uint32_t* tmask,
+                                              const int32_t* tbase) {
   const int lg = lane >> 4, lc = lane & 15;
   const int last = end - 1;
+  if constexpr (MOVE) {
+    // with the tile's own loads, so the move step adds no wait of its own
+    const int tl = min(tb, last) >> 5;
+    t.mk = tmask[tl];
+    t.bs = tbase[tl];
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = min(tb + 16 * j + lc, last);
@@ -440,8 +460,52 @@ __device__ __forceinline__ void compute_tile128(const KTile& t, const lds_u8* __
   }
 }
 
-template <int G, bool LB, bool VEC>
-__global__ __launch_bounds__(64) void attn_split_pipe128(AttnArgs a) {
+// Writes the kept rows of one tile to their compacted slots: K from the registers
+// the QK MFMA read (lane (g, c): row 16j + c, dims 32kk + 8g), V from the tile's LDS
+// block (lane l of block i: row 4i + l/16, 16-byte chunk l%16), log beta and pos
+// from the bias registers (lanes with c == 0: rows 16j + 4g + r).  Destination of
+// tile row r: base + number of kept rows of the tile before r.
+template <bool LB>
+__device__ __forceinline__ void move_tile128(const KTile& t, const lds_u8* __restrict__ vlds,
+                                             uint32_t mask, int base, int lane, uint16_t* kw,
+                                             uint16_t* vw, float* lbw, int32_t* pw) {
+  const int lg = lane >> 4, lc = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * j + lc;
+    if ((mask >> r) & 1u) {
+      const int dst = base + __popc(mask & ((1u << r) - 1u));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) *(u32x4*)(kw + (size_t)dst * 128 + 32 * kk + 8 * lg) = t.k[j][kk];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + lg;
+    if ((mask >> r) & 1u) {
+      const int dst = base + __popc(mask & ((1u << r) - 1u));
+      typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+      *(u32x4*)(vw + (size_t)dst * 128 + 8 * lc) = *(lds_u32x4*)(vlds + i * kVBlk + 16 * lane);
+    }
+  }
+  if (lc == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * j + 4 * lg + rr;
+        if ((mask >> r) & 1u) {
+          const int dst = base + __popc(mask & ((1u << r) - 1u));
+          if (LB) lbw[dst] = t.lb[j][rr];
+          pw[dst] = t.ps[j][rr];
+        }
+      }
+  }
+}
+
+template <int G, bool LB, bool VEC, bool MOVE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_split_pipe128(AttnArgs a) {
   static_assert(2 * G <= 16, "group too large for the hi/lo column split");
   __shared__ __attribute__((aligned(16))) unsigned char vbufA_[8 * kVBlk];
   __shared__ __attribute__((aligned(16))) unsigned char vbufB_[8 * kVBlk];
@@ -484,22 +548,90 @@ __global__ __launch_bounds__(64) void attn_split_pipe128(AttnArgs a) {
   // Tiles in pairs (A, B) with one loop exit, so each register set keeps its
   // registers and the waitcnt pass can leave the other stage's loads pending.
   KTile tA, tB;
-  // Split p takes tiles p, p + P, p + 2P, ... of the head (round-robin), so the
+  // Split p takes tiles lo + p, lo + p + P, ... of the head (round-robin), so the
   // waves of one head read neighbouring tiles at the same time.
-  const int T = (n + 31) >> 5;
-  const int ntiles = p < T ? (T - p + a.P - 1) / a.P : 0;
-  const int step = 32 * a.P;
+  const int Pl = gridDim.x;
+  const int T = min((n + 31) >> 5, a.tile_hi);
+  const int t_first = a.tile_lo + p;
+  const int ntiles = t_first < T ? (T - t_first + Pl - 1) / Pl : 0;
+  const int step = 32 * Pl;
+  // fused compaction: this head's plan
+  bool mv = false;
+  const uint32_t* tmask = nullptr;
+  const int32_t* tbase = nullptr;
+  uint16_t* kw = nullptr;
+  uint16_t* vw = nullptr;
+  float* lbw = nullptr;
+  int32_t* pw = nullptr;
+  if (MOVE) {
+    mv = a.plan.info[u].mode == MODE_EVICT;
+    tmask = a.plan.tile_mask + (size_t)u * a.plan.Tc;
+    tbase = a.plan.tile_base + (size_t)u * a.plan.Tc;
+    kw = (uint16_t*)a.kw + (size_t)u * a.cap * 128;
+    vw = (uint16_t*)a.vw + (size_t)u * a.cap * 128;
+    lbw = LB ? a.lbw + (size_t)u * a.cap : nullptr;
+    pw = a.posw + (size_t)u * a.cap;
+  }
+  auto moves = [&](const KTile& tt, const lds_u8* __restrict__ vl) {
+    if (MOVE && mv) {
+      // tile-uniform values: keep them in scalar registers
+      const uint32_t m = __builtin_amdgcn_readfirstlane(tt.mk);
+      if (m) move_tile128<LB>(tt, vl, m, __builtin_amdgcn_readfirstlane(tt.bs), lane, kw, vw, lbw, pw);
+    }
+  };
   if (ntiles > 0) {
-    int tb = 32 * p;
-    issue_tile128<VEC>(kb, vb, lbb, pb, tb, end, a.cap, lane, tA, vbufA);
+    int tb = 32 * t_first;
+    issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb, end, a.cap, lane, tA, vbufA, tmask, tbase);
     for (int k = 0; k < (ntiles >> 1); ++k) {
-      issue_tile128<VEC>(kb, vb, lbb, pb, tb + step, end, a.cap, lane, tB, vbufB);
+      issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + step, end, a.cap, lane, tB, vbufB, tmask, tbase);
       compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
-      issue_tile128<VEC>(kb, vb, lbb, pb, tb + 2 * step, end, a.cap, lane, tA, vbufA);
+      moves(tA, vbufA);
+      issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + 2 * step, end, a.cap, lane, tA, vbufA, tmask,
+                               tbase);
       compute_tile128<G>(tB, vbufB, tb + step, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      moves(tB, vbufB);
       tb += 2 * step;
     }
-    if (ntiles & 1) compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+    if (ntiles & 1) {
+      compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      moves(tA, vbufA);
+    }
+  }
+  // staged rows (source below the attended boundary): scratch -> destination.
+  // This split copies entries p, p + Pl, ...; each row is 32 pieces of 16 bytes
+  // (K then V) plus an 8-byte tail, and four pieces per lane are loaded before
+  // any is stored, so a few round trips cover the split's share.
+  if (MOVE && mv) {
+    const int ns = a.plan.stage_n[u];
+    const int ne = ns > p ? (ns - p + Pl - 1) / Pl : 0;
+    const int2* sl = a.plan.stage_list + (size_t)u * a.plan.Mk;
+    const unsigned char* sbase = a.plan.scratch + (size_t)u * a.plan.Mk * a.plan.srow;
+    constexpr int kPer = 4;
+    for (int q0 = 0; q0 < 32 * ne; q0 += 64 * kPer) {
+      u32x4 x[kPer];
+      int dst[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int q = q0 + 64 * r + lane;
+        const int e = min(q >> 5, ne - 1), pc = q & 31;
+        const int2 sd = sl[p + e * Pl];
+        dst[r] = q < 32 * ne ? sd.y : -1;
+        x[r] = *(const u32x4*)(sbase + (size_t)sd.y * a.plan.srow + 16 * pc);
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int pc = (q0 + 64 * r + lane) & 31;
+        if (dst[r] >= 0)
+          *(u32x4*)((pc < 16 ? kw : vw) + (size_t)dst[r] * 128 + 8 * (pc & 15)) = x[r];
+      }
+    }
+    for (int e = lane; e < ne; e += 64) {
+      const int d = sl[p + e * Pl].y;
+      const int32_t* tl = (const int32_t*)(sbase + (size_t)d * a.plan.srow + 256 + 256);
+      const int32_t l0 = tl[0], p0 = tl[1];
+      if (LB) lbw[d] = __int_as_float(l0);
+      pw[d] = p0;
+    }
   }
 
   lsum += __shfl_xor(lsum, 16, 64);
@@ -512,7 +644,7 @@ __global__ __launch_bounds__(64) void attn_split_pipe128(AttnArgs a) {
     for (int i = 0; i < 4; ++i) acc[nb][i] = (acc[nb][i] + __shfl(acc[nb][i], src, 64)) * inv;
   if (lc < G) {
     const int h = g * G + lc;
-    const size_t sidx = ((size_t)(b * a.Hq + h)) * a.P + p;
+    const size_t sidx = ((size_t)(b * a.Hq + h)) * a.P + a.p_off + p;
     float* pa = a.part_a + sidx * 128;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) *(f32x4*)(pa + 16 * nb + 4 * lg) = acc[nb];
@@ -626,7 +758,9 @@ constexpr int kMergeMaxP = 4096;
 
 __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
                                                             const float* part_ml, int P, int D,
-                                                            float* out, float* lse) {
+                                                            float* out, float* lse,
+                                                            const UnitInfo* info, int32_t* len,
+                                                            int G) {
   __shared__ float w[kMergeMaxP];
   __shared__ float red[kMergeThreads];
   __shared__ float gsum[kMergeThreads];
@@ -683,6 +817,11 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     out[(size_t)bh * D + tid] = W > 0.f ? acc / W : 0.f;
   }
   if (tid == 0) lse[bh] = W > 0.f ? M + __logf(W) : kNegInf;
+  // fused compaction: the head's new length (every split has read the old one)
+  if (info && tid == 0 && bh % G == 0) {
+    const int u = bh / G;
+    if (info[u].mode == MODE_EVICT) len[u] = info[u].kept;
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -702,10 +841,10 @@ static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s
 #define KVB_PIPE_CASE(GG)                                                                  \
   if (c->D == 128 && a.G == GG) {                                                          \
     const bool lb = c->log_beta != nullptr, vec = c->cap % 4 == 0 && c->cap >= 4;         \
-    if (lb && vec) hipLaunchKernelGGL((attn_split_pipe128<GG, true, true>), grid, dim3(64), 0, s, a);   \
-    else if (lb) hipLaunchKernelGGL((attn_split_pipe128<GG, true, false>), grid, dim3(64), 0, s, a);   \
-    else if (vec) hipLaunchKernelGGL((attn_split_pipe128<GG, false, true>), grid, dim3(64), 0, s, a);  \
-    else hipLaunchKernelGGL((attn_split_pipe128<GG, false, false>), grid, dim3(64), 0, s, a);          \
+    if (lb && vec) hipLaunchKernelGGL((attn_split_pipe128<GG, true, true, false>), grid, dim3(64), 0, s, a);   \
+    else if (lb) hipLaunchKernelGGL((attn_split_pipe128<GG, true, false, false>), grid, dim3(64), 0, s, a);   \
+    else if (vec) hipLaunchKernelGGL((attn_split_pipe128<GG, false, true, false>), grid, dim3(64), 0, s, a);  \
+    else hipLaunchKernelGGL((attn_split_pipe128<GG, false, false, false>), grid, dim3(64), 0, s, a);          \
     return KVB_OK;                                                                         \
   }
     KVB_PIPE_CASE(1) KVB_PIPE_CASE(2) KVB_PIPE_CASE(4) KVB_PIPE_CASE(8)
@@ -815,6 +954,9 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   a.G = G;
   a.P = P;
   a.scale_log2 = (scale > 0.f ? scale : 1.0f / sqrtf((float)cache->D)) * kLog2e;
+  a.tile_lo = 0;
+  a.tile_hi = 1 << 30;
+  a.p_off = 0;
 
   if (k_new) {
     TraceScope tr(kTrAppend, s);
@@ -830,6 +972,120 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   }
   TraceScope tr(kTrAttnMerge, s);
   hipLaunchKernelGGL(attn_merge, dim3(cache->B * Hq), dim3(kMergeThreads), 0, s, a.part_a,
-                     a.part_ml, P, cache->D, out, lse);
+                     a.part_ml, P, cache->D, out, lse, (const UnitInfo*)nullptr, (int32_t*)nullptr,
+                     G);
+  return launch_status();
+}
+
+// ------------------------------------------------------------------ fused attention + compaction
+namespace kvb {
+
+template <int G>
+static void launch_pipe_move(const kvb_cache* c, const AttnArgs& a, dim3 grid, hipStream_t s,
+                             bool move) {
+  const bool lb = c->log_beta != nullptr, vec = c->cap % 4 == 0 && c->cap >= 4;
+  if (move) {
+    if (lb && vec) hipLaunchKernelGGL((attn_split_pipe128<G, true, true, true>), grid, dim3(64), 0, s, a);
+    else if (lb) hipLaunchKernelGGL((attn_split_pipe128<G, true, false, true>), grid, dim3(64), 0, s, a);
+    else if (vec) hipLaunchKernelGGL((attn_split_pipe128<G, false, true, true>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((attn_split_pipe128<G, false, false, true>), grid, dim3(64), 0, s, a);
+  } else {
+    if (lb && vec) hipLaunchKernelGGL((attn_split_pipe128<G, true, true, false>), grid, dim3(64), 0, s, a);
+    else if (lb) hipLaunchKernelGGL((attn_split_pipe128<G, true, false, false>), grid, dim3(64), 0, s, a);
+    else if (vec) hipLaunchKernelGGL((attn_split_pipe128<G, false, true, false>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((attn_split_pipe128<G, false, false, false>), grid, dim3(64), 0, s, a);
+  }
+}
+
+static void launch_pipe_any(const kvb_cache* c, const AttnArgs& a, dim3 grid, hipStream_t s,
+                            bool move) {
+  switch (a.G) {
+    case 1: launch_pipe_move<1>(c, a, grid, s, move); break;
+    case 2: launch_pipe_move<2>(c, a, grid, s, move); break;
+    case 4: launch_pipe_move<4>(c, a, grid, s, move); break;
+    default: launch_pipe_move<8>(c, a, grid, s, move); break;
+  }
+}
+
+}  // namespace kvb
+
+extern "C" int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q, int32_t Hq,
+                                          const int32_t* t, float scale, int32_t M,
+                                          int32_t num_splits, int32_t phase, float* out,
+                                          float* lse, void* ws, size_t ws_bytes, void* ws_evict,
+                                          size_t ws_evict_bytes, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0 || M < 0) return KVB_EINVAL;
+  if (num_splits < 0 || num_splits > 4096 || phase < 0 || phase > 2) return KVB_EINVAL;
+  const int G = Hq / cache->Hkv;
+  if (!mfma_supported(cache, G) && (G > 16 || cache->D > 256)) return KVB_EUNSUPPORTED;
+  const int P = num_splits > 0 ? num_splits : auto_splits(cache);
+  if (!ws || ws_bytes < kv_attn_decode_workspace(cache, Hq, P)) return KVB_EWORKSPACE;
+  if (!ws_evict || ws_evict_bytes < kv_evict_workspace(cache, M)) return KVB_EWORKSPACE;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const bool fused = cache->dtype == KVB_BF16 && cache->D == 128 &&
+                     (G == 1 || G == 2 || G == 4 || G == 8) && P >= 2 && plan_in_lds(cache);
+  if (!fused) {
+    // same result through the unfused kernels: attention, then the planned moves
+    if (phase == 1) return KVB_OK;
+    st = kv_attn_decode(cache, q, Hq, t, scale, nullptr, nullptr, nullptr, P, out, lse, ws,
+                        ws_bytes, stream);
+    if (st) return st;
+    return kv_evict_apply(cache, M, ws_evict, ws_evict_bytes, stream);
+  }
+  // Phase 1 covers few tiles but runs beside the planner: half the splits keep
+  // enough waves in flight for it (measured on the 32K workload).
+  const int Ta = fused_za(M, cache->cap) / 32;
+  int Pa = P / 2;
+  if (Pa > Ta) Pa = Ta;
+  Pa = Pa < 1 ? 1 : (Pa > P - 1 ? P - 1 : Pa);
+  const int Pb = P - Pa;
+  const size_t S = (size_t)cache->B * Hq * P;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = cache->k;
+  a.v = cache->v;
+  a.log_beta = cache->log_beta;
+  a.pos = cache->pos;
+  a.len = cache->len;
+  a.q = q;
+  a.t = t;
+  a.part_a = (float*)((char*)ws + kWsHeader);
+  a.part_ml = (float*)((char*)ws + kWsHeader + align_up(S * cache->D * sizeof(float), 256));
+  a.B = cache->B;
+  a.Hkv = cache->Hkv;
+  a.cap = cache->cap;
+  a.D = cache->D;
+  a.Hq = Hq;
+  a.G = G;
+  a.P = P;
+  a.scale_log2 = (scale > 0.f ? scale : 1.0f / sqrtf((float)cache->D)) * kLog2e;
+  const int U = cache->B * cache->Hkv;
+  if (phase != 2) {  // tiles below the destination boundary: attention only
+    a.tile_lo = 0;
+    a.tile_hi = Ta;
+    a.p_off = 0;
+    TraceScope tr(kTrAttnSplit, s);
+    launch_pipe_any(cache, a, dim3(Pa, U), s, false);
+  }
+  if (phase != 1) {  // the remaining tiles, with their kept rows written to place
+    a.tile_lo = Ta;
+    a.tile_hi = 1 << 30;
+    a.p_off = Pa;
+    a.plan = fused_plan(cache, M, ws_evict);
+    a.kw = cache->k;
+    a.vw = cache->v;
+    a.lbw = cache->log_beta;
+    a.posw = cache->pos;
+    {
+      TraceScope tr(kTrAttnFused, s);
+      launch_pipe_any(cache, a, dim3(Pb, U), s, true);
+    }
+    TraceScope tr(kTrAttnMerge, s);
+    hipLaunchKernelGGL(attn_merge, dim3(cache->B * Hq), dim3(kMergeThreads), 0, s, a.part_a,
+                       a.part_ml, P, cache->D, out, lse, a.plan.info, cache->len, G);
+  }
   return launch_status();
 }

@@ -55,6 +55,40 @@ __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Per-head eviction plan header (workspace), written by the planners.
+enum { MODE_NOOP = 0, MODE_EVICT = 1, MODE_ERASE = 2 };
+struct UnitInfo {
+  uint64_t kstar;  // ordered 64-bit key of the threshold element
+  int32_t sstar;   // its slot
+  int32_t mode;
+  int32_t n;       // live slots before
+  int32_t kept;    // live slots after
+  int32_t pad[2];
+};
+static_assert(sizeof(UnitInfo) == 32, "UnitInfo layout");
+
+// Compaction state a fused attention launch reads from an eviction plan: per
+// 32-slot tile the keep mask and the destination of its first kept row, and the
+// kept rows whose source lies below `za` (staged in scratch by the planner).
+struct FusedPlan {
+  const UnitInfo* info;
+  const uint32_t* tile_mask;  // [U][Tc]
+  const int32_t* tile_base;   // [U][Tc]
+  const int32_t* stage_n;     // [U]
+  const int2* stage_list;     // [U][Mk]  (src, dst)
+  const unsigned char* scratch;  // [U][Mk][srow] by destination
+  int32_t Tc, Mk, srow;
+};
+
+// Host: the boundary below which a fused attention + compaction launch attends
+// before it moves any row (all destinations lie below it): M rounded up to a tile.
+inline int fused_za(int M, int cap) {
+  const int m = M < cap ? M : cap;
+  return (m + 31) / 32 * 32;
+}
+bool plan_in_lds(const kvb_cache* c);
+FusedPlan fused_plan(const kvb_cache* c, int32_t M, void* ws);
+
 // Host: 0 if the current device is gfx950, else KVB_EDEVICE (cached per device).
 int32_t check_device();
 
@@ -65,7 +99,8 @@ int32_t check_cache(const kvb_cache* c, bool need_kv);
 // launch stream around each traced kernel while enabled.
 enum TraceKernel {
   kTrAttnSplit = 1, kTrAttnMerge = 2, kTrAppend = 4, kTrEvictSelect = 8, kTrKeepCount = 16,
-  kTrKeepEmit = 32, kTrCompactMove = 64, kTrAsmLookup = 128, kTrAsmFinalize = 256
+  kTrKeepEmit = 32, kTrCompactMove = 64, kTrAsmLookup = 128, kTrAsmFinalize = 256,
+  kTrAttnFused = 512
 };
 struct TraceScope {
   TraceScope(int kernel, hipStream_t s);

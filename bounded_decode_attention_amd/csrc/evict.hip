@@ -35,17 +35,6 @@
 
 namespace kvb {
 
-enum { MODE_NOOP = 0, MODE_EVICT = 1, MODE_ERASE = 2 };
-
-struct UnitInfo {
-  uint64_t kstar;  // ordered 64-bit key of the threshold element
-  int32_t sstar;   // its slot
-  int32_t mode;
-  int32_t n;       // live slots before
-  int32_t kept;    // live slots after
-  int32_t pad[2];
-};
-static_assert(sizeof(UnitInfo) == 32, "UnitInfo layout");
 
 constexpr int kChunk = 4096;      // slots per keep_count / keep_emit workgroup
 constexpr int kChunkThreads = 256;
@@ -274,27 +263,14 @@ struct PlanArgs {
   int32_t* evicted_pos;
   int32_t* n_out;
   unsigned char* scratch;
+  uint32_t* tile_mask;  // [U][Tc]
+  int32_t* tile_base;   // [U][Tc]
+  int32_t* stage_n;     // [U]
+  int2* stage_list;     // [U][Mk]
   const void* k;
   const void* v;
-  int32_t cap, Hkv, M, Mk, max_evict, row_bytes, srow, move_rows;
+  int32_t cap, Hkv, M, Mk, max_evict, row_bytes, srow, move_rows, za, Tc;
 };
-
-__device__ void stage_row(const PlanArgs& a, int u, int src, int dst) {
-  unsigned char* s = a.scratch + ((size_t)u * a.Mk + dst) * a.srow;
-  const size_t off = ((size_t)u * a.cap + src) * a.row_bytes;
-  const u32x4* kp = (const u32x4*)((const unsigned char*)a.k + off);
-  const u32x4* vp = (const u32x4*)((const unsigned char*)a.v + off);
-  const int pieces = a.row_bytes / 16;
-  for (int i = 0; i < pieces; ++i) {
-    ((u32x4*)s)[i] = kp[i];
-    ((u32x4*)(s + a.row_bytes))[i] = vp[i];
-  }
-  int32_t* tail = (int32_t*)(s + 2 * a.row_bytes);
-  tail[0] = a.log_beta ? __float_as_int(a.log_beta[(size_t)u * a.cap + src]) : 0;
-  tail[1] = a.pos[(size_t)u * a.cap + src];
-}
-
-constexpr int kStageList = 1024;  // staged rows copied cooperatively per head
 
 __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   extern __shared__ uint32_t keys[];  // ord32 keys at skew(i)
@@ -302,7 +278,6 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   __shared__ int smem[kSelThreads / 64];
   __shared__ int out[4];
   __shared__ unsigned long long mm[2];
-  __shared__ int2 stage[kStageList];
   __shared__ int nstage;
 
   const int u = blockIdx.x;
@@ -423,64 +398,79 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   __syncthreads();
   const int sstar = out[2];
 
-  // ---- keep flags, scan, emit
+  // ---- keep flags per 32-slot tile (masks), scan, emit.  Kept rows whose source
+  // lies below za and differs from their destination are staged: any later move
+  // into [0, za) may overwrite them (za >= kept bounds every destination).
   auto keep = [&](int i) -> bool {
     const uint32_t k32 = keys[skew(i)];
     if (k32 != t32) return k32 > t32;
     const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
     return k64 > K || (k64 == K && i > sstar);
   };
+  auto tile_mask = [&](int tl) -> uint32_t {
+    uint32_t m = 0;
+    const int i0 = 32 * tl;
+    for (int s2 = 0; s2 < 32 && i0 + s2 < n; ++s2)
+      if (keep(i0 + s2)) m |= 1u << s2;
+    return m;
+  };
+  const int T = (n + 31) >> 5;
+  const int tpt = (T + kSelThreads - 1) / kSelThreads;
+  const int tl0 = min(T, tid * tpt), tl1 = min(T, tl0 + tpt);
   int kc = 0;
-  for (int i = lo; i < hi; ++i) kc += keep(i) ? 1 : 0;
+  for (int tl = tl0; tl < tl1; ++tl) kc += __popc(tile_mask(tl));
   int kept_all;
   int dst = block_excl_scan<kSelThreads>(kc, smem, kept_all);
-  int ev = lo - dst;
+  int ev = 32 * tl0 - dst;
   const int kept = min(kept_all, a.Mk);
-  for (int i = lo; i < hi; ++i) {
-    if (keep(i)) {
-      if (dst < a.Mk) {
-        a.keep_src[(size_t)u * a.Mk + dst] = i;
-        if (i != dst && i < kept && i >= (dst / a.move_rows + 1) * a.move_rows) {
-          const int slot = atomicAdd(&nstage, 1);
-          if (slot < kStageList)
-            stage[slot] = make_int2(i, dst);
-          else
-            stage_row(a, u, i, dst);  // list full: copy it here
+  int2* slist = a.stage_list + (size_t)u * a.Mk;
+  for (int tl = tl0; tl < tl1; ++tl) {
+    const uint32_t m = tile_mask(tl);
+    a.tile_mask[(size_t)u * a.Tc + tl] = m;
+    a.tile_base[(size_t)u * a.Tc + tl] = dst;
+    const int i0 = 32 * tl;
+    for (int s2 = 0; s2 < 32 && i0 + s2 < n; ++s2) {
+      const int i = i0 + s2;
+      if ((m >> s2) & 1u) {
+        if (dst < a.Mk) {
+          a.keep_src[(size_t)u * a.Mk + dst] = i;
+          if (i != dst && i < a.za) slist[atomicAdd(&nstage, 1)] = make_int2(i, dst);
         }
+        ++dst;
+      } else {
+        if (a.evicted_pos && ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
+        ++ev;
       }
-      ++dst;
-    } else {
-      if (a.evicted_pos && ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
-      ++ev;
     }
   }
   __syncthreads();
   // ---- staged rows: all threads copy 16-byte pieces (K, V) and the row tails
   {
-    const int ns = min(nstage, kStageList);
+    const int ns = min(nstage, a.Mk);
     const int ppr = a.row_bytes / 16;
     const int per = 2 * ppr + 1;
     const unsigned char* kb = (const unsigned char*)a.k + (size_t)u * a.cap * a.row_bytes;
     const unsigned char* vb = (const unsigned char*)a.v + (size_t)u * a.cap * a.row_bytes;
     for (int q = tid; q < ns * per; q += kSelThreads) {
       const int e = q / per, part = q - e * per;
-      const int src = stage[e].x, dst2 = stage[e].y;
-      unsigned char* sp = a.scratch + ((size_t)u * a.Mk + dst2) * a.srow;
+      const int2 sd = slist[e];
+      unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
       if (part < 2 * ppr) {
         const bool isv = part >= ppr;
         const int pc = isv ? part - ppr : part;
         *(u32x4*)(sp + (isv ? a.row_bytes : 0) + 16 * pc) =
-            *(const u32x4*)((isv ? vb : kb) + (size_t)src * a.row_bytes + 16 * pc);
+            *(const u32x4*)((isv ? vb : kb) + (size_t)sd.x * a.row_bytes + 16 * pc);
       } else {
         int32_t* tail = (int32_t*)(sp + 2 * a.row_bytes);
-        tail[0] = lb ? __float_as_int(lb[src]) : 0;
-        tail[1] = ps[src];
+        tail[0] = lb ? __float_as_int(lb[sd.x]) : 0;
+        tail[1] = ps[sd.x];
       }
     }
   }
   if (tid == 0) {
     UnitInfo v = {K, sstar, MODE_EVICT, n, kept, {0, 0}};
     a.info[u] = v;
+    a.stage_n[u] = min(nstage, a.Mk);
     if (a.n_out) a.n_out[u] = n - kept_all;
   }
 }
@@ -738,8 +728,8 @@ static size_t plan_lds_limit() {
 }
 
 struct CompactLayout {
-  size_t info, counts, keep_src, scratch, total;
-  int C, Mk, srow, move_rows, row_bytes;
+  size_t info, counts, keep_src, scratch, tile_mask, tile_base, stage_n, stage_list, total;
+  int C, Mk, srow, move_rows, row_bytes, Tc;
 };
 
 static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
@@ -755,11 +745,16 @@ static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
     L.move_rows = rpp * kMovePieces;
     if (L.move_rows > kMoveThreads) L.move_rows = kMoveThreads;  // one thread per row tail
   }
+  L.Tc = (c->cap + 31) / 32;
   L.info = kWsHeader;
   L.counts = L.info + align_up(U * sizeof(UnitInfo), 256);
   L.keep_src = L.counts + align_up(U * L.C * sizeof(int32_t), 256);
   L.scratch = L.keep_src + align_up(U * L.Mk * sizeof(int32_t), 256);
-  L.total = L.scratch + align_up(U * L.Mk * (size_t)L.srow, 256);
+  L.tile_mask = L.scratch + align_up(U * L.Mk * (size_t)L.srow, 256);
+  L.tile_base = L.tile_mask + align_up(U * L.Tc * sizeof(uint32_t), 256);
+  L.stage_n = L.tile_base + align_up(U * L.Tc * sizeof(int32_t), 256);
+  L.stage_list = L.stage_n + align_up(U * sizeof(int32_t), 256);
+  L.total = L.stage_list + align_up(U * L.Mk * sizeof(int2), 256);
   return L;
 }
 
@@ -822,7 +817,7 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
   a.max_evict = max_evict;
   a.n_out = n_evicted;
   const size_t lds_keys = ((size_t)cache->cap + cache->cap / 32 + 1) * sizeof(uint32_t);
-  if (lds_keys <= plan_lds_limit()) {
+  if (plan_in_lds(cache)) {
     PlanArgs pa;
     pa.log_beta = cache->log_beta;
     pa.pos = cache->pos;
@@ -843,6 +838,13 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     pa.row_bytes = a.row_bytes;
     pa.srow = a.srow;
     pa.move_rows = a.move_rows;
+    char* w = (char*)ws;
+    pa.tile_mask = (uint32_t*)(w + L.tile_mask);
+    pa.tile_base = (int32_t*)(w + L.tile_base);
+    pa.stage_n = (int32_t*)(w + L.stage_n);
+    pa.stage_list = (int2*)(w + L.stage_list);
+    pa.Tc = L.Tc;
+    pa.za = fused_za(M, cache->cap);
     TraceScope tr(kTrEvictSelect, s);
     hipLaunchKernelGGL(evict_plan_lds, dim3(cache->B * cache->Hkv), dim3(kSelThreads), lds_keys, s,
                        pa);
@@ -856,6 +858,29 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     launch_keep_chunks(cache, a, MODE_EVICT, s);
   }
   return launch_status();
+}
+
+// Whether kv_evict_plan uses the LDS planner (which also prepares the fused
+// attention + compaction path) for this cache.
+bool plan_in_lds(const kvb_cache* c) {
+  const size_t lds_keys = ((size_t)c->cap + c->cap / 32 + 1) * sizeof(uint32_t);
+  return lds_keys <= plan_lds_limit();
+}
+
+FusedPlan fused_plan(const kvb_cache* c, int32_t M, void* ws) {
+  const CompactLayout L = compact_layout(c, M < c->cap ? M : c->cap);
+  const char* w = (const char*)ws;
+  FusedPlan f;
+  f.info = (const UnitInfo*)(w + L.info);
+  f.tile_mask = (const uint32_t*)(w + L.tile_mask);
+  f.tile_base = (const int32_t*)(w + L.tile_base);
+  f.stage_n = (const int32_t*)(w + L.stage_n);
+  f.stage_list = (const int2*)(w + L.stage_list);
+  f.scratch = (const unsigned char*)(w + L.scratch);
+  f.Tc = L.Tc;
+  f.Mk = L.Mk;
+  f.srow = L.srow;
+  return f;
 }
 
 static int32_t evict_validate(const kvb_cache* cache, int32_t M, size_t ws_bytes, const void* ws,

@@ -176,6 +176,30 @@ int32_t kv_evict_plan(const kvb_cache* cache, const int32_t* t, int32_t M, int32
 int32_t kv_evict_apply(const kvb_cache* cache, int32_t M, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Attention and the planned compaction in one pass over the cache ([TRIM] 2.1 and
+ * 2.2): the result equals kv_attn_decode (no append) followed by kv_evict_apply,
+ * for a plan made by kv_evict_plan(cache, t, M, ..., ws_evict) with no cache write
+ * in between.  Attention reads every K/V row once; each kept row is written to its
+ * compacted slot from the data the attention already loaded, so the separate
+ * re-read of kept rows disappears.  All destinations lie below M rounded up to 32
+ * slots; those tiles are attended first (phase 1), the rest afterwards (phase 2,
+ * which also moves rows, merges the split states and sets len).
+ *   phase 0  both phases on `stream` (the plan must be complete before the call)
+ *   phase 1  attention over the first tiles only; needs no plan, so it may run
+ *            concurrently with kv_evict_plan (which only reads the cache)
+ *   phase 2  the rest; the plan must be complete; ws must hold phase 1's states
+ * Other arguments as kv_attn_decode (num_splits >= 2 for the fused kernels; the
+ * same num_splits and ws in both phases); ws_evict is the plan's workspace.
+ * Falls back to kv_attn_decode + kv_evict_apply (phase 1 then does nothing) for
+ * dtype/D/group combinations without the fused kernel or caches whose plan does not
+ * fit the single-workgroup planner.
+ */
+int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q, int32_t Hq, const int32_t* t,
+                               float scale, int32_t M, int32_t num_splits, int32_t phase,
+                               float* out, float* lse, void* ws, size_t ws_bytes, void* ws_evict,
+                               size_t ws_evict_bytes, void* stream);
+
+/*
  * Erase position ranges from every KV head of a sequence and compact in place
  * ([MEM] blocks and compression; system engineering).
  *
@@ -221,7 +245,8 @@ int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int3
  * on every launch of a kernel selected by `mask` records one pair on the launch
  * stream around that launch, until the pairs run out.  mask bits: 1 attention
  * split kernel, 2 split merge, 4 append, 8 eviction select, 16 keep count,
- * 32 keep emit, 64 compaction move, 128 ASM lookup, 256 ASM finalize.
+ * 32 keep emit, 64 compaction move, 128 ASM lookup, 256 ASM finalize, 512 the
+ * attention split kernel that also moves kept rows (kv_attn_decode_compact).
  * kvb_trace_read waits for the recorded pairs and writes, for the first `max`,
  * the kernel bit and the elapsed milliseconds (-1 if unavailable); it returns
  * how many it wrote (host arrays).  kvb_trace_reset reuses the pairs from the
