@@ -314,8 +314,7 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
 // instruction's 1 KB block), so it needs no VGPRs and no ds_write.  Instruction i
 // carries tile rows 4i..4i+3 and its block starts at i*1056 bytes: the 32-byte
 // pad puts the four lane groups of every transposed read in disjoint bank groups.
-// The two buffers are distinct arrays and the loop is unrolled by two, so each
-// stage's LDS reads wait only on that stage's own loads.
+// The two buffers are distinct arrays and the loop is unrolled by two.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -330,10 +329,10 @@ struct KTile {
   int bs;
 };
 
-// Issues every load of one tile with no branches (the waitcnt pass then keeps the
-// other stage's loads in flight).  Rows past the split end are clamped to its last
-// row (cache hits); with VEC (capacity % 4 == 0) log beta and pos are read four at
-// a time from base min(r0, cap - 4), which equals r0 for every slot below cap.
+// Issues every load of one tile with no branches.  Rows past the split end are
+// clamped to its last row (cache hits); with VEC (capacity % 4 == 0) log beta and
+// pos are read four at a time from base min(r0, cap - 4), which equals r0 for every
+// slot below cap.
 template <bool VEC, bool MOVE>
 __device__ __forceinline__ void issue_tile128(const uint16_t* kb, const uint16_t* vb,
                                               const float* lbb, const int32_t* pb, int tb,
@@ -546,7 +545,7 @@ void attn_split_pipe128(AttnArgs a) {
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Tiles in pairs (A, B) with one loop exit, so each register set keeps its
-  // registers and the waitcnt pass can leave the other stage's loads pending.
+  // registers.
   KTile tA, tB;
   // Split p takes tiles lo + p, lo + p + P, ... of the head (round-robin), so the
   // waves of one head read neighbouring tiles at the same time.
@@ -580,21 +579,30 @@ void attn_split_pipe128(AttnArgs a) {
     }
   };
   if (ntiles > 0) {
+    // Per tile: wait for its loads (the only ones outstanding), write its kept rows,
+    // issue the next tile's loads into the other register set and LDS buffer, then
+    // compute from this tile's registers and buffer while those loads are in
+    // flight.  The wait is explicit: the compiler does not order LDS reads after
+    // global_load_lds transfers into the same LDS.  The scheduling barriers keep
+    // the next tile's arithmetic from being hoisted above its wait.
     int tb = 32 * t_first;
     issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb, end, a.cap, lane, tA, vbufA, tmask, tbase);
     for (int k = 0; k < (ntiles >> 1); ++k) {
+      wait_vmem_all();
+      moves(tA, vbufA);
       issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + step, end, a.cap, lane, tB, vbufB, tmask, tbase);
       compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
-      moves(tA, vbufA);
+      wait_vmem_all();
+      moves(tB, vbufB);
       issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + 2 * step, end, a.cap, lane, tA, vbufA, tmask,
                                tbase);
       compute_tile128<G>(tB, vbufB, tb + step, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
-      moves(tB, vbufB);
       tb += 2 * step;
     }
     if (ntiles & 1) {
-      compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      wait_vmem_all();
       moves(tA, vbufA);
+      compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
     }
   }
   // staged rows (source below the attended boundary): scratch -> destination.

@@ -48,6 +48,15 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Wait for every outstanding vector memory operation (s_waitcnt vmcnt(0), other
+// counters untouched), fenced against instruction scheduling on both sides.  LDS
+// filled by global_load_lds is not tracked by the compiler's own waits.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

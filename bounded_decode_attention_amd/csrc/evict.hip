@@ -270,18 +270,23 @@ struct PlanArgs {
   const void* k;
   const void* v;
   int32_t cap, Hkv, M, Mk, max_evict, row_bytes, srow, move_rows, za, Tc;
+  int32_t vec;  // capacity % 4 == 0: log beta and pos read 16 bytes at a time
 };
+
+constexpr int kCand = 2048;  // candidate list: slots of the selected top-11-bit bucket
 
 __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   extern __shared__ uint32_t keys[];  // ord32 keys at skew(i)
-  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t hist[2048];     // histograms; tie flags; later each tile's first destination
+  __shared__ int cand[kCand];         // candidate slots; later each tile's keep mask
   __shared__ int smem[kSelThreads / 64];
   __shared__ int out[4];
   __shared__ unsigned long long mm[2];
-  __shared__ int nstage;
+  __shared__ int ncand, nflag, nstage;
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int n = min(a.len[u], a.cap);
   const int M = a.M;
   if (tid == 0) {
@@ -290,6 +295,8 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
     out[2] = -1;
     mm[0] = ~0ull;
     mm[1] = 0ull;
+    ncand = 0;
+    nflag = 0;
     nstage = 0;
   }
   if (n <= M) {
@@ -304,166 +311,329 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   const int32_t* ps = a.pos + (size_t)u * a.cap;
   const int tpos = a.tq[u / a.Hkv];
   int r = n - M;
+  auto key32 = [&](float l, int p) -> uint32_t {
+    const int d = tpos - p;
+    return ord32((!lb || d == 0) ? 0.0 : (double)d * (double)l);
+  };
 
-  // ---- pass 0: keys to LDS + histogram of the top 11 bits.  Sixteen rounds' loads
-  // are issued before any key is formed (the loop is latency bound otherwise).
+  // ---- pass 0: keys to LDS + histogram of the top 11 bits.  All of a round's
+  // loads are issued before any key is formed (the loop is latency bound otherwise).
   for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
   __syncthreads();
-  constexpr int kRounds = 16;
-  for (int i0 = tid; i0 < n; i0 += kRounds * kSelThreads) {
-    float lv[kRounds];
-    int pv[kRounds];
+  if (a.vec) {
+    // 16-byte loads: slots 4j .. 4j + 3 (every head's rows start 16-byte aligned)
+    const int nq = (n + 3) >> 2;
+    constexpr int kQ = 8;
+    for (int j0 = tid; j0 < nq; j0 += kQ * kSelThreads) {
+      f32x4 l4[kQ];
+      i32x4 p4[kQ];
 #pragma unroll
-    for (int e = 0; e < kRounds; ++e) {
-      const int i = min(i0 + e * kSelThreads, n - 1);
-      lv[e] = lb ? lb[i] : 0.f;
-      pv[e] = ps[i];
+      for (int e = 0; e < kQ; ++e) {
+        const int j = min(j0 + e * kSelThreads, nq - 1);
+        l4[e] = lb ? *(const f32x4*)(lb + 4 * j) : f32x4{0.f, 0.f, 0.f, 0.f};
+        p4[e] = *(const i32x4*)(ps + 4 * j);
+      }
+#pragma unroll
+      for (int e = 0; e < kQ; ++e) {
+        const int j = j0 + e * kSelThreads;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * j + c;
+          if (j < nq && i < n) {
+            const uint32_t k32 = key32(l4[e][c], p4[e][c]);
+            keys[skew(i)] = k32;
+            atomicAdd(&hist[k32 >> 21], 1u);
+          }
+        }
+      }
     }
+  } else {
+    constexpr int kRounds = 16;
+    for (int i0 = tid; i0 < n; i0 += kRounds * kSelThreads) {
+      float lv[kRounds];
+      int pv[kRounds];
 #pragma unroll
-    for (int e = 0; e < kRounds; ++e) {
-      const int i = i0 + e * kSelThreads;
-      if (i < n) {
-        const int d = tpos - pv[e];
-        const double k = (!lb || d == 0) ? 0.0 : (double)d * (double)lv[e];
-        const uint32_t k32 = ord32(k);
-        keys[skew(i)] = k32;
-        atomicAdd(&hist[k32 >> 21], 1u);
+      for (int e = 0; e < kRounds; ++e) {
+        const int i = min(i0 + e * kSelThreads, n - 1);
+        lv[e] = lb ? lb[i] : 0.f;
+        pv[e] = ps[i];
+      }
+#pragma unroll
+      for (int e = 0; e < kRounds; ++e) {
+        const int i = i0 + e * kSelThreads;
+        if (i < n) {
+          const uint32_t k32 = key32(lv[e], pv[e]);
+          keys[skew(i)] = k32;
+          atomicAdd(&hist[k32 >> 21], 1u);
+        }
       }
     }
   }
   __syncthreads();
   int bucket = select_bucket<kSelThreads>(hist, 2048, r, smem, out);
-  uint32_t prefix = (uint32_t)bucket;
-  // ---- passes 1, 2 over LDS
-  for (int pass = 1; pass < 3; ++pass) {
-    const int shift = pass == 1 ? 10 : 0;
-    const int bits = pass == 1 ? 11 : 10;
-    const int nb = 1 << bits;
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint32_t k32 = keys[skew(i)];
-      if ((k32 >> (shift + bits)) == prefix) atomicAdd(&hist[(k32 >> shift) & (nb - 1)], 1u);
+  const uint32_t b0 = (uint32_t)bucket;
+  const int c0 = (int)hist[b0];
+  uint32_t t32;
+  unsigned long long K;
+  if (c0 <= kCand) {
+    // ---- the bucket's slots to a list; the remaining passes and the ties use it
+    constexpr int kU = 8;  // LDS reads in flight per thread
+    for (int i0 = tid; i0 < n; i0 += kU * kSelThreads) {
+      uint32_t kk[kU];
+#pragma unroll
+      for (int e = 0; e < kU; ++e) kk[e] = keys[skew(min(i0 + e * kSelThreads, n - 1))];
+#pragma unroll
+      for (int e = 0; e < kU; ++e) {
+        const int i = i0 + e * kSelThreads;
+        if (i < n && (kk[e] >> 21) == b0) cand[atomicAdd(&ncand, 1)] = i;
+      }
     }
     __syncthreads();
-    bucket = select_bucket<kSelThreads>(hist, nb, r, smem, out);
-    prefix = (prefix << bits) | (uint32_t)bucket;
-  }
-  const uint32_t t32 = prefix;
-
-  // ---- exact keys of the float32 ties: min and max
-  for (int i = tid; i < n; i += kSelThreads) {
-    if (keys[skew(i)] != t32) continue;
-    const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
-    atomicMin(&mm[0], k64);
-    atomicMax(&mm[1], k64);
-  }
-  __syncthreads();
-  unsigned long long K = mm[0];
-  if (K != mm[1]) {
-    // distinct exact keys among the ties: radix over the 64-bit key (rare)
-    unsigned long long pfx = 0;
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    const int nc = ncand;
+    uint32_t prefix = b0;
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = pass == 1 ? 10 : 0;
+      const int bits = pass == 1 ? 11 : 10;
+      const int nb = 1 << bits;
+      for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+      for (int e = tid; e < nc; e += kSelThreads) {
+        const uint32_t k32 = keys[skew(cand[e])];
+        if ((k32 >> (shift + bits)) == prefix) atomicAdd(&hist[(k32 >> shift) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      bucket = select_bucket<kSelThreads>(hist, nb, r, smem, out);
+      prefix = (prefix << bits) | (uint32_t)bucket;
+    }
+    t32 = prefix;
+    // exact keys of the float32 ties
+    for (int e = tid; e < nc; e += kSelThreads) {
+      const int i = cand[e];
+      if (keys[skew(i)] != t32) continue;
+      const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+      atomicMin(&mm[0], k64);
+      atomicMax(&mm[1], k64);
+    }
+    __syncthreads();
+    K = mm[0];
+    if (K != mm[1]) {
+      unsigned long long pfx = 0;
+      for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        for (int e = tid; e < nc; e += kSelThreads) {
+          const int i = cand[e];
+          if (keys[skew(i)] != t32) continue;
+          const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+          if (pass == 0 || (k64 >> (shift + 8)) == pfx) atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        const int bk = select_bucket<kSelThreads>(hist, 256, r, smem, out);
+        pfx = (pfx << 8) | (unsigned long long)bk;
+      }
+      K = pfx;
+    }
+    // the r-th (slot order) of the candidates whose exact key is K
+    for (int e = tid; e < nc; e += kSelThreads) {
+      const int i = cand[e];
+      const bool f = keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K;
+      hist[e] = f ? 1u : 0u;
+      if (f) atomicAdd(&nflag, 1);
+    }
+    __syncthreads();
+    const int nf = nflag;
+    for (int e = tid; e < nc; e += kSelThreads) {
+      if (!hist[e]) continue;
+      const int i = cand[e];
+      int rank = 0;
+      if (nf > 1)
+        for (int f2 = 0; f2 < nc; ++f2) rank += (hist[f2] && cand[f2] < i) ? 1 : 0;
+      if (rank + 1 == r) out[2] = i;
+    }
+  } else {
+    // ---- large bucket: passes 1, 2 over all keys in LDS
+    uint32_t prefix = b0;
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = pass == 1 ? 10 : 0;
+      const int bits = pass == 1 ? 11 : 10;
+      const int nb = 1 << bits;
+      for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += kSelThreads) {
-        if (keys[skew(i)] != t32) continue;
-        const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
-        if (pass == 0 || (k64 >> (shift + 8)) == pfx) atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
+        const uint32_t k32 = keys[skew(i)];
+        if ((k32 >> (shift + bits)) == prefix) atomicAdd(&hist[(k32 >> shift) & (nb - 1)], 1u);
       }
       __syncthreads();
-      const int bk = select_bucket<kSelThreads>(hist, 256, r, smem, out);
-      pfx = (pfx << 8) | (unsigned long long)bk;
+      bucket = select_bucket<kSelThreads>(hist, nb, r, smem, out);
+      prefix = (prefix << bits) | (uint32_t)bucket;
     }
-    K = pfx;
-  }
-
-  // ---- slot of the r-th tie (slot order) with exact key K: contiguous ranges
-  const int ipt = (n + kSelThreads - 1) / kSelThreads;
-  const int lo = min(n, tid * ipt), hi = min(n, lo + ipt);
-  int c = 0;
-  for (int i = lo; i < hi; ++i)
-    if (keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K) ++c;
-  int tot;
-  const int before = block_excl_scan<kSelThreads>(c, smem, tot);
-  if (r > before && r <= before + c) {
-    int seen = before;
-    for (int i = lo; i < hi; ++i)
-      if (keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K && ++seen == r) {
-        out[2] = i;
-        break;
+    t32 = prefix;
+    for (int i = tid; i < n; i += kSelThreads) {
+      if (keys[skew(i)] != t32) continue;
+      const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+      atomicMin(&mm[0], k64);
+      atomicMax(&mm[1], k64);
+    }
+    __syncthreads();
+    K = mm[0];
+    if (K != mm[1]) {
+      unsigned long long pfx = 0;
+      for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kSelThreads) {
+          if (keys[skew(i)] != t32) continue;
+          const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+          if (pass == 0 || (k64 >> (shift + 8)) == pfx) atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        const int bk = select_bucket<kSelThreads>(hist, 256, r, smem, out);
+        pfx = (pfx << 8) | (unsigned long long)bk;
       }
+      K = pfx;
+    }
+    // slot of the r-th tie (slot order) with exact key K: contiguous ranges
+    const int ipt = (n + kSelThreads - 1) / kSelThreads;
+    const int lo = min(n, tid * ipt), hi = min(n, lo + ipt);
+    int c = 0;
+    for (int i = lo; i < hi; ++i)
+      if (keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K) ++c;
+    int tot;
+    const int before = block_excl_scan<kSelThreads>(c, smem, tot);
+    if (r > before && r <= before + c) {
+      int seen = before;
+      for (int i = lo; i < hi; ++i)
+        if (keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K && ++seen == r) {
+          out[2] = i;
+          break;
+        }
+    }
   }
   __syncthreads();
   const int sstar = out[2];
 
-  // ---- keep flags per 32-slot tile (masks), scan, emit.  Kept rows whose source
-  // lies below za and differs from their destination are staged: any later move
-  // into [0, za) may overwrite them (za >= kept bounds every destination).
-  auto keep = [&](int i) -> bool {
-    const uint32_t k32 = keys[skew(i)];
-    if (k32 != t32) return k32 > t32;
-    const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
-    return k64 > K || (k64 == K && i > sstar);
-  };
-  auto tile_mask = [&](int tl) -> uint32_t {
-    uint32_t m = 0;
-    const int i0 = 32 * tl;
-    for (int s2 = 0; s2 < 32 && i0 + s2 < n; ++s2)
-      if (keep(i0 + s2)) m |= 1u << s2;
-    return m;
-  };
+  // ---- keep masks per 32-slot tile (one ballot covers two tiles), tile bases by a
+  // scan, then per slot: destination (keep_src), evicted position, staging.  Kept
+  // rows whose source lies below za and differs from their destination are staged:
+  // any later move into [0, za) may overwrite them (za >= kept bounds every
+  // destination).
+  uint32_t* tmask = (uint32_t*)cand;  // kCand >= tiles: the keys fit in LDS
   const int T = (n + 31) >> 5;
-  const int tpt = (T + kSelThreads - 1) / kSelThreads;
-  const int tl0 = min(T, tid * tpt), tl1 = min(T, tl0 + tpt);
-  int kc = 0;
-  for (int tl = tl0; tl < tl1; ++tl) kc += __popc(tile_mask(tl));
-  int kept_all;
-  int dst = block_excl_scan<kSelThreads>(kc, smem, kept_all);
-  int ev = 32 * tl0 - dst;
-  const int kept = min(kept_all, a.Mk);
-  int2* slist = a.stage_list + (size_t)u * a.Mk;
-  for (int tl = tl0; tl < tl1; ++tl) {
-    const uint32_t m = tile_mask(tl);
-    a.tile_mask[(size_t)u * a.Tc + tl] = m;
-    a.tile_base[(size_t)u * a.Tc + tl] = dst;
-    const int i0 = 32 * tl;
-    for (int s2 = 0; s2 < 32 && i0 + s2 < n; ++s2) {
-      const int i = i0 + s2;
-      if ((m >> s2) & 1u) {
-        if (dst < a.Mk) {
-          a.keep_src[(size_t)u * a.Mk + dst] = i;
-          if (i != dst && i < a.za) slist[atomicAdd(&nstage, 1)] = make_int2(i, dst);
+  {
+    // wave wv takes 64-slot blocks wv, wv + 16, ...; four blocks per round
+    constexpr int kW = kSelThreads / 64, kU = 4;
+    const int nb64 = (n + 63) >> 6;
+    for (int b0r = wv; b0r < nb64; b0r += kU * kW) {
+      uint32_t kk[kU];
+#pragma unroll
+      for (int e = 0; e < kU; ++e) kk[e] = keys[skew(min(64 * (b0r + e * kW) + lane, n - 1))];
+#pragma unroll
+      for (int e = 0; e < kU; ++e) {
+        const int blk = b0r + e * kW;
+        const int i = 64 * blk + lane;
+        bool k = kk[e] > t32;
+        if (kk[e] == t32 && i < n) {  // float32 tie: the exact key decides
+          const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
+          k = k64 > K || (k64 == K && i > sstar);
         }
-        ++dst;
-      } else {
-        if (a.evicted_pos && ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
-        ++ev;
+        k = k && i < n;
+        const unsigned long long bal = __ballot(k);
+        if (lane == 0 && blk < nb64) {
+          tmask[2 * blk] = (uint32_t)bal;
+          if (2 * blk + 1 < T) tmask[2 * blk + 1] = (uint32_t)(bal >> 32);
+        }
       }
     }
   }
   __syncthreads();
-  // ---- staged rows: all threads copy 16-byte pieces (K, V) and the row tails
+  const int tpt = (T + kSelThreads - 1) / kSelThreads;
+  const int tl0 = min(T, tid * tpt), tl1 = min(T, tl0 + tpt);
+  int kc = 0;
+  for (int tl = tl0; tl < tl1; ++tl) kc += __popc(tmask[tl]);
+  int kept_all;
+  int dst = block_excl_scan<kSelThreads>(kc, smem, kept_all);
+  for (int tl = tl0; tl < tl1; ++tl) {
+    const uint32_t m = tmask[tl];
+    hist[tl] = (uint32_t)dst;
+    a.tile_mask[(size_t)u * a.Tc + tl] = m;
+    a.tile_base[(size_t)u * a.Tc + tl] = dst;
+    dst += __popc(m);
+  }
+  __syncthreads();
+  const int kept = min(kept_all, a.Mk);
+  int2* slist = a.stage_list + (size_t)u * a.Mk;
+  {
+    constexpr int kU = 4;
+    for (int i0 = tid; i0 < n; i0 += kU * kSelThreads) {
+      uint32_t mk[kU];
+      int bs[kU];
+#pragma unroll
+      for (int e = 0; e < kU; ++e) {
+        const int tl = min(i0 + e * kSelThreads, n - 1) >> 5;
+        mk[e] = tmask[tl];
+        bs[e] = (int)hist[tl];
+      }
+#pragma unroll
+      for (int e = 0; e < kU; ++e) {
+        const int i = i0 + e * kSelThreads;
+        if (i >= n) continue;
+        const int s2 = i & 31;
+        const int before = bs[e] + __popc(mk[e] & ((1u << s2) - 1u));
+        if ((mk[e] >> s2) & 1u) {
+          if (before < a.Mk) {
+            a.keep_src[(size_t)u * a.Mk + before] = i;
+            if (i != before && i < a.za) slist[atomicAdd(&nstage, 1)] = make_int2(i, before);
+          }
+        } else if (a.evicted_pos) {
+          const int ev = i - before;
+          if (ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // ---- staged rows to scratch: 16-byte pieces (K, V) and the 8-byte row tails;
+  // each thread loads a batch of pieces before storing any
   {
     const int ns = min(nstage, a.Mk);
     const int ppr = a.row_bytes / 16;
     const int per = 2 * ppr + 1;
     const unsigned char* kb = (const unsigned char*)a.k + (size_t)u * a.cap * a.row_bytes;
     const unsigned char* vb = (const unsigned char*)a.v + (size_t)u * a.cap * a.row_bytes;
-    for (int q = tid; q < ns * per; q += kSelThreads) {
-      const int e = q / per, part = q - e * per;
-      const int2 sd = slist[e];
-      unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
-      if (part < 2 * ppr) {
-        const bool isv = part >= ppr;
-        const int pc = isv ? part - ppr : part;
-        *(u32x4*)(sp + (isv ? a.row_bytes : 0) + 16 * pc) =
-            *(const u32x4*)((isv ? vb : kb) + (size_t)sd.x * a.row_bytes + 16 * pc);
-      } else {
-        int32_t* tail = (int32_t*)(sp + 2 * a.row_bytes);
-        tail[0] = lb ? __float_as_int(lb[sd.x]) : 0;
-        tail[1] = ps[sd.x];
+    constexpr int kB = 8;
+    for (int q0 = tid; q0 < ns * per; q0 += kB * kSelThreads) {
+      u32x4 x[kB];
+      unsigned char* to[kB];
+#pragma unroll
+      for (int e = 0; e < kB; ++e) {
+        const int q = q0 + e * kSelThreads;
+        to[e] = nullptr;
+        if (q < ns * per) {
+          const int en = q / per, part = q - en * per;
+          const int2 sd = slist[en];
+          unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
+          if (part < 2 * ppr) {
+            const bool isv = part >= ppr;
+            const int pc = isv ? part - ppr : part;
+            x[e] = *(const u32x4*)((isv ? vb : kb) + (size_t)sd.x * a.row_bytes + 16 * pc);
+            to[e] = sp + (isv ? a.row_bytes : 0) + 16 * pc;
+          } else {
+            x[e] = u32x4{lb ? __float_as_uint(lb[sd.x]) : 0u, (uint32_t)ps[sd.x], 0u, 0u};
+            to[e] = sp + 2 * a.row_bytes;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kB; ++e) {
+        if (!to[e]) continue;
+        if (q0 + e * kSelThreads < ns * per &&
+            (q0 + e * kSelThreads) % per == 2 * ppr) {
+          *(uint2*)to[e] = make_uint2(x[e][0], x[e][1]);
+        } else {
+          *(u32x4*)to[e] = x[e];
+        }
       }
     }
   }
@@ -845,6 +1015,7 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     pa.stage_list = (int2*)(w + L.stage_list);
     pa.Tc = L.Tc;
     pa.za = fused_za(M, cache->cap);
+    pa.vec = cache->cap % 4 == 0;
     TraceScope tr(kTrEvictSelect, s);
     hipLaunchKernelGGL(evict_plan_lds, dim3(cache->B * cache->Hkv), dim3(kSelThreads), lds_keys, s,
                        pa);
@@ -864,7 +1035,7 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
 // attention + compaction path) for this cache.
 bool plan_in_lds(const kvb_cache* c) {
   const size_t lds_keys = ((size_t)c->cap + c->cap / 32 + 1) * sizeof(uint32_t);
-  return lds_keys <= plan_lds_limit();
+  return lds_keys <= plan_lds_limit() && (c->cap + 31) / 32 <= kCand;
 }
 
 FusedPlan fused_plan(const kvb_cache* c, int32_t M, void* ws) {
