@@ -756,14 +756,15 @@ __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ merge
-// One 256-thread workgroup per (b, h) folds the P split states with the merge
-// operator.  Weights w_p = Z_p e^{m_p - M} are staged in LDS; thread group q
-// (256 / D groups) sums w_p a_p over its contiguous share of the splits with 8
-// loads in flight, and the groups' sums are added in group order, so the result
-// does not depend on timing.
-constexpr int kMergeThreads = 256;
+// One workgroup of NT threads per (b, h) folds the P split states with the merge
+// operator (NT = 512 for many splits, else 256).  Weights w_p = Z_p e^{m_p - M}
+// are staged in LDS; thread group q (NT / D groups) sums w_p a_p over its
+// contiguous share of the splits with 16 loads in flight; the maximum and the
+// weight total are tree reductions and the groups' sums are added in group order,
+// so the result does not depend on timing.
 constexpr int kMergeMaxP = 4096;
 
+template <int kMergeThreads>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
                                                             const float* part_ml, int P, int D,
                                                             float* out, float* lse,
@@ -795,11 +796,21 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     __syncthreads();
   }
   const float M = red[0];
+  __syncthreads();
+  float ws = 0.f;
   for (int p = tid; p < P; p += kMergeThreads) {
     const float Zp = ml[2 * p + 1];
-    w[p] = (Zp > 0.f && M != kNegInf) ? Zp * __expf(ml[2 * p] - M) : 0.f;
+    const float wp = (Zp > 0.f && M != kNegInf) ? Zp * __expf(ml[2 * p] - M) : 0.f;
+    w[p] = wp;
+    ws += wp;
   }
+  red[tid] = ws;
   __syncthreads();
+  for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float W = red[0];
   float o = 0.f;
 #pragma unroll
   for (int e = 0; e < kB; ++e)
@@ -812,13 +823,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
       if (pb + e < p1) o = fmaf(w[pb + e], x[e], o);
   }
   gsum[tid] = o;
-  if (tid == 0) {
-    float W = 0.f;
-    for (int p = 0; p < P; ++p) W += w[p];
-    red[0] = W;
-  }
   __syncthreads();
-  const float W = red[0];
   if (tid < D) {
     float acc = 0.f;
     for (int g = 0; g < NG; ++g) acc += gsum[g * D + tid];
@@ -833,6 +838,17 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
 }
 
 // ------------------------------------------------------------------ host
+static void launch_merge(const float* part_a, const float* part_ml, int P, int D, float* out,
+                         float* lse, const UnitInfo* info, int32_t* len, int G, int BH,
+                         hipStream_t s) {
+  if (P > 128)
+    hipLaunchKernelGGL(attn_merge<512>, dim3(BH), dim3(512), 0, s, part_a, part_ml, P, D, out,
+                       lse, info, len, G);
+  else
+    hipLaunchKernelGGL(attn_merge<256>, dim3(BH), dim3(256), 0, s, part_a, part_ml, P, D, out,
+                       lse, info, len, G);
+}
+
 static bool mfma_supported(const kvb_cache* c, int G) {
   return c->dtype == KVB_BF16 && (c->D == 64 || c->D == 128) &&
          (G == 1 || G == 2 || G == 4 || G == 8);
@@ -979,9 +995,8 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
     if ((st = launch_split(cache, a, s))) return st;
   }
   TraceScope tr(kTrAttnMerge, s);
-  hipLaunchKernelGGL(attn_merge, dim3(cache->B * Hq), dim3(kMergeThreads), 0, s, a.part_a,
-                     a.part_ml, P, cache->D, out, lse, (const UnitInfo*)nullptr, (int32_t*)nullptr,
-                     G);
+  launch_merge(a.part_a, a.part_ml, P, cache->D, out, lse, nullptr, nullptr, G,
+               cache->B * Hq, s);
   return launch_status();
 }
 
@@ -1092,8 +1107,8 @@ extern "C" int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q,
       launch_pipe_any(cache, a, dim3(Pb, U), s, true);
     }
     TraceScope tr(kTrAttnMerge, s);
-    hipLaunchKernelGGL(attn_merge, dim3(cache->B * Hq), dim3(kMergeThreads), 0, s, a.part_a,
-                       a.part_ml, P, cache->D, out, lse, a.plan.info, cache->len, G);
+    launch_merge(a.part_a, a.part_ml, P, cache->D, out, lse, a.plan.info, cache->len, G,
+                 cache->B * Hq, s);
   }
   return launch_status();
 }
