@@ -23,7 +23,8 @@ Every function is a direct, unblocked statement of what the pages define:
   section and the systems section on the modified engine).
 * ``asm``         -- cosine-argmax centroid lookup and lossless state merge
   (Context Memorization, method steps, steps 3 and 4; GQA extension in the
-  technical-novelty section).
+  technical-novelty section), and the two-level (hierarchical) lookup of the
+  same section.
 * ``bytes_model`` -- KV bytes per token, pinned to IndexMem's memory-wall figure
   ("IndexMem: Learned KV-Cache Eviction with Latent Memory for Long-Context LLM
   Inference", technical summary, section 1).
@@ -38,7 +39,8 @@ from .attn import (retention_bias, attention_state, attention, merge_states,
                         state_to_out_lse, split_attention, decode_attention)
 from .evict import (retention_keys, evict_plan, erase_plan, compact_unit,
                        Cache, evict_to_budget, erase_ranges, append_tokens)
-from .asm import cosine_similarities, cosine_lookup, asm_merge, asm_lookup_merge
+from .asm import (cosine_similarities, cosine_lookup, asm_merge, asm_lookup_merge,
+                  hier_lookup, asm_lookup_merge_hier)
 from .bytes_model import kv_bytes_per_token, attention_layer_bytes
 from .decode import run_decode_steps
 
@@ -48,5 +50,6 @@ __all__ = [
     "retention_keys", "evict_plan", "erase_plan", "compact_unit", "Cache",
     "evict_to_budget", "erase_ranges", "append_tokens",
     "cosine_similarities", "cosine_lookup", "asm_merge", "asm_lookup_merge",
+    "hier_lookup", "asm_lookup_merge_hier",
     "kv_bytes_per_token", "attention_layer_bytes", "run_decode_steps",
 ]

@@ -80,7 +80,14 @@ WORKLOADS = {
     "memento_1m": Workload("memento_1m", batch=1, hq=64, hkv=8, head_dim=128,
                            dtype="bf16", ctx=1 << 20, budget=65536, layers=1,
                            seed=1005, retention=False),
+    # two-level ASM lookup: 16K entries per KV head in 128 first-level clusters,
+    # the top 16 first-level centroids expanded
+    "asm_hier": Workload("asm_hier", batch=32, hq=32, hkv=8, head_dim=128,
+                         dtype="bf16", ctx=2048, budget=1 << 30, layers=36,
+                         seed=1006, retention=False, codebook=16384),
 }
+HIER_K1 = 128
+HIER_M = 16
 
 
 # --------------------------------------------------------------------------
@@ -187,6 +194,56 @@ def host_codebook(w: Workload, K: int | None = None, seed_offset: int = 29):
     abar = bf16_bits(rng.standard_normal(size=(w.hkv, K, w.head_dim)))
     log_zbar = rng.uniform(0.0, 12.0, size=(w.hkv, K)).astype(np.float32)
     return centroids, abar, log_zbar
+
+
+def host_hier_codebook(w: Workload, K: int, K1: int, spread: float = 1.0,
+                       seed_offset: int = 31):
+    """A two-level codebook per KV head, built from latent cluster directions.
+
+    Each of the K entries belongs to one of K1 clusters (drawn uniformly, so some
+    clusters may be small or empty); entry = normalise(u_j + spread * N(0, I/D))
+    for its cluster's unit direction u_j.  The first-level centroids are the u_j
+    themselves.  Entries are stored cluster by cluster (random order inside a
+    cluster).  Returns (c1 [Hkv][K1][D], offs [Hkv][K1+1] int32, stored
+    [Hkv][K][D], kid [Hkv][K] int32 = original index of each stored entry,
+    abar [Hkv][K][D] and log_zbar [Hkv][K] in original order); vectors are bf16
+    bits.
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset + 7919 * K1))
+    H, D = w.hkv, w.head_dim
+    u = rng.standard_normal((H, K1, D))
+    u /= np.sqrt((u * u).sum(-1, keepdims=True))
+    assign = rng.integers(0, K1, size=(H, K))
+    x = u[np.arange(H)[:, None], assign] + spread * rng.standard_normal((H, K, D)) / np.sqrt(D)
+    x /= np.sqrt((x * x).sum(-1, keepdims=True))
+    cent = bf16_bits(x)
+    stored = np.empty_like(cent)
+    kid = np.empty((H, K), np.int32)
+    offs = np.empty((H, K1 + 1), np.int32)
+    for g in range(H):
+        perm = np.lexsort((rng.permutation(K), assign[g]))
+        stored[g] = cent[g, perm]
+        kid[g] = perm
+        offs[g] = np.searchsorted(assign[g, perm], np.arange(K1 + 1))
+    abar = bf16_bits(rng.standard_normal((H, K, D)))
+    log_zbar = rng.uniform(0.0, 12.0, size=(H, K)).astype(np.float32)
+    return bf16_bits(u), offs, stored, kid, abar, log_zbar, cent
+
+
+def host_near_queries(w: Workload, entries, noise: float = 0.5, seed_offset: int = 37):
+    """Decode queries near stored entries: q = |N(0,1)| scale x (c_k + noise * N(0, I/D))
+    for a random entry k of the query head's KV head.  entries: [Hkv][K][D] bf16
+    bits (original order).  Returns q [B][Hq][D] bf16 bits."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    H, K, D = entries.shape
+    G = w.hq // H
+    B = w.batch
+    c = bf16_to_f64(entries)
+    k = rng.integers(0, K, size=(B, w.hq))
+    g = (np.arange(w.hq) // G)[None, :].repeat(B, 0)
+    q = c[g, k] + noise * rng.standard_normal((B, w.hq, D)) / np.sqrt(D)
+    q *= np.abs(rng.standard_normal((B, w.hq, 1))) + 0.5
+    return bf16_bits(q)
 
 
 def memento_layout(total: int = 1 << 20, seed: int = 1005, memento: int = 200,

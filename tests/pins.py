@@ -305,6 +305,66 @@ def check_lookup_bruteforce(seed=9):
     assert OA.cosine_lookup(np.array([0.0, 0.5]), C) == 0, "ties go to the lowest index"
 
 
+# ---------------------------------------------------------------- P10
+def check_hier_lookup(seed=10):
+    """Two-level lookup: expanding every first-level cluster is the linear lookup
+    (whatever the clustering and the order the entries are stored in); small
+    hand-built cases fix the expansion, the tie rules and the returned index."""
+    r = _rng(seed)
+    for K, K1, D in ((7, 3, 4), (40, 6, 8), (96, 12, 16)):
+        C = r.standard_normal((K, D)) * r.uniform(0.2, 3.0, size=(K, 1))
+        C[K - 1] = C[2]                                        # duplicate entry: tie
+        assign = r.integers(0, K1, size=K)
+        assign[:K1] = np.arange(K1)                            # no empty cluster
+        perm = np.lexsort((r.permutation(K), assign))          # cluster order, shuffled inside
+        offs = np.searchsorted(assign[perm], np.arange(K1 + 1))
+        c1 = r.standard_normal((K1, D))
+        for _ in range(4):
+            q = r.standard_normal(D)
+            assert OA.hier_lookup(q, c1, offs, C[perm], perm, K1) == OA.cosine_lookup(q, C), \
+                "full expansion != linear lookup"
+        j = int(r.integers(0, K))
+        if j == K - 1:
+            j = 2
+        assert OA.hier_lookup(1.7 * C[j], c1, offs, C[perm], perm, K1) == j, "q = lambda c_j"
+    # clusters {e0, e0+e1}, {e2, e3}: stored (1, 0, 3, 2) -> kid = (1, 0, 3, 2)
+    C = np.array([[1.0, 1.0, 0.0, 0.0], [1.0, 0.0, 0.0, 0.0],
+                  [0.0, 0.0, 0.0, 1.0], [0.0, 0.0, 1.0, 0.0]])
+    kid = np.array([1, 0, 3, 2])
+    offs = np.array([0, 2, 4])
+    c1 = np.array([[1.0, 0.5, 0.0, 0.0], [0.0, 0.0, 1.0, 1.0]])
+    q = np.array([1.0, 0.2, 0.9, 0.0])
+    # first level 0.72 / 0.47 keeps cluster 0, which holds the linear best e0
+    # (original index 0, stored second; cos 0.74 against 0.62 for e0+e1)
+    assert OA.cosine_lookup(q, C[np.argsort(kid)]) == 0
+    assert OA.hier_lookup(q, c1, offs, C, kid, 1) == 0, "expanded cluster, original index"
+    # first level 0.55 / 0.79 keeps cluster 1 while the linear best is e0 (cos 0.61);
+    # inside cluster 1, e3 and e2 tie at 0.56: the lower original index (2) wins
+    # although e3 is stored first
+    q = np.array([0.55, 0.0, 0.5, 0.5])
+    assert OA.cosine_lookup(q, C[np.argsort(kid)]) == 0
+    assert OA.hier_lookup(q, c1, offs, C, kid, 1) == 2, "best inside the kept cluster only"
+    assert OA.hier_lookup(q, c1, offs, C, kid, 2) == 0, "two clusters kept"
+    # first-level centroids of unequal length: cosine keeps cluster 0 (0.92 against
+    # 0.39), a raw dot product would keep cluster 1 (1.0 against 3.0)
+    c1d = np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 0.0, 5.0, 5.0]])
+    assert OA.hier_lookup(np.array([1.0, 0.0, 0.3, 0.3]), c1d, offs, C, kid, 1) == 0, \
+        "first level by cosine"
+    # equal first-level similarities: the lower j is kept
+    c1t = np.array([[0.0, 0.0, 1.0, 0.0], [1.0, 0.0, 0.0, 0.0]])
+    qt = np.array([1.0, 0.0, 1.0, 0.0])
+    # (j = 0 holds e0 -> index 0; keeping j = 1 instead would give e2 -> index 2)
+    assert OA.hier_lookup(qt, c1t, offs, C, kid, 1) == 0, "first-level tie -> lower j"
+    # equal entry similarities inside the kept clusters: the lowest original index
+    Ct = np.array([[0.0, 1.0], [0.0, 2.0], [1.0, 0.0]])
+    assert OA.hier_lookup(np.array([0.0, 1.0]), np.array([[0.0, 1.0]]), np.array([0, 3]),
+                          Ct, np.array([7, 4, 5]), 1) == 4, "entry tie -> lowest index"
+    # a zero query gives index 0; a kept cluster without entries gives index 0
+    assert OA.hier_lookup(np.zeros(4), c1, offs, C, kid, 2) == 0
+    assert OA.hier_lookup(np.array([0.0, 1.0]), np.array([[0.0, 1.0], [1.0, 0.0]]),
+                          np.array([0, 0, 3]), Ct, np.array([7, 4, 5]), 1) == 0
+
+
 # ---------------------------------------------------------------- P9
 def check_bytes_model():
     """IndexMem's memory-wall estimate: ~320 GB of KV for a 70B model at 1M tokens."""
@@ -315,4 +375,4 @@ def check_bytes_model():
 ALL = [check_attention_library, check_bias_closed_form, check_split_merge,
        check_asm_lossless, check_evict_bruteforce, check_evict_sliding_window,
        check_evict_invariants, check_compaction, check_erase_bruteforce,
-       check_lookup_bruteforce, check_bytes_model]
+       check_lookup_bruteforce, check_hier_lookup, check_bytes_model]

@@ -18,6 +18,7 @@ _orig_state = OT.attention_state
 _orig_merge = OT.merge_states
 _orig_keys = OE.retention_keys
 _orig_plan = OE.evict_plan
+_orig_hier = OA.hier_lookup
 
 
 def bias_sign_flipped(log_beta, pos, t):
@@ -139,6 +140,45 @@ def asm_merge_linear(out, lse, abar, log_zbar):
     return (w1 * np.asarray(out) + w2 * np.asarray(abar)) / (w1 + w2), np.logaddexp(lse, log_zbar)
 
 
+def _hier(q, c1, offs, centroids, kid, m, first_dot=False, keep=None, high_j=False,
+          pos_out=False, tie_pos=False):
+    q = np.asarray(q, np.float64)
+    if not np.any(q != 0.0):
+        return 0
+    K1 = len(c1)
+    s1 = np.asarray(c1, np.float64) @ q if first_dot else OA.cosine_similarities(q, c1)
+    order = np.lexsort((-np.arange(K1) if high_j else np.arange(K1), -s1))
+    kept = order[:m if keep is None else keep]
+    pos = np.concatenate([np.arange(offs[j], offs[j + 1]) for j in kept] +
+                         [np.zeros(0, np.int64)]).astype(np.int64)
+    if pos.size == 0:
+        return 0
+    s = OA.cosine_similarities(q, np.asarray(centroids)[pos])
+    ids = np.asarray(kid)[pos]
+    best = np.lexsort((pos if tie_pos else ids, -s))[0]
+    return int(pos[best]) if pos_out else int(ids[best])
+
+
+def hier_first_level_dot(q, c1, offs, centroids, kid, m):
+    return _hier(q, c1, offs, centroids, kid, m, first_dot=True)
+
+
+def hier_keeps_one_fewer(q, c1, offs, centroids, kid, m):
+    return _hier(q, c1, offs, centroids, kid, m, keep=max(m - 1, 0))
+
+
+def hier_first_tie_high(q, c1, offs, centroids, kid, m):
+    return _hier(q, c1, offs, centroids, kid, m, high_j=True)
+
+
+def hier_returns_position(q, c1, offs, centroids, kid, m):
+    return _hier(q, c1, offs, centroids, kid, m, pos_out=True)
+
+
+def hier_tie_by_position(q, c1, offs, centroids, kid, m):
+    return _hier(q, c1, offs, centroids, kid, m, tie_pos=True)
+
+
 def compact_reversed(cache, b, g, keep):
     n = keep.shape[0]
     idx = np.nonzero(keep)[0][::-1]
@@ -169,6 +209,11 @@ MUTANTS = [
     (OA, "cosine_lookup", lookup_last_tie),
     (OA, "asm_merge", asm_merge_linear),
     (OE, "compact_unit", compact_reversed),
+    (OA, "hier_lookup", hier_first_level_dot),
+    (OA, "hier_lookup", hier_keeps_one_fewer),
+    (OA, "hier_lookup", hier_first_tie_high),
+    (OA, "hier_lookup", hier_returns_position),
+    (OA, "hier_lookup", hier_tie_by_position),
 ]
 
 

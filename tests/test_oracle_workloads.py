@@ -70,3 +70,21 @@ def test_split_identity_on_workload_shapes():
         bounds = list(range(0, 512, S)) + [512]
         o, l, _ = oracle.split_attention(q, k, v, lb, pos, 512, 0.125, bounds)
         assert np.max(np.abs(o - full[0])) < 1e-12 and abs(l - full[1]) < 1e-12
+
+
+def test_hier_workload_matches_linear_on_near_queries():
+    """On the two-level workload's queries (each near a stored entry), expanding the
+    top 16 of 128 first-level clusters finds the linear lookup's entry (the pages
+    report this for top-16 expansion); a sample of 64 queries."""
+    w = synth.WORKLOADS["asm_hier"]
+    c1, offs, stored, kid, _, _, cent = synth.host_hier_codebook(w, w.codebook, synth.HIER_K1)
+    q = synth.bf16_to_f64(synth.host_near_queries(w, cent))
+    G = w.hq // w.hkv
+    agree = 0
+    for n, (b, h) in enumerate([(b, h) for b in range(2) for h in range(w.hq)]):
+        g = h // G
+        lin = oracle.cosine_lookup(q[b, h], synth.bf16_to_f64(cent[g]))
+        hi = oracle.hier_lookup(q[b, h], synth.bf16_to_f64(c1[g]), offs[g],
+                                synth.bf16_to_f64(stored[g]), kid[g], synth.HIER_M)
+        agree += lin == hi
+    assert agree >= 62, agree
