@@ -82,6 +82,80 @@ def cpu_baseline(w, host_units, t, M, budget_s=12.0):
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def asm_bench(args):
+    """Lookup + merge for one layer of the ASM workload's queries (32 sequences x 32
+    query heads, 8 KV heads, D = 128): the linear scan and the two-level index
+    (first-level clusters, top 16 kept), at 4K / 16K / 64K entries per KV head.
+    Inputs are resident on the device; each figure is the mean of 50 back-to-back
+    calls, and the per-kernel split comes from the library's HIP-event trace."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(
+                torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    base = synth.WORKLOADS["asm_hier"]
+    rows = []
+    for K, K1 in ((4096, 64), (16384, synth.HIER_K1), (65536, 256)):
+        w = dataclasses.replace(base, codebook=K)
+        c1, offs, st, kid, ab, lz, cent = synth.host_hier_codebook(w, K, K1)
+        q = synth.host_near_queries(w, cent)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed)
+        so = torch.randn((w.batch, w.hq, w.head_dim), device="cuda", generator=g)
+        sl = torch.rand((w.batch, w.hq), device="cuda", generator=g) * 10
+        dq, dc1, doffs, dst, dkid, dab, dlz, dcent = map(dev, (q, c1, offs, st, kid, ab, lz, cent))
+        wsl = torch.empty(kvb.asm_lookup_merge_workspace(w.batch, w.hq, w.hkv, w.head_dim, K),
+                          dtype=torch.uint8, device="cuda")
+        wsh = torch.empty(kvb.asm_lookup_merge_hier_workspace(w.batch, w.hq, w.hkv, K1,
+                                                              synth.HIER_M),
+                          dtype=torch.uint8, device="cuda")
+        calls = {
+            "linear": lambda: kvb.asm_lookup_merge(dq, dcent, dab, dlz, so, sl, ws=wsl),
+            "two_level": lambda: kvb.asm_lookup_merge_hier(dq, dc1, doffs, dst, dkid, synth.HIER_M,
+                                                           dab, dlz, so, sl, ws=wsh),
+        }
+        row = {"entries": K, "clusters": K1, "kept": synth.HIER_M}
+        idx = {}
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(50):
+                _, _, i = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            kvb.trace_enable(16, ("asm_lookup", "asm_finalize"))
+            fn()
+            kern = [round(ms * 1000, 1) for _, ms in kvb.trace_read()]
+            kvb.trace_disable()
+            row[name + "_us"] = round(e0.elapsed_time(e1) / 50 * 1000, 2)
+            row[name + "_kernels_us"] = kern
+            idx[name] = i.cpu().numpy()
+        row["same_index_fraction"] = float((idx["linear"] == idx["two_level"]).mean())
+        rows.append(row)
+        print(f"# {row}", file=sys.stderr, flush=True)
+    mid = rows[1]
+    print(json.dumps({
+        "metric": "ASM lookup + merge latency per layer (two-level index, 16K entries)",
+        "value": mid["two_level_us"], "unit": "us", "n_gpus": 1, "higher_is_better": False,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "asm_hier", "batch": base.batch, "q_heads": base.hq,
+                   "kv_heads": base.hkv, "head_dim": base.head_dim},
+        "sizes": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +171,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
+    ap.add_argument("--asm-lookup", action="store_true",
+                    help="time the attention-state-memory lookup + merge instead: linear and "
+                         "two-level index at 4K, 16K and 64K entries per KV head (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy kernel 5 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -110,6 +187,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "elementwise copy", "bytes_read": 1 << 30,
                           "bytes_written": 1 << 30, "launches": 5}))
+        return
+    if args.asm_lookup:
+        asm_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "

@@ -9,7 +9,8 @@ Entry points (same names as the C ABI in include/kvbound.h):
     kv_attn_decode, kv_evict_to_budget, kv_erase_ranges, asm_lookup_merge
 plus the workspace-size helpers and ``KVCache``, a holder of one layer's tensors.
 """
-from ._lib import (KVBError, KVCache, asm_lookup_merge, asm_lookup_merge_workspace,
+from ._lib import (KVBError, KVCache, asm_lookup_merge, asm_lookup_merge_hier,
+                   asm_lookup_merge_hier_workspace, asm_lookup_merge_workspace,
                    kv_append, kv_attn_decode, kv_attn_decode_compact, kv_attn_decode_splits,
                    kv_attn_decode_workspace,
                    kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_plan,
@@ -20,7 +21,8 @@ from ._lib import (KVBError, KVCache, asm_lookup_merge, asm_lookup_merge_workspa
 __all__ = [
     "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_attn_decode_compact",
-    "asm_lookup_merge", "kv_attn_decode_workspace", "kv_attn_decode_splits",
+    "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",
+    "kv_attn_decode_workspace", "kv_attn_decode_splits",
     "kv_evict_workspace", "kv_erase_workspace", "asm_lookup_merge_workspace",
     "library", "library_path", "strerror", "trace_enable", "trace_read", "trace_reset",
     "trace_disable",

@@ -47,6 +47,7 @@ def library():
             "kv_evict_workspace": (SZ, [CP, I32]),
             "kv_erase_workspace": (SZ, [CP]),
             "asm_lookup_merge_workspace": (SZ, [I32, I32, I32, I32, I32]),
+            "asm_lookup_merge_hier_workspace": (SZ, [I32, I32, I32, I32, I32]),
             "kv_attn_decode": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P]),
             "kv_evict_to_budget": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
             "kv_evict_plan": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
@@ -57,6 +58,8 @@ def library():
             "kv_erase_ranges": (I32, [CP, P, P, I32, P, P, SZ, P]),
             "asm_lookup_merge": (I32, [P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, P, P,
                                        SZ, P]),
+            "asm_lookup_merge_hier": (I32, [P, I32, I32, I32, I32, P, I32, P, P, P, I32, I32, P,
+                                            P, P, P, P, P, P, P, SZ, P]),
             "kvb_trace_enable": (I32, [I32, I32]),
             "kvb_trace_read": (I32, [P, P, I32]),
             "kvb_trace_reset": (None, []),
@@ -328,6 +331,43 @@ def asm_lookup_merge(q, centroids, abar, log_zbar, self_out, self_lse, out=None,
 TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "keep_count": 16, "keep_emit": 32, "compact_move": 64, "asm_lookup": 128,
               "asm_finalize": 256, "attn_fused": 512}
+
+
+def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:
+    return int(library().asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m))
+
+
+def asm_lookup_merge_hier(q, c1, offs, centroids, kid, m, abar, log_zbar, self_out, self_lse,
+                          out=None, out_lse=None, idx=None, ws=None, stream=None):
+    """Two-level lookup + merge (see asm_lookup_merge_hier in kvbound.h).
+    c1 [Hkv][K1][D], offs [Hkv][K1+1], centroids (cluster order) [Hkv][K][D],
+    kid [Hkv][K]; abar, log_zbar by original index.  Returns (out, out_lse, idx)."""
+    _need(q, "q", torch.bfloat16)
+    _need(c1, "c1", torch.bfloat16)
+    _need(offs, "offs", torch.int32)
+    _need(centroids, "centroids", torch.bfloat16)
+    _need(kid, "kid", torch.int32)
+    _need(abar, "abar", torch.bfloat16)
+    _need(log_zbar, "log_zbar", torch.float32)
+    _need(self_out, "self_out", torch.float32)
+    _need(self_lse, "self_lse", torch.float32)
+    B, Hq, D = q.shape
+    Hkv, K1, _ = c1.shape
+    K = centroids.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
+    ws = _ws(ws, asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m), q.device)
+    st = library().asm_lookup_merge_hier(_ptr(q), B, Hq, Hkv, D, _ptr(c1), K1, _ptr(offs),
+                                         _ptr(centroids), _ptr(kid), K, int(m), _ptr(abar),
+                                         _ptr(log_zbar), _ptr(self_out), _ptr(self_lse), _ptr(out),
+                                         _ptr(out_lse), _ptr(idx), _ptr(ws), ws.numel(),
+                                         _stream(stream))
+    _check(st, "asm_lookup_merge_hier")
+    return out, out_lse, idx
 
 
 def trace_enable(capacity: int, kernels=("attn_split",)):

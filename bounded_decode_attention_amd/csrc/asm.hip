@@ -16,6 +16,8 @@
 //                       reduces to one candidate per query and chunk.
 //   asm_finalize        per query: best over chunks -> idx; gather abar[idx],
 //                       log Zbar[idx]; merge with (self_out, self_lse).
+#include <string.h>
+
 #include "common.h"
 
 namespace kvb {
@@ -146,6 +148,29 @@ __global__ __launch_bounds__(64 * kAsmWaves) void asm_lookup_partial(AsmArgs a) 
   }
 }
 
+// Step 4 for query (b, h) with stored entry k of KV head g: merge (self_out,
+// self_lse) with (abar[k], log Zbar[k]) by their normalisers.  One wave.
+__device__ __forceinline__ void merge_entry(const AsmArgs& a, int bh, int g, int k, int lane) {
+  const int D = a.D;
+  const float lz = a.log_zbar[(size_t)g * a.K + k];
+  const float ls = a.self_lse[bh];
+  const float M = fmaxf(ls, lz);
+  float w1 = 0.f, w2 = 0.f, lse_out = kNegInf;
+  if (M != kNegInf) {
+    w1 = ls == kNegInf ? 0.f : __expf(ls - M);
+    w2 = lz == kNegInf ? 0.f : __expf(lz - M);
+    lse_out = M + __logf(w1 + w2);
+  }
+  const float inv = (w1 + w2) > 0.f ? 1.f / (w1 + w2) : 0.f;
+  const uint16_t* ab = a.abar + ((size_t)g * a.K + k) * D;
+  for (int d = lane; d < D; d += 64) {
+    const float so = a.self_out[(size_t)bh * D + d];
+    const float av = bf16_bits_to_f32(ab[d]);
+    a.out[(size_t)bh * D + d] = (w1 * so + w2 * av) * inv;
+  }
+  if (lane == 0) a.out_lse[bh] = lse_out;
+}
+
 // One wave per query (b, h): pick the best candidate, gather, merge.
 __global__ __launch_bounds__(64) void asm_finalize(AsmArgs a) {
   const int bh = blockIdx.x;
@@ -181,25 +206,253 @@ __global__ __launch_bounds__(64) void asm_finalize(AsmArgs a) {
       bk = ok;
     }
   }
-  int k = (q2 > 0.f && bk != 0x7FFFFFFF) ? bk : 0;
+  const int k = (q2 > 0.f && bk != 0x7FFFFFFF) ? bk : 0;
   if (a.idx && lane == 0) a.idx[bh] = k;
-  const float lz = a.log_zbar[(size_t)g * a.K + k];
-  const float ls = a.self_lse[bh];
-  const float M = fmaxf(ls, lz);
-  float w1 = 0.f, w2 = 0.f, lse_out = kNegInf;
-  if (M != kNegInf) {
-    w1 = ls == kNegInf ? 0.f : __expf(ls - M);
-    w2 = lz == kNegInf ? 0.f : __expf(lz - M);
-    lse_out = M + __logf(w1 + w2);
+  merge_entry(a, bh, g, k, lane);
+}
+
+// ------------------------------------------------------------------ two-level lookup
+// Same page, technical-novelty section: a hierarchical index replaces the linear
+// scan.  Entries are stored cluster by cluster (offs[j] .. offs[j+1]-1 hold the
+// entries of first-level cluster j; kid gives each stored entry's original index).
+//   asm_hier_select    per (query, KV head): cosine against the K1 first-level
+//                      centroids, then the m best (equal similarities: lower
+//                      cluster first) -> sel.
+//   asm_hier_score     per (cluster, KV head): the cluster's entries against the
+//                      queries that kept it (MFMA); each query's best entry as an
+//                      atomic maximum of (ordered cosine, ~original index), so equal
+//                      cosines go to the lowest original index whatever the order.
+//   asm_hier_finalize  per query: index, gather, merge (as the linear lookup).
+constexpr int kHierMaxK1 = 512;
+
+struct HierArgs {
+  AsmArgs a;                // q, abar and log_zbar (original order), self state, outputs
+  const uint16_t* c1;       // [Hkv][K1][D]
+  const int32_t* offs;      // [Hkv][K1 + 1]
+  const uint16_t* stored;   // [Hkv][K][D], cluster by cluster
+  const int32_t* kid;       // [Hkv][K]
+  int32_t* sel;             // [Hkv][NQ][m]
+  unsigned long long* best; // [Hkv][NQ]
+  int32_t K1, m, NQ;
+};
+
+// Order-preserving float -> unsigned map (+0 and -0 equal).
+__device__ __forceinline__ uint32_t ordf(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b << 1) == 0) b = 0;
+  return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+
+// Query row lc of a 16-query tile as the MFMA A operand (zero when absent).
+template <int D>
+__device__ __forceinline__ void load_query_rows(const AsmArgs& a, int g, int qi, bool ok, int lg,
+                                                u32x4* qa) {
+  constexpr int KK = D / 32;
+  const int b = ok ? qi / a.G : 0, jj = ok ? qi - (qi / a.G) * a.G : 0;
+  const uint16_t* qp = a.q + ((size_t)(b * a.Hq + g * a.G + jj)) * D;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    qa[kk] = ok ? *(const u32x4*)(qp + 32 * kk + 8 * lg) : z;
   }
-  const float inv = (w1 + w2) > 0.f ? 1.f / (w1 + w2) : 0.f;
-  const uint16_t* ab = a.abar + ((size_t)g * a.K + k) * D;
-  for (int d = lane; d < D; d += 64) {
-    const float so = a.self_out[(size_t)bh * D + d];
-    const float av = bf16_bits_to_f32(ab[d]);
-    a.out[(size_t)bh * D + d] = (w1 * so + w2 * av) * inv;
+}
+
+// Column lc of a 16-vector tile as the MFMA B operand, and its squared norm.
+template <int D>
+__device__ __forceinline__ float load_columns(const uint16_t* row, int lg, u32x4* cv) {
+  constexpr int KK = D / 32;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) cv[kk] = *(const u32x4*)(row + 32 * kk + 8 * lg);
+  float n2 = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lo = bf16_bits_to_f32(cv[kk][w] & 0xFFFFu);
+      const float hi = bf16_bits_to_f32(cv[kk][w] >> 16);
+      n2 = fmaf(lo, lo, n2);
+      n2 = fmaf(hi, hi, n2);
+    }
+  n2 += __shfl_xor(n2, 16, 64);
+  n2 += __shfl_xor(n2, 32, 64);
+  return n2;
+}
+
+// One wave per (query, KV head): the first-level cosines (lane l scores clusters
+// l, l + 64, ...), then the m best by repeated wave-wide selection.
+template <int D>
+__global__ __launch_bounds__(64) void asm_hier_select(HierArgs h) {
+  constexpr int kMaxPer = kHierMaxK1 / 64;
+  __shared__ float qs[D];
+  const AsmArgs& a = h.a;
+  const int qi = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+  const int b = qi / a.G, jj = qi - (qi / a.G) * a.G;
+  const uint16_t* qp = a.q + ((size_t)(b * a.Hq + g * a.G + jj)) * D;
+  for (int d = lane; d < D; d += 64) qs[d] = bf16_bits_to_f32(qp[d]);
+  __syncthreads();
+  const uint16_t* cb = h.c1 + (size_t)g * h.K1 * D;
+  float sc[kMaxPer];
+#pragma unroll
+  for (int e = 0; e < kMaxPer; ++e) {
+    sc[e] = kNegInf;
+    const int j = lane + 64 * e;
+    if (j < h.K1) {
+      const u32x4* row = (const u32x4*)(cb + (size_t)j * D);
+      u32x4 rv[D / 8];
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) rv[c] = row[c];
+      float dot = 0.f, n2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const u32x4 v = rv[c];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float lo = bf16_bits_to_f32(v[w] & 0xFFFFu);
+          const float hi = bf16_bits_to_f32(v[w] >> 16);
+          dot = fmaf(qs[8 * c + 2 * w], lo, dot);
+          dot = fmaf(qs[8 * c + 2 * w + 1], hi, dot);
+          n2 = fmaf(lo, lo, n2);
+          n2 = fmaf(hi, hi, n2);
+        }
+      }
+      sc[e] = n2 > 0.f ? dot * rsqrtf(n2) : kNegInf;
+    }
   }
-  if (lane == 0) a.out_lse[bh] = lse_out;
+  // the m largest in (similarity desc, j asc) order, by wave ballots: u = ordered
+  // bits of the similarity; T = the m-th largest u by bisection; keep every u > T
+  // and the lowest-j entries with u == T until m are kept.  Lane l holds clusters
+  // l + 64 e, so e-major lane order is j order.
+  uint32_t u[kMaxPer];
+#pragma unroll
+  for (int e = 0; e < kMaxPer; ++e) u[e] = ordf(sc[e]);
+  auto count_ge = [&](uint32_t th) -> int {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < kMaxPer; ++e)
+      c += __popcll(__ballot(lane + 64 * e < h.K1 && u[e] >= th));
+    return c;
+  };
+  unsigned long long lo = 0, hi = 0xFFFFFFFFull;  // count_ge(lo) >= m throughout
+  while (lo < hi) {
+    const unsigned long long mid = (lo + hi + 1) >> 1;
+    if (count_ge((uint32_t)mid) >= h.m) lo = mid;
+    else hi = mid - 1;
+  }
+  const uint32_t T = (uint32_t)lo;
+  int above = 0;
+#pragma unroll
+  for (int e = 0; e < kMaxPer; ++e)
+    above += __popcll(__ballot(lane + 64 * e < h.K1 && u[e] > T));
+  int slot = 0, ties = h.m - above;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int e = 0; e < kMaxPer; ++e) {
+    const bool valid = lane + 64 * e < h.K1;
+    const unsigned long long eq = __ballot(valid && u[e] == T);
+    const int eq_before = __popcll(eq & below);
+    const bool keep = (valid && u[e] > T) || (valid && u[e] == T && eq_before < ties);
+    const unsigned long long kb = __ballot(keep);
+    if (keep) h.sel[((size_t)g * h.NQ + qi) * h.m + slot + __popcll(kb & below)] = lane + 64 * e;
+    slot += __popcll(kb);
+    ties -= min(ties, __popcll(eq));
+  }
+  if (lane == 0) h.best[(size_t)g * h.NQ + qi] = 0ull;
+}
+
+// One workgroup per (cluster, KV head): find the queries that kept the cluster
+// (a scan of the selections, up to 1024 queries per round), then score the
+// cluster's entries against them on MFMA, 16 queries x 16 entries per tile.
+constexpr int kHierRound = 1024;
+
+template <int D>
+__global__ __launch_bounds__(256) void asm_hier_score(HierArgs h) {
+  constexpr int KK = D / 32;
+  __shared__ int qlist[kHierRound];
+  __shared__ int nlist;
+  const AsmArgs& a = h.a;
+  const int j = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int nq = a.B * a.G;
+  const int32_t* offs = h.offs + (size_t)g * (h.K1 + 1);
+  const int m0 = min(max(offs[j], 0), a.K), m1 = min(max(offs[j + 1], m0), a.K);
+  if (m0 >= m1) return;
+  const int32_t* sel = h.sel + (size_t)g * h.NQ * h.m;
+  const uint16_t* cb = h.stored + (size_t)g * a.K * D;
+  const int32_t* kid = h.kid + (size_t)g * a.K;
+  for (int base = 0; base < nq; base += kHierRound) {
+    if (tid == 0) nlist = 0;
+    __syncthreads();
+    // a query keeps a cluster at most once: scan its selections in memory order
+    const int p1 = min(nq, base + kHierRound) * h.m;
+    for (int p0 = base * h.m + tid; p0 < p1; p0 += 4 * 256) {
+      int sv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[e] = p0 + 256 * e < p1 ? sel[p0 + 256 * e] : -1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (sv[e] == j) qlist[atomicAdd(&nlist, 1)] = (p0 + 256 * e) / h.m;
+    }
+    __syncthreads();
+    const int nl = nlist;
+    // Entries are the MFMA's A rows and queries its B columns, so lane (g4, c)
+    // holds entries 4 g4 .. 4 g4 + 3 of a tile for query c: the best over a wave's
+    // entry tiles needs two shuffles at the end.  Wave w takes entry tiles w, w + 4, ...
+    for (int qt = 0; qt < nl; qt += 16) {
+      const bool okq = qt + lc < nl;
+      u32x4 qb[KK];
+      load_query_rows<D>(a, g, okq ? qlist[qt + lc] : 0, okq, lg, qb);
+      unsigned long long pk = 0ull;
+      for (int mt = m0 + 16 * wave; mt < m1; mt += 64) {
+        u32x4 cv[KK];
+        const float n2 = load_columns<D>(cb + (size_t)min(mt + lc, m1 - 1) * D, lg, cv);
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) S = mfma_16x16x32_bf16(cv[kk], qb[kk], S);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int me = 4 * lg + i;                 // entry row of S[i]
+          const float n2e = __shfl(n2, me, 64);      // lanes 0..15 hold the 16 norms
+          if (mt + me < m1) {
+            const int kd = kid[mt + me];
+            const float sc = n2e > 0.f ? S[i] * rsqrtf(n2e) : kNegInf;
+            const unsigned long long key =
+                ((unsigned long long)ordf(sc) << 32) | (0xFFFFFFFFu - (uint32_t)kd);
+            pk = key > pk ? key : pk;
+          }
+        }
+      }
+      unsigned long long o2 = __shfl_xor(pk, 16, 64);
+      pk = o2 > pk ? o2 : pk;
+      o2 = __shfl_xor(pk, 32, 64);
+      pk = o2 > pk ? o2 : pk;
+      if (lg == 0 && okq && pk != 0ull) atomicMax(&h.best[(size_t)g * h.NQ + qlist[qt + lc]], pk);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(64) void asm_hier_finalize(HierArgs h) {
+  const AsmArgs& a = h.a;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, hh = bh - (bh / a.Hq) * a.Hq;
+  const int g = hh / a.G, jj = hh - g * a.G;
+  const int qi = b * a.G + jj;
+  const int lane = threadIdx.x;
+  float q2 = 0.f;
+  for (int d = lane; d < a.D; d += 64) {
+    const float x = bf16_bits_to_f32(a.q[(size_t)bh * a.D + d]);
+    q2 = fmaf(x, x, q2);
+  }
+  q2 = wave_sum(q2);
+  const unsigned long long pk = h.best[(size_t)g * h.NQ + qi];
+  int k = 0;
+  if (q2 > 0.f && pk != 0ull) {
+    k = (int)(0xFFFFFFFFu - (uint32_t)(pk & 0xFFFFFFFFull));
+    k = min(max(k, 0), a.K - 1);
+  }
+  if (a.idx && lane == 0) a.idx[bh] = k;
+  merge_entry(a, bh, g, k, lane);
 }
 
 static void asm_dims(int B, int Hq, int Hkv, int K, int& G, int& QB, int& KC) {
@@ -265,5 +518,92 @@ extern "C" int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_
   }
   TraceScope tr(kTrAsmFinalize, s);
   hipLaunchKernelGGL(asm_finalize, dim3(B * Hq), dim3(64), 0, s, a);
+  return launch_status();
+}
+
+static size_t hier_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t m, int& NQ,
+                          size_t& o_sel, size_t& o_best) {
+  const int G = Hq / Hkv;
+  NQ = B * G;
+  o_sel = kWsHeader;
+  o_best = o_sel + align_up((size_t)Hkv * NQ * m * 4, 256);
+  return o_best + align_up((size_t)Hkv * NQ * 8, 256);
+}
+
+extern "C" size_t asm_lookup_merge_hier_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t K1,
+                                                  int32_t m) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || K1 < 1 || K1 > kHierMaxK1 || m < 1 || m > K1)
+    return 0;
+  int NQ;
+  size_t a, b;
+  return hier_layout(B, Hq, Hkv, m, NQ, a, b);
+}
+
+extern "C" int32_t asm_lookup_merge_hier(const void* q, int32_t B, int32_t Hq, int32_t Hkv,
+                                         int32_t D, const void* c1, int32_t K1,
+                                         const int32_t* offs, const void* centroids,
+                                         const int32_t* kid, int32_t K, int32_t m,
+                                         const void* abar, const float* log_zbar,
+                                         const float* self_out, const float* self_lse,
+                                         float* out, float* out_lse, int32_t* idx, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  if (!q || !c1 || !offs || !centroids || !kid || !abar || !log_zbar || !self_out ||
+      !self_lse || !out || !out_lse)
+    return KVB_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || K < 1 || K >= (1 << 24)) return KVB_EINVAL;
+  if (K1 < 1 || K1 > kHierMaxK1 || m < 1 || m > K1) return KVB_EINVAL;
+  if (D != 64 && D != 128) return KVB_EUNSUPPORTED;
+  if ((long long)B * (Hq / Hkv) > 65536) return KVB_EINVAL;
+  int NQ;
+  size_t o_sel, o_best;
+  const size_t need = hier_layout(B, Hq, Hkv, m, NQ, o_sel, o_best);
+  if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
+  int32_t st = check_device();
+  if (st) return st;
+  HierArgs h;
+  memset(&h, 0, sizeof(h));
+  AsmArgs& a = h.a;
+  a.q = (const uint16_t*)q;
+  a.cent = nullptr;
+  a.abar = (const uint16_t*)abar;
+  a.log_zbar = log_zbar;
+  a.self_out = self_out;
+  a.self_lse = self_lse;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.idx = idx;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.K = K;
+  a.G = Hq / Hkv;
+  h.c1 = (const uint16_t*)c1;
+  h.offs = offs;
+  h.stored = (const uint16_t*)centroids;
+  h.kid = kid;
+  char* w = (char*)ws;
+  h.sel = (int32_t*)(w + o_sel);
+  h.best = (unsigned long long*)(w + o_best);
+  h.K1 = K1;
+  h.m = m;
+  h.NQ = NQ;
+  hipStream_t s = (hipStream_t)stream;
+  {
+    TraceScope tr(kTrAsmLookup, s);
+    if (D == 128)
+      hipLaunchKernelGGL(asm_hier_select<128>, dim3(NQ, Hkv), dim3(64), 0, s, h);
+    else
+      hipLaunchKernelGGL(asm_hier_select<64>, dim3(NQ, Hkv), dim3(64), 0, s, h);
+  }
+  {
+    TraceScope tr(kTrAsmLookup, s);
+    if (D == 128)
+      hipLaunchKernelGGL(asm_hier_score<128>, dim3(K1, Hkv), dim3(256), 0, s, h);
+    else
+      hipLaunchKernelGGL(asm_hier_score<64>, dim3(K1, Hkv), dim3(256), 0, s, h);
+  }
+  TraceScope tr(kTrAsmFinalize, s);
+  hipLaunchKernelGGL(asm_hier_finalize, dim3(B * Hq), dim3(64), 0, s, h);
   return launch_status();
 }

@@ -84,6 +84,8 @@ size_t kv_attn_decode_workspace(const kvb_cache* cache, int32_t Hq, int32_t num_
 size_t kv_evict_workspace(const kvb_cache* cache, int32_t M);
 size_t kv_erase_workspace(const kvb_cache* cache);
 size_t asm_lookup_merge_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t K);
+size_t asm_lookup_merge_hier_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t K1,
+                                       int32_t m);
 
 /*
  * Decode-step grouped-query attention with the retention bias, split over the KV
@@ -238,6 +240,34 @@ int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int3
                          int32_t K, const float* self_out, const float* self_lse, float* out,
                          float* out_lse, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * The same lookup and merge through a two-level index ([ASM] technical novelty:
+ * hierarchical lookup; experiments: expanding the top 16 first-level centroids
+ * matches the linear lookup's top-1).  Per query head h of sequence b (KV head g):
+ *   1. cos(q, c1[g][j]) for the K1 first-level centroids; keep the m largest
+ *      (equal similarities: the lower j first);
+ *   2. idx = the original index of the entry with the largest cos(q, c) among the
+ *      entries of the kept clusters (equal similarities: the lowest original
+ *      index); a zero query, or kept clusters without entries, give idx 0;
+ *   3. merge with (abar[g][idx], log_zbar[g][idx]) as asm_lookup_merge does.
+ *
+ *   c1         [Hkv][K1][D] bf16 first-level centroids, 1 <= K1 <= 512, 1 <= m <= K1
+ *   offs       [Hkv][K1 + 1] int32: the entries of cluster j are stored at positions
+ *              offs[j] .. offs[j+1]-1 (non-decreasing, offs[0] = 0, offs[K1] = K;
+ *              values outside [0, K] are clamped)
+ *   centroids  [Hkv][K][D] bf16, stored cluster by cluster
+ *   kid        [Hkv][K] int32: original index (0 .. K-1) of each stored entry
+ *   abar, log_zbar  by original index, as for asm_lookup_merge
+ *   other arguments as asm_lookup_merge.
+ *   ws         workspace of asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) bytes.
+ */
+int32_t asm_lookup_merge_hier(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                              const void* c1, int32_t K1, const int32_t* offs,
+                              const void* centroids, const int32_t* kid, int32_t K, int32_t m,
+                              const void* abar, const float* log_zbar, const float* self_out,
+                              const float* self_lse, float* out, float* out_lse, int32_t* idx,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Kernel timing (a measurement aid; off by default; not thread-safe).

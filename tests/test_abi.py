@@ -108,3 +108,35 @@ def test_invalid_arguments_rejected_before_launch():
     bad = list(base)
     bad[0] = None
     assert L.asm_lookup_merge(*bad) == -1
+
+
+@needs_lib
+def test_hier_lookup_arguments_rejected_before_launch():
+    """Fake pointers: the two-level lookup's validation runs on the host first."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    ws = P(4096)
+    # q, B, Hq, Hkv, D, c1, K1, offs, centroids, kid, K, m, abar, log_zbar, self_out,
+    # self_lse, out, out_lse, idx, ws, ws_bytes, stream
+    base = [P(8), 2, 8, 2, 128, P(8), 64, P(8), P(8), P(8), 4096, 16, P(8), P(8), P(8), P(8),
+            P(8), P(8), None, ws, 1 << 30, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.asm_lookup_merge_hier(*a)
+
+    assert call(a4=96) == -2                 # D
+    assert call(a2=7) == -1                  # Hq % Hkv
+    assert call(a6=0) == -1                  # K1
+    assert call(a6=513) == -1                # K1 above 512
+    assert call(a11=0) == -1                 # m
+    assert call(a11=65) == -1                # m above K1
+    assert call(a7=None) == -1               # offs
+    assert call(a9=None) == -1               # kid
+    assert call(a10=1 << 24) == -1           # K
+    assert call(a20=64) == -4                # workspace too small
+    assert L.asm_lookup_merge_hier_workspace(2, 8, 2, 64, 16) > 256
+    assert L.asm_lookup_merge_hier_workspace(2, 8, 2, 64, 65) == 0
+    assert L.asm_lookup_merge_hier_workspace(2, 8, 2, 600, 16) == 0
