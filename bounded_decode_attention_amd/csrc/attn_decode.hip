@@ -1098,6 +1098,7 @@ extern "C" int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q,
     a.tile_hi = 1 << 30;
     a.p_off = Pa;
     a.plan = fused_plan(cache, M, ws_evict);
+    launch_fused_stage(cache, M, ws_evict, s);
     a.kw = cache->k;
     a.vw = cache->v;
     a.lbw = cache->log_beta;

@@ -97,6 +97,9 @@ inline int fused_za(int M, int cap) {
 }
 bool plan_in_lds(const kvb_cache* c);
 FusedPlan fused_plan(const kvb_cache* c, int32_t M, void* ws);
+// Copies the fused apply's staged rows (kept rows below the boundary that move) to
+// the plan's scratch; must run after kv_evict_plan and before any row is written.
+void launch_fused_stage(const kvb_cache* c, int32_t M, void* ws, hipStream_t s);
 
 // Host: 0 if the current device is gfx950, else KVB_EDEVICE (cached per device).
 int32_t check_device();

@@ -266,7 +266,8 @@ struct PlanArgs {
   uint32_t* tile_mask;  // [U][Tc]
   int32_t* tile_base;   // [U][Tc]
   int32_t* stage_n;     // [U]
-  int2* stage_list;     // [U][Mk]
+  int2* stage_list;     // [U][Mk]: every kept row below za that moves (fused apply)
+  int2* copy_list;      // [U][Mk]: the subset compact_move reads from scratch
   const void* k;
   const void* v;
   int32_t cap, Hkv, M, Mk, max_evict, row_bytes, srow, move_rows, za, Tc;
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   __shared__ int smem[kSelThreads / 64];
   __shared__ int out[4];
   __shared__ unsigned long long mm[2];
-  __shared__ int ncand, nflag, nstage;
+  __shared__ int ncand, nflag, nstage, ncopy;
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
     ncand = 0;
     nflag = 0;
     nstage = 0;
+    ncopy = 0;
   }
   if (n <= M) {
     if (tid == 0) {
@@ -515,10 +517,10 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   const int sstar = out[2];
 
   // ---- keep masks per 32-slot tile (one ballot covers two tiles), tile bases by a
-  // scan, then per slot: destination (keep_src), evicted position, staging.  Kept
-  // rows whose source lies below za and differs from their destination are staged:
-  // any later move into [0, za) may overwrite them (za >= kept bounds every
-  // destination).
+  // scan, then per slot: destination (keep_src), evicted position, and two lists:
+  // kept rows below za that move (the fused apply writes into [0, za) while reading
+  // the rest, so it copies them to scratch first; za >= kept bounds every
+  // destination), and the subset compact_move reads from scratch.
   uint32_t* tmask = (uint32_t*)cand;  // kCand >= tiles: the keys fit in LDS
   const int T = (n + 31) >> 5;
   {
@@ -564,6 +566,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   __syncthreads();
   const int kept = min(kept_all, a.Mk);
   int2* slist = a.stage_list + (size_t)u * a.Mk;
+  int2* clist = a.copy_list + (size_t)u * a.Mk;
   {
     constexpr int kU = 4;
     for (int i0 = tid; i0 < n; i0 += kU * kSelThreads) {
@@ -584,7 +587,13 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
         if ((mk[e] >> s2) & 1u) {
           if (before < a.Mk) {
             a.keep_src[(size_t)u * a.Mk + before] = i;
-            if (i != before && i < a.za) slist[atomicAdd(&nstage, 1)] = make_int2(i, before);
+            if (i != before && i < a.za) {
+              slist[atomicAdd(&nstage, 1)] = make_int2(i, before);
+              // compact_move's hazard rule: the source lies below kept and inside a
+              // later group's destination range
+              if (i < kept && i >= (before / a.move_rows + 1) * a.move_rows)
+                clist[atomicAdd(&ncopy, 1)] = make_int2(i, before);
+            }
           }
         } else if (a.evicted_pos) {
           const int ev = i - before;
@@ -594,10 +603,11 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
     }
   }
   __syncthreads();
-  // ---- staged rows to scratch: 16-byte pieces (K, V) and the 8-byte row tails;
-  // each thread loads a batch of pieces before storing any
+  // ---- the rows compact_move will read from scratch, copied there: 16-byte pieces
+  // (K, V) and the 8-byte row tails; each thread loads a batch before storing any.
+  // (The fused apply copies the rest of the stage list itself.)
   {
-    const int ns = min(nstage, a.Mk);
+    const int ns = min(ncopy, a.Mk);
     const int ppr = a.row_bytes / 16;
     const int per = 2 * ppr + 1;
     const unsigned char* kb = (const unsigned char*)a.k + (size_t)u * a.cap * a.row_bytes;
@@ -612,7 +622,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
         to[e] = nullptr;
         if (q < ns * per) {
           const int en = q / per, part = q - en * per;
-          const int2 sd = slist[en];
+          const int2 sd = clist[en];
           unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
           if (part < 2 * ppr) {
             const bool isv = part >= ppr;
@@ -898,7 +908,8 @@ static size_t plan_lds_limit() {
 }
 
 struct CompactLayout {
-  size_t info, counts, keep_src, scratch, tile_mask, tile_base, stage_n, stage_list, total;
+  size_t info, counts, keep_src, scratch, tile_mask, tile_base, stage_n, stage_list, copy_list,
+      total;
   int C, Mk, srow, move_rows, row_bytes, Tc;
 };
 
@@ -924,7 +935,8 @@ static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
   L.tile_base = L.tile_mask + align_up(U * L.Tc * sizeof(uint32_t), 256);
   L.stage_n = L.tile_base + align_up(U * L.Tc * sizeof(int32_t), 256);
   L.stage_list = L.stage_n + align_up(U * sizeof(int32_t), 256);
-  L.total = L.stage_list + align_up(U * L.Mk * sizeof(int2), 256);
+  L.copy_list = L.stage_list + align_up(U * L.Mk * sizeof(int2), 256);
+  L.total = L.copy_list + align_up(U * L.Mk * sizeof(int2), 256);
   return L;
 }
 
@@ -1013,6 +1025,7 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     pa.tile_base = (int32_t*)(w + L.tile_base);
     pa.stage_n = (int32_t*)(w + L.stage_n);
     pa.stage_list = (int2*)(w + L.stage_list);
+    pa.copy_list = (int2*)(w + L.copy_list);
     pa.Tc = L.Tc;
     pa.za = fused_za(M, cache->cap);
     pa.vec = cache->cap % 4 == 0;
@@ -1036,6 +1049,51 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
 bool plan_in_lds(const kvb_cache* c) {
   const size_t lds_keys = ((size_t)c->cap + c->cap / 32 + 1) * sizeof(uint32_t);
   return lds_keys <= plan_lds_limit() && (c->cap + 31) / 32 <= kCand;
+}
+
+// Copies every row of the stage list (kept rows below za that move) to scratch, by
+// destination, for the fused apply; one workgroup per (head, 64 entries).
+__global__ __launch_bounds__(256) void fused_stage_copy(const UnitInfo* info, const int32_t* stage_n,
+                                                        const int2* stage_list, unsigned char* scratch,
+                                                        const void* k, const void* v,
+                                                        const float* log_beta, const int32_t* pos,
+                                                        int cap, int Mk, int srow, int row_bytes) {
+  const int u = blockIdx.y;
+  if (info[u].mode != MODE_EVICT) return;
+  const int ns = min(stage_n[u], Mk);
+  const int e0 = blockIdx.x * 64;
+  if (e0 >= ns) return;
+  const int ppr = row_bytes / 16, per = 2 * ppr + 1;
+  const int e1 = min(ns, e0 + 64);
+  const unsigned char* kb = (const unsigned char*)k + (size_t)u * cap * row_bytes;
+  const unsigned char* vb = (const unsigned char*)v + (size_t)u * cap * row_bytes;
+  const int2* sl = stage_list + (size_t)u * Mk;
+  for (int q = threadIdx.x; q < (e1 - e0) * per; q += 256) {
+    const int en = e0 + q / per, part = q % per;
+    const int2 sd = sl[en];
+    unsigned char* sp = scratch + ((size_t)u * Mk + sd.y) * srow;
+    if (part < 2 * ppr) {
+      const bool isv = part >= ppr;
+      const int pc = isv ? part - ppr : part;
+      *(u32x4*)(sp + (isv ? row_bytes : 0) + 16 * pc) =
+          *(const u32x4*)((isv ? vb : kb) + (size_t)sd.x * row_bytes + 16 * pc);
+    } else {
+      int32_t* tail = (int32_t*)(sp + 2 * row_bytes);
+      tail[0] = log_beta ? __float_as_int(log_beta[(size_t)u * cap + sd.x]) : 0;
+      tail[1] = pos[(size_t)u * cap + sd.x];
+    }
+  }
+}
+
+void launch_fused_stage(const kvb_cache* c, int32_t M, void* ws, hipStream_t s) {
+  const CompactLayout L = compact_layout(c, M < c->cap ? M : c->cap);
+  char* w = (char*)ws;
+  const int U = c->B * c->Hkv;
+  dim3 grid((L.Mk + 63) / 64, U);
+  hipLaunchKernelGGL(fused_stage_copy, grid, dim3(256), 0, s, (const UnitInfo*)(w + L.info),
+                     (const int32_t*)(w + L.stage_n), (const int2*)(w + L.stage_list),
+                     (unsigned char*)(w + L.scratch), c->k, c->v, c->log_beta, c->pos, c->cap,
+                     L.Mk, L.srow, L.row_bytes);
 }
 
 FusedPlan fused_plan(const kvb_cache* c, int32_t M, void* ws) {

@@ -185,7 +185,8 @@ int32_t kv_evict_apply(const kvb_cache* cache, int32_t M, void* ws, size_t ws_by
  * compacted slot from the data the attention already loaded, so the separate
  * re-read of kept rows disappears.  All destinations lie below M rounded up to 32
  * slots; those tiles are attended first (phase 1), the rest afterwards (phase 2,
- * which also moves rows, merges the split states and sets len).
+ * which first copies the kept rows below that boundary that move to the plan's
+ * scratch, then moves rows, merges the split states and sets len).
  *   phase 0  both phases on `stream` (the plan must be complete before the call)
  *   phase 1  attention over the first tiles only; needs no plan, so it may run
  *            concurrently with kv_evict_plan (which only reads the cache)
