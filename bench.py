@@ -82,6 +82,107 @@ def cpu_baseline(w, host_units, t, M, budget_s=12.0):
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def steady_bench(args):
+    """Steady-state decode of the 32K workload's model shape under its budget: every
+    KV head of the 36 layers holds M = 4096 tokens; a step appends one token per
+    layer, attends over M + 1, evicts the lowest-retention token and compacts (every
+    kept row after the evicted slot moves down by one).  Eviction planning runs on a
+    second stream beside the attention, the compaction after it; the whole step is
+    captured once in a HIP graph and replayed (t advances on the device).  A second,
+    eager run of the same steps with the library's HIP-event trace gives the
+    per-kernel split."""
+    import dataclasses
+
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.layers:
+        w = dataclasses.replace(w, layers=args.layers)
+    L, M, B = w.layers, w.budget, w.batch
+    print(f"# generating {L} layers of {w.name} with {M} tokens per KV head", file=sys.stderr,
+          flush=True)
+    kvs, qs = [], []
+    for layer in range(L):
+        d = synth.device_cache(w, layer, n=M, cap=M + 32)
+        kvs.append(kvb.KVCache.from_dict(d))
+        qs.append(synth.device_queries(w, layer))
+    out = torch.empty((B, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, w.hq), dtype=torch.float32, device="cuda")
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, args.splits), dtype=torch.uint8,
+                       device="cuda")
+    ws_e = [torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device="cuda")
+            for _ in range(L)]
+    nev = torch.empty((L, B, w.hkv), dtype=torch.int32, device="cuda")
+    t = torch.full((B,), M, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    appended = [torch.cuda.Event() for _ in range(L)]
+    attended = [torch.cuda.Event() for _ in range(L)]
+
+    def step():
+        main = torch.cuda.current_stream()
+        for layer in range(L):
+            q, kn, vn, lb = qs[layer]
+            kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
+            appended[layer].record(main)
+            side.wait_event(appended[layer])
+            kvb.kv_evict_plan(kvs[layer], t, M, n_evicted=nev[layer], ws=ws_e[layer], stream=side)
+            kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=out, lse=lse,
+                               ws=ws_a, stream=main)
+            attended[layer].record(main)
+            side.wait_event(attended[layer])
+            kvb.kv_evict_apply(kvs[layer], M, ws_e[layer], stream=side)
+        main.wait_stream(side)
+        t.add_(1)
+
+    for _ in range(args.warmup + 1):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert bool((nev == 1).all()), "steady state: one eviction per head and layer"
+    # eager steps with the kernel trace
+    kvb.trace_enable(16 * L * args.steps + 64, ("attn_split", "attn_merge", "append",
+                                                "evict_select", "compact_move"))
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    per = {}
+    for name, kms in kvb.trace_read(1 << 20):
+        per.setdefault(name, []).append(kms)
+    kvb.trace_disable()
+    split = {k: round(sum(v) / len(v) * 1000, 1) for k, v in per.items()}
+    n = M + 1
+    attn_b = algorithmic_bytes(w, n, 0)[0]
+    print(json.dumps({
+        "metric": "steady-state bounded-KV decode steps/s (evict 1 of M+1 per layer and step)",
+        "value": round(1000.0 / ms, 3), "unit": "decode steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True},
+        "eager_ms_per_step": round(eager_ms, 4), "kernel_us_eager": split,
+        "attention_bytes_per_layer": attn_b}), flush=True)
+
+
 def asm_bench(args):
     """Lookup + merge for one layer of the ASM workload's queries (32 sequences x 32
     query heads, 8 KV heads, D = 128): the linear scan and the two-level index
@@ -171,6 +272,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
+    ap.add_argument("--steady", action="store_true",
+                    help="time the steady-state decode loop instead: every KV head holds M "
+                         "tokens, each step appends one and evicts one (one JSON line)")
     ap.add_argument("--asm-lookup", action="store_true",
                     help="time the attention-state-memory lookup + merge instead: linear and "
                          "two-level index at 4K, 16K and 64K entries per KV head (one JSON line)")
@@ -190,6 +294,9 @@ def main():
         return
     if args.asm_lookup:
         asm_bench(args)
+        return
+    if args.steady:
+        steady_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "

@@ -828,6 +828,9 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
     if (j0 >= kept) continue;
     const int rows = min(a.move_rows, kept - j0);
     const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
+    // src - dst never decreases along the destinations: if the group's last row
+    // stays in place, every row of the group does
+    if (ks[j0 + rows - 1] == j0 + rows - 1) continue;
     const unsigned char* scr = a.scratch + (size_t)u * a.Mk * a.srow;
     unsigned char* tb = (unsigned char*)(isv ? a.v : a.k) + (size_t)u * a.cap * a.row_bytes;
     float* lbb = a.log_beta ? (float*)a.log_beta + (size_t)u * a.cap : nullptr;
@@ -982,7 +985,9 @@ static void launch_keep_chunks(const kvb_cache* c, const KeepArgs& a, int mode, 
 static void launch_move(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s) {
   const int U = c->B * c->Hkv;
   const long long items = (long long)U * ((a.Mk + a.move_rows - 1) / a.move_rows);
-  const int blocks = (int)(items < 1024 ? items : 1024);  // persistent: 4 per CU
+  // one group per workgroup (many in flight hide the read latency); the kernel
+  // strides over groups if there are more than this
+  const int blocks = (int)(items < (1 << 20) ? items : (1 << 20));
   TraceScope tr(kTrCompactMove, s);
   hipLaunchKernelGGL(compact_move, dim3(blocks), dim3(kMoveThreads), 0, s, a, U,
                      mode == MODE_EVICT ? 1 : 0);

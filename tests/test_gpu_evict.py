@@ -222,3 +222,48 @@ def test_memento_full_size():
                         f"memento attention g={g}")
     del dc, c
     torch.cuda.empty_cache()
+
+
+def test_steady_state_full_shape():
+    """The 32K workload's layer shape at its budget: every head holds M = 4096
+    tokens; three steps of append + attention + evict 1 + compact.  Every head's
+    compacted rows against the oracle's plan; attention of sampled heads against the
+    oracle."""
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    M = w.budget
+    dc = synth.device_cache(w, layer=3, n=M, cap=M + 32)
+    c = kvb.KVCache.from_dict(dc)
+    G = w.group
+    for s in range(3):
+        say("steady step", s)
+        q, kn, vn, lbn = synth.device_queries(w, 3, step=s)
+        t = torch.full((w.batch,), M + s, dtype=torch.int32, device="cuda")
+        kvb.kv_append(c, kn, vn, lbn, t)
+        torch.cuda.synchronize()
+        n = M + 1
+        units = [(0, 0), (9, 5), (15, 7)]
+        sub = {(b, g): {k: to_host(getattr(c, k)[b:b + 1, g:g + 1, :n])
+                        for k in ("k", "v", "log_beta", "pos")} for (b, g) in units}
+        out, lse = kvb.kv_attn_decode(c, q, t)
+        lbh = to_host(c.log_beta[:, :, :n])
+        ph = to_host(c.pos[:, :, :n])
+        keep = {}
+        for b in range(w.batch):
+            for g in range(w.hkv):
+                k, _ = oracle.evict_plan(lbh[b, g], ph[b, g], n, M + s, M)
+                keep[(b, g)] = np.nonzero(k)[0]
+        snap = snapshot_rows(c, keep)
+        n_ev = kvb.kv_evict_to_budget(c, t, M)
+        torch.cuda.synchronize()
+        check_compacted(c, snap, f"steady {s}")
+        assert (to_host(n_ev) == 1).all()
+        oh, lh, qh = to_host(out), to_host(lse), to_host(q)
+        for (b, g), d in sub.items():
+            ro, rl = oracle.decode_attention(values(d["k"]), values(d["v"]), d["log_beta"],
+                                             d["pos"], np.array([[n]], np.int32),
+                                             values(qh[b:b + 1, g * G:(g + 1) * G]),
+                                             np.array([M + s]))
+            check_attention(oh[b:b + 1, g * G:(g + 1) * G], lh[b:b + 1, g * G:(g + 1) * G],
+                            ro, rl, f"steady {s} ({b},{g})")
+    del dc, c
+    torch.cuda.empty_cache()
