@@ -25,6 +25,9 @@ Every function is a direct, unblocked statement of what the pages define:
   (Context Memorization, method steps, steps 3 and 4; GQA extension in the
   technical-novelty section), and the two-level (hierarchical) lookup of the
   same section.
+* ``asm_build``   -- construction of that memory: prefix attention states of
+  calibration queries (chunked and merged), K-means over the queries, and the
+  merge of each cluster's states (Context Memorization, method steps 1 and 2).
 * ``bytes_model`` -- KV bytes per token, pinned to IndexMem's memory-wall figure
   ("IndexMem: Learned KV-Cache Eviction with Latent Memory for Long-Context LLM
   Inference", technical summary, section 1).
@@ -41,6 +44,8 @@ from .evict import (retention_keys, evict_plan, erase_plan, compact_unit,
                        Cache, evict_to_budget, erase_ranges, append_tokens)
 from .asm import (cosine_similarities, cosine_lookup, asm_merge, asm_lookup_merge,
                   hier_lookup, asm_lookup_merge_hier)
+from .asm_build import (chunk_bounds, prefix_states, nearest_centroid, centroid_update,
+                        kmeans, aggregate_states, build_memory)
 from .bytes_model import kv_bytes_per_token, attention_layer_bytes
 from .decode import run_decode_steps
 
@@ -51,5 +56,7 @@ __all__ = [
     "evict_to_budget", "erase_ranges", "append_tokens",
     "cosine_similarities", "cosine_lookup", "asm_merge", "asm_lookup_merge",
     "hier_lookup", "asm_lookup_merge_hier",
+    "chunk_bounds", "prefix_states", "nearest_centroid", "centroid_update", "kmeans",
+    "aggregate_states", "build_memory",
     "kv_bytes_per_token", "attention_layer_bytes", "run_decode_steps",
 ]

@@ -82,12 +82,20 @@ WORKLOADS = {
                            seed=1005, retention=False),
     # two-level ASM lookup: 16K entries per KV head in 128 first-level clusters,
     # the top 16 first-level centroids expanded
+    "asm_build": Workload("asm_build", batch=1, hq=32, hkv=8, head_dim=128,
+                          dtype="bf16", ctx=16384, budget=1 << 30, layers=1, seed=1007,
+                          retention=False, codebook=4096),
     "asm_hier": Workload("asm_hier", batch=32, hq=32, hkv=8, head_dim=128,
                          dtype="bf16", ctx=2048, budget=1 << 30, layers=36,
                          seed=1006, retention=False, codebook=16384),
 }
 HIER_K1 = 128
 HIER_M = 16
+# ASM memory construction: per KV head a 16K-token prefix encoded in 4 chunks,
+# 16K calibration queries clustered into K = 4096 entries by 10 Lloyd iterations
+BUILD_N = 16384
+BUILD_CHUNKS = 4
+BUILD_ITERS = 10
 
 
 # --------------------------------------------------------------------------
@@ -244,6 +252,27 @@ def host_near_queries(w: Workload, entries, noise: float = 0.5, seed_offset: int
     q = c[g, k] + noise * rng.standard_normal((B, w.hq, D)) / np.sqrt(D)
     q *= np.abs(rng.standard_normal((B, w.hq, 1))) + 0.5
     return bf16_bits(q)
+
+
+def host_asm_build(w: Workload, N: int, L: int | None = None, topics: int = 512,
+                   seed_offset: int = 41):
+    """Calibration data for building a memory, per KV head.
+
+    Prefix K, V [Hkv][L][D] ~ N(0, 1); calibration queries Q [Hkv][N][D] drawn
+    around `topics` random directions: q = 2 (u_topic + 0.6 N(0, I/D)) scaled by
+    (|N(0,1)| + 0.5), so that K-means has structure to find.  bf16 bits.
+    """
+    L = w.ctx if L is None else L
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    H, D = w.hkv, w.head_dim
+    Kp = bf16_bits(rng.standard_normal((H, L, D)))
+    Vp = bf16_bits(rng.standard_normal((H, L, D)))
+    u = rng.standard_normal((H, topics, D))
+    u /= np.sqrt((u * u).sum(-1, keepdims=True))
+    tpc = rng.integers(0, topics, size=(H, N))
+    q = u[np.arange(H)[:, None], tpc] + 0.6 * rng.standard_normal((H, N, D)) / np.sqrt(D)
+    q *= 2.0 * (np.abs(rng.standard_normal((H, N, 1))) + 0.5)
+    return bf16_bits(q), Kp, Vp
 
 
 def memento_layout(total: int = 1 << 20, seed: int = 1005, memento: int = 200,

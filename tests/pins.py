@@ -18,6 +18,7 @@ import scipy.special
 import torch
 
 import oracle.asm as OA
+import oracle.asm_build as OAB
 import oracle.attn as OT
 import oracle.bytes_model as OB
 import oracle.evict as OE
@@ -365,6 +366,66 @@ def check_hier_lookup(seed=10):
                           np.array([0, 0, 3]), Ct, np.array([7, 4, 5]), 1) == 0
 
 
+# ---------------------------------------------------------------- P11
+def check_asm_build(seed=11):
+    """Memory construction: chunked prefix states equal one-pass attention and a
+    library attention routine; K-means on hand-checked 1-D data, its tie rule, an
+    empty cluster, blob recovery and a non-increasing objective; the aggregation as
+    its closed form."""
+    r = _rng(seed)
+    # (1) prefix states: any chunking = one pass = SDPA
+    for L, D in ((1, 4), (37, 8), (200, 16)):
+        Kp = r.standard_normal((L, D))
+        Vp = r.standard_normal((L, D))
+        Q = r.standard_normal((5, D)) * 2.0
+        scale = 1.0 / math.sqrt(D)
+        a1, l1 = OAB.prefix_states(Q, Kp, Vp, scale, 1)
+        for ch in (2, 3, 4, L + 5):
+            a2, l2 = OAB.prefix_states(Q, Kp, Vp, scale, ch)
+            assert np.allclose(a1, a2, rtol=0, atol=1e-12) and np.allclose(l1, l2, rtol=0,
+                                                                            atol=1e-12)
+        for i in range(Q.shape[0]):
+            ref = _sdpa(Q[i], Kp, Vp, scale)
+            assert np.allclose(a1[i], ref, rtol=0, atol=1e-12), "prefix state != SDPA"
+            s_ = scale * (Kp @ Q[i])
+            assert abs(l1[i] - scipy.special.logsumexp(s_)) < 1e-12, "prefix lse != logsumexp"
+    assert OAB.chunk_bounds(10, 4) == [(0, 3), (3, 6), (6, 9), (9, 10)]
+    # (2) K-means, 1-D by hand: {0, 1, 10, 11, 12} from {0, 12} -> {0.5, 11}
+    X = np.array([[0.0], [1.0], [10.0], [11.0], [12.0]])
+    assign, C = OAB.kmeans(X, np.array([[0.0], [12.0]]), 3)
+    assert list(assign) == [0, 0, 1, 1, 1] and np.allclose(C[:, 0], [0.5, 11.0])
+    # equidistant -> lower index; a centroid with no members stays put
+    assert OAB.nearest_centroid(np.array([1.0]), np.array([[0.0], [2.0]])) == 0
+    assign, C = OAB.kmeans(X, np.array([[0.0], [12.0], [1000.0]]), 2)
+    assert C[2, 0] == 1000.0 and not np.any(assign == 2)
+    # separated blobs, one seed point in each: one iteration recovers the blobs;
+    # the within-cluster sum of squares never increases
+    centers = r.standard_normal((5, 8)) * 20.0
+    lab = r.integers(0, 5, size=300)
+    lab[:5] = np.arange(5)
+    Xb = centers[lab] + r.standard_normal((300, 8))
+    assign, _ = OAB.kmeans(Xb, Xb[:5], 1)
+    assert np.array_equal(assign, lab), "blobs not recovered"
+    Xr = r.standard_normal((120, 6))
+    C = Xr[:7].copy()
+    prev = np.inf
+    for _ in range(6):
+        assign, C = OAB.kmeans(Xr, C, 1)
+        sse = float(np.sum((Xr - C[assign]) ** 2))
+        assert sse <= prev + 1e-9, "K-means objective increased"
+        prev = sse
+    # (3) aggregation: Z-weighted mean of outputs, normalisers added
+    a = r.standard_normal((4, 3))
+    lse = np.array([2.0, -1.0, 0.5, -np.inf])
+    assign = np.array([1, 1, 0, 0])
+    abar, lz = OAB.aggregate_states(assign, a, lse, 3)
+    w = np.exp(lse[:2])
+    assert np.allclose(abar[1], (w[0] * a[0] + w[1] * a[1]) / (w[0] + w[1]), atol=1e-14)
+    assert abs(lz[1] - math.log(w[0] + w[1])) < 1e-14
+    assert np.allclose(abar[0], a[2]) and abs(lz[0] - 0.5) < 1e-14   # -inf member adds nothing
+    assert lz[2] == -np.inf and not np.any(abar[2])                   # empty cluster
+
+
 # ---------------------------------------------------------------- P9
 def check_bytes_model():
     """IndexMem's memory-wall estimate: ~320 GB of KV for a 70B model at 1M tokens."""
@@ -375,4 +436,4 @@ def check_bytes_model():
 ALL = [check_attention_library, check_bias_closed_form, check_split_merge,
        check_asm_lossless, check_evict_bruteforce, check_evict_sliding_window,
        check_evict_invariants, check_compaction, check_erase_bruteforce,
-       check_lookup_bruteforce, check_hier_lookup, check_bytes_model]
+       check_lookup_bruteforce, check_hier_lookup, check_asm_build, check_bytes_model]

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.asm as OA
+import oracle.asm_build as OAB
 import oracle.attn as OT
 import oracle.evict as OE
 import pins
@@ -19,6 +20,8 @@ _orig_merge = OT.merge_states
 _orig_keys = OE.retention_keys
 _orig_plan = OE.evict_plan
 _orig_hier = OA.hier_lookup
+_orig_update = OAB.centroid_update
+_orig_bounds = OAB.chunk_bounds
 
 
 def bias_sign_flipped(log_beta, pos, t):
@@ -179,6 +182,52 @@ def hier_tie_by_position(q, c1, offs, centroids, kid, m):
     return _hier(q, c1, offs, centroids, kid, m, tie_pos=True)
 
 
+def nearest_by_cosine(x, C):
+    C = np.asarray(C, np.float64)
+    x = np.asarray(x, np.float64)
+    cos = (C @ x) / (np.linalg.norm(C, axis=1) * np.linalg.norm(x) + 1e-300)
+    return int(np.argmax(cos))
+
+
+def nearest_ties_high(x, C):
+    d2 = np.sum((np.asarray(C, np.float64) - np.asarray(x, np.float64)) ** 2, axis=1)
+    return int(len(d2) - 1 - np.argmin(d2[::-1]))
+
+
+def update_sum_not_mean(X, assign, C):
+    C = np.array(C, np.float64)
+    for k in range(C.shape[0]):
+        members = np.asarray(X, np.float64)[assign == k]
+        if members.shape[0]:
+            C[k] = members.sum(axis=0)
+    return C
+
+
+def update_empty_to_zero(X, assign, C):
+    C2 = _orig_update(X, assign, C)
+    for k in range(C2.shape[0]):
+        if not np.any(assign == k):
+            C2[k] = 0.0
+    return C2
+
+
+def aggregate_plain_average(assign, a, lse, K):
+    a = np.asarray(a, np.float64)
+    abar = np.zeros((K, a.shape[1]))
+    lz = np.full(K, -np.inf)
+    for k in range(K):
+        idx = np.nonzero(np.asarray(assign) == k)[0]
+        if idx.size:
+            abar[k] = a[idx].mean(axis=0)
+            lz[k] = np.logaddexp.reduce(np.asarray(lse)[idx])
+    return abar, lz
+
+
+def bounds_drop_last(L, chunks):
+    b = _orig_bounds(L, chunks)
+    return b[:-1] if len(b) > 1 else b
+
+
 def compact_reversed(cache, b, g, keep):
     n = keep.shape[0]
     idx = np.nonzero(keep)[0][::-1]
@@ -214,6 +263,12 @@ MUTANTS = [
     (OA, "hier_lookup", hier_first_tie_high),
     (OA, "hier_lookup", hier_returns_position),
     (OA, "hier_lookup", hier_tie_by_position),
+    (OAB, "nearest_centroid", nearest_by_cosine),
+    (OAB, "nearest_centroid", nearest_ties_high),
+    (OAB, "centroid_update", update_sum_not_mean),
+    (OAB, "centroid_update", update_empty_to_zero),
+    (OAB, "aggregate_states", aggregate_plain_average),
+    (OAB, "chunk_bounds", bounds_drop_last),
 ]
 
 
