@@ -257,6 +257,91 @@ def asm_bench(args):
         "sizes": rows}), flush=True)
 
 
+def build_bench(args):
+    """Offline build of one layer's attention-state memory (8 KV heads; per head
+    16,384 calibration queries, a 16,384-token prefix encoded in 4 chunks, K-means
+    into 4,096 entries for 10 iterations from 4,096 of the queries, then
+    aggregation of the states).  Inputs are resident on the device; a step is one
+    asm_build_memory call (the initial centroids are copied in first, a 16 MB
+    device copy).  Kernel split and the MFMA roofline come from the library's
+    HIP-event trace of one traced step."""
+    import numpy as np
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS["asm_build"]
+    H, N, L, D, K = w.hkv, synth.BUILD_N, w.ctx, w.head_dim, w.codebook
+    C, iters = synth.BUILD_CHUNKS, synth.BUILD_ITERS
+    q, k, v = synth.host_asm_build(w, N)
+    init = synth.host_kmeans_init(w, q, K)
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(
+                torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    dq, dk, dv, dinit = map(dev, (q, k, v, init))
+    cent = torch.empty_like(dinit)
+    cb = torch.empty((H, K, D), dtype=torch.bfloat16, device="cuda")
+    ab = torch.empty((H, K, D), dtype=torch.bfloat16, device="cuda")
+    lz = torch.empty((H, K), dtype=torch.float32, device="cuda")
+    asg = torch.empty((H, N), dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvb.asm_build_memory_workspace(H, N, D, L, C, K), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        cent.copy_(dinit)
+        kvb.asm_build_memory(dq, dk, dv, cent, iters, chunks=C, centroids_bf16=cb, abar=ab,
+                             log_zbar=lz, assign=asg, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    names = ("asm_prefix", "asm_prefix_merge", "km_assign", "km_update", "asm_aggregate")
+    kvb.trace_enable(64, names)
+    step()
+    split = {}
+    for name, t in kvb.trace_read():
+        tot, n = split.get(name, (0.0, 0))
+        split[name] = (tot + t, n + 1)
+    kvb.trace_disable()
+    flops = {"asm_prefix": 4.0 * H * N * L * D,          # S = QK^T and O = PV, per launch
+             "km_assign": 2.0 * H * N * K * D}           # X C^T, per launch
+    kern = {}
+    for name, (tot, n) in split.items():
+        row = {"launches": n, "total_ms": round(tot, 4), "avg_ms": round(tot / n, 4)}
+        if name in flops:
+            row["tflops"] = round(flops[name] / (tot / n * 1e-3) / 1e12, 1)
+        kern[name] = row
+    dom = max(flops, key=lambda nm: split.get(nm, (0.0, 1))[0])
+    tot, n = split[dom]
+    ach = flops[dom] / (tot / n * 1e-3) / 1e12
+    print(f"# kernels {kern}", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "ASM memory build time per layer (prefix states, K-means, aggregation)",
+        "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "asm_build", "kv_heads": H, "head_dim": D, "queries": N,
+                   "prefix": L, "chunks": C, "entries": K, "iters": iters},
+        "kernels": kern,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4),
+                     "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +363,9 @@ def main():
     ap.add_argument("--asm-lookup", action="store_true",
                     help="time the attention-state-memory lookup + merge instead: linear and "
                          "two-level index at 4K, 16K and 64K entries per KV head (one JSON line)")
+    ap.add_argument("--asm-build", action="store_true",
+                    help="time the offline build of one layer's attention-state memory "
+                         "(prefix states in 4 chunks, K-means, aggregation; one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy kernel 5 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -294,6 +382,9 @@ def main():
         return
     if args.asm_lookup:
         asm_bench(args)
+        return
+    if args.asm_build:
+        build_bench(args)
         return
     if args.steady:
         steady_bench(args)

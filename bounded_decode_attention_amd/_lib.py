@@ -60,6 +60,14 @@ def library():
                                        SZ, P]),
             "asm_lookup_merge_hier": (I32, [P, I32, I32, I32, I32, P, I32, P, P, P, I32, I32, P,
                                             P, P, P, P, P, P, P, SZ, P]),
+            "asm_prefix_states_workspace": (SZ, [I32, I32, I32, I32, I32]),
+            "asm_kmeans_workspace": (SZ, [I32, I32, I32]),
+            "asm_build_memory_workspace": (SZ, [I32, I32, I32, I32, I32, I32]),
+            "asm_prefix_states": (I32, [P, I32, I32, I32, P, P, I32, I32, F, P, P, P, SZ, P]),
+            "asm_kmeans": (I32, [P, I32, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
+            "asm_aggregate_states": (I32, [P, P, P, I32, I32, I32, I32, P, P, P]),
+            "asm_build_memory": (I32, [P, I32, I32, I32, P, P, I32, I32, F, P, I32, I32, P, P, P,
+                                       P, P, SZ, P]),
             "kvb_trace_enable": (I32, [I32, I32]),
             "kvb_trace_read": (I32, [P, P, I32]),
             "kvb_trace_reset": (None, []),
@@ -330,7 +338,9 @@ def asm_lookup_merge(q, centroids, abar, log_zbar, self_out, self_lse, out=None,
 
 TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "keep_count": 16, "keep_emit": 32, "compact_move": 64, "asm_lookup": 128,
-              "asm_finalize": 256, "attn_fused": 512}
+              "asm_finalize": 256, "attn_fused": 512, "asm_prefix": 1024,
+              "asm_prefix_merge": 2048, "km_assign": 4096, "km_update": 8192,
+              "asm_aggregate": 16384}
 
 
 def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:
@@ -395,3 +405,126 @@ def trace_reset():
 
 def trace_disable():
     library().kvb_trace_disable()
+
+
+def asm_prefix_states_workspace(H, N, D, L, chunks) -> int:
+    return int(library().asm_prefix_states_workspace(H, N, D, L, chunks))
+
+
+def asm_kmeans_workspace(H, K, D) -> int:
+    return int(library().asm_kmeans_workspace(H, K, D))
+
+
+def asm_build_memory_workspace(H, N, D, L, chunks, K) -> int:
+    return int(library().asm_build_memory_workspace(H, N, D, L, chunks, K))
+
+
+def _prefix_shapes(q, k, v):
+    _need(q, "q", torch.bfloat16)
+    H, N, D = q.shape
+    if k is None or v is None:
+        raise ValueError("k and v are required (shape [H][0][D] for an empty prefix)")
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    if k.dim() != 3 or tuple(k.shape) != tuple(v.shape) or k.shape[0] != H or k.shape[2] != D:
+        raise ValueError("k, v must be [H][L][D] matching q [H][N][D]")
+    return H, N, D, k.shape[1]
+
+
+def asm_prefix_states(q, k, v, chunks: int = 1, scale: float = 0.0, a=None, lse=None, ws=None,
+                      stream=None):
+    """States (a [H][N][D] f32, lse [H][N] f32) of the queries q [H][N][D] over the
+    prefix k, v [H][L][D], computed in `chunks` chunks and merged."""
+    H, N, D, L = _prefix_shapes(q, k, v)
+    if a is None:
+        a = torch.empty((H, N, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    _need(a, "a", torch.float32)
+    _need(lse, "lse", torch.float32)
+    ws = _ws(ws, asm_prefix_states_workspace(H, N, D, L, chunks), q.device)
+    st = library().asm_prefix_states(_ptr(q), H, N, D, _ptr(k), _ptr(v), L, int(chunks),
+                                     float(scale), _ptr(a), _ptr(lse), _ptr(ws), ws.numel(),
+                                     _stream(stream))
+    _check(st, "asm_prefix_states")
+    return a, lse
+
+
+def asm_kmeans(x, centroids, iters: int, assign=None, counts=None, centroids_bf16=None, ws=None,
+               stream=None):
+    """Lloyd K-means of x [H][N][D] bf16 from centroids [H][K][D] f32 (updated in
+    place).  Returns (assign [H][N] i32, counts [H][K] i32, centroids_bf16 or None)."""
+    _need(x, "x", torch.bfloat16)
+    _need(centroids, "centroids", torch.float32)
+    H, N, D = x.shape
+    if centroids.dim() != 3 or centroids.shape[0] != H or centroids.shape[2] != D:
+        raise ValueError("centroids must be [H][K][D] matching x [H][N][D]")
+    K = centroids.shape[1]
+    if assign is None:
+        assign = torch.empty((H, N), dtype=torch.int32, device=x.device)
+    if counts is None:
+        counts = torch.empty((H, K), dtype=torch.int32, device=x.device)
+    _need(assign, "assign", torch.int32)
+    _need(counts, "counts", torch.int32)
+    if centroids_bf16 is not None:
+        _need(centroids_bf16, "centroids_bf16", torch.bfloat16)
+    ws = _ws(ws, asm_kmeans_workspace(H, K, D), x.device)
+    st = library().asm_kmeans(_ptr(x), H, N, D, _ptr(centroids), K, int(iters), _ptr(assign),
+                              _ptr(counts), _ptr(centroids_bf16), _ptr(ws), ws.numel(),
+                              _stream(stream))
+    _check(st, "asm_kmeans")
+    return assign, counts, centroids_bf16
+
+
+def asm_aggregate_states(assign, a, lse, K: int, abar=None, log_zbar=None, stream=None):
+    """Per cluster the merge of its members' states.  Returns (abar [H][K][D] bf16,
+    log_zbar [H][K] f32)."""
+    _need(assign, "assign", torch.int32)
+    _need(a, "a", torch.float32)
+    _need(lse, "lse", torch.float32)
+    H, N, D = a.shape
+    if tuple(assign.shape) != (H, N) or tuple(lse.shape) != (H, N):
+        raise ValueError("assign and lse must be [H][N] matching a [H][N][D]")
+    if abar is None:
+        abar = torch.empty((H, K, D), dtype=torch.bfloat16, device=a.device)
+    if log_zbar is None:
+        log_zbar = torch.empty((H, K), dtype=torch.float32, device=a.device)
+    _need(abar, "abar", torch.bfloat16)
+    _need(log_zbar, "log_zbar", torch.float32)
+    st = library().asm_aggregate_states(_ptr(assign), _ptr(a), _ptr(lse), H, N, D, int(K),
+                                        _ptr(abar), _ptr(log_zbar), _stream(stream))
+    _check(st, "asm_aggregate_states")
+    return abar, log_zbar
+
+
+def asm_build_memory(q, k, v, centroids, iters: int, chunks: int = 1, scale: float = 0.0,
+                     centroids_bf16=None, abar=None, log_zbar=None, assign=None, ws=None,
+                     stream=None):
+    """Offline memory build for one layer: prefix states, K-means, aggregation.
+    centroids [H][K][D] f32 holds the initial centroids and is updated in place.
+    Returns (centroids_bf16, abar, log_zbar, assign, ws); ws holds the states."""
+    H, N, D, L = _prefix_shapes(q, k, v)
+    _need(centroids, "centroids", torch.float32)
+    if centroids.dim() != 3 or centroids.shape[0] != H or centroids.shape[2] != D:
+        raise ValueError("centroids must be [H][K][D] matching q [H][N][D]")
+    K = centroids.shape[1]
+    dev = q.device
+    if centroids_bf16 is None:
+        centroids_bf16 = torch.empty((H, K, D), dtype=torch.bfloat16, device=dev)
+    if abar is None:
+        abar = torch.empty((H, K, D), dtype=torch.bfloat16, device=dev)
+    if log_zbar is None:
+        log_zbar = torch.empty((H, K), dtype=torch.float32, device=dev)
+    if assign is None:
+        assign = torch.empty((H, N), dtype=torch.int32, device=dev)
+    _need(centroids_bf16, "centroids_bf16", torch.bfloat16)
+    _need(abar, "abar", torch.bfloat16)
+    _need(log_zbar, "log_zbar", torch.float32)
+    _need(assign, "assign", torch.int32)
+    ws = _ws(ws, asm_build_memory_workspace(H, N, D, L, chunks, K), dev)
+    st = library().asm_build_memory(_ptr(q), H, N, D, _ptr(k), _ptr(v), L, int(chunks),
+                                    float(scale), _ptr(centroids), K, int(iters),
+                                    _ptr(centroids_bf16), _ptr(abar), _ptr(log_zbar),
+                                    _ptr(assign), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "asm_build_memory")
+    return centroids_bf16, abar, log_zbar, assign, ws

@@ -1,0 +1,871 @@
+// Attention-state memory construction (offline calibration) on the GPU.
+//
+// "Context Memorization for Efficient Long Context Generation": method step 1
+// (each calibration query's attention state over the prefix, a = attn(q, K_p, V_p)
+// with its normaliser Z), the chunked construction of the experiments (the prefix
+// encoded in chunks whose states are merged), and step 2 (K-means over the
+// collected queries; a cluster's query centroid is the mean of its members and
+// its stored state the merge of their states).  Calibration queries, centroids
+// and states are kept per KV head (the page's GQA extension).
+//
+// Kernels
+//   asm_prefix_chunk<D>  per (KV head, 128 queries, prefix chunk): attention on
+//                        v_mfma_f32_16x16x32_bf16 with the keys as rows.  S^T =
+//                        K Q^T leaves every lane four keys of one query, which is
+//                        the B-operand layout of O^T = V^T P^T once the two 16-key
+//                        halves of a 32-key step are interleaved in the contraction
+//                        index (the A operand, V^T, uses the same interleave); V is
+//                        transposed on its way into LDS, K is stored with a padded
+//                        row so the 16 rows an MFMA reads fall in distinct banks.
+//                        The weights P enter the value product as two bf16 parts.
+//   asm_prefix_merge<D>  per (KV head, query): merge of the chunks' states.
+//   km_prep<D>           fp32 centroids -> bf16 hi, bf16 lo = c - hi, |c|^2.
+//   km_assign<D>         per (KV head, 256 points): |c|^2 - 2 x.c for every
+//                        centroid on MFMA (x is exact in bf16; c = hi + lo keeps
+//                        16 significant bits), argmin with the lowest index on ties.
+//   km_reduce<D, MERGE>  per (KV head, 64 clusters): scans the assignment in index
+//                        order and accumulates each cluster's members in a fixed
+//                        order (no float atomics, so results repeat bit for bit);
+//                        MERGE = false writes member means as the new centroids
+//                        (and their hi/lo/|c|^2), MERGE = true the merged states.
+#include <string.h>
+
+#include "common.h"
+
+namespace kvb {
+
+constexpr int kPfxQB = 128;     // queries per workgroup (4 waves x 2 tiles of 16)
+constexpr int kPfxKT = 64;      // keys per LDS tile
+constexpr int kKmPB = 256;      // points per workgroup (4 waves x 4 tiles of 16)
+constexpr int kKmCT = 64;       // centroids per LDS tile
+constexpr int kRedRound = 1024; // labels scanned per round (one per thread)
+constexpr int kMaxPoints = 1 << 24;
+
+struct PrefixArgs {
+  const uint16_t* q;  // [H][N][D]
+  const uint16_t* k;  // [H][L][D]
+  const uint16_t* v;  // [H][L][D]
+  float* out;         // [C][H][N][D]
+  float* out_lse;     // [C][H][N]
+  int32_t H, N, L, csize;
+  float scale_log2;   // scale * log2(e)
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void asm_prefix_chunk(PrefixArgs p) {
+  constexpr int DS = D / 32;          // 32-wide contraction steps of S^T
+  constexpr int DT = D / 16;          // 16-row tiles of O^T
+  constexpr int KP = D + 8;           // padded K row in LDS (bf16)
+  constexpr int VP = kPfxKT + 4;      // padded V^T row in LDS (bf16)
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int LPT = kPfxKT * CPR / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kPfxKT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+
+  const int H = p.H;
+  const int h = blockIdx.x % H, qb = blockIdx.x / H, c = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int c0 = c * p.csize;
+  const int c1 = min(p.L, c0 + p.csize);
+  const int nt = c1 > c0 ? (c1 - c0 + kPfxKT - 1) / kPfxKT : 0;
+  const uint16_t* kh = p.k + (size_t)h * p.L * D;
+  const uint16_t* vh = p.v + (size_t)h * p.L * D;
+
+  // B operand of S^T: query column lc of each of the wave's two tiles
+  u32x4 qr[2][DS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int n = qb * kPfxQB + wave * 32 + qt * 16 + lc;
+    const uint16_t* qp = p.q + ((size_t)h * p.N + n) * D + 8 * lg;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      qr[qt][ds] = n < p.N ? *(const u32x4*)(qp + ds * 32) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x4 o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt][0] = o[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {kNegInf, kNegInf}, ls[2] = {0.f, 0.f};
+
+  u32x4 kr[LPT], vr[LPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int ci = tid + 256 * j, key = ci / CPR, col = ci % CPR;
+      const int gk = c0 + t * kPfxKT + key;
+      const bool ok = gk < c1;
+      kr[j] = ok ? *(const u32x4*)(kh + (size_t)gk * D + col * 8) : u32x4{0, 0, 0, 0};
+      vr[j] = ok ? *(const u32x4*)(vh + (size_t)gk * D + col * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int ci = tid + 256 * j, key = ci / CPR, col = ci % CPR;
+      *(u32x4*)&Ks[buf][key * KP + col * 8] = kr[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        Vt[buf][(col * 8 + e) * VP + key] = (uint16_t)(vr[j][e >> 1] >> (16 * (e & 1)));
+    }
+  };
+
+  if (nt > 0) load_tile(0);
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (t + 1 < nt) load_tile(t + 1);
+
+    // S^T tiles: rows = keys kt*16 + 4lg + i, column = this lane's query
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt][0] = s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const u32x4 a = *(const u32x4*)&Ks[buf][(kt * 16 + lc) * KP + ds * 32 + 8 * lg];
+        s[kt][0] = mfma_16x16x32_bf16(a, qr[0][ds], s[kt][0]);
+        s[kt][1] = mfma_16x16x32_bf16(a, qr[1][ds], s[kt][1]);
+      }
+    }
+    const int valid = c1 - (c0 + t * kPfxKT);  // >= 1
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[kt][qt][i] * p.scale_log2;
+          if (kt * 16 + 4 * lg + i >= valid) x = kNegInf;
+          s[kt][qt][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m[qt], mx);
+      const float alpha = exp2_fast(m[qt] - mn);
+      m[qt] = mn;
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = exp2_fast(s[kt][qt][i] - mn);
+          s[kt][qt][i] = pv;
+          sum += pv;
+        }
+      ls[qt] = ls[qt] * alpha + sum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= alpha;
+    }
+
+    // O^T += V^T P^T over two 32-key steps; contraction slot 8lg + j holds key
+    // 32ks + 4lg + j (j < 4) or 32ks + 16 + 4lg + (j - 4)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // P = P_hi + P_lo in bf16 (a single bf16 rounding of the weights would cost
+      // up to ~2e-3 of the output's scale)
+      u32x4 ph[2], pl[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        uint32_t hb[8], lb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? s[2 * ks][qt][e] : s[2 * ks + 1][qt][e - 4];
+          hb[e] = f32_to_bf16_rne(x);
+          lb[e] = f32_to_bf16_rne(x - bf16_bits_to_f32(hb[e]));
+        }
+        ph[qt] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
+                       hb[6] | (hb[7] << 16)};
+        pl[qt] = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
+                       lb[6] | (lb[7] << 16)};
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vp = &Vt[buf][(dt * 16 + lc) * VP + 32 * ks + 4 * lg];
+        const uint2 lo = *(const uint2*)vp, hi = *(const uint2*)(vp + 16);
+        const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+        o[dt][0] = mfma_16x16x32_bf16(a, ph[0], o[dt][0]);
+        o[dt][1] = mfma_16x16x32_bf16(a, ph[1], o[dt][1]);
+        o[dt][0] = mfma_16x16x32_bf16(a, pl[0], o[dt][0]);
+        o[dt][1] = mfma_16x16x32_bf16(a, pl[1], o[dt][1]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = ls[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int n = qb * kPfxQB + wave * 32 + qt * 16 + lc;
+    if (n >= p.N) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t row = ((size_t)c * H + h) * p.N + n;
+    float* dst = p.out + row * D + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *(f32x4*)(dst + dt * 16) = o[dt][qt] * inv;
+    if (lg == 0) p.out_lse[row] = l > 0.f ? m[qt] * kLn2 + logf(l) : kNegInf;
+  }
+}
+
+// Merge of C chunk states per (KV head, query) in chunk order: sixteen lanes per
+// row, D/16 consecutive elements per lane.
+template <int D>
+__global__ __launch_bounds__(256) void asm_prefix_merge(const float* part, const float* plse,
+                                                       float* a, float* lse, int32_t rows,
+                                                       int32_t C) {
+  constexpr int V = D / 16;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+  const int r = blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + lg;
+  if (r >= rows) return;
+  float M = kNegInf;
+  for (int c = 0; c < C; ++c) M = fmaxf(M, plse[(size_t)c * rows + r]);
+  float acc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) acc[j] = 0.f;
+  float Z = 0.f;
+  if (M != kNegInf) {
+    for (int c = 0; c < C; ++c) {
+      const float w = exp2_fast((plse[(size_t)c * rows + r] - M) * kLog2e);
+      const float* src = part + ((size_t)c * rows + r) * D + lc * V;
+      Z += w;
+#pragma unroll
+      for (int j = 0; j < V; j += 4) {
+        const f32x4 x = *(const f32x4*)(src + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j + e] += w * x[e];
+      }
+    }
+  }
+  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  float* dst = a + (size_t)r * D + lc * V;
+#pragma unroll
+  for (int j = 0; j < V; j += 4)
+    *(f32x4*)(dst + j) = f32x4{acc[j] * inv, acc[j + 1] * inv, acc[j + 2] * inv, acc[j + 3] * inv};
+  if (lc == 0) lse[r] = Z > 0.f ? M + logf(Z) : kNegInf;
+}
+
+struct KmArgs {
+  const uint16_t* x;   // [H][N][D] points (bf16)
+  float* cent;         // [H][K][D] centroids (fp32)
+  uint16_t* hi;        // [H][K][D] bf16 of the centroids, read by km_assign
+  uint16_t* hi_out;    // where km_reduce writes hi (hi, or the caller's bf16 copy)
+  uint16_t* lo;        // [H][K][D] bf16 of (c - hi)
+  float* cnorm;        // [H][K]  |c|^2
+  int32_t* assign;     // [H][N]
+  int32_t* counts;     // [H][K] or null
+  const float* a;      // [H][N][D] states (merge mode)
+  const float* lse;    // [H][N]
+  uint16_t* abar;      // [H][K][D] bf16
+  float* log_zbar;     // [H][K]
+  int32_t H, N, K;
+};
+
+// Writes hi, lo and |c|^2 of one centroid row held by 16 lanes (lane lc holds the
+// D/16 consecutive elements starting at lc * D/16); the caller's 16 lanes must be
+// active together.
+template <int D>
+__device__ __forceinline__ void km_prep_row(const KmArgs& k, size_t row, const float* v, int lc,
+                                            uint16_t* hi_dst) {
+  constexpr int V = D / 16;
+  uint32_t hb[V / 2], lb[V / 2];
+  float sq = 0.f;
+#pragma unroll
+  for (int j = 0; j < V; j += 2) {
+    const uint32_t h0 = f32_to_bf16_rne(v[j]), h1 = f32_to_bf16_rne(v[j + 1]);
+    const uint32_t l0 = f32_to_bf16_rne(v[j] - bf16_bits_to_f32(h0));
+    const uint32_t l1 = f32_to_bf16_rne(v[j + 1] - bf16_bits_to_f32(h1));
+    hb[j / 2] = h0 | (h1 << 16);
+    lb[j / 2] = l0 | (l1 << 16);
+    sq = fmaf(v[j], v[j], sq);
+    sq = fmaf(v[j + 1], v[j + 1], sq);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+  const size_t off = row * D + (size_t)lc * V;
+  if constexpr (V == 8) {
+    *(u32x4*)(hi_dst + off) = u32x4{hb[0], hb[1], hb[2], hb[3]};
+    *(u32x4*)(k.lo + off) = u32x4{lb[0], lb[1], lb[2], lb[3]};
+  } else {
+    *(uint2*)(hi_dst + off) = uint2{hb[0], hb[1]};
+    *(uint2*)(k.lo + off) = uint2{lb[0], lb[1]};
+  }
+  if (lc == 0) k.cnorm[row] = sq;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void km_prep(KmArgs k) {
+  constexpr int V = D / 16;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + lg;
+  if (row >= (size_t)k.H * k.K) return;
+  float v[V];
+  const float* src = k.cent + row * D + lc * V;
+#pragma unroll
+  for (int j = 0; j < V; j += 4) {
+    const f32x4 x = *(const f32x4*)(src + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[j + e] = x[e];
+  }
+  km_prep_row<D>(k, row, v, lc, k.hi);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void km_assign(KmArgs k) {
+  constexpr int DS = D / 32;
+  constexpr int CP = D + 8;  // padded centroid row in LDS (bf16)
+  constexpr int CPR = D / 8;
+  constexpr int LPT = kKmCT * CPR / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t Ch[2][kKmCT * CP];
+  __shared__ __attribute__((aligned(16))) uint16_t Cl[2][kKmCT * CP];
+  __shared__ __attribute__((aligned(16))) float Cn[2][kKmCT];
+
+  const int H = k.H, K = k.K;
+  const int h = blockIdx.x % H, pb = blockIdx.x / H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int nt = (K + kKmCT - 1) / kKmCT;
+  const uint16_t* hh = k.hi + (size_t)h * K * D;
+  const uint16_t* lh = k.lo + (size_t)h * K * D;
+  const float* nh = k.cnorm + (size_t)h * K;
+
+  u32x4 xr[4][DS];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    const int n = pb * kKmPB + wave * 64 + pt * 16 + lc;
+    const uint16_t* xp = k.x + ((size_t)h * k.N + n) * D + 8 * lg;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      xr[pt][ds] = n < k.N ? *(const u32x4*)(xp + ds * 32) : u32x4{0, 0, 0, 0};
+  }
+  float best[4];
+  int bi[4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    best[pt] = __builtin_huge_valf();
+    bi[pt] = 0x7FFFFFFF;
+  }
+
+  u32x4 hr[LPT], lr[LPT];
+  float cr = 0.f;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int ci = tid + 256 * j, row = ci / CPR, col = ci % CPR;
+      const int kk = t * kKmCT + row;
+      const bool ok = kk < K;
+      hr[j] = ok ? *(const u32x4*)(hh + (size_t)kk * D + col * 8) : u32x4{0, 0, 0, 0};
+      lr[j] = ok ? *(const u32x4*)(lh + (size_t)kk * D + col * 8) : u32x4{0, 0, 0, 0};
+    }
+    if (tid < kKmCT) {
+      const int kk = t * kKmCT + tid;
+      cr = kk < K ? nh[kk] : __builtin_huge_valf();
+    }
+  };
+
+  load_tile(0);
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int ci = tid + 256 * j, row = ci / CPR, col = ci % CPR;
+      *(u32x4*)&Ch[buf][row * CP + col * 8] = hr[j];
+      *(u32x4*)&Cl[buf][row * CP + col * 8] = lr[j];
+    }
+    if (tid < kKmCT) Cn[buf][tid] = cr;
+    __syncthreads();
+    if (t + 1 < nt) load_tile(t + 1);
+
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4 s[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) s[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const int off = (ct * 16 + lc) * CP + ds * 32 + 8 * lg;
+        const u32x4 ah = *(const u32x4*)&Ch[buf][off];
+        const u32x4 al = *(const u32x4*)&Cl[buf][off];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) s[pt] = mfma_16x16x32_bf16(ah, xr[pt][ds], s[pt]);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) s[pt] = mfma_16x16x32_bf16(al, xr[pt][ds], s[pt]);
+      }
+      const f32x4 cn = *(const f32x4*)&Cn[buf][ct * 16 + 4 * lg];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = t * kKmCT + ct * 16 + 4 * lg + i;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const float d = fmaf(-2.f, s[pt][i], cn[i]);
+          if (d < best[pt]) {
+            best[pt] = d;
+            bi[pt] = kk;
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float d2 = __shfl_xor(best[pt], o, 64);
+      const int i2 = __shfl_xor(bi[pt], o, 64);
+      if (d2 < best[pt] || (d2 == best[pt] && i2 < bi[pt])) {
+        best[pt] = d2;
+        bi[pt] = i2;
+      }
+    }
+    const int n = pb * kKmPB + wave * 64 + pt * 16 + lc;
+    if (lg == 0 && n < k.N) k.assign[(size_t)h * k.N + n] = bi[pt];
+  }
+}
+
+// One workgroup of 16 waves per (KV head, 64 clusters); wave w owns clusters
+// k0 + w + 16c (c = 0..3).  Rounds of 1024 labels: members of the block's clusters
+// are listed in index order in LDS, then each wave takes its clusters' members in
+// batches of four (lane group lg takes every fourth), so every sum is formed in an
+// order fixed by N and the assignment alone.
+template <int D, bool MERGE>
+__global__ __launch_bounds__(1024) void km_reduce(KmArgs k) {
+  constexpr int V = D / 16;
+  __shared__ uint32_t list[kRedRound];
+  __shared__ int wcnt[16];
+  const int H = k.H;
+  const int h = blockIdx.x % H, k0 = (blockIdx.x / H) * 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int32_t* lab = k.assign + (size_t)h * k.N;
+
+  float acc[4][V];
+  float mm[4], ss[4];
+  int cnt[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[c][j] = 0.f;
+    mm[c] = kNegInf;
+    ss[c] = 0.f;
+    cnt[c] = 0;
+  }
+
+  for (int r0 = 0; r0 < k.N; r0 += kRedRound) {
+    const int i = r0 + tid;
+    const int loc = i < k.N ? lab[i] - k0 : -1;
+    const bool in = (unsigned)loc < 64u;
+    const uint64_t bal = __ballot(in);
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int base = 0, n = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int cw = wcnt[w];
+      base += w < wave ? cw : 0;
+      n += cw;
+    }
+    if (in) list[base + __popcll(bal & ((1ull << lane) - 1ull))] = ((uint32_t)i << 6) | loc;
+    __syncthreads();
+
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const bool ok = j0 + lane < n;
+      const uint32_t e = ok ? list[j0 + lane] : 0u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint64_t mk = __ballot(ok && (e & 63u) == (uint32_t)(wave + 16 * c));
+        cnt[c] += __popcll(mk);
+        while (mk) {
+          int src[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            src[b] = -1;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int pos = mk ? __builtin_ctzll(mk) : -1;
+              if (g == lg) src[b] = pos;
+              mk &= mk - 1ull;
+            }
+          }
+          float val[4][V];
+          float vl[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t em = __shfl(e, src[b] < 0 ? 0 : src[b], 64);
+            const size_t pi = (size_t)h * k.N + (em >> 6);
+            vl[b] = kNegInf;
+#pragma unroll
+            for (int j = 0; j < V; ++j) val[b][j] = 0.f;
+            if (src[b] < 0) continue;
+            if constexpr (MERGE) {
+              const float* sp = k.a + pi * D + lc * V;
+#pragma unroll
+              for (int j = 0; j < V; j += 4) {
+                const f32x4 x = *(const f32x4*)(sp + j);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) val[b][j + q] = x[q];
+              }
+              vl[b] = k.lse[pi];
+            } else {
+              const uint16_t* xp = k.x + pi * D + lc * V;
+              uint32_t w[V / 2];
+              if constexpr (V == 8) {
+                const u32x4 x = *(const u32x4*)xp;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = x[q];
+              } else {
+                const uint2 x = *(const uint2*)xp;
+                w[0] = x.x;
+                w[1] = x.y;
+              }
+#pragma unroll
+              for (int q = 0; q < V / 2; ++q) {
+                val[b][2 * q] = bf16_bits_to_f32(w[q] & 0xFFFFu);
+                val[b][2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+              }
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            if (src[b] < 0) continue;
+            if constexpr (MERGE) {
+              if (vl[b] == kNegInf) continue;
+              const float mn = fmaxf(mm[c], vl[b]);
+              const float sc = exp2_fast((mm[c] - mn) * kLog2e);
+              const float wi = exp2_fast((vl[b] - mn) * kLog2e);
+#pragma unroll
+              for (int j = 0; j < V; ++j) acc[c][j] = acc[c][j] * sc + wi * val[b][j];
+              ss[c] = ss[c] * sc + wi;
+              mm[c] = mn;
+            } else {
+#pragma unroll
+              for (int j = 0; j < V; ++j) acc[c][j] += val[b][j];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // combine the four lane groups (xor 16, then xor 32)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      if constexpr (MERGE) {
+        const float m2 = __shfl_xor(mm[c], o, 64), s2 = __shfl_xor(ss[c], o, 64);
+        const float mn = fmaxf(mm[c], m2);
+        const float e1 = mn == kNegInf ? 0.f : exp2_fast((mm[c] - mn) * kLog2e);
+        const float e2 = mn == kNegInf ? 0.f : exp2_fast((m2 - mn) * kLog2e);
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const float a2 = __shfl_xor(acc[c][j], o, 64);
+          acc[c][j] = __fmul_rn(acc[c][j], e1) + __fmul_rn(a2, e2);
+        }
+        ss[c] = __fmul_rn(ss[c], e1) + __fmul_rn(s2, e2);
+        mm[c] = mn;
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[c][j] += __shfl_xor(acc[c][j], o, 64);
+      }
+    }
+  }
+
+  // lane group c writes cluster c of this wave
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int kk = k0 + wave + 16 * c;
+    if (lg != c || kk >= k.K) continue;
+    const size_t row = (size_t)h * k.K + kk;
+    if constexpr (MERGE) {
+      const bool any = ss[c] > 0.f;
+      const float inv = any ? 1.f / ss[c] : 0.f;
+      uint32_t w[V / 2];
+#pragma unroll
+      for (int q = 0; q < V / 2; ++q)
+        w[q] = f32_to_bf16_rne(acc[c][2 * q] * inv) | (f32_to_bf16_rne(acc[c][2 * q + 1] * inv) << 16);
+      uint16_t* dst = k.abar + row * D + lc * V;
+      if constexpr (V == 8)
+        *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+      else
+        *(uint2*)dst = uint2{w[0], w[1]};
+      if (lc == 0) k.log_zbar[row] = any ? mm[c] + logf(ss[c]) : kNegInf;
+    } else {
+      float v[V];
+      float* cp = k.cent + row * D + lc * V;
+      if (cnt[c] > 0) {
+        const float fc = (float)cnt[c];
+#pragma unroll
+        for (int j = 0; j < V; ++j) v[j] = acc[c][j] / fc;
+#pragma unroll
+        for (int j = 0; j < V; j += 4) *(f32x4*)(cp + j) = f32x4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; j += 4) {
+          const f32x4 x = *(const f32x4*)(cp + j);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[j + q] = x[q];
+        }
+      }
+      km_prep_row<D>(k, row, v, lc, k.hi_out);
+      if (lc == 0 && k.counts) k.counts[row] = cnt[c];
+    }
+  }
+}
+
+static int prefix_chunks(int L, int chunks, int& csize) {
+  if (L <= 0) {
+    csize = 1;
+    return 1;
+  }
+  csize = (L + chunks - 1) / chunks;
+  return (L + csize - 1) / csize;
+}
+
+static bool build_dims_ok(int H, int N, int D) {
+  if (H < 1 || N < 1 || N >= kMaxPoints) return false;
+  if ((long long)H * N >= (1ll << 30)) return false;
+  (void)D;
+  return true;
+}
+
+static int32_t launch_prefix(const void* q, int32_t H, int32_t N, int32_t D, const void* k,
+                             const void* v, int32_t L, int32_t chunks, float scale, float* a,
+                             float* lse, void* ws, hipStream_t s) {
+  int csize;
+  const int C = prefix_chunks(L, chunks, csize);
+  PrefixArgs p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.H = H;
+  p.N = N;
+  p.L = L;
+  p.csize = csize;
+  p.scale_log2 = scale * kLog2e;
+  const size_t rows = (size_t)H * N;
+  if (C == 1) {
+    p.out = a;
+    p.out_lse = lse;
+  } else {
+    p.out = (float*)((char*)ws + kWsHeader);
+    p.out_lse = (float*)((char*)ws + kWsHeader + align_up((size_t)C * rows * D * 4, 256));
+  }
+  const dim3 grid(H * ((N + kPfxQB - 1) / kPfxQB), C);
+  {
+    TraceScope tr(kTrAsmPrefix, s);
+    if (D == 128)
+      hipLaunchKernelGGL(asm_prefix_chunk<128>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(asm_prefix_chunk<64>, grid, dim3(256), 0, s, p);
+  }
+  if (C > 1) {
+    TraceScope tr(kTrAsmPrefixMerge, s);
+    const dim3 g2((unsigned)((rows + 15) / 16));
+    if (D == 128)
+      hipLaunchKernelGGL(asm_prefix_merge<128>, g2, dim3(256), 0, s, p.out, p.out_lse, a, lse,
+                         (int32_t)rows, C);
+    else
+      hipLaunchKernelGGL(asm_prefix_merge<64>, g2, dim3(256), 0, s, p.out, p.out_lse, a, lse,
+                         (int32_t)rows, C);
+  }
+  return launch_status();
+}
+
+static size_t km_layout(int H, int K, int D, size_t& o_hi, size_t& o_lo, size_t& o_n) {
+  const size_t cells = (size_t)H * K * D;
+  o_hi = kWsHeader;
+  o_lo = o_hi + align_up(cells * 2, 256);
+  o_n = o_lo + align_up(cells * 2, 256);
+  return o_n + align_up((size_t)H * K * 4, 256);
+}
+
+static void km_launch_assign(const KmArgs& k, int D, hipStream_t s) {
+  TraceScope tr(kTrKmAssign, s);
+  const dim3 g(k.H * ((k.N + kKmPB - 1) / kKmPB));
+  if (D == 128)
+    hipLaunchKernelGGL(km_assign<128>, g, dim3(256), 0, s, k);
+  else
+    hipLaunchKernelGGL(km_assign<64>, g, dim3(256), 0, s, k);
+}
+
+static void km_launch_reduce(const KmArgs& k, int D, bool merge, hipStream_t s) {
+  TraceScope tr(merge ? kTrAsmAggregate : kTrKmUpdate, s);
+  const dim3 g(k.H * ((k.K + 63) / 64));
+  if (merge) {
+    if (D == 128)
+      hipLaunchKernelGGL((km_reduce<128, true>), g, dim3(1024), 0, s, k);
+    else
+      hipLaunchKernelGGL((km_reduce<64, true>), g, dim3(1024), 0, s, k);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((km_reduce<128, false>), g, dim3(1024), 0, s, k);
+    else
+      hipLaunchKernelGGL((km_reduce<64, false>), g, dim3(1024), 0, s, k);
+  }
+}
+
+static int32_t launch_kmeans(const void* x, int32_t H, int32_t N, int32_t D, float* cent,
+                             int32_t K, int32_t iters, int32_t* assign, int32_t* counts,
+                             void* cent_bf16, void* ws, hipStream_t s) {
+  size_t o_hi, o_lo, o_n;
+  km_layout(H, K, D, o_hi, o_lo, o_n);
+  KmArgs k;
+  memset(&k, 0, sizeof(k));
+  k.x = (const uint16_t*)x;
+  k.cent = cent;
+  k.hi = (uint16_t*)((char*)ws + o_hi);
+  k.lo = (uint16_t*)((char*)ws + o_lo);
+  k.cnorm = (float*)((char*)ws + o_n);
+  k.assign = assign;
+  k.counts = counts;
+  k.H = H;
+  k.N = N;
+  k.K = K;
+  k.hi_out = k.hi;
+  {
+    TraceScope tr(kTrKmUpdate, s);
+    const dim3 g((unsigned)(((size_t)H * K + 15) / 16));
+    if (D == 128)
+      hipLaunchKernelGGL(km_prep<128>, g, dim3(256), 0, s, k);
+    else
+      hipLaunchKernelGGL(km_prep<64>, g, dim3(256), 0, s, k);
+  }
+  for (int it = 0; it < iters; ++it) {
+    km_launch_assign(k, D, s);
+    k.hi_out = (it == iters - 1 && cent_bf16) ? (uint16_t*)cent_bf16 : k.hi;
+    km_launch_reduce(k, D, false, s);
+  }
+  return launch_status();
+}
+
+static int32_t launch_aggregate(const int32_t* assign, const float* a, const float* lse,
+                                int32_t H, int32_t N, int32_t D, int32_t K, void* abar,
+                                float* log_zbar, hipStream_t s) {
+  KmArgs k;
+  memset(&k, 0, sizeof(k));
+  k.assign = (int32_t*)assign;
+  k.a = a;
+  k.lse = lse;
+  k.abar = (uint16_t*)abar;
+  k.log_zbar = log_zbar;
+  k.H = H;
+  k.N = N;
+  k.K = K;
+  km_launch_reduce(k, D, true, s);
+  return launch_status();
+}
+
+}  // namespace kvb
+
+using namespace kvb;
+
+extern "C" size_t asm_prefix_states_workspace(int32_t H, int32_t N, int32_t D, int32_t L,
+                                              int32_t chunks) {
+  if (!build_dims_ok(H, N, D) || L < 0 || chunks < 1 || (D != 64 && D != 128)) return 0;
+  int csize;
+  const int C = prefix_chunks(L, chunks, csize);
+  if (C == 1) return kWsHeader;
+  const size_t rows = (size_t)H * N;
+  return kWsHeader + align_up((size_t)C * rows * D * 4, 256) + align_up((size_t)C * rows * 4, 256);
+}
+
+extern "C" int32_t asm_prefix_states(const void* q, int32_t H, int32_t N, int32_t D,
+                                     const void* k, const void* v, int32_t L, int32_t chunks,
+                                     float scale, float* a, float* lse, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (!q || !a || !lse || (L > 0 && (!k || !v))) return KVB_EINVAL;
+  if (!build_dims_ok(H, N, D) || L < 0 || L >= (1 << 30) || chunks < 1 || chunks > 65535)
+    return KVB_EINVAL;
+  if (D != 64 && D != 128) return KVB_EUNSUPPORTED;
+  if ((long long)H * ((N + kPfxQB - 1) / kPfxQB) >= (1ll << 31)) return KVB_EINVAL;
+  const size_t need = asm_prefix_states_workspace(H, N, D, L, chunks);
+  if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
+  int32_t st = check_device();
+  if (st) return st;
+  if (!(scale > 0.f)) scale = 1.f / sqrtf((float)D);
+  return launch_prefix(q, H, N, D, k, v, L, chunks, scale, a, lse, ws, (hipStream_t)stream);
+}
+
+extern "C" size_t asm_kmeans_workspace(int32_t H, int32_t K, int32_t D) {
+  if (H < 1 || K < 1 || K >= kMaxPoints || (D != 64 && D != 128)) return 0;
+  size_t a, b, c;
+  return km_layout(H, K, D, a, b, c);
+}
+
+extern "C" int32_t asm_kmeans(const void* x, int32_t H, int32_t N, int32_t D, float* centroids,
+                              int32_t K, int32_t iters, int32_t* assign, int32_t* counts,
+                              void* centroids_bf16, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !centroids || !assign) return KVB_EINVAL;
+  if (!build_dims_ok(H, N, D) || K < 1 || K >= kMaxPoints || iters < 1 || iters > 100000)
+    return KVB_EINVAL;
+  if ((long long)H * K >= (1ll << 30)) return KVB_EINVAL;
+  if (D != 64 && D != 128) return KVB_EUNSUPPORTED;
+  const size_t need = asm_kmeans_workspace(H, K, D);
+  if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
+  int32_t st = check_device();
+  if (st) return st;
+  return launch_kmeans(x, H, N, D, centroids, K, iters, assign, counts, centroids_bf16, ws,
+                       (hipStream_t)stream);
+}
+
+extern "C" int32_t asm_aggregate_states(const int32_t* assign, const float* a, const float* lse,
+                                        int32_t H, int32_t N, int32_t D, int32_t K, void* abar,
+                                        float* log_zbar, void* stream) {
+  if (!assign || !a || !lse || !abar || !log_zbar) return KVB_EINVAL;
+  if (!build_dims_ok(H, N, D) || K < 1 || K >= kMaxPoints) return KVB_EINVAL;
+  if ((long long)H * K >= (1ll << 30)) return KVB_EINVAL;
+  if (D != 64 && D != 128) return KVB_EUNSUPPORTED;
+  int32_t st = check_device();
+  if (st) return st;
+  return launch_aggregate(assign, a, lse, H, N, D, K, abar, log_zbar, (hipStream_t)stream);
+}
+
+static size_t build_layout(int32_t H, int32_t N, int32_t D, int32_t L, int32_t chunks, int32_t K,
+                           size_t& o_a, size_t& o_l, size_t& o_p, size_t& o_k) {
+  const size_t rows = (size_t)H * N;
+  o_a = kWsHeader;
+  o_l = o_a + align_up(rows * D * 4, 256);
+  o_p = o_l + align_up(rows * 4, 256);
+  o_k = o_p + align_up(asm_prefix_states_workspace(H, N, D, L, chunks), 256);
+  return o_k + asm_kmeans_workspace(H, K, D);
+}
+
+extern "C" size_t asm_build_memory_workspace(int32_t H, int32_t N, int32_t D, int32_t L,
+                                             int32_t chunks, int32_t K) {
+  if (!asm_prefix_states_workspace(H, N, D, L, chunks) || !asm_kmeans_workspace(H, K, D))
+    return 0;
+  size_t a, b, c, d;
+  return build_layout(H, N, D, L, chunks, K, a, b, c, d);
+}
+
+extern "C" int32_t asm_build_memory(const void* q, int32_t H, int32_t N, int32_t D,
+                                    const void* k, const void* v, int32_t L, int32_t chunks,
+                                    float scale, float* centroids, int32_t K, int32_t iters,
+                                    void* centroids_bf16, void* abar, float* log_zbar,
+                                    int32_t* assign, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !centroids || !centroids_bf16 || !abar || !log_zbar || !assign) return KVB_EINVAL;
+  if (L > 0 && (!k || !v)) return KVB_EINVAL;
+  if (!build_dims_ok(H, N, D) || L < 0 || L >= (1 << 30) || chunks < 1 || chunks > 65535)
+    return KVB_EINVAL;
+  if (K < 1 || K >= kMaxPoints || (long long)H * K >= (1ll << 30) || iters < 1 || iters > 100000)
+    return KVB_EINVAL;
+  if (D != 64 && D != 128) return KVB_EUNSUPPORTED;
+  const size_t need = asm_build_memory_workspace(H, N, D, L, chunks, K);
+  if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
+  int32_t st = check_device();
+  if (st) return st;
+  if (!(scale > 0.f)) scale = 1.f / sqrtf((float)D);
+  size_t o_a, o_l, o_p, o_k;
+  build_layout(H, N, D, L, chunks, K, o_a, o_l, o_p, o_k);
+  char* w = (char*)ws;
+  float* a = (float*)(w + o_a);
+  float* lse = (float*)(w + o_l);
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_prefix(q, H, N, D, k, v, L, chunks, scale, a, lse, w + o_p, s);
+  if (st) return st;
+  st = launch_kmeans(q, H, N, D, centroids, K, iters, assign, nullptr, centroids_bf16, w + o_k, s);
+  if (st) return st;
+  return launch_aggregate(assign, a, lse, H, N, D, K, abar, log_zbar, s);
+}

@@ -86,6 +86,10 @@ size_t kv_erase_workspace(const kvb_cache* cache);
 size_t asm_lookup_merge_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t K);
 size_t asm_lookup_merge_hier_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t K1,
                                        int32_t m);
+size_t asm_prefix_states_workspace(int32_t H, int32_t N, int32_t D, int32_t L, int32_t chunks);
+size_t asm_kmeans_workspace(int32_t H, int32_t K, int32_t D);
+size_t asm_build_memory_workspace(int32_t H, int32_t N, int32_t D, int32_t L, int32_t chunks,
+                                  int32_t K);
 
 /*
  * Decode-step grouped-query attention with the retention bias, split over the KV
@@ -271,13 +275,98 @@ int32_t asm_lookup_merge_hier(const void* q, int32_t B, int32_t Hq, int32_t Hkv,
                               void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Attention states of calibration queries over a prefix ([ASM] method step 1, and
+ * the chunked construction of the experiments: the prefix encoded in chunks whose
+ * states are merged).  Per KV head h and query n:
+ *   a[h][n]   = sum_i e^{s_i} v_i / sum_i e^{s_i},  s_i = scale * (q[h][n] . k[h][i]),
+ *   lse[h][n] = log sum_i e^{s_i}  (the page's Z in log form).
+ * The L prefix tokens are cut into ceil(L / csize) consecutive chunks of csize =
+ * ceil(L / chunks) tokens (the last may be shorter); each chunk's state is
+ * computed on its own and the states are merged in chunk order with the merge
+ * operator.  L == 0 gives a = 0, lse = -inf.  Scores use bf16 MFMA products with
+ * float32 accumulation; the softmax weights enter the value product rounded to bf16.
+ *   q        [H][N][D] bf16 (the KV head's calibration queries; for GQA the group's
+ *            query heads stacked along N)
+ *   k, v     [H][L][D] bf16 (may be NULL when L == 0)
+ *   chunks   1..65535; scale: <= 0 selects 1/sqrt(D); D is 64 or 128; N < 2^24
+ *   a        [H][N][D] float32;  lse [H][N] float32
+ *   ws       asm_prefix_states_workspace(H, N, D, L, chunks) bytes (the chunk states
+ *            when there is more than one chunk).
+ */
+int32_t asm_prefix_states(const void* q, int32_t H, int32_t N, int32_t D, const void* k,
+                          const void* v, int32_t L, int32_t chunks, float scale, float* a,
+                          float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * K-means over each KV head's calibration queries ([ASM] method step 2: the
+ * collected queries are clustered and a cluster's query centroid is the mean of
+ * its members).  Lloyd iterations from the caller's initial centroids: every
+ * iteration assigns each point to the centroid at the smallest Euclidean
+ * distance (equal distances to the lowest index), then moves every centroid to
+ * the mean of its members; a centroid without members stays where it is.
+ * Distances are ranked by |c|^2 - 2 x.c in float32, x.c formed from the bf16 point
+ * and the centroid split into two bf16 parts (16 significant bits); member sums
+ * are float32 in an order fixed by N and the assignment, so results repeat bit
+ * for bit.
+ *   x          [H][N][D] bf16 points
+ *   centroids  [H][K][D] float32: initial centroids in, final centroids out
+ *   iters      1..100000 iterations; K < 2^24
+ *   assign     [H][N] int32 out: the last iteration's assignment
+ *   counts     [H][K] int32 out (may be NULL): member counts of that assignment
+ *   centroids_bf16 [H][K][D] bf16 out (may be NULL): final centroids rounded to
+ *              nearest-even bf16 (the codebook format asm_lookup_merge reads)
+ *   ws         asm_kmeans_workspace(H, K, D) bytes
+ */
+int32_t asm_kmeans(const void* x, int32_t H, int32_t N, int32_t D, float* centroids, int32_t K,
+                   int32_t iters, int32_t* assign, int32_t* counts, void* centroids_bf16,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Attention-aware aggregation ([ASM] method step 2 and technical novelty: a
+ * cluster's stored state is the merge of its members' states, not their average).
+ * For cluster k of KV head h, over the points n with assign[h][n] == k:
+ *   log_zbar[h][k] = log sum_n e^{lse[h][n]},
+ *   abar[h][k]     = sum_n e^{lse[h][n]} a[h][n] / sum_n e^{lse[h][n]}  (bf16, RNE);
+ * a cluster with no member (or only members with lse = -inf) gets abar = 0,
+ * log_zbar = -inf.  Labels outside 0..K-1 belong to no cluster.  Members are
+ * merged in an order fixed by N and the assignment (float32, bit-repeatable).
+ *   assign [H][N] int32; a [H][N][D] float32; lse [H][N] float32
+ *   abar   [H][K][D] bf16 out;  log_zbar [H][K] float32 out
+ */
+int32_t asm_aggregate_states(const int32_t* assign, const float* a, const float* lse, int32_t H,
+                             int32_t N, int32_t D, int32_t K, void* abar, float* log_zbar,
+                             void* stream);
+
+/*
+ * The whole offline build of an attention-state memory for one layer ([ASM]
+ * method steps 1-2): asm_prefix_states of the calibration queries q over the
+ * prefix (k, v) in `chunks` chunks, asm_kmeans of the same queries for `iters`
+ * iterations from the initial `centroids`, then asm_aggregate_states of the
+ * states by the final assignment.  The outputs are the codebook the lookup reads:
+ * centroids_bf16 [H][K][D] bf16, abar [H][K][D] bf16, log_zbar [H][K] float32,
+ * plus the float32 centroids (in place) and the assignment [H][N] int32.
+ *   ws  asm_build_memory_workspace(H, N, D, L, chunks, K) bytes; after the call
+ *       it holds the per-query states: a [H][N][D] float32 at byte offset 256,
+ *       lse [H][N] float32 at the next 256-byte boundary.
+ * Other arguments as for the three calls above.
+ */
+int32_t asm_build_memory(const void* q, int32_t H, int32_t N, int32_t D, const void* k,
+                         const void* v, int32_t L, int32_t chunks, float scale, float* centroids,
+                         int32_t K, int32_t iters, void* centroids_bf16, void* abar,
+                         float* log_zbar, int32_t* assign, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
  * Kernel timing (a measurement aid; off by default; not thread-safe).
  * kvb_trace_enable(capacity, mask) creates `capacity` HIP event pairs; from then
  * on every launch of a kernel selected by `mask` records one pair on the launch
  * stream around that launch, until the pairs run out.  mask bits: 1 attention
  * split kernel, 2 split merge, 4 append, 8 eviction select, 16 keep count,
  * 32 keep emit, 64 compaction move, 128 ASM lookup, 256 ASM finalize, 512 the
- * attention split kernel that also moves kept rows (kv_attn_decode_compact).
+ * attention split kernel that also moves kept rows (kv_attn_decode_compact),
+ * 1024 prefix-state chunk kernel, 2048 prefix chunk merge, 4096 K-means
+ * assignment, 8192 K-means centroid update (and the initial centroid split),
+ * 16384 state aggregation.
  * kvb_trace_read waits for the recorded pairs and writes, for the first `max`,
  * the kernel bit and the elapsed milliseconds (-1 if unavailable); it returns
  * how many it wrote (host arrays).  kvb_trace_reset reuses the pairs from the

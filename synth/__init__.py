@@ -275,6 +275,15 @@ def host_asm_build(w: Workload, N: int, L: int | None = None, topics: int = 512,
     return bf16_bits(q), Kp, Vp
 
 
+def host_kmeans_init(w: Workload, q: np.ndarray, K: int, seed_offset: int = 43) -> np.ndarray:
+    """Initial centroids [H][K][D] float32: K distinct calibration queries of each
+    KV head, picked by a seeded permutation (K <= N)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    H, N, _ = q.shape
+    vals = bf16_to_f64(q)
+    return np.stack([vals[h][rng.permutation(N)[:K]] for h in range(H)]).astype(np.float32)
+
+
 def memento_layout(total: int = 1 << 20, seed: int = 1005, memento: int = 200,
                    lo: int = 2048, hi: int = 16384):
     """Block/memento layout of a reasoning trace filling ``total`` slots.

@@ -140,3 +140,61 @@ def test_hier_lookup_arguments_rejected_before_launch():
     assert L.asm_lookup_merge_hier_workspace(2, 8, 2, 64, 16) > 256
     assert L.asm_lookup_merge_hier_workspace(2, 8, 2, 64, 65) == 0
     assert L.asm_lookup_merge_hier_workspace(2, 8, 2, 600, 16) == 0
+
+
+@needs_lib
+def test_build_entry_points_reject_arguments_before_launch():
+    """Fake pointers: the memory-build calls validate on the host first."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    ws = P(4096)
+    # asm_prefix_states: q, H, N, D, k, v, L, chunks, scale, a, lse, ws, ws_bytes, stream
+    pre = [P(8), 2, 100, 128, P(8), P(8), 300, 4, 0.0, P(8), P(8), ws, 1 << 30, None]
+
+    def call(fn, base, **kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return fn(*a)
+
+    f = L.asm_prefix_states
+    assert call(f, pre, a3=96) == -2          # D
+    assert call(f, pre, a1=0) == -1           # H
+    assert call(f, pre, a2=1 << 24) == -1     # N
+    assert call(f, pre, a7=0) == -1           # chunks
+    assert call(f, pre, a6=-1) == -1          # L
+    assert call(f, pre, a4=None) == -1        # k with L > 0
+    assert call(f, pre, a9=None) == -1        # a
+    assert call(f, pre, a12=64) == -4         # workspace too small for 4 chunk states
+    assert L.asm_prefix_states_workspace(2, 100, 128, 300, 1) == 256
+    assert L.asm_prefix_states_workspace(2, 100, 128, 0, 4) == 256
+    # 300 tokens in 4 chunks of 75: 4 states per query
+    assert L.asm_prefix_states_workspace(2, 100, 128, 300, 4) >= 256 + 4 * 200 * 129 * 4
+    # asm_kmeans: x, H, N, D, centroids, K, iters, assign, counts, cent_bf16, ws, ws_bytes, stream
+    km = [P(8), 2, 100, 128, P(8), 16, 3, P(8), None, None, ws, 1 << 30, None]
+    f = L.asm_kmeans
+    assert call(f, km, a3=64 + 8) == -2       # D
+    assert call(f, km, a5=0) == -1            # K
+    assert call(f, km, a6=0) == -1            # iters
+    assert call(f, km, a7=None) == -1         # assign
+    assert call(f, km, a4=None) == -1         # centroids
+    assert call(f, km, a11=100) == -4         # workspace
+    assert L.asm_kmeans_workspace(2, 16, 128) >= 256 + 2 * 2 * 16 * 128 * 2
+    # asm_aggregate_states: assign, a, lse, H, N, D, K, abar, log_zbar, stream
+    ag = [P(8), P(8), P(8), 2, 100, 128, 16, P(8), P(8), None]
+    f = L.asm_aggregate_states
+    assert call(f, ag, a5=32) == -2
+    assert call(f, ag, a6=0) == -1
+    assert call(f, ag, a0=None) == -1
+    assert call(f, ag, a8=None) == -1
+    # asm_build_memory: q, H, N, D, k, v, L, chunks, scale, centroids, K, iters,
+    # centroids_bf16, abar, log_zbar, assign, ws, ws_bytes, stream
+    bm = [P(8), 2, 100, 128, P(8), P(8), 300, 4, 0.0, P(8), 16, 3, P(8), P(8), P(8), P(8), ws,
+          1 << 30, None]
+    f = L.asm_build_memory
+    assert call(f, bm, a3=96) == -2
+    assert call(f, bm, a11=0) == -1
+    assert call(f, bm, a12=None) == -1
+    assert call(f, bm, a17=1024) == -4
+    assert (L.asm_build_memory_workspace(2, 100, 128, 300, 4, 16) >=
+            L.asm_prefix_states_workspace(2, 100, 128, 300, 4) + L.asm_kmeans_workspace(2, 16, 128))
