@@ -308,7 +308,8 @@ def build_bench(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    names = ("asm_prefix", "asm_prefix_merge", "km_assign", "km_update", "asm_aggregate")
+    names = ("asm_vt", "asm_prefix", "asm_prefix_merge", "km_assign", "km_update",
+             "asm_aggregate")
     kvb.trace_enable(64, names)
     step()
     split = {}

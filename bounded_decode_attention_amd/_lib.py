@@ -340,7 +340,7 @@ TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "keep_count": 16, "keep_emit": 32, "compact_move": 64, "asm_lookup": 128,
               "asm_finalize": 256, "attn_fused": 512, "asm_prefix": 1024,
               "asm_prefix_merge": 2048, "km_assign": 4096, "km_update": 8192,
-              "asm_aggregate": 16384}
+              "asm_aggregate": 16384, "asm_vt": 32768}
 
 
 def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:

@@ -34,33 +34,93 @@
 
 namespace kvb {
 
-constexpr int kPfxQB = 128;     // queries per workgroup (4 waves x 2 tiles of 16)
+constexpr int kPfxQB = 256;     // queries per workgroup (8 waves x 2 tiles of 16)
 constexpr int kPfxKT = 64;      // keys per LDS tile
 constexpr int kKmPB = 256;      // points per workgroup (4 waves x 4 tiles of 16)
 constexpr int kKmCT = 64;       // centroids per LDS tile
-constexpr int kRedRound = 1024; // labels scanned per round (one per thread)
 constexpr int kMaxPoints = 1 << 24;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 struct PrefixArgs {
-  const uint16_t* q;  // [H][N][D]
-  const uint16_t* k;  // [H][L][D]
-  const uint16_t* v;  // [H][L][D]
-  float* out;         // [C][H][N][D]
-  float* out_lse;     // [C][H][N]
-  int32_t H, N, L, csize;
-  float scale_log2;   // scale * log2(e)
+  const uint16_t* q;   // [H][N][D]
+  const uint16_t* k;   // [H][L][D]
+  const uint16_t* v;   // [H][L][D]
+  uint16_t* vt;        // [H][C][D][Lc]: V^T per chunk, keys interleaved (vt_prepare)
+  float* out;          // [C][H][N][D]
+  float* out_lse;      // [C][H][N]
+  int32_t H, N, L, C, csize, Lc;
+  float scale_log2;    // scale * log2(e)
 };
 
+// Position of chunk-local key kk in a V^T row: inside each 32-key block, keys
+// 4g..4g+3 and 16+4g..16+4g+3 fill positions 8g..8g+7, the contraction slots lane
+// group g supplies to O^T = V^T P^T (P^T arrives in the S^T accumulator layout).
+__device__ __forceinline__ int vt_position(int kk) {
+  const int w = kk & 31, g = (w & 15) >> 2, j = (w & 3) + (w >> 4) * 4;
+  return (kk & ~31) + 8 * g + j;
+}
+
+// V [H][L][D] -> V^T [H][C][D][Lc] (chunk-local keys at vt_position, zero past the
+// chunk's end).  One workgroup per (KV head, chunk, 64-key tile).
 template <int D>
-__global__ __launch_bounds__(256) void asm_prefix_chunk(PrefixArgs p) {
+__global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
+  constexpr int RP = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t vs[64 * RP];
+  const int tiles = p.Lc / 64;
+  const int tt = blockIdx.x % tiles, hc = blockIdx.x / tiles;
+  const int c = hc % p.C, h = hc / p.C;
+  const int c0 = c * p.csize, c1 = min(p.L, c0 + p.csize);
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int j = 0; j < 64 * CPR / 256; ++j) {
+    const int ci = tid + 256 * j, r = ci / CPR, col = ci % CPR;
+    const int gk = c0 + tt * 64 + r;
+    const u32x4 x = gk < c1 ? *(const u32x4*)(p.v + ((size_t)h * p.L + gk) * D + col * 8)
+                            : u32x4{0, 0, 0, 0};
+    *(u32x4*)&vs[r * RP + col * 8] = x;
+  }
+  __syncthreads();
+  uint16_t* dst = p.vt + ((size_t)h * p.C + c) * D * p.Lc + tt * 64;
+#pragma unroll
+  for (int j = 0; j < D * 8 / 256; ++j) {
+    const int ci = tid + 256 * j, d = ci / 8, q = ci % 8;  // positions 8q..8q+7 of row d
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      // inverse of vt_position inside a 32-key block: position 8g + j -> key
+      const int p0 = 8 * q + e, p1 = p0 + 1;
+      const int k0 = (p0 & ~31) + 4 * ((p0 & 31) >> 3) + (p0 & 3) + ((p0 & 4) ? 16 : 0);
+      const int k1 = (p1 & ~31) + 4 * ((p1 & 31) >> 3) + (p1 & 3) + ((p1 & 4) ? 16 : 0);
+      w[e / 2] = (uint32_t)vs[k0 * RP + d] | ((uint32_t)vs[k1 * RP + d] << 16);
+    }
+    *(u32x4*)(dst + (size_t)d * p.Lc + 8 * q) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// LDS 16-byte slot holding chunk c of K row r (XOR swizzle: the 16 rows one MFMA
+// operand read touches land in distinct banks).
+template <int D>
+__device__ __forceinline__ int k_slot(int r, int c) {
+  if constexpr (D == 128)
+    return c ^ (r & 15);
+  else
+    return c ^ ((r >> 1) & 7);
+}
+__device__ __forceinline__ int vt_slot(int d, int c) { return c ^ ((d >> 1) & 7); }
+
+template <int D>
+__global__ __launch_bounds__(512) void asm_prefix_chunk(PrefixArgs p) {
   constexpr int DS = D / 32;          // 32-wide contraction steps of S^T
   constexpr int DT = D / 16;          // 16-row tiles of O^T
-  constexpr int KP = D + 8;           // padded K row in LDS (bf16)
-  constexpr int VP = kPfxKT + 4;      // padded V^T row in LDS (bf16)
-  constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int LPT = kPfxKT * CPR / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kPfxKT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  constexpr int KRB = D * 2;          // K row bytes
+  constexpr int KCPR = D / 8;         // 16-byte chunks per K row
+  constexpr int KB = kPfxKT * KRB;    // K tile bytes
+  constexpr int VB = D * kPfxKT * 2;  // V^T tile bytes (D rows of 64 keys)
+  constexpr int KI = KB / 1024, VI = VB / 1024;  // 1 KB DMA instructions per tile
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * (KB + VB)];
 
   const int H = p.H;
   const int h = blockIdx.x % H, qb = blockIdx.x / H, c = blockIdx.y;
@@ -69,7 +129,7 @@ __global__ __launch_bounds__(256) void asm_prefix_chunk(PrefixArgs p) {
   const int c1 = min(p.L, c0 + p.csize);
   const int nt = c1 > c0 ? (c1 - c0 + kPfxKT - 1) / kPfxKT : 0;
   const uint16_t* kh = p.k + (size_t)h * p.L * D;
-  const uint16_t* vh = p.v + (size_t)h * p.L * D;
+  const uint16_t* vth = p.vt + ((size_t)h * p.C + c) * D * p.Lc;
 
   // B operand of S^T: query column lc of each of the wave's two tiles
   u32x4 qr[2][DS];
@@ -87,43 +147,46 @@ __global__ __launch_bounds__(256) void asm_prefix_chunk(PrefixArgs p) {
   for (int dt = 0; dt < DT; ++dt) o[dt][0] = o[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {kNegInf, kNegInf}, ls[2] = {0.f, 0.f};
 
-  u32x4 kr[LPT], vr[LPT];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ci = tid + 256 * j, key = ci / CPR, col = ci % CPR;
-      const int gk = c0 + t * kPfxKT + key;
-      const bool ok = gk < c1;
-      kr[j] = ok ? *(const u32x4*)(kh + (size_t)gk * D + col * 8) : u32x4{0, 0, 0, 0};
-      vr[j] = ok ? *(const u32x4*)(vh + (size_t)gk * D + col * 8) : u32x4{0, 0, 0, 0};
+  // Tile t's K rows (rows past the prefix end read its last row; their scores
+  // are masked) and V^T block into LDS buffer `buf`, HBM -> LDS directly.
+  auto issue = [&](int t, int buf) {
+    unsigned char* kb = lds + buf * (KB + VB);
+    unsigned char* vb = kb + KB;
+    for (int i = wave; i < KI; i += kPfxQB / 32) {
+      const int r = i * (1024 / KRB) + lane / KCPR, slot = lane % KCPR;
+      const int gk = min(c0 + t * kPfxKT + r, p.L - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(kh + (size_t)gk * D + k_slot<D>(r, slot) * 8),
+                                       (lds_void_t*)(kb + i * 1024), 16, 0, 0);
     }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ci = tid + 256 * j, key = ci / CPR, col = ci % CPR;
-      *(u32x4*)&Ks[buf][key * KP + col * 8] = kr[j];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Vt[buf][(col * 8 + e) * VP + key] = (uint16_t)(vr[j][e >> 1] >> (16 * (e & 1)));
+    for (int i = wave; i < VI; i += kPfxQB / 32) {
+      const int d = i * 8 + lane / 8, slot = lane % 8;
+      __builtin_amdgcn_global_load_lds(
+          (glb_void_t*)(vth + (size_t)d * p.Lc + t * kPfxKT + vt_slot(d, slot) * 8),
+          (lds_void_t*)(vb + i * 1024), 16, 0, 0);
     }
   };
 
-  if (nt > 0) load_tile(0);
+  if (nt > 0) issue(0, 0);
   for (int t = 0; t < nt; ++t) {
     const int buf = t & 1;
-    store_tile(buf);
+    // this wave's transfers for tile t have landed (the compiler does not track
+    // LDS written by global_load_lds); the barrier makes every wave's visible and
+    // frees the other buffer (its tile was computed by everyone)
+    wait_vmem_all();
     __syncthreads();
-    if (t + 1 < nt) load_tile(t + 1);
+    if (t + 1 < nt) issue(t + 1, buf ^ 1);
+    const unsigned char* kb = lds + buf * (KB + VB);
+    const unsigned char* vb = kb + KB;
 
     // S^T tiles: rows = keys kt*16 + 4lg + i, column = this lane's query
     f32x4 s[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       s[kt][0] = s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = kt * 16 + lc;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const u32x4 a = *(const u32x4*)&Ks[buf][(kt * 16 + lc) * KP + ds * 32 + 8 * lg];
+        const u32x4 a = *(const u32x4*)(kb + r * KRB + 16 * k_slot<D>(r, ds * 4 + lg));
         s[kt][0] = mfma_16x16x32_bf16(a, qr[0][ds], s[kt][0]);
         s[kt][1] = mfma_16x16x32_bf16(a, qr[1][ds], s[kt][1]);
       }
@@ -183,9 +246,8 @@ __global__ __launch_bounds__(256) void asm_prefix_chunk(PrefixArgs p) {
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vp = &Vt[buf][(dt * 16 + lc) * VP + 32 * ks + 4 * lg];
-        const uint2 lo = *(const uint2*)vp, hi = *(const uint2*)(vp + 16);
-        const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+        const int d = dt * 16 + lc;
+        const u32x4 a = *(const u32x4*)(vb + d * 128 + 16 * vt_slot(d, 4 * ks + lg));
         o[dt][0] = mfma_16x16x32_bf16(a, ph[0], o[dt][0]);
         o[dt][1] = mfma_16x16x32_bf16(a, ph[1], o[dt][1]);
         o[dt][0] = mfma_16x16x32_bf16(a, pl[0], o[dt][0]);
@@ -425,14 +487,20 @@ __global__ __launch_bounds__(256) void km_assign(KmArgs k) {
 }
 
 // One workgroup of 16 waves per (KV head, 64 clusters); wave w owns clusters
-// k0 + w + 16c (c = 0..3).  Rounds of 1024 labels: members of the block's clusters
-// are listed in index order in LDS, then each wave takes its clusters' members in
-// batches of four (lane group lg takes every fourth), so every sum is formed in an
-// order fixed by N and the assignment alone.
+// k0 + w + 16c (c = 0..3).  The assignment is taken in passes of 16 x 1024 labels:
+// wave w scans the pass's w-th run of 1024 labels (all loaded up front) and lists,
+// in index order, those that fall in the block's clusters in its own LDS region.
+// After one barrier each wave walks the regions in wave order (that is, in index
+// order), copies its own clusters' members to a private buffer and works them off
+// sixteen at a time, lane group lg taking every fourth, so that every sum is
+// formed in an order fixed by N and the assignment alone.
 template <int D, bool MERGE>
 __global__ __launch_bounds__(1024) void km_reduce(KmArgs k) {
   constexpr int V = D / 16;
-  __shared__ uint32_t list[kRedRound];
+  constexpr int kRun = 1024;  // labels per wave per pass
+  constexpr int kWaveBuf = 256;  // per-wave member buffer
+  __shared__ uint32_t list[16 * kRun];
+  __shared__ uint32_t wbuf[16 * kWaveBuf];
   __shared__ int wcnt[16];
   const int H = k.H;
   const int h = blockIdx.x % H, k0 = (blockIdx.x / H) * 64;
@@ -451,101 +519,120 @@ __global__ __launch_bounds__(1024) void km_reduce(KmArgs k) {
     cnt[c] = 0;
   }
 
-  for (int r0 = 0; r0 < k.N; r0 += kRedRound) {
-    const int i = r0 + tid;
-    const int loc = i < k.N ? lab[i] - k0 : -1;
-    const bool in = (unsigned)loc < 64u;
-    const uint64_t bal = __ballot(in);
-    if (lane == 0) wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int base = 0, n = 0;
+  // This wave's members, in index order, buffered in `mine` and worked off sixteen
+  // at a time: lane group lg takes entries lg, lg + 4, ... of each batch (all row
+  // loads of a batch are in flight together).
+  uint32_t* mine = wbuf + wave * kWaveBuf;
+  auto work_off = [&](int nm) {
+    for (int b0 = 0; b0 < nm; b0 += 16) {
+      uint32_t e[4];
+      float val[4][V];
+      float vl[4];
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const int cw = wcnt[w];
-      base += w < wave ? cw : 0;
-      n += cw;
-    }
-    if (in) list[base + __popcll(bal & ((1ull << lane) - 1ull))] = ((uint32_t)i << 6) | loc;
-    __syncthreads();
-
-    for (int j0 = 0; j0 < n; j0 += 64) {
-      const bool ok = j0 + lane < n;
-      const uint32_t e = ok ? list[j0 + lane] : 0u;
+      for (int bb = 0; bb < 4; ++bb) {
+        const int j = b0 + 4 * bb + lg;
+        e[bb] = j < nm ? mine[j] : 0xFFFFFFFFu;
+        vl[bb] = kNegInf;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint64_t mk = __ballot(ok && (e & 63u) == (uint32_t)(wave + 16 * c));
-        cnt[c] += __popcll(mk);
-        while (mk) {
-          int src[4];
+        for (int q = 0; q < V; ++q) val[bb][q] = 0.f;
+        if (e[bb] == 0xFFFFFFFFu) continue;
+        const size_t pi = (size_t)h * k.N + (e[bb] >> 6);
+        if constexpr (MERGE) {
+          const float* sp = k.a + pi * D + lc * V;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            src[b] = -1;
+          for (int q = 0; q < V; q += 4) {
+            const f32x4 x = *(const f32x4*)(sp + q);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int pos = mk ? __builtin_ctzll(mk) : -1;
-              if (g == lg) src[b] = pos;
-              mk &= mk - 1ull;
-            }
+            for (int r = 0; r < 4; ++r) val[bb][q + r] = x[r];
           }
-          float val[4][V];
-          float vl[4];
+          vl[bb] = k.lse[pi];
+        } else {
+          const uint16_t* xp = k.x + pi * D + lc * V;
+          uint32_t w[V / 2];
+          if constexpr (V == 8) {
+            const u32x4 x = *(const u32x4*)xp;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t em = __shfl(e, src[b] < 0 ? 0 : src[b], 64);
-            const size_t pi = (size_t)h * k.N + (em >> 6);
-            vl[b] = kNegInf;
-#pragma unroll
-            for (int j = 0; j < V; ++j) val[b][j] = 0.f;
-            if (src[b] < 0) continue;
-            if constexpr (MERGE) {
-              const float* sp = k.a + pi * D + lc * V;
-#pragma unroll
-              for (int j = 0; j < V; j += 4) {
-                const f32x4 x = *(const f32x4*)(sp + j);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) val[b][j + q] = x[q];
-              }
-              vl[b] = k.lse[pi];
-            } else {
-              const uint16_t* xp = k.x + pi * D + lc * V;
-              uint32_t w[V / 2];
-              if constexpr (V == 8) {
-                const u32x4 x = *(const u32x4*)xp;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) w[q] = x[q];
-              } else {
-                const uint2 x = *(const uint2*)xp;
-                w[0] = x.x;
-                w[1] = x.y;
-              }
-#pragma unroll
-              for (int q = 0; q < V / 2; ++q) {
-                val[b][2 * q] = bf16_bits_to_f32(w[q] & 0xFFFFu);
-                val[b][2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
-              }
-            }
+            for (int r = 0; r < 4; ++r) w[r] = x[r];
+          } else {
+            const uint2 x = *(const uint2*)xp;
+            w[0] = x.x;
+            w[1] = x.y;
           }
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            if (src[b] < 0) continue;
-            if constexpr (MERGE) {
-              if (vl[b] == kNegInf) continue;
-              const float mn = fmaxf(mm[c], vl[b]);
-              const float sc = exp2_fast((mm[c] - mn) * kLog2e);
-              const float wi = exp2_fast((vl[b] - mn) * kLog2e);
+          for (int r = 0; r < V / 2; ++r) {
+            val[bb][2 * r] = bf16_bits_to_f32(w[r] & 0xFFFFu);
+            val[bb][2 * r + 1] = bf16_bits_to_f32(w[r] >> 16);
+          }
+        }
+      }
 #pragma unroll
-              for (int j = 0; j < V; ++j) acc[c][j] = acc[c][j] * sc + wi * val[b][j];
-              ss[c] = ss[c] * sc + wi;
-              mm[c] = mn;
-            } else {
+      for (int bb = 0; bb < 4; ++bb) {
+        if (e[bb] == 0xFFFFFFFFu) continue;
+        const int cs = (int)((e[bb] & 63u) >> 4);
+        // selects rather than a branch per cluster: keeps acc[][] in registers
 #pragma unroll
-              for (int j = 0; j < V; ++j) acc[c][j] += val[b][j];
-            }
+        for (int c = 0; c < 4; ++c) {
+          const bool hit = c == cs;
+          cnt[c] += hit ? 1 : 0;
+          if constexpr (MERGE) {
+            const bool use = hit && vl[bb] != kNegInf;
+            const float mn = use ? fmaxf(mm[c], vl[bb]) : mm[c];
+            const float sc = use ? exp2_fast((mm[c] - mn) * kLog2e) : 1.f;
+            const float wi = use ? exp2_fast((vl[bb] - mn) * kLog2e) : 0.f;
+#pragma unroll
+            for (int q = 0; q < V; ++q)
+              acc[c][q] = use ? acc[c][q] * sc + wi * val[bb][q] : acc[c][q];
+            ss[c] = use ? ss[c] * sc + wi : ss[c];
+            mm[c] = mn;
+          } else {
+#pragma unroll
+            for (int q = 0; q < V; ++q) acc[c][q] = hit ? acc[c][q] + val[bb][q] : acc[c][q];
           }
         }
       }
     }
+  };
+
+  for (int s0 = 0; s0 < k.N; s0 += 16 * kRun) {
+    const int r0 = s0 + wave * kRun;
+    int labv[kRun / 64];
+#pragma unroll
+    for (int r = 0; r < kRun / 64; ++r) {
+      const int i = r0 + r * 64 + lane;
+      labv[r] = i < k.N ? lab[i] : -1;
+    }
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < kRun / 64; ++r) {
+      const int i = r0 + r * 64 + lane;
+      const int loc = labv[r] - k0;
+      const bool in = labv[r] >= 0 && (unsigned)loc < 64u;
+      const uint64_t bal = __ballot(in);
+      if (in) list[wave * kRun + n + __popcll(bal & ((1ull << lane) - 1ull))] =
+          ((uint32_t)i << 6) | loc;
+      n += __popcll(bal);
+    }
+    if (lane == 0) wcnt[wave] = n;
     __syncthreads();
+    // collect this wave's clusters' members from the regions, in wave (= index) order
+    int nm = 0;
+    for (int w2 = 0; w2 < 16; ++w2) {
+      const int n2 = wcnt[w2];
+      for (int j0 = 0; j0 < n2; j0 += 64) {
+        const bool ok = j0 + lane < n2;
+        const uint32_t ev = ok ? list[w2 * kRun + j0 + lane] : 0u;
+        const bool my = ok && (int)(ev & 15u) == wave;
+        const uint64_t bal = __ballot(my);
+        if (my) mine[nm + __popcll(bal & ((1ull << lane) - 1ull))] = ev;
+        nm += __popcll(bal);
+        if (nm > kWaveBuf - 64) {
+          work_off(nm);
+          nm = 0;
+        }
+      }
+    }
+    work_off(nm);
+    __syncthreads();  // regions and counts are rewritten by the next pass
   }
 
   // combine the four lane groups (xor 16, then xor 32)
@@ -569,6 +656,7 @@ __global__ __launch_bounds__(1024) void km_reduce(KmArgs k) {
 #pragma unroll
         for (int j = 0; j < V; ++j) acc[c][j] += __shfl_xor(acc[c][j], o, 64);
       }
+      cnt[c] += __shfl_xor(cnt[c], o, 64);
     }
   }
 
@@ -630,35 +718,60 @@ static bool build_dims_ok(int H, int N, int D) {
   return true;
 }
 
+// Workspace of the prefix-state computation: V^T per chunk, then (more than one
+// chunk) the chunk states and their lse.
+static size_t prefix_layout(int H, int N, int D, int L, int chunks, int& C, int& csize, int& Lc,
+                            size_t& o_vt, size_t& o_part, size_t& o_plse) {
+  C = prefix_chunks(L, chunks, csize);
+  Lc = (csize + kPfxKT - 1) / kPfxKT * kPfxKT;
+  const size_t rows = (size_t)H * N;
+  o_vt = kWsHeader;
+  o_part = o_vt + (L > 0 ? align_up((size_t)H * C * D * Lc * 2, 256) : 0);
+  o_plse = o_part + (C > 1 ? align_up((size_t)C * rows * D * 4, 256) : 0);
+  return o_plse + (C > 1 ? align_up((size_t)C * rows * 4, 256) : 0);
+}
+
 static int32_t launch_prefix(const void* q, int32_t H, int32_t N, int32_t D, const void* k,
                              const void* v, int32_t L, int32_t chunks, float scale, float* a,
                              float* lse, void* ws, hipStream_t s) {
-  int csize;
-  const int C = prefix_chunks(L, chunks, csize);
+  int C, csize, Lc;
+  size_t o_vt, o_part, o_plse;
+  prefix_layout(H, N, D, L, chunks, C, csize, Lc, o_vt, o_part, o_plse);
   PrefixArgs p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
+  p.vt = (uint16_t*)((char*)ws + o_vt);
   p.H = H;
   p.N = N;
   p.L = L;
+  p.C = C;
   p.csize = csize;
+  p.Lc = Lc;
   p.scale_log2 = scale * kLog2e;
   const size_t rows = (size_t)H * N;
   if (C == 1) {
     p.out = a;
     p.out_lse = lse;
   } else {
-    p.out = (float*)((char*)ws + kWsHeader);
-    p.out_lse = (float*)((char*)ws + kWsHeader + align_up((size_t)C * rows * D * 4, 256));
+    p.out = (float*)((char*)ws + o_part);
+    p.out_lse = (float*)((char*)ws + o_plse);
+  }
+  if (L > 0) {
+    TraceScope tr(kTrAsmVt, s);
+    const dim3 g((unsigned)((size_t)H * C * (Lc / kPfxKT)));
+    if (D == 128)
+      hipLaunchKernelGGL(vt_prepare<128>, g, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(vt_prepare<64>, g, dim3(256), 0, s, p);
   }
   const dim3 grid(H * ((N + kPfxQB - 1) / kPfxQB), C);
   {
     TraceScope tr(kTrAsmPrefix, s);
     if (D == 128)
-      hipLaunchKernelGGL(asm_prefix_chunk<128>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(asm_prefix_chunk<128>, grid, dim3(kPfxQB * 2), 0, s, p);
     else
-      hipLaunchKernelGGL(asm_prefix_chunk<64>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(asm_prefix_chunk<64>, grid, dim3(kPfxQB * 2), 0, s, p);
   }
   if (C > 1) {
     TraceScope tr(kTrAsmPrefixMerge, s);
@@ -763,12 +876,11 @@ using namespace kvb;
 
 extern "C" size_t asm_prefix_states_workspace(int32_t H, int32_t N, int32_t D, int32_t L,
                                               int32_t chunks) {
-  if (!build_dims_ok(H, N, D) || L < 0 || chunks < 1 || (D != 64 && D != 128)) return 0;
-  int csize;
-  const int C = prefix_chunks(L, chunks, csize);
-  if (C == 1) return kWsHeader;
-  const size_t rows = (size_t)H * N;
-  return kWsHeader + align_up((size_t)C * rows * D * 4, 256) + align_up((size_t)C * rows * 4, 256);
+  if (!build_dims_ok(H, N, D) || L < 0 || L >= (1 << 30) || chunks < 1 || (D != 64 && D != 128))
+    return 0;
+  int C, csize, Lc;
+  size_t a, b, c;
+  return prefix_layout(H, N, D, L, chunks, C, csize, Lc, a, b, c);
 }
 
 extern "C" int32_t asm_prefix_states(const void* q, int32_t H, int32_t N, int32_t D,

@@ -113,7 +113,7 @@ enum TraceKernel {
   kTrAttnSplit = 1, kTrAttnMerge = 2, kTrAppend = 4, kTrEvictSelect = 8, kTrKeepCount = 16,
   kTrKeepEmit = 32, kTrCompactMove = 64, kTrAsmLookup = 128, kTrAsmFinalize = 256,
   kTrAttnFused = 512, kTrAsmPrefix = 1024, kTrAsmPrefixMerge = 2048, kTrKmAssign = 4096,
-  kTrKmUpdate = 8192, kTrAsmAggregate = 16384
+  kTrKmUpdate = 8192, kTrAsmAggregate = 16384, kTrAsmVt = 32768
 };
 struct TraceScope {
   TraceScope(int kernel, hipStream_t s);

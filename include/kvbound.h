@@ -366,7 +366,8 @@ int32_t asm_build_memory(const void* q, int32_t H, int32_t N, int32_t D, const v
  * attention split kernel that also moves kept rows (kv_attn_decode_compact),
  * 1024 prefix-state chunk kernel, 2048 prefix chunk merge, 4096 K-means
  * assignment, 8192 K-means centroid update (and the initial centroid split),
- * 16384 state aggregation.
+ * 16384 state aggregation, 32768 the value transpose before the prefix-state
+ * chunk kernel.
  * kvb_trace_read waits for the recorded pairs and writes, for the first `max`,
  * the kernel bit and the elapsed milliseconds (-1 if unavailable); it returns
  * how many it wrote (host arrays).  kvb_trace_reset reuses the pairs from the
