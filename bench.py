@@ -87,7 +87,9 @@ def steady_bench(args):
     KV head of the 36 layers holds M = 4096 tokens; a step appends one token per
     layer, attends over M + 1, evicts the lowest-retention token and compacts (every
     kept row after the evicted slot moves down by one).  Eviction planning runs on a
-    second stream beside the attention, the compaction after it; the whole step is
+    second stream beside the attention; each compaction runs beside the next
+    layer's attention (the default; with --schedule deferred all compactions follow
+    the last layer's attention); the whole step is
     captured once in a HIP graph and replayed (t advances on the device).  A second,
     eager run of the same steps with the library's HIP-event trace gives the
     per-kernel split."""
@@ -120,6 +122,8 @@ def steady_bench(args):
     side = torch.cuda.Stream()
     appended = [torch.cuda.Event() for _ in range(L)]
     attended = [torch.cuda.Event() for _ in range(L)]
+    planned = [torch.cuda.Event() for _ in range(L)]
+    deferred = args.schedule == "deferred"  # default here: beside the next attention
 
     def step():
         main = torch.cuda.current_stream()
@@ -131,9 +135,16 @@ def steady_bench(args):
             kvb.kv_evict_plan(kvs[layer], t, M, n_evicted=nev[layer], ws=ws_e[layer], stream=side)
             kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=out, lse=lse,
                                ws=ws_a, stream=main)
+            if deferred:
+                planned[layer].record(side)
+                continue
             attended[layer].record(main)
             side.wait_event(attended[layer])
             kvb.kv_evict_apply(kvs[layer], M, ws_e[layer], stream=side)
+        if deferred:
+            for layer in range(L):
+                main.wait_event(planned[layer])
+                kvb.kv_evict_apply(kvs[layer], M, ws_e[layer], stream=main)
         main.wait_stream(side)
         t.add_(1)
 
@@ -178,7 +189,8 @@ def steady_bench(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
-                   "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True},
+                   "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True,
+                   "schedule": "deferred" if deferred else "both_beside"},
         "eager_ms_per_step": round(eager_ms, 4), "kernel_us_eager": split,
         "attention_bytes_per_layer": attn_b}), flush=True)
 
@@ -355,6 +367,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--serial", action="store_true",
                     help="run each layer's eviction planning on the attention stream (no overlap)")
+    ap.add_argument("--schedule", default=None,
+                    choices=["plan_beside", "both_beside", "deferred"],
+                    help="deferred (default of the 32K step): each layer's eviction plan runs "
+                         "beside its attention and all layers' compactions follow the last "
+                         "attention; plan_beside: each compaction right after its layer's "
+                         "attention; both_beside (default of --steady): each compaction beside "
+                         "the next layer's attention")
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
@@ -426,7 +445,11 @@ def main():
     first_ev = [torch.empty((B, w.hkv, 1), dtype=torch.int32, device=dev) for _ in range(L)]
     ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, args.splits), dtype=torch.uint8,
                        device=dev)
-    ws_e = torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device=dev)
+    sched = "serial" if args.serial else (args.schedule or "deferred")
+    # one eviction workspace per layer when the plans outlive the next layer's planning
+    n_ws = L if sched == "deferred" else 1
+    ws_es = [torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device=dev)
+             for _ in range(n_ws)]
     splits = args.splits or kvb.kv_attn_decode_splits(kvs[0], w.hq)
 
     def restore():
@@ -435,17 +458,20 @@ def main():
                 d[k][:, :, :M].copy_(p[k])
             d["len"].fill_(w.ctx)
 
-    # Per layer: append the decode token, then plan the eviction (reads log beta and
-    # positions only) on a side stream.  Default: attention over the whole cache
-    # beside the planner; the compaction pass (re-reads the kept rows) follows on
-    # the side stream, beside the next layer's attention.  --fused: attention over
-    # the tiles below the destination boundary runs beside the planner; the rest
-    # waits for the plan and writes every kept row to its compacted slot from the
-    # data it has loaded.  Layer l+1's
-    # work starts after layer l's attention (its inputs would come from it).  The
-    # side stream has default priority and is joined at the end.
+    # Per layer: append the decode token, plan the eviction (reads log beta and
+    # positions only) on a side stream beside the attention over the whole cache,
+    # then compact (re-reads the kept rows, writes them to their slots).  Where the
+    # compaction runs is the schedule: after the last layer's attention (deferred,
+    # the default: a layer is not attended again before the next step, and HBM sees
+    # the step's reads and its writes in two phases instead of interleaved), right
+    # after the layer's attention (plan_beside), or beside the next layer's
+    # attention on the side stream (both_beside).  --fused: attention over the tiles below
+    # the destination boundary runs beside the planner; the rest waits for the plan
+    # and writes every kept row to its compacted slot from the data it has loaded.
+    # Layer l+1's work starts after layer l's attention (its inputs would come from
+    # it).  The side stream has default priority and is joined at the end.
     main = torch.cuda.current_stream()
-    side = main if args.serial else torch.cuda.Stream()
+    side = main if sched == "serial" else torch.cuda.Stream()
     appended = [torch.cuda.Event() for _ in range(L)]
     planned = [torch.cuda.Event() for _ in range(L)]
     attended = [torch.cuda.Event() for _ in range(L)]
@@ -454,6 +480,7 @@ def main():
     def step():
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
+            ws_e = ws_es[layer % n_ws]
             kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
             if side is not main:
                 appended[layer].record(main)
@@ -473,10 +500,21 @@ def main():
                 continue
             kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=outs[layer],
                                lse=lses[layer], ws=ws_a, stream=main)
-            if side is not main:
+            if sched == "both_beside":
                 attended[layer].record(main)
                 side.wait_event(attended[layer])
-            kvb.kv_evict_apply(kvs[layer], M, ws_e, stream=side)
+                kvb.kv_evict_apply(kvs[layer], M, ws_e, stream=side)
+            elif sched in ("plan_beside", "serial"):
+                if side is not main:
+                    planned[layer].record(side)
+                    main.wait_event(planned[layer])
+                kvb.kv_evict_apply(kvs[layer], M, ws_e, stream=main)
+            else:
+                planned[layer].record(side)
+        if sched == "deferred":
+            for layer in range(L):
+                main.wait_event(planned[layer])
+                kvb.kv_evict_apply(kvs[layer], M, ws_es[layer], stream=main)
         if side is not main:
             main.wait_stream(side)
 
@@ -502,6 +540,20 @@ def main():
                 q0[b, g * w.group:(g + 1) * w.group].view(torch.int16).numpy().view(np.uint16),
                 kn0[b, g].view(torch.int16).numpy().view(np.uint16),
                 vn0[b, g].view(torch.int16).numpy().view(np.uint16), float(lb0[b, g])))
+
+    # secondary reference: a plain device copy (reads and writes 1 GiB each per call)
+    cx = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cy = torch.empty_like(cx)
+    cy.copy_(cx)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        cy.copy_(cx)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cx, cy
 
     kvb.trace_enable(2 * args.steps * L + 16, ("attn_split", "attn_fused"))
     e0 = torch.cuda.Event(enable_timing=True)
@@ -560,9 +612,10 @@ def main():
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "ctx": w.ctx, "budget": M, "layers": L,
                    "kv_splits": splits,
-                   "eviction_stream": "serial" if args.serial else "overlapped",
+                   "schedule": sched,
                    "compaction": "fused" if fused else "separate pass"},
         "kv_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "device_copy_gbps": round(copy_gbps, 1), "copy_frac": round(gbps / copy_gbps, 4),
         "bytes_per_step": total_b, "moved_rows_per_step": moved,
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

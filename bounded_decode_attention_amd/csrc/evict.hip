@@ -854,7 +854,7 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
       const unsigned char* from =
           staged ? scr + (size_t)j * a.srow + (isv ? a.row_bytes : 0) + 16 * pc
                  : tb + (size_t)src[q] * a.row_bytes + 16 * pc;
-      buf[q] = *(const u32x4*)from;
+      buf[q] = __builtin_nontemporal_load((const u32x4*)from);
     }
     int32_t tail_lb = 0, tail_pos = 0, tail_dst = -1;
     if (tid < rows) {
@@ -877,7 +877,7 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
     for (int q = 0; q < kMovePieces; ++q) {
       if (src[q] < 0) continue;
       const int j = j0 + r0 + q * rpp;
-      *(u32x4*)(tb + (size_t)j * a.row_bytes + 16 * pc) = buf[q];
+      __builtin_nontemporal_store(buf[q], (u32x4*)(tb + (size_t)j * a.row_bytes + 16 * pc));
     }
     if (tail_dst >= 0) {
       if (lbb) lbb[tail_dst] = __int_as_float(tail_lb);
