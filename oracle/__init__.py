@@ -28,6 +28,10 @@ Every function is a direct, unblocked statement of what the pages define:
 * ``asm_build``   -- construction of that memory: prefix attention states of
   calibration queries (chunked and merged), K-means over the queries, and the
   merge of each cluster's states (Context Memorization, method steps 1 and 2).
+* ``latent``      -- IndexMem's latent memory of evicted tokens: decayed
+  outer-product fast weights (M, b) and the gated residual read-out ("IndexMem:
+  Learned KV-Cache Eviction with Latent Memory for Long-Context LLM Inference",
+  technical summary, section 2, part B).
 * ``bytes_model`` -- KV bytes per token, pinned to IndexMem's memory-wall figure
   ("IndexMem: Learned KV-Cache Eviction with Latent Memory for Long-Context LLM
   Inference", technical summary, section 1).
@@ -47,6 +51,7 @@ from .asm import (cosine_similarities, cosine_lookup, asm_merge, asm_lookup_merg
 from .asm_build import (chunk_bounds, prefix_states, nearest_centroid, centroid_update,
                         kmeans, aggregate_states, build_memory)
 from .bytes_model import kv_bytes_per_token, attention_layer_bytes
+from .latent import phi, latent_absorb, latent_read, latent_residual
 from .decode import run_decode_steps
 
 __all__ = [
@@ -59,4 +64,5 @@ __all__ = [
     "chunk_bounds", "prefix_states", "nearest_centroid", "centroid_update", "kmeans",
     "aggregate_states", "build_memory",
     "kv_bytes_per_token", "attention_layer_bytes", "run_decode_steps",
+    "phi", "latent_absorb", "latent_read", "latent_residual",
 ]

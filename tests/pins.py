@@ -22,6 +22,7 @@ import oracle.asm_build as OAB
 import oracle.attn as OT
 import oracle.bytes_model as OB
 import oracle.evict as OE
+import oracle.latent as OL
 
 TOL = 1e-11
 
@@ -426,6 +427,55 @@ def check_asm_build(seed=11):
     assert lz[2] == -np.inf and not np.any(abar[2])                   # empty cluster
 
 
+# ---------------------------------------------------------------- P12
+def check_latent_memory(seed=12):
+    """Latent memory of evicted tokens: the feature map against torch's elu, the
+    decayed accumulation against its closed form (a weighted matrix product),
+    online = one call, empty = identity; the read of a one-token memory returns that
+    token's value, a two-token memory the feature-map-weighted average of the
+    values; the gate against scipy's expit."""
+    r = _rng(seed)
+    x = r.standard_normal(50) * 3.0
+    ref = torch.nn.functional.elu(torch.tensor(x, dtype=torch.float64)).numpy() + 1.0
+    assert np.allclose(OL.phi(x), ref, rtol=0, atol=1e-15), "phi != elu + 1"
+    D, n, lam = 6, 9, 0.85
+    M0 = r.standard_normal((D, D))
+    b0 = np.abs(r.standard_normal(D))
+    K = r.standard_normal((n, D))
+    V = r.standard_normal((n, D))
+    M1, b1 = OL.latent_absorb(M0, b0, K, V, lam)
+    w = lam ** (n - 1 - np.arange(n))
+    F = torch.nn.functional.elu(torch.tensor(K, dtype=torch.float64)).numpy() + 1.0
+    Mref = lam ** n * M0 + (torch.tensor(F * w[:, None]).T @ torch.tensor(V)).numpy()
+    bref = lam ** n * b0 + (F * w[:, None]).sum(0)
+    assert np.allclose(M1, Mref, rtol=0, atol=1e-12), "decayed accumulation"
+    assert np.allclose(b1, bref, rtol=0, atol=1e-12), "stabiliser accumulation"
+    Ma, ba = OL.latent_absorb(M0, b0, K[:4], V[:4], lam)
+    Mb, bb = OL.latent_absorb(Ma, ba, K[4:], V[4:], lam)
+    assert np.allclose(Mb, M1, rtol=0, atol=1e-12) and np.allclose(bb, b1, rtol=0, atol=1e-12)
+    Me, be = OL.latent_absorb(M0, b0, K[:0], V[:0], lam)
+    assert np.array_equal(Me, M0) and np.array_equal(be, b0), "empty absorb must be identity"
+    # one-token memory: the read is that token's value (eps = 0, W_o = I)
+    Z = np.zeros((D, D))
+    M1t, b1t = OL.latent_absorb(Z, np.zeros(D), K[:1], V[:1], lam)
+    q = r.standard_normal(D)
+    res, g = OL.latent_read(M1t, b1t, q, np.eye(D), np.zeros(D), 0.0, 0.0)
+    assert abs(g - 0.5) < 1e-15 and np.allclose(res, 0.5 * V[0], rtol=0, atol=1e-12)
+    # two tokens, lam = 1: weights phi(q).phi(k_i); projection applied after the read
+    M2, b2 = OL.latent_absorb(Z, np.zeros(D), K[:2], V[:2], 1.0)
+    W = r.standard_normal((D, D))
+    fq = torch.nn.functional.elu(torch.tensor(q)).numpy() + 1.0
+    a = np.array([fq @ F[0], fq @ F[1]])
+    want = W @ ((a[0] * V[0] + a[1] * V[1]) / (a[0] + a[1]))
+    wg = r.standard_normal(D)
+    res, g = OL.latent_read(M2, b2, q, W, wg, 0.3, 0.0)
+    assert abs(g - float(scipy.special.expit(wg @ q + 0.3))) < 1e-15, "gate != sigmoid"
+    assert np.allclose(res, g * want, rtol=0, atol=1e-12), "read of a two-token memory"
+    o = r.standard_normal(D)
+    assert np.allclose(OL.latent_residual(o, M2, b2, q, W, wg, 0.3, 0.0), o + g * want,
+                       rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- P9
 def check_bytes_model():
     """IndexMem's memory-wall estimate: ~320 GB of KV for a 70B model at 1M tokens."""
@@ -436,4 +486,4 @@ def check_bytes_model():
 ALL = [check_attention_library, check_bias_closed_form, check_split_merge,
        check_asm_lossless, check_evict_bruteforce, check_evict_sliding_window,
        check_evict_invariants, check_compaction, check_erase_bruteforce,
-       check_lookup_bruteforce, check_hier_lookup, check_asm_build, check_bytes_model]
+       check_lookup_bruteforce, check_hier_lookup, check_asm_build, check_latent_memory, check_bytes_model]

@@ -12,6 +12,7 @@ import oracle.asm as OA
 import oracle.asm_build as OAB
 import oracle.attn as OT
 import oracle.evict as OE
+import oracle.latent as OL
 import pins
 
 _orig_bias = OT.retention_bias
@@ -22,6 +23,8 @@ _orig_plan = OE.evict_plan
 _orig_hier = OA.hier_lookup
 _orig_update = OAB.centroid_update
 _orig_bounds = OAB.chunk_bounds
+_orig_absorb = OL.latent_absorb
+_orig_read = OL.latent_read
 
 
 def bias_sign_flipped(log_beta, pos, t):
@@ -239,6 +242,42 @@ def compact_reversed(cache, b, g, keep):
     return kept
 
 
+def phi_identity(x):
+    return np.asarray(x, np.float64)
+
+
+def absorb_no_decay(Mst, bst, K_ev, V_ev, lam):
+    return _orig_absorb(Mst, bst, K_ev, V_ev, 1.0)
+
+
+def absorb_reversed(Mst, bst, K_ev, V_ev, lam):
+    return _orig_absorb(Mst, bst, np.asarray(K_ev)[::-1], np.asarray(V_ev)[::-1], lam)
+
+
+def absorb_kv_swapped(Mst, bst, K_ev, V_ev, lam):
+    Mst = np.array(Mst, np.float64)
+    bst = np.array(bst, np.float64)
+    for k, v in zip(np.asarray(K_ev, np.float64), np.asarray(V_ev, np.float64)):
+        Mst = lam * Mst + np.outer(v, OL.phi(k))
+        bst = lam * bst + OL.phi(k)
+    return Mst, bst
+
+
+def read_no_stabiliser(Mst, bst, q, W_o, w_g, c_g, eps):
+    res, g = _orig_read(Mst, bst, q, W_o, w_g, c_g, eps)
+    f = OL.phi(q)
+    return res * (float(np.asarray(bst) @ f) + eps), g
+
+
+def read_gate_flipped(Mst, bst, q, W_o, w_g, c_g, eps):
+    res, g = _orig_read(Mst, bst, q, W_o, w_g, c_g, eps)
+    return res / g * (1.0 - g), 1.0 - g
+
+
+def read_no_projection(Mst, bst, q, W_o, w_g, c_g, eps):
+    return _orig_read(Mst, bst, q, np.eye(np.asarray(W_o).shape[0]), w_g, c_g, eps)
+
+
 MUTANTS = [
     (OT, "retention_bias", bias_sign_flipped),
     (OT, "retention_bias", bias_dropped),
@@ -269,6 +308,13 @@ MUTANTS = [
     (OAB, "centroid_update", update_empty_to_zero),
     (OAB, "aggregate_states", aggregate_plain_average),
     (OAB, "chunk_bounds", bounds_drop_last),
+    (OL, "phi", phi_identity),
+    (OL, "latent_absorb", absorb_no_decay),
+    (OL, "latent_absorb", absorb_reversed),
+    (OL, "latent_absorb", absorb_kv_swapped),
+    (OL, "latent_read", read_no_stabiliser),
+    (OL, "latent_read", read_gate_flipped),
+    (OL, "latent_read", read_no_projection),
 ]
 
 
