@@ -355,6 +355,75 @@ def build_bench(args):
     }), flush=True)
 
 
+def latent_bench(args):
+    """Latent memory of evicted tokens, one layer of the 32K decode workload (batch
+    16, 8 KV heads, D = 128): the update after the eviction of 32769 -> 4096 tokens
+    per KV head (28,673 absorbed each), the update in the steady state (one token per
+    KV head), and the read-out for the 32 query heads.  Plans are made once
+    (neither call changes the cache); each figure is the mean of repeated calls."""
+    import numpy as np
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    B, H, D, M = w.batch, w.hkv, w.head_dim, w.budget
+    prm = synth.host_latent_params(D, w.hq, 77)
+    mM = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
+    mb = torch.zeros((B, H, D), dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1000.0
+
+    rows = {}
+    for name, n in (("evict_32k", w.ctx + 1), ("steady", M + 1)):
+        dc = synth.device_cache(w, layer=0, n=n, cap=n + 31)
+        c = kvb.KVCache.from_dict(dc)
+        t = torch.full((B,), n, dtype=torch.int32, device="cuda")
+        nev, ws_e = kvb.kv_evict_plan(c, t, M)
+        ws = torch.empty(kvb.kv_latent_absorb_workspace(c), dtype=torch.uint8, device="cuda")
+        us = timed(lambda: kvb.kv_latent_absorb(c, M, ws_e, prm["lam"], mM, mb, ws=ws),
+                   10 if name == "evict_32k" else 50)
+        ne = int(nev.sum().item())
+        S = (n + 31 + 4095) // 4096
+        state_b = B * H * (D * D + D) * 4
+        chunks = sum(min(S, (int(x) + 4095) // 4096) for x in nev.flatten().tolist())
+        byts = ne * 2 * D * 2 + 2 * state_b + chunks * (D * D + D) * 4 * 2
+        rows[name] = {"evicted_per_head": ne // (B * H), "us": round(us, 1),
+                      "bytes": byts, "gbps": round(byts / (us * 1e-6) / 1e9, 1),
+                      "tflops": round(2.0 * ne * D * D / (us * 1e-6) / 1e12, 1)}
+        print(f"# {name} {rows[name]}", file=sys.stderr, flush=True)
+        del dc, c
+        torch.cuda.empty_cache()
+    q = synth.device_queries(w, 0)[0]
+    out = torch.zeros((B, w.hq, D), dtype=torch.float32, device="cuda")
+    W_o, w_g, c_g = (torch.from_numpy(prm[k]).cuda() for k in ("W_o", "w_g", "c_g"))
+    mb.fill_(1.0)
+    us = timed(lambda: kvb.kv_latent_read(q, mM, mb, W_o, w_g, c_g, prm["eps"], out), 50)
+    rows["read"] = {"us": round(us, 1)}
+    ev = rows["evict_32k"]
+    print(json.dumps({
+        "metric": "latent-memory update after evicting 32769 -> 4096 tokens per KV head",
+        "value": ev["us"], "unit": "us", "n_gpus": 1, "higher_is_better": False,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_32k (one layer)", "batch": B, "kv_heads": H,
+                   "head_dim": D, "budget": M, "lam": prm["lam"]},
+        "roofline": {"bound": "hbm", "kernel": "latent_absorb_part + list + combine",
+                     "achieved": ev["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ev["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cases": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +455,9 @@ def main():
     ap.add_argument("--asm-build", action="store_true",
                     help="time the offline build of one layer's attention-state memory "
                          "(prefix states in 4 chunks, K-means, aggregation; one JSON line)")
+    ap.add_argument("--latent", action="store_true",
+                    help="time the latent memory of evicted tokens (update after the 32K "
+                         "eviction, steady-state update, read-out; one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy kernel 5 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -405,6 +477,9 @@ def main():
         return
     if args.asm_build:
         build_bench(args)
+        return
+    if args.latent:
+        latent_bench(args)
         return
     if args.steady:
         steady_bench(args)

@@ -8,7 +8,8 @@ not build it, and every call fails loudly if it is missing.
 Entry points (same names as the C ABI in include/kvbound.h):
     kv_attn_decode, kv_evict_to_budget, kv_erase_ranges, asm_lookup_merge
 and, for building the memory asm_lookup_merge reads, asm_prefix_states,
-asm_kmeans, asm_aggregate_states, asm_build_memory;
+asm_kmeans, asm_aggregate_states, asm_build_memory; and the latent memory of
+evicted tokens, kv_latent_absorb and kv_latent_read;
 plus the workspace-size helpers and ``KVCache``, a holder of one layer's tensors.
 """
 from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
@@ -19,6 +20,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    kv_append, kv_attn_decode, kv_attn_decode_compact, kv_attn_decode_splits,
                    kv_attn_decode_workspace,
                    kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_plan,
+                   kv_latent_absorb, kv_latent_absorb_workspace, kv_latent_read,
                    kv_evict_to_budget,
                    kv_evict_workspace, library, library_path, strerror, trace_disable,
                    trace_enable, trace_read, trace_reset)
@@ -27,6 +29,7 @@ __all__ = [
     "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_attn_decode_compact",
     "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",
+    "kv_latent_absorb", "kv_latent_absorb_workspace", "kv_latent_read",
     "asm_prefix_states", "asm_kmeans", "asm_aggregate_states", "asm_build_memory",
     "asm_prefix_states_workspace", "asm_kmeans_workspace", "asm_build_memory_workspace",
     "kv_attn_decode_workspace", "kv_attn_decode_splits",

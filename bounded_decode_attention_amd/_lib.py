@@ -68,6 +68,9 @@ def library():
             "asm_aggregate_states": (I32, [P, P, P, I32, I32, I32, I32, P, P, P]),
             "asm_build_memory": (I32, [P, I32, I32, I32, P, P, I32, I32, F, P, I32, I32, P, P, P,
                                        P, P, SZ, P]),
+            "kv_latent_absorb_workspace": (SZ, [CP]),
+            "kv_latent_absorb": (I32, [CP, I32, P, SZ, F, P, P, P, SZ, P]),
+            "kv_latent_read": (I32, [P, I32, I32, I32, I32, P, P, P, P, P, F, P, P]),
             "kvb_trace_enable": (I32, [I32, I32]),
             "kvb_trace_read": (I32, [P, P, I32]),
             "kvb_trace_reset": (None, []),
@@ -340,7 +343,8 @@ TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "keep_count": 16, "keep_emit": 32, "compact_move": 64, "asm_lookup": 128,
               "asm_finalize": 256, "attn_fused": 512, "asm_prefix": 1024,
               "asm_prefix_merge": 2048, "km_assign": 4096, "km_update": 8192,
-              "asm_aggregate": 16384, "asm_vt": 32768}
+              "asm_aggregate": 16384, "asm_vt": 32768, "latent_absorb": 65536,
+              "latent_read": 131072}
 
 
 def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:
@@ -528,3 +532,44 @@ def asm_build_memory(q, k, v, centroids, iters: int, chunks: int = 1, scale: flo
                                     _ptr(assign), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "asm_build_memory")
     return centroids_bf16, abar, log_zbar, assign, ws
+
+
+def kv_latent_absorb_workspace(cache: KVCache) -> int:
+    return int(library().kv_latent_absorb_workspace(cache.desc))
+
+
+def kv_latent_absorb(cache: KVCache, M: int, ws_evict, lam: float, mem_M, mem_b, ws=None,
+                     stream=None):
+    """Absorb the tokens the plan in ws_evict evicts into the latent memory (mem_M
+    [B][Hkv][D][D], mem_b [B][Hkv][D], float32, updated in place).  Call between
+    kv_evict_plan and kv_evict_apply."""
+    _need(ws_evict, "ws_evict", torch.uint8)
+    _need(mem_M, "mem_M", torch.float32)
+    _need(mem_b, "mem_b", torch.float32)
+    D = cache.D
+    if tuple(mem_M.shape) != (cache.B, cache.Hkv, D, D) or tuple(mem_b.shape) != (cache.B,
+                                                                                   cache.Hkv, D):
+        raise ValueError("mem_M must be [B][Hkv][D][D], mem_b [B][Hkv][D]")
+    ws = _ws(ws, kv_latent_absorb_workspace(cache), mem_M.device)
+    st = library().kv_latent_absorb(cache.desc, int(M), _ptr(ws_evict), ws_evict.numel(),
+                                    float(lam), _ptr(mem_M), _ptr(mem_b), _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    _check(st, "kv_latent_absorb")
+
+
+def kv_latent_read(q, mem_M, mem_b, W_o, w_g, c_g, eps: float, out, stream=None):
+    """out [B][Hq][D] (float32, holding o_attn) += g(q) m(q) from the latent memory."""
+    _need(q, "q", torch.bfloat16)
+    for name, x in (("mem_M", mem_M), ("mem_b", mem_b), ("W_o", W_o), ("w_g", w_g),
+                    ("c_g", c_g), ("out", out)):
+        _need(x, name, torch.float32)
+    B, Hq, D = q.shape
+    Hkv = mem_M.shape[1]
+    if (tuple(mem_M.shape) != (B, Hkv, D, D) or tuple(mem_b.shape) != (B, Hkv, D)
+            or tuple(W_o.shape) != (D, D) or tuple(w_g.shape) != (Hq, D)
+            or tuple(c_g.shape) != (Hq,) or tuple(out.shape) != (B, Hq, D)):
+        raise ValueError("latent read shapes")
+    st = library().kv_latent_read(_ptr(q), B, Hq, Hkv, D, _ptr(mem_M), _ptr(mem_b), _ptr(W_o),
+                                  _ptr(w_g), _ptr(c_g), float(eps), _ptr(out), _stream(stream))
+    _check(st, "kv_latent_read")
+    return out

@@ -97,6 +97,15 @@ inline int fused_za(int M, int cap) {
 }
 bool plan_in_lds(const kvb_cache* c);
 FusedPlan fused_plan(const kvb_cache* c, int32_t M, void* ws);
+// Host: where an eviction plan (kv_evict_plan with budget M) keeps, per head, its
+// UnitInfo and the kept source slots in ascending order ([U][Mk], first `kept`
+// entries valid when mode == MODE_EVICT).
+struct EvictView {
+  const UnitInfo* info;
+  const int32_t* keep_src;
+  int32_t Mk;
+};
+EvictView evict_view(const kvb_cache* c, int32_t M, const void* ws);
 // Copies the fused apply's staged rows (kept rows below the boundary that move) to
 // the plan's scratch; must run after kv_evict_plan and before any row is written.
 void launch_fused_stage(const kvb_cache* c, int32_t M, void* ws, hipStream_t s);
@@ -113,7 +122,8 @@ enum TraceKernel {
   kTrAttnSplit = 1, kTrAttnMerge = 2, kTrAppend = 4, kTrEvictSelect = 8, kTrKeepCount = 16,
   kTrKeepEmit = 32, kTrCompactMove = 64, kTrAsmLookup = 128, kTrAsmFinalize = 256,
   kTrAttnFused = 512, kTrAsmPrefix = 1024, kTrAsmPrefixMerge = 2048, kTrKmAssign = 4096,
-  kTrKmUpdate = 8192, kTrAsmAggregate = 16384, kTrAsmVt = 32768
+  kTrKmUpdate = 8192, kTrAsmAggregate = 16384, kTrAsmVt = 32768,
+  kTrLatentAbsorb = 65536, kTrLatentRead = 131072
 };
 struct TraceScope {
   TraceScope(int kernel, hipStream_t s);

@@ -1117,6 +1117,16 @@ FusedPlan fused_plan(const kvb_cache* c, int32_t M, void* ws) {
   return f;
 }
 
+EvictView evict_view(const kvb_cache* c, int32_t M, const void* ws) {
+  const CompactLayout L = compact_layout(c, M < c->cap ? M : c->cap);
+  const char* w = (const char*)ws;
+  EvictView e;
+  e.info = (const UnitInfo*)(w + L.info);
+  e.keep_src = (const int32_t*)(w + L.keep_src);
+  e.Mk = L.Mk;
+  return e;
+}
+
 static int32_t evict_validate(const kvb_cache* cache, int32_t M, size_t ws_bytes, const void* ws,
                               CompactLayout& L) {
   int32_t st = check_cache(cache, true);

@@ -22,6 +22,9 @@
  *          background (online-softmax identity), method steps 1-4 (attention state
  *          (a, Z), merge operator, cosine-argmax retrieval, merge with the query's
  *          own state), technical novelty (GQA: centroids per KV head).
+ *  [IDX]   "IndexMem: Learned KV-Cache Eviction with Latent Memory for Long-Context
+ *          LLM Inference", technical summary, section 2 part B (latent memory of
+ *          evicted tokens: decayed outer-product fast weights, gated read-out).
  *  [MEM]   "MEMENTO: Teaching LLMs to Manage Their Own Context", blocks and
  *          compression (a finished thinking block's KV entries are removed once its
  *          memento exists) and system engineering (entries physically removed
@@ -88,6 +91,7 @@ size_t asm_lookup_merge_hier_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32
                                        int32_t m);
 size_t asm_prefix_states_workspace(int32_t H, int32_t N, int32_t D, int32_t L, int32_t chunks);
 size_t asm_kmeans_workspace(int32_t H, int32_t K, int32_t D);
+size_t kv_latent_absorb_workspace(const kvb_cache* cache);
 size_t asm_build_memory_workspace(int32_t H, int32_t N, int32_t D, int32_t L, int32_t chunks,
                                   int32_t K);
 
@@ -357,6 +361,43 @@ int32_t asm_build_memory(const void* q, int32_t H, int32_t N, int32_t D, const v
                          void* stream);
 
 /*
+ * Latent memory of evicted tokens, update ([IDX] section 2, part B: evicted tokens
+ * update a fixed-size state matrix M and a stabiliser vector b online, by an
+ * outer-product accumulation with decay).  Per KV head u, for the slots the plan
+ * in ws_evict evicts (kv_evict_plan with the same cache and M), in slot order,
+ * j = 0..n-1, with phi(x) = elu(x) + 1:
+ *   M[u] <- lam^n M[u] + sum_j lam^(n-1-j) phi(k_j) v_j^T
+ *   b[u] <- lam^n b[u] + sum_j lam^(n-1-j) phi(k_j)
+ * A head the plan leaves alone is not touched.  Call after kv_evict_plan and before
+ * kv_evict_apply (it reads the evicted rows in place).  phi(k) enters the matrix
+ * product as two bf16 parts (float32 accumulation); b is accumulated in float32.
+ *   cache      bf16, D = 64 or 128
+ *   ws_evict   the plan's workspace (ws_evict_bytes >= kv_evict_workspace(cache, M))
+ *   lam        decay per absorbed token, 0 < lam <= 1
+ *   mem_M      [B][Hkv][D][D] float32, in/out;  mem_b [B][Hkv][D] float32, in/out
+ *   ws         kv_latent_absorb_workspace(cache) bytes
+ */
+int32_t kv_latent_absorb(const kvb_cache* cache, int32_t M, const void* ws_evict,
+                         size_t ws_evict_bytes, float lam, float* mem_M, float* mem_b, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * Latent memory read-out added to the attention output ([IDX] section 2, part B:
+ * o = o_attn + g(q) m(q), a projection and a gate reading the memory).  For query
+ * head h of sequence b (KV head u = b * Hkv + h / (Hq / Hkv)), f = phi(q[b][h]):
+ *   r = M[u]^T f / (b[u] . f + eps),  m = W_o r,  g = 1 / (1 + e^-(w_g[h] . q + c_g[h])),
+ *   out[b][h] += g * m   (out holds o_attn on entry).
+ *   q      [B][Hq][D] bf16;  D = 64 or 128
+ *   W_o    [D][D] float32 (row-major, m = W_o r);  w_g [Hq][D], c_g [Hq] float32
+ *   eps    >= 0 (the caller keeps b . f + eps > 0; with an empty memory and eps = 0
+ *          the read is 0/0)
+ *   out    [B][Hq][D] float32, in/out
+ */
+int32_t kv_latent_read(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                       const float* mem_M, const float* mem_b, const float* W_o, const float* w_g,
+                       const float* c_g, float eps, float* out, void* stream);
+
+/*
  * Kernel timing (a measurement aid; off by default; not thread-safe).
  * kvb_trace_enable(capacity, mask) creates `capacity` HIP event pairs; from then
  * on every launch of a kernel selected by `mask` records one pair on the launch
@@ -367,7 +408,8 @@ int32_t asm_build_memory(const void* q, int32_t H, int32_t N, int32_t D, const v
  * 1024 prefix-state chunk kernel, 2048 prefix chunk merge, 4096 K-means
  * assignment, 8192 K-means centroid update (and the initial centroid split),
  * 16384 state aggregation, 32768 the value transpose before the prefix-state
- * chunk kernel.
+ * chunk kernel, 65536 latent-memory update (all its kernels), 131072 latent-memory
+ * read.
  * kvb_trace_read waits for the recorded pairs and writes, for the first `max`,
  * the kernel bit and the elapsed milliseconds (-1 if unavailable); it returns
  * how many it wrote (host arrays).  kvb_trace_reset reuses the pairs from the

@@ -284,6 +284,17 @@ def host_kmeans_init(w: Workload, q: np.ndarray, K: int, seed_offset: int = 43) 
     return np.stack([vals[h][rng.permutation(N)[:K]] for h in range(H)]).astype(np.float32)
 
 
+def host_latent_params(D: int, Hq: int, seed: int, lam: float = 0.9999, eps: float = 1e-6):
+    """Synthetic constants of the latent memory read: projection W_o [D][D]
+    ~ N(0, 1/D), gate weights w_g [Hq][D] ~ N(0, 1/D), gate bias c_g [Hq] ~ N(0, 1),
+    decay lam and eps as given (float32 values)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return {"lam": float(np.float32(lam)), "eps": float(np.float32(eps)),
+            "W_o": (rng.standard_normal((D, D)) / np.sqrt(D)).astype(np.float32),
+            "w_g": (rng.standard_normal((Hq, D)) / np.sqrt(D)).astype(np.float32),
+            "c_g": rng.standard_normal(Hq).astype(np.float32)}
+
+
 def memento_layout(total: int = 1 << 20, seed: int = 1005, memento: int = 200,
                    lo: int = 2048, hi: int = 16384):
     """Block/memento layout of a reasoning trace filling ``total`` slots.

@@ -200,3 +200,46 @@ def test_build_entry_points_reject_arguments_before_launch():
     assert call(f, bm, a17=1024) == -4
     assert (L.asm_build_memory_workspace(2, 100, 128, 300, 4, 16) >=
             L.asm_prefix_states_workspace(2, 100, 128, 300, 4) + L.asm_kmeans_workspace(2, 16, 128))
+
+
+@needs_lib
+def test_latent_entry_points_reject_arguments_before_launch():
+    L = kvb.library()
+    P = ctypes.c_void_p
+    c = _desc()
+    ws = P(4096)
+    wsz = L.kv_latent_absorb_workspace(ctypes.byref(c))
+    assert wsz > 256
+    ev = L.kv_evict_workspace(ctypes.byref(c), 50)
+    # cache, M, ws_evict, ws_evict_bytes, lam, mem_M, mem_b, ws, ws_bytes, stream
+    base = [ctypes.byref(c), 50, P(8), ev, 0.99, P(8), P(8), ws, wsz, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.kv_latent_absorb(*a)
+
+    assert call(a4=0.0) == -1                 # lam outside (0, 1]
+    assert call(a4=1.5) == -1
+    assert call(a5=None) == -1                # mem_M
+    assert call(a2=None) == -1                # plan workspace
+    assert call(a3=ev - 1) == -4              # plan workspace too small
+    assert call(a8=wsz - 1) == -4             # own workspace too small
+    c32 = _desc(dtype=0)
+    assert L.kv_latent_absorb(ctypes.byref(c32), 50, P(8), 1 << 40, 0.99, P(8), P(8), ws,
+                              1 << 40, None) == -2
+    # q, B, Hq, Hkv, D, mem_M, mem_b, W_o, w_g, c_g, eps, out, stream
+    rd = [P(8), 2, 8, 2, 128, P(8), P(8), P(8), P(8), P(8), 1e-6, P(8), None]
+    a = list(rd)
+    a[4] = 96
+    assert L.kv_latent_read(*a) == -2
+    a = list(rd)
+    a[2] = 7
+    assert L.kv_latent_read(*a) == -1
+    a = list(rd)
+    a[10] = -1.0
+    assert L.kv_latent_read(*a) == -1
+    a = list(rd)
+    a[7] = None
+    assert L.kv_latent_read(*a) == -1
