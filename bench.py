@@ -395,10 +395,8 @@ def latent_bench(args):
         us = timed(lambda: kvb.kv_latent_absorb(c, M, ws_e, prm["lam"], mM, mb, ws=ws),
                    10 if name == "evict_32k" else 50)
         ne = int(nev.sum().item())
-        S = (n + 31 + 4095) // 4096
-        state_b = B * H * (D * D + D) * 4
-        chunks = sum(min(S, (int(x) + 4095) // 4096) for x in nev.flatten().tolist())
-        byts = ne * 2 * D * 2 + 2 * state_b + chunks * (D * D + D) * 4 * 2
+        # algorithmic bytes: the evicted rows read once, the state read and written
+        byts = ne * 2 * D * 2 + 2 * B * H * (D * D + D) * 4
         rows[name] = {"evicted_per_head": ne // (B * H), "us": round(us, 1),
                       "bytes": byts, "gbps": round(byts / (us * 1e-6) / 1e9, 1),
                       "tflops": round(2.0 * ne * D * D / (us * 1e-6) / 1e12, 1)}

@@ -232,17 +232,14 @@ __global__ __launch_bounds__(512) void asm_prefix_chunk(PrefixArgs p) {
       u32x4 ph[2], pl[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        uint32_t hb[8], lb[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = e < 4 ? s[2 * ks][qt][e] : s[2 * ks + 1][qt][e - 4];
-          hb[e] = f32_to_bf16_rne(x);
-          lb[e] = f32_to_bf16_rne(x - bf16_bits_to_f32(hb[e]));
-        }
-        ph[qt] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                       hb[6] | (hb[7] << 16)};
-        pl[qt] = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
-                       lb[6] | (lb[7] << 16)};
+        const f32x4 x0 = s[2 * ks][qt], x1 = s[2 * ks + 1][qt];
+        uint32_t hb[4], lb[4];
+        split_bf16x2(x0[0], x0[1], hb[0], lb[0]);
+        split_bf16x2(x0[2], x0[3], hb[1], lb[1]);
+        split_bf16x2(x1[0], x1[1], hb[2], lb[2]);
+        split_bf16x2(x1[2], x1[3], hb[3], lb[3]);
+        ph[qt] = u32x4{hb[0], hb[1], hb[2], hb[3]};
+        pl[qt] = u32x4{lb[0], lb[1], lb[2], lb[3]};
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -336,11 +333,7 @@ __device__ __forceinline__ void km_prep_row(const KmArgs& k, size_t row, const f
   float sq = 0.f;
 #pragma unroll
   for (int j = 0; j < V; j += 2) {
-    const uint32_t h0 = f32_to_bf16_rne(v[j]), h1 = f32_to_bf16_rne(v[j + 1]);
-    const uint32_t l0 = f32_to_bf16_rne(v[j] - bf16_bits_to_f32(h0));
-    const uint32_t l1 = f32_to_bf16_rne(v[j + 1] - bf16_bits_to_f32(h1));
-    hb[j / 2] = h0 | (h1 << 16);
-    lb[j / 2] = l0 | (l1 << 16);
+    split_bf16x2(v[j], v[j + 1], hb[j / 2], lb[j / 2]);
     sq = fmaf(v[j], v[j], sq);
     sq = fmaf(v[j + 1], v[j + 1], sq);
   }

@@ -29,6 +29,21 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
 // 2^x on the transcendental unit (v_exp_f32); inputs here are <= 0 or -inf.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two floats to packed bf16 (a in the low half), round to nearest-even, on the
+// hardware conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// hi = bf16(a), bf16(b) packed; lo = bf16 of the remainders, packed: a = hi + lo to
+// about 16 significant bits.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
 // bf16 bits of x rounded to nearest-even (x finite).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
@@ -55,6 +70,15 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier for LDS traffic only: after it every wave's LDS writes are
+// complete and visible, while global loads a wave has in flight stay in flight
+// (__syncthreads() fences global memory too and so waits for them).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
@@ -104,6 +128,11 @@ struct EvictView {
   const UnitInfo* info;
   const int32_t* keep_src;
   int32_t Mk;
+  // per 32-slot tile of an evicted head: keep bits and kept slots before the tile
+  // (written by the LDS planner only: null when the plan came from the other path)
+  const uint32_t* tile_mask;
+  const int32_t* tile_base;
+  int32_t Tc;
 };
 EvictView evict_view(const kvb_cache* c, int32_t M, const void* ws);
 // Copies the fused apply's staged rows (kept rows below the boundary that move) to

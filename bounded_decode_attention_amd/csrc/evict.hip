@@ -1124,6 +1124,10 @@ EvictView evict_view(const kvb_cache* c, int32_t M, const void* ws) {
   e.info = (const UnitInfo*)(w + L.info);
   e.keep_src = (const int32_t*)(w + L.keep_src);
   e.Mk = L.Mk;
+  const bool lds = plan_in_lds(c);
+  e.tile_mask = lds ? (const uint32_t*)(w + L.tile_mask) : nullptr;
+  e.tile_base = lds ? (const int32_t*)(w + L.tile_base) : nullptr;
+  e.Tc = L.Tc;
   return e;
 }
 

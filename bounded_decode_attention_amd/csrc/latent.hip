@@ -12,16 +12,21 @@
 //
 // Kernels
 //   latent_list            per (head, 256 slots): slot s of a head the plan evicts is
-//                          evicted iff it is not in the plan's ascending kept list
-//                          (binary search); its rank among the evicted slots is s
-//                          minus the kept slots below it.
-//   latent_absorb_part<D>  per (head, 4096 evicted tokens): rows gathered 64 at a
-//                          time (slot indices fetched a tile ahead of the rows);
-//                          phi(k) times its decay weight (relative to the chunk end)
-//                          is split into two bf16 parts and, with v, transposed 4x8
-//                          per thread into LDS as [d][token]; the chunk's
+//                          evicted iff the plan does not keep it; its rank among the
+//                          evicted slots is s minus the kept slots below it (from the
+//                          plan's per-32-slot keep masks and counts, or a binary
+//                          search of its ascending kept list).
+//   latent_absorb_part<D>  per (head, 2048 evicted tokens), 8 waves: rows gathered
+//                          64 at a time (slot indices fetched a tile ahead of the
+//                          rows); phi(k) times its decay weight (relative to the
+//                          chunk end) is split into two bf16 parts and, with v,
+//                          transposed 2x8 per thread into LDS as [d][token]; the chunk's
 //                          Phi^T V (D x D) accumulates on v_mfma_f32_16x16x32_bf16,
 //                          its sum of weighted phi(k) in float32.
+//   latent_absorb_small<D> per (head with at most 32 evicted tokens, 1024 state
+//                          elements): the tokens from the gaps of the kept list, the
+//                          state updated directly (float32); the kernels above and
+//                          below skip such heads.
 //   latent_absorb_combine  per (head, 1024 state elements): lam^n * old plus the
 //                          chunk partials scaled by lam^(tokens after the chunk), in
 //                          chunk order.
@@ -33,8 +38,9 @@
 
 namespace kvb {
 
-constexpr int kLatChunk = 4096;  // evicted tokens per partial
+constexpr int kLatChunk = 2048;  // evicted tokens per partial
 constexpr int kLatTile = 64;     // tokens per LDS tile
+constexpr int kLatSmall = 32;    // heads with at most this many evicted: direct update
 
 struct LatentArgs {
   const uint16_t* k;
@@ -43,6 +49,9 @@ struct LatentArgs {
   const UnitInfo* info;
   const int32_t* keep_src;
   int32_t Mk;
+  const uint32_t* tile_mask;  // [U][Tc] keep bits per 32 slots, or null
+  const int32_t* tile_base;   // [U][Tc] kept slots before each tile
+  int32_t Tc;
   int32_t* ev;       // [U][cap] evicted slots in order
   int32_t* ev_n;     // [U]
   float* part;       // [U][S][D*D + D]
@@ -59,16 +68,26 @@ __global__ __launch_bounds__(256) void latent_list(LatentArgs a) {
   const int n = ev ? min(inf.n, a.cap) : 0;
   const int kept = ev ? min(inf.kept, a.Mk) : 0;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.ev_n[u] = n - kept;
+  if (n - kept <= kLatSmall) return;  // latent_absorb_small takes this head
   const int s = blockIdx.x * 256 + threadIdx.x;
   if (s >= n) return;
-  const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
-  int lo = 0, hi = kept;  // first index with ks[idx] >= s
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (ks[mid] < s) lo = mid + 1;
-    else hi = mid;
+  int lo;  // kept slots below s
+  if (a.tile_mask) {
+    const uint32_t m = a.tile_mask[(size_t)u * a.Tc + (s >> 5)];
+    const uint32_t bit = 1u << (s & 31);
+    if (m & bit) return;
+    lo = a.tile_base[(size_t)u * a.Tc + (s >> 5)] + __popc(m & (bit - 1u));
+  } else {
+    const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
+    int l = 0, h = kept;  // first index with ks[idx] >= s
+    while (l < h) {
+      const int mid = (l + h) >> 1;
+      if (ks[mid] < s) l = mid + 1;
+      else h = mid;
+    }
+    if (l < kept && ks[l] == s) return;
+    lo = l;
   }
-  if (lo < kept && ks[lo] == s) return;
   a.ev[(size_t)u * a.cap + (s - lo)] = s;
 }
 
@@ -78,25 +97,25 @@ __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : 
 __device__ __forceinline__ int lat_slot(int d, int c) { return c ^ ((d >> 1) & 7); }
 
 template <int D>
-__global__ __launch_bounds__(256) void latent_absorb_part(LatentArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void latent_absorb_part(LatentArgs a) {
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int NT = D / 16;           // 16-wide tiles per dimension
-  constexpr int TPW = NT * NT / 4;     // output tiles per wave
+  constexpr int TPW = NT * NT / 8;     // output tiles per wave (8 waves)
   constexpr int RB = kLatTile * 2;     // LDS row bytes (64 tokens, bf16)
   __shared__ __attribute__((aligned(16))) unsigned char ph[D * RB];
   __shared__ __attribute__((aligned(16))) unsigned char pl[D * RB];
   __shared__ __attribute__((aligned(16))) unsigned char vt[D * RB];
-  __shared__ float bred[16][D];
 
   const int u = blockIdx.y, c = blockIdx.x;
   const int ne = a.ev_n[u];
   const int j0 = c * kLatChunk;
-  if (j0 >= ne) return;
+  if (j0 >= ne || ne <= kLatSmall) return;
   const int j1 = min(ne, j0 + kLatChunk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
-  // each thread: 4 consecutive tokens (quad qd) x one 16-byte chunk ch, of k and of v
-  const int qd = tid & 15, ch = tid >> 4;
-  const bool act = ch < CPR;
+  // each thread: tokens 2qd, 2qd + 1 of the tile x one 16-byte chunk ch, of k and of v
+  const int qd = tid & 31, ch = tid >> 5;
+  const bool act = CPR == 16 || ch < CPR;  // (all threads for D = 128)
   const int32_t* evl = a.ev + (size_t)u * a.cap;
   const size_t uoff = (size_t)u * a.cap * D + (act ? ch : 0) * 8;
 
@@ -107,77 +126,71 @@ __global__ __launch_bounds__(256) void latent_absorb_part(LatentArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) bs[e] = 0.f;
 
-  int idx[4];
-  u32x4 kr[4], vr[4];
-  auto load_idx = [&](int t0) {
+  // two tiles of rows in flight: buffer P = (tile index & 1).  Each step first
+  // fetches the slot indices of the tile three ahead, then issues the rows of the
+  // tile two ahead from indices fetched one step earlier; loads are unconditional
+  // (past the chunk end they repeat its last token, whose weight is zero) and a
+  // loaded index is not touched until the next step, so no wait drains the rows
+  // in flight.
+  int rawi[2][2];
+  u32x4 kr[2][2], vr[2][2];
+  auto load_idx = [&](int P, int t0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int jj = t0 + 4 * qd + r;
+    for (int r = 0; r < 2; ++r) rawi[P][r] = evl[min(t0 + 2 * qd + r, j1 - 1)];
+  };
+  auto load_rows = [&](int P) {
+    if (!act) return;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
       // (the clamp only guards the read; every listed slot is below cap)
-      idx[r] = (act && jj < j1) ? min(evl[jj], a.cap - 1) : -1;
+      const size_t off = uoff + (size_t)min(rawi[P][r], a.cap - 1) * D;
+      kr[P][r] = *(const u32x4*)(a.k + off);
+      vr[P][r] = *(const u32x4*)(a.v + off);
     }
   };
-  auto load_rows = [&]() {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const size_t off = uoff + (size_t)(idx[r] < 0 ? 0 : idx[r]) * D;
-      kr[r] = idx[r] >= 0 ? *(const u32x4*)(a.k + off) : u32x4{0, 0, 0, 0};
-      vr[r] = idx[r] >= 0 ? *(const u32x4*)(a.v + off) : u32x4{0, 0, 0, 0};
-    }
-  };
-
-  load_idx(j0);
-  load_rows();
-  if (j0 + kLatTile < j1) load_idx(j0 + kLatTile);
-  for (int t0 = j0; t0 < j1; t0 += kLatTile) {
-    __syncthreads();  // the previous tile's operands are consumed
+  auto step = [&](const int P, int t0) {
+    barrier_lds();  // the previous tile's operands are consumed (rows stay in flight)
     if (act) {
-      float f[4][8];
+      float wt[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jj = t0 + 4 * qd + r;
-        const bool ok = jj < j1;
-        const float wt = ok ? exp2_fast((float)(j1 - 1 - jj) * a.log2_lam) : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (kr[r][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          f[r][e] = ok ? wt * phi_elu1(bf16_bits_to_f32(bits)) : 0.f;
-          bs[e] += f[r][e];
-        }
+      for (int r = 0; r < 2; ++r) {
+        const int jj = t0 + 2 * qd + r;
+        wt[r] = jj < j1 ? exp2_fast((float)(j1 - 1 - jj) * a.log2_lam) : 0.f;
       }
+      // one dimension at a time: the 2 tokens' weighted phi(k), split, and v (a
+      // token past the chunk end has weight 0, so its phi(k) column is 0)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = ch * 8 + e;
-        const int off = d * RB + 16 * lat_slot(d, qd >> 1) + 8 * (qd & 1);
-        uint32_t wh[2], wl[2], wv[2];
+        float f[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint32_t h0 = f32_to_bf16_rne(f[2 * q][e]), h1 = f32_to_bf16_rne(f[2 * q + 1][e]);
-          const uint32_t l0 = f32_to_bf16_rne(f[2 * q][e] - bf16_bits_to_f32(h0));
-          const uint32_t l1 = f32_to_bf16_rne(f[2 * q + 1][e] - bf16_bits_to_f32(h1));
-          wh[q] = h0 | (h1 << 16);
-          wl[q] = l0 | (l1 << 16);
-          const uint32_t x0 = vr[2 * q][e >> 1], x1 = vr[2 * q + 1][e >> 1];
-          wv[q] = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
+        for (int r = 0; r < 2; ++r) {
+          const uint32_t bits = (kr[P][r][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          f[r] = wt[r] * phi_elu1(bf16_bits_to_f32(bits));
+          bs[e] += f[r];
         }
-        *(uint2*)(ph + off) = uint2{wh[0], wh[1]};
-        *(uint2*)(pl + off) = uint2{wl[0], wl[1]};
-        *(uint2*)(vt + off) = uint2{wv[0], wv[1]};
+        const int d = ch * 8 + e;
+        const int off = d * RB + 16 * lat_slot(d, qd >> 2) + 4 * (qd & 3);
+        uint32_t wh, wl;
+        split_bf16x2(f[0], f[1], wh, wl);
+        const uint32_t x0 = vr[P][0][e >> 1], x1 = vr[P][1][e >> 1];
+        const uint32_t wv = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
+        *(uint32_t*)(ph + off) = wh;
+        *(uint32_t*)(pl + off) = wl;
+        *(uint32_t*)(vt + off) = wv;
       }
     }
-    __syncthreads();
-    if (t0 + kLatTile < j1) {
-      load_rows();                                         // tile t+1 (indices ready)
-      if (t0 + 2 * kLatTile < j1) load_idx(t0 + 2 * kLatTile);  // indices of tile t+2
-    }
-    // Phi^T V: output tile (d1 tile, d2 tile), contraction over this tile's tokens
+    barrier_lds();
+    load_idx(P ^ 1, t0 + 3 * kLatTile);    // indices of tile t0 + 3T
+    load_rows(P);                          // tile t0 + 2T (indices fetched last step)
+    // Phi^T V over this tile's tokens: wave output tile tt = wave * TPW + i is
+    // (d1 tile tt / NT, d2 tile tt % NT)
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tt = wave * TPW + i, dt1 = tt / NT, dt2 = tt % NT;
-      const int d1 = dt1 * 16 + lc, d2 = dt2 * 16 + lc;
+    for (int ks = 0; ks < 2; ++ks) {
+      const int cc = 4 * ks + lg;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int cc = 4 * ks + lg;
+      for (int i = 0; i < TPW; ++i) {
+        const int tt = wave * TPW + i;
+        const int d1 = (tt / NT) * 16 + lc, d2 = (tt % NT) * 16 + lc;
         const u32x4 ah = *(const u32x4*)(ph + d1 * RB + 16 * lat_slot(d1, cc));
         const u32x4 al = *(const u32x4*)(pl + d1 * RB + 16 * lat_slot(d1, cc));
         const u32x4 bv = *(const u32x4*)(vt + d2 * RB + 16 * lat_slot(d2, cc));
@@ -185,6 +198,16 @@ __global__ __launch_bounds__(256) void latent_absorb_part(LatentArgs a) {
         acc[i] = mfma_16x16x32_bf16(al, bv, acc[i]);
       }
     }
+  };
+
+  load_idx(0, j0);
+  load_rows(0);
+  load_idx(1, j0 + kLatTile);
+  load_rows(1);
+  load_idx(0, j0 + 2 * kLatTile);
+  for (int t0 = j0; t0 < j1; t0 += 2 * kLatTile) {
+    step(0, t0);
+    if (t0 + kLatTile < j1) step(1, t0 + kLatTile);
   }
 
   float* out = a.part + ((size_t)u * a.S + c) * (D * D + D);
@@ -194,7 +217,10 @@ __global__ __launch_bounds__(256) void latent_absorb_part(LatentArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) out[(size_t)(dt1 * 16 + 4 * lg + r) * D + dt2 * 16 + lc] = acc[i][r];
   }
-  // weighted phi(k) sums: the 16 quad threads of each chunk, in quad order
+  // weighted phi(k) sums: the 32 pair threads of each chunk, in pair order (the
+  // reduction reuses the first operand buffer once every wave is past its reads)
+  float(*bred)[D] = (float(*)[D])ph;
+  __syncthreads();
   if (act) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) bred[qd][ch * 8 + e] = bs[e];
@@ -203,8 +229,67 @@ __global__ __launch_bounds__(256) void latent_absorb_part(LatentArgs a) {
   if (tid < D) {
     float s2 = 0.f;
 #pragma unroll
-    for (int o = 0; o < 16; ++o) s2 += bred[o][tid];
+    for (int o = 0; o < 32; ++o) s2 += bred[o][tid];
     out[D * D + tid] = s2;
+  }
+}
+
+// Heads with 1..kLatSmall evicted tokens, one workgroup each: the evicted slots are
+// the gaps of the ascending kept list (the slots between kept entry i-1 and entry
+// i have rank s - i among the evicted); their weighted phi(k) and v are staged in
+// LDS (float32) and every state element is updated in place, summing the tokens
+// in order.
+template <int D>
+__global__ __launch_bounds__(256) void latent_absorb_small(LatentArgs a) {
+  __shared__ int evs[kLatSmall];
+  __shared__ float fk[kLatSmall][D];
+  __shared__ float fv[kLatSmall][D];
+  const int u = blockIdx.y;
+  const UnitInfo inf = a.info[u];
+  if (inf.mode != MODE_EVICT) return;
+  const int n = min(inf.n, a.cap), kept = min(inf.kept, a.Mk);
+  const int ne = n - kept;
+  if (ne <= 0 || ne > kLatSmall) return;
+  const int tid = threadIdx.x;
+  const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
+  for (int i = tid; i <= kept; i += 256) {
+    const int prev = i > 0 ? ks[i - 1] : -1;
+    const int next = i < kept ? ks[i] : n;
+    for (int s = prev + 1; s < next; ++s)
+      if (s - i < kLatSmall) evs[s - i] = s;
+  }
+  __syncthreads();
+  for (int e = tid; e < ne * D; e += 256) {
+    const int j = e / D, d = e - j * D;
+    const size_t row = ((size_t)u * a.cap + evs[j]) * D + d;
+    const float wt = exp2_fast((float)(ne - 1 - j) * a.log2_lam);
+    fk[j][d] = wt * phi_elu1(bf16_bits_to_f32(a.k[row]));
+    fv[j][d] = bf16_bits_to_f32(a.v[row]);
+  }
+  __syncthreads();
+  // this block's 1024 elements of (M, b), four per thread, loads first
+  const float decay_all = exp2_fast((float)ne * a.log2_lam);
+  const int E = D * D + D;
+  float old[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = blockIdx.x * 1024 + r * 256 + tid;
+    old[r] = e < D * D ? a.mem_M[(size_t)u * D * D + e]
+                       : (e < E ? a.mem_b[(size_t)u * D + (e - D * D)] : 0.f);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = blockIdx.x * 1024 + r * 256 + tid;
+    if (e >= E) continue;
+    float acc = decay_all * old[r];
+    if (e < D * D) {
+      const int d1 = e / D, d2 = e - d1 * D;
+      for (int j = 0; j < ne; ++j) acc = fmaf(fk[j][d1], fv[j][d2], acc);
+      a.mem_M[(size_t)u * D * D + e] = acc;
+    } else {
+      for (int j = 0; j < ne; ++j) acc += fk[j][e - D * D];
+      a.mem_b[(size_t)u * D + (e - D * D)] = acc;
+    }
   }
 }
 
@@ -212,7 +297,7 @@ __global__ __launch_bounds__(256) void latent_absorb_part(LatentArgs a) {
 __global__ __launch_bounds__(256) void latent_absorb_combine(LatentArgs a, int D) {
   const int u = blockIdx.y;
   const int ne = a.ev_n[u];
-  if (ne <= 0) return;
+  if (ne <= kLatSmall) return;
   const int E = D * D + D;
   const int S = (ne + kLatChunk - 1) / kLatChunk;
   const float decay_all = exp2_fast((float)ne * a.log2_lam);
@@ -221,9 +306,16 @@ __global__ __launch_bounds__(256) void latent_absorb_combine(LatentArgs a, int D
        e += 256) {
     float* dst = e < D * D ? a.mem_M + (size_t)u * D * D + e : a.mem_b + (size_t)u * D + (e - D * D);
     float acc = decay_all * *dst;
-    for (int c = 0; c < S; ++c) {
-      const int j1 = min(ne, (c + 1) * kLatChunk);
-      acc += exp2_fast((float)(ne - j1) * a.log2_lam) * pu[(size_t)c * E + e];
+    for (int c0 = 0; c0 < S; c0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = c0 + q < S ? pu[(size_t)(c0 + q) * E + e] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (c0 + q >= S) break;
+        const int j1 = min(ne, (c0 + q + 1) * kLatChunk);
+        acc += exp2_fast((float)(ne - j1) * a.log2_lam) * x[q];
+      }
     }
     *dst = acc;
   }
@@ -342,6 +434,9 @@ extern "C" int32_t kv_latent_absorb(const kvb_cache* cache, int32_t M, const voi
   a.info = e.info;
   a.keep_src = e.keep_src;
   a.Mk = e.Mk;
+  a.tile_mask = e.tile_mask;
+  a.tile_base = e.tile_base;
+  a.Tc = e.Tc;
   char* w = (char*)ws;
   a.ev = (int32_t*)(w + o_ev);
   a.ev_n = (int32_t*)(w + o_n);
@@ -355,9 +450,15 @@ extern "C" int32_t kv_latent_absorb(const kvb_cache* cache, int32_t M, const voi
   TraceScope tr(kTrLatentAbsorb, s);
   hipLaunchKernelGGL(latent_list, dim3((cache->cap + 255) / 256, U), dim3(256), 0, s, a);
   if (cache->D == 128)
-    hipLaunchKernelGGL(latent_absorb_part<128>, dim3(S, U), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(latent_absorb_small<128>, dim3((128 * 128 + 128 + 1023) / 1024, U),
+                       dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(latent_absorb_part<64>, dim3(S, U), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(latent_absorb_small<64>, dim3((64 * 64 + 64 + 1023) / 1024, U), dim3(256),
+                       0, s, a);
+  if (cache->D == 128)
+    hipLaunchKernelGGL(latent_absorb_part<128>, dim3(S, U), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(latent_absorb_part<64>, dim3(S, U), dim3(512), 0, s, a);
   const int E = cache->D * cache->D + cache->D;
   hipLaunchKernelGGL(latent_absorb_combine, dim3((E + 1023) / 1024, U), dim3(256), 0, s, a,
                      cache->D);

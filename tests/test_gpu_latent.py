@@ -89,6 +89,22 @@ def test_absorb_vs_oracle(D, n, M, lam):
     _check_state(gM, gb, RM, Rb, M0, b0, nev, f"D{D} n{n} M{M}")
 
 
+def test_absorb_large_cache_plan():
+    """A cache too large for the planner's LDS path (45,000 slots): the evicted
+    slots come from the plan's kept list instead of its per-tile masks."""
+    say("latent absorb, large cache")
+    B, H, D, n, M = 1, 2, 128, 45000, 4000
+    lam = float(np.float32(0.99995))
+    d = _cache(91, B, H, n, n + 7, D, lens=[[n, n - 3000]])
+    t = np.array([n], np.int32)
+    rng = np.random.default_rng(9)
+    M0 = rng.standard_normal((B, H, D, D)).astype(np.float32)
+    b0 = np.abs(rng.standard_normal((B, H, D))).astype(np.float32)
+    RM, Rb, nev = _ref_absorb(d, t, M, lam, M0, b0)
+    _, gM, gb = _gpu_absorb(d, t, M, lam, M0, b0)
+    _check_state(gM, gb, RM, Rb, M0, b0, nev, "large cache")
+
+
 def test_absorb_steps_then_read():
     """Several decode steps (append, evict 1..2, absorb), then the read-out added to
     the attention output; checked against the oracle at every step."""
