@@ -24,9 +24,9 @@
 //                          Phi^T V (D x D) accumulates on v_mfma_f32_16x16x32_bf16,
 //                          its sum of weighted phi(k) in float32.
 //   latent_absorb_small<D> per (head with at most 32 evicted tokens, 1024 state
-//                          elements): the tokens from the gaps of the kept list, the
-//                          state updated directly (float32); the kernels above and
-//                          below skip such heads.
+//                          elements): the listed tokens' weighted phi(k) and v staged
+//                          in LDS, the state updated directly (float32); the chunk
+//                          kernels skip such heads.
 //   latent_absorb_combine  per (head, 1024 state elements): lam^n * old plus the
 //                          chunk partials scaled by lam^(tokens after the chunk), in
 //                          chunk order.
@@ -68,7 +68,6 @@ __global__ __launch_bounds__(256) void latent_list(LatentArgs a) {
   const int n = ev ? min(inf.n, a.cap) : 0;
   const int kept = ev ? min(inf.kept, a.Mk) : 0;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.ev_n[u] = n - kept;
-  if (n - kept <= kLatSmall) return;  // latent_absorb_small takes this head
   const int s = blockIdx.x * 256 + threadIdx.x;
   if (s >= n) return;
   int lo;  // kept slots below s
@@ -234,11 +233,9 @@ void latent_absorb_part(LatentArgs a) {
   }
 }
 
-// Heads with 1..kLatSmall evicted tokens, one workgroup each: the evicted slots are
-// the gaps of the ascending kept list (the slots between kept entry i-1 and entry
-// i have rank s - i among the evicted); their weighted phi(k) and v are staged in
-// LDS (float32) and every state element is updated in place, summing the tokens
-// in order.
+// Heads with 1..kLatSmall evicted tokens: the listed evicted slots' weighted phi(k)
+// and v are staged in LDS (float32) and this block's state elements are updated in
+// place, summing the tokens in order.
 template <int D>
 __global__ __launch_bounds__(256) void latent_absorb_small(LatentArgs a) {
   __shared__ int evs[kLatSmall];
@@ -251,13 +248,7 @@ __global__ __launch_bounds__(256) void latent_absorb_small(LatentArgs a) {
   const int ne = n - kept;
   if (ne <= 0 || ne > kLatSmall) return;
   const int tid = threadIdx.x;
-  const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
-  for (int i = tid; i <= kept; i += 256) {
-    const int prev = i > 0 ? ks[i - 1] : -1;
-    const int next = i < kept ? ks[i] : n;
-    for (int s = prev + 1; s < next; ++s)
-      if (s - i < kLatSmall) evs[s - i] = s;
-  }
+  if (tid < ne) evs[tid] = min(a.ev[(size_t)u * a.cap + tid], a.cap - 1);
   __syncthreads();
   for (int e = tid; e < ne * D; e += 256) {
     const int j = e / D, d = e - j * D;
