@@ -435,12 +435,14 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="run each layer's eviction planning on the attention stream (no overlap)")
     ap.add_argument("--schedule", default=None,
-                    choices=["plan_beside", "both_beside", "deferred"],
-                    help="deferred (default of the 32K step): each layer's eviction plan runs "
-                         "beside its attention and all layers' compactions follow the last "
-                         "attention; plan_beside: each compaction right after its layer's "
-                         "attention; both_beside (default of --steady): each compaction beside "
-                         "the next layer's attention")
+                    choices=["plan_beside", "both_beside", "deferred", "deferred_plan"],
+                    help="deferred_plan (default of the 32K step): all layers' eviction "
+                         "plans and compactions follow the last attention, each plan running "
+                         "beside the previous layer's compaction; deferred: each plan beside "
+                         "its layer's attention, the compactions after the last attention; "
+                         "plan_beside: each compaction right after its layer's attention; "
+                         "both_beside (default of --steady): each compaction beside the next "
+                         "layer's attention")
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
@@ -518,9 +520,9 @@ def main():
     first_ev = [torch.empty((B, w.hkv, 1), dtype=torch.int32, device=dev) for _ in range(L)]
     ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, args.splits), dtype=torch.uint8,
                        device=dev)
-    sched = "serial" if args.serial else (args.schedule or "deferred")
+    sched = "serial" if args.serial else (args.schedule or "deferred_plan")
     # one eviction workspace per layer when the plans outlive the next layer's planning
-    n_ws = L if sched == "deferred" else 1
+    n_ws = L if sched in ("deferred", "deferred_plan") else 1
     ws_es = [torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device=dev)
              for _ in range(n_ws)]
     splits = args.splits or kvb.kv_attn_decode_splits(kvs[0], w.hq)
@@ -555,11 +557,12 @@ def main():
             q, kn, vn, lb = qs[layer]
             ws_e = ws_es[layer % n_ws]
             kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
-            if side is not main:
-                appended[layer].record(main)
-                side.wait_event(appended[layer])
-            kvb.kv_evict_plan(kvs[layer], t, M, evicted_pos=first_ev[layer],
-                              n_evicted=nev[layer], ws=ws_e, stream=side)
+            if sched != "deferred_plan":
+                if side is not main:
+                    appended[layer].record(main)
+                    side.wait_event(appended[layer])
+                kvb.kv_evict_plan(kvs[layer], t, M, evicted_pos=first_ev[layer],
+                                  n_evicted=nev[layer], ws=ws_e, stream=side)
             if fused:
                 kvb.kv_attn_decode_compact(kvs[layer], q, t, M, ws_e, num_splits=args.splits,
                                            phase=1, out=outs[layer], lse=lses[layer], ws=ws_a,
@@ -582,9 +585,16 @@ def main():
                     planned[layer].record(side)
                     main.wait_event(planned[layer])
                 kvb.kv_evict_apply(kvs[layer], M, ws_e, stream=main)
-            else:
+            elif sched == "deferred":
                 planned[layer].record(side)
-        if sched == "deferred":
+        if sched == "deferred_plan":
+            attended[0].record(main)
+            side.wait_event(attended[0])
+            for layer in range(L):
+                kvb.kv_evict_plan(kvs[layer], t, M, evicted_pos=first_ev[layer],
+                                  n_evicted=nev[layer], ws=ws_es[layer], stream=side)
+                planned[layer].record(side)
+        if sched in ("deferred", "deferred_plan"):
             for layer in range(L):
                 main.wait_event(planned[layer])
                 kvb.kv_evict_apply(kvs[layer], M, ws_es[layer], stream=main)
