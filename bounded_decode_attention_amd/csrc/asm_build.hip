@@ -22,7 +22,9 @@
 //   km_prep<D>           fp32 centroids -> bf16 hi, bf16 lo = c - hi, |c|^2.
 //   km_assign<D>         per (KV head, 256 points): |c|^2 - 2 x.c for every
 //                        centroid on MFMA (x is exact in bf16; c = hi + lo keeps
-//                        16 significant bits), argmin with the lowest index on ties.
+//                        16 significant bits), argmin with the lowest index on ties;
+//                        centroid tiles go HBM -> LDS by global_load_lds into
+//                        XOR-swizzled rows, double-buffered.
 //   km_reduce<D, MERGE>  per (KV head, 64 clusters): scans the assignment in index
 //                        order and accumulates each cluster's members in a fixed
 //                        order (no float atomics, so results repeat bit for bit);
@@ -370,11 +372,11 @@ __global__ __launch_bounds__(256) void km_prep(KmArgs k) {
 template <int D>
 __global__ __launch_bounds__(256) void km_assign(KmArgs k) {
   constexpr int DS = D / 32;
-  constexpr int CP = D + 8;  // padded centroid row in LDS (bf16)
-  constexpr int CPR = D / 8;
-  constexpr int LPT = kKmCT * CPR / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Ch[2][kKmCT * CP];
-  __shared__ __attribute__((aligned(16))) uint16_t Cl[2][kKmCT * CP];
+  constexpr int RB = D * 2;           // centroid row bytes
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int TB = kKmCT * RB;      // bytes of one tile of one part
+  constexpr int NI = TB / 1024;       // 1 KB DMA instructions per part and tile
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2 * TB];
   __shared__ __attribute__((aligned(16))) float Cn[2][kKmCT];
 
   const int H = k.H, K = k.K;
@@ -402,46 +404,47 @@ __global__ __launch_bounds__(256) void km_assign(KmArgs k) {
     bi[pt] = 0x7FFFFFFF;
   }
 
-  u32x4 hr[LPT], lr[LPT];
-  float cr = 0.f;
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ci = tid + 256 * j, row = ci / CPR, col = ci % CPR;
-      const int kk = t * kKmCT + row;
-      const bool ok = kk < K;
-      hr[j] = ok ? *(const u32x4*)(hh + (size_t)kk * D + col * 8) : u32x4{0, 0, 0, 0};
-      lr[j] = ok ? *(const u32x4*)(lh + (size_t)kk * D + col * 8) : u32x4{0, 0, 0, 0};
+  // Tile t's hi and lo rows HBM -> LDS (rows past K repeat row K-1: their norm is
+  // replaced by +inf below), and their norms; XOR-swizzled 16-byte slots.
+  auto issue = [&](int t, int buf) {
+    for (int i = wave; i < NI; i += 4) {
+      const int r = i * (1024 / RB) + lane / CPR, slot = lane % CPR;
+      const int c = (CPR == 16) ? (slot ^ (r & 15)) : (slot ^ ((r >> 1) & 7));
+      const size_t src = (size_t)min(t * kKmCT + r, K - 1) * D + c * 8;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(hh + src), (lds_void_t*)(lds[buf] + i * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(lh + src),
+                                       (lds_void_t*)(lds[buf] + TB + i * 1024), 16, 0, 0);
     }
-    if (tid < kKmCT) {
-      const int kk = t * kKmCT + tid;
-      cr = kk < K ? nh[kk] : __builtin_huge_valf();
-    }
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(nh + min(t * kKmCT + lane, K - 1)),
+                                       (lds_void_t*)Cn[buf], 4, 0, 0);
   };
 
-  load_tile(0);
+  issue(0, 0);
   for (int t = 0; t < nt; ++t) {
     const int buf = t & 1;
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ci = tid + 256 * j, row = ci / CPR, col = ci % CPR;
-      *(u32x4*)&Ch[buf][row * CP + col * 8] = hr[j];
-      *(u32x4*)&Cl[buf][row * CP + col * 8] = lr[j];
-    }
-    if (tid < kKmCT) Cn[buf][tid] = cr;
+    // this wave's transfers for tile t have landed (LDS written by global_load_lds
+    // is not tracked by the compiler); the barrier makes every wave's visible and
+    // frees the other buffer
+    wait_vmem_all();
     __syncthreads();
-    if (t + 1 < nt) load_tile(t + 1);
+    if (t + 1 < nt) issue(t + 1, buf ^ 1);
+    const unsigned char* ch = lds[buf];
+    const unsigned char* cl = lds[buf] + TB;
 
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       f32x4 s[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) s[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = ct * 16 + lc;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const int off = (ct * 16 + lc) * CP + ds * 32 + 8 * lg;
-        const u32x4 ah = *(const u32x4*)&Ch[buf][off];
-        const u32x4 al = *(const u32x4*)&Cl[buf][off];
+        const int cc = ds * 4 + lg;
+        const int slot = (CPR == 16) ? (cc ^ (row & 15)) : (cc ^ ((row >> 1) & 7));
+        const u32x4 ah = *(const u32x4*)(ch + row * RB + 16 * slot);
+        const u32x4 al = *(const u32x4*)(cl + row * RB + 16 * slot);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) s[pt] = mfma_16x16x32_bf16(ah, xr[pt][ds], s[pt]);
 #pragma unroll
@@ -451,9 +454,10 @@ __global__ __launch_bounds__(256) void km_assign(KmArgs k) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kk = t * kKmCT + ct * 16 + 4 * lg + i;
+        const float cni = kk < K ? cn[i] : __builtin_huge_valf();
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const float d = fmaf(-2.f, s[pt][i], cn[i]);
+          const float d = fmaf(-2.f, s[pt][i], cni);
           if (d < best[pt]) {
             best[pt] = d;
             bi[pt] = kk;
