@@ -556,7 +556,8 @@ def main():
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
             ws_e = ws_es[layer % n_ws]
-            kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
+            if sched != "deferred_plan":  # deferred_plan: the attention call appends
+                kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
             if sched != "deferred_plan":
                 if side is not main:
                     appended[layer].record(main)
@@ -574,8 +575,13 @@ def main():
                                            phase=2, out=outs[layer], lse=lses[layer], ws=ws_a,
                                            stream=main)
                 continue
-            kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=outs[layer],
-                               lse=lses[layer], ws=ws_a, stream=main)
+            if sched == "deferred_plan":
+                kvb.kv_attn_decode(kvs[layer], q, t, k_new=kn, v_new=vn, log_beta_new=lb,
+                                   num_splits=args.splits, out=outs[layer], lse=lses[layer],
+                                   ws=ws_a, stream=main)
+            else:
+                kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=outs[layer],
+                                   lse=lses[layer], ws=ws_a, stream=main)
             if sched == "both_beside":
                 attended[layer].record(main)
                 side.wait_event(attended[layer])

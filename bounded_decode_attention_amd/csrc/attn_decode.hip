@@ -54,6 +54,9 @@ struct AttnArgs {
   void* vw;
   float* lbw;
   int32_t* posw;
+  // when non-null, the first split of each head records the head's len here (the
+  // merge then appends the decode token and needs the length before it)
+  int32_t* n_rec;
 };
 
 // ------------------------------------------------------------------ append
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
   const int lc = lane & 15;
 
   const int n = min(a.len[u], a.cap);
+  if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
   int lo, end;
   split_range(n, p, a.P, lo, end);
   // 16-byte loads of log beta / pos need a 4-slot aligned head base
@@ -518,6 +522,7 @@ void attn_split_pipe128(AttnArgs a) {
   const int lg = lane >> 4;
   const int lc = lane & 15;
   const int n = min(a.len[u], a.cap);
+  if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
   const int end = n;
 
   const int hcol = lc < G ? lc : (lc < 2 * G ? lc - G : -1);
@@ -673,6 +678,7 @@ __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
   const int lane = threadIdx.x;
   const int D = a.D, G = a.G;
   const int n = min(a.len[u], a.cap);
+  if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
   int lo, end;
   split_range(n, p, a.P, lo, end);
 
@@ -764,12 +770,36 @@ __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
 // so the result does not depend on timing.
 constexpr int kMergeMaxP = 4096;
 
+// The decode token, merged as a one-token state and appended to the cache by the
+// merge (kv_attn_decode with k_new): its logit is scale * q.k_new (no bias: its
+// distance is 0), its value v_new.
+struct NewTok {
+  const void* k_new;   // [U][D] cache dtype, or null (no decode token)
+  const void* v_new;
+  const float* lb_new; // [U] or null
+  const int32_t* t;    // [B]
+  const void* q;       // [B][Hq][D] cache dtype
+  const int32_t* n_rec;  // [U] len before the append (recorded by the split kernel)
+  void* k;
+  void* v;
+  float* log_beta;
+  int32_t* pos;
+  int32_t* len;
+  int32_t* status;
+  int32_t cap, Hkv, elem;
+  float scale;         // natural-log scale of q.k
+};
+
+__device__ __forceinline__ float load_elem(const void* p, size_t i, int elem) {
+  return elem == 2 ? bf16_bits_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
 template <int kMergeThreads>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
                                                             const float* part_ml, int P, int D,
                                                             float* out, float* lse,
                                                             const UnitInfo* info, int32_t* len,
-                                                            int G) {
+                                                            int G, NewTok nt) {
   __shared__ float w[kMergeMaxP];
   __shared__ float red[kMergeThreads];
   __shared__ float gsum[kMergeThreads];
@@ -786,6 +816,25 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
   float x[kB];
 #pragma unroll
   for (int e = 0; e < kB; ++e) x[e] = p0 + e < p1 ? pa[(size_t)(p0 + e) * D + d] : 0.f;
+  // the decode token's logit (when it is appended here)
+  const int u = bh / G;
+  bool incl = false;
+  float s_new = kNegInf;
+  if (nt.k_new) {
+    incl = nt.n_rec[u] < nt.cap;
+    float pr = 0.f;
+    if (incl && tid < D)
+      pr = load_elem(nt.q, (size_t)bh * D + tid, nt.elem) *
+           load_elem(nt.k_new, (size_t)u * D + tid, nt.elem);
+    red[tid] = pr;
+    __syncthreads();
+    for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    if (incl) s_new = red[0] * nt.scale;
+    __syncthreads();
+  }
   float mx = kNegInf;
   for (int p = tid; p < P; p += kMergeThreads)
     if (ml[2 * p + 1] > 0.f) mx = fmaxf(mx, ml[2 * p]);
@@ -795,7 +844,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
     __syncthreads();
   }
-  const float M = red[0];
+  const float M = fmaxf(red[0], s_new);
   __syncthreads();
   float ws = 0.f;
   for (int p = tid; p < P; p += kMergeThreads) {
@@ -810,7 +859,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     if (tid < o) red[tid] += red[tid + o];
     __syncthreads();
   }
-  const float W = red[0];
+  const float w_new = incl ? __expf(s_new - M) : 0.f;
+  const float W = red[0] + w_new;
   float o = 0.f;
 #pragma unroll
   for (int e = 0; e < kB; ++e)
@@ -827,12 +877,32 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
   if (tid < D) {
     float acc = 0.f;
     for (int g = 0; g < NG; ++g) acc += gsum[g * D + tid];
+    if (incl) acc = fmaf(w_new, load_elem(nt.v_new, (size_t)u * D + tid, nt.elem), acc);
     out[(size_t)bh * D + tid] = W > 0.f ? acc / W : 0.f;
   }
   if (tid == 0) lse[bh] = W > 0.f ? M + __logf(W) : kNegInf;
+  // append the decode token (first query head of each KV head); every split has
+  // read the old len, and the other merge blocks use the recorded one
+  if (nt.k_new && bh % G == 0) {
+    if (!incl) {
+      if (tid == 0) nt.status[0] = KVB_ECAPACITY;
+    } else {
+      const int s0 = nt.n_rec[u];
+      const int words = D * nt.elem / 4;
+      const size_t dst = ((size_t)u * nt.cap + s0) * words;
+      for (int w = tid; w < words; w += kMergeThreads) {
+        ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
+        ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
+      }
+      if (tid == 0) {
+        nt.pos[(size_t)u * nt.cap + s0] = nt.t[u / nt.Hkv];
+        if (nt.log_beta) nt.log_beta[(size_t)u * nt.cap + s0] = nt.lb_new[u];
+        nt.len[u] = s0 + 1;
+      }
+    }
+  }
   // fused compaction: the head's new length (every split has read the old one)
   if (info && tid == 0 && bh % G == 0) {
-    const int u = bh / G;
     if (info[u].mode == MODE_EVICT) len[u] = info[u].kept;
   }
 }
@@ -840,13 +910,16 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
 // ------------------------------------------------------------------ host
 static void launch_merge(const float* part_a, const float* part_ml, int P, int D, float* out,
                          float* lse, const UnitInfo* info, int32_t* len, int G, int BH,
-                         hipStream_t s) {
+                         hipStream_t s, const NewTok* nt = nullptr) {
+  NewTok none;
+  memset(&none, 0, sizeof(none));
+  const NewTok& n = nt ? *nt : none;
   if (P > 128)
     hipLaunchKernelGGL(attn_merge<512>, dim3(BH), dim3(512), 0, s, part_a, part_ml, P, D, out,
-                       lse, info, len, G);
+                       lse, info, len, G, n);
   else
     hipLaunchKernelGGL(attn_merge<256>, dim3(BH), dim3(256), 0, s, part_a, part_ml, P, D, out,
-                       lse, info, len, G);
+                       lse, info, len, G, n);
 }
 
 static bool mfma_supported(const kvb_cache* c, int G) {
@@ -920,7 +993,8 @@ extern "C" size_t kv_attn_decode_workspace(const kvb_cache* cache, int32_t Hq, i
   if (!cache || Hq < 1 || cache->B < 1 || cache->D < 1) return 0;
   const size_t P = num_splits > 0 ? (size_t)num_splits : (size_t)auto_splits(cache);
   const size_t S = (size_t)cache->B * Hq * P;
-  return kWsHeader + align_up(S * cache->D * sizeof(float), 256) + align_up(S * 2 * sizeof(float), 256);
+  return kWsHeader + align_up(S * cache->D * sizeof(float), 256) +
+         align_up(S * 2 * sizeof(float), 256) + align_up((size_t)cache->B * cache->Hkv * 4, 256);
 }
 
 extern "C" int32_t kv_append(const kvb_cache* cache, const void* k_new, const void* v_new,
@@ -982,13 +1056,30 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   a.tile_hi = 1 << 30;
   a.p_off = 0;
 
+  // with a decode token: attend over the cached tokens (the splits record each
+  // head's len), then the merge adds the token's own state and appends it
+  NewTok nt;
+  memset(&nt, 0, sizeof(nt));
+  a.n_rec = nullptr;
   if (k_new) {
-    TraceScope tr(kTrAppend, s);
-    const int elem = cache->dtype == KVB_BF16 ? 2 : 4;
-    hipLaunchKernelGGL(kv_append, dim3(cache->B * cache->Hkv), dim3(64), 0, s, cache->k,
-                       cache->v, cache->log_beta, cache->pos, cache->len, cache->cap,
-                       cache->D * elem / 4, k_new, v_new, log_beta_new, t, cache->Hkv,
-                       (int32_t*)ws);
+    a.n_rec = (int32_t*)((char*)ws + kWsHeader + align_up(S * cache->D * sizeof(float), 256) +
+                         align_up(S * 2 * sizeof(float), 256));
+    nt.k_new = k_new;
+    nt.v_new = v_new;
+    nt.lb_new = log_beta_new;
+    nt.t = t;
+    nt.q = q;
+    nt.n_rec = a.n_rec;
+    nt.k = cache->k;
+    nt.v = cache->v;
+    nt.log_beta = cache->log_beta;
+    nt.pos = cache->pos;
+    nt.len = cache->len;
+    nt.status = (int32_t*)ws;
+    nt.cap = cache->cap;
+    nt.Hkv = cache->Hkv;
+    nt.elem = cache->dtype == KVB_BF16 ? 2 : 4;
+    nt.scale = a.scale_log2 * kLn2;
   }
   {
     TraceScope tr(kTrAttnSplit, s);
@@ -996,7 +1087,7 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   }
   TraceScope tr(kTrAttnMerge, s);
   launch_merge(a.part_a, a.part_ml, P, cache->D, out, lse, nullptr, nullptr, G,
-               cache->B * Hq, s);
+               cache->B * Hq, s, k_new ? &nt : nullptr);
   return launch_status();
 }
 

@@ -99,10 +99,14 @@ size_t asm_build_memory_workspace(int32_t H, int32_t N, int32_t D, int32_t L, in
  * Decode-step grouped-query attention with the retention bias, split over the KV
  * axis ([TRIM] 2.1; [ASM] background and method steps 1-2).
  *
- * Optional append first: if k_new != NULL, each head (b, g) writes k_new[b][g],
+ * Optional decode token: if k_new != NULL, each head (b, g) gets k_new[b][g],
  * v_new[b][g] (and log_beta_new[b][g] when the cache has log_beta) at slot
- * len[b][g] with pos = t[b], then len[b][g] += 1.  A head whose len already equals
- * cap is not appended to (its len stays; the caller must keep cap > len).
+ * len[b][g] with pos = t[b], then len[b][g] += 1, and the attention below covers
+ * it.  A head whose len already equals cap is not appended to (its len stays, the
+ * token is not attended, and the workspace status word becomes KVB_ECAPACITY; the
+ * caller must keep cap > len).  The splits cover the cached slots; the token's own
+ * state (logit scale * q.k_new, no bias at distance 0) is merged last, and the row
+ * is written by the merge, after every split has read the cache.
  *
  * Then for every query head h of sequence b (KV head g = h / (Hq/Hkv)) over the
  * live slots i < len[b][g]:
@@ -127,7 +131,8 @@ size_t asm_build_memory_workspace(int32_t H, int32_t N, int32_t D, int32_t L, in
  *   ws         workspace of kv_attn_decode_workspace(cache, Hq, num_splits) bytes;
  *              after the call it holds the split states: a [B][Hq][num_splits][D]
  *              float32 at byte offset 256, then (m, Z) [B][Hq][num_splits][2]
- *              float32 at the next 256-byte boundary.
+ *              float32 at the next 256-byte boundary, then (with a decode token)
+ *              each head's len before the append [B][Hkv] int32 at the next.
  */
 int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq, const int32_t* t,
                        float scale, const void* k_new, const void* v_new,

@@ -87,6 +87,39 @@ def test_attention_append_then_attend():
     check_attention(to_host(out), to_host(lse), ref_out, ref_lse, "append")
 
 
+def test_attention_decode_token_full_and_empty_heads():
+    """The decode token when a head is full (not appended, not attended, status
+    KVB_ECAPACITY) and when a head is empty (its own state is the whole result)."""
+    B, Hq, Hkv, D, cap = 1, 8, 4, 128, 64
+    d = _rand_cache(17, B, Hkv, cap, cap, D, "bf16")
+    d["len"] = np.array([[cap, 0, 5, cap - 1]], np.int32)
+    q = _queries(18, B, Hq, D, "bf16")
+    rng = np.random.default_rng(19)
+    kn = synth.bf16_bits(rng.standard_normal((B, Hkv, D)))
+    vn = synth.bf16_bits(rng.standard_normal((B, Hkv, D)))
+    lbn = np.full((B, Hkv), -0.25, np.float32)
+    t = np.array([cap + 3], np.int32)
+    c = dev_cache(d)
+    ws = torch.zeros(kvb.kv_attn_decode_workspace(c, Hq), dtype=torch.uint8, device="cuda")
+    out, lse = kvb.kv_attn_decode(c, to_dev(q), to_dev(t), k_new=to_dev(kn), v_new=to_dev(vn),
+                                  log_beta_new=to_dev(lbn), ws=ws)
+    torch.cuda.synchronize()
+    status = int(to_host(ws[:4]).view(np.int32)[0])
+    assert status == -3, f"status {status}: the full head must report KVB_ECAPACITY"
+    got = host_dict(c)
+    assert got["len"].tolist() == [[cap, 1, 6, cap]]
+    ref = oracle.Cache.from_arrays(d)
+    for g in range(Hkv):          # the oracle's append, skipping the full head
+        s0 = int(ref.length[0, g])
+        if s0 < cap:
+            ref.k[0, g, s0], ref.v[0, g, s0] = kn[0, g], vn[0, g]
+            ref.log_beta[0, g, s0], ref.pos[0, g, s0] = lbn[0, g], t[0]
+            ref.length[0, g] = s0 + 1
+    rd = {"k": ref.k, "v": ref.v, "log_beta": ref.log_beta, "pos": ref.pos, "len": ref.length}
+    ref_out, ref_lse = oracle_attention(rd, q, t)
+    check_attention(to_host(out), to_host(lse), ref_out, ref_lse, "full and empty heads")
+
+
 def test_attention_edges():
     """Empty heads, a single live token, all-but-newest weights zero (log beta = -inf),
     a decode token at the same position as a live slot, more splits than tiles."""
