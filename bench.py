@@ -486,7 +486,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path shards by KV head with no exchange; see DESIGN.md).",
+              "(the hot path shards by KV head with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 
