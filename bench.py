@@ -11,7 +11,7 @@ HBM before the timed region.  Eviction is destructive, so the first M slots of
 every layer (the only ones compaction writes) are restored from a pristine copy
 between steps, outside the timed region.
 
-Prints one JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -485,7 +485,7 @@ def main():
         steady_bench(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
               "(the hot path shards by KV head with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
