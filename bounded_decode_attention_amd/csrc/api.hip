@@ -110,6 +110,7 @@ extern "C" const char* kvb_strerror(int32_t status) {
     case KVB_EWORKSPACE: return "workspace missing or too small";
     case KVB_EDEVICE: return "no gfx950 device";
     case KVB_ELAUNCH: return "kernel launch failed";
+    case KVB_ERANGE: return "input value outside the supported range (saturated)";
     default: return "unknown status";
   }
 }

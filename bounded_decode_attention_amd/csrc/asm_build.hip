@@ -9,15 +9,15 @@
 // and states are kept per KV head (the page's GQA extension).
 //
 // Kernels
-//   asm_prefix_chunk<D>  per (KV head, 128 queries, prefix chunk): attention on
+//   asm_prefix_chunk<D>  per (KV head, 256 queries, prefix chunk), 8 waves: attention on
 //                        v_mfma_f32_16x16x32_bf16 with the keys as rows.  S^T =
 //                        K Q^T leaves every lane four keys of one query, which is
 //                        the B-operand layout of O^T = V^T P^T once the two 16-key
 //                        halves of a 32-key step are interleaved in the contraction
 //                        index (the A operand, V^T, uses the same interleave); V is
-//                        transposed on its way into LDS, K is stored with a padded
-//                        row so the 16 rows an MFMA reads fall in distinct banks.
-//                        The weights P enter the value product as two bf16 parts.
+//                        transposed (to fp16) by a pre-pass; K and V^T tiles go to
+//                        XOR-swizzled LDS rows by global_load_lds.  The value
+//                        product runs on v_mfma_f32_16x16x32_f16 (P rounded to fp16).
 //   asm_prefix_merge<D>  per (KV head, query): merge of the chunks' states.
 //   km_prep<D>           fp32 centroids -> bf16 hi, bf16 lo = c - hi, |c|^2.
 //   km_assign<D>         per (KV head, 256 points): |c|^2 - 2 x.c for every
@@ -49,7 +49,8 @@ struct PrefixArgs {
   const uint16_t* q;   // [H][N][D]
   const uint16_t* k;   // [H][L][D]
   const uint16_t* v;   // [H][L][D]
-  uint16_t* vt;        // [H][C][D][Lc]: V^T per chunk, keys interleaved (vt_prepare)
+  uint16_t* vt;        // [H][C][D][Lc]: V^T per chunk in fp16, keys interleaved (vt_prepare)
+  int32_t* status;     // workspace status word (KVB_ERANGE if a value saturated)
   float* out;          // [C][H][N][D]
   float* out_lse;      // [C][H][N]
   int32_t H, N, L, C, csize, Lc;
@@ -64,8 +65,9 @@ __device__ __forceinline__ int vt_position(int kk) {
   return (kk & ~31) + 8 * g + j;
 }
 
-// V [H][L][D] -> V^T [H][C][D][Lc] (chunk-local keys at vt_position, zero past the
-// chunk's end).  One workgroup per (KV head, chunk, 64-key tile).
+// V [H][L][D] bf16 -> V^T [H][C][D][Lc] fp16 (chunk-local keys at vt_position, zero
+// past the chunk's end; |v| > 65504 saturates and sets the status word).  One
+// workgroup per (KV head, chunk, 64-key tile).
 template <int D>
 __global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
   constexpr int RP = D + 8;
@@ -90,14 +92,19 @@ __global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
   for (int j = 0; j < D * 8 / 256; ++j) {
     const int ci = tid + 256 * j, d = ci / 8, q = ci % 8;  // positions 8q..8q+7 of row d
     uint32_t w[4];
+    bool sat = false;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       // inverse of vt_position inside a 32-key block: position 8g + j -> key
       const int p0 = 8 * q + e, p1 = p0 + 1;
       const int k0 = (p0 & ~31) + 4 * ((p0 & 31) >> 3) + (p0 & 3) + ((p0 & 4) ? 16 : 0);
       const int k1 = (p1 & ~31) + 4 * ((p1 & 31) >> 3) + (p1 & 3) + ((p1 & 4) ? 16 : 0);
-      w[e / 2] = (uint32_t)vs[k0 * RP + d] | ((uint32_t)vs[k1 * RP + d] << 16);
+      const float x0 = bf16_bits_to_f32(vs[k0 * RP + d]), x1 = bf16_bits_to_f32(vs[k1 * RP + d]);
+      sat |= fabsf(x0) > 65504.f || fabsf(x1) > 65504.f;
+      w[e / 2] = pack_f16x2(fminf(fmaxf(x0, -65504.f), 65504.f),
+                            fminf(fmaxf(x1, -65504.f), 65504.f));
     }
+    if (sat) p.status[0] = KVB_ERANGE;
     *(u32x4*)(dst + (size_t)d * p.Lc + 8 * q) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
@@ -229,28 +236,21 @@ __global__ __launch_bounds__(512) void asm_prefix_chunk(PrefixArgs p) {
     // 32ks + 4lg + j (j < 4) or 32ks + 16 + 4lg + (j - 4)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      // P = P_hi + P_lo in bf16 (a single bf16 rounding of the weights would cost
-      // up to ~2e-3 of the output's scale)
-      u32x4 ph[2], pl[2];
+      // P in fp16 (11 significant bits; a single bf16 rounding of the weights would
+      // cost up to ~2e-3 of the output's scale), V^T in fp16
+      u32x4 pf[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         const f32x4 x0 = s[2 * ks][qt], x1 = s[2 * ks + 1][qt];
-        uint32_t hb[4], lb[4];
-        split_bf16x2(x0[0], x0[1], hb[0], lb[0]);
-        split_bf16x2(x0[2], x0[3], hb[1], lb[1]);
-        split_bf16x2(x1[0], x1[1], hb[2], lb[2]);
-        split_bf16x2(x1[2], x1[3], hb[3], lb[3]);
-        ph[qt] = u32x4{hb[0], hb[1], hb[2], hb[3]};
-        pl[qt] = u32x4{lb[0], lb[1], lb[2], lb[3]};
+        pf[qt] = u32x4{pack_f16x2(x0[0], x0[1]), pack_f16x2(x0[2], x0[3]),
+                       pack_f16x2(x1[0], x1[1]), pack_f16x2(x1[2], x1[3])};
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = dt * 16 + lc;
         const u32x4 a = *(const u32x4*)(vb + d * 128 + 16 * vt_slot(d, 4 * ks + lg));
-        o[dt][0] = mfma_16x16x32_bf16(a, ph[0], o[dt][0]);
-        o[dt][1] = mfma_16x16x32_bf16(a, ph[1], o[dt][1]);
-        o[dt][0] = mfma_16x16x32_bf16(a, pl[0], o[dt][0]);
-        o[dt][1] = mfma_16x16x32_bf16(a, pl[1], o[dt][1]);
+        o[dt][0] = mfma_16x16x32_f16(a, pf[0], o[dt][0]);
+        o[dt][1] = mfma_16x16x32_f16(a, pf[1], o[dt][1]);
       }
     }
   }
@@ -730,7 +730,7 @@ static size_t prefix_layout(int H, int N, int D, int L, int chunks, int& C, int&
 
 static int32_t launch_prefix(const void* q, int32_t H, int32_t N, int32_t D, const void* k,
                              const void* v, int32_t L, int32_t chunks, float scale, float* a,
-                             float* lse, void* ws, hipStream_t s) {
+                             float* lse, void* ws, int32_t* status, hipStream_t s) {
   int C, csize, Lc;
   size_t o_vt, o_part, o_plse;
   prefix_layout(H, N, D, L, chunks, C, csize, Lc, o_vt, o_part, o_plse);
@@ -739,6 +739,7 @@ static int32_t launch_prefix(const void* q, int32_t H, int32_t N, int32_t D, con
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
   p.vt = (uint16_t*)((char*)ws + o_vt);
+  p.status = status;
   p.H = H;
   p.N = N;
   p.L = L;
@@ -894,7 +895,8 @@ extern "C" int32_t asm_prefix_states(const void* q, int32_t H, int32_t N, int32_
   int32_t st = check_device();
   if (st) return st;
   if (!(scale > 0.f)) scale = 1.f / sqrtf((float)D);
-  return launch_prefix(q, H, N, D, k, v, L, chunks, scale, a, lse, ws, (hipStream_t)stream);
+  return launch_prefix(q, H, N, D, k, v, L, chunks, scale, a, lse, ws, (int32_t*)ws,
+                       (hipStream_t)stream);
 }
 
 extern "C" size_t asm_kmeans_workspace(int32_t H, int32_t K, int32_t D) {
@@ -972,7 +974,7 @@ extern "C" int32_t asm_build_memory(const void* q, int32_t H, int32_t N, int32_t
   float* a = (float*)(w + o_a);
   float* lse = (float*)(w + o_l);
   hipStream_t s = (hipStream_t)stream;
-  st = launch_prefix(q, H, N, D, k, v, L, chunks, scale, a, lse, w + o_p, s);
+  st = launch_prefix(q, H, N, D, k, v, L, chunks, scale, a, lse, w + o_p, (int32_t*)w, s);
   if (st) return st;
   st = launch_kmeans(q, H, N, D, centroids, K, iters, assign, nullptr, centroids_bf16, w + o_k, s);
   if (st) return st;

@@ -47,7 +47,9 @@ typedef enum {
   KVB_ECAPACITY = -3,    /* cache capacity too small for the request            */
   KVB_EWORKSPACE = -4,   /* ws is NULL or ws_bytes below the required size       */
   KVB_EDEVICE = -5,      /* no usable HIP device, or the device is not gfx950    */
-  KVB_ELAUNCH = -6       /* a kernel launch failed (hipGetLastError)            */
+  KVB_ELAUNCH = -6,      /* a kernel launch failed (hipGetLastError)            */
+  KVB_ERANGE = -7        /* (workspace status word only) an input value outside the
+                            range a kernel's arithmetic supports; it was saturated */
 } kvb_status;
 
 typedef enum { KVB_F32 = 0, KVB_BF16 = 1 } kvb_dtype;
@@ -293,7 +295,10 @@ int32_t asm_lookup_merge_hier(const void* q, int32_t B, int32_t Hq, int32_t Hkv,
  * ceil(L / chunks) tokens (the last may be shorter); each chunk's state is
  * computed on its own and the states are merged in chunk order with the merge
  * operator.  L == 0 gives a = 0, lse = -inf.  Scores use bf16 MFMA products with
- * float32 accumulation; the softmax weights enter the value product rounded to bf16.
+ * float32 accumulation; the value product runs in fp16 (float32 accumulation): the
+ * softmax weights rounded to fp16, v converted to fp16 (exact for |v| <= 65504;
+ * larger values saturate to +-65504 and the workspace status word, the int32 at
+ * byte offset 0, is set to KVB_ERANGE; the call never clears it).
  *   q        [H][N][D] bf16 (the KV head's calibration queries; for GQA the group's
  *            query heads stacked along N)
  *   k, v     [H][L][D] bf16 (may be NULL when L == 0)
@@ -354,8 +359,8 @@ int32_t asm_aggregate_states(const int32_t* assign, const float* a, const float*
  * states by the final assignment.  The outputs are the codebook the lookup reads:
  * centroids_bf16 [H][K][D] bf16, abar [H][K][D] bf16, log_zbar [H][K] float32,
  * plus the float32 centroids (in place) and the assignment [H][N] int32.
- *   ws  asm_build_memory_workspace(H, N, D, L, chunks, K) bytes; after the call
- *       it holds the per-query states: a [H][N][D] float32 at byte offset 256,
+ *   ws  asm_build_memory_workspace(H, N, D, L, chunks, K) bytes (its status word as
+ *       for asm_prefix_states); after the call it holds the per-query states: a [H][N][D] float32 at byte offset 256,
  *       lse [H][N] float32 at the next 256-byte boundary.
  * Other arguments as for the three calls above.
  */

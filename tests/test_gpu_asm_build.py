@@ -95,8 +95,31 @@ def test_prefix_states_empty_prefix_and_chunking_is_lossless():
     a4, l4 = kvb.asm_prefix_states(to_dev(q), to_dev(k), to_dev(v), chunks=4)
     torch.cuda.synchronize()
     a1, l1, a4, l4 = map(to_host, (a1, l1, a4, l4))
+    # the weights enter the value product rounded to fp16 relative to each chunking's
+    # running maximum, so the two agree to that rounding (each is within the 2e-3 bar
+    # of the oracle); the normalisers are summed unrounded
     err = np.abs(a1 - a4).max(-1) / np.abs(a1).max(-1)
-    assert err.max() <= 1e-5 and np.abs(l1 - l4).max() <= 1e-5
+    assert err.max() <= 1e-3 and np.abs(l1 - l4).max() <= 1e-5
+
+
+def test_prefix_states_value_range():
+    """Values of v beyond the fp16 range of the value product saturate to +-65504
+    and set the workspace status word to KVB_ERANGE; in-range inputs leave it."""
+    q, k, v = _inputs(1, 40, 300, 128, 55)
+    ws = torch.zeros(kvb.asm_prefix_states_workspace(1, 40, 128, 300, 2), dtype=torch.uint8,
+                     device="cuda")
+    kvb.asm_prefix_states(to_dev(q), to_dev(k), to_dev(v), chunks=2, ws=ws)
+    torch.cuda.synchronize()
+    assert int(to_host(ws[:4]).view(np.int32)[0]) == 0
+    v2 = v.copy()
+    v2[0, 17, 5] = synth.bf16_bits(np.array([1.0e5]))[0]
+    v2[0, 200, 9] = synth.bf16_bits(np.array([-3.0e6]))[0]
+    a, lse = kvb.asm_prefix_states(to_dev(q), to_dev(k), to_dev(v2), chunks=2, ws=ws)
+    torch.cuda.synchronize()
+    assert int(to_host(ws[:4]).view(np.int32)[0]) == -7
+    vc = np.clip(values(v2[0]), -65504.0, 65504.0)
+    ra, rl = oracle.prefix_states(values(q[0]), values(k[0]), vc, 1 / np.sqrt(128), 2)
+    _check_states(to_host(a)[0], to_host(lse)[0], ra, rl, "saturated v")
 
 
 @pytest.mark.parametrize("D", [64, 128])
