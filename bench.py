@@ -443,6 +443,8 @@ def main():
                          "plan_beside: each compaction right after its layer's attention; "
                          "both_beside (default of --steady): each compaction beside the next "
                          "layer's attention")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode step: replay the step as one captured HIP graph")
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
@@ -545,14 +547,14 @@ def main():
     # and writes every kept row to its compacted slot from the data it has loaded.
     # Layer l+1's work starts after layer l's attention (its inputs would come from
     # it).  The side stream has default priority and is joined at the end.
-    main = torch.cuda.current_stream()
-    side = main if sched == "serial" else torch.cuda.Stream()
+    side_stream = torch.cuda.Stream()
     appended = [torch.cuda.Event() for _ in range(L)]
     planned = [torch.cuda.Event() for _ in range(L)]
     attended = [torch.cuda.Event() for _ in range(L)]
     fused = args.fused
 
-    def step():
+    def step(main):
+        side = main if sched == "serial" else side_stream
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
             ws_e = ws_es[layer % n_ws]
@@ -609,8 +611,21 @@ def main():
 
     for _ in range(args.warmup):
         restore()
-        step()
+        step(torch.cuda.current_stream())
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # the whole step (both streams) captured once; replayed after each restore
+        restore()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            restore()
+            graph.replay()
+        torch.cuda.synchronize()
 
     # CPU baseline inputs: whole heads of layer 0 as drawn (read before the timed run)
     host_units = []
@@ -644,18 +659,30 @@ def main():
     copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del cx, cy
 
-    kvb.trace_enable(2 * args.steps * L + 16, ("attn_split", "attn_fused"))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     times = []
+    if graph is not None:
+        for _ in range(args.steps):
+            restore()
+            torch.cuda.synchronize()
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+    kvb.trace_enable(2 * args.steps * L + 16, ("attn_split", "attn_fused"))
+    eager_times = []
     for _ in range(args.steps):
         restore()
         torch.cuda.synchronize()
         e0.record()
-        step()
+        step(torch.cuda.current_stream())
         e1.record()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
+        eager_times.append(e0.elapsed_time(e1))
+    if graph is None:
+        times = eager_times
     trace = kvb.trace_read()
     kvb.trace_disable()
     # per layer: the attention split launch(es) of that layer (fused: both phases)
@@ -702,10 +729,12 @@ def main():
                    "head_dim": w.head_dim, "ctx": w.ctx, "budget": M, "layers": L,
                    "kv_splits": splits,
                    "schedule": sched,
-                   "compaction": "fused" if fused else "separate pass"},
+                   "compaction": "fused" if fused else "separate pass",
+                   "launch": "graph" if graph is not None else "eager"},
         "kv_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "device_copy_gbps": round(copy_gbps, 1), "copy_frac": round(gbps / copy_gbps, 4),
         "bytes_per_step": total_b, "moved_rows_per_step": moved,
+        "eager_ms_per_step": round(sum(eager_times) / len(eager_times), 4),
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,

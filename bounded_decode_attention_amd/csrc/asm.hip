@@ -8,11 +8,13 @@
 // searches its KV head's codebook with its own query.
 //
 // Kernels
-//   asm_lookup_partial  per (KV head, block of 16 queries, chunk of centroids):
-//                       S = Q C^T on v_mfma_f32_16x16x32_bf16 with the queries as
-//                       rows; each lane scores one centroid column against four
-//                       queries, scales by 1/|c_k| (the |q| factor is common to all
-//                       k), keeps the best (score, lowest k), and the workgroup
+//   asm_lookup_partial  per (KV head, four blocks of 16 queries, chunk of 256
+//                       centroids): S = Q C^T on v_mfma_f32_16x16x32_bf16 with the
+//                       queries as rows; each centroid tile is loaded once (all of
+//                       a wave's tiles up front) and serves the four query blocks;
+//                       each lane scores one centroid column against four queries
+//                       per block, scales by 1/|c_k| (the |q| factor is common to
+//                       all k), keeps the best (score, lowest k), and the workgroup
 //                       reduces to one candidate per query and chunk.
 //   asm_finalize        per query: best over chunks -> idx; gather abar[idx],
 //                       log Zbar[idx]; merge with (self_out, self_lse).
@@ -23,7 +25,9 @@
 namespace kvb {
 
 constexpr int kAsmWaves = 4;
-constexpr int kAsmChunk = 1024;  // centroids per workgroup
+constexpr int kAsmChunk = 256;  // centroids per workgroup
+constexpr int kAsmIt = kAsmChunk / (16 * kAsmWaves);  // 16-centroid tiles per wave
+constexpr int kAsmQB = 4;  // blocks of 16 queries per workgroup (share each centroid load)
 
 struct AsmArgs {
   const uint16_t* q;
@@ -47,68 +51,84 @@ __device__ __forceinline__ bool better(float s, int k, float bs, int bk) {
 template <int D>
 __global__ __launch_bounds__(64 * kAsmWaves) void asm_lookup_partial(AsmArgs a) {
   constexpr int KK = D / 32;
-  __shared__ float red_s[kAsmWaves][16];
-  __shared__ int red_k[kAsmWaves][16];
+  __shared__ float red_s[kAsmWaves][kAsmQB * 16];
+  __shared__ int red_k[kAsmWaves][kAsmQB * 16];
 
-  const int chunk = blockIdx.x, g = blockIdx.y, qb = blockIdx.z;
+  const int chunk = blockIdx.x, g = blockIdx.y, qz = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lg = lane >> 4, lc = lane & 15;
   const int nq = a.B * a.G;
 
-  // A operand: query row lc of this block (zero past the last query)
-  const int qi = qb * 16 + lc;
-  u32x4 qa[KK];
-  {
+  // A operands: query row lc of each of this workgroup's kAsmQB query blocks (zero
+  // past the last query)
+  u32x4 qa[kAsmQB][KK];
+#pragma unroll
+  for (int j = 0; j < kAsmQB; ++j) {
+    const int qi = (qz * kAsmQB + j) * 16 + lc;
     const bool ok = qi < nq;
-    const int b = ok ? qi / a.G : 0, j = ok ? qi - (qi / a.G) * a.G : 0;
-    const uint16_t* qp = a.q + ((size_t)(b * a.Hq + g * a.G + j)) * D;
+    const int b = ok ? qi / a.G : 0, jj = ok ? qi - (qi / a.G) * a.G : 0;
+    const uint16_t* qp = a.q + ((size_t)(b * a.Hq + g * a.G + jj)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      qa[kk] = ok ? *(const u32x4*)(qp + 32 * kk + 8 * lg) : z;
+      qa[j][kk] = ok ? *(const u32x4*)(qp + 32 * kk + 8 * lg) : z;
     }
   }
 
-  float best[4];
-  int bestk[4];
+  float best[kAsmQB][4];
+  int bestk[kAsmQB][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    best[i] = kNegInf;
-    bestk[i] = 0x7FFFFFFF;
-  }
+  for (int j = 0; j < kAsmQB; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      best[j][i] = kNegInf;
+      bestk[j][i] = 0x7FFFFFFF;
+    }
   const uint16_t* cb = a.cent + (size_t)g * a.K * D;
   const int k0 = chunk * kAsmChunk;
   const int k1 = min(k0 + kAsmChunk, a.K);
-  for (int kt = k0 + wave * 16; kt < k1; kt += 16 * kAsmWaves) {
-    const int kc = kt + lc;  // this lane's centroid column
-    const int kr = min(kc, a.K - 1);
-    u32x4 cv[KK];
+  // every centroid tile of this wave is loaded before any is scored (one memory
+  // round trip); columns past the codebook read its last row and are never scored
+  u32x4 cv[kAsmIt][KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) cv[kk] = *(const u32x4*)(cb + (size_t)kr * D + 32 * kk + 8 * lg);
+  for (int it = 0; it < kAsmIt; ++it) {
+    const int kr = min(k0 + 16 * (wave + kAsmWaves * it) + lc, a.K - 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      cv[it][kk] = *(const u32x4*)(cb + (size_t)kr * D + 32 * kk + 8 * lg);
+  }
+#pragma unroll
+  for (int it = 0; it < kAsmIt; ++it) {
+    const int kc = k0 + 16 * (wave + kAsmWaves * it) + lc;  // this lane's centroid column
     // |c|^2 of the column: 8 dims per lane per k-step, then over the 4 lane groups
     float n2 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float lo = bf16_bits_to_f32(cv[kk][w] & 0xFFFFu);
-        const float hi = bf16_bits_to_f32(cv[kk][w] >> 16);
+        const float lo = bf16_bits_to_f32(cv[it][kk][w] & 0xFFFFu);
+        const float hi = bf16_bits_to_f32(cv[it][kk][w] >> 16);
         n2 = fmaf(lo, lo, n2);
         n2 = fmaf(hi, hi, n2);
       }
     n2 += __shfl_xor(n2, 16, 64);
     n2 += __shfl_xor(n2, 32, 64);
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) S = mfma_16x16x32_bf16(qa[kk], cv[kk], S);
     const float inv = n2 > 0.f ? rsqrtf(n2) : 0.f;
-    if (kc < k1 && n2 > 0.f) {
+    const bool live = kc < k1 && n2 > 0.f;
+    // the centroid tile is the B operand of every query block's product
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = S[i] * inv;
-        if (better(sc, kc, best[i], bestk[i])) {
-          best[i] = sc;
-          bestk[i] = kc;
+    for (int j = 0; j < kAsmQB; ++j) {
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) S = mfma_16x16x32_bf16(qa[j][kk], cv[it][kk], S);
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sc = S[i] * inv;
+          if (better(sc, kc, best[j][i], bestk[j][i])) {
+            best[j][i] = sc;
+            bestk[j][i] = kc;
+          }
         }
       }
     }
@@ -117,34 +137,42 @@ __global__ __launch_bounds__(64 * kAsmWaves) void asm_lookup_partial(AsmArgs a) 
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float os = __shfl_xor(best[i], o, 64);
-      const int ok = __shfl_xor(bestk[i], o, 64);
-      if (better(os, ok, best[i], bestk[i])) {
-        best[i] = os;
-        bestk[i] = ok;
+    for (int j = 0; j < kAsmQB; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float os = __shfl_xor(best[j][i], o, 64);
+        const int ok = __shfl_xor(bestk[j][i], o, 64);
+        if (better(os, ok, best[j][i], bestk[j][i])) {
+          best[j][i] = os;
+          bestk[j][i] = ok;
+        }
       }
-    }
   }
   if (lc == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      red_s[wave][4 * lg + i] = best[i];
-      red_k[wave][4 * lg + i] = bestk[i];
-    }
+    for (int j = 0; j < kAsmQB; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        red_s[wave][16 * j + 4 * lg + i] = best[j][i];
+        red_k[wave][16 * j + 4 * lg + i] = bestk[j][i];
+      }
   }
   __syncthreads();
-  if (threadIdx.x < 16) {
-    float bs = red_s[0][threadIdx.x];
-    int bk = red_k[0][threadIdx.x];
+  if (threadIdx.x < kAsmQB * 16) {
+    const int r = threadIdx.x;
+    float bs = red_s[0][r];
+    int bk = red_k[0][r];
     for (int w = 1; w < kAsmWaves; ++w)
-      if (better(red_s[w][threadIdx.x], red_k[w][threadIdx.x], bs, bk)) {
-        bs = red_s[w][threadIdx.x];
-        bk = red_k[w][threadIdx.x];
+      if (better(red_s[w][r], red_k[w][r], bs, bk)) {
+        bs = red_s[w][r];
+        bk = red_k[w][r];
       }
-    const size_t o = ((size_t)g * a.QB * 16 + qb * 16 + threadIdx.x) * a.KC + chunk;
-    a.cand_score[o] = bs;
-    a.cand_idx[o] = bk;
+    const int row = qz * kAsmQB * 16 + r;  // query row (block row * 16 + lane)
+    if (row < a.QB * 16) {
+      const size_t o = ((size_t)g * a.QB * 16 + row) * a.KC + chunk;
+      a.cand_score[o] = bs;
+      a.cand_idx[o] = bk;
+    }
   }
 }
 
@@ -508,7 +536,7 @@ extern "C" int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_
   a.cand_score = (float*)((char*)ws + kWsHeader);
   a.cand_idx = (int32_t*)((char*)ws + kWsHeader + align_up(n * 4, 256));
   hipStream_t s = (hipStream_t)stream;
-  dim3 grid(a.KC, Hkv, a.QB);
+  dim3 grid(a.KC, Hkv, (a.QB + kAsmQB - 1) / kAsmQB);
   {
     TraceScope tr(kTrAsmLookup, s);
     if (D == 128)

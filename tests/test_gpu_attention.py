@@ -122,7 +122,8 @@ def test_attention_decode_token_full_and_empty_heads():
 
 def test_attention_edges():
     """Empty heads, a single live token, all-but-newest weights zero (log beta = -inf),
-    a decode token at the same position as a live slot, more splits than tiles."""
+    a decode token at the same position as a live slot, more splits than tiles (up
+    to the 4096 limit, past the merge's 1024 states held in registers)."""
     B, Hq, Hkv, D, n = 2, 8, 4, 128, 70
     d = _rand_cache(9, B, Hkv, n, n, D, "bf16", lens=[[0, 1, 70, 33], [70, 0, 2, 64]])
     d["log_beta"][0, 2, :] = -np.inf                  # only distance-0 tokens keep weight
@@ -130,7 +131,7 @@ def test_attention_edges():
     q = _queries(10, B, Hq, D, "bf16")
     t = np.array([69, 75], np.int32)                  # b=0: t equals the last live position
     c = dev_cache(d)
-    for P in (1, 2, 64, 300):
+    for P in (1, 2, 64, 300, 1100, 4096):
         out, lse = kvb.kv_attn_decode(c, to_dev(q), to_dev(t), num_splits=P)
         torch.cuda.synchronize()
         ref_out, ref_lse = oracle_attention(d, q, t)
