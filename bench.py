@@ -735,6 +735,9 @@ def main():
         "device_copy_gbps": round(copy_gbps, 1), "copy_frac": round(gbps / copy_gbps, 4),
         "bytes_per_step": total_b, "moved_rows_per_step": moved,
         "eager_ms_per_step": round(sum(eager_times) / len(eager_times), 4),
+        # with --graph the replays carry no events: kernel times come from the
+        # eager steps that follow them (same kernels, same inputs)
+        "kernel_times_from": "eager steps" if graph is not None else "timed steps",
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,

@@ -353,11 +353,12 @@ __global__ __launch_bounds__(64) void asm_hier_select(HierArgs h) {
   uint32_t u[kMaxPer];
 #pragma unroll
   for (int e = 0; e < kMaxPer; ++e) u[e] = ordf(sc[e]);
+  // (64 e < K1 is uniform: the slices past the last cluster are skipped)
   auto count_ge = [&](uint32_t th) -> int {
     int c = 0;
 #pragma unroll
     for (int e = 0; e < kMaxPer; ++e)
-      c += __popcll(__ballot(lane + 64 * e < h.K1 && u[e] >= th));
+      if (64 * e < h.K1) c += __popcll(__ballot(lane + 64 * e < h.K1 && u[e] >= th));
     return c;
   };
   unsigned long long lo = 0, hi = 0xFFFFFFFFull;  // count_ge(lo) >= m throughout
@@ -370,11 +371,12 @@ __global__ __launch_bounds__(64) void asm_hier_select(HierArgs h) {
   int above = 0;
 #pragma unroll
   for (int e = 0; e < kMaxPer; ++e)
-    above += __popcll(__ballot(lane + 64 * e < h.K1 && u[e] > T));
+    if (64 * e < h.K1) above += __popcll(__ballot(lane + 64 * e < h.K1 && u[e] > T));
   int slot = 0, ties = h.m - above;
   const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int e = 0; e < kMaxPer; ++e) {
+    if (64 * e >= h.K1) break;
     const bool valid = lane + 64 * e < h.K1;
     const unsigned long long eq = __ballot(valid && u[e] == T);
     const int eq_before = __popcll(eq & below);
@@ -388,74 +390,125 @@ __global__ __launch_bounds__(64) void asm_hier_select(HierArgs h) {
 }
 
 // One workgroup per (cluster, KV head): find the queries that kept the cluster
-// (a scan of the selections, up to 1024 queries per round), then score the
-// cluster's entries against them on MFMA, 16 queries x 16 entries per tile.
-constexpr int kHierRound = 1024;
+// (a scan of the selections, up to kHierRound queries per round), copy their rows
+// to LDS, then score the cluster's entries against them on MFMA: each wave loads
+// its 16-entry tiles once and runs every 16-query tile of the list against them;
+// each query's best (ordered cosine, ~original index) is an LDS atomic maximum,
+// then one global atomic maximum per listed query.
+constexpr int kHierRound = 256;
 
 template <int D>
 __global__ __launch_bounds__(256) void asm_hier_score(HierArgs h) {
   constexpr int KK = D / 32;
+  constexpr int kRowW = D / 8;  // 16-byte pieces per query row
   __shared__ int qlist[kHierRound];
   __shared__ int nlist;
+  // one 16-byte pad per row: the 16 rows of a tile read from different banks
+  __shared__ __attribute__((aligned(16))) u32x4 qrows[kHierRound][kRowW + 1];
+  __shared__ unsigned long long qbest[kHierRound];
   const AsmArgs& a = h.a;
   const int j = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
   const int nq = a.B * a.G;
   const int32_t* offs = h.offs + (size_t)g * (h.K1 + 1);
-  const int m0 = min(max(offs[j], 0), a.K), m1 = min(max(offs[j + 1], m0), a.K);
-  if (m0 >= m1) return;
   const int32_t* sel = h.sel + (size_t)g * h.NQ * h.m;
   const uint16_t* cb = h.stored + (size_t)g * a.K * D;
   const int32_t* kid = h.kid + (size_t)g * a.K;
+  const int o0 = offs[j], o1 = offs[j + 1];
+  // the first kPre x 256 selections are loaded together with the cluster's range
+  constexpr int kPre = 8;
+  int sv0[kPre];
+  {
+    const int pf = min(nq, kHierRound) * h.m;
+#pragma unroll
+    for (int e = 0; e < kPre; ++e) sv0[e] = tid + 256 * e < pf ? sel[tid + 256 * e] : -1;
+  }
+  const int m0 = min(max(o0, 0), a.K), m1 = min(max(o1, m0), a.K);
+  if (m0 >= m1) return;
   for (int base = 0; base < nq; base += kHierRound) {
     if (tid == 0) nlist = 0;
+    qbest[tid] = 0ull;  // kHierRound == blockDim
     __syncthreads();
     // a query keeps a cluster at most once: scan its selections in memory order
     const int p1 = min(nq, base + kHierRound) * h.m;
-    for (int p0 = base * h.m + tid; p0 < p1; p0 += 4 * 256) {
-      int sv[4];
+    int pstart = base * h.m + tid;
+    if (base == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sv[e] = p0 + 256 * e < p1 ? sel[p0 + 256 * e] : -1;
+      for (int e = 0; e < kPre; ++e)
+        if (sv0[e] == j) qlist[atomicAdd(&nlist, 1)] = (tid + 256 * e) / h.m;
+      pstart += kPre * 256;
+    }
+    for (int p0 = pstart; p0 < p1; p0 += kPre * 256) {
+      int sv[kPre];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < kPre; ++e) sv[e] = p0 + 256 * e < p1 ? sel[p0 + 256 * e] : -1;
+#pragma unroll
+      for (int e = 0; e < kPre; ++e)
         if (sv[e] == j) qlist[atomicAdd(&nlist, 1)] = (p0 + 256 * e) / h.m;
     }
     __syncthreads();
     const int nl = nlist;
+    if (nl == 0) continue;  // uniform
+    // the listed queries' rows -> LDS (rows past the list up to the tile edge: 0)
+    const int nlt = (nl + 15) & ~15;
+    for (int e = tid; e < nlt * kRowW; e += 256) {
+      const int r = e / kRowW, c = e - r * kRowW;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r < nl) {
+        const int qi = qlist[r];
+        const int b = qi / a.G, jj = qi - (qi / a.G) * a.G;
+        v = *(const u32x4*)(a.q + ((size_t)(b * a.Hq + g * a.G + jj)) * D + 8 * c);
+      }
+      qrows[r][c] = v;
+    }
+    __syncthreads();
     // Entries are the MFMA's A rows and queries its B columns, so lane (g4, c)
-    // holds entries 4 g4 .. 4 g4 + 3 of a tile for query c: the best over a wave's
-    // entry tiles needs two shuffles at the end.  Wave w takes entry tiles w, w + 4, ...
-    for (int qt = 0; qt < nl; qt += 16) {
-      const bool okq = qt + lc < nl;
-      u32x4 qb[KK];
-      load_query_rows<D>(a, g, okq ? qlist[qt + lc] : 0, okq, lg, qb);
-      unsigned long long pk = 0ull;
-      for (int mt = m0 + 16 * wave; mt < m1; mt += 64) {
-        u32x4 cv[KK];
-        const float n2 = load_columns<D>(cb + (size_t)min(mt + lc, m1 - 1) * D, lg, cv);
+    // holds entries 4 g4 .. 4 g4 + 3 of a tile for query c.  Wave w takes entry
+    // tiles w, w + 4, ...
+    for (int mt = m0 + 16 * wave; mt < m1; mt += 64) {
+      u32x4 cv[KK];
+      int kd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kd[i] = kid[min(mt + 4 * lg + i, m1 - 1)];
+      const float n2 = load_columns<D>(cb + (size_t)min(mt + lc, m1 - 1) * D, lg, cv);
+      float inv[4];
+      bool live[4], nz[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int me = 4 * lg + i;             // entry row of S[i]
+        const float n2e = __shfl(n2, me, 64);  // lanes 0..15 hold the 16 norms
+        live[i] = mt + me < m1;
+        nz[i] = n2e > 0.f;                     // a zero entry scores -inf
+        inv[i] = nz[i] ? rsqrtf(n2e) : 0.f;
+      }
+      for (int qt = 0; qt < nl; qt += 16) {
+        u32x4 qb[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qb[kk] = qrows[qt + lc][4 * kk + lg];
         f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) S = mfma_16x16x32_bf16(cv[kk], qb[kk], S);
+        unsigned long long pk = 0ull;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int me = 4 * lg + i;                 // entry row of S[i]
-          const float n2e = __shfl(n2, me, 64);      // lanes 0..15 hold the 16 norms
-          if (mt + me < m1) {
-            const int kd = kid[mt + me];
-            const float sc = n2e > 0.f ? S[i] * rsqrtf(n2e) : kNegInf;
+          if (live[i]) {
+            const float sc = nz[i] ? S[i] * inv[i] : kNegInf;
             const unsigned long long key =
-                ((unsigned long long)ordf(sc) << 32) | (0xFFFFFFFFu - (uint32_t)kd);
+                ((unsigned long long)ordf(sc) << 32) | (0xFFFFFFFFu - (uint32_t)kd[i]);
             pk = key > pk ? key : pk;
           }
         }
+        unsigned long long o2 = __shfl_xor(pk, 16, 64);
+        pk = o2 > pk ? o2 : pk;
+        o2 = __shfl_xor(pk, 32, 64);
+        pk = o2 > pk ? o2 : pk;
+        if (lg == 0 && qt + lc < nl && pk != 0ull) atomicMax(&qbest[qt + lc], pk);
       }
-      unsigned long long o2 = __shfl_xor(pk, 16, 64);
-      pk = o2 > pk ? o2 : pk;
-      o2 = __shfl_xor(pk, 32, 64);
-      pk = o2 > pk ? o2 : pk;
-      if (lg == 0 && okq && pk != 0ull) atomicMax(&h.best[(size_t)g * h.NQ + qlist[qt + lc]], pk);
     }
+    __syncthreads();
+    for (int r = tid; r < nl; r += 256)
+      if (qbest[r] != 0ull) atomicMax(&h.best[(size_t)g * h.NQ + qlist[r]], qbest[r]);
     __syncthreads();
   }
 }
