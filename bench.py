@@ -92,7 +92,10 @@ def steady_bench(args):
     the last layer's attention); the whole step is
     captured once in a HIP graph and replayed (t advances on the device).  A second,
     eager run of the same steps with the library's HIP-event trace gives the
-    per-kernel split."""
+    per-kernel split.  Each head has a first-slot entry (kvb_cache.start; its
+    slots form a ring) unless --no-start: eviction then shifts the shorter side of
+    the evicted slot (the rows before it move up one slot when that side is shorter)
+    instead of always the rows after it."""
     import dataclasses
 
     import torch
@@ -109,6 +112,8 @@ def steady_bench(args):
     kvs, qs = [], []
     for layer in range(L):
         d = synth.device_cache(w, layer, n=M, cap=M + 32)
+        if not args.no_start:
+            d["start"] = torch.zeros((B, w.hkv), dtype=torch.int32, device="cuda")
         kvs.append(kvb.KVCache.from_dict(d))
         qs.append(synth.device_queries(w, layer))
     out = torch.empty((B, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
@@ -160,12 +165,13 @@ def steady_bench(args):
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    nsteps = args.steps
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(nsteps):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / nsteps
     assert bool((nev == 1).all()), "steady state: one eviction per head and layer"
     # eager steps with the kernel trace
     kvb.trace_enable(16 * L * args.steps + 64, ("attn_split", "attn_merge", "append",
@@ -186,11 +192,12 @@ def steady_bench(args):
     print(json.dumps({
         "metric": "steady-state bounded-KV decode steps/s (evict 1 of M+1 per layer and step)",
         "value": round(1000.0 / ms, 3), "unit": "decode steps/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "steps": nsteps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True,
-                   "schedule": "deferred" if deferred else "both_beside"},
+                   "schedule": "deferred" if deferred else "both_beside",
+                   "head_start": not args.no_start},
         "eager_ms_per_step": round(eager_ms, 4), "kernel_us_eager": split,
         "attention_bytes_per_layer": attn_b}), flush=True)
 
@@ -448,6 +455,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
+    ap.add_argument("--no-start", action="store_true",
+                    help="steady state: heads without a first-slot entry (every eviction "
+                         "shifts the rows after the evicted slot)")
     ap.add_argument("--steady", action="store_true",
                     help="time the steady-state decode loop instead: every KV head holds M "
                          "tokens, each step appends one and evicts one (one JSON line)")

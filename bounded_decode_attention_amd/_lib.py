@@ -23,7 +23,8 @@ class _Cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("log_beta", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("len", ctypes.c_void_p), ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32),
-                ("cap", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("cap", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("start", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -122,9 +123,12 @@ class KVCache:
     log_beta  [B][Hkv][cap] float32, or None (beta == 1)
     pos       [B][Hkv][cap] int32
     length    [B][Hkv] int32 (device)
+    start     [B][Hkv] int32 (device) first live slot per head, or None (all 0);
+              eviction then compacts each head toward whichever end moves fewer
+              rows and updates start
     """
 
-    def __init__(self, k, v, log_beta, pos, length):
+    def __init__(self, k, v, log_beta, pos, length, start=None):
         _need(k, "k")
         _need(v, "v", k.dtype)
         if k.dtype not in (torch.bfloat16, torch.float32):
@@ -140,16 +144,22 @@ class KVCache:
         _need(length, "length", torch.int32)
         if tuple(pos.shape) != (B, H, cap) or tuple(length.shape) != (B, H):
             raise ValueError("pos must be [B][Hkv][cap], length [B][Hkv]")
+        if start is not None:
+            _need(start, "start", torch.int32)
+            if tuple(start.shape) != (B, H):
+                raise ValueError("start must be [B][Hkv]")
         self.k, self.v, self.log_beta, self.pos, self.length = k, v, log_beta, pos, length
+        self.start = start
         self.B, self.Hkv, self.cap, self.D = B, H, cap, D
         self.dtype = KVB_BF16 if k.dtype == torch.bfloat16 else KVB_F32
         self._desc = _Cache(k.data_ptr(), v.data_ptr(),
                             None if log_beta is None else log_beta.data_ptr(),
-                            pos.data_ptr(), length.data_ptr(), B, H, cap, D, self.dtype)
+                            pos.data_ptr(), length.data_ptr(), B, H, cap, D, self.dtype,
+                            None if start is None else start.data_ptr())
 
     @classmethod
     def from_dict(cls, d):
-        return cls(d["k"], d["v"], d.get("log_beta"), d["pos"], d["len"])
+        return cls(d["k"], d["v"], d.get("log_beta"), d["pos"], d["len"], d.get("start"))
 
     @property
     def desc(self):

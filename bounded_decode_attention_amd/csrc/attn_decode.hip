@@ -39,6 +39,7 @@ struct AttnArgs {
   const float* log_beta;
   const int32_t* pos;
   const int32_t* len;
+  const int32_t* start;  // [U] first live slot per head, or null (0)
   const void* q;
   const int32_t* t;
   float* part_a;   // [B][Hq][P][D]
@@ -61,16 +62,18 @@ struct AttnArgs {
 
 // ------------------------------------------------------------------ append
 __global__ __launch_bounds__(64) void kv_append(void* k, void* v, float* log_beta, int32_t* pos,
-                                                int32_t* len, int32_t cap, int32_t row_words,
-                                                const void* k_new, const void* v_new,
-                                                const float* lb_new, const int32_t* t,
-                                                int32_t Hkv, int32_t* status) {
+                                                int32_t* len, const int32_t* start, int32_t cap,
+                                                int32_t row_words, const void* k_new,
+                                                const void* v_new, const float* lb_new,
+                                                const int32_t* t, int32_t Hkv, int32_t* status) {
   const int u = blockIdx.x;
-  const int s = len[u];
-  if (s >= cap) {
+  const int s0 = head_start(start, u);
+  const int n = len[u];
+  if (n >= cap) {
     if (threadIdx.x == 0) status[0] = KVB_ECAPACITY;
     return;
   }
+  const int s = s0 + n < cap ? s0 + n : s0 + n - cap;  // slot of the new token
   const size_t dst = ((size_t)u * cap + s) * row_words;
   const uint32_t* kn = (const uint32_t*)k_new + (size_t)u * row_words;
   const uint32_t* vn = (const uint32_t*)v_new + (size_t)u * row_words;
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(64) void kv_append(void* k, void* v, float* log_bet
     if (log_beta) log_beta[(size_t)u * cap + s] = lb_new[u];
   }
   __syncthreads();
-  if (threadIdx.x == 0) len[u] = s + 1;
+  if (threadIdx.x == 0) len[u] = n + 1;
 }
 
 // Token range of split p of a head with n live tokens: whole 32-token tiles,
@@ -123,12 +126,17 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
   const int lg = lane >> 4;
   const int lc = lane & 15;
 
+  const int s0 = head_start(a.start, u);
   const int n = min(a.len[u], a.cap);
   if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
   int lo, end;
   split_range(n, p, a.P, lo, end);
   // 16-byte loads of log beta / pos need a 4-slot aligned head base
-  const bool vec_ok = ((size_t)u * a.cap & 3) == 0;
+  const size_t row0 = (size_t)u * a.cap + s0;  // the head's first live slot
+  const bool vec_ok = (row0 & 3) == 0;
+  // rows at or past capu continue at the start of the head's slots
+  const int capu = a.cap - s0;
+  auto wr = [&](int r) { return r < capu ? r : r - a.cap; };
 
   // q as the B operand: column lc is head lc (lc < G), head lc-G (G <= lc < 2G), or 0.
   const int hcol = lc < G ? lc : (lc < 2 * G ? lc - G : -1);
@@ -143,10 +151,10 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
     }
   }
 
-  const uint16_t* kb = (const uint16_t*)a.k + (size_t)u * a.cap * D;
-  const uint16_t* vb = (const uint16_t*)a.v + (size_t)u * a.cap * D;
-  const float* lbb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
-  const int32_t* pb = a.pos + (size_t)u * a.cap;
+  const uint16_t* kb = (const uint16_t*)a.k + row0 * D;
+  const uint16_t* vb = (const uint16_t*)a.v + row0 * D;
+  const float* lbb = a.log_beta ? a.log_beta + row0 : nullptr;
+  const int32_t* pb = a.pos + row0;
   const int qpos = a.t[b];
   const float sc = a.scale_log2;
 
@@ -166,16 +174,18 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
     for (int j = 0; j < 2; ++j) {
       int row = tb + 16 * j + lc;
       if (!full) row = min(row, last);
+      row = wr(row);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kr[j][kk] = *(const u32x4*)(kb + (size_t)row * D + 32 * kk + 8 * lg);
+        kr[j][kk] = *(const u32x4*)(kb + (ptrdiff_t)row * D + 32 * kk + 8 * lg);
     }
     u32x4 vr[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int row = tb + RPI * i + lane / CH;
       if (!full) row = min(row, last);
-      vr[i] = *(const u32x4*)(vb + (size_t)row * D + 8 * (lane % CH));
+      row = wr(row);
+      vr[i] = *(const u32x4*)(vb + (ptrdiff_t)row * D + 8 * (lane % CH));
     }
     float lbv[2][4];
     int pv[2][4];
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r0 = tb + 16 * j + 4 * lg;
-        if (full && vec_ok) {
+        if (full && vec_ok && r0 + 4 <= capu) {
           const f32x4 l4 = *(const f32x4*)(lbb + r0);
           const i32x4 p4 = *(const i32x4*)(pb + r0);
 #pragma unroll
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = min(r0 + r, last);
+            const int row = wr(min(r0 + r, last));
             lbv[j][r] = lbb[row];
             pv[j][r] = pb[row];
           }
@@ -334,17 +344,20 @@ struct KTile {
 };
 
 // Issues every load of one tile with no branches.  Rows past the split end are
-// clamped to its last row (cache hits); with VEC (capacity % 4 == 0) log beta and
-// pos are read four at a time from base min(r0, cap - 4), which equals r0 for every
-// slot below cap.
+// clamped to its last row (cache hits); with VEC (capacity % 4 == 0, heads at slot 0)
+// log beta and pos are read four at a time from base min(r0, cap - 4), which equals
+// r0 for every slot below cap.  Rows are relative to the head's first live slot;
+// row r lies at r - cap from it once r reaches capu = cap - first slot (the head
+// continues at the start of its slots).
 template <bool VEC, bool MOVE>
 __device__ __forceinline__ void issue_tile128(const uint16_t* kb, const uint16_t* vb,
                                               const float* lbb, const int32_t* pb, int tb,
-                                              int end, int cap, int lane, KTile& t,
+                                              int end, int capu, int cap, int lane, KTile& t,
                                               lds_u8* __restrict__ vlds, const uint32_t* tmask,
                                               const int32_t* tbase) {
   const int lg = lane >> 4, lc = lane & 15;
   const int last = end - 1;
+  auto wr = [&](int r) { return r < capu ? r : r - cap; };
   if constexpr (MOVE) {
     // with the tile's own loads, so the move step adds no wait of its own
     const int tl = min(tb, last) >> 5;
@@ -353,21 +366,22 @@ __device__ __forceinline__ void issue_tile128(const uint16_t* kb, const uint16_t
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int row = min(tb + 16 * j + lc, last);
+    const int row = wr(min(tb + 16 * j + lc, last));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) t.k[j][kk] = *(const u32x4*)(kb + (size_t)row * 128 + 32 * kk + 8 * lg);
+    for (int kk = 0; kk < 4; ++kk)
+      t.k[j][kk] = *(const u32x4*)(kb + (ptrdiff_t)row * 128 + 32 * kk + 8 * lg);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = min(tb + 4 * i + lg, last);
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (size_t)row * 128 + 8 * lc),
+    const int row = wr(min(tb + 4 * i + lg, last));
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (ptrdiff_t)row * 128 + 8 * lc),
                                      (lds_void_t*)(vlds + i * kVBlk), 16, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r0 = tb + 16 * j + 4 * lg;
     if constexpr (VEC) {
-      const int rb = min(r0, cap - 4);
+      const int rb = min(r0, capu - 4);
       const f32x4 l4 = *(const f32x4*)(lbb + rb);
       const i32x4 p4 = *(const i32x4*)(pb + rb);
 #pragma unroll
@@ -378,7 +392,7 @@ __device__ __forceinline__ void issue_tile128(const uint16_t* kb, const uint16_t
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = min(r0 + r, last);
+        const int row = wr(min(r0 + r, last));
         t.lb[j][r] = lbb[row];
         t.ps[j][r] = pb[row];
       }
@@ -521,9 +535,12 @@ void attn_split_pipe128(AttnArgs a) {
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
   const int lc = lane & 15;
+  const int s0 = head_start(a.start, u);
+  const int capu = a.cap - s0;  // rows before the head wraps to the start of its slots
   const int n = min(a.len[u], a.cap);
   if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
   const int end = n;
+  const size_t row0 = (size_t)u * a.cap + s0;  // the head's first live slot
 
   const int hcol = lc < G ? lc : (lc < 2 * G ? lc - G : -1);
   u32x4 qv[4];
@@ -536,11 +553,11 @@ void attn_split_pipe128(AttnArgs a) {
       qv[kk] = hcol >= 0 ? *(const u32x4*)(qp + 32 * kk + 8 * lg) : z;
     }
   }
-  const uint16_t* kb = (const uint16_t*)a.k + (size_t)u * a.cap * 128;
-  const uint16_t* vb = (const uint16_t*)a.v + (size_t)u * a.cap * 128;
+  const uint16_t* kb = (const uint16_t*)a.k + row0 * 128;
+  const uint16_t* vb = (const uint16_t*)a.v + row0 * 128;
   // without a retention array the bias loads read pos twice (harmless, unused)
-  const int32_t* pb = a.pos + (size_t)u * a.cap;
-  const float* lbb = LB ? a.log_beta + (size_t)u * a.cap : (const float*)pb;
+  const int32_t* pb = a.pos + row0;
+  const float* lbb = LB ? a.log_beta + row0 : (const float*)pb;
   const int qpos = a.t[b];
   const float sc = a.scale_log2;
 
@@ -571,10 +588,10 @@ void attn_split_pipe128(AttnArgs a) {
     mv = a.plan.info[u].mode == MODE_EVICT;
     tmask = a.plan.tile_mask + (size_t)u * a.plan.Tc;
     tbase = a.plan.tile_base + (size_t)u * a.plan.Tc;
-    kw = (uint16_t*)a.kw + (size_t)u * a.cap * 128;
-    vw = (uint16_t*)a.vw + (size_t)u * a.cap * 128;
-    lbw = LB ? a.lbw + (size_t)u * a.cap : nullptr;
-    pw = a.posw + (size_t)u * a.cap;
+    kw = (uint16_t*)a.kw + row0 * 128;
+    vw = (uint16_t*)a.vw + row0 * 128;
+    lbw = LB ? a.lbw + row0 : nullptr;
+    pw = a.posw + row0;
   }
   auto moves = [&](const KTile& tt, const lds_u8* __restrict__ vl) {
     if (MOVE && mv) {
@@ -591,15 +608,15 @@ void attn_split_pipe128(AttnArgs a) {
     // global_load_lds transfers into the same LDS.  The scheduling barriers keep
     // the next tile's arithmetic from being hoisted above its wait.
     int tb = 32 * t_first;
-    issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb, end, a.cap, lane, tA, vbufA, tmask, tbase);
+    issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb, end, capu, a.cap, lane, tA, vbufA, tmask, tbase);
     for (int k = 0; k < (ntiles >> 1); ++k) {
       wait_vmem_all();
       moves(tA, vbufA);
-      issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + step, end, a.cap, lane, tB, vbufB, tmask, tbase);
+      issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + step, end, capu, a.cap, lane, tB, vbufB, tmask, tbase);
       compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
       wait_vmem_all();
       moves(tB, vbufB);
-      issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + 2 * step, end, a.cap, lane, tA, vbufA, tmask,
+      issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + 2 * step, end, capu, a.cap, lane, tA, vbufA, tmask,
                                tbase);
       compute_tile128<G>(tB, vbufB, tb + step, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
       tb += 2 * step;
@@ -677,10 +694,12 @@ __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
   const int g = u - b * a.Hkv;
   const int lane = threadIdx.x;
   const int D = a.D, G = a.G;
+  const int s0 = head_start(a.start, u);
   const int n = min(a.len[u], a.cap);
   if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
   int lo, end;
   split_range(n, p, a.P, lo, end);
+  const size_t row0 = (size_t)u * a.cap + s0;  // the head's first live slot
 
   auto ld = [](const T* ptr) -> float {
     if constexpr (sizeof(T) == 2) return bf16_bits_to_f32(*(const uint16_t*)ptr);
@@ -705,24 +724,26 @@ __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < DPL; ++j) acc[h][j] = 0.f;
   }
-  const T* kb = (const T*)a.k + (size_t)u * a.cap * D;
-  const T* vb = (const T*)a.v + (size_t)u * a.cap * D;
-  const float* lbb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
-  const int32_t* pb = a.pos + (size_t)u * a.cap;
+  const T* kb = (const T*)a.k + row0 * D;
+  const T* vb = (const T*)a.v + row0 * D;
+  const float* lbb = a.log_beta ? a.log_beta + row0 : nullptr;
+  const int32_t* pb = a.pos + row0;
   const int qpos = a.t[b];
 
   for (int tok = lo; tok < end; ++tok) {
+    // the head continues at the start of its slots past the end
+    const ptrdiff_t r = tok < a.cap - s0 ? tok : tok - a.cap;
     float kf[DPL], vf[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; ++j) {
       const int d = lane + 64 * j;
-      kf[j] = d < D ? ld(kb + (size_t)tok * D + d) : 0.f;
-      vf[j] = d < D ? ld(vb + (size_t)tok * D + d) : 0.f;
+      kf[j] = d < D ? ld(kb + r * D + d) : 0.f;
+      vf[j] = d < D ? ld(vb + r * D + d) : 0.f;
     }
     float bias = 0.f;
     if (lbb) {
-      const int dd = qpos - pb[tok];
-      bias = dd != 0 ? (float)dd * lbb[tok] : 0.f;
+      const int dd = qpos - pb[r];
+      bias = dd != 0 ? (float)dd * lbb[r] : 0.f;
     }
 #pragma unroll
     for (int h = 0; h < MAXG; ++h) {
@@ -785,6 +806,7 @@ struct NewTok {
   float* log_beta;
   int32_t* pos;
   int32_t* len;
+  const int32_t* start;  // [U] first live slot per head, or null (0)
   int32_t* status;
   int32_t cap, Hkv, elem;
   float scale;         // natural-log scale of q.k
@@ -887,7 +909,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     if (!incl) {
       if (tid == 0) nt.status[0] = KVB_ECAPACITY;
     } else {
-      const int s0 = nt.n_rec[u];
+      const int n0 = nt.n_rec[u];
+      int s0 = head_start(nt.start, u) + n0;  // slot of the decode token
+      if (s0 >= nt.cap) s0 -= nt.cap;
       const int words = D * nt.elem / 4;
       const size_t dst = ((size_t)u * nt.cap + s0) * words;
       for (int w = tid; w < words; w += kMergeThreads) {
@@ -897,7 +921,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
       if (tid == 0) {
         nt.pos[(size_t)u * nt.cap + s0] = nt.t[u / nt.Hkv];
         if (nt.log_beta) nt.log_beta[(size_t)u * nt.cap + s0] = nt.lb_new[u];
-        nt.len[u] = s0 + 1;
+        nt.len[u] = n0 + 1;
       }
     }
   }
@@ -927,6 +951,12 @@ static bool mfma_supported(const kvb_cache* c, int G) {
          (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
+// 16-byte loads of log beta and pos: every head's first live slot must be a
+// multiple of 4 (per-head starts are not known on the host).
+static bool vec_bias_loads(const kvb_cache* c) {
+  return c->cap % 4 == 0 && c->cap >= 4 && c->start == nullptr;
+}
+
 template <int D, int G>
 static void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((attn_split_mfma<D, G>), grid, dim3(64), 0, s, a);
@@ -937,7 +967,7 @@ static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s
   if (mfma_supported(c, a.G)) {
 #define KVB_PIPE_CASE(GG)                                                                  \
   if (c->D == 128 && a.G == GG) {                                                          \
-    const bool lb = c->log_beta != nullptr, vec = c->cap % 4 == 0 && c->cap >= 4;         \
+    const bool lb = c->log_beta != nullptr, vec = vec_bias_loads(c);                      \
     if (lb && vec) hipLaunchKernelGGL((attn_split_pipe128<GG, true, true, false>), grid, dim3(64), 0, s, a);   \
     else if (lb) hipLaunchKernelGGL((attn_split_pipe128<GG, true, false, false>), grid, dim3(64), 0, s, a);   \
     else if (vec) hipLaunchKernelGGL((attn_split_pipe128<GG, false, true, false>), grid, dim3(64), 0, s, a);  \
@@ -1009,7 +1039,8 @@ extern "C" int32_t kv_append(const kvb_cache* cache, const void* k_new, const vo
   const int elem = cache->dtype == KVB_BF16 ? 2 : 4;
   TraceScope tr(kTrAppend, s);
   hipLaunchKernelGGL(kv_append, dim3(cache->B * cache->Hkv), dim3(64), 0, s, cache->k, cache->v,
-                     cache->log_beta, cache->pos, cache->len, cache->cap, cache->D * elem / 4,
+                     cache->log_beta, cache->pos, cache->len, cache->start, cache->cap,
+                     cache->D * elem / 4,
                      k_new, v_new, log_beta_new, t, cache->Hkv, (int32_t*)ws);
   return launch_status();
 }
@@ -1040,6 +1071,7 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   a.log_beta = cache->log_beta;
   a.pos = cache->pos;
   a.len = cache->len;
+  a.start = cache->start;
   a.q = q;
   a.t = t;
   a.part_a = (float*)((char*)ws + kWsHeader);
@@ -1075,6 +1107,7 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
     nt.log_beta = cache->log_beta;
     nt.pos = cache->pos;
     nt.len = cache->len;
+    nt.start = cache->start;
     nt.status = (int32_t*)ws;
     nt.cap = cache->cap;
     nt.Hkv = cache->Hkv;
@@ -1139,8 +1172,10 @@ extern "C" int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q,
   if (!ws_evict || ws_evict_bytes < kv_evict_workspace(cache, M)) return KVB_EWORKSPACE;
   if ((st = check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
+  // (per-head starts: the unfused path)
   const bool fused = cache->dtype == KVB_BF16 && cache->D == 128 &&
-                     (G == 1 || G == 2 || G == 4 || G == 8) && P >= 2 && plan_in_lds(cache);
+                     (G == 1 || G == 2 || G == 4 || G == 8) && P >= 2 && plan_in_lds(cache) &&
+                     cache->start == nullptr;
   if (!fused) {
     // same result through the unfused kernels: attention, then the planned moves
     if (phase == 1) return KVB_OK;
@@ -1164,6 +1199,7 @@ extern "C" int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q,
   a.log_beta = cache->log_beta;
   a.pos = cache->pos;
   a.len = cache->len;
+  a.start = cache->start;
   a.q = q;
   a.t = t;
   a.part_a = (float*)((char*)ws + kWsHeader);

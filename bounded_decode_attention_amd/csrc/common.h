@@ -104,13 +104,21 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Per-head eviction plan header (workspace), written by the planners.
 enum { MODE_NOOP = 0, MODE_EVICT = 1, MODE_ERASE = 2 };
+// First live slot of head u: live slots are start[u] .. start[u] + len[u] - 1
+// (every head starts at slot 0 without a start array).
+__device__ __forceinline__ int head_start(const int32_t* start, int u) {
+  return start ? start[u] : 0;
+}
+
 struct UnitInfo {
   uint64_t kstar;  // ordered 64-bit key of the threshold element
   int32_t sstar;   // its slot
   int32_t mode;
   int32_t n;       // live slots before
   int32_t kept;    // live slots after
-  int32_t pad[2];
+  int32_t nstart;  // first live slot after the compaction
+  int32_t ostart;  // first live slot before it (the start array is rewritten by the
+                   // compaction, so its workgroups read this copy)
 };
 static_assert(sizeof(UnitInfo) == 32, "UnitInfo layout");
 

@@ -42,8 +42,19 @@ constexpr int kPerThread = kChunk / kChunkThreads;
 constexpr int kSelThreads = 1024;
 
 // ---------------------------------------------------------------- keys
-__device__ __forceinline__ double retention_key(const float* lb, const int32_t* ps, int i,
-                                                int tq) {
+// A head's per-slot array seen from its first live slot: index i is i slots past
+// it, continuing at the start of the head's slots once i reaches capu = cap - first
+// slot.
+template <typename T>
+struct Ring {
+  T* p;
+  int capu, cap;
+  __device__ __forceinline__ T& operator[](int i) const { return p[i < capu ? i : i - cap]; }
+  __device__ __forceinline__ explicit operator bool() const { return p != nullptr; }
+};
+
+template <typename LB, typename PS>
+__device__ __forceinline__ double retention_key(const LB& lb, const PS& ps, int i, int tq) {
   if (!lb) return 0.0;
   const int d = tq - ps[i];
   if (d == 0) return 0.0;
@@ -130,7 +141,8 @@ __device__ __forceinline__ int select_bucket(const uint32_t* hist, int nb, int& 
 // ---------------------------------------------------------------- select
 __global__ __launch_bounds__(kSelThreads) void evict_select(const float* lb_all,
                                                             const int32_t* pos_all,
-                                                            const int32_t* len, int cap,
+                                                            const int32_t* len,
+                                                            const int32_t* start, int cap,
                                                             int Hkv, const int32_t* tq, int M,
                                                             UnitInfo* info, int32_t* n_out) {
   __shared__ uint32_t hist[2048];
@@ -141,6 +153,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_select(const float* lb_all,
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
+  const int s0 = head_start(start, u);
   const int n = min(len[u], cap);
   if (tid == 0) {
     out[0] = 0;
@@ -149,14 +162,14 @@ __global__ __launch_bounds__(kSelThreads) void evict_select(const float* lb_all,
   }
   if (n <= M) {
     if (tid == 0) {
-      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, {0, 0}};
+      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, s0, s0};
       info[u] = z;
       if (n_out) n_out[u] = 0;
     }
     return;
   }
-  const float* lb = lb_all ? lb_all + (size_t)u * cap : nullptr;
-  const int32_t* ps = pos_all + (size_t)u * cap;
+  const Ring<const float> lb{lb_all ? lb_all + (size_t)u * cap + s0 : nullptr, cap - s0, cap};
+  const Ring<const int32_t> ps{pos_all + (size_t)u * cap + s0, cap - s0, cap};
   const int tpos = tq[u / Hkv];
   int r = n - M;  // 1-based rank of the last evicted element
 
@@ -239,9 +252,26 @@ __global__ __launch_bounds__(kSelThreads) void evict_select(const float* lb_all,
     seen += total;
   }
   if (tid == 0) {
-    UnitInfo v = {K, sstar, MODE_EVICT, n, M, {0, 0}};
+    UnitInfo v = {K, sstar, MODE_EVICT, n, M, s0, s0};
     info[u] = v;
   }
+}
+
+// ---------------------------------------------------------------- staging rule
+// Kept row j moves from slot os + src (os: the head's first live slot before the
+// compaction) to slot ns + j (ns: after it).  compact_move's workgroups own groups
+// of mr destinations and write only those; a source that lies inside another
+// group's destination range could be overwritten before it is read, so it is
+// copied to scratch (by destination index) before any move starts.  Moving toward
+// the head's first slot (ns <= os, src >= j) the endangered sources lie in later
+// groups' ranges, below ns + kept; moving toward the end (ns > os, src <= j) in
+// earlier groups' ranges, at or above ns.
+__device__ __forceinline__ bool staged_row(int os, int ns, int src, int j, int kept, int mr) {
+  const int sa = os + src, da = ns + j;
+  if (sa == da) return false;
+  const int g0 = ns + (j / mr) * mr;  // the group's first destination slot
+  if (ns <= os) return sa >= g0 + mr && sa < ns + kept;
+  return sa < g0 && sa >= ns;
 }
 
 // ---------------------------------------------------------------- fused LDS planner
@@ -257,6 +287,7 @@ struct PlanArgs {
   const float* log_beta;
   const int32_t* pos;
   const int32_t* len;
+  const int32_t* start;  // [U] or null
   const int32_t* tq;
   UnitInfo* info;
   int32_t* keep_src;
@@ -284,10 +315,14 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   __shared__ int out[4];
   __shared__ unsigned long long mm[2];
   __shared__ int ncand, nflag, nstage, ncopy;
+  __shared__ int efirst, elast;  // first and last evicted slot
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
+  const int s0 = head_start(a.start, u);
+  const size_t row0 = (size_t)u * a.cap + s0;  // the head's first live slot
+  const int capu = a.cap - s0;                 // slots before the head wraps
   const int n = min(a.len[u], a.cap);
   const int M = a.M;
   if (tid == 0) {
@@ -300,17 +335,19 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
     nflag = 0;
     nstage = 0;
     ncopy = 0;
+    efirst = 0x7FFFFFFF;
+    elast = -1;
   }
   if (n <= M) {
     if (tid == 0) {
-      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, {0, 0}};
+      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, s0, s0};
       a.info[u] = z;
       if (a.n_out) a.n_out[u] = 0;
     }
     return;
   }
-  const float* lb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
-  const int32_t* ps = a.pos + (size_t)u * a.cap;
+  const Ring<const float> lb{a.log_beta ? a.log_beta + row0 : nullptr, capu, a.cap};
+  const Ring<const int32_t> ps{a.pos + row0, capu, a.cap};
   const int tpos = a.tq[u / a.Hkv];
   int r = n - M;
   auto key32 = [&](float l, int p) -> uint32_t {
@@ -322,9 +359,14 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   // loads are issued before any key is formed (the loop is latency bound otherwise).
   for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
   __syncthreads();
-  if (a.vec) {
-    // 16-byte loads: slots 4j .. 4j + 3 (every head's rows start 16-byte aligned)
-    const int nq = (n + 3) >> 2;
+  if (a.vec && n <= capu) {
+    // 16-byte loads of aligned quads (capacity % 4 == 0, so a quad holding a live
+    // slot lies inside the head's rows; the head does not wrap): quad j holds slots
+    // 4j - a0 .. 4j - a0 + 3
+    const int a0 = (int)(row0 & 3);
+    const float* lbq = lb ? lb.p - a0 : nullptr;
+    const int32_t* psq = ps.p - a0;
+    const int nq = (n + a0 + 3) >> 2;
     constexpr int kQ = 8;
     for (int j0 = tid; j0 < nq; j0 += kQ * kSelThreads) {
       f32x4 l4[kQ];
@@ -332,16 +374,16 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
 #pragma unroll
       for (int e = 0; e < kQ; ++e) {
         const int j = min(j0 + e * kSelThreads, nq - 1);
-        l4[e] = lb ? *(const f32x4*)(lb + 4 * j) : f32x4{0.f, 0.f, 0.f, 0.f};
-        p4[e] = *(const i32x4*)(ps + 4 * j);
+        l4[e] = lbq ? *(const f32x4*)(lbq + 4 * j) : f32x4{0.f, 0.f, 0.f, 0.f};
+        p4[e] = *(const i32x4*)(psq + 4 * j);
       }
 #pragma unroll
       for (int e = 0; e < kQ; ++e) {
         const int j = j0 + e * kSelThreads;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int i = 4 * j + c;
-          if (j < nq && i < n) {
+          const int i = 4 * j + c - a0;
+          if (j < nq && i >= 0 && i < n) {
             const uint32_t k32 = key32(l4[e][c], p4[e][c]);
             keys[skew(i)] = k32;
             atomicAdd(&hist[k32 >> 21], 1u);
@@ -556,15 +598,38 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   for (int tl = tl0; tl < tl1; ++tl) kc += __popc(tmask[tl]);
   int kept_all;
   int dst = block_excl_scan<kSelThreads>(kc, smem, kept_all);
+  int ef = 0x7FFFFFFF, el = -1;
   for (int tl = tl0; tl < tl1; ++tl) {
     const uint32_t m = tmask[tl];
     hist[tl] = (uint32_t)dst;
     a.tile_mask[(size_t)u * a.Tc + tl] = m;
     a.tile_base[(size_t)u * a.Tc + tl] = dst;
     dst += __popc(m);
+    const int live = min(32, n - 32 * tl);
+    const uint32_t evb = ~m & (live == 32 ? 0xFFFFFFFFu : ((1u << live) - 1u));
+    if (evb) {
+      ef = min(ef, 32 * tl + __ffs(evb) - 1);
+      el = max(el, 32 * tl + 31 - __clz(evb));
+    }
+  }
+  if (el >= 0) {
+    atomicMin(&efirst, ef);
+    atomicMax(&elast, el);
   }
   __syncthreads();
   const int kept = min(kept_all, a.Mk);
+  // With a start array the head is compacted toward whichever end moves fewer
+  // rows: toward its first slot the kept rows after the first evicted slot move,
+  // toward its last slot the kept rows before the last evicted slot (the first
+  // slot then advances by the evicted count, around the end of the head's slots).
+  // nstart is kept unwrapped (s0 <= nstart < s0 + cap) for the staging rule.
+  int nstart = s0;
+  if (a.start && elast >= 0) {
+    const int nev = n - kept;
+    const int fwd = kept - efirst;
+    const int bwd = elast + 1 - nev;
+    if (bwd < fwd) nstart = s0 + nev;
+  }
   int2* slist = a.stage_list + (size_t)u * a.Mk;
   int2* clist = a.copy_list + (size_t)u * a.Mk;
   {
@@ -587,13 +652,9 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
         if ((mk[e] >> s2) & 1u) {
           if (before < a.Mk) {
             a.keep_src[(size_t)u * a.Mk + before] = i;
-            if (i != before && i < a.za) {
-              slist[atomicAdd(&nstage, 1)] = make_int2(i, before);
-              // compact_move's hazard rule: the source lies below kept and inside a
-              // later group's destination range
-              if (i < kept && i >= (before / a.move_rows + 1) * a.move_rows)
-                clist[atomicAdd(&ncopy, 1)] = make_int2(i, before);
-            }
+            if (i != before && i < a.za) slist[atomicAdd(&nstage, 1)] = make_int2(i, before);
+            if (staged_row(s0, nstart, i, before, kept, a.move_rows))
+              clist[atomicAdd(&ncopy, 1)] = make_int2(i, before);
           }
         } else if (a.evicted_pos) {
           const int ev = i - before;
@@ -610,8 +671,8 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
     const int ns = min(ncopy, a.Mk);
     const int ppr = a.row_bytes / 16;
     const int per = 2 * ppr + 1;
-    const unsigned char* kb = (const unsigned char*)a.k + (size_t)u * a.cap * a.row_bytes;
-    const unsigned char* vb = (const unsigned char*)a.v + (size_t)u * a.cap * a.row_bytes;
+    const unsigned char* kb = (const unsigned char*)a.k + row0 * a.row_bytes;
+    const unsigned char* vb = (const unsigned char*)a.v + row0 * a.row_bytes;
     constexpr int kB = 8;
     for (int q0 = tid; q0 < ns * per; q0 += kB * kSelThreads) {
       u32x4 x[kB];
@@ -627,7 +688,8 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
           if (part < 2 * ppr) {
             const bool isv = part >= ppr;
             const int pc = isv ? part - ppr : part;
-            x[e] = *(const u32x4*)((isv ? vb : kb) + (size_t)sd.x * a.row_bytes + 16 * pc);
+            const ptrdiff_t rs = sd.x < capu ? sd.x : sd.x - a.cap;
+            x[e] = *(const u32x4*)((isv ? vb : kb) + rs * a.row_bytes + 16 * pc);
             to[e] = sp + (isv ? a.row_bytes : 0) + 16 * pc;
           } else {
             x[e] = u32x4{lb ? __float_as_uint(lb[sd.x]) : 0u, (uint32_t)ps[sd.x], 0u, 0u};
@@ -648,7 +710,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
     }
   }
   if (tid == 0) {
-    UnitInfo v = {K, sstar, MODE_EVICT, n, kept, {0, 0}};
+    UnitInfo v = {K, sstar, MODE_EVICT, n, kept, nstart, s0};
     a.info[u] = v;
     a.stage_n[u] = min(nstage, a.Mk);
     if (a.n_out) a.n_out[u] = n - kept_all;
@@ -660,6 +722,7 @@ struct KeepArgs {
   const float* log_beta;
   const int32_t* pos;
   int32_t* len;
+  int32_t* start;           // [U] or null
   const int32_t* tq;
   const int32_t* ranges;    // erase: [B][R][2]
   const int32_t* n_ranges;  // erase: [B]
@@ -691,10 +754,12 @@ __device__ __forceinline__ bool in_ranges(const int32_t* rg, int nr, int p) {
 
 template <int MODE>
 __device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int n, bool* f) {
-  const int32_t* ps = a.pos + (size_t)u * a.cap;
+  const int s0 = head_start(a.start, u);
+  const size_t row0 = (size_t)u * a.cap + s0;
+  const Ring<const int32_t> ps{a.pos + row0, a.cap - s0, a.cap};
   if (MODE == MODE_EVICT) {
     const UnitInfo inf = a.info[u];
-    const float* lb = a.log_beta ? a.log_beta + (size_t)u * a.cap : nullptr;
+    const Ring<const float> lb{a.log_beta ? a.log_beta + row0 : nullptr, a.cap - s0, a.cap};
     const int tpos = a.tq[u / a.Hkv];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -736,9 +801,12 @@ __global__ __launch_bounds__(kChunkThreads) void keep_count(KeepArgs a) {
   if (threadIdx.x == 0) a.counts[(size_t)u * a.C + c] = tot;
 }
 
-__device__ __forceinline__ void copy_row_to_scratch(const KeepArgs& a, int u, int src, int dst) {
+// src: slot relative to the head's first live slot s0; dst: destination index.
+__device__ __forceinline__ void copy_row_to_scratch(const KeepArgs& a, int u, int s0, int src,
+                                                    int dst) {
   unsigned char* s = a.scratch + ((size_t)u * a.Mk + dst) * a.srow;
-  const size_t off = ((size_t)u * a.cap + src) * a.row_bytes;
+  const int slot = s0 + src < a.cap ? s0 + src : s0 + src - a.cap;
+  const size_t off = ((size_t)u * a.cap + slot) * a.row_bytes;
   const u32x4* kp = (const u32x4*)((const unsigned char*)a.k + off);
   const u32x4* vp = (const u32x4*)((const unsigned char*)a.v + off);
   const int pieces = a.row_bytes / 16;
@@ -747,8 +815,8 @@ __device__ __forceinline__ void copy_row_to_scratch(const KeepArgs& a, int u, in
     ((u32x4*)(s + a.row_bytes))[i] = vp[i];
   }
   int32_t* tail = (int32_t*)(s + 2 * a.row_bytes);
-  tail[0] = a.log_beta ? __float_as_int(a.log_beta[(size_t)u * a.cap + src]) : 0;
-  tail[1] = a.pos[(size_t)u * a.cap + src];
+  tail[0] = a.log_beta ? __float_as_int(a.log_beta[(size_t)u * a.cap + slot]) : 0;
+  tail[1] = a.pos[(size_t)u * a.cap + slot];
 }
 
 template <int MODE>
@@ -756,6 +824,7 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   __shared__ int smem[kChunkThreads / 64];
   const int u = blockIdx.y, c = blockIdx.x;
   if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
+  const int s0 = head_start(a.start, u);
   const int n = min(a.len[u], a.cap);
   // kept rows before this chunk, and in total
   int before = 0, all = 0;
@@ -768,6 +837,8 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   all = block_sum<kChunkThreads>(all, smem);
   if (c == 0 && threadIdx.x == 0) {
     a.info[u].kept = all;
+    a.info[u].nstart = s0;
+    a.info[u].ostart = s0;
     if (MODE == MODE_ERASE) a.info[u].mode = MODE_ERASE;
     if (a.n_out) a.n_out[u] = n - all;
   }
@@ -781,7 +852,7 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   for (int e = 0; e < kPerThread; ++e) cnt += f[e] ? 1 : 0;
   int total;
   int dst = before + block_excl_scan<kChunkThreads>(cnt, smem, total);
-  const int32_t* ps = a.pos + (size_t)u * a.cap;
+  const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const int i = i0 + e;
@@ -789,8 +860,7 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
     if (f[e]) {
       if (dst < a.Mk) {  // always true when the threshold is consistent
         a.keep_src[(size_t)u * a.Mk + dst] = i;
-        if (i != dst && i < all && i >= (dst / a.move_rows + 1) * a.move_rows)
-          copy_row_to_scratch(a, u, i, dst);
+        if (staged_row(s0, s0, i, dst, all, a.move_rows)) copy_row_to_scratch(a, u, s0, i, dst);
       }
       ++dst;
     } else if (MODE == MODE_EVICT && a.evicted_pos) {
@@ -823,18 +893,29 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
     const UnitInfo inf = a.info[u];
     if (check_mode && inf.mode == MODE_NOOP) continue;
     const int kept = min(inf.kept, a.Mk);
-    if (ch == 0 && tid == 0) a.len[u] = kept;
+    const int os = inf.ostart, ns = inf.nstart;
+    // slots are kept unwrapped below (< 2 cap); addresses wrap
+    auto wrap = [&](int x) { return x < a.cap ? x : x - a.cap; };
+    if (ch == 0 && tid == 0) {
+      a.len[u] = kept;
+      if (a.start) a.start[u] = wrap(ns);
+    }
     const int j0 = ch * a.move_rows;
     if (j0 >= kept) continue;
     const int rows = min(a.move_rows, kept - j0);
     const int32_t* ks = a.keep_src + (size_t)u * a.Mk;
-    // src - dst never decreases along the destinations: if the group's last row
-    // stays in place, every row of the group does
-    if (ks[j0 + rows - 1] == j0 + rows - 1) continue;
+    // (os + src) - (ns + j) never decreases along the destinations and ends at or
+    // above 0 toward the first slot, at or below 0 toward the end: a group whose
+    // last (first) row stays in place moves no row
+    if (ns <= os ? os + ks[j0 + rows - 1] == ns + j0 + rows - 1 : os + ks[j0] == ns + j0) continue;
     const unsigned char* scr = a.scratch + (size_t)u * a.Mk * a.srow;
     unsigned char* tb = (unsigned char*)(isv ? a.v : a.k) + (size_t)u * a.cap * a.row_bytes;
     float* lbb = a.log_beta ? (float*)a.log_beta + (size_t)u * a.cap : nullptr;
     int32_t* pb = (int32_t*)a.pos + (size_t)u * a.cap;
+    // this group's staged sources (staged_row for the group's rows): the slots of
+    // the other groups' destinations that can be overwritten first
+    const int st_lo = ns <= os ? ns + j0 + a.move_rows : ns;
+    const int st_hi = ns <= os ? ns + kept : ns + j0;
 
     int src[kMovePieces];
 #pragma unroll
@@ -842,42 +923,42 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
       const int row = r0 + q * rpp;
       src[q] = (r0 < rpp && row < rows) ? ks[j0 + row] : -1;
     }
+    bool mv[kMovePieces];  // this piece's row moves
     u32x4 buf[kMovePieces];
 #pragma unroll
     for (int q = 0; q < kMovePieces; ++q) {
       const int j = j0 + r0 + q * rpp;
-      if (src[q] < 0 || src[q] == j) {
-        src[q] = -1;
-        continue;
-      }
-      const bool staged = src[q] < kept && src[q] >= j0 + a.move_rows;
+      const int sa = os + src[q];
+      mv[q] = src[q] >= 0 && sa != ns + j;
+      const bool staged = sa >= st_lo && sa < st_hi;
       const unsigned char* from =
           staged ? scr + (size_t)j * a.srow + (isv ? a.row_bytes : 0) + 16 * pc
-                 : tb + (size_t)src[q] * a.row_bytes + 16 * pc;
-      buf[q] = __builtin_nontemporal_load((const u32x4*)from);
+                 : tb + (size_t)wrap(sa) * a.row_bytes + 16 * pc;
+      buf[q] = mv[q] ? __builtin_nontemporal_load((const u32x4*)from) : u32x4{0u, 0u, 0u, 0u};
     }
     int32_t tail_lb = 0, tail_pos = 0, tail_dst = -1;
     if (tid < rows) {
       const int j = j0 + tid;
-      const int s = ks[j];
-      if (s != j) {
-        if (s < kept && s >= j0 + a.move_rows) {
+      const int sr = ks[j];
+      if (os + sr != ns + j) {
+        if (os + sr >= st_lo && os + sr < st_hi) {
           const int32_t* tl = (const int32_t*)(scr + (size_t)j * a.srow + 2 * a.row_bytes);
           tail_lb = tl[0];
           tail_pos = tl[1];
         } else {
-          tail_lb = lbb ? __float_as_int(lbb[s]) : 0;
-          tail_pos = pb[s];
+          tail_lb = lbb ? __float_as_int(lbb[wrap(os + sr)]) : 0;
+          tail_pos = pb[wrap(os + sr)];
         }
-        tail_dst = j;
+        tail_dst = wrap(ns + j);
       }
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kMovePieces; ++q) {
-      if (src[q] < 0) continue;
       const int j = j0 + r0 + q * rpp;
-      __builtin_nontemporal_store(buf[q], (u32x4*)(tb + (size_t)j * a.row_bytes + 16 * pc));
+      if (mv[q])
+        __builtin_nontemporal_store(buf[q],
+                                    (u32x4*)(tb + (size_t)wrap(ns + j) * a.row_bytes + 16 * pc));
     }
     if (tail_dst >= 0) {
       if (lbb) lbb[tail_dst] = __int_as_float(tail_lb);
@@ -950,6 +1031,7 @@ static KeepArgs keep_args(const kvb_cache* c, const CompactLayout& L, void* ws) 
   a.log_beta = c->log_beta;
   a.pos = c->pos;
   a.len = c->len;
+  a.start = c->start;
   a.info = (UnitInfo*)(w + L.info);
   a.counts = (int32_t*)(w + L.counts);
   a.keep_src = (int32_t*)(w + L.keep_src);
@@ -1009,6 +1091,7 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     pa.log_beta = cache->log_beta;
     pa.pos = cache->pos;
     pa.len = cache->len;
+    pa.start = cache->start;
     pa.tq = t;
     pa.info = a.info;
     pa.keep_src = a.keep_src;
@@ -1041,7 +1124,8 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     {
       TraceScope tr(kTrEvictSelect, s);
       hipLaunchKernelGGL(evict_select, dim3(cache->B * cache->Hkv), dim3(kSelThreads), 0, s,
-                         cache->log_beta, cache->pos, cache->len, cache->cap, cache->Hkv, t, M,
+                         cache->log_beta, cache->pos, cache->len, cache->start, cache->cap,
+                         cache->Hkv, t, M,
                          a.info, n_evicted);
     }
     launch_keep_chunks(cache, a, MODE_EVICT, s);
@@ -1056,36 +1140,60 @@ bool plan_in_lds(const kvb_cache* c) {
   return lds_keys <= plan_lds_limit() && (c->cap + 31) / 32 <= kCand;
 }
 
-// Copies every row of the stage list (kept rows below za that move) to scratch, by
-// destination, for the fused apply; one workgroup per (head, 64 entries).
-__global__ __launch_bounds__(256) void fused_stage_copy(const UnitInfo* info, const int32_t* stage_n,
-                                                        const int2* stage_list, unsigned char* scratch,
-                                                        const void* k, const void* v,
-                                                        const float* log_beta, const int32_t* pos,
-                                                        int cap, int Mk, int srow, int row_bytes) {
+// Copies the stage list (kept rows below za that move) to scratch by destination
+// index, for the fused apply: one workgroup per (head, 64 entries); sources are
+// slots from the head's first live slot.  Each thread issues a batch of loads
+// before storing any.
+__global__ __launch_bounds__(256) void stage_copy(const UnitInfo* info, const int32_t* count,
+                                                  const int2* list, unsigned char* scratch,
+                                                  const void* k, const void* v,
+                                                  const float* log_beta, const int32_t* pos,
+                                                  int cap, int Mk, int srow, int row_bytes) {
   const int u = blockIdx.y;
-  if (info[u].mode != MODE_EVICT) return;
-  const int ns = min(stage_n[u], Mk);
+  const UnitInfo inf = info[u];
+  if (inf.mode != MODE_EVICT) return;
+  const int ns = min(count[u], Mk);
   const int e0 = blockIdx.x * 64;
   if (e0 >= ns) return;
   const int ppr = row_bytes / 16, per = 2 * ppr + 1;
-  const int e1 = min(ns, e0 + 64);
-  const unsigned char* kb = (const unsigned char*)k + (size_t)u * cap * row_bytes;
-  const unsigned char* vb = (const unsigned char*)v + (size_t)u * cap * row_bytes;
-  const int2* sl = stage_list + (size_t)u * Mk;
-  for (int q = threadIdx.x; q < (e1 - e0) * per; q += 256) {
-    const int en = e0 + q / per, part = q % per;
-    const int2 sd = sl[en];
-    unsigned char* sp = scratch + ((size_t)u * Mk + sd.y) * srow;
-    if (part < 2 * ppr) {
-      const bool isv = part >= ppr;
-      const int pc = isv ? part - ppr : part;
-      *(u32x4*)(sp + (isv ? row_bytes : 0) + 16 * pc) =
-          *(const u32x4*)((isv ? vb : kb) + (size_t)sd.x * row_bytes + 16 * pc);
-    } else {
-      int32_t* tail = (int32_t*)(sp + 2 * row_bytes);
-      tail[0] = log_beta ? __float_as_int(log_beta[(size_t)u * cap + sd.x]) : 0;
-      tail[1] = pos[(size_t)u * cap + sd.x];
+  const int total = (min(ns, e0 + 64) - e0) * per;
+  const size_t row0 = (size_t)u * cap + inf.ostart;
+  const unsigned char* kb = (const unsigned char*)k + row0 * row_bytes;
+  const unsigned char* vb = (const unsigned char*)v + row0 * row_bytes;
+  const int2* sl = list + (size_t)u * Mk;
+  constexpr int kB = 9;  // 64 rows of 33 pieces (D = 128 bf16) in one batch
+  for (int q0 = threadIdx.x; q0 < total; q0 += kB * 256) {
+    u32x4 x[kB];
+    unsigned char* to[kB];
+    bool tail[kB];
+#pragma unroll
+    for (int e = 0; e < kB; ++e) {
+      const int q = q0 + e * 256;
+      to[e] = nullptr;
+      tail[e] = false;
+      if (q < total) {
+        const int en = e0 + q / per, part = q - (q / per) * per;
+        const int2 sd = sl[en];
+        unsigned char* sp = scratch + ((size_t)u * Mk + sd.y) * srow;
+        const ptrdiff_t rs = inf.ostart + sd.x < cap ? sd.x : sd.x - cap;  // around the end
+        if (part < 2 * ppr) {
+          const bool isv = part >= ppr;
+          const int pc = isv ? part - ppr : part;
+          x[e] = *(const u32x4*)((isv ? vb : kb) + rs * row_bytes + 16 * pc);
+          to[e] = sp + (isv ? row_bytes : 0) + 16 * pc;
+        } else {
+          x[e] = u32x4{log_beta ? __float_as_uint(log_beta[row0 + rs]) : 0u,
+                       (uint32_t)pos[row0 + rs], 0u, 0u};
+          to[e] = sp + 2 * row_bytes;
+          tail[e] = true;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kB; ++e) {
+      if (!to[e]) continue;
+      if (tail[e]) *(uint2*)to[e] = make_uint2(x[e][0], x[e][1]);
+      else *(u32x4*)to[e] = x[e];
     }
   }
 }
@@ -1095,7 +1203,7 @@ void launch_fused_stage(const kvb_cache* c, int32_t M, void* ws, hipStream_t s) 
   char* w = (char*)ws;
   const int U = c->B * c->Hkv;
   dim3 grid((L.Mk + 63) / 64, U);
-  hipLaunchKernelGGL(fused_stage_copy, grid, dim3(256), 0, s, (const UnitInfo*)(w + L.info),
+  hipLaunchKernelGGL(stage_copy, grid, dim3(256), 0, s, (const UnitInfo*)(w + L.info),
                      (const int32_t*)(w + L.stage_n), (const int2*)(w + L.stage_list),
                      (unsigned char*)(w + L.scratch), c->k, c->v, c->log_beta, c->pos, c->cap,
                      L.Mk, L.srow, L.row_bytes);

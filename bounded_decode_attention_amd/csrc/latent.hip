@@ -87,7 +87,8 @@ __global__ __launch_bounds__(256) void latent_list(LatentArgs a) {
     if (l < kept && ks[l] == s) return;
     lo = l;
   }
-  a.ev[(size_t)u * a.cap + (s - lo)] = s;
+  const int slot = inf.ostart + s;  // the head's slot (around the end of its slots)
+  a.ev[(size_t)u * a.cap + (s - lo)] = slot < a.cap ? slot : slot - a.cap;
 }
 
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }

@@ -65,6 +65,14 @@ typedef enum { KVB_F32 = 0, KVB_BF16 = 1 } kvb_dtype;
  *             the live slots of a head positions must be strictly increasing.
  *   len       [B][Hkv] int32 live slots per head, device resident; slots at and
  *             beyond len are unspecified.
+ *   start     [B][Hkv] int32 first live slot per head, device resident, or NULL
+ *             (every head starts at slot 0).  A head's cap slots form a ring: its
+ *             i-th live token (position order) is in slot (start[u] + i) mod cap;
+ *             the other slots are unspecified.  Requires 0 <= start[u] < cap.
+ *             With a start array, eviction compacts each head toward whichever
+ *             end moves fewer rows and updates start (see kv_evict_to_budget);
+ *             the decode token goes to slot (start + len) mod cap.  Without one,
+ *             head u's live slots are 0 .. len[u] - 1.
  * The caller owns all of it.  Requires 1 <= B, Hkv; 1 <= cap < 2^30;
  * D in {64, 128} for KVB_BF16 (any 1 <= D <= 256 for KVB_F32); D % 8 == 0.
  */
@@ -76,6 +84,7 @@ typedef struct {
   int32_t* len;
   int32_t B, Hkv, cap, D;
   int32_t dtype; /* kvb_dtype */
+  int32_t* start;
 } kvb_cache;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -103,7 +112,8 @@ size_t asm_build_memory_workspace(int32_t H, int32_t N, int32_t D, int32_t L, in
  *
  * Optional decode token: if k_new != NULL, each head (b, g) gets k_new[b][g],
  * v_new[b][g] (and log_beta_new[b][g] when the cache has log_beta) at slot
- * len[b][g] with pos = t[b], then len[b][g] += 1, and the attention below covers
+ * len[b][g] (start + len mod cap with a start array) with pos = t[b], then
+ * len[b][g] += 1, and the attention below covers
  * it.  A head whose len already equals cap is not appended to (its len stays, the
  * token is not attended, and the workspace status word becomes KVB_ECAPACITY; the
  * caller must keep cap > len).  The splits cover the cached slots; the token's own
@@ -164,6 +174,13 @@ int32_t kv_append(const kvb_cache* cache, const void* k_new, const void* v_new,
  * first in (kappa, pos) ascending order are evicted (ties: lower position first).
  * The surviving rows (k, v, log_beta, pos) move, in their slot order, to slots
  * [0, M) and len becomes M.  Heads with len <= M are untouched.
+ * With a start array (slots relative to start, around the ring): a head whose
+ * cache fits the single-workgroup planner (about 34K slots on gfx950) is compacted
+ * toward whichever end moves fewer rows -- toward its first slot (start kept; the
+ * kept rows after the first evicted slot move) or toward its last slot (start +=
+ * number evicted, mod cap; the kept rows before the last evicted slot move).  At
+ * budget M with one token over, that moves min(e, M - e) rows for an eviction at
+ * slot e instead of M - e.  Larger heads are compacted toward their first slot.
  *
  *   t          [B] int32 current token position of each sequence
  *   M          budget, >= 0
