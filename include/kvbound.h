@@ -226,8 +226,8 @@ int32_t kv_evict_apply(const kvb_cache* cache, int32_t M, void* ws, size_t ws_by
  * Other arguments as kv_attn_decode (num_splits >= 2 for the fused kernels; the
  * same num_splits and ws in both phases); ws_evict is the plan's workspace.
  * Falls back to kv_attn_decode + kv_evict_apply (phase 1 then does nothing) for
- * dtype/D/group combinations without the fused kernel or caches whose plan does not
- * fit the single-workgroup planner.
+ * dtype/D/group combinations without the fused kernel, caches whose plan does not
+ * fit the single-workgroup planner, and caches with a start array.
  */
 int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q, int32_t Hq, const int32_t* t,
                                float scale, int32_t M, int32_t num_splits, int32_t phase,
