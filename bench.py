@@ -85,17 +85,17 @@ def cpu_baseline(w, host_units, t, M, budget_s=12.0):
 def steady_bench(args):
     """Steady-state decode of the 32K workload's model shape under its budget: every
     KV head of the 36 layers holds M = 4096 tokens; a step appends one token per
-    layer, attends over M + 1, evicts the lowest-retention token and compacts (every
-    kept row after the evicted slot moves down by one).  Eviction planning runs on a
-    second stream beside the attention; each compaction runs beside the next
-    layer's attention (the default; with --schedule deferred all compactions follow
-    the last layer's attention); the whole step is
-    captured once in a HIP graph and replayed (t advances on the device).  A second,
-    eager run of the same steps with the library's HIP-event trace gives the
-    per-kernel split.  Each head has a first-slot entry (kvb_cache.start; its
-    slots form a ring) unless --no-start: eviction then shifts the shorter side of
-    the evicted slot (the rows before it move up one slot when that side is shorter)
-    instead of always the rows after it."""
+    layer, attends over M + 1, evicts the lowest-retention token and compacts.  Each
+    head has a first-slot entry (kvb_cache.start; its slots form a ring) unless
+    --no-start, so the compaction moves the shorter side of the evicted slot (the
+    rows before it up one slot, or the rows after it down one) instead of always the
+    rows after it.  Default schedule (fused_append): the attention call appends the
+    decode token; the layer's eviction plan and compaction run on a second stream
+    beside the next layer's attention (--schedule both_beside: separate append, the
+    plan beside the layer's own attention; deferred: all compactions after the last
+    attention).  The whole step is captured once in a HIP graph and replayed (t
+    advances on the device).  A second, eager run of the same steps with the
+    library's HIP-event trace gives the per-kernel split."""
     import dataclasses
 
     import torch
@@ -128,12 +128,25 @@ def steady_bench(args):
     appended = [torch.cuda.Event() for _ in range(L)]
     attended = [torch.cuda.Event() for _ in range(L)]
     planned = [torch.cuda.Event() for _ in range(L)]
-    deferred = args.schedule == "deferred"  # default here: beside the next attention
+    deferred = args.schedule == "deferred"
+    fused_append = args.schedule in (None, "fused_append")  # the default here
 
     def step():
         main = torch.cuda.current_stream()
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
+            if fused_append:
+                # the attention call appends the decode token; the layer's plan and
+                # compaction follow it on the side stream, beside the next attention
+                kvb.kv_attn_decode(kvs[layer], q, t, k_new=kn, v_new=vn, log_beta_new=lb,
+                                   num_splits=args.splits, out=out, lse=lse, ws=ws_a,
+                                   stream=main)
+                attended[layer].record(main)
+                side.wait_event(attended[layer])
+                kvb.kv_evict_plan(kvs[layer], t, M, n_evicted=nev[layer], ws=ws_e[layer],
+                                  stream=side)
+                kvb.kv_evict_apply(kvs[layer], M, ws_e[layer], stream=side)
+                continue
             kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
             appended[layer].record(main)
             side.wait_event(appended[layer])
@@ -196,7 +209,7 @@ def steady_bench(args):
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True,
-                   "schedule": "deferred" if deferred else "both_beside",
+                   "schedule": args.schedule or "fused_append",
                    "head_start": not args.no_start},
         "eager_ms_per_step": round(eager_ms, 4), "kernel_us_eager": split,
         "attention_bytes_per_layer": attn_b}), flush=True)
@@ -442,14 +455,16 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="run each layer's eviction planning on the attention stream (no overlap)")
     ap.add_argument("--schedule", default=None,
-                    choices=["plan_beside", "both_beside", "deferred", "deferred_plan"],
+                    choices=["plan_beside", "both_beside", "deferred", "deferred_plan",
+                             "fused_append"],
                     help="deferred_plan (default of the 32K step): all layers' eviction "
                          "plans and compactions follow the last attention, each plan running "
                          "beside the previous layer's compaction; deferred: each plan beside "
                          "its layer's attention, the compactions after the last attention; "
                          "plan_beside: each compaction right after its layer's attention; "
-                         "both_beside (default of --steady): each compaction beside the next "
-                         "layer's attention")
+                         "both_beside: each compaction beside the next layer's attention; "
+                         "fused_append (default of --steady): the attention call appends, each "
+                         "layer's plan and compaction beside the next layer's attention")
     ap.add_argument("--graph", action="store_true",
                     help="decode step: replay the step as one captured HIP graph")
     ap.add_argument("--fused", action="store_true",
