@@ -67,7 +67,10 @@ __device__ __forceinline__ int vt_position(int kk) {
 
 // V [H][L][D] bf16 -> V^T [H][C][D][Lc] fp16 (chunk-local keys at vt_position, zero
 // past the chunk's end; |v| > 65504 saturates and sets the status word).  One
-// workgroup per (KV head, chunk, 64-key tile).
+// workgroup per (KV head, chunk, 64-key tile).  The tile is staged in LDS with rows
+// of 32 keys and above swapped in 16-byte column pairs (chunk c at c ^ 1): a wave's
+// transposed reads take rows k and k + 32 together, which would otherwise share
+// banks.
 template <int D>
 __global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
   constexpr int RP = D + 8;
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
     const int gk = c0 + tt * 64 + r;
     const u32x4 x = gk < c1 ? *(const u32x4*)(p.v + ((size_t)h * p.L + gk) * D + col * 8)
                             : u32x4{0, 0, 0, 0};
-    *(u32x4*)&vs[r * RP + col * 8] = x;
+    *(u32x4*)&vs[r * RP + ((col ^ ((r >> 5) & 1)) << 3)] = x;
   }
   __syncthreads();
   uint16_t* dst = p.vt + ((size_t)h * p.C + c) * D * p.Lc + tt * 64;
@@ -99,7 +102,9 @@ __global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
       const int p0 = 8 * q + e, p1 = p0 + 1;
       const int k0 = (p0 & ~31) + 4 * ((p0 & 31) >> 3) + (p0 & 3) + ((p0 & 4) ? 16 : 0);
       const int k1 = (p1 & ~31) + 4 * ((p1 & 31) >> 3) + (p1 & 3) + ((p1 & 4) ? 16 : 0);
-      const float x0 = bf16_bits_to_f32(vs[k0 * RP + d]), x1 = bf16_bits_to_f32(vs[k1 * RP + d]);
+      const int c0s = (((d >> 3) ^ ((k0 >> 5) & 1)) << 3) + (d & 7);
+      const int c1s = (((d >> 3) ^ ((k1 >> 5) & 1)) << 3) + (d & 7);
+      const float x0 = bf16_bits_to_f32(vs[k0 * RP + c0s]), x1 = bf16_bits_to_f32(vs[k1 * RP + c1s]);
       sat |= fabsf(x0) > 65504.f || fabsf(x1) > 65504.f;
       w[e / 2] = pack_f16x2(fminf(fmaxf(x0, -65504.f), 65504.f),
                             fminf(fmaxf(x1, -65504.f), 65504.f));
