@@ -23,12 +23,15 @@
 //   compact_move   per group of MOVE_ROWS destination rows: read every source row
 //                  (from the cache, or from scratch for staged rows), barrier, write.
 //
-// In-place safety: kept row j moves from src_j >= j to j.  A workgroup owns the
-// destination rows [j0, j0 + R); the only rows it writes are its own.  A source
-// row can be clobbered only if it lies below `kept` (nothing is written at or
-// beyond kept) and inside another workgroup's destination range; those sources
-// (src_j >= j0 + R of their own group) are staged by keep_emit, before any move
-// starts.  Sources inside the group's own range are read before the barrier.
+// In-place safety: kept row j moves from slot os + src_j to slot ns + j (os, ns: the
+// head's first live slot before and after; equal unless the head has a start array
+// and is compacted toward its last slot, ns = os + evicted; slots count around the
+// head's ring).  A workgroup owns the destination rows [j0, j0 + R); the only rows
+// it writes are its own.  Toward the first slot (src_j >= j) a source can be
+// clobbered only inside a later group's destination range; toward the last slot
+// (src_j <= j + evicted) only inside an earlier group's.  Those sources are staged
+// to scratch by the planner (staged_row), before any move starts.  Sources inside
+// the group's own range are read before the barrier.
 #include <string.h>
 
 #include "common.h"

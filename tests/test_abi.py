@@ -243,3 +243,26 @@ def test_latent_entry_points_reject_arguments_before_launch():
     a = list(rd)
     a[7] = None
     assert L.kv_latent_read(*a) == -1
+
+
+def test_cache_descriptor_layout_matches_header(tmp_path):
+    """The ctypes descriptor has the C struct's size and field offsets (compiled from
+    the header with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f[0] for f in _lib._Cache._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvbound.h"\nint main(void) {\n'
+                   '  printf("size %zu\\n", sizeof(kvb_cache));\n'
+                   + "".join(f'  printf("{f} %zu\\n", offsetof(kvb_cache, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(_lib._Cache)
+    for f in fields:
+        assert int(out[f]) == getattr(_lib._Cache, f).offset, f

@@ -294,3 +294,25 @@ def test_start_latent_absorb():
         ev.append(err)
         assert err < 1e-3, (g, err)
     say("latent rel err", ev)
+
+
+def test_start_fused_entry_falls_back():
+    """kv_attn_decode_compact on ring heads takes the unfused path: attention, then
+    the planned compaction (toward either end), as separate calls would."""
+    B, H, Hq, n, M, D = 1, 2, 8, 2000, 700, 128
+    cap = n + 64
+    d = _dense(61, B, H, n, n, D)
+    starts = np.array([[9, cap - 500]], np.int32)
+    rng = np.random.default_rng(6)
+    q = synth.bf16_bits(rng.standard_normal((B, Hq, D)))
+    t = np.array([n + 4], np.int32)
+    c = _placed(d, starts, cap, 2)
+    ws_e = torch.empty(kvb.kv_evict_workspace(c, M), dtype=torch.uint8, device="cuda")
+    kvb.kv_evict_plan(c, to_dev(t), M, ws=ws_e)
+    out, lse = kvb.kv_attn_decode_compact(c, to_dev(q), to_dev(t), M, ws_e)
+    torch.cuda.synchronize()
+    ro, rl = oracle_attention(d, q, t)
+    check_attention(to_host(out), to_host(lse), ro, rl, "fused entry on ring heads")
+    ref, ref_ev, _ = oracle.evict_to_budget(oracle.Cache.from_arrays(d), t, M)
+    check_layout(_logical(c), ref, "fused entry layout")
+    assert np.array_equal(to_host(c.start), _expected_start(d, ref_ev, starts, cap))
