@@ -375,6 +375,98 @@ def build_bench(args):
     }), flush=True)
 
 
+def memento_bench(args):
+    """MEMENTO-style erasure on the 1M-slot workload (batch 1, 64 query / 8 KV heads,
+    D = 128, bf16; thinking blocks of 2K-16K tokens each followed by a 200-token
+    memento): erase every completed block (range compaction), append the decode
+    token and attend with beta == 1 over the kept tokens, evict to M = 65536 (a
+    no-op).  Each trial restores the overwritten slots and the lengths first
+    (untimed); the median over the trials is reported with min and max."""
+    import numpy as np
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS["memento_1m"]
+    blocks, ranges = synth.memento_layout(total=w.ctx, seed=w.seed)
+    kept = 200 * (len(blocks) - 1) + blocks[-1][1]
+    print(f"# memento_1m: {len(blocks)} blocks, {ranges.shape[0]} erased ranges, "
+          f"{kept} tokens kept per KV head", file=sys.stderr, flush=True)
+    dc = synth.device_cache(w, layer=0)
+    q, kn, vn, _ = synth.device_queries(w, 0)
+    c = kvb.KVCache.from_dict(dc)
+    keep_slots = ((kept + 1 + 1023) // 1024) * 1024  # slots a trial overwrites
+    prist = {k: dc[k][:, :, :keep_slots].clone() for k in ("k", "v", "pos")}
+    rg = torch.from_numpy(ranges[None].copy()).cuda()
+    nr = torch.tensor([ranges.shape[0]], dtype=torch.int32, device="cuda")
+    t = torch.full((1,), w.ctx, dtype=torch.int32, device="cuda")
+    ws_er = torch.empty(kvb.kv_erase_workspace(c), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(c, w.hq, 0), dtype=torch.uint8,
+                       device="cuda")
+    ws_ev = torch.empty(kvb.kv_evict_workspace(c, w.budget), dtype=torch.uint8, device="cuda")
+    n_er = torch.empty((1, w.hkv), dtype=torch.int32, device="cuda")
+    n_ev = torch.empty((1, w.hkv), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, w.hq), dtype=torch.float32, device="cuda")
+
+    def restore():
+        for k in ("k", "v", "pos"):
+            dc[k][:, :, :keep_slots].copy_(prist[k])
+        dc["len"].fill_(w.ctx)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def trial():
+        restore()
+        torch.cuda.synchronize()
+        ev[0].record()
+        kvb.kv_erase_ranges(c, rg, nr, n_erased=n_er, ws=ws_er)
+        ev[1].record()
+        kvb.kv_attn_decode(c, q, t, k_new=kn, v_new=vn, out=out, lse=lse, ws=ws_a)
+        ev[2].record()
+        kvb.kv_evict_to_budget(c, t, w.budget, n_evicted=n_ev, ws=ws_ev)
+        ev[3].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(3)]
+
+    for _ in range(args.warmup):
+        trial()
+    trials = max(args.steps, 20)
+    res = np.array([trial() for _ in range(trials)])
+    assert int(n_er.min()) == int(n_er.max()) == w.ctx - kept, "erased count"
+    assert bool((dc["len"] == kept + 1).all()), "kept + decode token"
+    assert int(n_ev.max()) == 0, "eviction to 65536 is a no-op"
+    kvb.trace_enable(64 * trials + 64, ("keep_count", "keep_emit", "compact_move",
+                                        "attn_split", "attn_merge", "evict_select"))
+    for _ in range(trials):
+        trial()
+    per = {}
+    for name, kms in kvb.trace_read(1 << 16):
+        per.setdefault(name, []).append(kms * 1000.0)
+    kvb.trace_disable()
+    U, D, e = w.units, w.head_dim, w.elem_bytes
+    erase_b = U * w.ctx * 4 + U * kept * 2 * (2 * D * e + 4)  # pos scan + moves
+    attn_b = algorithmic_bytes(w, kept + 1, 0)[0]
+    med = np.median(res, axis=0)
+    total = float(np.sum(med))
+    print(json.dumps({
+        "metric": "MEMENTO erase + bounded decode attention latency, one layer (1M-slot cache)",
+        "value": round(total, 2), "unit": "us", "n_gpus": 1, "trials": trials,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": 1, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": D, "slots": w.ctx, "blocks": len(blocks),
+                   "erased_ranges": int(ranges.shape[0]), "kept": kept, "budget": w.budget},
+        "erase_us": {"median": round(float(med[0]), 2), "min": round(float(res[:, 0].min()), 2),
+                     "max": round(float(res[:, 0].max()), 2),
+                     "bytes": erase_b, "gbps": round(erase_b / (med[0] * 1e-6) / 1e9, 1)},
+        "attention_us": {"median": round(float(med[1]), 2), "min": round(float(res[:, 1].min()), 2),
+                         "max": round(float(res[:, 1].max()), 2),
+                         "bytes": attn_b, "gbps": round(attn_b / (med[1] * 1e-6) / 1e9, 1)},
+        "evict_us": {"median": round(float(med[2]), 2)},
+        "kernel_us": {k: round(float(np.median(v)), 1) for k, v in per.items()}}), flush=True)
+
+
 def latent_bench(args):
     """Latent memory of evicted tokens, one layer of the 32K decode workload (batch
     16, 8 KV heads, D = 128): the update after the eviction of 32769 -> 4096 tokens
@@ -482,6 +574,9 @@ def main():
     ap.add_argument("--asm-build", action="store_true",
                     help="time the offline build of one layer's attention-state memory "
                          "(prefix states in 4 chunks, K-means, aggregation; one JSON line)")
+    ap.add_argument("--memento", action="store_true",
+                    help="time MEMENTO erasure + attention on the 1M-slot workload instead "
+                         "(one JSON line)")
     ap.add_argument("--latent", action="store_true",
                     help="time the latent memory of evicted tokens (update after the 32K "
                          "eviction, steady-state update, read-out; one JSON line)")
@@ -507,6 +602,9 @@ def main():
         return
     if args.latent:
         latent_bench(args)
+        return
+    if args.memento:
+        memento_bench(args)
         return
     if args.steady:
         steady_bench(args)

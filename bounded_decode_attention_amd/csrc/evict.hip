@@ -740,19 +740,16 @@ struct KeepArgs {
   int32_t cap, Hkv, R, C, Mk, max_evict, row_bytes, srow, move_rows;
 };
 
-__device__ __forceinline__ bool in_ranges(const int32_t* rg, int nr, int p) {
-  // last range with start <= p
-  int lo = 0, hi = nr - 1, found = -1;
-  while (lo <= hi) {
+// Index of the first range whose end lies above p (nr if none); the ranges are
+// sorted and disjoint.
+__device__ __forceinline__ int first_range_ending_after(const int32_t* rg, int nr, int p) {
+  int lo = 0, hi = nr;
+  while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (rg[2 * mid] <= p) {
-      found = mid;
-      lo = mid + 1;
-    } else {
-      hi = mid - 1;
-    }
+    if (rg[2 * mid + 1] <= p) lo = mid + 1;
+    else hi = mid;
   }
-  return found >= 0 && p < rg[2 * found + 1];
+  return lo;
 }
 
 template <int MODE>
@@ -775,13 +772,20 @@ __device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int
       }
     }
   } else {
+    // positions increase along the slots: one search for the thread's first slot,
+    // then the range index only moves forward
     const int b = u / a.Hkv;
     const int32_t* rg = a.ranges + (size_t)b * a.R * 2;
     const int nr = a.n_ranges[b];
+    int pv[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) pv[e] = i0 + e < n ? ps[i0 + e] : 0;
+    int ri = i0 < n ? first_range_ending_after(rg, nr, pv[0]) : nr;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const int i = i0 + e;
-      f[e] = i < n && !in_ranges(rg, nr, ps[i]);
+      const int p = pv[e];
+      while (ri < nr && rg[2 * ri + 1] <= p) ++ri;
+      f[e] = i0 + e < n && !(ri < nr && rg[2 * ri] <= p);
     }
   }
 }
@@ -804,27 +808,11 @@ __global__ __launch_bounds__(kChunkThreads) void keep_count(KeepArgs a) {
   if (threadIdx.x == 0) a.counts[(size_t)u * a.C + c] = tot;
 }
 
-// src: slot relative to the head's first live slot s0; dst: destination index.
-__device__ __forceinline__ void copy_row_to_scratch(const KeepArgs& a, int u, int s0, int src,
-                                                    int dst) {
-  unsigned char* s = a.scratch + ((size_t)u * a.Mk + dst) * a.srow;
-  const int slot = s0 + src < a.cap ? s0 + src : s0 + src - a.cap;
-  const size_t off = ((size_t)u * a.cap + slot) * a.row_bytes;
-  const u32x4* kp = (const u32x4*)((const unsigned char*)a.k + off);
-  const u32x4* vp = (const u32x4*)((const unsigned char*)a.v + off);
-  const int pieces = a.row_bytes / 16;
-  for (int i = 0; i < pieces; ++i) {
-    ((u32x4*)s)[i] = kp[i];
-    ((u32x4*)(s + a.row_bytes))[i] = vp[i];
-  }
-  int32_t* tail = (int32_t*)(s + 2 * a.row_bytes);
-  tail[0] = a.log_beta ? __float_as_int(a.log_beta[(size_t)u * a.cap + slot]) : 0;
-  tail[1] = a.pos[(size_t)u * a.cap + slot];
-}
-
 template <int MODE>
 __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   __shared__ int smem[kChunkThreads / 64];
+  __shared__ int2 stg[kChunk];  // this chunk's staged rows (source, destination)
+  __shared__ int nstg;
   const int u = blockIdx.y, c = blockIdx.x;
   if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
   const int s0 = head_start(a.start, u);
@@ -847,6 +835,7 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   }
   const int base = c * kChunk;
   if (base >= n) return;
+  if (threadIdx.x == 0) nstg = 0;
   const int i0 = base + threadIdx.x * kPerThread;
   bool f[kPerThread];
   keep_flags<MODE>(a, u, i0, n, f);
@@ -863,12 +852,54 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
     if (f[e]) {
       if (dst < a.Mk) {  // always true when the threshold is consistent
         a.keep_src[(size_t)u * a.Mk + dst] = i;
-        if (staged_row(s0, s0, i, dst, all, a.move_rows)) copy_row_to_scratch(a, u, s0, i, dst);
+        if (staged_row(s0, s0, i, dst, all, a.move_rows)) stg[atomicAdd(&nstg, 1)] = make_int2(i, dst);
       }
       ++dst;
     } else if (MODE == MODE_EVICT && a.evicted_pos) {
       const int ev = i - dst;  // evicted slots before i
       if (ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
+    }
+  }
+  __syncthreads();
+  // the staged rows to scratch (by destination): 16-byte pieces of K and V and the
+  // 8-byte row tails, a batch of loads per thread before any store
+  const int ns = nstg;
+  const int ppr = a.row_bytes / 16, per = 2 * ppr + 1;
+  const size_t ub = (size_t)u * a.cap;
+  constexpr int kB = 8;
+  for (int q0 = threadIdx.x; q0 < ns * per; q0 += kB * kChunkThreads) {
+    u32x4 x[kB];
+    unsigned char* to[kB];
+    bool tail[kB];
+#pragma unroll
+    for (int e = 0; e < kB; ++e) {
+      const int q = q0 + e * kChunkThreads;
+      to[e] = nullptr;
+      tail[e] = false;
+      if (q < ns * per) {
+        const int en = q / per, part = q - en * per;
+        const int2 sd = stg[en];
+        const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
+        unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
+        if (part < 2 * ppr) {
+          const bool isv = part >= ppr;
+          const int pc = isv ? part - ppr : part;
+          x[e] = *(const u32x4*)((const unsigned char*)(isv ? a.v : a.k) + row * a.row_bytes +
+                                 16 * pc);
+          to[e] = sp + (isv ? a.row_bytes : 0) + 16 * pc;
+        } else {
+          x[e] = u32x4{a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u, (uint32_t)a.pos[row],
+                       0u, 0u};
+          to[e] = sp + 2 * a.row_bytes;
+          tail[e] = true;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kB; ++e) {
+      if (!to[e]) continue;
+      if (tail[e]) *(uint2*)to[e] = make_uint2(x[e][0], x[e][1]);
+      else *(u32x4*)to[e] = x[e];
     }
   }
 }
@@ -891,8 +922,13 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
   const int r0 = tid / cols;
   const bool isv = col >= ppr;
   const int pc = isv ? col - ppr : col;
+  // one item per workgroup: item w = (head u, group ch), groups of a head on
+  // neighbouring workgroups; when the grid strides (many more groups than
+  // workgroups), heads fastest, so the groups that hold rows (the first kept /
+  // move_rows of every head) are the first items, spread over the grid
+  const bool strided = U * cpu > (int)gridDim.x;
   for (int w = blockIdx.x; w < U * cpu; w += gridDim.x) {
-    const int u = w / cpu, ch = w - u * cpu;
+    const int u = strided ? w % U : w / cpu, ch = strided ? w / U : w % cpu;
     const UnitInfo inf = a.info[u];
     if (check_mode && inf.mode == MODE_NOOP) continue;
     const int kept = min(inf.kept, a.Mk);
@@ -1070,9 +1106,10 @@ static void launch_keep_chunks(const kvb_cache* c, const KeepArgs& a, int mode, 
 static void launch_move(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s) {
   const int U = c->B * c->Hkv;
   const long long items = (long long)U * ((a.Mk + a.move_rows - 1) / a.move_rows);
-  // one group per workgroup (many in flight hide the read latency); the kernel
-  // strides over groups if there are more than this
-  const int blocks = (int)(items < (1 << 20) ? items : (1 << 20));
+  // one group per workgroup (many in flight hide the read latency) up to 16384
+  // workgroups; past that the kernel strides over the groups (heads fastest, so the
+  // groups with rows to move, the first of every head, come first)
+  const int blocks = (int)(items < 16384 ? items : 16384);
   TraceScope tr(kTrCompactMove, s);
   hipLaunchKernelGGL(compact_move, dim3(blocks), dim3(kMoveThreads), 0, s, a, U,
                      mode == MODE_EVICT ? 1 : 0);
