@@ -93,9 +93,11 @@ def steady_bench(args):
     decode token; the layer's eviction plan and compaction run on a second stream
     beside the next layer's attention (--schedule both_beside: separate append, the
     plan beside the layer's own attention; deferred: all compactions after the last
-    attention).  The whole step is captured once in a HIP graph and replayed (t
-    advances on the device).  A second, eager run of the same steps with the
-    library's HIP-event trace gives the per-kernel split."""
+    attention).  Each head's attention is cut into 32 splits (--splits to change;
+    finer splits than the library's default of 16 here share the GPU better with the
+    second stream's compaction).  The whole step is captured once in a HIP graph and
+    replayed (t advances on the device).  A second, eager run of the same steps with
+    the library's HIP-event trace gives the per-kernel split."""
     import dataclasses
 
     import torch
@@ -118,7 +120,8 @@ def steady_bench(args):
         qs.append(synth.device_queries(w, layer))
     out = torch.empty((B, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, w.hq), dtype=torch.float32, device="cuda")
-    ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, args.splits), dtype=torch.uint8,
+    P = args.splits or 32
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, P), dtype=torch.uint8,
                        device="cuda")
     ws_e = [torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device="cuda")
             for _ in range(L)]
@@ -139,8 +142,7 @@ def steady_bench(args):
                 # the attention call appends the decode token; the layer's plan and
                 # compaction follow it on the side stream, beside the next attention
                 kvb.kv_attn_decode(kvs[layer], q, t, k_new=kn, v_new=vn, log_beta_new=lb,
-                                   num_splits=args.splits, out=out, lse=lse, ws=ws_a,
-                                   stream=main)
+                                   num_splits=P, out=out, lse=lse, ws=ws_a, stream=main)
                 attended[layer].record(main)
                 side.wait_event(attended[layer])
                 kvb.kv_evict_plan(kvs[layer], t, M, n_evicted=nev[layer], ws=ws_e[layer],
@@ -151,8 +153,8 @@ def steady_bench(args):
             appended[layer].record(main)
             side.wait_event(appended[layer])
             kvb.kv_evict_plan(kvs[layer], t, M, n_evicted=nev[layer], ws=ws_e[layer], stream=side)
-            kvb.kv_attn_decode(kvs[layer], q, t, num_splits=args.splits, out=out, lse=lse,
-                               ws=ws_a, stream=main)
+            kvb.kv_attn_decode(kvs[layer], q, t, num_splits=P, out=out, lse=lse, ws=ws_a,
+                               stream=main)
             if deferred:
                 planned[layer].record(side)
                 continue
@@ -210,7 +212,7 @@ def steady_bench(args):
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True,
                    "schedule": args.schedule or "fused_append",
-                   "head_start": not args.no_start},
+                   "head_start": not args.no_start, "kv_splits": P},
         "eager_ms_per_step": round(eager_ms, 4), "kernel_us_eager": split,
         "attention_bytes_per_layer": attn_b}), flush=True)
 
@@ -287,6 +289,137 @@ def asm_bench(args):
         "config": {"workload": "asm_hier", "batch": base.batch, "q_heads": base.hq,
                    "kv_heads": base.hkv, "head_dim": base.head_dim},
         "sizes": rows}), flush=True)
+
+
+def asm_step_bench(args):
+    """One decode step of the ASM workload over its 36 layers: per layer, attention
+    over the 2048 generated tokens of each (sequence, KV head) with the decode token
+    appended (no retention bias), then the cosine lookup of every query head in its
+    KV head's 4096-entry codebook and the merge of the chosen entry's state with the
+    attention state -- by kv_attn_decode_asm (three launches), or with
+    --asm-two-calls by kv_attn_decode then asm_lookup_merge (four).  Batch 32, 32 query / 8 KV heads, D = 128, bf16.  The caches
+    and codebooks of all layers are resident; each step restores the lengths
+    (untimed).  The attention kernel and the lookup are traced with HIP events on
+    their stream in the timed steps."""
+    import dataclasses
+
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS["asm_lookup"]
+    if args.layers:
+        w = dataclasses.replace(w, layers=args.layers)
+    L, B = w.layers, w.batch
+    print(f"# generating {L} layers of {w.name}", file=sys.stderr, flush=True)
+    caches, kvs, qs, books = [], [], [], []
+    for layer in range(L):
+        d = synth.device_cache(w, layer)
+        caches.append(d)
+        kvs.append(kvb.KVCache.from_dict(d))
+        qs.append(synth.device_queries(w, layer))
+        books.append(synth.device_codebook(w, layer))
+    torch.cuda.synchronize()
+    t = torch.full((B,), w.ctx, dtype=torch.int32, device="cuda")
+    P = args.splits
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, P), dtype=torch.uint8,
+                       device="cuda")
+    ws_l = torch.empty(kvb.asm_lookup_merge_workspace(B, w.hq, w.hkv, w.head_dim, w.codebook),
+                       dtype=torch.uint8, device="cuda")
+    so = torch.empty((B, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
+    sl = torch.empty((B, w.hq), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(so)
+    out_lse = torch.empty_like(sl)
+    idx = torch.empty((B, w.hq), dtype=torch.int32, device="cuda")
+
+    ws_f = torch.empty(kvb.kv_attn_decode_asm_workspace(kvs[0], w.hq, P, w.codebook),
+                       dtype=torch.uint8, device="cuda")
+    two_calls = args.asm_two_calls
+
+    def step():
+        for layer in range(L):
+            q, kn, vn, _ = qs[layer]
+            cent, abar, lz = books[layer]
+            if two_calls:
+                kvb.kv_attn_decode(kvs[layer], q, t, k_new=kn, v_new=vn, num_splits=P, out=so,
+                                   lse=sl, ws=ws_a)
+                kvb.asm_lookup_merge(q, cent, abar, lz, so, sl, out=out, out_lse=out_lse,
+                                     idx=idx, ws=ws_l)
+            else:
+                kvb.kv_attn_decode_asm(kvs[layer], q, t, cent, abar, lz, k_new=kn, v_new=vn,
+                                       num_splits=P, out=out, lse=out_lse, idx=idx, ws=ws_f)
+
+    def restore():
+        for d in caches:
+            d["len"].fill_(w.ctx)
+
+    for _ in range(args.warmup):
+        restore()
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        restore()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            restore()
+            graph.replay()
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        out_t = []
+        for _ in range(args.steps):
+            restore()
+            torch.cuda.synchronize()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out_t.append(e0.elapsed_time(e1))
+        return out_t
+
+    # the timed steps carry no trace events; kernel times come from further eager steps
+    times = timed(graph.replay if graph is not None else step)
+    kvb.trace_enable(4 * args.steps * L + 16, ("attn_split", "attn_merge", "asm_lookup",
+                                               "asm_finalize"))
+    timed(step)
+    per = {}
+    for name, kms in kvb.trace_read(1 << 16):
+        per.setdefault(name, []).append(kms)
+    kvb.trace_disable()
+    ms = sum(times) / len(times)
+    n = w.ctx + 1
+    attn_b = algorithmic_bytes(w, n, 0)[0] - w.units * n * 8  # no bias: K, V, q, out only
+    # the codebook, the chosen entry's state (bf16 a-bar row + log Z-bar) gathered per
+    # query head, the chosen index written; q is read and (out, lse) written once, in
+    # attn_b; the attention's own (out, lse) handed to a second call is overhead
+    look_b = (w.hkv * w.codebook * w.head_dim * 2 + B * w.hq * (w.head_dim * 2 + 4)
+              + B * w.hq * 4)
+    split_ms = sum(per["attn_split"]) / len(per["attn_split"])
+    print(json.dumps({
+        "metric": "ASM decode steps/s (attention over 2048 tokens + centroid lookup + merge, "
+                  "36 layers)",
+        "value": round(1000.0 / ms, 3), "unit": "decode steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.head_dim, "tokens": w.ctx, "codebook": w.codebook,
+                   "layers": L, "entry": "kv_attn_decode + asm_lookup_merge" if two_calls
+                   else "kv_attn_decode_asm", "launch": "graph" if graph is not None
+                   else "eager", "kv_splits": P or kvb.kv_attn_decode_splits(kvs[0], w.hq)},
+        "bytes_per_step": L * (attn_b + look_b),
+        "gbps": round(L * (attn_b + look_b) / (ms * 1e-3) / 1e9, 1),
+        "attn_split_us": round(split_ms * 1000, 2),
+        "attn_split_gbps": round(attn_b / (split_ms * 1e-3) / 1e9, 1),
+        "lookup_kernels_us": {k: round(sum(v) / len(v) * 1000, 2) for k, v in per.items()
+                              if k != "attn_split"}}), flush=True)
 
 
 def build_bench(args):
@@ -558,7 +691,7 @@ def main():
                          "fused_append (default of --steady): the attention call appends, each "
                          "layer's plan and compaction beside the next layer's attention")
     ap.add_argument("--graph", action="store_true",
-                    help="decode step: replay the step as one captured HIP graph")
+                    help="decode / ASM step: replay the step as one captured HIP graph")
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
@@ -574,6 +707,11 @@ def main():
     ap.add_argument("--asm-build", action="store_true",
                     help="time the offline build of one layer's attention-state memory "
                          "(prefix states in 4 chunks, K-means, aggregation; one JSON line)")
+    ap.add_argument("--asm-step", action="store_true",
+                    help="time one decode step of the ASM workload (36 layers of attention "
+                         "over 2048 tokens + lookup + merge) instead (one JSON line)")
+    ap.add_argument("--asm-two-calls", action="store_true",
+                    help="--asm-step: attention and lookup + merge as two calls")
     ap.add_argument("--memento", action="store_true",
                     help="time MEMENTO erasure + attention on the 1M-slot workload instead "
                          "(one JSON line)")
@@ -605,6 +743,9 @@ def main():
         return
     if args.memento:
         memento_bench(args)
+        return
+    if args.asm_step:
+        asm_step_bench(args)
         return
     if args.steady:
         steady_bench(args)

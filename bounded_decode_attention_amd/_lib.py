@@ -50,6 +50,9 @@ def library():
             "asm_lookup_merge_workspace": (SZ, [I32, I32, I32, I32, I32]),
             "asm_lookup_merge_hier_workspace": (SZ, [I32, I32, I32, I32, I32]),
             "kv_attn_decode": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P]),
+            "kv_attn_decode_asm_workspace": (SZ, [CP, I32, I32, I32]),
+            "kv_attn_decode_asm": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, I32, P, P, P,
+                                         P, SZ, P]),
             "kv_evict_to_budget": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
             "kv_evict_plan": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
             "kv_evict_apply": (I32, [CP, I32, P, SZ, P]),
@@ -218,6 +221,47 @@ def kv_attn_decode(cache: KVCache, q, t, scale: float = 0.0, k_new=None, v_new=N
                                   _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "kv_attn_decode")
     return out, lse
+
+
+def kv_attn_decode_asm_workspace(cache: KVCache, Hq: int, num_splits: int, K: int) -> int:
+    return int(library().kv_attn_decode_asm_workspace(cache.desc, Hq, num_splits, K))
+
+
+def kv_attn_decode_asm(cache: KVCache, q, t, centroids, abar, log_zbar, scale: float = 0.0,
+                       k_new=None, v_new=None, log_beta_new=None, num_splits: int = 0, out=None,
+                       lse=None, idx=None, ws=None, stream=None):
+    """kv_attn_decode then asm_lookup_merge on its state, the lookup's merge done by
+    the attention's merge (see kv_attn_decode_asm in kvbound.h).  centroids, abar
+    [Hkv][K][D] bf16; log_zbar [Hkv][K] f32.  Returns (out, lse, idx)."""
+    _need(q, "q", torch.bfloat16)
+    _need(t, "t", torch.int32)
+    _need(centroids, "centroids", torch.bfloat16)
+    _need(abar, "abar", torch.bfloat16)
+    _need(log_zbar, "log_zbar", torch.float32)
+    B, Hq, D = q.shape
+    K = centroids.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _need(idx, "idx", torch.int32)
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x is not None:
+            _need(x, name, torch.bfloat16)
+    if log_beta_new is not None:
+        _need(log_beta_new, "log_beta_new", torch.float32)
+    ws = _ws(ws, kv_attn_decode_asm_workspace(cache, Hq, num_splits, K), q.device)
+    st = library().kv_attn_decode_asm(cache.desc, _ptr(q), Hq, _ptr(t), float(scale),
+                                      _ptr(k_new), _ptr(v_new), _ptr(log_beta_new),
+                                      int(num_splits), _ptr(centroids), _ptr(abar),
+                                      _ptr(log_zbar), int(K), _ptr(out), _ptr(lse), _ptr(idx),
+                                      _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_attn_decode_asm")
+    return out, lse, idx
 
 
 def kv_evict_to_budget(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=None, ws=None,

@@ -194,7 +194,7 @@ __device__ __forceinline__ void merge_entry(const AsmArgs& a, int bh, int g, int
   for (int d = lane; d < D; d += 64) {
     const float so = a.self_out[(size_t)bh * D + d];
     const float av = bf16_bits_to_f32(ab[d]);
-    a.out[(size_t)bh * D + d] = (w1 * so + w2 * av) * inv;
+    a.out[(size_t)bh * D + d] = fmaf(w1, so, w2 * av) * inv;
   }
   if (lane == 0) a.out_lse[bh] = lse_out;
 }
@@ -536,10 +536,33 @@ __global__ __launch_bounds__(64) void asm_hier_finalize(HierArgs h) {
   merge_entry(a, bh, g, k, lane);
 }
 
-static void asm_dims(int B, int Hq, int Hkv, int K, int& G, int& QB, int& KC) {
+void asm_dims(int B, int Hq, int Hkv, int K, int& G, int& QB, int& KC) {
   G = Hq / Hkv;
   QB = (B * G + 15) / 16;
   KC = (K + kAsmChunk - 1) / kAsmChunk;
+}
+
+void launch_asm_candidates(const uint16_t* q, int B, int Hq, int Hkv, int D,
+                           const uint16_t* centroids, int K, float* cand_score,
+                           int32_t* cand_idx, hipStream_t s) {
+  AsmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.cent = centroids;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.K = K;
+  asm_dims(B, Hq, Hkv, K, a.G, a.QB, a.KC);
+  a.cand_score = cand_score;
+  a.cand_idx = cand_idx;
+  dim3 grid(a.KC, Hkv, (a.QB + kAsmQB - 1) / kAsmQB);
+  TraceScope tr(kTrAsmLookup, s);
+  if (D == 128)
+    hipLaunchKernelGGL(asm_lookup_partial<128>, grid, dim3(64 * kAsmWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL(asm_lookup_partial<64>, grid, dim3(64 * kAsmWaves), 0, s, a);
 }
 
 }  // namespace kvb

@@ -821,8 +821,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
                                                             const float* part_ml, int P, int D,
                                                             float* out, float* lse,
                                                             const UnitInfo* info, int32_t* len,
-                                                            int G, NewTok nt) {
+                                                            int G, NewTok nt, AsmTail at) {
   __shared__ float w[kMergeMaxP];
+  __shared__ int s_k;  // the lookup's entry (with an ASM tail)
   __shared__ float red[kMergeThreads];
   __shared__ float gsum[kMergeThreads];
   const int bh = blockIdx.x;
@@ -894,15 +895,72 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     for (int e = 0; e < kB; ++e)
       if (pb + e < p1) o = fmaf(w[pb + e], x[e], o);
   }
+  // ASM tail (the lookup's step 4): the best candidate entry of this query head
+  if (at.cand_score && tid < 64) {
+    const int b = bh / at.Hq, h = bh - b * at.Hq;
+    const int g = h / G, j = h - g * G;
+    float q2 = 0.f;
+    for (int d = tid; d < D; d += 64) {
+      const float x = bf16_bits_to_f32(at.q[(size_t)bh * D + d]);
+      q2 = fmaf(x, x, q2);
+    }
+    q2 = wave_sum(q2);
+    float bs = kNegInf;
+    int bk = 0x7FFFFFFF;
+    const size_t base = ((size_t)g * at.QB * 16 + b * G + j) * at.KC;
+    for (int c = tid; c < at.KC; c += 64) {
+      const float sc = at.cand_score[base + c];
+      const int k = at.cand_idx[base + c];
+      if (sc > bs || (sc == bs && k < bk)) {
+        bs = sc;
+        bk = k;
+      }
+    }
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+      const float os = __shfl_xor(bs, o2, 64);
+      const int ok = __shfl_xor(bk, o2, 64);
+      if (os > bs || (os == bs && ok < bk)) {
+        bs = os;
+        bk = ok;
+      }
+    }
+    if (tid == 0) {
+      const int k = (q2 > 0.f && bk != 0x7FFFFFFF) ? bk : 0;
+      s_k = k;
+      if (at.idx) at.idx[bh] = k;
+    }
+  }
   gsum[tid] = o;
   __syncthreads();
+  const float lse_self = W > 0.f ? M + __logf(W) : kNegInf;
+  // merge with the entry's stored state by the normalisers (as asm_lookup_merge)
+  float w1 = 0.f, w2 = 0.f, lse_out = lse_self;
+  const uint16_t* ab = nullptr;
+  if (at.cand_score) {
+    const int h = bh - (bh / at.Hq) * at.Hq, g = h / G;
+    const float lz = at.log_zbar[(size_t)g * at.K + s_k];
+    const float Mx = fmaxf(lse_self, lz);
+    lse_out = kNegInf;
+    if (Mx != kNegInf) {
+      w1 = lse_self == kNegInf ? 0.f : __expf(lse_self - Mx);
+      w2 = lz == kNegInf ? 0.f : __expf(lz - Mx);
+      lse_out = Mx + __logf(w1 + w2);
+    }
+    ab = at.abar + ((size_t)g * at.K + s_k) * D;
+  }
   if (tid < D) {
     float acc = 0.f;
     for (int g = 0; g < NG; ++g) acc += gsum[g * D + tid];
     if (incl) acc = fmaf(w_new, load_elem(nt.v_new, (size_t)u * D + tid, nt.elem), acc);
-    out[(size_t)bh * D + tid] = W > 0.f ? acc / W : 0.f;
+    float so = W > 0.f ? acc / W : 0.f;
+    if (ab) {
+      const float inv = (w1 + w2) > 0.f ? 1.f / (w1 + w2) : 0.f;
+      so = fmaf(w1, so, w2 * bf16_bits_to_f32(ab[tid])) * inv;
+    }
+    out[(size_t)bh * D + tid] = so;
   }
-  if (tid == 0) lse[bh] = W > 0.f ? M + __logf(W) : kNegInf;
+  if (tid == 0) lse[bh] = lse_out;
   // append the decode token (first query head of each KV head); every split has
   // read the old len, and the other merge blocks use the recorded one
   if (nt.k_new && bh % G == 0) {
@@ -934,16 +992,20 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
 // ------------------------------------------------------------------ host
 static void launch_merge(const float* part_a, const float* part_ml, int P, int D, float* out,
                          float* lse, const UnitInfo* info, int32_t* len, int G, int BH,
-                         hipStream_t s, const NewTok* nt = nullptr) {
+                         hipStream_t s, const NewTok* nt = nullptr,
+                         const AsmTail* tail = nullptr) {
   NewTok none;
   memset(&none, 0, sizeof(none));
   const NewTok& n = nt ? *nt : none;
+  AsmTail no_tail;
+  memset(&no_tail, 0, sizeof(no_tail));
+  const AsmTail& at = tail ? *tail : no_tail;
   if (P > 128)
     hipLaunchKernelGGL(attn_merge<512>, dim3(BH), dim3(512), 0, s, part_a, part_ml, P, D, out,
-                       lse, info, len, G, n);
+                       lse, info, len, G, n, at);
   else
     hipLaunchKernelGGL(attn_merge<256>, dim3(BH), dim3(256), 0, s, part_a, part_ml, P, D, out,
-                       lse, info, len, G, n);
+                       lse, info, len, G, n, at);
 }
 
 static bool mfma_supported(const kvb_cache* c, int G) {
@@ -998,10 +1060,12 @@ static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s
 }
 
 // About two rounds of resident waves (2 per SIMD): fewer, longer splits stream
-// better than many short ones, and keep the merged partial states small.
+// better than many short ones, and keep the merged partial states small.  A split
+// covers at least 256 slots (two 128-token tiles): on short heads one-tile splits
+// spend their time in set-up and partial-state writes.
 static int32_t auto_splits(const kvb_cache* c) {
   const long long units = (long long)c->B * c->Hkv;
-  const long long tiles = (c->cap + 31) / 32;
+  const long long tiles = c->cap / 256;
   long long P = (4096 + units - 1) / units;
   if (P > tiles) P = tiles;
   if (P > 1024) P = 1024;
@@ -1045,11 +1109,13 @@ extern "C" int32_t kv_append(const kvb_cache* cache, const void* k_new, const vo
   return launch_status();
 }
 
-extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq,
-                                  const int32_t* t, float scale, const void* k_new,
-                                  const void* v_new, const float* log_beta_new,
-                                  int32_t num_splits, float* out, float* lse, void* ws,
-                                  size_t ws_bytes, void* stream) {
+// The decode attention; with an ASM tail its merge also merges each query head's
+// chosen codebook entry (kv_attn_decode_asm).
+static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t Hq,
+                                const int32_t* t, float scale, const void* k_new,
+                                const void* v_new, const float* log_beta_new,
+                                int32_t num_splits, float* out, float* lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream, const AsmTail* tail) {
   int32_t st = check_cache(cache, true);
   if (st) return st;
   if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
@@ -1063,7 +1129,7 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
   if ((st = check_device())) return st;
 
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   const size_t S = (size_t)cache->B * Hq * P;
   AttnArgs a;
   a.k = cache->k;
@@ -1120,8 +1186,72 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
   }
   TraceScope tr(kTrAttnMerge, s);
   launch_merge(a.part_a, a.part_ml, P, cache->D, out, lse, nullptr, nullptr, G,
-               cache->B * Hq, s, k_new ? &nt : nullptr);
+               cache->B * Hq, s, k_new ? &nt : nullptr, tail);
   return launch_status();
+}
+
+extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq,
+                                  const int32_t* t, float scale, const void* k_new,
+                                  const void* v_new, const float* log_beta_new,
+                                  int32_t num_splits, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, num_splits, out,
+                          lse, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+extern "C" size_t kv_attn_decode_asm_workspace(const kvb_cache* cache, int32_t Hq,
+                                               int32_t num_splits, int32_t K) {
+  const size_t wa = kv_attn_decode_workspace(cache, Hq, num_splits);
+  if (!wa || K < 1 || cache->Hkv < 1 || Hq % cache->Hkv) return 0;
+  int G, QB, KC;
+  asm_dims(cache->B, Hq, cache->Hkv, K, G, QB, KC);
+  const size_t n = (size_t)cache->Hkv * QB * 16 * KC;
+  return align_up(wa, 256) + 2 * align_up(n * 4, 256);
+}
+
+extern "C" int32_t kv_attn_decode_asm(const kvb_cache* cache, const void* q, int32_t Hq,
+                                      const int32_t* t, float scale, const void* k_new,
+                                      const void* v_new, const float* log_beta_new,
+                                      int32_t num_splits, const void* centroids,
+                                      const void* abar, const float* log_zbar, int32_t K,
+                                      float* out, float* lse, int32_t* idx, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!q || !centroids || !abar || !log_zbar) return KVB_EINVAL;
+  if (cache->dtype != KVB_BF16) return KVB_EUNSUPPORTED;  // q and the codebook are bf16
+  if (K < 1 || K >= (1 << 24) || Hq < 1 || Hq % cache->Hkv) return KVB_EINVAL;
+  if ((long long)cache->B * (Hq / cache->Hkv) > 65536) return KVB_EINVAL;
+  if (num_splits < 0 || num_splits > 4096) return KVB_EINVAL;
+  const int P = num_splits > 0 ? num_splits : auto_splits(cache);
+  const size_t need = kv_attn_decode_asm_workspace(cache, Hq, P, K);
+  if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
+  if ((st = check_device())) return st;
+  int G, QB, KC;
+  asm_dims(cache->B, Hq, cache->Hkv, K, G, QB, KC);
+  const size_t wa = align_up(kv_attn_decode_workspace(cache, Hq, P), 256);
+  const size_t n = (size_t)cache->Hkv * QB * 16 * KC;
+  AsmTail at;
+  at.cand_score = (const float*)((char*)ws + wa);
+  at.cand_idx = (const int32_t*)((char*)ws + wa + align_up(n * 4, 256));
+  at.q = (const uint16_t*)q;
+  at.abar = (const uint16_t*)abar;
+  at.log_zbar = log_zbar;
+  at.idx = idx;
+  at.K = K;
+  at.KC = KC;
+  at.QB = QB;
+  at.Hq = Hq;
+  hipStream_t s = (hipStream_t)stream;
+  // the lookup needs only q and the codebook: its candidates first, then the
+  // attention, whose merge finishes the lookup.  (Beside the splits, on a second
+  // stream, the candidate scan is starved by the splits' workgroups and the layer
+  // takes longer.)
+  launch_asm_candidates((const uint16_t*)q, cache->B, Hq, cache->Hkv, cache->D,
+                        (const uint16_t*)centroids, K, (float*)at.cand_score,
+                        (int32_t*)at.cand_idx, s);
+  return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, P, out, lse, ws,
+                          wa, s, &at);
 }
 
 // ------------------------------------------------------------------ fused attention + compaction

@@ -122,6 +122,27 @@ struct UnitInfo {
 };
 static_assert(sizeof(UnitInfo) == 32, "UnitInfo layout");
 
+// ASM lookup's candidates and stored states, for the attention merge that also
+// performs the lookup's merge (kv_attn_decode_asm): per query row of KV head g the
+// best (score, lowest index) of KC chunk candidates at
+// [g][qrow][c] (qrow = b * G + j), then entry k's (abar, log Zbar).
+struct AsmTail {
+  const float* cand_score;  // null: no lookup merge
+  const int32_t* cand_idx;
+  const uint16_t* q;        // [B][Hq][D] bf16 (zero query -> entry 0)
+  const uint16_t* abar;     // [Hkv][K][D] bf16
+  const float* log_zbar;    // [Hkv][K]
+  int32_t* idx;             // [B][Hq] or null
+  int32_t K, KC, QB, Hq;
+};
+
+// Lookup candidates (the first kernel of asm_lookup_merge): per KV head, query row
+// and 256-centroid chunk, the best cosine and its index.
+void asm_dims(int B, int Hq, int Hkv, int K, int& G, int& QB, int& KC);
+void launch_asm_candidates(const uint16_t* q, int B, int Hq, int Hkv, int D,
+                           const uint16_t* centroids, int K, float* cand_score,
+                           int32_t* cand_idx, hipStream_t s);
+
 // Compaction state a fused attention launch reads from an eviction plan: per
 // 32-slot tile the keep mask and the destination of its first kept row, and the
 // kept rows whose source lies below `za` (staged in scratch by the planner).

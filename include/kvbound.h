@@ -90,7 +90,8 @@ typedef struct {
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kvb_strerror(int32_t status);
 
-/* Number of KV splits kv_attn_decode uses for num_splits == 0 (host only). */
+/* Number of KV splits kv_attn_decode uses for num_splits == 0 (host only): about
+ * 4096 / (B * Hkv), at least one, at most one per 256 slots of capacity. */
 int32_t kv_attn_decode_splits(const kvb_cache* cache, int32_t Hq);
 
 /* Workspace sizes in bytes (host only; no device access). */
@@ -273,6 +274,26 @@ int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int3
                          int32_t K, const float* self_out, const float* self_lse, float* out,
                          float* out_lse, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * kv_attn_decode followed by asm_lookup_merge on its output, in three launches
+ * instead of four ([ASM] method steps 1-4): the lookup's candidate scan (it needs
+ * only q and the codebook) runs first, and the attention's split merge also picks
+ * each query head's entry and merges it.  Results equal the two calls' (same
+ * arithmetic); out and lse hold the merged state, idx the chosen entries.
+ *   Arguments as kv_attn_decode (bf16 cache, D 128 or 64) and asm_lookup_merge
+ *   (centroids, abar [Hkv][K][D] bf16; log_zbar [Hkv][K] f32; 1 <= K < 2^24).
+ *   ws         workspace of kv_attn_decode_asm_workspace(cache, Hq, num_splits, K)
+ *              bytes; the attention's part (and status word) comes first.
+ */
+size_t kv_attn_decode_asm_workspace(const kvb_cache* cache, int32_t Hq, int32_t num_splits,
+                                    int32_t K);
+int32_t kv_attn_decode_asm(const kvb_cache* cache, const void* q, int32_t Hq, const int32_t* t,
+                           float scale, const void* k_new, const void* v_new,
+                           const float* log_beta_new, int32_t num_splits,
+                           const void* centroids, const void* abar, const float* log_zbar,
+                           int32_t K, float* out, float* lse, int32_t* idx, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /*
  * The same lookup and merge through a two-level index ([ASM] technical novelty:

@@ -57,7 +57,9 @@ def test_workspace_sizes_host_only():
     L = kvb.library()
     c = _desc()
     P = L.kv_attn_decode_splits(ctypes.byref(c), 8)
-    assert 1 <= P <= 4  # 100-slot cache: 4 tiles
+    assert P == 1  # 100-slot cache: a split covers at least 256 slots
+    assert L.kv_attn_decode_splits(ctypes.byref(_desc(cap=2080, B=32, Hkv=8)), 32) == 8
+    assert L.kv_attn_decode_splits(ctypes.byref(_desc(cap=32800, B=16, Hkv=8)), 32) == 32
     assert L.kv_attn_decode_workspace(ctypes.byref(c), 8, 0) >= 256 + 2 * 8 * P * 130 * 4
     assert L.kv_evict_workspace(ctypes.byref(c), 10) > 256
     assert L.kv_erase_workspace(ctypes.byref(c)) >= L.kv_evict_workspace(ctypes.byref(c), 10)
@@ -266,3 +268,22 @@ def test_cache_descriptor_layout_matches_header(tmp_path):
     assert int(out["size"]) == ctypes.sizeof(_lib._Cache)
     for f in fields:
         assert int(out[f]) == getattr(_lib._Cache, f).offset, f
+
+
+@needs_lib
+def test_fused_asm_entry_rejects_arguments_before_launch():
+    """kv_attn_decode_asm: fake (never dereferenced) pointers; validation first."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    good = _desc()
+    need = L.kv_attn_decode_asm_workspace(ctypes.byref(good), 8, 0, 4096)
+    assert need > L.kv_attn_decode_workspace(ctypes.byref(good), 8, 0)
+    args = lambda **kw: [kw.get("q", P(64)), 8, P(72), 0.0, None, None, None, 0,  # noqa: E731
+                         kw.get("cent", P(8)), P(16), P(24), kw.get("K", 4096), P(80), P(88),
+                         None, P(4096), kw.get("ws_bytes", need), None]
+    assert L.kv_attn_decode_asm(ctypes.byref(good), *args(cent=None)) == -1
+    assert L.kv_attn_decode_asm(ctypes.byref(good), *args(q=None)) == -1
+    assert L.kv_attn_decode_asm(ctypes.byref(good), *args(K=0)) == -1
+    assert L.kv_attn_decode_asm(ctypes.byref(_desc(dtype=0, D=64)), *args()) == -2  # f32 cache
+    assert L.kv_attn_decode_asm(ctypes.byref(good), *args(ws_bytes=need - 1)) == -4
+    assert L.kv_attn_decode_asm_workspace(ctypes.byref(good), 7, 0, 4096) == 0    # Hq % Hkv
