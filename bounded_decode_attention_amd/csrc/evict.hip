@@ -10,11 +10,14 @@
 // every slot whose position lies in one of the sequence's half-open ranges.
 //
 // Kernels
-//   evict_select   one 1024-thread workgroup per head: finds the threshold
-//                  element (kappa*, slot*) -- the (n-M)-th in (kappa, slot) order --
-//                  by a 3-pass radix select on the float32-rounded key (a monotone
-//                  map of kappa), then an exact pass on the 64-bit key among the
-//                  float32 ties, then the slot among exact ties.
+//   sel_init, sel_hist, sel_collect, sel_finish
+//                  (heads too long for the LDS planner) find the threshold element
+//                  (kappa*, slot*) -- the (n-M)-th in (kappa, slot) order -- by radix
+//                  passes on the float32-rounded key (a monotone map of kappa), many
+//                  workgroups per head, until the bucket holding it has at most 4096
+//                  members, which are listed (exact 64-bit key, slot) and the
+//                  selection finished in LDS; if more than 4096 share one float32
+//                  key, exact passes on the 64-bit key and a slot pass over the head.
 //   keep_count     per 4096-slot chunk: number of kept slots.
 //   keep_emit      per chunk: exclusive scan -> destination slot of every kept
 //                  row (keep_src[dst] = src); evicted positions; rows whose source
@@ -142,121 +145,362 @@ __device__ __forceinline__ int select_bucket(const uint32_t* hist, int nb, int& 
 }
 
 // ---------------------------------------------------------------- select
-__global__ __launch_bounds__(kSelThreads) void evict_select(const float* lb_all,
-                                                            const int32_t* pos_all,
-                                                            const int32_t* len,
-                                                            const int32_t* start, int cap,
-                                                            int Hkv, const int32_t* tq, int M,
-                                                            UnitInfo* info, int32_t* n_out) {
-  __shared__ uint32_t hist[2048];
-  __shared__ unsigned long long bmin[1024];
-  __shared__ unsigned long long bmax[1024];
-  __shared__ int smem[kSelThreads / 64];
-  __shared__ int out[4];
+// Chunked selection for heads too long for the LDS planner.  Several workgroups
+// per head: histogram passes over slices of the head (radix on the float32-rounded
+// key, 11 + 11 + 10 bits) added into per-head global histograms, one launch per
+// pass; every workgroup of a later launch replays the earlier passes' bucket
+// choices from those histograms (deterministic), so no launch in between is
+// needed.  (Letting the last workgroup of a pass record the choice instead needs
+// a device-wide release fence in every workgroup, which writes back the L2 of its
+// XCD and made the pass several times slower.)  The passes stop once the bucket
+// holding the threshold has at most kSelCand members; these are listed (exact
+// key, slot) and one workgroup per head finishes the selection in LDS.  If more
+// share one float32 key, that workgroup runs exact passes over the whole head
+// instead.
+constexpr int kSelB = 16;       // slots per thread per round
+constexpr int kSelCand = 4096;  // bucket size finished from a list
+constexpr int kSelNT = 256;     // threads of the slice kernels
+constexpr int kSelRounds = 2;   // rounds per slice workgroup
+constexpr int kSelSlice = kSelRounds * kSelNT * kSelB;  // slots per slice workgroup
 
+struct SelArgs {
+  const float* log_beta;
+  const int32_t* pos;
+  const int32_t* len;
+  const int32_t* start;
+  const int32_t* tq;
+  uint32_t* hist;        // [U][3][2048]
+  int32_t* nlist;        // [U]
+  unsigned long long* lk;  // [U][kSelCand] listed exact keys
+  int32_t* ls;           // [U][kSelCand] their slots
+  UnitInfo* info;
+  int32_t* n_out;
+  int32_t cap, Hkv, M;
+};
+
+// Keys of the slots base + e * NT + tid, e < kSelB: every load of the round is
+// issued before the first key is formed.  Slots past n get key 0 (callers skip
+// them).
+template <int NT, typename LB, typename PS>
+__device__ __forceinline__ void sel_keys(const LB& lb, const PS& ps, int base, int n, int tpos,
+                                         double* k) {
+  int p[kSelB];
+  float b[kSelB];
+#pragma unroll
+  for (int e = 0; e < kSelB; ++e) {
+    const int i = min(base + e * NT + (int)threadIdx.x, n - 1);
+    p[e] = ps[i];
+    b[e] = lb ? lb[i] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < kSelB; ++e) {
+    const int d = tpos - p[e];
+    k[e] = (!lb || d == 0) ? 0.0 : (double)d * (double)b[e];  // = retention_key
+  }
+}
+
+// Whether float32-ordered key k32 starts with the pbits-bit prefix.
+__device__ __forceinline__ bool has_prefix(uint32_t k32, uint32_t prefix, int pbits) {
+  return pbits == 0 || (pbits == 32 ? k32 : (k32 >> (32 - pbits))) == prefix;
+}
+
+struct SelPos {
+  uint32_t prefix;  // the fixed top pbits bits of the float32 key
+  int pbits;
+  int r;    // 1-based rank of the threshold among the keys with that prefix
+  int cnt;  // keys with that prefix
+};
+
+// The bucket choices of passes 0 .. upto-1, from the head's histograms (whole
+// workgroup; stops early once the bucket is small enough to list).
+template <int NT>
+__device__ SelPos sel_replay(const uint32_t* gh, int upto, int n, int M, int* smem, int* out) {
+  SelPos sp = {0u, 0, n - M, n};
+  for (int p = 0; p < upto && sp.cnt > kSelCand; ++p) {
+    const int width = p == 2 ? 10 : 11;
+    const uint32_t* h = gh + p * 2048;
+    const int b = select_bucket<NT>(h, 1 << width, sp.r, smem, out);
+    sp.cnt = (int)h[b];
+    sp.prefix = (sp.prefix << width) | (uint32_t)b;
+    sp.pbits += width;
+  }
+  return sp;
+}
+
+// Clears the head's histograms and list counter.
+__global__ __launch_bounds__(kSelNT) void sel_init(SelArgs a) {
   const int u = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int s0 = head_start(start, u);
-  const int n = min(len[u], cap);
-  if (tid == 0) {
-    out[0] = 0;
-    out[1] = 1;
-    out[2] = -1;
-  }
-  if (n <= M) {
-    if (tid == 0) {
-      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, s0, s0};
-      info[u] = z;
-      if (n_out) n_out[u] = 0;
-    }
-    return;
-  }
-  const Ring<const float> lb{lb_all ? lb_all + (size_t)u * cap + s0 : nullptr, cap - s0, cap};
-  const Ring<const int32_t> ps{pos_all + (size_t)u * cap + s0, cap - s0, cap};
-  const int tpos = tq[u / Hkv];
-  int r = n - M;  // 1-based rank of the last evicted element
+  for (int i = threadIdx.x; i < 3 * 2048; i += kSelNT) a.hist[(size_t)u * 3 * 2048 + i] = 0u;
+  if (threadIdx.x == 0) a.nlist[u] = 0;
+}
 
-  // ---- radix select on the float32-rounded key: 11 + 11 + 10 bits
-  uint32_t prefix = 0;
-  int bucket = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    for (int i = tid; i < nb; i += kSelThreads) {
-      hist[i] = 0;
-      if (pass == 2) {
-        bmin[i] = ~0ull;
-        bmax[i] = 0ull;
-      }
+// Histogram pass `pass` over one slice of one head.  (Four copies of every bin,
+// to spread a wave's same-bin atomics, made the pass slower: the larger LDS
+// footprint costs more occupancy than the conflicts it saves.)
+__global__ __launch_bounds__(kSelNT) void sel_hist(SelArgs a, int pass) {
+  __shared__ uint32_t h[2048];
+  __shared__ int smem[kSelNT / 64];
+  __shared__ int out[4];
+  const int u = blockIdx.y, tid = threadIdx.x;
+  const int n = min(a.len[u], a.cap);
+  const int base0 = blockIdx.x * kSelSlice;
+  if (n <= a.M || base0 >= n) return;
+  uint32_t* gh = a.hist + (size_t)u * 3 * 2048;
+  const SelPos sp = sel_replay<kSelNT>(gh, pass, n, a.M, smem, out);
+  if (sp.cnt <= kSelCand) return;
+  const int width = pass == 2 ? 10 : 11;
+  const int nb = 1 << width;
+  const int shift = 32 - sp.pbits - width;
+  for (int i = tid; i < nb; i += kSelNT) h[i] = 0u;
+  __syncthreads();
+  const int s0 = head_start(a.start, u);
+  const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
+                             a.cap - s0, a.cap};
+  const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
+  const int tpos = a.tq[u / a.Hkv];
+  for (int base = base0; base < min(base0 + kSelSlice, n); base += kSelNT * kSelB) {
+    double kk[kSelB];
+    sel_keys<kSelNT>(lb, ps, base, n, tpos, kk);
+#pragma unroll
+    for (int e = 0; e < kSelB; ++e) {
+      if (base + e * kSelNT + tid >= n) continue;
+      const uint32_t k32 = ord32(kk[e]);
+      if (!has_prefix(k32, sp.prefix, sp.pbits)) continue;
+      atomicAdd(&h[(k32 >> shift) & (uint32_t)(nb - 1)], 1u);
     }
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const double k = retention_key(lb, ps, i, tpos);
-      const uint32_t k32 = ord32(k);
-      const bool match = pass == 0 || (k32 >> (shift + (pass == 2 ? 10 : 11))) == prefix;
-      if (match) {
-        const uint32_t d = (k32 >> shift) & (uint32_t)(nb - 1);
-        atomicAdd(&hist[d], 1u);
-        if (pass == 2) {
-          const unsigned long long k64 = ord64(k);
-          atomicMin(&bmin[d], k64);
-          atomicMax(&bmax[d], k64);
+  }
+  __syncthreads();
+  for (int i = tid; i < nb; i += kSelNT)
+    if (h[i]) atomicAdd(&gh[pass * 2048 + i], h[i]);
+}
+
+// Lists the members of the final bucket (exact key, slot) from one slice: first
+// in LDS, then one global reservation per workgroup (a per-head counter taking
+// every wave's reservation serialises at one address).
+__global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
+  __shared__ int smem[kSelNT / 64];
+  __shared__ int out[4];
+  __shared__ unsigned long long ck[kSelCand];
+  __shared__ int cs[kSelCand];
+  __shared__ int nloc, gbase;
+  const int u = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int n = min(a.len[u], a.cap);
+  const int base0 = blockIdx.x * kSelSlice;
+  if (n <= a.M || base0 >= n) return;
+  if (tid == 0) nloc = 0;
+  __syncthreads();
+  const SelPos sp = sel_replay<kSelNT>(a.hist + (size_t)u * 3 * 2048, 3, n, a.M, smem, out);
+  if (sp.cnt > kSelCand) return;
+  const int s0 = head_start(a.start, u);
+  const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
+                             a.cap - s0, a.cap};
+  const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
+  const int tpos = a.tq[u / a.Hkv];
+  for (int base = base0; base < min(base0 + kSelSlice, n); base += kSelNT * kSelB) {
+    double kk[kSelB];
+    sel_keys<kSelNT>(lb, ps, base, n, tpos, kk);
+#pragma unroll
+    for (int e = 0; e < kSelB; ++e) {
+      const int i = base + e * kSelNT + tid;
+      const bool m = i < n && has_prefix(ord32(kk[e]), sp.prefix, sp.pbits);
+      const unsigned long long mask = __ballot(m);
+      if (!mask) continue;
+      int wb = 0;
+      if (lane == 0) wb = atomicAdd(&nloc, __popcll(mask));
+      wb = __shfl(wb, 0, 64);
+      if (m) {
+        const int j = wb + __popcll(mask & ((1ull << lane) - 1ull));
+        if (j < kSelCand) {  // always: at most cnt members match
+          ck[j] = ord64(kk[e]);
+          cs[j] = i;
         }
       }
     }
-    __syncthreads();
-    bucket = select_bucket<kSelThreads>(hist, nb, r, smem, out);
-    prefix = (prefix << (pass == 2 ? 10 : 11)) | (uint32_t)bucket;
   }
-  const uint32_t t32 = prefix;
-  unsigned long long K = bmin[bucket];
-  const unsigned long long kmax = bmax[bucket];
   __syncthreads();
-
-  // ---- exact 64-bit key among the float32 ties (only when they differ)
-  if (K != kmax) {
-    unsigned long long pfx = 0;
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kSelThreads) {
-        const double k = retention_key(lb, ps, i, tpos);
-        if (ord32(k) != t32) continue;
-        const unsigned long long k64 = ord64(k);
-        if (pass == 0 || (k64 >> (shift + 8)) == pfx)
-          atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      const int bk = select_bucket<kSelThreads>(hist, 256, r, smem, out);
-      pfx = (pfx << 8) | (unsigned long long)bk;
+  const int nl = min(nloc, kSelCand);
+  if (nl == 0) return;
+  if (tid == 0) gbase = atomicAdd(&a.nlist[u], nl);
+  __syncthreads();
+  unsigned long long* lk = a.lk + (size_t)u * kSelCand;
+  int32_t* ls = a.ls + (size_t)u * kSelCand;
+  for (int j = tid; j < nl; j += kSelNT) {
+    const int g = gbase + j;
+    if (g < kSelCand) {  // always: exactly cnt members over all slices
+      lk[g] = ck[j];
+      ls[g] = cs[j];
     }
-    K = pfx;
   }
+}
 
-  // ---- slot of the r-th element (slot order) whose exact key is K
-  int sstar = -1;
-  int seen = 0;
-  for (int base = 0; base < n; base += kSelThreads) {
-    const int i = base + tid;
-    bool f = false;
-    if (i < n) {
-      const double k = retention_key(lb, ps, i, tpos);
-      f = ord64(k) == K;
+// One workgroup per head: the threshold (kappa*, slot*) from the list, or from
+// exact passes over the head when more than kSelCand keys share its float32 key.
+__global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ unsigned long long ck[kSelCand];
+  __shared__ int cs[kSelCand];
+  __shared__ unsigned long long kext[2];
+  __shared__ int smem[kSelThreads / 64];
+  __shared__ int out[4];
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int s0 = head_start(a.start, u);
+  const int n = min(a.len[u], a.cap);
+  if (n <= a.M) {
+    if (tid == 0) {
+      UnitInfo z = {0ull, -1, MODE_NOOP, n, n, s0, s0};
+      a.info[u] = z;
+      if (a.n_out) a.n_out[u] = 0;
     }
-    int total;
-    const int excl = block_excl_scan<kSelThreads>(f ? 1 : 0, smem, total);
-    if (f && seen + excl + 1 == r) out[2] = i;
-    __syncthreads();
-    if (seen + total >= r) {
-      sstar = out[2];
-      break;
-    }
-    seen += total;
+    return;
   }
   if (tid == 0) {
-    UnitInfo v = {K, sstar, MODE_EVICT, n, M, s0, s0};
-    info[u] = v;
+    out[2] = -1;
+    kext[0] = ~0ull;
+    kext[1] = 0ull;
+  }
+  __syncthreads();
+  const SelPos sp = sel_replay<kSelThreads>(a.hist + (size_t)u * 3 * 2048, 3, n, a.M, smem, out);
+  int r = sp.r;
+  unsigned long long K;
+  int sstar = -1;
+  if (sp.cnt <= kSelCand) {
+    // the r-th of the listed members in (key, slot) order: radix on the key below
+    // the members' common top bits, then on the slot among equal keys
+    const int nc = min(min(a.nlist[u], sp.cnt), kSelCand);
+    unsigned long long lo = ~0ull, hi = 0ull;
+    for (int j = tid; j < nc; j += kSelThreads) {
+      const unsigned long long k64 = a.lk[(size_t)u * kSelCand + j];
+      ck[j] = k64;
+      cs[j] = a.ls[(size_t)u * kSelCand + j];
+      lo = k64 < lo ? k64 : lo;
+      hi = k64 > hi ? k64 : hi;
+    }
+    if (lo != ~0ull) {
+      atomicMin(&kext[0], lo);
+      atomicMax(&kext[1], hi);
+    }
+    __syncthreads();
+    const unsigned long long kmin = kext[0], kmax = kext[1];
+    K = kmin;
+    if (kmin != kmax) {
+      int top = 63 - __clzll((long long)(kmin ^ kmax));  // highest differing bit
+      unsigned long long pfx = top == 63 ? 0ull : kmin >> (top + 1);
+      for (; top >= 0; top -= 8) {
+        const int width = top + 1 < 8 ? top + 1 : 8;
+        const int shift = top + 1 - width;
+        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        for (int j = tid; j < nc; j += kSelThreads) {
+          const unsigned long long k64 = ck[j];
+          if (top == 63 || (k64 >> (top + 1)) == pfx)
+            atomicAdd(&hist[(k64 >> shift) & ((1u << width) - 1u)], 1u);
+        }
+        __syncthreads();
+        const int bk = select_bucket<kSelThreads>(hist, 1 << width, r, smem, out);
+        pfx = (pfx << width) | (unsigned long long)bk;
+      }
+      K = pfx;
+    }
+    // slot: the r-th smallest among the members whose key is K (slots < 2^30)
+    uint32_t sp2 = 0;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = 20 - 10 * pass;
+      for (int i = tid; i < 1024; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+      for (int j = tid; j < nc; j += kSelThreads) {
+        if (ck[j] != K) continue;
+        const uint32_t sl = (uint32_t)cs[j];
+        if (pass == 0 || (sl >> (shift + 10)) == sp2) atomicAdd(&hist[(sl >> shift) & 1023u], 1u);
+      }
+      __syncthreads();
+      const int bk = select_bucket<kSelThreads>(hist, 1024, r, smem, out);
+      sp2 = (sp2 << 10) | (uint32_t)bk;
+    }
+    sstar = (int)sp2;
+  } else {
+    // more than kSelCand keys share the float32 key t32: the exact key by radix
+    // passes over the head (skipped when those keys are all equal), then the slot
+    // of the r-th of its ties in slot order
+    const uint32_t t32 = sp.prefix;
+    const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
+                               a.cap - s0, a.cap};
+    const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
+    const int tpos = a.tq[u / a.Hkv];
+    unsigned long long lo = ~0ull, hi = 0ull;
+    for (int base = 0; base < n; base += kSelThreads * kSelB) {
+      double kk[kSelB];
+      sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+#pragma unroll
+      for (int e = 0; e < kSelB; ++e) {
+        if (base + e * kSelThreads + tid >= n || ord32(kk[e]) != t32) continue;
+        const unsigned long long k64 = ord64(kk[e]);
+        lo = k64 < lo ? k64 : lo;
+        hi = k64 > hi ? k64 : hi;
+      }
+    }
+    if (lo != ~0ull) {
+      atomicMin(&kext[0], lo);
+      atomicMax(&kext[1], hi);
+    }
+    __syncthreads();
+    K = kext[0];
+    if (K != kext[1]) {
+      unsigned long long pfx = 0;
+      for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        for (int base = 0; base < n; base += kSelThreads * kSelB) {
+          double kk[kSelB];
+          sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+#pragma unroll
+          for (int e = 0; e < kSelB; ++e) {
+            if (base + e * kSelThreads + tid >= n || ord32(kk[e]) != t32) continue;
+            const unsigned long long k64 = ord64(kk[e]);
+            if (pass == 0 || (k64 >> (shift + 8)) == pfx)
+              atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
+          }
+        }
+        __syncthreads();
+        const int bk = select_bucket<kSelThreads>(hist, 256, r, smem, out);
+        pfx = (pfx << 8) | (unsigned long long)bk;
+      }
+      K = pfx;
+    }
+    // a round's ties are counted at once; only the round holding the r-th is
+    // walked in slot order (row e of a round = slots base + e * kSelThreads + tid)
+    int seen = 0;
+    for (int base = 0; base < n && sstar < 0; base += kSelThreads * kSelB) {
+      double kk[kSelB];
+      sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+      bool f[kSelB];
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < kSelB; ++e) {
+        f[e] = base + e * kSelThreads + tid < n && ord64(kk[e]) == K;
+        c += f[e] ? 1 : 0;
+      }
+      const int total = block_sum<kSelThreads>(c, smem);
+      if (seen + total < r) {
+        seen += total;
+        continue;
+      }
+      for (int e = 0; e < kSelB; ++e) {
+        int tot_e;
+        const int excl = block_excl_scan<kSelThreads>(f[e] ? 1 : 0, smem, tot_e);
+        if (f[e] && seen + excl + 1 == r) out[2] = base + e * kSelThreads + tid;
+        __syncthreads();
+        if (seen + tot_e >= r) {
+          sstar = out[2];
+          break;
+        }
+        seen += tot_e;
+      }
+    }
+  }
+  if (tid == 0) {
+    UnitInfo v = {K, sstar, MODE_EVICT, n, a.M, s0, s0};
+    a.info[u] = v;
   }
 }
 
@@ -752,8 +996,13 @@ __device__ __forceinline__ int first_range_ending_after(const int32_t* rg, int n
   return lo;
 }
 
+// Keep flags of the thread's kPerThread consecutive slots i0 .. i0 + kPerThread - 1
+// (i0 = chunk start + tid * kPerThread); called by the whole workgroup.  Eviction
+// keys are formed from coalesced loads (slot chunk + e * kChunkThreads + tid) and
+// the flags handed to the owning threads through kf (kChunk bytes of LDS).
 template <int MODE>
-__device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int n, bool* f) {
+__device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int n, bool* f,
+                                           uint8_t* kf) {
   const int s0 = head_start(a.start, u);
   const size_t row0 = (size_t)u * a.cap + s0;
   const Ring<const int32_t> ps{a.pos + row0, a.cap - s0, a.cap};
@@ -761,16 +1010,31 @@ __device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int
     const UnitInfo inf = a.info[u];
     const Ring<const float> lb{a.log_beta ? a.log_beta + row0 : nullptr, a.cap - s0, a.cap};
     const int tpos = a.tq[u / a.Hkv];
+    const int base = i0 - (int)threadIdx.x * kPerThread;
+    int p[kPerThread];
+    float b[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const int i = i0 + e;
-      if (i < n) {
-        const unsigned long long k64 = ord64(retention_key(lb, ps, i, tpos));
-        f[e] = k64 > inf.kstar || (k64 == inf.kstar && i > inf.sstar);
-      } else {
-        f[e] = false;
-      }
+      const int i = min(base + e * kChunkThreads + (int)threadIdx.x, n - 1);
+      p[e] = ps[i];
+      b[e] = lb ? lb[i] : 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = base + e * kChunkThreads + (int)threadIdx.x;
+      const int d = tpos - p[e];
+      const double k = (!lb || d == 0) ? 0.0 : (double)d * (double)b[e];  // = retention_key
+      const unsigned long long k64 = ord64(k);
+      kf[e * kChunkThreads + threadIdx.x] =
+          i < n && (k64 > inf.kstar || (k64 == inf.kstar && i > inf.sstar));
+    }
+    __syncthreads();
+    static_assert(kPerThread == 16, "one 16-byte LDS read per thread");
+    const uint4 w = *(const uint4*)(kf + threadIdx.x * kPerThread);
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) f[e] = (wv[e >> 2] >> (8 * (e & 3))) & 0xffu;
+    __syncthreads();
   } else {
     // positions increase along the slots: one search for the thread's first slot,
     // then the range index only moves forward
@@ -793,6 +1057,7 @@ __device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int
 template <int MODE>
 __global__ __launch_bounds__(kChunkThreads) void keep_count(KeepArgs a) {
   __shared__ int smem[kChunkThreads / 64];
+  __shared__ __align__(16) uint8_t kf[kChunk];
   const int u = blockIdx.y, c = blockIdx.x;
   if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
   const int n = min(a.len[u], a.cap);
@@ -800,7 +1065,7 @@ __global__ __launch_bounds__(kChunkThreads) void keep_count(KeepArgs a) {
   int cnt = 0;
   if (base < n) {
     bool f[kPerThread];
-    keep_flags<MODE>(a, u, base + threadIdx.x * kPerThread, n, f);
+    keep_flags<MODE>(a, u, base + threadIdx.x * kPerThread, n, f, kf);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) cnt += f[e] ? 1 : 0;
   }
@@ -812,6 +1077,7 @@ template <int MODE>
 __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   __shared__ int smem[kChunkThreads / 64];
   __shared__ int2 stg[kChunk];  // this chunk's staged rows (source, destination)
+  __shared__ __align__(16) uint8_t kf[kChunk];
   __shared__ int nstg;
   const int u = blockIdx.y, c = blockIdx.x;
   if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
@@ -838,7 +1104,7 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   if (threadIdx.x == 0) nstg = 0;
   const int i0 = base + threadIdx.x * kPerThread;
   bool f[kPerThread];
-  keep_flags<MODE>(a, u, i0, n, f);
+  keep_flags<MODE>(a, u, i0, n, f, kf);
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) cnt += f[e] ? 1 : 0;
@@ -1032,7 +1298,7 @@ static size_t plan_lds_limit() {
 
 struct CompactLayout {
   size_t info, counts, keep_src, scratch, tile_mask, tile_base, stage_n, stage_list, copy_list,
-      total;
+      sel_hist, sel_nlist, sel_lk, sel_ls, total;
   int C, Mk, srow, move_rows, row_bytes, Tc;
 };
 
@@ -1059,7 +1325,14 @@ static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
   L.stage_n = L.tile_base + align_up(U * L.Tc * sizeof(int32_t), 256);
   L.stage_list = L.stage_n + align_up(U * sizeof(int32_t), 256);
   L.copy_list = L.stage_list + align_up(U * L.Mk * sizeof(int2), 256);
-  L.total = L.copy_list + align_up(U * L.Mk * sizeof(int2), 256);
+  L.sel_hist = L.copy_list + align_up(U * L.Mk * sizeof(int2), 256);
+  // the chunked selection's histograms and list: only for heads the LDS planner
+  // cannot take
+  const bool chunked = !plan_in_lds(c);
+  L.sel_nlist = L.sel_hist + (chunked ? align_up(U * 3 * 2048 * sizeof(uint32_t), 256) : 0);
+  L.sel_lk = L.sel_nlist + (chunked ? align_up(U * sizeof(int32_t), 256) : 0);
+  L.sel_ls = L.sel_lk + (chunked ? align_up(U * kSelCand * sizeof(uint64_t), 256) : 0);
+  L.total = L.sel_ls + (chunked ? align_up(U * kSelCand * sizeof(int32_t), 256) : 0);
   return L;
 }
 
@@ -1161,12 +1434,31 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     hipLaunchKernelGGL(evict_plan_lds, dim3(cache->B * cache->Hkv), dim3(kSelThreads), lds_keys, s,
                        pa);
   } else {
+    SelArgs sa;
+    char* w = (char*)ws;
+    sa.log_beta = cache->log_beta;
+    sa.pos = cache->pos;
+    sa.len = cache->len;
+    sa.start = cache->start;
+    sa.tq = t;
+    sa.hist = (uint32_t*)(w + L.sel_hist);
+    sa.nlist = (int32_t*)(w + L.sel_nlist);
+    sa.lk = (unsigned long long*)(w + L.sel_lk);
+    sa.ls = (int32_t*)(w + L.sel_ls);
+    sa.info = a.info;
+    sa.n_out = n_evicted;
+    sa.cap = cache->cap;
+    sa.Hkv = cache->Hkv;
+    sa.M = M;
+    const int U = cache->B * cache->Hkv;
+    const dim3 slices((cache->cap + kSelSlice - 1) / kSelSlice, U);
     {
       TraceScope tr(kTrEvictSelect, s);
-      hipLaunchKernelGGL(evict_select, dim3(cache->B * cache->Hkv), dim3(kSelThreads), 0, s,
-                         cache->log_beta, cache->pos, cache->len, cache->start, cache->cap,
-                         cache->Hkv, t, M,
-                         a.info, n_evicted);
+      hipLaunchKernelGGL(sel_init, dim3(U), dim3(kSelNT), 0, s, sa);
+      for (int pass = 0; pass < 3; ++pass)
+        hipLaunchKernelGGL(sel_hist, slices, dim3(kSelNT), 0, s, sa, pass);
+      hipLaunchKernelGGL(sel_collect, slices, dim3(kSelNT), 0, s, sa);
+      hipLaunchKernelGGL(sel_finish, dim3(U), dim3(kSelThreads), 0, s, sa);
     }
     launch_keep_chunks(cache, a, MODE_EVICT, s);
   }

@@ -115,6 +115,33 @@ def test_evict_steady_state_shift():
         check_layout(host_dict(c), ref, f"steady step {s}")
 
 
+def test_evict_ties_and_special_keys_large_heads():
+    """The chunked selection (heads too long for the LDS planner, 40,000 slots):
+    all keys equal (evict by position), log beta = -inf every third slot, +0 / -0
+    and a slot at the decode position, and a cluster of 20,000 keys that round to
+    the same few float32 values but differ as doubles (lb_i = fl32(c / d_i)), the
+    eviction threshold inside the cluster so the exact 64-bit pass and the slot
+    search among exact ties both run."""
+    B, H, n = 1, 4, 40000
+    d = _cache(5, B, H, n, n + 3, 64)
+    lb = d["log_beta"]
+    t = np.array([n - 1], np.int32)                # pos n-1 sits at distance 0
+    lb[0, 0, :n] = np.float32(0.0)                  # every key 0
+    lb[0, 1, ::3] = -np.inf
+    lb[0, 3, :n] = np.where(np.arange(n) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+    lb[0, 3, 1000:30000] = np.float32(-0.001)
+    dist = (t[0] - np.arange(n)).astype(np.float64)
+    cl = np.arange(5000, 25000)
+    c = -5.0
+    lb[0, 2, cl] = (c / dist[cl]).astype(np.float32)
+    keys = dist * lb[0, 2, :n].astype(np.float64)
+    below = int(np.sum(keys < keys[cl].min()))
+    kc = keys[cl]
+    assert len(np.unique(kc.astype(np.float32))) < 40 < len(np.unique(kc))  # float32 ties
+    for M in (1, 20000, 39999, n - below - 10000):
+        _evict_and_check(d, t, M, f"large ties M={M}", max_evict=64)
+
+
 def test_evict_float32_and_d64():
     for dtype, D in (("f32", 64), ("bf16", 64), ("f32", 128)):
         d = _cache(31, 1, 2, 3000, 3001, D, dtype=dtype)
