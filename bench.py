@@ -133,11 +133,21 @@ def steady_bench(args):
     planned = [torch.cuda.Event() for _ in range(L)]
     deferred = args.schedule == "deferred"
     fused_append = args.schedule in (None, "fused_append")  # the default here
+    one = args.schedule == "evict_one"
 
     def step():
         main = torch.cuda.current_stream()
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
+            if one:
+                # the attention call appends the decode token; the layer's eviction
+                # (one launch) follows it on the side stream, beside the next attention
+                kvb.kv_attn_decode(kvs[layer], q, t, k_new=kn, v_new=vn, log_beta_new=lb,
+                                   num_splits=P, out=out, lse=lse, ws=ws_a, stream=main)
+                attended[layer].record(main)
+                side.wait_event(attended[layer])
+                kvb.kv_evict_one(kvs[layer], t, M, n_evicted=nev[layer], stream=side)
+                continue
             if fused_append:
                 # the attention call appends the decode token; the layer's plan and
                 # compaction follow it on the side stream, beside the next attention
@@ -190,7 +200,7 @@ def steady_bench(args):
     assert bool((nev == 1).all()), "steady state: one eviction per head and layer"
     # eager steps with the kernel trace
     kvb.trace_enable(16 * L * args.steps + 64, ("attn_split", "attn_merge", "append",
-                                                "evict_select", "compact_move"))
+                                                "evict_select", "compact_move", "evict_one"))
     e0.record()
     for _ in range(args.steps):
         step()
@@ -681,15 +691,17 @@ def main():
                     help="run each layer's eviction planning on the attention stream (no overlap)")
     ap.add_argument("--schedule", default=None,
                     choices=["plan_beside", "both_beside", "deferred", "deferred_plan",
-                             "fused_append"],
+                             "fused_append", "evict_one"],
                     help="deferred_plan (default of the 32K step): all layers' eviction "
                          "plans and compactions follow the last attention, each plan running "
                          "beside the previous layer's compaction; deferred: each plan beside "
                          "its layer's attention, the compactions after the last attention; "
                          "plan_beside: each compaction right after its layer's attention; "
                          "both_beside: each compaction beside the next layer's attention; "
-                         "fused_append (default of --steady): the attention call appends, each "
-                         "layer's plan and compaction beside the next layer's attention")
+                         "fused_append (--steady): the attention call appends, each layer's "
+                         "plan and compaction beside the next layer's attention; evict_one "
+                         "(--steady): the attention call appends, each layer's one-launch "
+                         "eviction (kv_evict_one) beside the next layer's attention")
     ap.add_argument("--graph", action="store_true",
                     help="decode / ASM step: replay the step as one captured HIP graph")
     ap.add_argument("--fused", action="store_true",

@@ -19,7 +19,8 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    asm_lookup_merge_hier_workspace, asm_lookup_merge_workspace,
                    kv_append, kv_attn_decode, kv_attn_decode_asm, kv_attn_decode_asm_workspace,
                    kv_attn_decode_compact, kv_attn_decode_splits, kv_attn_decode_workspace,
-                   kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_plan,
+                   kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_one,
+                   kv_evict_plan,
                    kv_latent_absorb, kv_latent_absorb_workspace, kv_latent_read,
                    kv_evict_to_budget,
                    kv_evict_workspace, library, library_path, strerror, trace_disable,
@@ -27,7 +28,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
 
 __all__ = [
     "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
-    "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_attn_decode_compact",
+    "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_evict_one", "kv_attn_decode_compact",
     "kv_attn_decode_asm", "kv_attn_decode_asm_workspace",
     "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",
     "kv_latent_absorb", "kv_latent_absorb_workspace", "kv_latent_read",

@@ -56,6 +56,7 @@ def library():
             "kv_evict_to_budget": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
             "kv_evict_plan": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
             "kv_evict_apply": (I32, [CP, I32, P, SZ, P]),
+            "kv_evict_one": (I32, [CP, P, I32, P, I32, P, P]),
             "kv_append": (I32, [CP, P, P, P, P, P, SZ, P]),
             "kv_attn_decode_compact": (I32, [CP, P, I32, P, F, I32, I32, I32, P, P, P, SZ, P, SZ,
                                              P]),
@@ -324,6 +325,25 @@ def kv_evict_apply(cache: KVCache, M: int, ws, stream=None):
     _check(st, "kv_evict_apply")
 
 
+def kv_evict_one(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=None, stream=None):
+    """Eviction for heads at most one token over budget M (see kv_evict_one in
+    kvbound.h): one launch, no workspace.  Returns n_evicted [B][Hkv] int32 (1, 0,
+    or -(n - M) for a head left untouched because it is further over)."""
+    _need(t, "t", torch.int32)
+    B, H = cache.length.shape
+    if n_evicted is None:
+        n_evicted = torch.empty((B, H), dtype=torch.int32, device=t.device)
+    _need(n_evicted, "n_evicted", torch.int32)
+    me = 0
+    if evicted_pos is not None:
+        _need(evicted_pos, "evicted_pos", torch.int32)
+        me = evicted_pos.shape[-1]
+    st = library().kv_evict_one(cache.desc, _ptr(t), int(M), _ptr(evicted_pos), me,
+                                _ptr(n_evicted), _stream(stream))
+    _check(st, "kv_evict_one")
+    return n_evicted
+
+
 def kv_attn_decode_compact(cache: KVCache, q, t, M: int, ws_evict, scale: float = 0.0,
                            num_splits: int = 0, phase: int = 0, out=None, lse=None, ws=None,
                            stream=None):
@@ -398,7 +418,7 @@ TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "asm_finalize": 256, "attn_fused": 512, "asm_prefix": 1024,
               "asm_prefix_merge": 2048, "km_assign": 4096, "km_update": 8192,
               "asm_aggregate": 16384, "asm_vt": 32768, "latent_absorb": 65536,
-              "latent_read": 131072}
+              "latent_read": 131072, "evict_one": 262144}
 
 
 def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:

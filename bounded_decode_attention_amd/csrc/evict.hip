@@ -1273,6 +1273,175 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
   }
 }
 
+// ---------------------------------------------------------------- one eviction
+// kv_evict_one: a head exactly one token over its budget loses the token with the
+// lowest (kappa, slot) -- the same rule as the general selection with n - M = 1 --
+// and the gap closes by shifting the shorter side one slot (with a start array:
+// the rows before it up, start + 1, when there are fewer of them than after it;
+// otherwise the rows after it down), the direction the general planner picks for
+// one eviction.  One 1024-thread workgroup per head: an argmin over the head's keys
+// (coalesced, 16 slots in flight per thread), then the shift in chunks of rows,
+// each chunk read into registers completely before any of it is written.
+struct OneArgs {
+  void* k;
+  void* v;
+  float* log_beta;
+  int32_t* pos;
+  int32_t* len;
+  int32_t* start;
+  const int32_t* tq;
+  int32_t* evicted_pos;
+  int32_t* n_out;
+  int32_t cap, Hkv, M, max_evict, row_bytes;
+};
+constexpr int kOneItems = 8;  // 16-byte items per thread per chunk
+
+__global__ __launch_bounds__(kSelThreads) void evict_one(OneArgs a) {
+  __shared__ unsigned long long wkey[kSelThreads / 64];
+  __shared__ int wslot[kSelThreads / 64];
+  __shared__ int es;
+  const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int s0 = head_start(a.start, u);
+  const int n = min(a.len[u], a.cap);
+  if (n <= a.M || n > a.M + 1) {
+    if (tid == 0 && a.n_out) a.n_out[u] = n <= a.M ? 0 : -(n - a.M);
+    return;
+  }
+  const size_t row0 = (size_t)u * a.cap;
+  const Ring<const float> lb{a.log_beta ? a.log_beta + row0 + s0 : nullptr, a.cap - s0, a.cap};
+  const Ring<const int32_t> ps{a.pos + row0 + s0, a.cap - s0, a.cap};
+  const int tpos = a.tq[u / a.Hkv];
+
+  // ---- the slot with the lowest (exact key, slot)
+  unsigned long long bk = ~0ull;
+  int bs = 0x7FFFFFFF;
+  for (int base = 0; base < n; base += kSelThreads * kSelB) {
+    double kk[kSelB];
+    sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+#pragma unroll
+    for (int e = 0; e < kSelB; ++e) {
+      const int i = base + e * kSelThreads + tid;
+      if (i >= n) continue;
+      const unsigned long long k64 = ord64(kk[e]);
+      if (k64 < bk || (k64 == bk && i < bs)) {
+        bk = k64;
+        bs = i;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long ok = __shfl_xor(bk, o, 64);
+    const int os = __shfl_xor(bs, o, 64);
+    if (ok < bk || (ok == bk && os < bs)) {
+      bk = ok;
+      bs = os;
+    }
+  }
+  if (lane == 0) {
+    wkey[w] = bk;
+    wslot[w] = bs;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long k = wkey[0];
+    int sl = wslot[0];
+    for (int i = 1; i < kSelThreads / 64; ++i)
+      if (wkey[i] < k || (wkey[i] == k && wslot[i] < sl)) {
+        k = wkey[i];
+        sl = wslot[i];
+      }
+    es = sl;
+    if (a.evicted_pos && a.max_evict > 0) a.evicted_pos[(size_t)u * a.max_evict] = ps[sl];
+    if (a.n_out) a.n_out[u] = 1;
+  }
+  wait_vmem_all();
+  __syncthreads();
+  const int e = es;
+
+  // ---- close the gap: rows (e, n) down one slot, or rows [0, e) up one
+  const bool up = a.start != nullptr && e < n - 1 - e;
+  const int ppr = a.row_bytes / 16;
+  const int per = 2 * ppr + 1;  // 16-byte pieces of K and V, then (log beta, pos)
+  const int R = (kSelThreads * kOneItems) / per;  // rows per chunk
+  unsigned char* kb = (unsigned char*)a.k + row0 * a.row_bytes;
+  unsigned char* vb = (unsigned char*)a.v + row0 * a.row_bytes;
+  float* lbb = a.log_beta ? a.log_beta + row0 : nullptr;
+  int32_t* pb = a.pos + row0;
+  const int first = up ? 0 : e + 1, last = up ? e : n;  // rows [first, last) move
+  const int nchunks = (last - first + R - 1) / R;
+  // down: ascending chunks; up: descending.  Chunk c + 1's sources never overlap
+  // chunk c's destinations, and chunk c's sources are all in registers (every
+  // thread waited, then the barrier) before chunk c + 1 -- whose destinations take
+  // chunk c's last source -- stores; so chunk c + 1 is loaded while c is stored.
+  auto chunk = [&](int c, int& r0, int& r1) {
+    r0 = up ? max(last - (c + 1) * R, first) : first + c * R;
+    r1 = up ? last - c * R : min(first + (c + 1) * R, last);
+  };
+  auto load = [&](int c, u32x4* buf) {
+    int r0, r1;
+    chunk(c, r0, r1);
+    const int items = (r1 - r0) * per;
+#pragma unroll
+    for (int q = 0; q < kOneItems; ++q) {
+      const int it = tid + q * kSelThreads;
+      buf[q] = u32x4{0u, 0u, 0u, 0u};
+      if (it < items) {
+        const int row = r0 + it / per;
+        const int pt = it - (it / per) * per;
+        const int sj = s0 + row;
+        const int src = sj < a.cap ? sj : sj - a.cap;
+        if (pt < 2 * ppr) {
+          const bool isv = pt >= ppr;
+          buf[q] = *(const u32x4*)((isv ? vb : kb) + (size_t)src * a.row_bytes +
+                                   16 * (isv ? pt - ppr : pt));
+        } else {
+          buf[q] = u32x4{lbb ? __float_as_uint(lbb[src]) : 0u, (uint32_t)pb[src], 0u, 0u};
+        }
+      }
+    }
+  };
+  auto store = [&](int c, const u32x4* buf) {
+    int r0, r1;
+    chunk(c, r0, r1);
+    const int items = (r1 - r0) * per;
+#pragma unroll
+    for (int q = 0; q < kOneItems; ++q) {
+      const int it = tid + q * kSelThreads;
+      if (it >= items) continue;
+      const int row = r0 + it / per;
+      const int pt = it - (it / per) * per;
+      const int dj = s0 + (up ? row + 1 : row - 1);
+      const int dst = dj < a.cap ? dj : dj - a.cap;
+      if (pt < 2 * ppr) {
+        const bool isv = pt >= ppr;
+        *(u32x4*)((isv ? vb : kb) + (size_t)dst * a.row_bytes + 16 * (isv ? pt - ppr : pt)) =
+            buf[q];
+      } else {
+        if (lbb) lbb[dst] = __uint_as_float(buf[q][0]);
+        pb[dst] = (int32_t)buf[q][1];
+      }
+    }
+  };
+  u32x4 b0[kOneItems], b1[kOneItems];
+  if (nchunks > 0) load(0, b0);
+  for (int c = 0; c < nchunks; c += 2) {
+    wait_vmem_all();
+    __syncthreads();
+    if (c + 1 < nchunks) load(c + 1, b1);
+    store(c, b0);
+    if (c + 1 >= nchunks) break;
+    wait_vmem_all();
+    __syncthreads();
+    if (c + 2 < nchunks) load(c + 2, b0);
+    store(c + 1, b1);
+  }
+  if (tid == 0) {
+    a.len[u] = n - 1;
+    if (up) a.start[u] = s0 + 1 < a.cap ? s0 + 1 : 0;
+  }
+}
+
 // ---------------------------------------------------------------- host
 // Dynamic LDS available to evict_plan_lds (static LDS of the kernel excluded).
 static size_t plan_lds_limit() {
@@ -1624,6 +1793,34 @@ extern "C" int32_t kv_evict_to_budget(const kvb_cache* cache, const int32_t* t, 
   int32_t st = kv_evict_plan(cache, t, M, evicted_pos, max_evict, n_evicted, ws, ws_bytes, stream);
   if (st) return st;
   return kv_evict_apply(cache, M, ws, ws_bytes, stream);
+}
+
+extern "C" int32_t kv_evict_one(const kvb_cache* cache, const int32_t* t, int32_t M,
+                                int32_t* evicted_pos, int32_t max_evict, int32_t* n_evicted,
+                                void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!t || M < 0 || max_evict < 0 || (evicted_pos && max_evict == 0)) return KVB_EINVAL;
+  if ((st = check_device())) return st;
+  OneArgs a;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.log_beta = cache->log_beta;
+  a.pos = cache->pos;
+  a.len = cache->len;
+  a.start = cache->start;
+  a.tq = t;
+  a.evicted_pos = evicted_pos;
+  a.n_out = n_evicted;
+  a.cap = cache->cap;
+  a.Hkv = cache->Hkv;
+  a.M = M;
+  a.max_evict = max_evict;
+  a.row_bytes = cache->D * (cache->dtype == KVB_BF16 ? 2 : 4);
+  hipStream_t s = (hipStream_t)stream;
+  TraceScope tr(kTrEvictOne, s);
+  hipLaunchKernelGGL(evict_one, dim3(cache->B * cache->Hkv), dim3(kSelThreads), 0, s, a);
+  return launch_status();
 }
 
 extern "C" int32_t kv_erase_ranges(const kvb_cache* cache, const int32_t* ranges,

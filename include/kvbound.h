@@ -211,6 +211,23 @@ int32_t kv_evict_plan(const kvb_cache* cache, const int32_t* t, int32_t M, int32
 int32_t kv_evict_apply(const kvb_cache* cache, int32_t M, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kv_evict_to_budget for the steady state of bounded decoding, where each step
+ * puts a head at most one token over its budget ([TRIM] 2.2, inference: one token
+ * in, the lowest-retention token out): in one launch, with no workspace.  A head
+ * with n = M + 1 live tokens loses the slot with the lowest (kappa, slot)
+ * (kappa as for kv_evict_to_budget) and is compacted exactly as
+ * kv_evict_to_budget compacts it: with a start array the rows before the evicted
+ * slot move up one slot (start + 1, mod cap) when there are fewer of them than
+ * rows after it, otherwise the rows after it move down one slot.  Heads with
+ * n <= M are left as they are (n_evicted 0); heads with n > M + 1 are also left as
+ * they are, with n_evicted = -(n - M) (use kv_evict_to_budget for them).
+ *   t, M, evicted_pos, max_evict, n_evicted as kv_evict_to_budget (at most one
+ *   position is written per head).
+ */
+int32_t kv_evict_one(const kvb_cache* cache, const int32_t* t, int32_t M, int32_t* evicted_pos,
+                     int32_t max_evict, int32_t* n_evicted, void* stream);
+
+/*
  * Attention and the planned compaction in one pass over the cache ([TRIM] 2.1 and
  * 2.2): the result equals kv_attn_decode (no append) followed by kv_evict_apply,
  * for a plan made by kv_evict_plan(cache, t, M, ..., ws_evict) with no cache write

@@ -222,10 +222,12 @@ def test_start_erase():
     assert np.array_equal(to_host(c.start), starts)
 
 
-def test_start_steady_loop():
+@pytest.mark.parametrize("one", [False, True])
+def test_start_steady_loop(one):
     """Decode steps at budget M (append, attend, evict one) with and without a start
     array, 4 spare slots: outputs bit-identical, layouts equal to the oracle, and
-    heads wrap around the end of their slots."""
+    heads wrap around the end of their slots.  Eviction by kv_evict_to_budget, or
+    by kv_evict_one."""
     B, H, Hq, D, M = 2, 2, 8, 128, 300
     cap = M + 4
     d = _dense(41, B, H, M, cap, D)
@@ -247,7 +249,11 @@ def test_start_steady_loop():
         for c in (plain, st):
             o, l = kvb.kv_attn_decode(c, to_dev(q), to_dev(t), k_new=to_dev(kn), v_new=to_dev(vn),
                                       log_beta_new=to_dev(lbn))
-            kvb.kv_evict_to_budget(c, to_dev(t), M)
+            if one:
+                ne = kvb.kv_evict_one(c, to_dev(t), M)
+                assert bool((ne == 1).all())
+            else:
+                kvb.kv_evict_to_budget(c, to_dev(t), M)
             outs.append((o, l))
         torch.cuda.synchronize()
         assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), s
@@ -316,3 +322,106 @@ def test_start_fused_entry_falls_back():
     ref, ref_ev, _ = oracle.evict_to_budget(oracle.Cache.from_arrays(d), t, M)
     check_layout(_logical(c), ref, "fused entry layout")
     assert np.array_equal(to_host(c.start), _expected_start(d, ref_ev, starts, cap))
+
+
+def _copy_cache(c: kvb.KVCache) -> kvb.KVCache:
+    cl = (lambda x: None if x is None else x.clone())
+    return kvb.KVCache(cl(c.k), cl(c.v), cl(c.log_beta), cl(c.pos), cl(c.length),
+                       start=cl(c.start))
+
+
+def _same_cache(c1: kvb.KVCache, c2: kvb.KVCache, what):
+    """Bit-equal lengths, starts and live rows (slot by slot)."""
+    assert torch.equal(c1.length, c2.length), f"{what} len"
+    if c1.start is not None:
+        assert torch.equal(c1.start, c2.start), f"{what} start"
+    ln = to_host(c1.length)
+    st = to_host(c1.start) if c1.start is not None else np.zeros_like(ln)
+    cap = c1.k.shape[2]
+    arrs = [(to_host(getattr(c1, nm)), to_host(getattr(c2, nm)), nm)
+            for nm in ("k", "v", "pos", "log_beta") if getattr(c1, nm) is not None]
+    for b in range(ln.shape[0]):
+        for g in range(ln.shape[1]):
+            sl = _ring(int(st[b, g]), int(ln[b, g]), cap)
+            for x1, x2, nm in arrs:
+                assert np.array_equal(x1[b, g, sl], x2[b, g, sl]), f"{what} ({b},{g}) {nm}"
+
+
+@pytest.mark.parametrize("ring", [True, False])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_evict_one_equals_evict_to_budget(ring, dtype, D):
+    """kv_evict_one on heads one token over M: the same evicted position, layout,
+    len and start as kv_evict_to_budget (evicted slot at the first / last slot, in
+    the middle, at the tie e = n - 1 - e, equal keys resolved by slot, log beta =
+    -inf), heads at or below M untouched, heads further over flagged and untouched;
+    the logical layout also against the oracle."""
+    B, H, M = 2, 6, 300
+    n = M + 1
+    cap = n + 20
+    d = _dense(11 + D, B, H, n, cap, D, dtype=dtype)
+    lb = d["log_beta"]
+    lb[0, 0, :n] = -0.5
+    lb[0, 0, 0] = -60.0                                      # lowest key at slot 0
+    lb[0, 1, :n] = -0.01
+    lb[0, 1, n - 1] = -np.inf                                # at the last slot
+    lb[0, 2, :n] = 0.0                                       # every key 0: slot 0 goes
+    lb[0, 3, :n] = -0.01
+    lb[0, 3, 150] = -np.inf                                  # e = 150 = n - 1 - e
+    lb[0, 4, :n] = -0.01
+    lb[0, 4, 149] = -np.inf                                  # just below the middle
+    lb[1, 0, :n] = -0.01
+    lb[1, 0, 151] = -np.inf                                  # just above the middle
+    d["len"][1, 1] = M                                       # at budget: untouched
+    d["len"][1, 2] = M - 7
+    d["len"][1, 3] = M + 3                                   # further over: flagged
+    t = np.array([n + 2, n + 9], np.int32)
+    rng = np.random.default_rng(D)
+    starts = np.zeros((B, H), np.int64)
+    if ring:
+        starts = rng.integers(0, cap, (B, H))
+        starts[0, 5] = cap - 1                               # the ring wraps at once
+    c1 = _placed(d, starts, cap, 3)
+    if not ring:
+        c1 = kvb.KVCache(c1.k, c1.v, c1.log_beta, c1.pos, c1.length)
+    c2 = _copy_cache(c1)
+    say("evict_one", ring, dtype, D)
+    ev1 = torch.full((B, H, 2), -7, dtype=torch.int32, device="cuda")
+    n1 = kvb.kv_evict_one(c1, to_dev(t), M, evicted_pos=ev1)
+    torch.cuda.synchronize()
+    n1h = to_host(n1)
+    assert n1h[1, 3] == -3 and n1h[1, 1] == 0 and n1h[1, 2] == 0
+    assert int(to_host(c1.length)[1, 3]) == M + 3, "flagged head untouched"
+    # the general path on the copy, with the flagged head brought to M + 1 first
+    # in neither: compare every other head
+    ev2 = torch.full((B, H, 2), -7, dtype=torch.int32, device="cuda")
+    keep13 = c2.length[1, 3].item()
+    c2.length[1, 3] = M
+    n2 = kvb.kv_evict_to_budget(c2, to_dev(t), M, evicted_pos=ev2)
+    torch.cuda.synchronize()
+    c2.length[1, 3] = keep13
+    n2h = to_host(n2)
+    n2h[1, 3] = -3
+    assert np.array_equal(n1h, n2h), "n_evicted"
+    e1, e2 = to_host(ev1), to_host(ev2)
+    for b in range(B):
+        for g in range(H):
+            if n1h[b, g] == 1:
+                assert e1[b, g, 0] == e2[b, g, 0], f"evicted pos ({b},{g})"
+    if ring:
+        st1, st2 = to_host(c1.start), to_host(c2.start)
+        assert np.array_equal(np.delete(st1.ravel(), 9), np.delete(st2.ravel(), 9))
+    # the flagged head's rows were never touched in either; compare the others
+    c2.length[1, 3] = c1.length[1, 3]
+    if ring:
+        c2.start[1, 3] = c1.start[1, 3]
+    _same_cache(c1, c2, f"evict_one ring={ring} {dtype} D={D}")
+    # against the oracle (logical layout; the flagged head excluded)
+    dd = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+    dd["len"][1, 3] = M
+    ref, _, _ = oracle.evict_to_budget(oracle.Cache.from_arrays(dd), t, M)
+    got = _logical(c1) if ring else {"k": to_host(c1.k), "v": to_host(c1.v),
+                                     "log_beta": to_host(c1.log_beta), "pos": to_host(c1.pos),
+                                     "len": to_host(c1.length)}
+    got["len"] = got["len"].copy()
+    got["len"][1, 3] = M
+    check_layout(got, ref, f"evict_one oracle ring={ring}")
