@@ -703,7 +703,11 @@ def main():
                          "(--steady): the attention call appends, each layer's one-launch "
                          "eviction (kv_evict_one) beside the next layer's attention")
     ap.add_argument("--graph", action="store_true",
-                    help="decode / ASM step: replay the step as one captured HIP graph")
+                    help="ASM step: replay the step as one captured HIP graph (the decode "
+                         "step does so unless --eager)")
+    ap.add_argument("--eager", action="store_true",
+                    help="decode step: launch the step's kernels one by one instead of "
+                         "replaying the step captured once as a HIP graph")
     ap.add_argument("--fused", action="store_true",
                     help="fused attention + compaction kernels (kv_attn_decode_compact) instead "
                          "of attention followed by a separate compaction pass")
@@ -890,7 +894,7 @@ def main():
         step(torch.cuda.current_stream())
     torch.cuda.synchronize()
     graph = None
-    if args.graph:
+    if not args.eager:
         # the whole step (both streams) captured once; replayed after each restore
         restore()
         torch.cuda.synchronize()
@@ -1011,7 +1015,7 @@ def main():
         "device_copy_gbps": round(copy_gbps, 1), "copy_frac": round(gbps / copy_gbps, 4),
         "bytes_per_step": total_b, "moved_rows_per_step": moved,
         "eager_ms_per_step": round(sum(eager_times) / len(eager_times), 4),
-        # with --graph the replays carry no events: kernel times come from the
+        # graph replays carry no events: kernel times come from the
         # eager steps that follow them (same kernels, same inputs)
         "kernel_times_from": "eager steps" if graph is not None else "timed steps",
         "roofline": {"bound": "hbm", "kernel": kernel,
