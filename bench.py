@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -46,8 +47,9 @@ def source_digest(path):
 
 def cpu_baseline(w, host_units, t, M, budget_s=12.0):
     """The float64 oracle, as it stands, on whole heads of one layer (append +
-    attention for the head's query group + eviction + compaction), timed until
-    ``budget_s`` of CPU work; extrapolated to the full step (units x layers)."""
+    attention for the head's query group + eviction + compaction), the layer's heads
+    taken in turn (again from the first once all were run) until ``budget_s`` of CPU
+    work; extrapolated to the full step (units x layers)."""
     import numpy as np
 
     import oracle
@@ -57,9 +59,11 @@ def cpu_baseline(w, host_units, t, M, budget_s=12.0):
         threads = max([i.get("num_threads", 1) for i in info] + [1])
     except Exception:  # pragma: no cover
         threads = 1
+    if not host_units:
+        return None
     done = 0
     elapsed = 0.0
-    for (k, v, lb, pos, n, q, kn, vn, lbn) in host_units:
+    for (k, v, lb, pos, n, q, kn, vn, lbn) in itertools.cycle(host_units):
         t0 = time.perf_counter()
         c = oracle.Cache(k[None, None].copy(), v[None, None].copy(), lb[None, None].copy(),
                          pos[None, None].copy(), np.array([[n]], np.int32))
@@ -76,9 +80,10 @@ def cpu_baseline(w, host_units, t, M, budget_s=12.0):
     unit_s = elapsed / done
     step_s = unit_s * w.units * w.layers
     return {"value": 1.0 / step_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} whole KV heads of layer 0 ({w.ctx + 1} tokens, {w.group} query "
-                      f"heads each: append + attention + eviction to {M} + compaction), "
-                      f"{elapsed:.1f} s, extrapolated x{w.units} heads x{w.layers} layers",
+            "sample": f"{done} runs over the {len(host_units)} whole KV heads of layer 0 "
+                      f"({w.ctx + 1} tokens, {w.group} query heads each: append + attention "
+                      f"+ eviction to {M} + compaction), {elapsed:.1f} s, extrapolated to "
+                      f"{w.units} heads x {w.layers} layers",
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
