@@ -32,6 +32,8 @@ Every function is a direct, unblocked statement of what the pages define:
   outer-product fast weights (M, b) and the gated residual read-out ("IndexMem:
   Learned KV-Cache Eviction with Latent Memory for Long-Context LLM Inference",
   technical summary, section 2, part B).
+* ``decode``      -- the decode loop (append, attend, evict) of "Cache What
+  Lasts", section 2.2 (inference).
 * ``bytes_model`` -- KV bytes per token, pinned to IndexMem's memory-wall figure
   ("IndexMem: Learned KV-Cache Eviction with Latent Memory for Long-Context LLM
   Inference", technical summary, section 1).
@@ -50,7 +52,7 @@ from .asm import (cosine_similarities, cosine_lookup, asm_merge, asm_lookup_merg
                   hier_lookup, asm_lookup_merge_hier)
 from .asm_build import (chunk_bounds, prefix_states, nearest_centroid, centroid_update,
                         kmeans, aggregate_states, build_memory)
-from .bytes_model import kv_bytes_per_token, attention_layer_bytes
+from .bytes_model import kv_bytes_per_token
 from .latent import phi, latent_absorb, latent_read, latent_residual
 from .decode import run_decode_steps
 
@@ -63,6 +65,6 @@ __all__ = [
     "hier_lookup", "asm_lookup_merge_hier",
     "chunk_bounds", "prefix_states", "nearest_centroid", "centroid_update", "kmeans",
     "aggregate_states", "build_memory",
-    "kv_bytes_per_token", "attention_layer_bytes", "run_decode_steps",
+    "kv_bytes_per_token", "run_decode_steps",
     "phi", "latent_absorb", "latent_read", "latent_residual",
 ]

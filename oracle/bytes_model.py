@@ -16,20 +16,3 @@ def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, elem_bytes: in
     """Bytes of K plus V for one token across all layers and KV heads."""
     return 2 * layers * kv_heads * head_dim * elem_bytes
 
-
-def attention_layer_bytes(units: int, n: int, head_dim: int, elem_bytes: int,
-                          retention: bool, batch: int, hq: int, moved: int = 0,
-                          evict: bool = False) -> int:
-    """Algorithmic bytes of one layer's decode step (each byte touched once).
-
-    units = B * Hkv heads each read n K rows and n V rows; the retention array
-    (4 B) and positions (4 B) are read once per slot when the bias or eviction
-    needs them; each moved row (K, V, log beta, pos) is read and written once;
-    q is read and (out, lse) written once.
-    """
-    A = units * n * 2 * head_dim * elem_bytes
-    if retention or evict:
-        A += units * n * 8
-    A += moved * 2 * (2 * head_dim * elem_bytes + 8)
-    A += batch * hq * head_dim * elem_bytes + batch * hq * (head_dim + 1) * 4
-    return A

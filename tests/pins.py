@@ -483,7 +483,217 @@ def check_bytes_model():
     assert per_tok * (1 << 20) == 320 * (1 << 30)
 
 
+# ---------------------------------------------------------------- P13
+def _sdpa_heads(q, K, V, mask, scale):
+    """torch SDPA (float64, CPU) over [B][H] heads of one query each."""
+    qt = torch.tensor(q, dtype=torch.float64).unsqueeze(2)          # [B][H][1][D]
+    Kt = torch.tensor(K, dtype=torch.float64)                       # [B][H][n][D]
+    Vt = torch.tensor(V, dtype=torch.float64)
+    mt = torch.tensor(mask, dtype=torch.float64).unsqueeze(2)       # [B][H][1][n]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mt,
+                                                         scale=scale)
+    return o.squeeze(2).numpy()
+
+
+def _retention_mask(lb32, pos, t, n, cap):
+    """Additive mask of one head: log(beta^d) from the plain power (no product of
+    logs), -inf for slots at or beyond the live length."""
+    m = np.full(cap, -np.inf)
+    for i in range(n):
+        d = int(t - pos[i])
+        if lb32 is None:
+            m[i] = 0.0
+            continue
+        w = math.exp(float(lb32[i])) ** d                  # beta^0 == 1, also for beta == 0
+        m[i] = math.log(w) if w > 0.0 else -np.inf
+    return m
+
+
+def check_decode_attention_gqa(seed=13):
+    """Batched grouped-query attention against torch SDPA with K and V repeated per
+    group (repeat_interleave: query head h reads KV head h // G), on ragged lengths
+    (an empty head included), gapped positions and a distinct decode position per
+    sequence.  scale None (or <= 0) must be torch's own default 1/sqrt(D)."""
+    r = _rng(seed)
+    B, Hkv, G, cap, D = 2, 3, 4, 21, 16
+    Hq = Hkv * G
+    k = r.standard_normal((B, Hkv, cap, D)) * 1.5
+    v = r.standard_normal((B, Hkv, cap, D))
+    q = r.standard_normal((B, Hq, D))
+    length = np.array([[21, 7, 0], [13, 1, 19]], np.int32)
+    pos = np.zeros((B, Hkv, cap), np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            pos[b, g] = np.sort(r.choice(60, size=cap, replace=False))
+    t = np.array([int(pos[0].max()) + 2, int(pos[1].max())], np.int64)
+    lb = np.log(r.uniform(0.6, 1.0, size=(B, Hkv, cap))).astype(np.float32)
+    # the decode token itself (distance 0) with beta = 0 in one head
+    pos[1, 2, length[1, 2] - 1] = t[1]
+    lb[1, 2, length[1, 2] - 1] = -np.inf
+    for log_beta in (None, lb):
+        mask = np.stack([np.stack([_retention_mask(None if log_beta is None else
+                                                   log_beta[b, g], pos[b, g], t[b],
+                                                   int(length[b, g]), cap)
+                                   for g in range(Hkv)]) for b in range(B)])
+        Kr = np.repeat(k, G, axis=1)
+        Vr = np.repeat(v, G, axis=1)
+        Mr = np.repeat(mask, G, axis=1)
+        live = np.repeat(length, G, axis=1) > 0
+        Mr_safe = np.where(live[:, :, None], Mr, 0.0)        # SDPA of an empty head is NaN
+        for scale, torch_scale in ((None, None), (0.0, None), (0.37, 0.37)):
+            ref = _sdpa_heads(q, Kr, Vr, Mr_safe, torch_scale)
+            sc = 1.0 / math.sqrt(D) if torch_scale is None else torch_scale
+            logits = torch.tensor(np.einsum("bhnd,bhd->bhn", Kr, q) * sc + Mr_safe)
+            ref_l = torch.logsumexp(logits, dim=-1).numpy()
+            out, lse = OT.decode_attention(k, v, log_beta, pos, length, q, t, scale)
+            for b in range(B):
+                for h in range(Hq):
+                    if live[b, h]:
+                        assert np.max(np.abs(out[b, h] - ref[b, h])) < 1e-12, \
+                            "GQA attention != SDPA with K/V repeated per group"
+                        assert abs(lse[b, h] - ref_l[b, h]) < 1e-12, "GQA lse != logsumexp"
+                    else:                                  # empty head: (0, -inf)
+                        assert not np.any(out[b, h]) and lse[b, h] == -np.inf
+
+
+# ---------------------------------------------------------------- P14
+def _state_sdpa(q, K, V, scale):
+    """(out, lse) of one query over a key block: torch SDPA + scipy logsumexp."""
+    return _sdpa(q, K, V, scale), float(scipy.special.logsumexp(scale * (K @ q)))
+
+
+def _asm_batched_case(r, B, Hkv, G, K, D, clustered):
+    """A codebook per KV head and queries built so that every answer is known by
+    construction: query (b, h) is lambda times entry j(b, h) of KV head h // G (so
+    that entry is its cosine argmax), the entries chosen in a group are distinct,
+    and the chosen entry's stored state is that same query's attention state over a
+    prefix of its own.  The batched lookup + merge must then return j(b, h) and
+    attention over [prefix; own tokens] (torch SDPA), i.e. the page's lossless
+    merge; any other head map, or looking up with another head's query, picks
+    another entry."""
+    Hq = Hkv * G
+    scale = 1.0 / math.sqrt(D)
+    if clustered:
+        K1 = K // 3
+        u = r.standard_normal((Hkv, K1, D))
+        u /= np.linalg.norm(u, axis=2, keepdims=True)
+        assign = np.tile(np.repeat(np.arange(K1), 3), (Hkv, 1))
+        C = u[np.arange(Hkv)[:, None], assign] + 0.08 * r.standard_normal((Hkv, K, D))
+    else:
+        C = r.standard_normal((Hkv, K, D)) * r.uniform(0.5, 2.0, size=(Hkv, K, 1))
+    abar = r.standard_normal((Hkv, K, D))
+    lzb = r.uniform(-2.0, 6.0, size=(Hkv, K))
+    q = np.zeros((B, Hq, D))
+    want_idx = np.zeros((B, Hq), np.int64)
+    want_o = np.zeros((B, Hq, D))
+    want_l = np.zeros((B, Hq))
+    self_o = np.zeros((B, Hq, D))
+    self_l = np.zeros((B, Hq))
+    for g in range(Hkv):
+        js = r.permutation(K)[: B * G]
+        for b in range(B):
+            for hh in range(G):
+                h = g * G + hh
+                j = int(js[b * G + hh])
+                want_idx[b, h] = j
+                q[b, h] = float(r.uniform(0.5, 3.0)) * C[g, j]
+                npre, nself = int(r.integers(1, 9)), int(r.integers(0, 6))
+                Kp, Vp = r.standard_normal((npre, D)), r.standard_normal((npre, D))
+                Ks, Vs = r.standard_normal((nself, D)), r.standard_normal((nself, D))
+                abar[g, j], lzb[g, j] = _state_sdpa(q[b, h], Kp, Vp, scale)
+                if nself:
+                    self_o[b, h], self_l[b, h] = _state_sdpa(q[b, h], Ks, Vs, scale)
+                else:                                       # no own tokens yet
+                    self_l[b, h] = -np.inf
+                want_o[b, h], want_l[b, h] = _state_sdpa(q[b, h], np.vstack([Kp, Ks]),
+                                                         np.vstack([Vp, Vs]), scale)
+    return C, abar, lzb, q, self_o, self_l, want_idx, want_o, want_l
+
+
+def check_asm_batched(seed=14):
+    """Batched ASM lookup + merge (linear and two-level) on cases whose index and
+    merged output are known by construction (see _asm_batched_case)."""
+    r = _rng(seed)
+    B, Hkv, G, K, D = 2, 3, 2, 12, 24
+    C, abar, lzb, q, so, sl, wi, wo, wl = _asm_batched_case(r, B, Hkv, G, K, D, False)
+    out, lse, idx = OA.asm_lookup_merge(q, C, abar, lzb, so, sl)
+    assert np.array_equal(idx, wi), "batched lookup: wrong entry (head map / query)"
+    assert np.max(np.abs(out - wo)) < 1e-12 and np.max(np.abs(lse - wl)) < 1e-12, \
+        "batched lookup + merge != attention over [prefix; own tokens]"
+    # two-level: entries near their first-level centroid, stored cluster by cluster
+    # (shuffled inside), so the query's own cluster has the best first-level cosine
+    C, abar, lzb, q, so, sl, wi, wo, wl = _asm_batched_case(r, B, Hkv, G, K, D, True)
+    K1 = K // 3
+    c1 = np.stack([np.stack([C[g, 3 * j:3 * j + 3].mean(0) for j in range(K1)])
+                   for g in range(Hkv)])
+    kid = np.stack([np.concatenate([3 * j + r.permutation(3) for j in range(K1)])
+                    for g in range(Hkv)])
+    offs = np.tile(np.arange(0, K + 1, 3), (Hkv, 1))
+    Cs = np.stack([C[g, kid[g]] for g in range(Hkv)])
+    for m in (1, 2, K1):
+        out, lse, idx = OA.asm_lookup_merge_hier(q, c1, offs, Cs, kid, m, abar, lzb, so, sl)
+        assert np.array_equal(idx, wi), "batched two-level lookup: wrong entry"
+        assert np.max(np.abs(out - wo)) < 1e-12 and np.max(np.abs(lse - wl)) < 1e-12, \
+            "batched two-level lookup + merge != attention over [prefix; own tokens]"
+
+
+# ---------------------------------------------------------------- P15
+def check_decode_loop_order(seed=15):
+    """Two decode steps with budget M = 3 whose evictions are fixed by hand: one token
+    with beta = 0.05 goes at step 0, one with beta = 0.5 at step 1 (every other beta
+    is 0.95).  Each step's output must be attention over exactly the tokens live
+    after the append and before the eviction (torch SDPA over that hand-listed set,
+    weights beta^d as plain powers), in the order the TRIM-KV inference section
+    gives: the new token joins the cache, is attended to, then the cache is cut back
+    to M."""
+    r = _rng(seed)
+    B, Hkv, G, D, cap, M = 1, 1, 2, 8, 8, 3
+    Hq = Hkv * G
+    k = np.zeros((B, Hkv, cap, D), np.float32)
+    v = np.zeros((B, Hkv, cap, D), np.float32)
+    beta = {0: 0.95, 1: 0.05, 2: 0.95, 3: 0.5, 4: 0.95}    # by position
+    kr = r.standard_normal((5, D)).astype(np.float32)      # rows by position
+    vr = r.standard_normal((5, D)).astype(np.float32)
+    lb = np.zeros((B, Hkv, cap), np.float32)
+    for p in range(3):
+        k[0, 0, p], v[0, 0, p], lb[0, 0, p] = kr[p], vr[p], np.float32(math.log(beta[p]))
+    pos = np.zeros((B, Hkv, cap), np.int32)
+    pos[0, 0, :3] = [0, 1, 2]
+    cache = OE.Cache(k, v, lb, pos, np.array([[3]], np.int32))
+    qs = r.standard_normal((2, B, Hq, D))
+    k_news = np.stack([kr[3:4][None], kr[4:5][None]])      # [S][B][Hkv][D]
+    v_news = np.stack([vr[3:4][None], vr[4:5][None]])
+    lb_news = np.array([[[math.log(beta[3])]], [[math.log(beta[4])]]], np.float32)
+    final, steps = run_decode(cache, qs, k_news, v_news, lb_news, 3, M)
+    live = ([0, 1, 2, 3], [0, 2, 3, 4])                    # attended at steps 0 and 1
+    gone = ([1], [3])
+    for s in range(2):
+        t = 3 + s
+        P = np.array(live[s])
+        Kl = kr[P].astype(np.float64)
+        Vl = vr[P].astype(np.float64)
+        # beta as the stored float32 log beta represents it, raised to the distance
+        bf = {p: math.exp(float(np.float32(math.log(beta[p])))) for p in P}
+        mask = np.array([math.log(bf[p] ** (t - p)) for p in P])
+        out, lse, ev, n_ev = steps[s]
+        for h in range(Hq):
+            ref = _sdpa(qs[s, 0, h], Kl, Vl, 1.0 / math.sqrt(D), mask)
+            assert np.max(np.abs(out[0, h] - ref)) < 1e-12, \
+                f"step {s}: output is not attention over the appended, un-evicted cache"
+            ref_l = scipy.special.logsumexp(Kl @ qs[s, 0, h] / math.sqrt(D) + mask)
+            assert abs(lse[0, h] - ref_l) < 1e-12
+        assert list(ev[0][0]) == gone[s] and n_ev[0, 0] == 1, f"step {s}: eviction"
+    assert final.length[0, 0] == M and list(final.pos[0, 0, :M]) == [0, 2, 4]
+    assert np.array_equal(final.k[0, 0, :M], kr[[0, 2, 4]])
+
+
+def run_decode(*a, **kw):
+    import oracle.decode as OD
+    return OD.run_decode_steps(*a, **kw)
+
+
 ALL = [check_attention_library, check_bias_closed_form, check_split_merge,
        check_asm_lossless, check_evict_bruteforce, check_evict_sliding_window,
        check_evict_invariants, check_compaction, check_erase_bruteforce,
-       check_lookup_bruteforce, check_hier_lookup, check_asm_build, check_latent_memory, check_bytes_model]
+       check_lookup_bruteforce, check_hier_lookup, check_asm_build, check_latent_memory, check_bytes_model,
+       check_decode_attention_gqa, check_asm_batched, check_decode_loop_order]

@@ -11,6 +11,7 @@ import pytest
 import oracle.asm as OA
 import oracle.asm_build as OAB
 import oracle.attn as OT
+import oracle.decode as OD
 import oracle.evict as OE
 import oracle.latent as OL
 import pins
@@ -25,6 +26,8 @@ _orig_update = OAB.centroid_update
 _orig_bounds = OAB.chunk_bounds
 _orig_absorb = OL.latent_absorb
 _orig_read = OL.latent_read
+_orig_lookup = OA.cosine_lookup
+_orig_hier_b = OA.hier_lookup
 
 
 def bias_sign_flipped(log_beta, pos, t):
@@ -278,6 +281,107 @@ def read_no_projection(Mst, bst, q, W_o, w_g, c_g, eps):
     return _orig_read(Mst, bst, q, np.eye(np.asarray(W_o).shape[0]), w_g, c_g, eps)
 
 
+def _decode_attention(k, v, log_beta, pos, length, q, t, scale=None, head_map=None,
+                      default=None):
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = default(D) if default else 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = head_map(h, G, Hkv) if head_map else h // G
+            n = int(length[b][g])
+            lb = None if log_beta is None else log_beta[b][g][:n]
+            out[b, h], lse[b, h] = OT.attention(q[b, h], k[b][g][:n], v[b][g][:n], lb,
+                                                pos[b][g][:n], int(t[b]), scale)
+    return out, lse
+
+
+def decode_attention_h_mod(*a, **kw):
+    return _decode_attention(*a, head_map=lambda h, G, Hkv: h % Hkv, **kw)
+
+
+def decode_attention_sqrt_default(*a, **kw):
+    return _decode_attention(*a, default=lambda D: np.sqrt(D), **kw)
+
+
+def _asm_batched(q, centroids, abar, log_zbar, self_out, self_lse, lookup, head_map=None,
+                 first_head=False):
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = centroids.shape[0] if hasattr(centroids, "shape") else len(centroids)
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    idx = np.zeros((B, Hq), dtype=np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            g = head_map(h, G, Hkv) if head_map else h // G
+            c = lookup(q[b, g * G] if first_head else q[b, h], g)
+            idx[b, h] = c
+            out[b, h], lse[b, h] = OA.asm_merge(self_out[b, h], self_lse[b, h],
+                                                abar[g][c], log_zbar[g][c])
+    return out, lse, idx
+
+
+def asm_batched_h_mod(q, C, abar, lz, so, sl):
+    return _asm_batched(q, C, abar, lz, so, sl, lambda x, g: _orig_lookup(x, C[g]),
+                        head_map=lambda h, G, Hkv: h % Hkv)
+
+
+def asm_batched_first_head(q, C, abar, lz, so, sl):
+    return _asm_batched(q, C, abar, lz, so, sl, lambda x, g: _orig_lookup(x, C[g]),
+                        first_head=True)
+
+
+def asm_hier_batched_h_mod(q, c1, offs, C, kid, m, abar, lz, so, sl):
+    return _asm_batched(q, c1, abar, lz, so, sl,
+                        lambda x, g: _orig_hier_b(x, c1[g], offs[g], C[g], kid[g], m),
+                        head_map=lambda h, G, Hkv: h % Hkv)
+
+
+def asm_hier_batched_first_head(q, c1, offs, C, kid, m, abar, lz, so, sl):
+    return _asm_batched(q, c1, abar, lz, so, sl,
+                        lambda x, g: _orig_hier_b(x, c1[g], offs[g], C[g], kid[g], m),
+                        first_head=True)
+
+
+def decode_evict_before_attend(*a, **kw):
+    # append, evict, then attend
+    cache, qs, k_news, v_news, lb_news, t0, M = a[:7]
+    c = cache.copy()
+    B = c.length.shape[0]
+    steps = []
+    for s in range(len(qs)):
+        t = np.full(B, t0 + s, dtype=np.int64)
+        OE.append_tokens(c, k_news[s], v_news[s], None if lb_news is None else lb_news[s], t)
+        c, ev, n_ev = OE.evict_to_budget(c, t, M)
+        out, lse = OT.decode_attention(c.values("k"), c.values("v"), c.log_beta, c.pos,
+                                       c.length, qs[s], t, kw.get("scale"))
+        steps.append((out, lse, ev, n_ev))
+    return c, steps
+
+
+def decode_attend_before_append(*a, **kw):
+    # the decode token is left out of its own step's attention
+    cache, qs, k_news, v_news, lb_news, t0, M = a[:7]
+    c = cache.copy()
+    B = c.length.shape[0]
+    steps = []
+    for s in range(len(qs)):
+        t = np.full(B, t0 + s, dtype=np.int64)
+        out, lse = OT.decode_attention(c.values("k"), c.values("v"), c.log_beta, c.pos,
+                                       c.length, qs[s], t, kw.get("scale"))
+        OE.append_tokens(c, k_news[s], v_news[s], None if lb_news is None else lb_news[s], t)
+        c, ev, n_ev = OE.evict_to_budget(c, t, M)
+        steps.append((out, lse, ev, n_ev))
+    return c, steps
+
+
 MUTANTS = [
     (OT, "retention_bias", bias_sign_flipped),
     (OT, "retention_bias", bias_dropped),
@@ -315,6 +419,14 @@ MUTANTS = [
     (OL, "latent_read", read_no_stabiliser),
     (OL, "latent_read", read_gate_flipped),
     (OL, "latent_read", read_no_projection),
+    (OT, "decode_attention", decode_attention_h_mod),
+    (OT, "decode_attention", decode_attention_sqrt_default),
+    (OA, "asm_lookup_merge", asm_batched_h_mod),
+    (OA, "asm_lookup_merge", asm_batched_first_head),
+    (OA, "asm_lookup_merge_hier", asm_hier_batched_h_mod),
+    (OA, "asm_lookup_merge_hier", asm_hier_batched_first_head),
+    (OD, "run_decode_steps", decode_evict_before_attend),
+    (OD, "run_decode_steps", decode_attend_before_append),
 ]
 
 
