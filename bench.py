@@ -45,11 +45,16 @@ def source_digest(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def cpu_baseline(w, host_units, t, M, budget_s=12.0):
-    """The float64 oracle, as it stands, on whole heads of one layer (append +
-    attention for the head's query group + eviction + compaction), the layer's heads
-    taken in turn (again from the first once all were run) until ``budget_s`` of CPU
-    work; extrapolated to the full step (units x layers)."""
+def cpu_baseline(w, host_units, t, M, budget_s=12.0, gpu_res=None):
+    """The float64 oracle, as it stands, on whole heads (append + attention for the
+    head's query group + eviction + compaction), the heads taken in turn (again from
+    the first once all were run) until ``budget_s`` of CPU work and every head was
+    run once; the time per head is extrapolated to the full step (units x layers).
+
+    With ``gpu_res`` (the timed step's results on the same inputs, per layer), each
+    head's first oracle run is also compared with them, outside the timed part: the
+    compacted layout (len, and K, V, log beta, pos of every kept slot) bit for bit,
+    and every query head's output and lse within 2e-3."""
     import numpy as np
 
     import oracle
@@ -63,28 +68,57 @@ def cpu_baseline(w, host_units, t, M, budget_s=12.0):
         return None
     done = 0
     elapsed = 0.0
-    for (k, v, lb, pos, n, q, kn, vn, lbn) in itertools.cycle(host_units):
+    checked = set()
+    worst = 0.0
+    for i, (layer, b, g, k, v, lb, pos, n, q, kn, vn, lbn) in enumerate(
+            itertools.cycle(host_units)):
         t0 = time.perf_counter()
         c = oracle.Cache(k[None, None].copy(), v[None, None].copy(), lb[None, None].copy(),
                          pos[None, None].copy(), np.array([[n]], np.int32))
         oracle.append_tokens(c, kn[None, None], vn[None, None], np.array([[lbn]], np.float32),
                              np.array([t]))
-        oracle.decode_attention(c.values("k"), c.values("v"), c.log_beta, c.pos, c.length,
-                                ((q.astype(np.uint32) << 16).view(np.float32)
-                                 .astype(np.float64))[None], np.array([t]))
-        oracle.evict_to_budget(c, np.array([t]), M)
+        ro, rl = oracle.decode_attention(c.values("k"), c.values("v"), c.log_beta, c.pos,
+                                         c.length, ((q.astype(np.uint32) << 16)
+                                                    .view(np.float32).astype(np.float64))[None],
+                                         np.array([t]))
+        ce, _, _ = oracle.evict_to_budget(c, np.array([t]), M)
         elapsed += time.perf_counter() - t0
         done += 1
-        if elapsed >= budget_s:
+        u = i % len(host_units)
+        if gpu_res is not None and u not in checked:
+            r = gpu_res[layer]
+            kept = int(ce.length[0, 0])
+            assert r["len"][b, g] == kept, f"layer {layer} head ({b},{g}): len"
+            for name in ("k", "v", "log_beta", "pos"):
+                got = r[name][b, g, :kept]
+                want = getattr(ce, name)[0, 0, :kept]
+                assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), \
+                    f"layer {layer} head ({b},{g}): compacted {name} differs from the oracle"
+            G = w.group
+            for j in range(G):
+                o, l = r["out"][b, g * G + j], r["lse"][b, g * G + j]
+                err = float(np.max(np.abs(o - ro[0, j])) / np.max(np.abs(ro[0, j])))
+                assert err <= 2e-3 and abs(float(l) - rl[0, j]) <= 2e-3, \
+                    f"layer {layer} query head ({b},{g * G + j}): rel err {err:.2e}"
+                worst = max(worst, err)
+            checked.add(u)
+        if elapsed >= budget_s and done >= len(host_units):
             break
     unit_s = elapsed / done
     step_s = unit_s * w.units * w.layers
-    return {"value": 1.0 / step_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} runs over the {len(host_units)} whole KV heads of layer 0 "
-                      f"({w.ctx + 1} tokens, {w.group} query heads each: append + attention "
-                      f"+ eviction to {M} + compaction), {elapsed:.1f} s, extrapolated to "
-                      f"{w.units} heads x {w.layers} layers",
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+    layers = sorted({hu[0] for hu in host_units})
+    res = {"value": 1.0 / step_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} runs over the {len(host_units)} whole KV heads of layers "
+                     f"{layers} ({w.ctx + 1} tokens, {w.group} query heads each: append + "
+                     f"attention + eviction to {M} + compaction), {elapsed:.1f} s, "
+                     f"extrapolated to {w.units} heads x {w.layers} layers",
+           "affinity_cpus": len(os.sched_getaffinity(0))}
+    if gpu_res is not None:
+        res["checked_against_gpu"] = {
+            "what": "the timed step replayed on restored inputs: compacted layouts bit for "
+                    "bit, attention out/lse within 2e-3",
+            "kv_heads": len(checked), "max_rel_err": float(f"{worst:.3e}")}
+    return res
 
 
 def steady_bench(args):
@@ -808,9 +842,16 @@ def main():
     ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, args.splits), dtype=torch.uint8,
                        device=dev)
     sched = "serial" if args.serial else (args.schedule or "deferred_plan")
-    # one eviction workspace per layer when the plans outlive the next layer's planning
+    if args.fused and sched in ("deferred", "deferred_plan"):
+        # the fused pair needs the layer's plan between its two phases
+        if args.schedule:
+            sys.exit(f"bench.py: --fused needs the plan before each layer's second phase; "
+                     f"--schedule {args.schedule} defers it")
+        sched = "plan_beside"
+    # one eviction workspace per layer when the plans outlive the next layer's planning;
+    # zero-filled, so a plan header that was never written reads as 'nothing to do'
     n_ws = L if sched in ("deferred", "deferred_plan") else 1
-    ws_es = [torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device=dev)
+    ws_es = [torch.zeros(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device=dev)
              for _ in range(n_ws)]
     splits = args.splits or kvb.kv_attn_decode_splits(kvs[0], w.hq)
 
@@ -913,22 +954,27 @@ def main():
         torch.cuda.synchronize()
 
     # CPU baseline inputs: whole heads of layer 0 as drawn (read before the timed run)
+    # (the first and the last layer: the last one's plan runs last in the default schedule)
     host_units = []
     if not args.no_cpu:
         restore()
         torch.cuda.synchronize()
-        d0 = caches[0]
-        q0, kn0, vn0, lb0 = (x.cpu() for x in qs[0])
-        for u in range(w.units):
-            b, g = divmod(u, w.hkv)
-            host_units.append((
-                d0["k"][b, g, :n].view(torch.int16).cpu().numpy().view(np.uint16),
-                d0["v"][b, g, :n].view(torch.int16).cpu().numpy().view(np.uint16),
-                d0["log_beta"][b, g, :n].cpu().numpy(), d0["pos"][b, g, :n].cpu().numpy(),
-                w.ctx,
-                q0[b, g * w.group:(g + 1) * w.group].view(torch.int16).numpy().view(np.uint16),
-                kn0[b, g].view(torch.int16).numpy().view(np.uint16),
-                vn0[b, g].view(torch.int16).numpy().view(np.uint16), float(lb0[b, g])))
+        for layer in sorted({0, L - 1}):
+            d0 = caches[layer]
+            q0, kn0, vn0, lb0 = (x.cpu() for x in qs[layer])
+            for u in range(w.units):
+                b, g = divmod(u, w.hkv)
+                host_units.append((
+                    layer, b, g,
+                    # slots 0 .. ctx (the append overwrites slot ctx)
+                    d0["k"][b, g, :n].view(torch.int16).cpu().numpy().view(np.uint16),
+                    d0["v"][b, g, :n].view(torch.int16).cpu().numpy().view(np.uint16),
+                    d0["log_beta"][b, g, :n].cpu().numpy(),
+                    d0["pos"][b, g, :n].cpu().numpy(), w.ctx,
+                    q0[b, g * w.group:(g + 1) * w.group].view(torch.int16).numpy()
+                    .view(np.uint16),
+                    kn0[b, g].view(torch.int16).numpy().view(np.uint16),
+                    vn0[b, g].view(torch.int16).numpy().view(np.uint16), float(lb0[b, g])))
 
     # secondary reference: a plain device copy (reads and writes 1 GiB each per call)
     cx = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -973,6 +1019,29 @@ def main():
     # per layer: the attention split launch(es) of that layer (fused: both phases)
     split_ms = [ms for name, ms in trace if name == "attn_split"]
     fused_ms = [ms for name, ms in trace if name == "attn_fused"]
+
+    # the timed step (graph replay, or eager) once more on restored inputs; its results
+    # for the CPU baseline's layers are kept on the host and compared with the oracle's
+    # in the cpu_baseline leg
+    gpu_res = None
+    if host_units:
+        restore()
+        torch.cuda.synchronize()
+        if graph is not None:
+            graph.replay()
+        else:
+            step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        gpu_res = {}
+        for layer in sorted({hu[0] for hu in host_units}):
+            d = caches[layer]
+            gpu_res[layer] = {
+                "out": outs[layer].cpu().numpy(), "lse": lses[layer].cpu().numpy(),
+                "len": d["len"].cpu().numpy(),
+                "k": d["k"][:, :, :M].view(torch.int16).cpu().numpy().view(np.uint16),
+                "v": d["v"][:, :, :M].view(torch.int16).cpu().numpy().view(np.uint16),
+                "log_beta": d["log_beta"][:, :, :M].cpu().numpy(),
+                "pos": d["pos"][:, :, :M].cpu().numpy()}
 
     # sanity: every head evicted to M; moved rows from the first evicted position
     moved = 0
@@ -1034,7 +1103,8 @@ def main():
         line["roofline"]["phase_ms"] = [round(sum(split_ms) / len(split_ms), 5),
                                         round(sum(fused_ms) / len(fused_ms), 5)]
     if host_units:
-        line["cpu_baseline"] = cpu_baseline(w, host_units, w.ctx, M, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, host_units, w.ctx, M, args.cpu_seconds,
+                                            gpu_res)
     print(json.dumps(line), flush=True)
 
 

@@ -17,7 +17,8 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    asm_lookup_merge, asm_lookup_merge_hier, asm_prefix_states,
                    asm_prefix_states_workspace,
                    asm_lookup_merge_hier_workspace, asm_lookup_merge_workspace,
-                   kv_append, kv_attn_decode, kv_attn_decode_asm, kv_attn_decode_asm_workspace,
+                   kv_append, kv_attn_decode, kv_attn_decode_asm,
+                   kv_attn_decode_asm_workspace, workspace_status,
                    kv_attn_decode_compact, kv_attn_decode_splits, kv_attn_decode_workspace,
                    kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_one,
                    kv_evict_plan,
@@ -28,6 +29,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
 
 __all__ = [
     "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
+    "workspace_status",
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_evict_one", "kv_attn_decode_compact",
     "kv_attn_decode_asm", "kv_attn_decode_asm_workspace",
     "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",

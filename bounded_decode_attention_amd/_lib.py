@@ -198,10 +198,22 @@ def asm_lookup_merge_workspace(B, Hq, Hkv, D, K) -> int:
     return int(library().asm_lookup_merge_workspace(B, Hq, Hkv, D, K))
 
 
+def workspace_status(ws, stream=None) -> int:
+    """The status word (int32 at byte 0) a call left in its workspace; waits for
+    the stream first."""
+    (stream or torch.cuda.current_stream()).synchronize()
+    return int(ws[:4].view(torch.int32).item())
+
+
+def _check_ws(ws, stream, where):
+    _check(workspace_status(ws, stream), where)
+
+
 def kv_attn_decode(cache: KVCache, q, t, scale: float = 0.0, k_new=None, v_new=None,
                    log_beta_new=None, num_splits: int = 0, out=None, lse=None, ws=None,
-                   stream=None):
-    """Append (optional) + retention-biased GQA decode attention.  Returns (out, lse)."""
+                   stream=None, check_status: bool = False):
+    """Append (optional) + retention-biased GQA decode attention.  Returns (out, lse).
+    check_status: wait for the call and raise if its status word reports a full head."""
     _need(q, "q", cache.k.dtype)
     _need(t, "t", torch.int32)
     B, Hq, D = q.shape
@@ -221,6 +233,8 @@ def kv_attn_decode(cache: KVCache, q, t, scale: float = 0.0, k_new=None, v_new=N
                                   _ptr(v_new), _ptr(log_beta_new), int(num_splits), _ptr(out),
                                   _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "kv_attn_decode")
+    if check_status:
+        _check_ws(ws, stream, "kv_attn_decode (device status)")
     return out, lse
 
 
@@ -287,8 +301,10 @@ def kv_evict_to_budget(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=No
     return n_evicted
 
 
-def kv_append(cache: KVCache, k_new, v_new, log_beta_new, t, ws=None, stream=None):
-    """Append one token per KV head (slot len, pos = t[b]); len += 1."""
+def kv_append(cache: KVCache, k_new, v_new, log_beta_new, t, ws=None, stream=None,
+              check_status: bool = False):
+    """Append one token per KV head (slot len, pos = t[b]); len += 1.
+    check_status: wait for the call and raise if a head was full."""
     _need(k_new, "k_new", cache.k.dtype)
     _need(v_new, "v_new", cache.k.dtype)
     _need(t, "t", torch.int32)
@@ -298,6 +314,8 @@ def kv_append(cache: KVCache, k_new, v_new, log_beta_new, t, ws=None, stream=Non
     st = library().kv_append(cache.desc, _ptr(k_new), _ptr(v_new), _ptr(log_beta_new), _ptr(t),
                              _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "kv_append")
+    if check_status:
+        _check_ws(ws, stream, "kv_append (device status)")
 
 
 def kv_evict_plan(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=None, ws=None,

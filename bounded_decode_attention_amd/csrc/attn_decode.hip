@@ -58,9 +58,18 @@ struct AttnArgs {
   // when non-null, the first split of each head records the head's len here (the
   // merge then appends the decode token and needs the length before it)
   int32_t* n_rec;
+  // when non-null, the call's workspace status word: the first workgroup resets it
+  // to KVB_OK (the merge, a later launch of the same call, may set an error)
+  int32_t* status = nullptr;
 };
 
 // ------------------------------------------------------------------ append
+// Resets a call's workspace status word (a store, not a memset node, so the call
+// can be captured in a graph); the append kernel then reports full heads in it.
+__global__ __launch_bounds__(64) void status_reset(int32_t* status) {
+  if (threadIdx.x == 0) status[0] = KVB_OK;
+}
+
 __global__ __launch_bounds__(64) void kv_append(void* k, void* v, float* log_beta, int32_t* pos,
                                                 int32_t* len, const int32_t* start, int32_t cap,
                                                 int32_t row_words, const void* k_new,
@@ -129,6 +138,7 @@ __global__ __launch_bounds__(64) void attn_split_mfma(AttnArgs a) {
   const int s0 = head_start(a.start, u);
   const int n = min(a.len[u], a.cap);
   if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
+  if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.status[0] = KVB_OK;
   int lo, end;
   split_range(n, p, a.P, lo, end);
   // 16-byte loads of log beta / pos need a 4-slot aligned head base
@@ -539,6 +549,7 @@ void attn_split_pipe128(AttnArgs a) {
   const int capu = a.cap - s0;  // rows before the head wraps to the start of its slots
   const int n = min(a.len[u], a.cap);
   if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
+  if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.status[0] = KVB_OK;
   const int end = n;
   const size_t row0 = (size_t)u * a.cap + s0;  // the head's first live slot
 
@@ -697,6 +708,7 @@ __global__ __launch_bounds__(64) void attn_split_generic(AttnArgs a) {
   const int s0 = head_start(a.start, u);
   const int n = min(a.len[u], a.cap);
   if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
+  if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.status[0] = KVB_OK;
   int lo, end;
   split_range(n, p, a.P, lo, end);
   const size_t row0 = (size_t)u * a.cap + s0;  // the head's first live slot
@@ -1102,6 +1114,7 @@ extern "C" int32_t kv_append(const kvb_cache* cache, const void* k_new, const vo
   hipStream_t s = (hipStream_t)stream;
   const int elem = cache->dtype == KVB_BF16 ? 2 : 4;
   TraceScope tr(kTrAppend, s);
+  hipLaunchKernelGGL(status_reset, dim3(1), dim3(64), 0, s, (int32_t*)ws);
   hipLaunchKernelGGL(kv_append, dim3(cache->B * cache->Hkv), dim3(64), 0, s, cache->k, cache->v,
                      cache->log_beta, cache->pos, cache->len, cache->start, cache->cap,
                      cache->D * elem / 4,
@@ -1115,7 +1128,8 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
                                 const int32_t* t, float scale, const void* k_new,
                                 const void* v_new, const float* log_beta_new,
                                 int32_t num_splits, float* out, float* lse, void* ws,
-                                size_t ws_bytes, hipStream_t stream, const AsmTail* tail) {
+                                size_t ws_bytes, hipStream_t stream, const AsmTail* tail,
+                                int32_t* status = nullptr) {
   int32_t st = check_cache(cache, true);
   if (st) return st;
   if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
@@ -1153,6 +1167,8 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
   a.tile_lo = 0;
   a.tile_hi = 1 << 30;
   a.p_off = 0;
+  if (!status) status = (int32_t*)ws;
+  a.status = status;
 
   // with a decode token: attend over the cached tokens (the splits record each
   // head's len), then the merge adds the token's own state and appends it
@@ -1174,7 +1190,7 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
     nt.pos = cache->pos;
     nt.len = cache->len;
     nt.start = cache->start;
-    nt.status = (int32_t*)ws;
+    nt.status = status;
     nt.cap = cache->cap;
     nt.Hkv = cache->Hkv;
     nt.elem = cache->dtype == KVB_BF16 ? 2 : 4;

@@ -5,9 +5,12 @@
  * "host".  Every call is asynchronous on `stream` (a hipStream_t passed as
  * void*; NULL means the default stream), performs no host synchronisation, and
  * allocates nothing: scratch memory is the caller's workspace `ws` of at least
- * the size the matching *_workspace() function returns.  The library keeps no
- * state between calls; calls on different streams must not share a workspace
- * or a cache.
+ * the size the matching *_workspace() function returns.
+ * Host-side state is limited to: a per-device cache of the gfx950 check (written
+ * once per device, idempotent), the kvb_trace_* event table (process-global, not
+ * thread-safe; tracing is a measurement aid).  Results never depend on earlier
+ * calls except through the caller's buffers.  Calls on different streams must not
+ * share a workspace or a cache.
  *
  * Errors: arguments are validated on the host before anything is launched; a
  * failed check returns a negative kvb_status and leaves all memory untouched.
@@ -116,8 +119,11 @@ size_t asm_build_memory_workspace(int32_t H, int32_t N, int32_t D, int32_t L, in
  * len[b][g] (start + len mod cap with a start array) with pos = t[b], then
  * len[b][g] += 1, and the attention below covers
  * it.  A head whose len already equals cap is not appended to (its len stays, the
- * token is not attended, and the workspace status word becomes KVB_ECAPACITY; the
- * caller must keep cap > len).  The splits cover the cached slots; the token's own
+ * token is not attended, and the workspace status word -- the int32 at byte offset
+ * 0 of ws -- becomes KVB_ECAPACITY; the caller must keep cap > len).  Every call
+ * first resets that word to KVB_OK on the device (a kernel store, so the call can
+ * be captured in a HIP graph), so after the call's work completes it holds this
+ * call's outcome.  The splits cover the cached slots; the token's own
  * state (logit scale * q.k_new, no bias at distance 0) is merged last, and the row
  * is written by the merge, after every split has read the cache.
  *
@@ -158,7 +164,8 @@ int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq, const 
  * callers that start eviction planning (kv_evict_plan) as soon as the token is in
  * the cache, concurrently with the attention that follows.
  *   k_new, v_new [B][Hkv][D] cache dtype; log_beta_new [B][Hkv] f32 (required iff
- *   cache->log_beta != NULL); t [B] int32; ws: at least 256 bytes (status word).
+ *   cache->log_beta != NULL); t [B] int32; ws: at least 256 bytes (status word:
+ *   reset to KVB_OK by the call, KVB_ECAPACITY if a head was full).
  */
 int32_t kv_append(const kvb_cache* cache, const void* k_new, const void* v_new,
                   const float* log_beta_new, const int32_t* t, void* ws, size_t ws_bytes,

@@ -16,6 +16,11 @@ needs_lib = pytest.mark.skipif(not os.path.exists(kvb.library_path()),
                                reason="libkvbound.so not built")
 
 
+def _has_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -287,3 +292,19 @@ def test_fused_asm_entry_rejects_arguments_before_launch():
     assert L.kv_attn_decode_asm(ctypes.byref(_desc(dtype=0, D=64)), *args()) == -2  # f32 cache
     assert L.kv_attn_decode_asm(ctypes.byref(good), *args(ws_bytes=need - 1)) == -4
     assert L.kv_attn_decode_asm_workspace(ctypes.byref(good), 7, 0, 4096) == 0    # Hq % Hkv
+
+
+@needs_lib
+@pytest.mark.skipif(_has_gpu(), reason="a GPU is present")
+def test_valid_calls_without_a_gpu_return_edevice():
+    """Arguments that pass every host check reach the device check: without a HIP
+    device the call returns KVB_EDEVICE (-5) and launches nothing."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    good = _desc()
+    ws = P(4096)
+    args = [P(64), 8, P(72), 0.0, None, None, None, 0, P(80), P(88), ws, 1 << 30, None]
+    assert L.kv_attn_decode(ctypes.byref(good), *args) == -5
+    assert L.kv_evict_to_budget(ctypes.byref(good), P(8), 5, None, 0, None, ws, 1 << 30,
+                                None) == -5
+    assert L.kv_append(ctypes.byref(good), P(8), P(8), None, P(8), ws, 256, None) == -5
