@@ -7,7 +7,8 @@ not build it, and every call fails loudly if it is missing.
 
 Entry points (same names as the C ABI in include/kvbound.h):
     kv_attn_decode, kv_evict_to_budget, kv_erase_ranges, asm_lookup_merge
-(kv_attn_decode_asm: the first and the last in one call), and, for building the memory asm_lookup_merge reads, asm_prefix_states,
+(kv_attn_decode_asm: the first and the last in one call; kv_attn_decode_noalloc:
+the first without a workspace, for callers that cannot allocate), and, for building the memory asm_lookup_merge reads, asm_prefix_states,
 asm_kmeans, asm_aggregate_states, asm_build_memory; and the latent memory of
 evicted tokens, kv_latent_absorb and kv_latent_read;
 plus the workspace-size helpers and ``KVCache``, a holder of one layer's tensors.
@@ -17,8 +18,8 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    asm_lookup_merge, asm_lookup_merge_hier, asm_prefix_states,
                    asm_prefix_states_workspace,
                    asm_lookup_merge_hier_workspace, asm_lookup_merge_workspace,
-                   kv_append, kv_attn_decode, kv_attn_decode_asm,
-                   kv_attn_decode_asm_workspace, workspace_status,
+                   NOALLOC_SCRATCH_BYTES, kv_append, kv_attn_decode, kv_attn_decode_asm,
+                   kv_attn_decode_asm_workspace, kv_attn_decode_noalloc, workspace_status,
                    kv_attn_decode_compact, kv_attn_decode_splits, kv_attn_decode_workspace,
                    kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_one,
                    kv_evict_plan,
@@ -29,7 +30,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
 
 __all__ = [
     "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
-    "workspace_status",
+    "kv_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "workspace_status",
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_evict_one", "kv_attn_decode_compact",
     "kv_attn_decode_asm", "kv_attn_decode_asm_workspace",
     "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",

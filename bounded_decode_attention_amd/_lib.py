@@ -11,6 +11,7 @@ _LIB_PATH = os.path.join(_HERE, "libkvbound.so")
 _lib = None
 
 KVB_F32, KVB_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20    # KVB_NOALLOC_SCRATCH_BYTES in kvbound.h
 
 
 class KVBError(RuntimeError):
@@ -50,6 +51,7 @@ def library():
             "asm_lookup_merge_workspace": (SZ, [I32, I32, I32, I32, I32]),
             "asm_lookup_merge_hier_workspace": (SZ, [I32, I32, I32, I32, I32]),
             "kv_attn_decode": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P]),
+            "kv_attn_decode_noalloc": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, P]),
             "kv_attn_decode_asm_workspace": (SZ, [CP, I32, I32, I32]),
             "kv_attn_decode_asm": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, I32, P, P, P,
                                          P, SZ, P]),
@@ -235,6 +237,38 @@ def kv_attn_decode(cache: KVCache, q, t, scale: float = 0.0, k_new=None, v_new=N
     _check(st, "kv_attn_decode")
     if check_status:
         _check_ws(ws, stream, "kv_attn_decode (device status)")
+    return out, lse
+
+
+def kv_attn_decode_noalloc(cache: KVCache, q, t, out, lse, scale: float = 0.0, k_new=None,
+                           v_new=None, log_beta_new=None, num_splits: int = 0, status=None,
+                           stream=None):
+    """kv_attn_decode on the library's device-resident scratch (no workspace, nothing
+    allocated here or in the library): out [B][Hq][D] f32 and lse [B][Hq] f32 are the
+    caller's; status: optional int32 device tensor of one element that receives the
+    call's status word."""
+    _need(q, "q", cache.k.dtype)
+    _need(t, "t", torch.int32)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out must be [B][Hq][D] and lse [B][Hq]")
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x is not None:
+            _need(x, name, cache.k.dtype)
+    if log_beta_new is not None:
+        _need(log_beta_new, "log_beta_new", torch.float32)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    st = library().kv_attn_decode_noalloc(cache.desc, _ptr(q), Hq, _ptr(t), float(scale),
+                                          _ptr(k_new), _ptr(v_new), _ptr(log_beta_new),
+                                          int(num_splits), _ptr(out), _ptr(lse), _ptr(status),
+                                          _stream(stream))
+    if st == -4:
+        raise KVBError(st, "kv_attn_decode_noalloc: the call needs more than the "
+                       f"{NOALLOC_SCRATCH_BYTES >> 20} MiB device scratch")
+    _check(st, "kv_attn_decode_noalloc")
     return out, lse
 
 

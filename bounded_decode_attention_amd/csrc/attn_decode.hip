@@ -29,6 +29,8 @@
 //         32-byte bank groups.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace kvb {
@@ -1213,6 +1215,51 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
                                   size_t ws_bytes, void* stream) {
   return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, num_splits, out,
                           lse, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+// ------------------------------------------------------------------ no-alloc entry
+// Scratch of kv_attn_decode_noalloc: a device global, so each GPU the library runs
+// on holds its own copy (zero-filled .bss of the code object) until the process
+// ends.  In host code the array's name only stands for the symbol: its device
+// address, per device, comes from hipGetSymbolAddress (made once per device, with
+// that device current) and is what the kernels get.
+namespace kvb {
+static __device__ __align__(256) unsigned char scratch[KVB_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static int32_t scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVB_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVB_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KVB_OK;
+}
+}  // namespace kvb
+
+extern "C" int32_t kv_attn_decode_noalloc(const kvb_cache* cache, const void* q, int32_t Hq,
+                                          const int32_t* t, float scale, const void* k_new,
+                                          const void* v_new, const float* log_beta_new,
+                                          int32_t num_splits, float* out, float* lse,
+                                          int32_t* status, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
+  if (num_splits < 0 || num_splits > 4096) return KVB_EINVAL;
+  const size_t need = kv_attn_decode_workspace(cache, Hq, num_splits);
+  if (need == 0 || need > KVB_NOALLOC_SCRATCH_BYTES) return KVB_EWORKSPACE;
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, num_splits, out,
+                          lse, ws, KVB_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream, nullptr,
+                          status);
 }
 
 extern "C" size_t kv_attn_decode_asm_workspace(const kvb_cache* cache, int32_t Hq,

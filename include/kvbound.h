@@ -5,10 +5,12 @@
  * "host".  Every call is asynchronous on `stream` (a hipStream_t passed as
  * void*; NULL means the default stream), performs no host synchronisation, and
  * allocates nothing: scratch memory is the caller's workspace `ws` of at least
- * the size the matching *_workspace() function returns.
+ * the size the matching *_workspace() function returns (the one exception,
+ * kv_attn_decode_noalloc, uses a fixed device-resident scratch array instead).
  * Host-side state is limited to: a per-device cache of the gfx950 check (written
  * once per device, idempotent), the kvb_trace_* event table (process-global, not
- * thread-safe; tracing is a measurement aid).  Results never depend on earlier
+ * thread-safe; tracing is a measurement aid), and the per-device address of the
+ * no-alloc scratch array (guarded by a mutex).  Results never depend on earlier
  * calls except through the caller's buffers.  Calls on different streams must not
  * share a workspace or a cache.
  *
@@ -56,6 +58,9 @@ typedef enum {
 } kvb_status;
 
 typedef enum { KVB_F32 = 0, KVB_BF16 = 1 } kvb_dtype;
+
+/* Size of the device-resident scratch array behind kv_attn_decode_noalloc. */
+#define KVB_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * One layer's KV cache; a plain descriptor, read during the call, not retained.
@@ -157,6 +162,31 @@ int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t Hq, const 
                        float scale, const void* k_new, const void* v_new,
                        const float* log_beta_new, int32_t num_splits, float* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_attn_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * kv_attn_decode (bit for bit, for the same num_splits); the split states live in
+ * a device-resident array of KVB_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU
+ * holds from the library's load until the process ends.  The array's device
+ * address is looked up once per device on the first call made with that device
+ * current.
+ *   status  [1] int32 device pointer or NULL: receives the call's status word
+ *           (KVB_OK, or KVB_ECAPACITY when a head was full; reset by every call);
+ *           NULL keeps it in the scratch array, where the caller cannot read it.
+ * Returns KVB_EWORKSPACE, launching nothing, when the call would need more than
+ * KVB_NOALLOC_SCRATCH_BYTES (kv_attn_decode_workspace(cache, Hq, num_splits) >
+ * KVB_NOALLOC_SCRATCH_BYTES; e.g. B * Hq * num_splits * (D + 2) * 4 bytes of split
+ * states).  Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap in time on one GPU (different streams, or different
+ * host threads) race and give undefined results; serialise them.
+ */
+int32_t kv_attn_decode_noalloc(const kvb_cache* cache, const void* q, int32_t Hq,
+                               const int32_t* t, float scale, const void* k_new,
+                               const void* v_new, const float* log_beta_new,
+                               int32_t num_splits, float* out, float* lse, int32_t* status,
+                               void* stream);
 
 /*
  * Append one token per KV head: the same append kv_attn_decode performs when

@@ -295,6 +295,35 @@ def test_fused_asm_entry_rejects_arguments_before_launch():
 
 
 @needs_lib
+def test_noalloc_entry_rejects_arguments_before_launch():
+    """kv_attn_decode_noalloc: fake pointers; invalid arguments, and a call that
+    would need more than the fixed device scratch, are refused on the host."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    good = _desc()
+    # q, Hq, t, scale, k_new, v_new, log_beta_new, num_splits, out, lse, status, stream
+    args = [P(64), 8, P(72), 0.0, None, None, None, 0, P(80), P(88), None, None]
+    assert L.kv_attn_decode_noalloc(None, *args) == -1
+    assert L.kv_attn_decode_noalloc(ctypes.byref(good), P(64), 7, *args[2:]) == -1
+    a = list(args)
+    a[7] = 5000
+    assert L.kv_attn_decode_noalloc(ctypes.byref(good), *a) == -1
+    a = list(args)
+    a[8] = None
+    assert L.kv_attn_decode_noalloc(ctypes.byref(good), *a) == -1
+    big = _desc(B=64, Hkv=8, cap=8192)
+    assert L.kv_attn_decode_workspace(ctypes.byref(big), 64, 32) > kvb.NOALLOC_SCRATCH_BYTES
+    a = [P(64), 64, P(72), 0.0, None, None, None, 32, P(80), P(88), None, None]
+    assert L.kv_attn_decode_noalloc(ctypes.byref(big), *a) == -4
+
+
+def test_noalloc_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+KVB_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == kvb.NOALLOC_SCRATCH_BYTES
+
+
+@needs_lib
 @pytest.mark.skipif(_has_gpu(), reason="a GPU is present")
 def test_valid_calls_without_a_gpu_return_edevice():
     """Arguments that pass every host check reach the device check: without a HIP
@@ -305,6 +334,8 @@ def test_valid_calls_without_a_gpu_return_edevice():
     ws = P(4096)
     args = [P(64), 8, P(72), 0.0, None, None, None, 0, P(80), P(88), ws, 1 << 30, None]
     assert L.kv_attn_decode(ctypes.byref(good), *args) == -5
+    assert L.kv_attn_decode_noalloc(ctypes.byref(good), P(64), 8, P(72), 0.0, None, None, None,
+                                    0, P(80), P(88), None, None) == -5
     assert L.kv_evict_to_budget(ctypes.byref(good), P(8), 5, None, 0, None, ws, 1 << 30,
                                 None) == -5
     assert L.kv_append(ctypes.byref(good), P(8), P(8), None, P(8), ws, 256, None) == -5
