@@ -109,8 +109,8 @@ def cpu_baseline(w, host_units, t, M, budget_s=12.0, gpu_res=None):
     layers = sorted({hu[0] for hu in host_units})
     res = {"value": 1.0 / step_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
            "sample": f"{done} runs over the {len(host_units)} whole KV heads of layers "
-                     f"{layers} ({w.ctx + 1} tokens, {w.group} query heads each: append + "
-                     f"attention + eviction to {M} + compaction), {elapsed:.1f} s, "
+                     f"{layers} ({host_units[0][7] + 1} tokens, {w.group} query heads each: "
+                     f"append + attention + eviction to {M} + compaction), {elapsed:.1f} s, "
                      f"extrapolated to {w.units} heads x {w.layers} layers",
            "affinity_cpus": len(os.sched_getaffinity(0))}
     if gpu_res is not None:
@@ -174,10 +174,12 @@ def steady_bench(args):
     fused_append = args.schedule in (None, "fused_append")  # the default here
     one = args.schedule == "evict_one"
 
-    def step():
+    def step(ev=None):
+        # ev: optional [L][B][Hkv][1] int32, each layer's evicted position per head
         main = torch.cuda.current_stream()
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
+            evl = None if ev is None else ev[layer]
             if one:
                 # the attention call appends the decode token; the layer's eviction
                 # (one launch) follows it on the side stream, beside the next attention
@@ -185,7 +187,8 @@ def steady_bench(args):
                                    num_splits=P, out=out, lse=lse, ws=ws_a, stream=main)
                 attended[layer].record(main)
                 side.wait_event(attended[layer])
-                kvb.kv_evict_one(kvs[layer], t, M, n_evicted=nev[layer], stream=side)
+                kvb.kv_evict_one(kvs[layer], t, M, evicted_pos=evl, n_evicted=nev[layer],
+                                 stream=side)
                 continue
             if fused_append:
                 # the attention call appends the decode token; the layer's plan and
@@ -194,14 +197,15 @@ def steady_bench(args):
                                    num_splits=P, out=out, lse=lse, ws=ws_a, stream=main)
                 attended[layer].record(main)
                 side.wait_event(attended[layer])
-                kvb.kv_evict_plan(kvs[layer], t, M, n_evicted=nev[layer], ws=ws_e[layer],
-                                  stream=side)
+                kvb.kv_evict_plan(kvs[layer], t, M, evicted_pos=evl, n_evicted=nev[layer],
+                                  ws=ws_e[layer], stream=side)
                 kvb.kv_evict_apply(kvs[layer], M, ws_e[layer], stream=side)
                 continue
             kvb.kv_append(kvs[layer], kn, vn, lb, t, ws=ws_a, stream=main)
             appended[layer].record(main)
             side.wait_event(appended[layer])
-            kvb.kv_evict_plan(kvs[layer], t, M, n_evicted=nev[layer], ws=ws_e[layer], stream=side)
+            kvb.kv_evict_plan(kvs[layer], t, M, evicted_pos=evl, n_evicted=nev[layer],
+                              ws=ws_e[layer], stream=side)
             kvb.kv_attn_decode(kvs[layer], q, t, num_splits=P, out=out, lse=lse, ws=ws_a,
                                stream=main)
             if deferred:
@@ -216,6 +220,22 @@ def steady_bench(args):
                 kvb.kv_evict_apply(kvs[layer], M, ws_e[layer], stream=main)
         main.wait_stream(side)
         t.add_(1)
+
+    # CPU baseline inputs: the whole heads of layer 0 as drawn (M tokens each, t = M)
+    host_units = []
+    if not args.no_cpu:
+        import numpy as np
+        torch.cuda.synchronize()
+        d0, (q0, kn0, vn0, lb0) = kvs[0], qs[0]
+        q0, kn0, vn0, lb0 = (x.cpu() for x in (q0, kn0, vn0, lb0))
+        bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+        for u in range(w.units):
+            b, g = divmod(u, w.hkv)
+            host_units.append((0, b, g, bits(d0.k[b, g, :M + 1]), bits(d0.v[b, g, :M + 1]),
+                               d0.log_beta[b, g, :M + 1].cpu().numpy(),
+                               d0.pos[b, g, :M + 1].cpu().numpy(), M,
+                               bits(q0[b, g * w.group:(g + 1) * w.group]), bits(kn0[b, g]),
+                               bits(vn0[b, g]), float(lb0[b, g])))
 
     for _ in range(args.warmup + 1):
         step()
@@ -253,7 +273,37 @@ def steady_bench(args):
     split = {k: round(sum(v) / len(v) * 1000, 1) for k, v in per.items()}
     n = M + 1
     attn_b = algorithmic_bytes(w, n, 0)[0]
-    print(json.dumps({
+
+    # rows one step moves: each head's evicted slot e (from its evicted position and
+    # the head's positions in order) moves min(e, n - 1 - e) rows with a start array
+    # (the shorter side), n - 1 - e without; taken on one more eager step
+    import numpy as np
+    torch.cuda.synchronize()
+    logical = []
+    for c in kvs:
+        pos_h = c.pos.cpu().numpy()
+        st_h = c.start.cpu().numpy() if c.start is not None else np.zeros((B, w.hkv), np.int64)
+        ln_h = c.length.cpu().numpy()
+        logical.append((pos_h, st_h, ln_h))
+    ev = torch.full((L, B, w.hkv, 1), -1, dtype=torch.int32, device="cuda")
+    step(ev)
+    torch.cuda.synchronize()
+    evh = ev.cpu().numpy()
+    moved = 0
+    for layer, (pos_h, st_h, ln_h) in enumerate(logical):
+        cap = pos_h.shape[2]
+        for b in range(B):
+            for g in range(w.hkv):
+                nn = int(ln_h[b, g]) + 1                        # after the append
+                order = (int(st_h[b, g]) + np.arange(nn - 1)) % cap
+                p_log = np.append(pos_h[b, g, order], int(t[0].item()) - 1)
+                e = int(np.searchsorted(p_log, evh[layer, b, g, 0]))
+                moved += min(e, nn - 1 - e) if not args.no_start else nn - 1 - e
+    moves_b = algorithmic_bytes(w, n, moved)[1]
+    step_b = L * attn_b + moves_b
+    gbps = step_b / (ms * 1e-3) / 1e9
+    attn_us = split.get("attn_split", 0.0)
+    line = {
         "metric": "steady-state bounded-KV decode steps/s (evict 1 of M+1 per layer and step)",
         "value": round(1000.0 / ms, 3), "unit": "decode steps/s", "n_gpus": 1,
         "steps": nsteps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -263,7 +313,19 @@ def steady_bench(args):
                    "schedule": args.schedule or "fused_append",
                    "head_start": not args.no_start, "kv_splits": P},
         "eager_ms_per_step": round(eager_ms, 4), "kernel_us_eager": split,
-        "attention_bytes_per_layer": attn_b}), flush=True)
+        "attention_bytes_per_layer": attn_b, "moved_rows_per_step": moved,
+        "bytes_per_step": step_b, "kv_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "attn_split_pipe128<G=4> (M + 1 tokens)",
+                     "achieved": round(attn_b / (attn_us * 1e-6) / 1e9, 1) if attn_us else None,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_b / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                     if attn_us else None, "traffic": None, "bytes_per_launch": attn_b,
+                     "avg_launch_ms": round(attn_us / 1000, 5)},
+        "cpu_baseline": None}
+    if host_units:
+        line["cpu_baseline"] = cpu_baseline(w, host_units, M, M, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
 
 
 def asm_bench(args):
@@ -403,6 +465,21 @@ def asm_step_bench(args):
         for d in caches:
             d["len"].fill_(w.ctx)
 
+    # CPU baseline inputs: the whole KV heads of layer 0 with their codebooks
+    host_units = []
+    if not args.no_cpu:
+        import numpy as np
+        bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+        d0, (q0, kn0, vn0, _) = caches[0], qs[0]
+        cent0, abar0, lz0 = books[0]
+        cb = [(bits(cent0[g]), bits(abar0[g]), lz0[g].cpu().numpy()) for g in range(w.hkv)]
+        for u in range(w.units):
+            b, g = divmod(u, w.hkv)
+            host_units.append((bits(d0["k"][b, g, :w.ctx + 1]), bits(d0["v"][b, g, :w.ctx + 1]),
+                               d0["pos"][b, g, :w.ctx + 1].cpu().numpy(),
+                               bits(q0[b, g * w.group:(g + 1) * w.group]), bits(kn0[b, g]),
+                               bits(vn0[b, g]), cb[g]))
+
     for _ in range(args.warmup):
         restore()
         step()
@@ -452,7 +529,10 @@ def asm_step_bench(args):
     look_b = (w.hkv * w.codebook * w.head_dim * 2 + B * w.hq * (w.head_dim * 2 + 4)
               + B * w.hq * 4)
     split_ms = sum(per["attn_split"]) / len(per["attn_split"])
-    print(json.dumps({
+    # the split launch also scans the codebook (kv_attn_decode_asm): its bytes are the
+    # attention's plus the codebook's
+    unit_b = attn_b + (0 if two_calls else w.hkv * w.codebook * w.head_dim * 2)
+    line = {
         "metric": "ASM decode steps/s (attention over 2048 tokens + centroid lookup + merge, "
                   "36 layers)",
         "value": round(1000.0 / ms, 3), "unit": "decode steps/s", "n_gpus": 1,
@@ -468,7 +548,56 @@ def asm_step_bench(args):
         "attn_split_us": round(split_ms * 1000, 2),
         "attn_split_gbps": round(attn_b / (split_ms * 1e-3) / 1e9, 1),
         "lookup_kernels_us": {k: round(sum(v) / len(v) * 1000, 2) for k, v in per.items()
-                              if k != "attn_split"}}), flush=True)
+                              if k != "attn_split"},
+        "hbm_frac": round(L * (attn_b + look_b) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "attn_split_asm<G=4>" if not two_calls
+                     else "attn_split_pipe128<G=4>",
+                     "achieved": round(unit_b / (split_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(unit_b / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": unit_b,
+                     "avg_launch_ms": round(split_ms, 5)},
+        "cpu_baseline": asm_cpu_baseline(w, host_units, args.cpu_seconds) if host_units
+        else None}
+    print(json.dumps(line), flush=True)
+
+
+def asm_cpu_baseline(w, host_units, budget_s):
+    """The float64 oracle, as it stands, on whole KV heads of the ASM workload: append
+    the decode token, attention of the head's query group over its 2049 tokens,
+    cosine lookup of each query in the head's codebook and the merge; heads taken
+    in turn until ``budget_s`` of CPU work; extrapolated to units x layers."""
+    import numpy as np
+
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    f64 = lambda x: (np.asarray(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    done, elapsed = 0, 0.0
+    for (k, v, pos, q, kn, vn, (cent, abar, lz)) in itertools.cycle(host_units):
+        t0 = time.perf_counter()
+        n = w.ctx
+        c = oracle.Cache(k[None, None].copy(), v[None, None].copy(), None, pos[None, None].copy(),
+                         np.array([[n]], np.int32))
+        oracle.append_tokens(c, kn[None, None], vn[None, None], None, np.array([n]))
+        so, sl = oracle.decode_attention(c.values("k"), c.values("v"), None, c.pos, c.length,
+                                         f64(q)[None], np.array([n]))
+        oracle.asm_lookup_merge(f64(q)[None], f64(cent)[None], f64(abar)[None],
+                                np.asarray(lz, np.float64)[None], so, sl)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    step_s = elapsed / done * w.units * w.layers
+    return {"value": 1.0 / step_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} runs over the {len(host_units)} whole KV heads of layer 0 "
+                      f"({w.ctx + 1} tokens, {w.group} query heads, {w.codebook} codebook "
+                      f"entries each: append + attention + lookup + merge), {elapsed:.1f} s, "
+                      f"extrapolated to {w.units} heads x {w.layers} layers",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def build_bench(args):
@@ -619,8 +748,9 @@ def memento_bench(args):
     assert int(n_er.min()) == int(n_er.max()) == w.ctx - kept, "erased count"
     assert bool((dc["len"] == kept + 1).all()), "kept + decode token"
     assert int(n_ev.max()) == 0, "eviction to 65536 is a no-op"
-    kvb.trace_enable(64 * trials + 64, ("keep_count", "keep_emit", "compact_move",
-                                        "attn_split", "attn_merge", "evict_select"))
+    kvb.trace_enable(64 * trials + 64, ("erase_search", "erase_plan", "keep_count",
+                                        "keep_emit", "compact_move", "attn_split",
+                                        "attn_merge", "evict_select"))
     for _ in range(trials):
         trial()
     per = {}
@@ -628,7 +758,9 @@ def memento_bench(args):
         per.setdefault(name, []).append(kms * 1000.0)
     kvb.trace_disable()
     U, D, e = w.units, w.head_dim, w.elem_bytes
-    erase_b = U * w.ctx * 4 + U * kept * 2 * (2 * D * e + 4)  # pos scan + moves
+    # kept rows moved (K, V, pos read and written); the erase locates each range's
+    # slots by searching the sorted positions, so it reads no position scan
+    erase_b = U * kept * 2 * (2 * D * e + 4)
     attn_b = algorithmic_bytes(w, kept + 1, 0)[0]
     med = np.median(res, axis=0)
     total = float(np.sum(med))

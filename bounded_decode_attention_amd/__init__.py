@@ -20,6 +20,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    asm_lookup_merge_hier_workspace, asm_lookup_merge_workspace,
                    NOALLOC_SCRATCH_BYTES, kv_append, kv_attn_decode, kv_attn_decode_asm,
                    kv_attn_decode_asm_workspace, kv_attn_decode_noalloc, workspace_status,
+                   kv_check_cache, CHECK_BITS,
                    kv_attn_decode_compact, kv_attn_decode_splits, kv_attn_decode_workspace,
                    kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_one,
                    kv_evict_plan,
@@ -31,6 +32,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
 __all__ = [
     "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
     "kv_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "workspace_status",
+    "kv_check_cache", "CHECK_BITS",
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_evict_one", "kv_attn_decode_compact",
     "kv_attn_decode_asm", "kv_attn_decode_asm_workspace",
     "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",

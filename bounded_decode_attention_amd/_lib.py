@@ -52,6 +52,7 @@ def library():
             "asm_lookup_merge_hier_workspace": (SZ, [I32, I32, I32, I32, I32]),
             "kv_attn_decode": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P]),
             "kv_attn_decode_noalloc": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, P]),
+            "kv_check_cache": (I32, [CP, P, P, P, I32, P, P]),
             "kv_attn_decode_asm_workspace": (SZ, [CP, I32, I32, I32]),
             "kv_attn_decode_asm": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, I32, P, P, P,
                                          P, SZ, P]),
@@ -335,6 +336,30 @@ def kv_evict_to_budget(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=No
     return n_evicted
 
 
+CHECK_BITS = {"len": 1, "start": 2, "pos_order": 4, "pos_after_t": 8, "log_beta_nan": 16,
+              "log_beta_positive": 32, "ranges": 64}
+
+
+def kv_check_cache(cache: KVCache, t=None, ranges=None, n_ranges=None, flags=None,
+                   stream=None):
+    """Device-side precondition check (kv_check_cache in kvbound.h).  Returns the
+    [B][Hkv] int32 tensor of violation bits (CHECK_BITS); 0 means none."""
+    if t is not None:
+        _need(t, "t", torch.int32)
+    R = 0
+    if n_ranges is not None:
+        _need(n_ranges, "n_ranges", torch.int32)
+        _need(ranges, "ranges", torch.int32)
+        R = ranges.shape[1]
+    if flags is None:
+        flags = torch.empty((cache.B, cache.Hkv), dtype=torch.int32, device=cache.pos.device)
+    _need(flags, "flags", torch.int32)
+    st = library().kv_check_cache(cache.desc, _ptr(t), _ptr(ranges), _ptr(n_ranges), int(R),
+                                  _ptr(flags), _stream(stream))
+    _check(st, "kv_check_cache")
+    return flags
+
+
 def kv_append(cache: KVCache, k_new, v_new, log_beta_new, t, ws=None, stream=None,
               check_status: bool = False):
     """Append one token per KV head (slot len, pos = t[b]); len += 1.
@@ -470,7 +495,8 @@ TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "asm_finalize": 256, "attn_fused": 512, "asm_prefix": 1024,
               "asm_prefix_merge": 2048, "km_assign": 4096, "km_update": 8192,
               "asm_aggregate": 16384, "asm_vt": 32768, "latent_absorb": 65536,
-              "latent_read": 131072, "evict_one": 262144}
+              "latent_read": 131072, "evict_one": 262144, "erase_search": 524288,
+              "erase_plan": 1048576}
 
 
 def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:

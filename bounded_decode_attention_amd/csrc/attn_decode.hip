@@ -32,6 +32,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "asm_scan.h"
 
 namespace kvb {
 
@@ -346,6 +347,12 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kVBlk = 1056;  // bytes per V DMA instruction block (1 KB + pad)
+// Cache-policy operand of the V transfers: the non-temporal (streaming) hint.  Each
+// V row is read once per launch; marking the stream non-temporal took the 32K
+// layer from 372 to 331 us (5.9 -> 6.6 TB/s) with bit-identical results.  The same
+// hint on the K register loads helped less with it than without it, so K loads
+// stay plain.
+constexpr int kNonTemporal = 2;
 
 struct KTile {
   u32x4 k[2][4];
@@ -387,15 +394,15 @@ __device__ __forceinline__ void issue_tile128(const uint16_t* kb, const uint16_t
   for (int i = 0; i < 8; ++i) {
     const int row = wr(min(tb + 4 * i + lg, last));
     __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (ptrdiff_t)row * 128 + 8 * lc),
-                                     (lds_void_t*)(vlds + i * kVBlk), 16, 0, 0);
+                                     (lds_void_t*)(vlds + i * kVBlk), 16, 0, kNonTemporal);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r0 = tb + 16 * j + 4 * lg;
     if constexpr (VEC) {
       const int rb = min(r0, capu - 4);
-      const f32x4 l4 = *(const f32x4*)(lbb + rb);
-      const i32x4 p4 = *(const i32x4*)(pb + rb);
+      const f32x4 l4 = __builtin_nontemporal_load((const f32x4*)(lbb + rb));
+      const i32x4 p4 = __builtin_nontemporal_load((const i32x4*)(pb + rb));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         t.lb[j][r] = l4[r];
@@ -532,16 +539,16 @@ __device__ __forceinline__ void move_tile128(const KTile& t, const lds_u8* __res
   }
 }
 
+// One split (p, head u) of the pipelined kernel; the launch has gridDim.x splits per
+// head.  A device function so that a launch can also carry other work (the ASM
+// candidate scan of kv_attn_decode_asm) in workgroups of its own.
 template <int G, bool LB, bool VEC, bool MOVE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_split_pipe128(AttnArgs a) {
+__device__ __forceinline__ void pipe128_split(const AttnArgs& a, const int p, const int u) {
   static_assert(2 * G <= 16, "group too large for the hi/lo column split");
   __shared__ __attribute__((aligned(16))) unsigned char vbufA_[8 * kVBlk];
   __shared__ __attribute__((aligned(16))) unsigned char vbufB_[8 * kVBlk];
   lds_u8* vbufA = (lds_u8*)vbufA_;
   lds_u8* vbufB = (lds_u8*)vbufB_;
-  const int u = blockIdx.y;
-  const int p = blockIdx.x;
   const int b = u / a.Hkv;
   const int g = u - b * a.Hkv;
   const int lane = threadIdx.x;
@@ -550,8 +557,8 @@ void attn_split_pipe128(AttnArgs a) {
   const int s0 = head_start(a.start, u);
   const int capu = a.cap - s0;  // rows before the head wraps to the start of its slots
   const int n = min(a.len[u], a.cap);
-  if (a.n_rec && blockIdx.x == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
-  if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.status[0] = KVB_OK;
+  if (a.n_rec && p == 0 && threadIdx.x == 0) a.n_rec[u] = a.len[u];
+  if (a.status && p == 0 && u == 0 && threadIdx.x == 0) a.status[0] = KVB_OK;
   const int end = n;
   const size_t row0 = (size_t)u * a.cap + s0;  // the head's first live slot
 
@@ -696,6 +703,33 @@ void attn_split_pipe128(AttnArgs a) {
       a.part_ml[2 * sidx + 1] = lsum;
     }
   }
+}
+
+template <int G, bool LB, bool VEC, bool MOVE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_split_pipe128(AttnArgs a) {
+  pipe128_split<G, LB, VEC, MOVE>(a, blockIdx.x, blockIdx.y);
+}
+
+// The splits plus the ASM lookup's candidate scan in one launch: rows y < crow of
+// the grid are scan tasks (one wave each, dispatched first), the rest the splits of
+// head y - crow.  The scan's few microseconds of latency-bound work then overlap
+// the splits instead of preceding them as a launch of their own.
+template <int G, bool LB, bool VEC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_split_asm(AttnArgs a, AsmScanArgs c, int crow) {
+  if ((int)blockIdx.y < crow) {
+    asm_scan_wave<128>(c, (int)(blockIdx.y * gridDim.x + blockIdx.x));
+    return;
+  }
+  pipe128_split<G, LB, VEC, false>(a, blockIdx.x, (int)blockIdx.y - crow);
+}
+
+// The candidate scan alone (one wave per task), where the splits are not the
+// pipelined kernel.
+template <int D>
+__global__ __launch_bounds__(64) void asm_scan_kernel(AsmScanArgs c) {
+  asm_scan_wave<D>(c, (int)blockIdx.x);
 }
 
 // ------------------------------------------------------------------ generic split
@@ -1003,6 +1037,178 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
   }
 }
 
+// The merge for at most 64 splits and D in {64, 128}: one thread per output
+// dimension, reductions over the splits by wave shuffles (wave 0, one split per
+// lane) instead of workgroup-wide trees, so the chain is one round of loads (split
+// states, decode token, lookup candidates), a few shuffles, the chosen entry's
+// gather and the stores.  Same arithmetic per output as attn_merge up to the
+// order of the per-dimension sum (here split by split, in order).
+template <int D>
+__global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const float* part_ml,
+                                                      int P, float* out, float* lse,
+                                                      const UnitInfo* info, int32_t* len,
+                                                      int G, NewTok nt, AsmTail at) {
+  constexpr int NW = D / 64;
+  __shared__ float s_w[64];
+  __shared__ float s_red[2][NW];
+  __shared__ float s_mw[2];
+  __shared__ int s_k;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* ml = part_ml + (size_t)bh * P * 2;
+  const float* pa = part_a + (size_t)bh * P * D;
+  const int u = bh / G;
+  // every load of the first round: this dimension's split outputs (first 16), the
+  // split (m, Z) in wave 0, the decode token's q.k product terms, the candidates
+  constexpr int kB = 16;
+  float x[kB];
+#pragma unroll
+  for (int e = 0; e < kB; ++e) x[e] = e < P ? pa[(size_t)e * D + tid] : 0.f;
+  float mp = kNegInf, zp = 0.f;
+  if (wave == 0 && lane < P) {
+    mp = ml[2 * lane];
+    zp = ml[2 * lane + 1];
+  }
+  bool incl = false;
+  float pr = 0.f;
+  if (nt.k_new) {
+    incl = nt.n_rec[u] < nt.cap;
+    if (incl)
+      pr = load_elem(nt.q, (size_t)bh * D + tid, nt.elem) *
+           load_elem(nt.k_new, (size_t)u * D + tid, nt.elem);
+  }
+  float q2 = 0.f;
+  float cs = kNegInf;
+  int ck = 0x7FFFFFFF;
+  const int bq = bh / (at.cand_score ? at.Hq : 1);
+  const int hq = bh - bq * (at.cand_score ? at.Hq : 1);
+  if (at.cand_score) {
+    const float xq = bf16_bits_to_f32(at.q[(size_t)bh * D + tid]);
+    q2 = xq * xq;
+    if (wave == 0) {
+      const int g = hq / G, j = hq - g * G;
+      const size_t base = ((size_t)g * at.QB * 16 + bq * G + j) * at.KC;
+      for (int c = lane; c < at.KC; c += 64) {
+        const float sc = at.cand_score[base + c];
+        const int k = at.cand_idx[base + c];
+        if (sc > cs || (sc == cs && k < ck)) {
+          cs = sc;
+          ck = k;
+        }
+      }
+    }
+  }
+  // decode-token logit and |q|^2 over the workgroup
+  pr = wave_sum(pr);
+  q2 = wave_sum(q2);
+  if (lane == 0) {
+    s_red[0][wave] = pr;
+    s_red[1][wave] = q2;
+  }
+  __syncthreads();
+  float s_new = kNegInf;
+  if (incl) {
+    float dsum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) dsum += s_red[0][w2];
+    s_new = dsum * nt.scale;
+  }
+  // split maximum, weights and total, and the lookup's best entry (wave 0)
+  if (wave == 0) {
+    const float Mp = wave_max(zp > 0.f ? mp : kNegInf);
+    const float M = fmaxf(Mp, s_new);
+    const float wp = (zp > 0.f && M != kNegInf) ? zp * __expf(mp - M) : 0.f;
+    const float W = wave_sum(wp);
+    if (lane < P) s_w[lane] = wp;
+    if (lane == 0) {
+      s_mw[0] = M;
+      s_mw[1] = W;
+    }
+    if (at.cand_score) {
+#pragma unroll
+      for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+        const float os = __shfl_xor(cs, o2, 64);
+        const int ok = __shfl_xor(ck, o2, 64);
+        if (os > cs || (os == cs && ok < ck)) {
+          cs = os;
+          ck = ok;
+        }
+      }
+      if (lane == 0) {
+        float qq = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) qq += s_red[1][w2];
+        const int k = (qq > 0.f && ck != 0x7FFFFFFF) ? ck : 0;
+        s_k = k;
+        if (at.idx) at.idx[bh] = k;
+      }
+    }
+  }
+  __syncthreads();
+  const float M = s_mw[0];
+  const float w_new = incl ? __expf(s_new - M) : 0.f;
+  const float W = s_mw[1] + w_new;
+  float o = 0.f;
+#pragma unroll
+  for (int e = 0; e < kB; ++e)
+    if (e < P) o = fmaf(s_w[e], x[e], o);
+  for (int pb = kB; pb < P; pb += kB) {
+#pragma unroll
+    for (int e = 0; e < kB; ++e) x[e] = pb + e < P ? pa[(size_t)(pb + e) * D + tid] : 0.f;
+#pragma unroll
+    for (int e = 0; e < kB; ++e)
+      if (pb + e < P) o = fmaf(s_w[pb + e], x[e], o);
+  }
+  if (incl) o = fmaf(w_new, load_elem(nt.v_new, (size_t)u * D + tid, nt.elem), o);
+  float so = W > 0.f ? o / W : 0.f;
+  const float lse_self = W > 0.f ? M + __logf(W) : kNegInf;
+  float lse_out = lse_self;
+  if (at.cand_score) {
+    // merge with the entry's stored state by the normalisers (as asm_lookup_merge)
+    const int g = hq / G;
+    const int k = s_k;
+    const float lz = at.log_zbar[(size_t)g * at.K + k];
+    const float av = bf16_bits_to_f32(at.abar[((size_t)g * at.K + k) * D + tid]);
+    const float Mx = fmaxf(lse_self, lz);
+    float w1 = 0.f, w2 = 0.f;
+    lse_out = kNegInf;
+    if (Mx != kNegInf) {
+      w1 = lse_self == kNegInf ? 0.f : __expf(lse_self - Mx);
+      w2 = lz == kNegInf ? 0.f : __expf(lz - Mx);
+      lse_out = Mx + __logf(w1 + w2);
+    }
+    const float inv = (w1 + w2) > 0.f ? 1.f / (w1 + w2) : 0.f;
+    so = fmaf(w1, so, w2 * av) * inv;
+  }
+  out[(size_t)bh * D + tid] = so;
+  if (tid == 0) lse[bh] = lse_out;
+  // append the decode token (first query head of each KV head); every split has
+  // read the old len, and the other merge blocks use the recorded one
+  if (nt.k_new && bh % G == 0) {
+    if (!incl) {
+      if (tid == 0) nt.status[0] = KVB_ECAPACITY;
+    } else {
+      const int n0 = nt.n_rec[u];
+      int s0 = head_start(nt.start, u) + n0;  // slot of the decode token
+      if (s0 >= nt.cap) s0 -= nt.cap;
+      const int words = D * nt.elem / 4;
+      const size_t dst = ((size_t)u * nt.cap + s0) * words;
+      for (int w = tid; w < words; w += D) {
+        ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
+        ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
+      }
+      if (tid == 0) {
+        nt.pos[(size_t)u * nt.cap + s0] = nt.t[u / nt.Hkv];
+        if (nt.log_beta) nt.log_beta[(size_t)u * nt.cap + s0] = nt.lb_new[u];
+        nt.len[u] = n0 + 1;
+      }
+    }
+  }
+  // fused compaction: the head's new length (every split has read the old one)
+  if (info && tid == 0 && bh % G == 0) {
+    if (info[u].mode == MODE_EVICT) len[u] = info[u].kept;
+  }
+}
+
 // ------------------------------------------------------------------ host
 static void launch_merge(const float* part_a, const float* part_ml, int P, int D, float* out,
                          float* lse, const UnitInfo* info, int32_t* len, int G, int BH,
@@ -1014,6 +1220,16 @@ static void launch_merge(const float* part_a, const float* part_ml, int P, int D
   AsmTail no_tail;
   memset(&no_tail, 0, sizeof(no_tail));
   const AsmTail& at = tail ? *tail : no_tail;
+  if (P <= 64 && D == 128) {
+    hipLaunchKernelGGL(attn_merge_small<128>, dim3(BH), dim3(128), 0, s, part_a, part_ml, P, out,
+                       lse, info, len, G, n, at);
+    return;
+  }
+  if (P <= 64 && D == 64) {
+    hipLaunchKernelGGL(attn_merge_small<64>, dim3(BH), dim3(64), 0, s, part_a, part_ml, P, out,
+                       lse, info, len, G, n, at);
+    return;
+  }
   if (P > 128)
     hipLaunchKernelGGL(attn_merge<512>, dim3(BH), dim3(512), 0, s, part_a, part_ml, P, D, out,
                        lse, info, len, G, n, at);
@@ -1038,8 +1254,35 @@ static void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((attn_split_mfma<D, G>), grid, dim3(64), 0, s, a);
 }
 
-static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s) {
+static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s,
+                            const AsmScanArgs* scan = nullptr) {
   dim3 grid(a.P, c->B * c->Hkv);
+  const long long crow_ll = scan ? ((long long)scan->tasks + a.P - 1) / a.P : 0;
+  if (scan && c->dtype == KVB_BF16 && c->D == 128 &&
+      (a.G == 1 || a.G == 2 || a.G == 4 || a.G == 8) &&
+      crow_ll + (long long)c->B * c->Hkv <= 65535) {
+    // the candidate scan rides in the first rows of the split launch
+    const int crow = (int)crow_ll;
+    dim3 g2(a.P, crow + c->B * c->Hkv);
+#define KVB_ASM_CASE(GG)                                                                   \
+  if (a.G == GG) {                                                                         \
+    const bool lb = c->log_beta != nullptr, vec = vec_bias_loads(c);                      \
+    if (lb && vec) hipLaunchKernelGGL((attn_split_asm<GG, true, true>), g2, dim3(64), 0, s, a, *scan, crow);   \
+    else if (lb) hipLaunchKernelGGL((attn_split_asm<GG, true, false>), g2, dim3(64), 0, s, a, *scan, crow);   \
+    else if (vec) hipLaunchKernelGGL((attn_split_asm<GG, false, true>), g2, dim3(64), 0, s, a, *scan, crow);  \
+    else hipLaunchKernelGGL((attn_split_asm<GG, false, false>), g2, dim3(64), 0, s, a, *scan, crow);          \
+    return KVB_OK;                                                                         \
+  }
+    KVB_ASM_CASE(1) KVB_ASM_CASE(2) KVB_ASM_CASE(4) KVB_ASM_CASE(8)
+#undef KVB_ASM_CASE
+  }
+  if (scan) {
+    // other shapes: the scan as a launch of its own before the splits
+    if (c->D == 128)
+      hipLaunchKernelGGL(asm_scan_kernel<128>, dim3(scan->tasks), dim3(64), 0, s, *scan);
+    else
+      hipLaunchKernelGGL(asm_scan_kernel<64>, dim3(scan->tasks), dim3(64), 0, s, *scan);
+  }
   if (mfma_supported(c, a.G)) {
 #define KVB_PIPE_CASE(GG)                                                                  \
   if (c->D == 128 && a.G == GG) {                                                          \
@@ -1073,14 +1316,31 @@ static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s
   return KVB_EUNSUPPORTED;
 }
 
-// About two rounds of resident waves (2 per SIMD): fewer, longer splits stream
-// better than many short ones, and keep the merged partial states small.  A split
-// covers at least 256 slots (two 128-token tiles): on short heads one-tile splits
-// spend their time in set-up and partial-state writes.
+// Candidate-scan dimensions of kv_attn_decode_asm: QB blocks of 16 query rows per KV
+// head, KC chunks of kScanChunk centroids, one task per (chunk, head, 64 rows).
+static AsmScanArgs scan_dims(int B, int Hq, int Hkv, int K) {
+  AsmScanArgs c;
+  memset(&c, 0, sizeof(c));
+  c.B = B;
+  c.Hq = Hq;
+  c.Hkv = Hkv;
+  c.K = K;
+  c.G = Hq / Hkv;
+  c.QB = (B * c.G + 15) / 16;
+  c.KC = (K + kScanChunk - 1) / kScanChunk;
+  c.tasks = c.KC * Hkv * ((c.QB + kScanQB - 1) / kScanQB);
+  return c;
+}
+
+// About one round of resident waves (2 per SIMD on 256 CUs): fewer, longer splits
+// stream better than many short ones (on the 32K layer 16 splits per head take 331
+// us, 32 take 337 us, 64 take 374 us), and keep the merged partial states small.  A
+// split covers at least 256 slots (two 128-token tiles): on short heads one-tile
+// splits spend their time in set-up and partial-state writes.
 static int32_t auto_splits(const kvb_cache* c) {
   const long long units = (long long)c->B * c->Hkv;
   const long long tiles = c->cap / 256;
-  long long P = (4096 + units - 1) / units;
+  long long P = (2048 + units - 1) / units;
   if (P > tiles) P = tiles;
   if (P > 1024) P = 1024;
   if (P < 1) P = 1;
@@ -1131,7 +1391,8 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
                                 const void* v_new, const float* log_beta_new,
                                 int32_t num_splits, float* out, float* lse, void* ws,
                                 size_t ws_bytes, hipStream_t stream, const AsmTail* tail,
-                                int32_t* status = nullptr) {
+                                int32_t* status = nullptr,
+                                const AsmScanArgs* scan = nullptr) {
   int32_t st = check_cache(cache, true);
   if (st) return st;
   if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
@@ -1200,7 +1461,7 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
   }
   {
     TraceScope tr(kTrAttnSplit, s);
-    if ((st = launch_split(cache, a, s))) return st;
+    if ((st = launch_split(cache, a, s, scan))) return st;
   }
   TraceScope tr(kTrAttnMerge, s);
   launch_merge(a.part_a, a.part_ml, P, cache->D, out, lse, nullptr, nullptr, G,
@@ -1266,9 +1527,8 @@ extern "C" size_t kv_attn_decode_asm_workspace(const kvb_cache* cache, int32_t H
                                                int32_t num_splits, int32_t K) {
   const size_t wa = kv_attn_decode_workspace(cache, Hq, num_splits);
   if (!wa || K < 1 || cache->Hkv < 1 || Hq % cache->Hkv) return 0;
-  int G, QB, KC;
-  asm_dims(cache->B, Hq, cache->Hkv, K, G, QB, KC);
-  const size_t n = (size_t)cache->Hkv * QB * 16 * KC;
+  const AsmScanArgs c = scan_dims(cache->B, Hq, cache->Hkv, K);
+  const size_t n = (size_t)cache->Hkv * c.QB * 16 * c.KC;
   return align_up(wa, 256) + 2 * align_up(n * 4, 256);
 }
 
@@ -1290,31 +1550,30 @@ extern "C" int32_t kv_attn_decode_asm(const kvb_cache* cache, const void* q, int
   const size_t need = kv_attn_decode_asm_workspace(cache, Hq, P, K);
   if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
   if ((st = check_device())) return st;
-  int G, QB, KC;
-  asm_dims(cache->B, Hq, cache->Hkv, K, G, QB, KC);
+  AsmScanArgs sc = scan_dims(cache->B, Hq, cache->Hkv, K);
   const size_t wa = align_up(kv_attn_decode_workspace(cache, Hq, P), 256);
-  const size_t n = (size_t)cache->Hkv * QB * 16 * KC;
+  const size_t n = (size_t)cache->Hkv * sc.QB * 16 * sc.KC;
+  sc.q = (const uint16_t*)q;
+  sc.cent = (const uint16_t*)centroids;
+  sc.cand_score = (float*)((char*)ws + wa);
+  sc.cand_idx = (int32_t*)((char*)ws + wa + align_up(n * 4, 256));
   AsmTail at;
-  at.cand_score = (const float*)((char*)ws + wa);
-  at.cand_idx = (const int32_t*)((char*)ws + wa + align_up(n * 4, 256));
+  at.cand_score = sc.cand_score;
+  at.cand_idx = sc.cand_idx;
   at.q = (const uint16_t*)q;
   at.abar = (const uint16_t*)abar;
   at.log_zbar = log_zbar;
   at.idx = idx;
   at.K = K;
-  at.KC = KC;
-  at.QB = QB;
+  at.KC = sc.KC;
+  at.QB = sc.QB;
   at.Hq = Hq;
-  hipStream_t s = (hipStream_t)stream;
-  // the lookup needs only q and the codebook: its candidates first, then the
-  // attention, whose merge finishes the lookup.  (Beside the splits, on a second
-  // stream, the candidate scan is starved by the splits' workgroups and the layer
-  // takes longer.)
-  launch_asm_candidates((const uint16_t*)q, cache->B, Hq, cache->Hkv, cache->D,
-                        (const uint16_t*)centroids, K, (float*)at.cand_score,
-                        (int32_t*)at.cand_idx, s);
+  // the lookup needs only q and the codebook: its candidate scan runs in the first
+  // workgroups of the split launch, and the attention's merge finishes the lookup.
+  // (As a launch of its own before the splits it added ~13 us of latency to the
+  // layer; beside them on a second stream it was starved by their workgroups.)
   return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, P, out, lse, ws,
-                          wa, s, &at);
+                          wa, (hipStream_t)stream, &at, nullptr, &sc);
 }
 
 // ------------------------------------------------------------------ fused attention + compaction

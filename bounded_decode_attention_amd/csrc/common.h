@@ -195,7 +195,8 @@ enum TraceKernel {
   kTrKeepEmit = 32, kTrCompactMove = 64, kTrAsmLookup = 128, kTrAsmFinalize = 256,
   kTrAttnFused = 512, kTrAsmPrefix = 1024, kTrAsmPrefixMerge = 2048, kTrKmAssign = 4096,
   kTrKmUpdate = 8192, kTrAsmAggregate = 16384, kTrAsmVt = 32768,
-  kTrLatentAbsorb = 65536, kTrLatentRead = 131072, kTrEvictOne = 262144
+  kTrLatentAbsorb = 65536, kTrLatentRead = 131072, kTrEvictOne = 262144,
+  kTrEraseSearch = 524288, kTrErasePlan = 1048576
 };
 struct TraceScope {
   TraceScope(int kernel, hipStream_t s);

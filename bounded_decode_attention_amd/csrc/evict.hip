@@ -46,6 +46,8 @@ constexpr int kChunk = 4096;      // slots per keep_count / keep_emit workgroup
 constexpr int kChunkThreads = 256;
 constexpr int kPerThread = kChunk / kChunkThreads;
 constexpr int kSelThreads = 1024;
+// byte offset of the erase path's largest-kept-count word in the workspace header
+constexpr size_t kWsMaxKept = 128;
 
 // ---------------------------------------------------------------- keys
 // A head's per-slot array seen from its first live slot: index i is i slots past
@@ -602,6 +604,10 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
     return ord32((!lb || d == 0) ? 0.0 : (double)d * (double)l);
   };
 
+  // One eviction (the steady state: n = M + 1): the threshold is the minimum of
+  // (key, slot), found by reductions instead of radix passes.
+  const bool one = r == 1;
+  uint32_t kmin = 0xFFFFFFFFu;  // this thread's smallest float32-ordered key
   // ---- pass 0: keys to LDS + histogram of the top 11 bits.  All of a round's
   // loads are issued before any key is formed (the loop is latency bound otherwise).
   for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
@@ -633,7 +639,8 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
           if (j < nq && i >= 0 && i < n) {
             const uint32_t k32 = key32(l4[e][c], p4[e][c]);
             keys[skew(i)] = k32;
-            atomicAdd(&hist[k32 >> 21], 1u);
+            if (one) kmin = min(kmin, k32);
+            else atomicAdd(&hist[k32 >> 21], 1u);
           }
         }
       }
@@ -655,17 +662,36 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
         if (i < n) {
           const uint32_t k32 = key32(lv[e], pv[e]);
           keys[skew(i)] = k32;
-          atomicAdd(&hist[k32 >> 21], 1u);
+          if (one) kmin = min(kmin, k32);
+          else atomicAdd(&hist[k32 >> 21], 1u);
         }
       }
     }
   }
   __syncthreads();
+  uint32_t t32;
+  unsigned long long K;
+  if (one) {
+    // the smallest float32 key, then the smallest exact key among its ties, then
+    // the lowest slot among those
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    if (lane == 0) hist[wv] = kmin;
+    __syncthreads();
+    t32 = hist[0];
+    for (int w2 = 1; w2 < kSelThreads / 64; ++w2) t32 = min(t32, hist[w2]);
+    for (int i = tid; i < n; i += kSelThreads)
+      if (keys[skew(i)] == t32) atomicMin(&mm[0], ord64(retention_key(lb, ps, i, tpos)));
+    __syncthreads();
+    K = mm[0];
+    if (tid == 0) out[2] = 0x7FFFFFFF;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads)
+      if (keys[skew(i)] == t32 && ord64(retention_key(lb, ps, i, tpos)) == K) atomicMin(&out[2], i);
+  } else {
   int bucket = select_bucket<kSelThreads>(hist, 2048, r, smem, out);
   const uint32_t b0 = (uint32_t)bucket;
   const int c0 = (int)hist[b0];
-  uint32_t t32;
-  unsigned long long K;
   if (c0 <= kCand) {
     // ---- the bucket's slots to a list; the remaining passes and the ties use it
     constexpr int kU = 8;  // LDS reads in flight per thread
@@ -802,6 +828,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
         }
     }
   }
+  }  // general case
   __syncthreads();
   const int sstar = out[2];
 
@@ -1170,15 +1197,164 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- erase by range endpoints
+// Positions increase along a head's live slots, so the slots an erase range [s, e)
+// covers form one run, [lb(s), lb(e)) with lb(x) = number of live slots whose position
+// is below x, and the kept slots are the runs between consecutive ranges.  Instead of
+// testing every slot, erase_search finds lb at each range endpoint and erase_plan
+// lays the kept runs end to end (keep_src, staging, the head's new length); the
+// rows then move with compact_move as for an eviction.
+constexpr int kEraseMaxR = 4096;  // ranges per sequence on this path (LDS tables)
+
+// One wave per (endpoint, head): 64 evenly spaced probes per round cut the search
+// interval 64-fold (four dependent loads for a 1M-slot head).  Invariant: slots
+// below lo have positions below x, slots at or above hi do not.  The probes that
+// fall below x are a prefix of the lanes; malformed (unsorted) positions still give
+// a value in [0, n] after at most ~log64(n) + 1 rounds.
+__global__ __launch_bounds__(256) void erase_search(KeepArgs a, int32_t* ep, int32_t* max_kept) {
+  const int u = blockIdx.y;
+  const int b = u / a.Hkv;
+  const int e = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *max_kept = 0;
+  const int nr = max(0, min(a.n_ranges[b], a.R));
+  if (e >= 2 * nr) return;
+  const int x = a.ranges[(size_t)b * a.R * 2 + e];
+  const int s0 = head_start(a.start, u);
+  const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
+  const int n = min(a.len[u], a.cap);
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int step = (hi - lo + 63) >> 6;
+    const int i = lo + lane * step;
+    const bool below = i < hi && ps[i] < x;
+    const int c = __popcll(__ballot(below));
+    if (c == 0) break;                   // the probe at lo is not below x: lb = lo
+    const int nxt = lo + c * step;       // first probe not below x (or past hi)
+    lo = lo + (c - 1) * step + 1;
+    hi = min(hi, nxt);
+  }
+  if (lane == 0) ep[(size_t)u * 2 * a.R + e] = lo;
+}
+
+// Grid (kErasePlanBlocks, heads).  Kept run k is [a_k, b_k) with a_0 = 0,
+// a_k = lb(e_{k-1}), b_k = lb(s_k), b_nr = n; its rows go to slots d_k .. d_k +
+// (b_k - a_k) - 1, d_k the exclusive prefix of the run lengths.  Each workgroup
+// builds the (small) run table in LDS once, then takes destination blocks of one
+// row per thread, strided over the grid: writes keep_src and copies to scratch the
+// rows compact_move must not read in place (staged_row), as keep_emit does.
+constexpr int kErasePlanBlocks = 64;
+__global__ __launch_bounds__(kChunkThreads) void erase_plan(KeepArgs a, const int32_t* ep,
+                                                            int32_t* max_kept) {
+  __shared__ int s_a[kEraseMaxR + 1];
+  __shared__ int s_d[kEraseMaxR + 1];
+  __shared__ int smem[kChunkThreads / 64];
+  __shared__ int2 stg[kChunkThreads];
+  __shared__ int nstg;
+  const int u = blockIdx.y;
+  const int b = u / a.Hkv;
+  const int tid = threadIdx.x;
+  const int nr = max(0, min(a.n_ranges[b], a.R));
+  const int n = min(a.len[u], a.cap);
+  const int s0 = head_start(a.start, u);
+  const int32_t* e = ep + (size_t)u * 2 * a.R;
+  int carry = 0;
+  for (int k0 = 0; k0 <= nr; k0 += kChunkThreads) {
+    const int k = k0 + tid;
+    int len = 0;
+    if (k <= nr) {
+      const int ak = k == 0 ? 0 : e[2 * k - 1];
+      const int bk = k == nr ? n : e[2 * k];
+      len = max(bk - ak, 0);
+      s_a[k] = ak;
+    }
+    int tot;
+    const int ex = block_excl_scan<kChunkThreads>(len, smem, tot);
+    if (k <= nr) s_d[k] = carry + ex;
+    carry += tot;
+  }
+  const int kept = min(carry, n);
+  if (blockIdx.x == 0 && tid == 0) {
+    UnitInfo inf = a.info[u];
+    inf.mode = MODE_ERASE;
+    inf.n = n;
+    inf.kept = kept;
+    inf.nstart = s0;
+    inf.ostart = s0;
+    a.info[u] = inf;
+    if (a.n_out) a.n_out[u] = n - kept;
+    atomicMax(max_kept, kept);
+  }
+  __syncthreads();
+  const int jmax = min(kept, a.Mk);
+  const int ppr = a.row_bytes / 16;
+  const size_t ub = (size_t)u * a.cap;
+  for (int j0 = blockIdx.x * kChunkThreads; j0 < jmax; j0 += gridDim.x * kChunkThreads) {
+    if (tid == 0) nstg = 0;
+    __syncthreads();
+    const int j = j0 + tid;
+    if (j < jmax) {
+      // the last run starting at or below j (runs of length 0 share their start)
+      int lo = 0, hi = nr;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_d[mid] <= j) lo = mid;
+        else hi = mid - 1;
+      }
+      const int src = s_a[lo] + (j - s_d[lo]);
+      a.keep_src[(size_t)u * a.Mk + j] = src;
+      if (staged_row(s0, s0, src, j, kept, a.move_rows)) stg[atomicAdd(&nstg, 1)] = make_int2(src, j);
+    }
+    __syncthreads();
+    // this block's staged rows to scratch (by destination), one row per thread: all
+    // of a row's 16-byte pieces (K, V) and its tail are loaded before any store, so
+    // the copy costs one memory round trip (latency, not bytes, bounds it)
+    const int ns = nstg;
+    if (tid < ns) {
+      const int2 sd = stg[tid];
+      const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
+      unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
+      const unsigned char* kr = (const unsigned char*)a.k + row * a.row_bytes;
+      const unsigned char* vr = (const unsigned char*)a.v + row * a.row_bytes;
+      for (int p0 = 0; p0 < ppr; p0 += 8) {  // 8 pieces of K and 8 of V per batch
+        u32x4 xk[8], xv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (p0 + q < ppr) {
+            xk[q] = *(const u32x4*)(kr + 16 * (p0 + q));
+            xv[q] = *(const u32x4*)(vr + 16 * (p0 + q));
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (p0 + q < ppr) {
+            *(u32x4*)(sp + 16 * (p0 + q)) = xk[q];
+            *(u32x4*)(sp + a.row_bytes + 16 * (p0 + q)) = xv[q];
+          }
+        }
+      }
+      *(uint2*)(sp + 2 * a.row_bytes) =
+          make_uint2(a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u, (uint32_t)a.pos[row]);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- move
 constexpr int kMoveThreads = 256;
-constexpr int kMovePieces = 8;  // 16-byte pieces per thread per group
+// 16-byte pieces per thread per group (groups of 64 destination rows for D = 128 in
+// bf16), stores with the non-temporal hint.  Alone, plain stores and 32-row groups
+// were faster (99 against 117 us on the 32K layer); inside the decode step, where
+// the compactions run beside the next layers' planners, this form gave the shortest
+// step (16.4-16.8 against 17.0 ms).
+constexpr int kMovePieces = 8;
 
 // Thread layout: piece column pc = tid % (2*ppr) (K chunks, then V chunks) is fixed
 // per thread; the thread moves that column of rows tid / (2*ppr) + q * rpp,
 // q < kMovePieces (rpp = rows per pass).  All reads of the group are issued
 // before the barrier, all writes after it.
-__global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, int check_mode) {
+__global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, int check_mode,
+                                                              const int32_t* max_kept) {
   const int cpu = (a.Mk + a.move_rows - 1) / a.move_rows;
   const int ppr = a.row_bytes / 16;   // 16-byte pieces per row per tensor
   const int cols = 2 * ppr;
@@ -1193,7 +1369,10 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move(KeepArgs a, int U, 
   // workgroups), heads fastest, so the groups that hold rows (the first kept /
   // move_rows of every head) are the first items, spread over the grid
   const bool strided = U * cpu > (int)gridDim.x;
-  for (int w = blockIdx.x; w < U * cpu; w += gridDim.x) {
+  // with heads fastest, the items past the largest kept count hold no rows
+  int items = U * cpu;
+  if (strided && max_kept) items = min(items, U * ((*max_kept + a.move_rows - 1) / a.move_rows));
+  for (int w = blockIdx.x; w < items; w += gridDim.x) {
     const int u = strided ? w % U : w / cpu, ch = strided ? w / U : w % cpu;
     const UnitInfo inf = a.info[u];
     if (check_mode && inf.mode == MODE_NOOP) continue;
@@ -1545,16 +1724,18 @@ static void launch_keep_chunks(const kvb_cache* c, const KeepArgs& a, int mode, 
   }
 }
 
-static void launch_move(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s) {
+static void launch_move(const kvb_cache* c, const KeepArgs& a, int mode, hipStream_t s,
+                        const int32_t* max_kept = nullptr, int max_blocks = 16384) {
   const int U = c->B * c->Hkv;
   const long long items = (long long)U * ((a.Mk + a.move_rows - 1) / a.move_rows);
-  // one group per workgroup (many in flight hide the read latency) up to 16384
+  // one group per workgroup (many in flight hide the read latency) up to max_blocks
   // workgroups; past that the kernel strides over the groups (heads fastest, so the
-  // groups with rows to move, the first of every head, come first)
-  const int blocks = (int)(items < 16384 ? items : 16384);
+  // groups with rows to move, the first of every head, come first, and with
+  // max_kept the loop ends after the last of them)
+  const int blocks = (int)(items < max_blocks ? items : max_blocks);
   TraceScope tr(kTrCompactMove, s);
   hipLaunchKernelGGL(compact_move, dim3(blocks), dim3(kMoveThreads), 0, s, a, U,
-                     mode == MODE_EVICT ? 1 : 0);
+                     mode == MODE_EVICT ? 1 : 0, max_kept);
 }
 
 // Eviction plan: selection, destinations, evicted positions, staging.  Reads the
@@ -1838,6 +2019,28 @@ extern "C" int32_t kv_erase_ranges(const kvb_cache* cache, const int32_t* ranges
   a.n_ranges = n_ranges;
   a.R = R;
   a.n_out = n_erased;
+  const int U = cache->B * cache->Hkv;
+  if (R <= kEraseMaxR && 2 * (size_t)R <= (size_t)L.Tc) {
+    // endpoint table in the (otherwise unused) tile-mask area; the largest kept
+    // count in the header
+    int32_t* ep = (int32_t*)((char*)ws + L.tile_mask);
+    int32_t* max_kept = (int32_t*)((char*)ws + kWsMaxKept);
+    if (R > 0) {
+      TraceScope tr(kTrEraseSearch, s);
+      hipLaunchKernelGGL(erase_search, dim3((2 * R + 3) / 4, U), dim3(256), 0, s, a, ep,
+                         max_kept);
+    } else {
+      TraceScope tr(kTrEraseSearch, s);
+      hipLaunchKernelGGL(erase_search, dim3(1, U), dim3(256), 0, s, a, ep, max_kept);
+    }
+    {
+      TraceScope tr(kTrErasePlan, s);
+      hipLaunchKernelGGL(erase_plan, dim3(kErasePlanBlocks, U), dim3(kChunkThreads), 0, s, a, ep,
+                         max_kept);
+    }
+    launch_move(cache, a, MODE_ERASE, s, max_kept, 4096);
+    return launch_status();
+  }
   launch_keep_chunks(cache, a, MODE_ERASE, s);
   launch_move(cache, a, MODE_ERASE, s);
   return launch_status();

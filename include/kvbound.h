@@ -95,11 +95,23 @@ typedef struct {
   int32_t* start;
 } kvb_cache;
 
+/* Violation bits written by kv_check_cache, per KV head. */
+enum {
+  KVB_CHECK_LEN = 1,               /* len < 0 or len > cap                                */
+  KVB_CHECK_START = 2,             /* start outside [0, cap)                              */
+  KVB_CHECK_POS_ORDER = 4,         /* live positions not strictly increasing along slots  */
+  KVB_CHECK_POS_AFTER_T = 8,       /* a live position above t[b] (negative distance)      */
+  KVB_CHECK_LOG_BETA_NAN = 16,     /* a live log beta is NaN                              */
+  KVB_CHECK_LOG_BETA_POSITIVE = 32,/* a live log beta above 0 (beta > 1)                  */
+  KVB_CHECK_RANGES = 64            /* the sequence's erase ranges: s >= e, unsorted or
+                                      overlapping, or n_ranges[b] outside [0, R]          */
+};
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kvb_strerror(int32_t status);
 
 /* Number of KV splits kv_attn_decode uses for num_splits == 0 (host only): about
- * 4096 / (B * Hkv), at least one, at most one per 256 slots of capacity. */
+ * 2048 / (B * Hkv), at least one, at most one per 256 slots of capacity. */
 int32_t kv_attn_decode_splits(const kvb_cache* cache, int32_t Hq);
 
 /* Workspace sizes in bytes (host only; no device access). */
@@ -187,6 +199,23 @@ int32_t kv_attn_decode_noalloc(const kvb_cache* cache, const void* q, int32_t Hq
                                const void* v_new, const float* log_beta_new,
                                int32_t num_splits, float* out, float* lse, int32_t* status,
                                void* stream);
+
+/*
+ * Device-side check of the preconditions the other calls take as given ([TRIM] 2.1:
+ * positions i <= t and retention scores beta in (0, 1]; [MEM] erase ranges as sorted
+ * disjoint half-open position intervals).  For every KV head u = (b, g), flags[u]
+ * receives the OR of the KVB_CHECK_* bits the head violates over its live slots
+ * (0: none).  A debugging aid: it reads each head's positions and
+ * log beta once, writes only flags, and allocates nothing.
+ *   t         [B] int32 decode positions, or NULL (no distance check)
+ *   ranges    [B][R][2] int32 and n_ranges [B] int32 (as for kv_erase_ranges), or
+ *             n_ranges NULL (no range check)
+ *   flags     [B][Hkv] int32 (device)
+ * Malformed values are only reported: every read stays inside the descriptor's
+ * arrays (len is clamped to [0, cap], start to 0 when out of range).
+ */
+int32_t kv_check_cache(const kvb_cache* cache, const int32_t* t, const int32_t* ranges,
+                       const int32_t* n_ranges, int32_t R, int32_t* flags, void* stream);
 
 /*
  * Append one token per KV head: the same append kv_attn_decode performs when

@@ -64,7 +64,7 @@ def test_workspace_sizes_host_only():
     P = L.kv_attn_decode_splits(ctypes.byref(c), 8)
     assert P == 1  # 100-slot cache: a split covers at least 256 slots
     assert L.kv_attn_decode_splits(ctypes.byref(_desc(cap=2080, B=32, Hkv=8)), 32) == 8
-    assert L.kv_attn_decode_splits(ctypes.byref(_desc(cap=32800, B=16, Hkv=8)), 32) == 32
+    assert L.kv_attn_decode_splits(ctypes.byref(_desc(cap=32800, B=16, Hkv=8)), 32) == 16
     assert L.kv_attn_decode_workspace(ctypes.byref(c), 8, 0) >= 256 + 2 * 8 * P * 130 * 4
     assert L.kv_evict_workspace(ctypes.byref(c), 10) > 256
     assert L.kv_erase_workspace(ctypes.byref(c)) >= L.kv_evict_workspace(ctypes.byref(c), 10)
@@ -339,3 +339,15 @@ def test_valid_calls_without_a_gpu_return_edevice():
     assert L.kv_evict_to_budget(ctypes.byref(good), P(8), 5, None, 0, None, ws, 1 << 30,
                                 None) == -5
     assert L.kv_append(ctypes.byref(good), P(8), P(8), None, P(8), ws, 256, None) == -5
+
+
+@needs_lib
+def test_check_cache_rejects_arguments_before_launch():
+    L = kvb.library()
+    P = ctypes.c_void_p
+    good = _desc()
+    assert L.kv_check_cache(None, None, None, None, 0, P(8), None) == -1
+    assert L.kv_check_cache(ctypes.byref(good), None, None, None, 0, None, None) == -1  # flags
+    assert L.kv_check_cache(ctypes.byref(good), None, None, None, -1, P(8), None) == -1
+    assert L.kv_check_cache(ctypes.byref(good), None, None, P(8), 3, P(8), None) == -1  # ranges
+    assert L.kv_check_cache(ctypes.byref(_desc(pos=None)), None, None, None, 0, P(8), None) == -1

@@ -165,21 +165,38 @@ def test_attention_scale_and_errors():
                            ws=torch.empty(300, dtype=torch.uint8, device="cuda"))
 
 
-def _sampled_full_size(w, units, splits_list, layer=0):
-    say("full-size", w.name, "units", units)
+def _oracle_unit(w, b, g, s, knh, vnh, lbh, qh):
+    """Oracle attention of KV head (b, g)'s query group over its cached tokens with the
+    decode token appended (as the call did), from the head's exact input bits."""
+    n = w.ctx
+    G = w.group
+    dd = {"k": np.concatenate([s["k"][:n], knh[b, g][None]])[None, None],
+          "v": np.concatenate([s["v"][:n], vnh[b, g][None]])[None, None],
+          "log_beta": None if s["log_beta"] is None else
+          np.append(s["log_beta"][:n], np.float32(lbh[b, g]))[None, None],
+          "pos": np.append(s["pos"][:n], np.int32(w.ctx))[None, None],
+          "len": np.array([[n + 1]], np.int32)}
+    qs = qh[b:b + 1, g * G:(g + 1) * G]
+    return oracle.decode_attention(values(dd["k"]), values(dd["v"]), dd["log_beta"], dd["pos"],
+                                   dd["len"], values(qs), np.array([w.ctx]))
+
+
+def _full_size(w, layer, units, splits_list):
+    """Decode attention over one full layer of the workload, with the decode token
+    appended by the first call (later calls attend over the same tokens with other
+    split counts); every listed KV head's query group against the oracle.  The
+    heads' inputs are read back after the calls: they write slot n (the decode
+    token) only, which the oracle reconstructs from k_new, v_new."""
+    say("full-size", w.name, "layer", layer, "units", len(units), "splits", splits_list)
     dc = synth.device_cache(w, layer)
     q, kn, vn, lbn = synth.device_queries(w, layer)
     t = torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda")
-    # read back the exact input bits of the sampled heads before any kernel runs
     G = w.group
-    sub = {}
-    for (b, g) in units:
-        sub[(b, g)] = {k: to_host(dc[k][b:b + 1, g:g + 1]) if dc[k] is not None else None
-                       for k in ("k", "v", "log_beta", "pos")}
     qh = to_host(q)
     knh, vnh = to_host(kn), to_host(vn)
     lbh = to_host(lbn) if lbn is not None else None
     c = kvb.KVCache.from_dict(dc)
+    outs = []
     for i, P in enumerate(splits_list):
         if i == 0:
             out, lse = kvb.kv_attn_decode(c, q, t, k_new=kn, v_new=vn, log_beta_new=lbn,
@@ -187,33 +204,36 @@ def _sampled_full_size(w, units, splits_list, layer=0):
         else:
             out, lse = kvb.kv_attn_decode(c, q, t, num_splits=P)
         torch.cuda.synchronize()
-        oh, lh = to_host(out), to_host(lse)
-        for (b, g), s in sub.items():
-            # append the decode token to the host copy, as the call did
-            n = w.ctx
-            dd = {"k": s["k"].copy(), "v": s["v"].copy(),
-                  "log_beta": None if s["log_beta"] is None else s["log_beta"].copy(),
-                  "pos": s["pos"].copy(), "len": np.array([[n + 1]], np.int32)}
-            dd["k"][0, 0, n] = knh[b, g]
-            dd["v"][0, 0, n] = vnh[b, g]
-            dd["pos"][0, 0, n] = w.ctx
-            if dd["log_beta"] is not None:
-                dd["log_beta"][0, 0, n] = lbh[b, g]
-            qs = qh[b:b + 1, g * G:(g + 1) * G]
-            ref_out, ref_lse = oracle.decode_attention(
-                values(dd["k"]), values(dd["v"]), dd["log_beta"], dd["pos"], dd["len"],
-                values(qs), np.array([w.ctx]))
-            check_attention(oh[b:b + 1, g * G:(g + 1) * G], lh[b:b + 1, g * G:(g + 1) * G],
-                            ref_out, ref_lse, f"{w.name} ({b},{g}) P={P}")
+        outs.append((P, to_host(out), to_host(lse)))
+    worst = 0.0
+    for j, (b, g) in enumerate(units):
+        s = {k: to_host(dc[k][b, g]) if dc[k] is not None else None
+             for k in ("k", "v", "log_beta", "pos")}
+        ref_out, ref_lse = _oracle_unit(w, b, g, s, knh, vnh, lbh, qh)
+        for P, oh, lh in outs:
+            worst = max(worst, check_attention(oh[b:b + 1, g * G:(g + 1) * G],
+                                               lh[b:b + 1, g * G:(g + 1) * G], ref_out, ref_lse,
+                                               f"{w.name} layer {layer} ({b},{g}) P={P}"))
+        if j % 32 == 31:
+            say("  checked", j + 1, "heads")
+    say("  worst relative error", worst)
     del dc, c
     torch.cuda.empty_cache()
 
 
 def test_attention_full_size_qwen3_8b_32k():
+    """Every KV head (all 128 query groups) of a 32K layer at the default split
+    count, and at 128 splits."""
     w = synth.WORKLOADS["qwen3_8b_32k"]
-    _sampled_full_size(w, [(0, 0), (7, 3), (15, 7)], [0, 128])
+    _full_size(w, 0, [(b, g) for b in range(w.batch) for g in range(w.hkv)], [0, 128])
 
 
 def test_attention_full_size_qwen3_32b_128k():
+    """Eight KV heads (64 query heads) of each of two 128K layers, at the default
+    split count and at 64, 128 and 256 splits."""
     w = synth.WORKLOADS["qwen3_32b_128k"]
-    _sampled_full_size(w, [(0, 0), (5, 6)], [64, 128, 256])
+    rng = np.random.default_rng(5)
+    for layer in (0, 37):
+        units = sorted(set((int(b), int(g)) for b, g in
+                           zip(rng.integers(0, w.batch, 40), rng.integers(0, w.hkv, 40))))[:8]
+        _full_size(w, layer, units, [0, 64, 128, 256])

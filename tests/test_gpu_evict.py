@@ -68,6 +68,30 @@ def test_evict_ties_and_special_keys():
         _evict_and_check(d, t, M, f"ties M={M}")
 
 
+def test_evict_one_float32_tie_cluster():
+    """One eviction (n = M + 1, the planner's reduction path) whose minimum sits in a
+    cluster of keys that round to the same float32 value but differ as doubles
+    (lb_i = fl32(c / d_i)); equal exact minima at two slots (the lower goes); every
+    key equal; -inf keys."""
+    B, H, n = 1, 4, 5000
+    d = _cache(7, B, H, n, n + 3, 128)
+    lb = d["log_beta"]
+    t = np.array([n + 5], np.int32)
+    dist = (t[0] - np.arange(n)).astype(np.float64)
+    cl = np.arange(1000, 3000)
+    lb[0, 0, :n] = np.float32(-0.5)                 # far from the cluster's keys
+    lb[0, 0, cl] = (-7.0 / dist[cl]).astype(np.float32)
+    keys = dist * lb[0, 0, :n].astype(np.float64)
+    assert len(np.unique(keys[cl].astype(np.float32))) < len(np.unique(keys[cl]))
+    lb[0, 1, :n] = np.float32(-0.25)
+    lb[0, 1, 1005] = np.float32(-5.0)                # d = 4000: key -20000
+    lb[0, 1, 3005] = np.float32(-10.0)               # d = 2000: key -20000 (exact tie)
+    lb[0, 2, :n] = np.float32(0.0)                   # all keys 0: the oldest goes
+    lb[0, 3, :n] = np.float32(-0.1)
+    lb[0, 3, [7, 4000, 4500]] = -np.inf              # the first -inf goes
+    _evict_and_check(d, t, n - 1, "one eviction")
+
+
 def test_evict_float32_tiny_workload_steps():
     """The tiny workload: 16 decode steps of append + attention + eviction."""
     w = synth.WORKLOADS["tiny"]
@@ -204,6 +228,71 @@ def test_erase_vs_oracle():
                                          [ranges[b, :nr[b]] for b in range(B)])
         check_layout(host_dict(c), ref, f"erase {trial}")
         assert np.array_equal(to_host(n_er), ref_n)
+
+
+def _erase_case(d, ranges, nr, what):
+    B = d["len"].shape[0]
+    c = dev_cache(d)
+    n_er = kvb.kv_erase_ranges(c, to_dev(ranges), to_dev(nr))
+    torch.cuda.synchronize()
+    ref, ref_n = oracle.erase_ranges(oracle.Cache.from_arrays(d),
+                                     [ranges[b, :nr[b]] for b in range(B)])
+    check_layout(host_dict(c), ref, what)
+    assert np.array_equal(to_host(n_er), ref_n), what
+
+
+def test_erase_edge_cases():
+    """Gapped positions (not equal to slots), ragged lengths per head, ranges that
+    cover nothing, everything or a single slot, a small shift (most kept rows move by
+    a few slots, so many sources lie in other groups' destinations), R = 0, and
+    n_ranges below R with junk in the unused entries."""
+    rng = np.random.default_rng(21)
+    B, H, n, cap = 2, 3, 6000, 6100
+    d = _cache(61, B, H, n, cap, 128, lens=[[6000, 17, 0], [1, 4321, 5999]])
+    gaps = np.cumsum(rng.integers(1, 4, size=(B, H, cap)), axis=2).astype(np.int32)
+    d["pos"] = gaps
+    R = 6
+    cases = {
+        "nothing": [[(-100, -50)], [(10 ** 8, 10 ** 8 + 5)]],
+        "everything": [[(0, 10 ** 8)], [(-5, 10 ** 8)]],
+        "single slots": [[(int(gaps[0, 0, 5]), int(gaps[0, 0, 5]) + 1),
+                          (int(gaps[0, 0, 100]), int(gaps[0, 0, 101]))],
+                         [(int(gaps[1, 1, 0]), int(gaps[1, 1, 0]) + 1)]],
+        "small shift": [[(0, int(gaps[0, 0, 7]))], [(int(gaps[1, 2, 3]), int(gaps[1, 2, 9]))]],
+        "empty ranges": [[(5, 5), (9, 9)], [(7, 7)]],
+        "many": [sorted_pairs(rng, 20000, 6), sorted_pairs(rng, 20000, 6)],
+    }
+    for name, per_b in cases.items():
+        ranges = np.full((B, R, 2), 123456, np.int32)      # junk past n_ranges
+        nr = np.zeros(B, np.int32)
+        for b in range(B):
+            for i, (s0, e0) in enumerate(per_b[b]):
+                ranges[b, i] = (s0, e0)
+            nr[b] = len(per_b[b])
+        say("erase edge case", name)
+        _erase_case(d, ranges, nr, name)
+    say("erase R = 0")
+    _erase_case(d, np.zeros((B, 0, 2), np.int32), np.zeros(B, np.int32), "R = 0")
+
+
+def sorted_pairs(rng, hi, k):
+    e = np.sort(rng.choice(hi, size=2 * k, replace=False))
+    return [(int(e[2 * i]), int(e[2 * i + 1])) for i in range(k)]
+
+
+def test_erase_many_ranges_chunked_path():
+    """More ranges than the endpoint tables hold for this capacity: the per-chunk
+    scan path."""
+    rng = np.random.default_rng(23)
+    B, H, n, cap = 2, 2, 3000, 3000
+    d = _cache(63, B, H, n, cap, 128)
+    R = 300
+    ranges = np.zeros((B, R, 2), np.int32)
+    nr = np.array([R, 170], np.int32)
+    for b in range(B):
+        ranges[b, :nr[b]] = np.array(sorted_pairs(rng, 3100, int(nr[b])), np.int32)
+    say("erase chunked path", R)
+    _erase_case(d, ranges, nr, "many ranges")
 
 
 def test_memento_full_size():
