@@ -1,8 +1,10 @@
 // One-wave candidate scan of the ASM cosine lookup ("Context Memorization for
 // Efficient Long Context Generation", method step 3; GQA: one codebook per KV
-// head), for kv_attn_decode_asm: a task is (64-centroid chunk, KV head, 64 query
-// rows); the wave scores its 64 x 64 cosines on MFMA and writes, per query row, the
-// best (score, lowest index) of the chunk.  Scores are q . c_k / |c_k| (|q| is
+// head), for kv_attn_decode_asm: a task is (128-centroid chunk, KV head, 64 query
+// rows); the wave scores its 128 x 64 cosines on MFMA, four 16-centroid tiles in
+// flight at a time, and writes, per query row, the best (score, lowest index) of
+// the chunk.  (64-centroid tasks took 53.6 us per split launch on the ASM
+// workload, 128-centroid ones 51.6 us, 256-centroid ones 51.9 us.)  Scores are q . c_k / |c_k| (|q| is
 // common to a query row, so it does not change the row's argmax).  The merge kernel
 // of the attention picks each row's best over the chunks (same rule).
 #pragma once
@@ -11,8 +13,8 @@
 
 namespace kvb {
 
-constexpr int kScanChunk = 64;  // centroids per task (four 16-column tiles)
-constexpr int kScanQB = 4;      // 16-query blocks per task
+constexpr int kScanChunk = 128;  // centroids per task (eight 16-column tiles, two rounds)
+constexpr int kScanQB = 4;       // 16-query blocks per task
 
 struct AsmScanArgs {
   const uint16_t* q;     // [B][Hq][D] bf16
@@ -53,15 +55,6 @@ __device__ __forceinline__ void asm_scan_wave(const AsmScanArgs& a, int task) {
   const uint16_t* cb = a.cent + (size_t)g * a.K * D;
   const int k0 = chunk * kScanChunk;
   const int k1 = min(k0 + kScanChunk, a.K);
-  // all four centroid tiles in flight at once; columns past the codebook read its
-  // last row and are never scored
-  u32x4 cv[4][KK];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int kr = min(k0 + 16 * it + lc, a.K - 1);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) cv[it][kk] = *(const u32x4*)(cb + (size_t)kr * D + 32 * kk + 8 * lg);
-  }
   float best[kScanQB][4];
   int bestk[kScanQB][4];
 #pragma unroll
@@ -71,10 +64,18 @@ __device__ __forceinline__ void asm_scan_wave(const AsmScanArgs& a, int task) {
       best[j][i] = kNegInf;
       bestk[j][i] = 0x7FFFFFFF;
     }
+  for (int t0 = 0; t0 < kScanChunk / 16; t0 += 4) {  // four centroid tiles per round
+  u32x4 cv[4][KK];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int kc = k0 + 16 * it + lc;  // this lane's centroid column
-    float n2 = 0.f;                    // |c|^2: 8 dims per lane per k-step, then 4 groups
+    const int kr = min(k0 + 16 * (t0 + it) + lc, a.K - 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) cv[it][kk] = *(const u32x4*)(cb + (size_t)kr * D + 32 * kk + 8 * lg);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int kc = k0 + 16 * (t0 + it) + lc;  // this lane's centroid column
+    float n2 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
@@ -104,6 +105,7 @@ __device__ __forceinline__ void asm_scan_wave(const AsmScanArgs& a, int task) {
         }
       }
     }
+  }
   }
   // over the 16 centroid columns (lanes with equal lg), then lane lc == 0 writes
 #pragma unroll

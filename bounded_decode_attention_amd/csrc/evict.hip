@@ -58,6 +58,10 @@ struct Ring {
   T* p;
   int capu, cap;
   __device__ __forceinline__ T& operator[](int i) const { return p[i < capu ? i : i - cap]; }
+  // the same element read with the non-temporal (streaming) hint: whole-head scans
+  __device__ __forceinline__ T ld(int i) const {
+    return __builtin_nontemporal_load(&p[i < capu ? i : i - cap]);
+  }
   __device__ __forceinline__ explicit operator bool() const { return p != nullptr; }
 };
 
@@ -177,7 +181,8 @@ struct SelArgs {
   int32_t* ls;           // [U][kSelCand] their slots
   UnitInfo* info;
   int32_t* n_out;
-  int32_t cap, Hkv, M;
+  int32_t* counts;       // [U][C] kept slots per kChunk-slot chunk (for keep_emit)
+  int32_t cap, Hkv, M, C;
 };
 
 // Keys of the slots base + e * NT + tid, e < kSelB: every load of the round is
@@ -191,8 +196,8 @@ __device__ __forceinline__ void sel_keys(const LB& lb, const PS& ps, int base, i
 #pragma unroll
   for (int e = 0; e < kSelB; ++e) {
     const int i = min(base + e * NT + (int)threadIdx.x, n - 1);
-    p[e] = ps[i];
-    b[e] = lb ? lb[i] : 0.f;
+    p[e] = ps.ld(i);
+    b[e] = lb ? lb.ld(i) : 0.f;
   }
 #pragma unroll
   for (int e = 0; e < kSelB; ++e) {
@@ -288,11 +293,22 @@ __global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
   const int u = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int n = min(a.len[u], a.cap);
   const int base0 = blockIdx.x * kSelSlice;
-  if (n <= a.M || base0 >= n) return;
+  static_assert(kSelSlice % kChunk == 0, "a slice covers whole keep_emit chunks");
+  constexpr int kCps = kSelSlice / kChunk;  // chunks per slice
+  if (n <= a.M) return;
+  if (base0 >= n) {  // no live slot: these chunks keep nothing
+    if (tid < kCps && base0 / kChunk + tid < a.C) a.counts[(size_t)u * a.C + base0 / kChunk + tid] = 0;
+    return;
+  }
   if (tid == 0) nloc = 0;
   __syncthreads();
   const SelPos sp = sel_replay<kSelNT>(a.hist + (size_t)u * 3 * 2048, 3, n, a.M, smem, out);
-  if (sp.cnt > kSelCand) return;
+  if (sp.cnt > kSelCand) return;  // sel_finish counts the kept slots itself
+  // slots whose key lies above the threshold's bucket are kept whatever the
+  // threshold inside it; sel_finish adds the bucket's kept members
+  int above[kCps];
+#pragma unroll
+  for (int c = 0; c < kCps; ++c) above[c] = 0;
   const int s0 = head_start(a.start, u);
   const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
                              a.cap - s0, a.cap};
@@ -304,7 +320,10 @@ __global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
 #pragma unroll
     for (int e = 0; e < kSelB; ++e) {
       const int i = base + e * kSelNT + tid;
-      const bool m = i < n && has_prefix(ord32(kk[e]), sp.prefix, sp.pbits);
+      const uint32_t k32 = ord32(kk[e]);
+      const bool m = i < n && has_prefix(k32, sp.prefix, sp.pbits);
+      if (i < n && sp.pbits > 0 && (k32 >> (32 - sp.pbits)) > sp.prefix)
+        ++above[(i - base0) / kChunk];
       const unsigned long long mask = __ballot(m);
       if (!mask) continue;
       int wb = 0;
@@ -318,6 +337,11 @@ __global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
         }
       }
     }
+  }
+#pragma unroll
+  for (int c = 0; c < kCps; ++c) {
+    const int tot = block_sum<kSelNT>(above[c], smem);
+    if (tid == 0 && base0 / kChunk + c < a.C) a.counts[(size_t)u * a.C + base0 / kChunk + c] = tot;
   }
   __syncthreads();
   const int nl = min(nloc, kSelCand);
@@ -419,6 +443,11 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
       sp2 = (sp2 << 10) | (uint32_t)bk;
     }
     sstar = (int)sp2;
+    // the bucket's kept members into their chunks' counts (sel_collect wrote the
+    // counts of the keys above the bucket)
+    for (int j = tid; j < nc; j += kSelThreads)
+      if (ck[j] > K || (ck[j] == K && cs[j] > sstar))
+        atomicAdd(&a.counts[(size_t)u * a.C + cs[j] / kChunk], 1);
   } else {
     // more than kSelCand keys share the float32 key t32: the exact key by radix
     // passes over the head (skipped when those keys are all equal), then the slot
@@ -498,6 +527,29 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
         }
         seen += tot_e;
       }
+    }
+    // kept slots per chunk (sel_collect did not count for this head), counted in
+    // LDS for windows of 2048 chunks and stored
+    uint32_t* cc = hist;
+    for (int cw = 0; cw < a.C; cw += 2048) {
+      for (int i = tid; i < 2048; i += kSelThreads) cc[i] = 0u;
+      __syncthreads();
+      const int lo = cw * kChunk, hi2 = min(n, (cw + 2048) * kChunk);
+      for (int base = lo; base < hi2; base += kSelThreads * kSelB) {
+        double kk[kSelB];
+        sel_keys<kSelThreads>(lb, ps, base, hi2, tpos, kk);
+#pragma unroll
+        for (int e = 0; e < kSelB; ++e) {
+          const int i = base + e * kSelThreads + tid;
+          if (i >= hi2) continue;
+          const unsigned long long k64 = ord64(kk[e]);
+          if (k64 > K || (k64 == K && i > sstar)) atomicAdd(&cc[i / kChunk - cw], 1u);
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < 2048 && cw + c < a.C; c += kSelThreads)
+        a.counts[(size_t)u * a.C + cw + c] = (int)cc[c];
+      __syncthreads();
     }
   }
   if (tid == 0) {
@@ -1043,8 +1095,8 @@ __device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       const int i = min(base + e * kChunkThreads + (int)threadIdx.x, n - 1);
-      p[e] = ps[i];
-      b[e] = lb ? lb[i] : 0.f;
+      p[e] = ps.ld(i);
+      b[e] = lb ? lb.ld(i) : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -1154,46 +1206,36 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
     }
   }
   __syncthreads();
-  // the staged rows to scratch (by destination): 16-byte pieces of K and V and the
-  // 8-byte row tails, a batch of loads per thread before any store
+  // the staged rows to scratch (by destination), one row per thread: all of a
+  // row's 16-byte pieces (K, V) and its tail in flight before any store
   const int ns = nstg;
-  const int ppr = a.row_bytes / 16, per = 2 * ppr + 1;
+  const int ppr = a.row_bytes / 16;
   const size_t ub = (size_t)u * a.cap;
-  constexpr int kB = 8;
-  for (int q0 = threadIdx.x; q0 < ns * per; q0 += kB * kChunkThreads) {
-    u32x4 x[kB];
-    unsigned char* to[kB];
-    bool tail[kB];
+  for (int en = threadIdx.x; en < ns; en += kChunkThreads) {
+    const int2 sd = stg[en];
+    const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
+    unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
+    const unsigned char* kr = (const unsigned char*)a.k + row * a.row_bytes;
+    const unsigned char* vr = (const unsigned char*)a.v + row * a.row_bytes;
+    for (int p0 = 0; p0 < ppr; p0 += 8) {
+      u32x4 xk[8], xv[8];
 #pragma unroll
-    for (int e = 0; e < kB; ++e) {
-      const int q = q0 + e * kChunkThreads;
-      to[e] = nullptr;
-      tail[e] = false;
-      if (q < ns * per) {
-        const int en = q / per, part = q - en * per;
-        const int2 sd = stg[en];
-        const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
-        unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
-        if (part < 2 * ppr) {
-          const bool isv = part >= ppr;
-          const int pc = isv ? part - ppr : part;
-          x[e] = *(const u32x4*)((const unsigned char*)(isv ? a.v : a.k) + row * a.row_bytes +
-                                 16 * pc);
-          to[e] = sp + (isv ? a.row_bytes : 0) + 16 * pc;
-        } else {
-          x[e] = u32x4{a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u, (uint32_t)a.pos[row],
-                       0u, 0u};
-          to[e] = sp + 2 * a.row_bytes;
-          tail[e] = true;
+      for (int q = 0; q < 8; ++q) {
+        if (p0 + q < ppr) {
+          xk[q] = *(const u32x4*)(kr + 16 * (p0 + q));
+          xv[q] = *(const u32x4*)(vr + 16 * (p0 + q));
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (p0 + q < ppr) {
+          *(u32x4*)(sp + 16 * (p0 + q)) = xk[q];
+          *(u32x4*)(sp + a.row_bytes + 16 * (p0 + q)) = xv[q];
         }
       }
     }
-#pragma unroll
-    for (int e = 0; e < kB; ++e) {
-      if (!to[e]) continue;
-      if (tail[e]) *(uint2*)to[e] = make_uint2(x[e][0], x[e][1]);
-      else *(u32x4*)to[e] = x[e];
-    }
+    *(uint2*)(sp + 2 * a.row_bytes) =
+        make_uint2(a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u, (uint32_t)a.pos[row]);
   }
 }
 
@@ -1712,8 +1754,7 @@ static void launch_keep_chunks(const kvb_cache* c, const KeepArgs& a, int mode, 
   const int U = c->B * c->Hkv;
   dim3 grid(a.C, U);
   if (mode == MODE_EVICT) {
-    { TraceScope tr(kTrKeepCount, s);
-      hipLaunchKernelGGL(keep_count<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a); }
+    // the chunk counts come from the selection (sel_collect, sel_finish)
     { TraceScope tr(kTrKeepEmit, s);
       hipLaunchKernelGGL(keep_emit<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a); }
   } else {
@@ -1797,6 +1838,8 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     sa.ls = (int32_t*)(w + L.sel_ls);
     sa.info = a.info;
     sa.n_out = n_evicted;
+    sa.counts = a.counts;
+    sa.C = a.C;
     sa.cap = cache->cap;
     sa.Hkv = cache->Hkv;
     sa.M = M;
