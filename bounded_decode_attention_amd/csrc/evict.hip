@@ -283,12 +283,15 @@ __global__ __launch_bounds__(kSelNT) void sel_hist(SelArgs a, int pass) {
 
 // Lists the members of the final bucket (exact key, slot) from one slice: first
 // in LDS, then one global reservation per workgroup (a per-head counter taking
-// every wave's reservation serialises at one address).
+// every wave's reservation serialises at one address).  The LDS list holds
+// kCollectLds members (a slice usually has a few hundred); members past it take a
+// global reservation per wave, so the small list keeps occupancy high.
+constexpr int kCollectLds = 1024;
 __global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
   __shared__ int smem[kSelNT / 64];
   __shared__ int out[4];
-  __shared__ unsigned long long ck[kSelCand];
-  __shared__ int cs[kSelCand];
+  __shared__ unsigned long long ck[kCollectLds];
+  __shared__ int cs[kCollectLds];
   __shared__ int nloc, gbase;
   const int u = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int n = min(a.len[u], a.cap);
@@ -329,11 +332,26 @@ __global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
       int wb = 0;
       if (lane == 0) wb = atomicAdd(&nloc, __popcll(mask));
       wb = __shfl(wb, 0, 64);
+      // members whose LDS position lies past the list go straight to the head's
+      // list (a reservation per wave); the LDS positions below kCollectLds are all
+      // written, so the flush below copies min(nloc, kCollectLds) valid entries
+      const int pc = __popcll(mask);
+      const int over = max(0, wb + pc - kCollectLds);
+      int gb = 0;
+      if (over > 0 && lane == 0) gb = atomicAdd(&a.nlist[u], min(over, pc));
+      gb = __shfl(gb, 0, 64);
       if (m) {
-        const int j = wb + __popcll(mask & ((1ull << lane) - 1ull));
-        if (j < kSelCand) {  // always: at most cnt members match
+        const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+        const int j = wb + rank;
+        if (j < kCollectLds) {
           ck[j] = ord64(kk[e]);
           cs[j] = i;
+        } else {
+          const int g = gb + (j - max(wb, kCollectLds));
+          if (g < kSelCand) {  // always: exactly cnt members over all slices
+            a.lk[(size_t)u * kSelCand + g] = ord64(kk[e]);
+            a.ls[(size_t)u * kSelCand + g] = i;
+          }
         }
       }
     }
@@ -344,7 +362,7 @@ __global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
     if (tid == 0 && base0 / kChunk + c < a.C) a.counts[(size_t)u * a.C + base0 / kChunk + c] = tot;
   }
   __syncthreads();
-  const int nl = min(nloc, kSelCand);
+  const int nl = min(nloc, kCollectLds);
   if (nl == 0) return;
   if (tid == 0) gbase = atomicAdd(&a.nlist[u], nl);
   __syncthreads();
@@ -574,6 +592,8 @@ __device__ __forceinline__ bool staged_row(int os, int ns, int src, int j, int k
   if (ns <= os) return sa >= g0 + mr && sa < ns + kept;
   return sa < g0 && sa >= ns;
 }
+
+
 
 // ---------------------------------------------------------------- fused LDS planner
 // One 1024-thread workgroup per head, for heads whose float32-rounded keys fit in
@@ -1063,6 +1083,48 @@ struct KeepArgs {
   int32_t cap, Hkv, R, C, Mk, max_evict, row_bytes, srow, move_rows;
 };
 
+// Copies the ns staged rows listed in stg (source slot, destination row) of head u
+// to scratch with the whole workgroup: consecutive threads take consecutive
+// 16-byte pieces of a row, so a load instruction covers whole lines of a few rows
+// (a thread per row touches 64 rows per instruction); each thread's batch of
+// pieces is loaded before any of it is stored.
+template <int NT>
+__device__ __forceinline__ void stage_list_rows(const KeepArgs& a, int u, int s0,
+                                                const int2* stg, int ns) {
+  const int ppr = a.row_bytes / 16;   // pieces per tensor row
+  const int per = 2 * ppr;            // K then V
+  const size_t ub = (size_t)u * a.cap;
+  constexpr int kB = 16;
+  for (int q0 = threadIdx.x; q0 < ns * per; q0 += kB * NT) {
+    u32x4 x[kB];
+    unsigned char* to[kB];
+#pragma unroll
+    for (int e = 0; e < kB; ++e) {
+      const int q = q0 + e * NT;
+      to[e] = nullptr;
+      if (q < ns * per) {
+        const int en = q / per, part = q - en * per;
+        const int2 sd = stg[en];
+        const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
+        const bool isv = part >= ppr;
+        const int pc = isv ? part - ppr : part;
+        x[e] = *(const u32x4*)((const unsigned char*)(isv ? a.v : a.k) + row * a.row_bytes + 16 * pc);
+        to[e] = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow + (isv ? a.row_bytes : 0) + 16 * pc;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kB; ++e)
+      if (to[e]) *(u32x4*)to[e] = x[e];
+  }
+  for (int en = threadIdx.x; en < ns; en += NT) {  // the 8-byte tails
+    const int2 sd = stg[en];
+    const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
+    const uint32_t l = a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u;
+    const uint32_t p = (uint32_t)a.pos[row];
+    *(uint2*)(a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow + 2 * a.row_bytes) = make_uint2(l, p);
+  }
+}
+
 // Index of the first range whose end lies above p (nr if none); the ranges are
 // sorted and disjoint.
 __device__ __forceinline__ int first_range_ending_after(const int32_t* rg, int nr, int p) {
@@ -1206,37 +1268,8 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
     }
   }
   __syncthreads();
-  // the staged rows to scratch (by destination), one row per thread: all of a
-  // row's 16-byte pieces (K, V) and its tail in flight before any store
-  const int ns = nstg;
-  const int ppr = a.row_bytes / 16;
-  const size_t ub = (size_t)u * a.cap;
-  for (int en = threadIdx.x; en < ns; en += kChunkThreads) {
-    const int2 sd = stg[en];
-    const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
-    unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
-    const unsigned char* kr = (const unsigned char*)a.k + row * a.row_bytes;
-    const unsigned char* vr = (const unsigned char*)a.v + row * a.row_bytes;
-    for (int p0 = 0; p0 < ppr; p0 += 8) {
-      u32x4 xk[8], xv[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (p0 + q < ppr) {
-          xk[q] = *(const u32x4*)(kr + 16 * (p0 + q));
-          xv[q] = *(const u32x4*)(vr + 16 * (p0 + q));
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (p0 + q < ppr) {
-          *(u32x4*)(sp + 16 * (p0 + q)) = xk[q];
-          *(u32x4*)(sp + a.row_bytes + 16 * (p0 + q)) = xv[q];
-        }
-      }
-    }
-    *(uint2*)(sp + 2 * a.row_bytes) =
-        make_uint2(a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u, (uint32_t)a.pos[row]);
-  }
+  // the staged rows to scratch (by destination)
+  stage_list_rows<kChunkThreads>(a, u, s0, stg, nstg);
 }
 
 // ---------------------------------------------------------------- erase by range endpoints
@@ -1329,8 +1362,6 @@ __global__ __launch_bounds__(kChunkThreads) void erase_plan(KeepArgs a, const in
   }
   __syncthreads();
   const int jmax = min(kept, a.Mk);
-  const int ppr = a.row_bytes / 16;
-  const size_t ub = (size_t)u * a.cap;
   for (int j0 = blockIdx.x * kChunkThreads; j0 < jmax; j0 += gridDim.x * kChunkThreads) {
     if (tid == 0) nstg = 0;
     __syncthreads();
@@ -1348,36 +1379,8 @@ __global__ __launch_bounds__(kChunkThreads) void erase_plan(KeepArgs a, const in
       if (staged_row(s0, s0, src, j, kept, a.move_rows)) stg[atomicAdd(&nstg, 1)] = make_int2(src, j);
     }
     __syncthreads();
-    // this block's staged rows to scratch (by destination), one row per thread: all
-    // of a row's 16-byte pieces (K, V) and its tail are loaded before any store, so
-    // the copy costs one memory round trip (latency, not bytes, bounds it)
-    const int ns = nstg;
-    if (tid < ns) {
-      const int2 sd = stg[tid];
-      const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
-      unsigned char* sp = a.scratch + ((size_t)u * a.Mk + sd.y) * a.srow;
-      const unsigned char* kr = (const unsigned char*)a.k + row * a.row_bytes;
-      const unsigned char* vr = (const unsigned char*)a.v + row * a.row_bytes;
-      for (int p0 = 0; p0 < ppr; p0 += 8) {  // 8 pieces of K and 8 of V per batch
-        u32x4 xk[8], xv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (p0 + q < ppr) {
-            xk[q] = *(const u32x4*)(kr + 16 * (p0 + q));
-            xv[q] = *(const u32x4*)(vr + 16 * (p0 + q));
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (p0 + q < ppr) {
-            *(u32x4*)(sp + 16 * (p0 + q)) = xk[q];
-            *(u32x4*)(sp + a.row_bytes + 16 * (p0 + q)) = xv[q];
-          }
-        }
-      }
-      *(uint2*)(sp + 2 * a.row_bytes) =
-          make_uint2(a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u, (uint32_t)a.pos[row]);
-    }
+    // this block's staged rows to scratch (by destination)
+    stage_list_rows<kChunkThreads>(a, u, s0, stg, nstg);
     __syncthreads();
   }
 }
@@ -1677,8 +1680,9 @@ static size_t plan_lds_limit() {
       if (hipFuncGetAttributes(&fa, (const void*)evict_plan_lds) == hipSuccess)
         static_lds = fa.sharedSizeBytes;
       limit = (size_t)v > static_lds + 256 ? (size_t)v - static_lds - 256 : 1;
-      hipFuncSetAttribute((const void*)evict_plan_lds,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit);
+      if (hipFuncSetAttribute((const void*)evict_plan_lds,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
+        limit = 1;
     } else {
       limit = 1;
     }

@@ -166,6 +166,26 @@ def test_evict_ties_and_special_keys_large_heads():
         _evict_and_check(d, t, M, f"large ties M={M}", max_evict=64)
 
 
+def test_evict_large_head_bucket_in_one_slice():
+    """Chunked selection where the threshold's bucket (3000 keys sharing their top
+    11 bits, all in one 8192-slot slice) holds more members than a slice lists in
+    LDS, so part of the list goes to the head's list directly; the threshold sits
+    inside the bucket."""
+    B, H, n = 1, 2, 40000
+    d = _cache(9, B, H, n, n + 3, 128)
+    lb = d["log_beta"]
+    t = np.array([n], np.int32)
+    dist = (t[0] - np.arange(n)).astype(np.float64)
+    lb[0, :, :n] = np.float32(-1e-4)
+    cl = np.arange(10000, 13000)
+    for g in range(H):
+        lb[0, g, cl] = (-1000.0 * (1.0 + 1e-4 * ((cl * (7 + g)) % 97)) / dist[cl]).astype(np.float32)
+    keys = dist[cl] * lb[0, 0, cl].astype(np.float64)
+    assert np.all(np.abs(keys) > 999) and np.all(np.abs(keys) < 1011)
+    for M in (n - 1500, n - 2999, n - 1):
+        _evict_and_check(d, t, M, f"bucket in one slice M={M}", max_evict=64)
+
+
 def test_evict_float32_and_d64():
     for dtype, D in (("f32", 64), ("bf16", 64), ("f32", 128)):
         d = _cache(31, 1, 2, 3000, 3001, D, dtype=dtype)
