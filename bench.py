@@ -692,7 +692,8 @@ def memento_bench(args):
     memento): erase every completed block (range compaction), append the decode
     token and attend with beta == 1 over the kept tokens, evict to M = 65536 (a
     no-op).  Each trial restores the overwritten slots and the lengths first
-    (untimed); the median over the trials is reported with min and max."""
+    (untimed); the median over the trials is reported with min and max.  The calls
+    are queued behind a GPU spin, so the times are device times."""
     import numpy as np
     import torch
 
@@ -731,6 +732,9 @@ def memento_bench(args):
     def trial():
         restore()
         torch.cuda.synchronize()
+        # keep the GPU busy while the three calls are queued, so that the events
+        # time the device work and not the host's launch latency
+        torch.cuda._sleep(2_000_000)
         ev[0].record()
         kvb.kv_erase_ranges(c, rg, nr, n_erased=n_er, ws=ws_er)
         ev[1].record()

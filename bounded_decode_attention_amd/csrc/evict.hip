@@ -1315,17 +1315,21 @@ __global__ __launch_bounds__(256) void erase_search(KeepArgs a, int32_t* ep, int
 // Grid (kErasePlanBlocks, heads).  Kept run k is [a_k, b_k) with a_0 = 0,
 // a_k = lb(e_{k-1}), b_k = lb(s_k), b_nr = n; its rows go to slots d_k .. d_k +
 // (b_k - a_k) - 1, d_k the exclusive prefix of the run lengths.  Each workgroup
-// builds the (small) run table in LDS once, then takes destination blocks of one
-// row per thread, strided over the grid: writes keep_src and copies to scratch the
-// rows compact_move must not read in place (staged_row), as keep_emit does.
+// builds the (small) run table in LDS once, then writes keep_src for destination
+// blocks of one row per thread, strided over the grid.  The rows compact_move must
+// not read in place (staged_row) are those whose source lies below the kept count,
+// so they belong to the runs starting there and sit at the first destinations; a
+// second pass copies them to scratch in 16-row slices strided over the grid, so
+// that the copying is spread over every workgroup of the head instead of falling
+// on the first few.
 constexpr int kErasePlanBlocks = 64;
+constexpr int kEraseSlice = 16;  // staged rows per slice in the copy pass
 __global__ __launch_bounds__(kChunkThreads) void erase_plan(KeepArgs a, const int32_t* ep,
                                                             int32_t* max_kept) {
   __shared__ int s_a[kEraseMaxR + 1];
   __shared__ int s_d[kEraseMaxR + 1];
   __shared__ int smem[kChunkThreads / 64];
-  __shared__ int2 stg[kChunkThreads];
-  __shared__ int nstg;
+  __shared__ int s_stage_end;
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
   const int tid = threadIdx.x;
@@ -1333,6 +1337,7 @@ __global__ __launch_bounds__(kChunkThreads) void erase_plan(KeepArgs a, const in
   const int n = min(a.len[u], a.cap);
   const int s0 = head_start(a.start, u);
   const int32_t* e = ep + (size_t)u * 2 * a.R;
+  if (tid == 0) s_stage_end = 0;
   int carry = 0;
   for (int k0 = 0; k0 <= nr; k0 += kChunkThreads) {
     const int k = k0 + tid;
@@ -1349,6 +1354,15 @@ __global__ __launch_bounds__(kChunkThreads) void erase_plan(KeepArgs a, const in
     carry += tot;
   }
   const int kept = min(carry, n);
+  __syncthreads();
+  // one past the last destination whose row may be staged: over the runs that
+  // move, the end of each one's rows with sources below the kept count (does not
+  // assume the runs are ordered)
+  for (int k = tid; k <= nr; k += kChunkThreads) {
+    const int len = (k < nr ? s_d[k + 1] : carry) - s_d[k];
+    if (len > 0 && s_a[k] < kept && s_a[k] != s_d[k])
+      atomicMax(&s_stage_end, s_d[k] + min(len, kept - s_a[k]));
+  }
   if (blockIdx.x == 0 && tid == 0) {
     UnitInfo inf = a.info[u];
     inf.mode = MODE_ERASE;
@@ -1362,26 +1376,55 @@ __global__ __launch_bounds__(kChunkThreads) void erase_plan(KeepArgs a, const in
   }
   __syncthreads();
   const int jmax = min(kept, a.Mk);
-  for (int j0 = blockIdx.x * kChunkThreads; j0 < jmax; j0 += gridDim.x * kChunkThreads) {
-    if (tid == 0) nstg = 0;
-    __syncthreads();
-    const int j = j0 + tid;
-    if (j < jmax) {
-      // the last run starting at or below j (runs of length 0 share their start)
-      int lo = 0, hi = nr;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_d[mid] <= j) lo = mid;
-        else hi = mid - 1;
-      }
-      const int src = s_a[lo] + (j - s_d[lo]);
-      a.keep_src[(size_t)u * a.Mk + j] = src;
-      if (staged_row(s0, s0, src, j, kept, a.move_rows)) stg[atomicAdd(&nstg, 1)] = make_int2(src, j);
+  // the last run starting at or below destination j (runs of length 0 share
+  // their start with the next one)
+  auto source_of = [&](int j) {
+    int lo = 0, hi = nr;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_d[mid] <= j) lo = mid;
+      else hi = mid - 1;
     }
-    __syncthreads();
-    // this block's staged rows to scratch (by destination)
-    stage_list_rows<kChunkThreads>(a, u, s0, stg, nstg);
-    __syncthreads();
+    return s_a[lo] + (j - s_d[lo]);
+  };
+  for (int j = blockIdx.x * kChunkThreads + tid; j < jmax; j += gridDim.x * kChunkThreads)
+    a.keep_src[(size_t)u * a.Mk + j] = source_of(j);
+
+  // copy pass: kChunkThreads / kEraseSlice threads per row, 16-byte pieces of K
+  // then V; every thread loads its pieces before storing them
+  constexpr int kTpr = kChunkThreads / kEraseSlice;
+  const int send = min(s_stage_end, jmax);
+  const int ppr = a.row_bytes / 16, per = 2 * ppr;
+  const size_t ub = (size_t)u * a.cap;
+  const int sub = tid % kTpr;
+  for (int z0 = blockIdx.x * kEraseSlice; z0 < send; z0 += gridDim.x * kEraseSlice) {
+    const int j = z0 + tid / kTpr;
+    if (j >= send) continue;
+    const int src = source_of(j);
+    if (!staged_row(s0, s0, src, j, kept, a.move_rows)) continue;
+    const size_t row = ub + (s0 + src < a.cap ? s0 + src : s0 + src - a.cap);
+    unsigned char* sp = a.scratch + ((size_t)u * a.Mk + j) * a.srow;
+    for (int p0 = sub; p0 < per; p0 += 4 * kTpr) {
+      u32x4 x[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pc = p0 + t * kTpr;
+        if (pc < per) {
+          const bool isv = pc >= ppr;
+          x[t] = *(const u32x4*)((const unsigned char*)(isv ? a.v : a.k) + row * a.row_bytes +
+                                 16 * (isv ? pc - ppr : pc));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pc = p0 + t * kTpr;
+        if (pc < per) *(u32x4*)(sp + 16 * pc) = x[t];  // K then V, as in the cache
+      }
+    }
+    if (sub == 0) {
+      const uint32_t l = a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u;
+      *(uint2*)(sp + 2 * a.row_bytes) = make_uint2(l, (uint32_t)a.pos[row]);
+    }
   }
 }
 
