@@ -10,15 +10,16 @@
 // every slot whose position lies in one of the sequence's half-open ranges.
 //
 // Kernels
-//   sel_init, sel_hist, sel_collect, sel_finish
+//   sel_init, sel_hist0, sel_refine x2, sel_finish
 //                  (heads too long for the LDS planner) find the threshold element
 //                  (kappa*, slot*) -- the (n-M)-th in (kappa, slot) order -- by radix
 //                  passes on the float32-rounded key (a monotone map of kappa), many
 //                  workgroups per head, until the bucket holding it has at most 4096
-//                  members, which are listed (exact 64-bit key, slot) and the
-//                  selection finished in LDS; if more than 4096 share one float32
-//                  key, exact passes on the 64-bit key and a slot pass over the head.
-//   keep_count     per 4096-slot chunk: number of kept slots.
+//                  members, whose slots are listed and the selection finished in
+//                  LDS on their exact keys; if more than 4096 share the 22-bit
+//                  bucket, exact passes on the 64-bit key and a slot pass over the
+//                  head.  The result: a keep bit per slot, kept slots per chunk.
+//   keep_count     (erase) per 4096-slot chunk: number of kept slots.
 //   keep_emit      per chunk: exclusive scan -> destination slot of every kept
 //                  row (keep_src[dst] = src); evicted positions; rows whose source
 //                  would be overwritten by another workgroup's writes are copied
@@ -80,10 +81,52 @@ __device__ __forceinline__ uint64_t ord64(double k) {
   if ((b << 1) == 0) b = 0;
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
-__device__ __forceinline__ uint32_t ord32(double k) {
-  uint32_t b = __float_as_uint((float)k);  // round to nearest: monotone in k
+__device__ __forceinline__ uint32_t ord32f(float k) {
+  uint32_t b = __float_as_uint(k);
   if ((b << 1) == 0) b = 0;
   return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t ord32(double k) {
+  return ord32f((float)k);  // round to nearest: monotone in k
+}
+// Inverse of ord64 (up to the sign of zero).
+__device__ __forceinline__ double unord64(uint64_t o) {
+  const uint64_t b = (o >> 63) ? (o & 0x7fffffffffffffffull) : ~o;
+  return __longlong_as_double((long long)b);
+}
+
+// The retention key d * log beta (d = t - pos) and its float32 rounding.  The
+// exact key is the double product (exact while |d| < 2^29).  For |d| <= 2^24, d is
+// exact in float32 and one float32 multiply rounds the exact product once, which
+// is what rounding the double product to float32 does; so the float32 key, which all
+// the radix passes look at, costs one float multiply.  No log beta (lb null):
+// every key is 0.
+template <typename LB>
+__device__ __forceinline__ double key_f64(const LB& lb, int d, float b) {
+  return (!lb || d == 0) ? 0.0 : (double)d * (double)b;
+}
+template <typename LB>
+__device__ __forceinline__ uint32_t key_ord32(const LB& lb, int d, float b) {
+  if (!lb || d == 0) return 0x80000000u;  // ord32f(0)
+  if (d <= (1 << 24) && d >= -(1 << 24)) return ord32f((float)d * b);
+  return ord32((double)d * (double)b);
+}
+// key_ord32 of a thread's N slots: the float multiply for all, then (only in a
+// wave holding one) the distances beyond 2^24 from the double product.
+template <int N, typename LB>
+__device__ __forceinline__ void keys_ord32(const LB& lb, const int* d, const float* b,
+                                           uint32_t* k) {
+  bool far = false;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    k[e] = (!lb || d[e] == 0) ? 0x80000000u : ord32f((float)d[e] * b[e]);
+    far |= d[e] > (1 << 24) || d[e] < -(1 << 24);
+  }
+  if (__ballot(far) != 0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (d[e] > (1 << 24) || d[e] < -(1 << 24)) k[e] = key_ord32(lb, d[e], b[e]);
+  }
 }
 
 // ---------------------------------------------------------------- block helpers
@@ -150,24 +193,55 @@ __device__ __forceinline__ int select_bucket(const uint32_t* hist, int nb, int& 
   return bucket;
 }
 
+// The blocks of bsz slots of an n-slot head that workgroup x takes: block x, and
+// (with fold) the last workgroup with work also takes the head's last block when
+// that one is short (at most bsz / 4 slots), so that a head a few slots past a
+// multiple of bsz does not need one more workgroup, which would wait for a free
+// slot on the chip when the grid exceeds what the chip holds at once.  (The
+// selection kernels fit a 128K-slot layer at once, where the folded workgroup's
+// second pass costs more than it saves.)  Returns (first, last); last < first: no
+// work.
+__device__ __forceinline__ int2 wg_blocks(int x, int n, int bsz, bool fold_short = true) {
+  const int nb = (n + bsz - 1) / bsz;
+  const bool fold = fold_short && nb >= 2 && n - (nb - 1) * bsz <= bsz / 4;
+  const int lastwg = fold ? nb - 2 : nb - 1;
+  if (x > lastwg) return make_int2(0, -1);
+  return make_int2(x, x == lastwg ? nb - 1 : x);
+}
+
 // ---------------------------------------------------------------- select
 // Chunked selection for heads too long for the LDS planner.  Several workgroups
-// per head: histogram passes over slices of the head (radix on the float32-rounded
-// key, 11 + 11 + 10 bits) added into per-head global histograms, one launch per
-// pass; every workgroup of a later launch replays the earlier passes' bucket
-// choices from those histograms (deterministic), so no launch in between is
-// needed.  (Letting the last workgroup of a pass record the choice instead needs
-// a device-wide release fence in every workgroup, which writes back the L2 of its
-// XCD and made the pass several times slower.)  The passes stop once the bucket
-// holding the threshold has at most kSelCand members; these are listed (exact
-// key, slot) and one workgroup per head finishes the selection in LDS.  If more
-// share one float32 key, that workgroup runs exact passes over the whole head
-// instead.
+// per head (slices of kSelSlice slots): a histogram pass of the top 11 bits of
+// the float32-rounded key (sel_hist0) added into a per-head global histogram;
+// then two refine launches.  Each refine workgroup loads its slice's keys, replays
+// the earlier passes' bucket choices from the global histograms while the loads
+// are in flight (deterministic, so no launch in between is needed), and either
+// lists the slots of the bucket holding the threshold once it has at most
+// kSelCand members (recording the level in the head's SelHead, and marking the
+// slots above the bucket in the head's keep bits), or adds the next 11-bit
+// histogram pass.  A refine launch after the listing one reads that record and
+// exits.  (Letting the last workgroup of a pass record the choice instead needs a
+// device-wide release fence in every workgroup, which writes back the L2 of its
+// XCD and made the pass several times slower.)  One workgroup per head then
+// finishes the selection from the list in LDS and marks the bucket's kept
+// members; if more than kSelCand keys share the 22-bit bucket, that workgroup
+// runs exact passes over the whole head instead.
 constexpr int kSelB = 16;       // slots per thread per round
 constexpr int kSelCand = 4096;  // bucket size finished from a list
 constexpr int kSelNT = 256;     // threads of the slice kernels
 constexpr int kSelRounds = 2;   // rounds per slice workgroup
+constexpr int kSelRefines = 2;  // refine launches (histogram passes of 11 + 11 bits)
+constexpr int kSelHistWords = kSelRefines * 2048;  // per head: pass p's bins at p * 2048
 constexpr int kSelSlice = kSelRounds * kSelNT * kSelB;  // slots per slice workgroup
+static_assert(kSelNT * kSelB == kChunk, "a round covers one keep_emit chunk");
+
+struct SelHead {      // per head
+  int32_t nlist;      // members listed
+  int32_t level;      // the refine launch that listed them (0: not listed)
+  uint32_t prefix;    // the bucket listed: its top pbits bits of the float32 key
+  int32_t pbits, r, cnt;  // rank of the threshold inside it, its size
+  int32_t pad[2];
+};
 
 struct SelArgs {
   const float* log_beta;
@@ -175,35 +249,30 @@ struct SelArgs {
   const int32_t* len;
   const int32_t* start;
   const int32_t* tq;
-  uint32_t* hist;        // [U][3][2048]
-  int32_t* nlist;        // [U]
-  unsigned long long* lk;  // [U][kSelCand] listed exact keys
-  int32_t* ls;           // [U][kSelCand] their slots
+  uint32_t* hist;        // [U][kSelRefines][2048]
+  SelHead* head;         // [U]
+  int32_t* ls;           // [U][kSelCand] the listed slots
   UnitInfo* info;
   int32_t* n_out;
   int32_t* counts;       // [U][C] kept slots per kChunk-slot chunk (for keep_emit)
-  int32_t cap, Hkv, M, C;
+  uint32_t* keepbits;    // [U][W] bit i % 32 of word i / 32: slot i is kept
+  int32_t cap, Hkv, M, C, W;
 };
 
-// Keys of the slots base + e * NT + tid, e < kSelB: every load of the round is
-// issued before the first key is formed.  Slots past n get key 0 (callers skip
-// them).
+// Distances d = t - pos and log betas of the slots base + e * NT + tid, e < kSelB:
+// every load of the round is issued before any is used.  Slots past n repeat slot
+// n - 1 (callers skip them).
 template <int NT, typename LB, typename PS>
-__device__ __forceinline__ void sel_keys(const LB& lb, const PS& ps, int base, int n, int tpos,
-                                         double* k) {
-  int p[kSelB];
-  float b[kSelB];
+__device__ __forceinline__ void sel_load(const LB& lb, const PS& ps, int base, int n, int tpos,
+                                         int* d, float* b) {
 #pragma unroll
   for (int e = 0; e < kSelB; ++e) {
     const int i = min(base + e * NT + (int)threadIdx.x, n - 1);
-    p[e] = ps.ld(i);
+    d[e] = ps.ld(i);
     b[e] = lb ? lb.ld(i) : 0.f;
   }
 #pragma unroll
-  for (int e = 0; e < kSelB; ++e) {
-    const int d = tpos - p[e];
-    k[e] = (!lb || d == 0) ? 0.0 : (double)d * (double)b[e];  // = retention_key
-  }
+  for (int e = 0; e < kSelB; ++e) d[e] = tpos - d[e];
 }
 
 // Whether float32-ordered key k32 starts with the pbits-bit prefix.
@@ -216,6 +285,10 @@ struct SelPos {
   int pbits;
   int r;    // 1-based rank of the threshold among the keys with that prefix
   int cnt;  // keys with that prefix
+  // the prefix as a mask and value over the whole key: k32 has the prefix iff
+  // (k32 & pmask) == pval, and lies in a higher bucket iff (k32 & pmask) > pval
+  __device__ __forceinline__ uint32_t pmask() const { return pbits == 0 ? 0u : ~0u << (32 - pbits); }
+  __device__ __forceinline__ uint32_t pval() const { return pbits == 0 ? 0u : prefix << (32 - pbits); }
 };
 
 // The bucket choices of passes 0 .. upto-1, from the head's histograms (whole
@@ -234,146 +307,231 @@ __device__ SelPos sel_replay(const uint32_t* gh, int upto, int n, int M, int* sm
   return sp;
 }
 
-// Clears the head's histograms and list counter.
+// Clears the head's histograms, record and chunk counts.
 __global__ __launch_bounds__(kSelNT) void sel_init(SelArgs a) {
   const int u = blockIdx.x;
-  for (int i = threadIdx.x; i < 3 * 2048; i += kSelNT) a.hist[(size_t)u * 3 * 2048 + i] = 0u;
-  if (threadIdx.x == 0) a.nlist[u] = 0;
+  for (int i = threadIdx.x; i < kSelHistWords; i += kSelNT) a.hist[(size_t)u * kSelHistWords + i] = 0u;
+  for (int i = threadIdx.x; i < a.C; i += kSelNT) a.counts[(size_t)u * a.C + i] = 0;
+  if (threadIdx.x < (int)(sizeof(SelHead) / 4)) ((int32_t*)(a.head + u))[threadIdx.x] = 0;
 }
 
-// Histogram pass `pass` over one slice of one head.  (Four copies of every bin,
-// to spread a wave's same-bin atomics, made the pass slower: the larger LDS
-// footprint costs more occupancy than the conflicts it saves.)
-__global__ __launch_bounds__(kSelNT) void sel_hist(SelArgs a, int pass) {
-  __shared__ uint32_t h[2048];
-  __shared__ int smem[kSelNT / 64];
-  __shared__ int out[4];
-  const int u = blockIdx.y, tid = threadIdx.x;
-  const int n = min(a.len[u], a.cap);
-  const int base0 = blockIdx.x * kSelSlice;
-  if (n <= a.M || base0 >= n) return;
-  uint32_t* gh = a.hist + (size_t)u * 3 * 2048;
-  const SelPos sp = sel_replay<kSelNT>(gh, pass, n, a.M, smem, out);
-  if (sp.cnt <= kSelCand) return;
-  const int width = pass == 2 ? 10 : 11;
+// The slice's keys, all loads in flight at once: round rr holds slots base0 +
+// rr * kChunk + e * kSelNT + tid.
+template <typename LB, typename PS>
+__device__ __forceinline__ void slice_load(const LB& lb, const PS& ps, int base0, int n, int tpos,
+                                           int (&d)[kSelRounds][kSelB],
+                                           float (&b)[kSelRounds][kSelB]) {
+#pragma unroll
+  for (int rr = 0; rr < kSelRounds; ++rr) {
+#pragma unroll
+    for (int e = 0; e < kSelB; ++e) {
+      const int i = min(base0 + rr * kChunk + e * kSelNT + (int)threadIdx.x, n - 1);
+      d[rr][e] = ps.ld(i);
+      b[rr][e] = lb ? lb.ld(i) : 0.f;
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < kSelRounds; ++rr)
+#pragma unroll
+    for (int e = 0; e < kSelB; ++e) d[rr][e] = tpos - d[rr][e];
+}
+
+// Adds the slice's keys with the given prefix to the head's histogram of the
+// width bits below it (LDS first, then one global add per non-empty bin).  (Four
+// copies of every bin, to spread a wave's same-bin atomics, made the pass slower:
+// the larger LDS footprint costs more occupancy than the conflicts it saves.)
+__device__ __forceinline__ void slice_hist(const uint32_t (&k)[kSelRounds][kSelB], int base0,
+                                           int n, const SelPos& sp, int width, uint32_t* h,
+                                           uint32_t* gh) {
+  const int tid = threadIdx.x;
   const int nb = 1 << width;
   const int shift = 32 - sp.pbits - width;
+  const uint32_t pm = sp.pmask(), pv = sp.pval();
   for (int i = tid; i < nb; i += kSelNT) h[i] = 0u;
   __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < kSelRounds; ++rr)
+#pragma unroll
+    for (int e = 0; e < kSelB; ++e) {
+      if (base0 + rr * kChunk + e * kSelNT + tid >= n || (k[rr][e] & pm) != pv) continue;
+      atomicAdd(&h[(k[rr][e] >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+  __syncthreads();
+  for (int i = tid; i < nb; i += kSelNT)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// The float32-ordered keys of the loaded slots.
+template <typename LB>
+__device__ __forceinline__ void slice_keys(const LB& lb, const int (&d)[kSelRounds][kSelB],
+                                           const float (&b)[kSelRounds][kSelB],
+                                           uint32_t (&k)[kSelRounds][kSelB]) {
+#pragma unroll
+  for (int rr = 0; rr < kSelRounds; ++rr) keys_ord32<kSelB>(lb, d[rr], b[rr], k[rr]);
+}
+
+// Pass 0: the top 11 bits of every key of the workgroup's slices.  Heads of at
+// most kSelCand slots are listed whole by the first refine launch.
+// (At most 96 registers, so that five workgroups fit a compute unit and every
+// slice of a 128K-slot layer is resident at once.)
+__global__ __launch_bounds__(kSelNT) __attribute__((amdgpu_waves_per_eu(5, 8))) void sel_hist0(SelArgs a) {
+  __shared__ uint32_t h[2048];
+  const int u = blockIdx.y;
+  const int n = min(a.len[u], a.cap);
+  const int2 br = wg_blocks(blockIdx.x, n, kSelSlice, false);
+  if (n <= a.M || n <= kSelCand || br.y < br.x) return;
   const int s0 = head_start(a.start, u);
   const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
                              a.cap - s0, a.cap};
   const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
-  const int tpos = a.tq[u / a.Hkv];
-  for (int base = base0; base < min(base0 + kSelSlice, n); base += kSelNT * kSelB) {
-    double kk[kSelB];
-    sel_keys<kSelNT>(lb, ps, base, n, tpos, kk);
-#pragma unroll
-    for (int e = 0; e < kSelB; ++e) {
-      if (base + e * kSelNT + tid >= n) continue;
-      const uint32_t k32 = ord32(kk[e]);
-      if (!has_prefix(k32, sp.prefix, sp.pbits)) continue;
-      atomicAdd(&h[(k32 >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
+  const SelPos sp = {0u, 0, 0, n};
+#pragma unroll 1
+  for (int blk = br.x; blk <= br.y; ++blk) {
+    int d[kSelRounds][kSelB];
+    float b[kSelRounds][kSelB];
+    slice_load(lb, ps, blk * kSelSlice, n, a.tq[u / a.Hkv], d, b);
+    uint32_t k[kSelRounds][kSelB];
+    slice_keys(lb, d, b, k);
+    slice_hist(k, blk * kSelSlice, n, sp, 11, h, a.hist + (size_t)u * kSelHistWords);
   }
-  __syncthreads();
-  for (int i = tid; i < nb; i += kSelNT)
-    if (h[i]) atomicAdd(&gh[pass * 2048 + i], h[i]);
 }
 
-// Lists the members of the final bucket (exact key, slot) from one slice: first
-// in LDS, then one global reservation per workgroup (a per-head counter taking
-// every wave's reservation serialises at one address).  The LDS list holds
-// kCollectLds members (a slice usually has a few hundred); members past it take a
-// global reservation per wave, so the small list keeps occupancy high.
-constexpr int kCollectLds = 1024;
-__global__ __launch_bounds__(kSelNT) void sel_collect(SelArgs a) {
+// Refine launch `pass` (1, 2) over the workgroup's slices: lists the slots of
+// the threshold's bucket if it is small enough after the first `pass` passes (and
+// no earlier launch listed it), else adds histogram pass `pass`.  The list goes
+// to LDS first and takes one global reservation per workgroup (a per-head counter
+// taking every wave's reservation serialises at one address); members past the
+// LDS list take a global reservation per wave.  The listing launch also stores,
+// per kChunk-slot chunk, the slots whose key lies above the bucket (kept whatever
+// the threshold inside it; sel_finish adds the bucket's kept members).  Only the
+// float32 keys stay in registers once formed; sel_finish forms the members' exact
+// keys.  (At most 96 registers, as sel_hist0.)
+constexpr int kCollectLds = 2048;
+__global__ __launch_bounds__(kSelNT) __attribute__((amdgpu_waves_per_eu(5, 8))) void sel_refine(SelArgs a, int pass) {
   __shared__ int smem[kSelNT / 64];
   __shared__ int out[4];
-  __shared__ unsigned long long ck[kCollectLds];
-  __shared__ int cs[kCollectLds];
+  __shared__ __align__(16) uint32_t lds[2048];  // the histogram, or the list
+  static_assert(kCollectLds <= 2048, "the list fits the histogram's space");
+  int* cs = (int*)lds;
   __shared__ int nloc, gbase;
   const int u = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int n = min(a.len[u], a.cap);
-  const int base0 = blockIdx.x * kSelSlice;
-  static_assert(kSelSlice % kChunk == 0, "a slice covers whole keep_emit chunks");
-  constexpr int kCps = kSelSlice / kChunk;  // chunks per slice
-  if (n <= a.M) return;
-  if (base0 >= n) {  // no live slot: these chunks keep nothing
-    if (tid < kCps && base0 / kChunk + tid < a.C) a.counts[(size_t)u * a.C + base0 / kChunk + tid] = 0;
-    return;
-  }
-  if (tid == 0) nloc = 0;
-  __syncthreads();
-  const SelPos sp = sel_replay<kSelNT>(a.hist + (size_t)u * 3 * 2048, 3, n, a.M, smem, out);
-  if (sp.cnt > kSelCand) return;  // sel_finish counts the kept slots itself
-  // slots whose key lies above the threshold's bucket are kept whatever the
-  // threshold inside it; sel_finish adds the bucket's kept members
-  int above[kCps];
-#pragma unroll
-  for (int c = 0; c < kCps; ++c) above[c] = 0;
+  const int2 br = wg_blocks(blockIdx.x, n, kSelSlice, false);
+  if (n <= a.M || br.y < br.x) return;
+  const int lvl = a.head[u].level;
+  if (lvl != 0 && lvl < pass) return;  // listed by an earlier launch
   const int s0 = head_start(a.start, u);
   const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
                              a.cap - s0, a.cap};
   const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
   const int tpos = a.tq[u / a.Hkv];
-  for (int base = base0; base < min(base0 + kSelSlice, n); base += kSelNT * kSelB) {
-    double kk[kSelB];
-    sel_keys<kSelNT>(lb, ps, base, n, tpos, kk);
+  int d[kSelRounds][kSelB];
+  float b[kSelRounds][kSelB];
+  slice_load(lb, ps, br.x * kSelSlice, n, tpos, d, b);  // in flight during the replay
+  if (tid == 0) nloc = 0;
+  uint32_t* gh = a.hist + (size_t)u * kSelHistWords;
+  const SelPos sp = sel_replay<kSelNT>(gh, pass, n, a.M, smem, out);
+  __syncthreads();  // nloc cleared (the replay may take no pass)
+  // more than kSelCand keys share one float32 key after the last pass: sel_finish
+  // takes the head
+  const bool listing = sp.cnt <= kSelCand;
+  if (!listing && pass == kSelRefines) return;
+  if (listing && blockIdx.x == 0 && tid == 0) {
+    SelHead* hd = a.head + u;
+    hd->level = pass;
+    hd->prefix = sp.prefix;
+    hd->pbits = sp.pbits;
+    hd->r = sp.r;
+    hd->cnt = sp.cnt;
+  }
+  constexpr int kCps = kSelSlice / kChunk;  // chunks per slice
+  const uint32_t pm = sp.pmask(), pv = sp.pval();
+  for (int blk = br.x;;) {
+    const int base0 = blk * kSelSlice;
+    uint32_t k[kSelRounds][kSelB];
+    slice_keys(lb, d, b, k);
+    if (!listing) {
+      slice_hist(k, base0, n, sp, pass == 2 ? 10 : 11, lds, gh + pass * 2048);
+    } else {
+      int above[kCps];
 #pragma unroll
-    for (int e = 0; e < kSelB; ++e) {
-      const int i = base + e * kSelNT + tid;
-      const uint32_t k32 = ord32(kk[e]);
-      const bool m = i < n && has_prefix(k32, sp.prefix, sp.pbits);
-      if (i < n && sp.pbits > 0 && (k32 >> (32 - sp.pbits)) > sp.prefix)
-        ++above[(i - base0) / kChunk];
-      const unsigned long long mask = __ballot(m);
-      if (!mask) continue;
-      int wb = 0;
-      if (lane == 0) wb = atomicAdd(&nloc, __popcll(mask));
-      wb = __shfl(wb, 0, 64);
-      // members whose LDS position lies past the list go straight to the head's
-      // list (a reservation per wave); the LDS positions below kCollectLds are all
-      // written, so the flush below copies min(nloc, kCollectLds) valid entries
-      const int pc = __popcll(mask);
-      const int over = max(0, wb + pc - kCollectLds);
-      int gb = 0;
-      if (over > 0 && lane == 0) gb = atomicAdd(&a.nlist[u], min(over, pc));
-      gb = __shfl(gb, 0, 64);
-      if (m) {
-        const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-        const int j = wb + rank;
-        if (j < kCollectLds) {
-          ck[j] = ord64(kk[e]);
-          cs[j] = i;
-        } else {
-          const int g = gb + (j - max(wb, kCollectLds));
-          if (g < kSelCand) {  // always: exactly cnt members over all slices
-            a.lk[(size_t)u * kSelCand + g] = ord64(kk[e]);
-            a.ls[(size_t)u * kSelCand + g] = i;
+      for (int rr = 0; rr < kCps; ++rr) above[rr] = 0;
+#pragma unroll
+      for (int rr = 0; rr < kCps; ++rr) {
+        const int base = base0 + rr * kChunk;
+        if (base >= n) break;
+        uint32_t mbits = 0;  // bit e: slot base + e * kSelNT + tid is a member
+#pragma unroll
+        for (int e = 0; e < kSelB; ++e) {
+          const bool live = base + e * kSelNT + tid < n;
+          const uint32_t kp = k[rr][e] & pm;
+          mbits |= (live && kp == pv) ? 1u << e : 0u;
+          // keys above the bucket: kept (sel_finish adds the bucket's kept members)
+          const unsigned long long ab = __ballot(live && kp > pv);
+          above[rr] += (live && kp > pv) ? 1 : 0;
+          const int w0 = (base + e * kSelNT + (tid & ~63)) >> 5;
+          if (lane == 0 && w0 + 1 < a.W) {
+            uint32_t* kb = a.keepbits + (size_t)u * a.W + w0;
+            kb[0] = (uint32_t)ab;
+            kb[1] = (uint32_t)(ab >> 32);
+          } else if (lane == 0 && w0 < a.W) {
+            a.keepbits[(size_t)u * a.W + w0] = (uint32_t)ab;
           }
         }
+        // the wave's members take consecutive list positions: one reservation per
+        // wave
+        const int c = __popc(mbits);
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        const int wtot = __shfl(incl, 63, 64);
+        if (wtot == 0) continue;
+        int wb = 0;
+        if (lane == 63) wb = atomicAdd(&nloc, wtot);
+        wb = __shfl(wb, 63, 64);
+        // members whose LDS position lies past the list go straight to the head's
+        // list (one reservation per wave); the LDS positions below kCollectLds are
+        // all written, so the flush below copies min(nloc, kCollectLds) entries
+        const int over = min(max(0, wb + wtot - kCollectLds), wtot);
+        int gb = 0;
+        if (over > 0 && lane == 63) gb = atomicAdd(&a.head[u].nlist, over);
+        gb = __shfl(gb, 63, 64);
+        int j = wb + incl - c;
+#pragma unroll
+        for (int e = 0; e < kSelB; ++e) {
+          if (!((mbits >> e) & 1u)) continue;
+          const int i = base + e * kSelNT + tid;
+          if (j < kCollectLds) {
+            cs[j] = i;
+          } else {
+            const int g = gb + (j - max(wb, kCollectLds));
+            if (g < kSelCand) a.ls[(size_t)u * kSelCand + g] = i;  // always: cnt in all
+          }
+          ++j;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kCps; ++c) {
+        const int tot = block_sum<kSelNT>(above[c], smem);
+        if (tid == 0 && base0 / kChunk + c < a.C) a.counts[(size_t)u * a.C + base0 / kChunk + c] = tot;
       }
     }
+    if (++blk > br.y) break;
+    slice_load(lb, ps, blk * kSelSlice, n, tpos, d, b);
   }
-#pragma unroll
-  for (int c = 0; c < kCps; ++c) {
-    const int tot = block_sum<kSelNT>(above[c], smem);
-    if (tid == 0 && base0 / kChunk + c < a.C) a.counts[(size_t)u * a.C + base0 / kChunk + c] = tot;
-  }
+  if (!listing) return;
   __syncthreads();
   const int nl = min(nloc, kCollectLds);
   if (nl == 0) return;
-  if (tid == 0) gbase = atomicAdd(&a.nlist[u], nl);
+  if (tid == 0) gbase = atomicAdd(&a.head[u].nlist, nl);
   __syncthreads();
-  unsigned long long* lk = a.lk + (size_t)u * kSelCand;
   int32_t* ls = a.ls + (size_t)u * kSelCand;
   for (int j = tid; j < nl; j += kSelNT) {
     const int g = gbase + j;
-    if (g < kSelCand) {  // always: exactly cnt members over all slices
-      lk[g] = ck[j];
-      ls[g] = cs[j];
-    }
+    if (g < kSelCand) ls[g] = cs[j];  // always: exactly cnt members over all slices
   }
 }
 
@@ -384,11 +542,13 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
   __shared__ unsigned long long ck[kSelCand];
   __shared__ int cs[kSelCand];
   __shared__ unsigned long long kext[2];
+  __shared__ unsigned long long wext[2][kSelThreads / 64];
   __shared__ int smem[kSelThreads / 64];
   __shared__ int out[4];
   const int u = blockIdx.x, tid = threadIdx.x;
   const int s0 = head_start(a.start, u);
   const int n = min(a.len[u], a.cap);
+  const SelHead hd = a.head[u];  // issued early: its latency overlaps the checks below
   if (n <= a.M) {
     if (tid == 0) {
       UnitInfo z = {0ull, -1, MODE_NOOP, n, n, s0, s0};
@@ -403,36 +563,78 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
     kext[1] = 0ull;
   }
   __syncthreads();
-  const SelPos sp = sel_replay<kSelThreads>(a.hist + (size_t)u * 3 * 2048, 3, n, a.M, smem, out);
+  // the listed bucket, or (none listed) the float32 key more than kSelCand share
+  const SelPos sp = hd.level != 0
+                        ? SelPos{hd.prefix, hd.pbits, hd.r, hd.cnt}
+                        : sel_replay<kSelThreads>(a.hist + (size_t)u * kSelHistWords, kSelRefines, n,
+                                                  a.M, smem, out);
   int r = sp.r;
   unsigned long long K;
   int sstar = -1;
   if (sp.cnt <= kSelCand) {
     // the r-th of the listed members in (key, slot) order: radix on the key below
     // the members' common top bits, then on the slot among equal keys
-    const int nc = min(min(a.nlist[u], sp.cnt), kSelCand);
-    unsigned long long lo = ~0ull, hi = 0ull;
-    for (int j = tid; j < nc; j += kSelThreads) {
-      const unsigned long long k64 = a.lk[(size_t)u * kSelCand + j];
-      ck[j] = k64;
-      cs[j] = a.ls[(size_t)u * kSelCand + j];
-      lo = k64 < lo ? k64 : lo;
-      hi = k64 > hi ? k64 : hi;
+    const int nc = min(min(hd.nlist, sp.cnt), kSelCand);
+    // every load in flight at once, then the smallest and largest key by wave
+    // shuffles and one LDS slot per wave
+    constexpr int kPer = kSelCand / kSelThreads;
+    const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
+                               a.cap - s0, a.cap};
+    const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
+    const int tpos = a.tq[u / a.Hkv];
+    int sv[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = tid + e * kSelThreads;
+      sv[e] = j < nc ? a.ls[(size_t)u * kSelCand + j] : 0;
     }
-    if (lo != ~0ull) {
-      atomicMin(&kext[0], lo);
-      atomicMax(&kext[1], hi);
+    int dv[kPer];
+    float bv[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      dv[e] = ps[sv[e]];
+      bv[e] = lb ? lb[sv[e]] : 0.f;
+    }
+    unsigned long long kv[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) kv[e] = ord64(key_f64(lb, tpos - dv[e], bv[e]));
+    unsigned long long lo = ~0ull, hi = 0ull;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = tid + e * kSelThreads;
+      if (j < nc) {
+        ck[j] = kv[e];
+        cs[j] = sv[e];
+        lo = kv[e] < lo ? kv[e] : lo;
+        hi = kv[e] > hi ? kv[e] : hi;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
+      lo = l2 < lo ? l2 : lo;
+      hi = h2 > hi ? h2 : hi;
+    }
+    if ((tid & 63) == 0) {
+      wext[0][tid >> 6] = lo;
+      wext[1][tid >> 6] = hi;
     }
     __syncthreads();
-    const unsigned long long kmin = kext[0], kmax = kext[1];
+    unsigned long long kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      kmin = wext[0][w] < kmin ? wext[0][w] : kmin;
+      kmax = wext[1][w] > kmax ? wext[1][w] : kmax;
+    }
     K = kmin;
+    bool unique = false;  // the bucket narrowed to one member: it is the threshold
     if (kmin != kmax) {
       int top = 63 - __clzll((long long)(kmin ^ kmax));  // highest differing bit
       unsigned long long pfx = top == 63 ? 0ull : kmin >> (top + 1);
-      for (; top >= 0; top -= 8) {
-        const int width = top + 1 < 8 ? top + 1 : 8;
+      for (; top >= 0; top -= 11) {
+        const int width = top + 1 < 11 ? top + 1 : 11;
         const int shift = top + 1 - width;
-        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+        for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
         __syncthreads();
         for (int j = tid; j < nc; j += kSelThreads) {
           const unsigned long long k64 = ck[j];
@@ -442,12 +644,23 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
         __syncthreads();
         const int bk = select_bucket<kSelThreads>(hist, 1 << width, r, smem, out);
         pfx = (pfx << width) | (unsigned long long)bk;
+        const bool one = hist[bk] == 1;
+        __syncthreads();  // every count read before the next pass clears them
+        if (one) {  // r == 1: the one member with this prefix
+          for (int j = tid; j < nc; j += kSelThreads)
+            if ((ck[j] >> shift) == pfx) out[2] = j;
+          __syncthreads();
+          K = ck[out[2]];
+          sstar = cs[out[2]];
+          unique = true;
+          break;
+        }
       }
-      K = pfx;
+      if (!unique) K = pfx;
     }
     // slot: the r-th smallest among the members whose key is K (slots < 2^30)
     uint32_t sp2 = 0;
-    for (int pass = 0; pass < 3; ++pass) {
+    for (int pass = 0; pass < 3 && !unique; ++pass) {
       const int shift = 20 - 10 * pass;
       for (int i = tid; i < 1024; i += kSelThreads) hist[i] = 0;
       __syncthreads();
@@ -460,29 +673,44 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
       const int bk = select_bucket<kSelThreads>(hist, 1024, r, smem, out);
       sp2 = (sp2 << 10) | (uint32_t)bk;
     }
-    sstar = (int)sp2;
-    // the bucket's kept members into their chunks' counts (sel_collect wrote the
-    // counts of the keys above the bucket)
+    if (!unique) sstar = (int)sp2;
+    // the bucket's kept members into their chunks' counts (sel_refine wrote the
+    // counts of the keys above the bucket): summed in LDS, then one add per chunk
+    const bool in_lds = a.C <= 2048;
+    if (in_lds) {
+      for (int i = tid; i < a.C; i += kSelThreads) hist[i] = 0u;
+      __syncthreads();
+    }
     for (int j = tid; j < nc; j += kSelThreads)
-      if (ck[j] > K || (ck[j] == K && cs[j] > sstar))
-        atomicAdd(&a.counts[(size_t)u * a.C + cs[j] / kChunk], 1);
+      if (ck[j] > K || (ck[j] == K && cs[j] > sstar)) {
+        atomicOr(&a.keepbits[(size_t)u * a.W + cs[j] / 32], 1u << (cs[j] & 31));
+        if (in_lds) atomicAdd(&hist[cs[j] / kChunk], 1u);
+        else atomicAdd(&a.counts[(size_t)u * a.C + cs[j] / kChunk], 1);
+      }
+    if (in_lds) {
+      __syncthreads();
+      for (int i = tid; i < a.C; i += kSelThreads)
+        if (hist[i]) a.counts[(size_t)u * a.C + i] += (int)hist[i];
+    }
   } else {
-    // more than kSelCand keys share the float32 key t32: the exact key by radix
-    // passes over the head (skipped when those keys are all equal), then the slot
-    // of the r-th of its ties in slot order
-    const uint32_t t32 = sp.prefix;
+    // more than kSelCand keys share the threshold's bucket (the top sp.pbits bits
+    // of the float32 key): the exact key by radix passes over the head (skipped
+    // when those keys are all equal), then the slot of the r-th of its ties in
+    // slot order
+    const uint32_t pm = sp.pmask(), pv = sp.pval();
     const Ring<const float> lb{a.log_beta ? a.log_beta + (size_t)u * a.cap + s0 : nullptr,
                                a.cap - s0, a.cap};
     const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
     const int tpos = a.tq[u / a.Hkv];
     unsigned long long lo = ~0ull, hi = 0ull;
     for (int base = 0; base < n; base += kSelThreads * kSelB) {
-      double kk[kSelB];
-      sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+      int dd[kSelB];
+      float bb[kSelB];
+      sel_load<kSelThreads>(lb, ps, base, n, tpos, dd, bb);
 #pragma unroll
       for (int e = 0; e < kSelB; ++e) {
-        if (base + e * kSelThreads + tid >= n || ord32(kk[e]) != t32) continue;
-        const unsigned long long k64 = ord64(kk[e]);
+        if (base + e * kSelThreads + tid >= n || (key_ord32(lb, dd[e], bb[e]) & pm) != pv) continue;
+        const unsigned long long k64 = ord64(key_f64(lb, dd[e], bb[e]));
         lo = k64 < lo ? k64 : lo;
         hi = k64 > hi ? k64 : hi;
       }
@@ -500,12 +728,13 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
         for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
         __syncthreads();
         for (int base = 0; base < n; base += kSelThreads * kSelB) {
-          double kk[kSelB];
-          sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+          int dd[kSelB];
+          float bb[kSelB];
+          sel_load<kSelThreads>(lb, ps, base, n, tpos, dd, bb);
 #pragma unroll
           for (int e = 0; e < kSelB; ++e) {
-            if (base + e * kSelThreads + tid >= n || ord32(kk[e]) != t32) continue;
-            const unsigned long long k64 = ord64(kk[e]);
+            if (base + e * kSelThreads + tid >= n || (key_ord32(lb, dd[e], bb[e]) & pm) != pv) continue;
+            const unsigned long long k64 = ord64(key_f64(lb, dd[e], bb[e]));
             if (pass == 0 || (k64 >> (shift + 8)) == pfx)
               atomicAdd(&hist[(k64 >> shift) & 255u], 1u);
           }
@@ -520,13 +749,14 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
     // walked in slot order (row e of a round = slots base + e * kSelThreads + tid)
     int seen = 0;
     for (int base = 0; base < n && sstar < 0; base += kSelThreads * kSelB) {
-      double kk[kSelB];
-      sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+      int dd[kSelB];
+      float bb[kSelB];
+      sel_load<kSelThreads>(lb, ps, base, n, tpos, dd, bb);
       bool f[kSelB];
       int c = 0;
 #pragma unroll
       for (int e = 0; e < kSelB; ++e) {
-        f[e] = base + e * kSelThreads + tid < n && ord64(kk[e]) == K;
+        f[e] = base + e * kSelThreads + tid < n && ord64(key_f64(lb, dd[e], bb[e])) == K;
         c += f[e] ? 1 : 0;
       }
       const int total = block_sum<kSelThreads>(c, smem);
@@ -546,22 +776,32 @@ __global__ __launch_bounds__(kSelThreads) void sel_finish(SelArgs a) {
         seen += tot_e;
       }
     }
-    // kept slots per chunk (sel_collect did not count for this head), counted in
-    // LDS for windows of 2048 chunks and stored
+    // kept slots (sel_refine did not mark them for this head): their bits, and
+    // their number per chunk counted in LDS for windows of 2048 chunks
     uint32_t* cc = hist;
     for (int cw = 0; cw < a.C; cw += 2048) {
       for (int i = tid; i < 2048; i += kSelThreads) cc[i] = 0u;
       __syncthreads();
       const int lo = cw * kChunk, hi2 = min(n, (cw + 2048) * kChunk);
       for (int base = lo; base < hi2; base += kSelThreads * kSelB) {
-        double kk[kSelB];
-        sel_keys<kSelThreads>(lb, ps, base, hi2, tpos, kk);
+        int dd[kSelB];
+        float bb[kSelB];
+        sel_load<kSelThreads>(lb, ps, base, hi2, tpos, dd, bb);
 #pragma unroll
         for (int e = 0; e < kSelB; ++e) {
           const int i = base + e * kSelThreads + tid;
-          if (i >= hi2) continue;
-          const unsigned long long k64 = ord64(kk[e]);
-          if (k64 > K || (k64 == K && i > sstar)) atomicAdd(&cc[i / kChunk - cw], 1u);
+          bool kept = false;
+          if (i < hi2) {
+            const unsigned long long k64 = ord64(key_f64(lb, dd[e], bb[e]));
+            kept = k64 > K || (k64 == K && i > sstar);
+            if (kept) atomicAdd(&cc[i / kChunk - cw], 1u);
+          }
+          const unsigned long long kb = __ballot(kept);  // the wave's 64 slots
+          const int w0 = (i - (tid & 63)) >> 5;
+          if ((tid & 63) == 0 && i < hi2) {
+            a.keepbits[(size_t)u * a.W + w0] = (uint32_t)kb;
+            if (w0 + 1 < a.W) a.keepbits[(size_t)u * a.W + w0 + 1] = (uint32_t)(kb >> 32);
+          }
         }
       }
       __syncthreads();
@@ -671,10 +911,7 @@ __global__ __launch_bounds__(kSelThreads) void evict_plan_lds(PlanArgs a) {
   const Ring<const int32_t> ps{a.pos + row0, capu, a.cap};
   const int tpos = a.tq[u / a.Hkv];
   int r = n - M;
-  auto key32 = [&](float l, int p) -> uint32_t {
-    const int d = tpos - p;
-    return ord32((!lb || d == 0) ? 0.0 : (double)d * (double)l);
-  };
+  auto key32 = [&](float l, int p) -> uint32_t { return key_ord32(lb, tpos - p, l); };
 
   // One eviction (the steady state: n = M + 1): the threshold is the minimum of
   // (key, slot), found by reductions instead of radix passes.
@@ -1078,23 +1315,24 @@ struct KeepArgs {
   unsigned char* scratch;   // [U][Mk][srow]
   int32_t* evicted_pos;     // [U][max_evict] or null
   int32_t* n_out;           // [U] or null
+  const uint32_t* keepbits;  // evict: [U][W] from the selection
   const void* k;
   const void* v;
-  int32_t cap, Hkv, R, C, Mk, max_evict, row_bytes, srow, move_rows;
+  int32_t cap, Hkv, R, C, W, Mk, max_evict, row_bytes, srow, move_rows;
 };
 
-// Copies the ns staged rows listed in stg (source slot, destination row) of head u
-// to scratch with the whole workgroup: consecutive threads take consecutive
-// 16-byte pieces of a row, so a load instruction covers whole lines of a few rows
+// Copies the ns staged rows of head u to scratch with the whole workgroup (stg(en)
+// gives entry en's source slot and destination row): consecutive threads take
+// consecutive 16-byte pieces of a row, so a load instruction covers whole lines of a few rows
 // (a thread per row touches 64 rows per instruction); each thread's batch of
 // pieces is loaded before any of it is stored.
-template <int NT>
-__device__ __forceinline__ void stage_list_rows(const KeepArgs& a, int u, int s0,
-                                                const int2* stg, int ns) {
+template <int NT, typename Ent>
+__device__ __forceinline__ void stage_list_rows(const KeepArgs& a, int u, int s0, Ent stg,
+                                                int ns) {
   const int ppr = a.row_bytes / 16;   // pieces per tensor row
   const int per = 2 * ppr;            // K then V
   const size_t ub = (size_t)u * a.cap;
-  constexpr int kB = 16;
+  constexpr int kB = 4;
   for (int q0 = threadIdx.x; q0 < ns * per; q0 += kB * NT) {
     u32x4 x[kB];
     unsigned char* to[kB];
@@ -1104,7 +1342,7 @@ __device__ __forceinline__ void stage_list_rows(const KeepArgs& a, int u, int s0
       to[e] = nullptr;
       if (q < ns * per) {
         const int en = q / per, part = q - en * per;
-        const int2 sd = stg[en];
+        const int2 sd = stg(en);
         const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
         const bool isv = part >= ppr;
         const int pc = isv ? part - ppr : part;
@@ -1117,7 +1355,7 @@ __device__ __forceinline__ void stage_list_rows(const KeepArgs& a, int u, int s0
       if (to[e]) *(u32x4*)to[e] = x[e];
   }
   for (int en = threadIdx.x; en < ns; en += NT) {  // the 8-byte tails
-    const int2 sd = stg[en];
+    const int2 sd = stg(en);
     const size_t row = ub + (s0 + sd.x < a.cap ? s0 + sd.x : s0 + sd.x - a.cap);
     const uint32_t l = a.log_beta ? __float_as_uint(a.log_beta[row]) : 0u;
     const uint32_t p = (uint32_t)a.pos[row];
@@ -1137,79 +1375,40 @@ __device__ __forceinline__ int first_range_ending_after(const int32_t* rg, int n
   return lo;
 }
 
-// Keep flags of the thread's kPerThread consecutive slots i0 .. i0 + kPerThread - 1
-// (i0 = chunk start + tid * kPerThread); called by the whole workgroup.  Eviction
-// keys are formed from coalesced loads (slot chunk + e * kChunkThreads + tid) and
-// the flags handed to the owning threads through kf (kChunk bytes of LDS).
+// Erase keep flags of the thread's kPerThread consecutive slots i0 ..
+// i0 + kPerThread - 1 (i0 = chunk start + tid * kPerThread), as a bit mask.
 template <int MODE>
-__device__ __forceinline__ void keep_flags(const KeepArgs& a, int u, int i0, int n, bool* f,
-                                           uint8_t* kf) {
+__device__ __forceinline__ uint32_t keep_flags(const KeepArgs& a, int u, int i0, int n) {
+  static_assert(MODE == MODE_ERASE, "eviction flags come from the selection's keep bits");
   const int s0 = head_start(a.start, u);
-  const size_t row0 = (size_t)u * a.cap + s0;
-  const Ring<const int32_t> ps{a.pos + row0, a.cap - s0, a.cap};
-  if (MODE == MODE_EVICT) {
-    const UnitInfo inf = a.info[u];
-    const Ring<const float> lb{a.log_beta ? a.log_beta + row0 : nullptr, a.cap - s0, a.cap};
-    const int tpos = a.tq[u / a.Hkv];
-    const int base = i0 - (int)threadIdx.x * kPerThread;
-    int p[kPerThread];
-    float b[kPerThread];
+  const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
+  uint32_t fm = 0;  // bit e: slot i0 + e is kept
+  // positions increase along the slots: one search for the thread's first slot,
+  // then the range index only moves forward
+  const int b = u / a.Hkv;
+  const int32_t* rg = a.ranges + (size_t)b * a.R * 2;
+  const int nr = a.n_ranges[b];
+  int pv[kPerThread];
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int i = min(base + e * kChunkThreads + (int)threadIdx.x, n - 1);
-      p[e] = ps.ld(i);
-      b[e] = lb ? lb.ld(i) : 0.f;
-    }
+  for (int e = 0; e < kPerThread; ++e) pv[e] = i0 + e < n ? ps[i0 + e] : 0;
+  int ri = i0 < n ? first_range_ending_after(rg, nr, pv[0]) : nr;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int i = base + e * kChunkThreads + (int)threadIdx.x;
-      const int d = tpos - p[e];
-      const double k = (!lb || d == 0) ? 0.0 : (double)d * (double)b[e];  // = retention_key
-      const unsigned long long k64 = ord64(k);
-      kf[e * kChunkThreads + threadIdx.x] =
-          i < n && (k64 > inf.kstar || (k64 == inf.kstar && i > inf.sstar));
-    }
-    __syncthreads();
-    static_assert(kPerThread == 16, "one 16-byte LDS read per thread");
-    const uint4 w = *(const uint4*)(kf + threadIdx.x * kPerThread);
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) f[e] = (wv[e >> 2] >> (8 * (e & 3))) & 0xffu;
-    __syncthreads();
-  } else {
-    // positions increase along the slots: one search for the thread's first slot,
-    // then the range index only moves forward
-    const int b = u / a.Hkv;
-    const int32_t* rg = a.ranges + (size_t)b * a.R * 2;
-    const int nr = a.n_ranges[b];
-    int pv[kPerThread];
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) pv[e] = i0 + e < n ? ps[i0 + e] : 0;
-    int ri = i0 < n ? first_range_ending_after(rg, nr, pv[0]) : nr;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int p = pv[e];
-      while (ri < nr && rg[2 * ri + 1] <= p) ++ri;
-      f[e] = i0 + e < n && !(ri < nr && rg[2 * ri] <= p);
-    }
+  for (int e = 0; e < kPerThread; ++e) {
+    const int p = pv[e];
+    while (ri < nr && rg[2 * ri + 1] <= p) ++ri;
+    fm |= (i0 + e < n && !(ri < nr && rg[2 * ri] <= p)) ? 1u << e : 0u;
   }
+  return fm;
 }
 
 template <int MODE>
 __global__ __launch_bounds__(kChunkThreads) void keep_count(KeepArgs a) {
   __shared__ int smem[kChunkThreads / 64];
-  __shared__ __align__(16) uint8_t kf[kChunk];
   const int u = blockIdx.y, c = blockIdx.x;
-  if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
   const int n = min(a.len[u], a.cap);
   const int base = c * kChunk;
   int cnt = 0;
-  if (base < n) {
-    bool f[kPerThread];
-    keep_flags<MODE>(a, u, base + threadIdx.x * kPerThread, n, f, kf);
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) cnt += f[e] ? 1 : 0;
-  }
+  if (base < n) cnt = __popc(keep_flags<MODE>(a, u, base + threadIdx.x * kPerThread, n));
   const int tot = block_sum<kChunkThreads>(cnt, smem);
   if (threadIdx.x == 0) a.counts[(size_t)u * a.C + c] = tot;
 }
@@ -1217,8 +1416,10 @@ __global__ __launch_bounds__(kChunkThreads) void keep_count(KeepArgs a) {
 template <int MODE>
 __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
   __shared__ int smem[kChunkThreads / 64];
-  __shared__ int2 stg[kChunk];  // this chunk's staged rows (source, destination)
-  __shared__ __align__(16) uint8_t kf[kChunk];
+  // this chunk's staged rows: source offset in the chunk << 16 | destination
+  // offset among the chunk's kept rows (both below kChunk)
+  static_assert(kChunk <= 65536, "16-bit offsets");
+  __shared__ uint32_t stg[kChunk];
   __shared__ int nstg;
   const int u = blockIdx.y, c = blockIdx.x;
   if (MODE == MODE_EVICT && a.info[u].mode == MODE_NOOP) return;
@@ -1240,36 +1441,52 @@ __global__ __launch_bounds__(kChunkThreads) void keep_emit(KeepArgs a) {
     if (MODE == MODE_ERASE) a.info[u].mode = MODE_ERASE;
     if (a.n_out) a.n_out[u] = n - all;
   }
-  const int base = c * kChunk;
-  if (base >= n) return;
-  if (threadIdx.x == 0) nstg = 0;
-  const int i0 = base + threadIdx.x * kPerThread;
-  bool f[kPerThread];
-  keep_flags<MODE>(a, u, i0, n, f, kf);
-  int cnt = 0;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) cnt += f[e] ? 1 : 0;
-  int total;
-  int dst = before + block_excl_scan<kChunkThreads>(cnt, smem, total);
+  const int2 br = wg_blocks(c, n, kChunk);  // this chunk, and a short last one
   const Ring<const int32_t> ps{a.pos + (size_t)u * a.cap + s0, a.cap - s0, a.cap};
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int i = i0 + e;
-    if (i >= n) break;
-    if (f[e]) {
-      if (dst < a.Mk) {  // always true when the threshold is consistent
-        a.keep_src[(size_t)u * a.Mk + dst] = i;
-        if (staged_row(s0, s0, i, dst, all, a.move_rows)) stg[atomicAdd(&nstg, 1)] = make_int2(i, dst);
+  for (int ch = br.x; ch <= br.y; ++ch) {
+    const int base = ch * kChunk;
+    if (threadIdx.x == 0) nstg = 0;
+    const int i0 = base + threadIdx.x * kPerThread;
+    uint32_t fm = 0;  // bit e: slot i0 + e is kept
+    if constexpr (MODE == MODE_EVICT) {
+      static_assert(kPerThread == 16, "half a word of keep bits per thread");
+      if (i0 < n) {
+        fm = (a.keepbits[(size_t)u * a.W + (i0 >> 5)] >> (i0 & 31)) & 0xFFFFu;
+        if (n - i0 < 16) fm &= (1u << (n - i0)) - 1u;
       }
-      ++dst;
-    } else if (MODE == MODE_EVICT && a.evicted_pos) {
-      const int ev = i - dst;  // evicted slots before i
-      if (ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
+    } else {
+      fm = keep_flags<MODE>(a, u, i0, n);
     }
+    const int cnt = __popc(fm);
+    int total;
+    int dst = before + block_excl_scan<kChunkThreads>(cnt, smem, total);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e;
+      if ((fm >> e) & 1u) {
+        if (dst < a.Mk) {  // always true when the threshold is consistent
+          a.keep_src[(size_t)u * a.Mk + dst] = i;
+          if (staged_row(s0, s0, i, dst, all, a.move_rows))
+            stg[atomicAdd(&nstg, 1)] = (uint32_t)(i - base) << 16 | (uint32_t)(dst - before);
+        }
+        ++dst;
+      } else if (i < n && MODE == MODE_EVICT && a.evicted_pos) {
+        const int ev = i - dst;  // evicted slots before i
+        if (ev < a.max_evict) a.evicted_pos[(size_t)u * a.max_evict + ev] = ps[i];
+      }
+    }
+    __syncthreads();
+    // the staged rows to scratch (by destination)
+    stage_list_rows<kChunkThreads>(
+        a, u, s0,
+        [&](int en) {
+          const uint32_t e = stg[en];
+          return make_int2(base + (int)(e >> 16), before + (int)(e & 0xffffu));
+        },
+        nstg);
+    before += total;
+    __syncthreads();  // the list read before the next chunk's flags reuse it
   }
-  __syncthreads();
-  // the staged rows to scratch (by destination)
-  stage_list_rows<kChunkThreads>(a, u, s0, stg, nstg);
 }
 
 // ---------------------------------------------------------------- erase by range endpoints
@@ -1583,13 +1800,14 @@ __global__ __launch_bounds__(kSelThreads) void evict_one(OneArgs a) {
   unsigned long long bk = ~0ull;
   int bs = 0x7FFFFFFF;
   for (int base = 0; base < n; base += kSelThreads * kSelB) {
-    double kk[kSelB];
-    sel_keys<kSelThreads>(lb, ps, base, n, tpos, kk);
+    int dd[kSelB];
+    float bb[kSelB];
+    sel_load<kSelThreads>(lb, ps, base, n, tpos, dd, bb);
 #pragma unroll
     for (int e = 0; e < kSelB; ++e) {
       const int i = base + e * kSelThreads + tid;
       if (i >= n) continue;
-      const unsigned long long k64 = ord64(kk[e]);
+      const unsigned long long k64 = ord64(key_f64(lb, dd[e], bb[e]));
       if (k64 < bk || (k64 == bk && i < bs)) {
         bk = k64;
         bs = i;
@@ -1735,8 +1953,8 @@ static size_t plan_lds_limit() {
 
 struct CompactLayout {
   size_t info, counts, keep_src, scratch, tile_mask, tile_base, stage_n, stage_list, copy_list,
-      sel_hist, sel_nlist, sel_lk, sel_ls, total;
-  int C, Mk, srow, move_rows, row_bytes, Tc;
+      sel_hist, sel_nlist, sel_ls, sel_bits, total;
+  int C, W, Mk, srow, move_rows, row_bytes, Tc;
 };
 
 static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
@@ -1766,10 +1984,11 @@ static CompactLayout compact_layout(const kvb_cache* c, int Mk) {
   // the chunked selection's histograms and list: only for heads the LDS planner
   // cannot take
   const bool chunked = !plan_in_lds(c);
-  L.sel_nlist = L.sel_hist + (chunked ? align_up(U * 3 * 2048 * sizeof(uint32_t), 256) : 0);
-  L.sel_lk = L.sel_nlist + (chunked ? align_up(U * sizeof(int32_t), 256) : 0);
-  L.sel_ls = L.sel_lk + (chunked ? align_up(U * kSelCand * sizeof(uint64_t), 256) : 0);
-  L.total = L.sel_ls + (chunked ? align_up(U * kSelCand * sizeof(int32_t), 256) : 0);
+  L.sel_nlist = L.sel_hist + (chunked ? align_up(U * kSelHistWords * sizeof(uint32_t), 256) : 0);
+  L.sel_ls = L.sel_nlist + (chunked ? align_up(U * sizeof(SelHead), 256) : 0);
+  L.W = (c->cap + 31) / 32;
+  L.sel_bits = L.sel_ls + (chunked ? align_up(U * kSelCand * sizeof(int32_t), 256) : 0);
+  L.total = L.sel_bits + (chunked ? align_up(U * L.W * sizeof(uint32_t), 256) : 0);
   return L;
 }
 
@@ -1790,6 +2009,7 @@ static KeepArgs keep_args(const kvb_cache* c, const CompactLayout& L, void* ws) 
   a.cap = c->cap;
   a.Hkv = c->Hkv;
   a.C = L.C;
+  a.W = L.W;
   a.Mk = L.Mk;
   a.row_bytes = L.row_bytes;
   a.srow = L.srow;
@@ -1801,7 +2021,7 @@ static void launch_keep_chunks(const kvb_cache* c, const KeepArgs& a, int mode, 
   const int U = c->B * c->Hkv;
   dim3 grid(a.C, U);
   if (mode == MODE_EVICT) {
-    // the chunk counts come from the selection (sel_collect, sel_finish)
+    // the chunk counts come from the selection (sel_refine, sel_finish)
     { TraceScope tr(kTrKeepEmit, s);
       hipLaunchKernelGGL(keep_emit<MODE_EVICT>, grid, dim3(kChunkThreads), 0, s, a); }
   } else {
@@ -1880,9 +2100,10 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     sa.start = cache->start;
     sa.tq = t;
     sa.hist = (uint32_t*)(w + L.sel_hist);
-    sa.nlist = (int32_t*)(w + L.sel_nlist);
-    sa.lk = (unsigned long long*)(w + L.sel_lk);
+    sa.head = (SelHead*)(w + L.sel_nlist);
     sa.ls = (int32_t*)(w + L.sel_ls);
+    sa.keepbits = (uint32_t*)(w + L.sel_bits);
+    sa.W = L.W;
     sa.info = a.info;
     sa.n_out = n_evicted;
     sa.counts = a.counts;
@@ -1895,12 +2116,14 @@ static int32_t evict_plan(const kvb_cache* cache, const CompactLayout& L, const 
     {
       TraceScope tr(kTrEvictSelect, s);
       hipLaunchKernelGGL(sel_init, dim3(U), dim3(kSelNT), 0, s, sa);
-      for (int pass = 0; pass < 3; ++pass)
-        hipLaunchKernelGGL(sel_hist, slices, dim3(kSelNT), 0, s, sa, pass);
-      hipLaunchKernelGGL(sel_collect, slices, dim3(kSelNT), 0, s, sa);
+      hipLaunchKernelGGL(sel_hist0, slices, dim3(kSelNT), 0, s, sa);
+      for (int pass = 1; pass <= kSelRefines; ++pass)
+        hipLaunchKernelGGL(sel_refine, slices, dim3(kSelNT), 0, s, sa, pass);
       hipLaunchKernelGGL(sel_finish, dim3(U), dim3(kSelThreads), 0, s, sa);
     }
-    launch_keep_chunks(cache, a, MODE_EVICT, s);
+    KeepArgs ka = a;
+    ka.keepbits = sa.keepbits;
+    launch_keep_chunks(cache, ka, MODE_EVICT, s);
   }
   return launch_status();
 }

@@ -92,6 +92,27 @@ def test_evict_one_float32_tie_cluster():
     _evict_and_check(d, t, n - 1, "one eviction")
 
 
+@pytest.mark.parametrize("n", [5000, 40000])
+def test_evict_subnormal_and_far_keys(n):
+    """Keys whose float32 rounding is subnormal (subnormal log beta, or tiny log
+    beta times a distance), distances above 2^24 (beyond which the float32 key is
+    rounded from the double product), on the LDS planner (5000 slots) and on the
+    chunked selection (40000)."""
+    B, H = 2, 2
+    d = _cache(11 + n, B, H, n, n + 3, 64)
+    lb = d["log_beta"]
+    rng = np.random.default_rng(n)
+    bits = rng.integers(1, 1 << 23, n).astype(np.uint32) | np.uint32(0x80000000)
+    lb[0, 0, :n] = np.where(np.arange(n) % 2 == 0, bits.view(np.float32),
+                            np.float32(-1e-37))                 # subnormal and tiny normal
+    lb[0, 1, :n] = (-rng.uniform(1e-44, 1e-35, n)).astype(np.float32)  # across the boundary
+    lb[0, 1, 100:300] = lb[0, 1, 99]                            # equal keys by slot
+    lb[1, :, :n] = (-rng.uniform(0.0, 1e-3, (H, n))).astype(np.float32)
+    t = np.array([n + 5, (1 << 25) + 7], np.int32)              # row 1: d > 2^24
+    for M in (n // 3, n - 1):
+        _evict_and_check(d, t, M, f"subnormal/far n={n} M={M}")
+
+
 def test_evict_float32_tiny_workload_steps():
     """The tiny workload: 16 decode steps of append + attention + eviction."""
     w = synth.WORKLOADS["tiny"]
@@ -184,6 +205,29 @@ def test_evict_large_head_bucket_in_one_slice():
     assert np.all(np.abs(keys) > 999) and np.all(np.abs(keys) < 1011)
     for M in (n - 1500, n - 2999, n - 1):
         _evict_and_check(d, t, M, f"bucket in one slice M={M}", max_evict=64)
+
+
+def test_evict_dense_bucket_exact_fallback():
+    """Chunked selection where more than 4096 keys (8000, spread over ~1000 float32
+    values) share the threshold's 22-bit float32 bucket, so the selection finishes
+    by exact passes over the head; the threshold sits inside that bucket."""
+    B, H, n = 1, 2, 40000
+    d = _cache(13, B, H, n, n + 3, 64)
+    lb = d["log_beta"]
+    t = np.array([n], np.int32)
+    dist = (t[0] - np.arange(n)).astype(np.float64)
+    lb[0, :, :n] = np.float32(-1e-4)                 # keys above -4: kept first
+    cl = np.arange(15000, 23000)
+    rng = np.random.default_rng(13)
+    for g in range(H):
+        kap = -1000.001 - 0.06 * rng.random(cl.size)   # inside one 1/16-wide bucket
+        lb[0, g, cl] = (kap / dist[cl]).astype(np.float32)
+    lb[0, :, :5000] = np.float32(-1.0)                # keys below the cluster: evicted first
+    keys = dist[cl] * lb[0, 0, cl].astype(np.float64)
+    k32 = np.unique(keys.astype(np.float32).view(np.uint32) >> 10)
+    assert k32.size == 1, "the cluster shares its top 22 float32 bits"
+    for M in (n - 5000 - 4000, n - 5000 - 7000, n - 5000 - 100):
+        _evict_and_check(d, t, M, f"dense bucket M={M}", max_evict=64)
 
 
 def test_evict_float32_and_d64():
