@@ -128,11 +128,15 @@ def steady_bench(args):
     head has a first-slot entry (kvb_cache.start; its slots form a ring) unless
     --no-start, so the compaction moves the shorter side of the evicted slot (the
     rows before it up one slot, or the rows after it down one) instead of always the
-    rows after it.  Default schedule (fused_append): the attention call appends the
-    decode token; the layer's eviction plan and compaction run on a second stream
-    beside the next layer's attention (--schedule both_beside: separate append, the
-    plan beside the layer's own attention; deferred: all compactions after the last
-    attention).  Each head's attention is cut into 32 splits (--splits to change;
+    rows after it.  Default schedule (plan_one): the attention call
+    (kv_attn_decode_plan_one) appends the decode token and plans each head's eviction
+    with fill, so kv_evict_one_apply (on a second stream, beside the next layer's
+    attention) moves one row per head: the decode token into the evicted slot (the
+    slots then hold the live tokens out of position order); --schedule
+    plan_one_shift keeps position order with the shift; fused_append: a separate
+    eviction plan and compaction instead; both_beside: separate append, the plan
+    beside the layer's own attention; deferred: all compactions after the last
+    attention.  Each head's attention is cut into 32 splits (--splits to change;
     finer splits than the library's default of 16 here share the GPU better with the
     second stream's compaction).  The whole step is captured once in a HIP graph and
     replayed (t advances on the device).  A second, eager run of the same steps with
@@ -150,20 +154,29 @@ def steady_bench(args):
     L, M, B = w.layers, w.budget, w.batch
     print(f"# generating {L} layers of {w.name} with {M} tokens per KV head", file=sys.stderr,
           flush=True)
+    plan1 = args.schedule in (None, "plan_one", "plan_one_shift")
+    fill = args.schedule in (None, "plan_one")  # the default here
+    # fill moves no rows, so its heads need no first-slot array (and without one the
+    # attention reads log beta and pos 16 bytes at a time)
+    use_start = not args.no_start and not fill
     kvs, qs = [], []
     for layer in range(L):
         d = synth.device_cache(w, layer, n=M, cap=M + 32)
-        if not args.no_start:
+        if use_start:
             d["start"] = torch.zeros((B, w.hkv), dtype=torch.int32, device="cuda")
         kvs.append(kvb.KVCache.from_dict(d))
         qs.append(synth.device_queries(w, layer))
     out = torch.empty((B, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, w.hq), dtype=torch.float32, device="cuda")
-    P = args.splits or 32
+    P = args.splits or (16 if fill else 32)
     ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, P), dtype=torch.uint8,
                        device="cuda")
-    ws_e = [torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8, device="cuda")
-            for _ in range(L)]
+    if plan1:
+        ws_e = [torch.empty(kvb.kv_evict_one_workspace(kvs[0], P), dtype=torch.uint8,
+                            device="cuda") for _ in range(L)]
+    else:
+        ws_e = [torch.empty(kvb.kv_evict_workspace(kvs[0], M), dtype=torch.uint8,
+                            device="cuda") for _ in range(L)]
     nev = torch.empty((L, B, w.hkv), dtype=torch.int32, device="cuda")
     t = torch.full((B,), M, dtype=torch.int32, device="cuda")
     side = torch.cuda.Stream()
@@ -171,7 +184,7 @@ def steady_bench(args):
     attended = [torch.cuda.Event() for _ in range(L)]
     planned = [torch.cuda.Event() for _ in range(L)]
     deferred = args.schedule == "deferred"
-    fused_append = args.schedule in (None, "fused_append")  # the default here
+    fused_append = args.schedule == "fused_append"
     one = args.schedule == "evict_one"
 
     def step(ev=None):
@@ -180,6 +193,18 @@ def steady_bench(args):
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
             evl = None if ev is None else ev[layer]
+            if plan1:
+                # the attention call appends the decode token and its splits select
+                # each head's eviction; the layer's apply (select + shift) follows it
+                # on the side stream, beside the next attention
+                kvb.kv_attn_decode_plan_one(kvs[layer], q, t, ws_e[layer], k_new=kn, v_new=vn,
+                                            log_beta_new=lb, num_splits=P, fill=fill, out=out,
+                                            lse=lse, ws=ws_a, stream=main)
+                attended[layer].record(main)
+                side.wait_event(attended[layer])
+                kvb.kv_evict_one_apply(kvs[layer], t, M, ws_e[layer], evicted_pos=evl,
+                                       n_evicted=nev[layer], fill=fill, stream=side)
+                continue
             if one:
                 # the attention call appends the decode token; the layer's eviction
                 # (one launch) follows it on the side stream, beside the next attention
@@ -259,7 +284,8 @@ def steady_bench(args):
     assert bool((nev == 1).all()), "steady state: one eviction per head and layer"
     # eager steps with the kernel trace
     kvb.trace_enable(16 * L * args.steps + 64, ("attn_split", "attn_merge", "append",
-                                                "evict_select", "compact_move", "evict_one"))
+                                                "evict_select", "compact_move", "evict_one",
+                                                "one_shift"))
     e0.record()
     for _ in range(args.steps):
         step()
@@ -292,13 +318,18 @@ def steady_bench(args):
     moved = 0
     for layer, (pos_h, st_h, ln_h) in enumerate(logical):
         cap = pos_h.shape[2]
+        if fill:
+            # the decode token (position t - 1 of that step) moves into the evicted
+            # slot unless it is the evicted token itself
+            moved += int(np.sum(evh[layer, :, :, 0] != int(t[0].item()) - 1))
+            continue
         for b in range(B):
             for g in range(w.hkv):
                 nn = int(ln_h[b, g]) + 1                        # after the append
                 order = (int(st_h[b, g]) + np.arange(nn - 1)) % cap
                 p_log = np.append(pos_h[b, g, order], int(t[0].item()) - 1)
                 e = int(np.searchsorted(p_log, evh[layer, b, g, 0]))
-                moved += min(e, nn - 1 - e) if not args.no_start else nn - 1 - e
+                moved += min(e, nn - 1 - e) if use_start else nn - 1 - e
     moves_b = algorithmic_bytes(w, n, moved)[1]
     step_b = L * attn_b + moves_b
     gbps = step_b / (ms * 1e-3) / 1e9
@@ -310,8 +341,10 @@ def steady_bench(args):
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True,
-                   "schedule": args.schedule or "fused_append",
-                   "head_start": not args.no_start, "kv_splits": P},
+                   "schedule": args.schedule or "plan_one",
+                   "layout": "fill (evicted slot takes the decode token)" if fill
+                   else "position order (shift)",
+                   "head_start": use_start, "kv_splits": P},
         "eager_ms_per_step": round(eager_ms, 4), "kernel_us_eager": split,
         "attention_bytes_per_layer": attn_b, "moved_rows_per_step": moved,
         "bytes_per_step": step_b, "kv_gbps": round(gbps, 1),
@@ -866,7 +899,7 @@ def main():
                     help="run each layer's eviction planning on the attention stream (no overlap)")
     ap.add_argument("--schedule", default=None,
                     choices=["plan_beside", "both_beside", "deferred", "deferred_plan",
-                             "fused_append", "evict_one"],
+                             "fused_append", "evict_one", "plan_one", "plan_one_shift"],
                     help="deferred_plan (default of the 32K step): all layers' eviction "
                          "plans and compactions follow the last attention, each plan running "
                          "beside the previous layer's compaction; deferred: each plan beside "
@@ -876,7 +909,12 @@ def main():
                          "fused_append (--steady): the attention call appends, each layer's "
                          "plan and compaction beside the next layer's attention; evict_one "
                          "(--steady): the attention call appends, each layer's one-launch "
-                         "eviction (kv_evict_one) beside the next layer's attention")
+                         "eviction (kv_evict_one) beside the next layer's attention; plan_one "
+                         "(--steady default): the attention call appends and plans the "
+                         "eviction (kv_attn_decode_plan_one with fill: the evicted slot takes "
+                         "the decode token), each layer's kv_evict_one_apply beside the next "
+                         "layer's attention; plan_one_shift: the same with the order-keeping "
+                         "shift")
     ap.add_argument("--graph", action="store_true",
                     help="ASM step: replay the step as one captured HIP graph (the decode "
                          "step does so unless --eager)")

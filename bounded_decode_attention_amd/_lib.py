@@ -60,6 +60,10 @@ def library():
             "kv_evict_plan": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
             "kv_evict_apply": (I32, [CP, I32, P, SZ, P]),
             "kv_evict_one": (I32, [CP, P, I32, P, I32, P, P]),
+            "kv_evict_one_workspace": (SZ, [CP, I32]),
+            "kv_attn_decode_plan_one": (I32, [CP, P, I32, P, F, P, P, P, I32, I32, P, P, P, SZ,
+                                              P, SZ, P]),
+            "kv_evict_one_apply": (I32, [CP, P, I32, P, I32, P, I32, P, SZ, P]),
             "kv_append": (I32, [CP, P, P, P, P, P, SZ, P]),
             "kv_attn_decode_compact": (I32, [CP, P, I32, P, F, I32, I32, I32, P, P, P, SZ, P, SZ,
                                              P]),
@@ -421,6 +425,65 @@ def kv_evict_one(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=None, st
     return n_evicted
 
 
+def kv_evict_one_workspace(cache: KVCache, num_splits: int = 0) -> int:
+    return int(library().kv_evict_one_workspace(cache.desc, int(num_splits)))
+
+
+def kv_attn_decode_plan_one(cache: KVCache, q, t, ws_evict, scale: float = 0.0, k_new=None,
+                            v_new=None, log_beta_new=None, num_splits: int = 0,
+                            fill: bool = False, out=None, lse=None, ws=None, stream=None):
+    """kv_attn_decode that also plans each head's one-token eviction in ws_evict
+    (kv_evict_one_workspace bytes) for kv_evict_one_apply; fill: the evicted slot
+    will take the head's last live row instead of a shift.  Returns (out, lse)."""
+    _need(q, "q", cache.k.dtype)
+    _need(t, "t", torch.int32)
+    _need(ws_evict, "ws_evict")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x is not None:
+            _need(x, name, cache.k.dtype)
+    if log_beta_new is not None:
+        _need(log_beta_new, "log_beta_new", torch.float32)
+    ws = _ws(ws, kv_attn_decode_workspace(cache, Hq, num_splits), q.device)
+    st = library().kv_attn_decode_plan_one(
+        cache.desc, _ptr(q), Hq, _ptr(t), float(scale), _ptr(k_new), _ptr(v_new),
+        _ptr(log_beta_new), int(num_splits), 1 if fill else 0, _ptr(out), _ptr(lse), _ptr(ws),
+        ws.numel(), _ptr(ws_evict), ws_evict.numel() * ws_evict.element_size(),
+        _stream(stream))
+    _check(st, "kv_attn_decode_plan_one")
+    return out, lse
+
+
+def kv_evict_one_apply(cache: KVCache, t, M: int, ws_evict, evicted_pos=None, n_evicted=None,
+                       fill: bool = False, stream=None):
+    """The eviction kv_attn_decode_plan_one planned (see kvbound.h): heads at M + 1
+    lose their lowest-retention token (fill: the decode token takes its slot; pass
+    the value the plan was made with).  Returns n_evicted [B][Hkv] int32 (1, 0, or
+    -(n - M) for a head left untouched)."""
+    _need(t, "t", torch.int32)
+    _need(ws_evict, "ws_evict")
+    B, H = cache.length.shape
+    if n_evicted is None:
+        n_evicted = torch.empty((B, H), dtype=torch.int32, device=t.device)
+    _need(n_evicted, "n_evicted", torch.int32)
+    me = 0
+    if evicted_pos is not None:
+        _need(evicted_pos, "evicted_pos", torch.int32)
+        me = evicted_pos.shape[-1]
+    st = library().kv_evict_one_apply(cache.desc, _ptr(t), int(M), _ptr(evicted_pos), me,
+                                      _ptr(n_evicted), 1 if fill else 0, _ptr(ws_evict),
+                                      ws_evict.numel() * ws_evict.element_size(),
+                                      _stream(stream))
+    _check(st, "kv_evict_one_apply")
+    return n_evicted
+
+
 def kv_attn_decode_compact(cache: KVCache, q, t, M: int, ws_evict, scale: float = 0.0,
                            num_splits: int = 0, phase: int = 0, out=None, lse=None, ws=None,
                            stream=None):
@@ -496,7 +559,7 @@ TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "asm_prefix_merge": 2048, "km_assign": 4096, "km_update": 8192,
               "asm_aggregate": 16384, "asm_vt": 32768, "latent_absorb": 65536,
               "latent_read": 131072, "evict_one": 262144, "erase_search": 524288,
-              "erase_plan": 1048576}
+              "erase_plan": 1048576, "one_shift": 4194304}
 
 
 def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:

@@ -64,6 +64,8 @@ struct AttnArgs {
   // when non-null, the call's workspace status word: the first workgroup resets it
   // to KVB_OK (the merge, a later launch of the same call, may set an error)
   int32_t* status = nullptr;
+  // one-eviction candidates (kv_attn_decode_plan_one): [U][P] per split; null: none
+  OneCand* cand = nullptr;
 };
 
 // ------------------------------------------------------------------ append
@@ -496,6 +498,32 @@ __device__ __forceinline__ void compute_tile128(const KTile& t, const lds_u8* __
   }
 }
 
+// One-eviction candidate over one tile: the lowest (retention key, position) among
+// the tile's rows below `end` that this lane's group holds (rows 16j + 4g + r), with
+// its row.  The key (t - pos) * log beta is formed exactly in double (a < 2^30
+// integer times a float), 0 at distance 0 or without a retention array; -0 compares
+// equal to +0.
+template <bool LB>
+__device__ __forceinline__ void sel_tile128(const KTile& t, int tb, int end, int lane, int qpos,
+                                            double& bk, int& bp, int& bs) {
+  const int lg = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tb + 16 * j + 4 * lg + r;
+      const int ps = t.ps[j][r];
+      const int d = qpos - ps;
+      const double key = (LB && d != 0) ? (double)d * (double)t.lb[j][r] : 0.0;
+      if (tok < end && (key < bk || (key == bk && ps < bp))) {
+        bk = key;
+        bp = ps;
+        bs = tok;
+      }
+    }
+  }
+}
+
 // Writes the kept rows of one tile to their compacted slots: K from the registers
 // the QK MFMA read (lane (g, c): row 16j + c, dims 32kk + 8g), V from the tile's LDS
 // block (lane l of block i: row 4i + l/16, 16-byte chunk l%16), log beta and pos
@@ -542,7 +570,7 @@ __device__ __forceinline__ void move_tile128(const KTile& t, const lds_u8* __res
 // One split (p, head u) of the pipelined kernel; the launch has gridDim.x splits per
 // head.  A device function so that a launch can also carry other work (the ASM
 // candidate scan of kv_attn_decode_asm) in workgroups of its own.
-template <int G, bool LB, bool VEC, bool MOVE>
+template <int G, bool LB, bool VEC, bool MOVE, bool SEL = false>
 __device__ __forceinline__ void pipe128_split(const AttnArgs& a, const int p, const int u) {
   static_assert(2 * G <= 16, "group too large for the hi/lo column split");
   __shared__ __attribute__((aligned(16))) unsigned char vbufA_[8 * kVBlk];
@@ -585,6 +613,9 @@ __device__ __forceinline__ void pipe128_split(const AttnArgs& a, const int p, co
   f32x4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one-eviction candidate of this split (SEL)
+  double bk = __builtin_huge_val();
+  int bp = 0x7FFFFFFF, bs = 0x7FFFFFFF;
 
   // Tiles in pairs (A, B) with one loop exit, so each register set keeps its
   // registers.
@@ -634,17 +665,33 @@ __device__ __forceinline__ void pipe128_split(const AttnArgs& a, const int p, co
       moves(tA, vbufA);
       issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + step, end, capu, a.cap, lane, tB, vbufB, tmask, tbase);
       compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      if (SEL) sel_tile128<LB>(tA, tb, end, lane, qpos, bk, bp, bs);
       wait_vmem_all();
       moves(tB, vbufB);
       issue_tile128<VEC, MOVE>(kb, vb, lbb, pb, tb + 2 * step, end, capu, a.cap, lane, tA, vbufA, tmask,
                                tbase);
       compute_tile128<G>(tB, vbufB, tb + step, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      if (SEL) sel_tile128<LB>(tB, tb + step, end, lane, qpos, bk, bp, bs);
       tb += 2 * step;
     }
     if (ntiles & 1) {
       wait_vmem_all();
       moves(tA, vbufA);
       compute_tile128<G>(tA, vbufA, tb, end, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      if (SEL) sel_tile128<LB>(tA, tb, end, lane, qpos, bk, bp, bs);
+    }
+  }
+  if constexpr (SEL) {
+    // the four lane groups' candidates
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1)
+      one_better(bk, bp, bs, __shfl_xor(bk, o, 64), __shfl_xor(bp, o, 64), __shfl_xor(bs, o, 64));
+    if (lane == 0) {
+      OneCand c;
+      c.key = bk;
+      c.slot = bs;
+      c.pos = bp;
+      a.cand[(size_t)u * a.P + a.p_off + p] = c;
     }
   }
   // staged rows (source below the attended boundary): scratch -> destination.
@@ -705,10 +752,10 @@ __device__ __forceinline__ void pipe128_split(const AttnArgs& a, const int p, co
   }
 }
 
-template <int G, bool LB, bool VEC, bool MOVE>
+template <int G, bool LB, bool VEC, bool MOVE, bool SEL = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_split_pipe128(AttnArgs a) {
-  pipe128_split<G, LB, VEC, MOVE>(a, blockIdx.x, blockIdx.y);
+  pipe128_split<G, LB, VEC, MOVE, SEL>(a, blockIdx.x, blockIdx.y);
 }
 
 // The splits plus the ASM lookup's candidate scan in one launch: rows y < crow of
@@ -1047,8 +1094,9 @@ template <int D>
 __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const float* part_ml,
                                                       int P, float* out, float* lse,
                                                       const UnitInfo* info, int32_t* len,
-                                                      int G, NewTok nt, AsmTail at) {
+                                                      int G, NewTok nt, AsmTail at, OnePlan op) {
   constexpr int NW = D / 64;
+  __shared__ int s_e;
   __shared__ float s_w[64];
   __shared__ float s_red[2][NW];
   __shared__ float s_mw[2];
@@ -1076,6 +1124,10 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
       pr = load_elem(nt.q, (size_t)bh * D + tid, nt.elem) *
            load_elem(nt.k_new, (size_t)u * D + tid, nt.elem);
   }
+  // the one-eviction candidates (the head's first query head plans)
+  const bool plans = op.cand && bh % G == 0;
+  OneCand oc;
+  if (plans) oc = one_plan_load(op, u, tid);
   float q2 = 0.f;
   float cs = kNegInf;
   int ck = 0x7FFFFFFF;
@@ -1207,28 +1259,47 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
   if (info && tid == 0 && bh % G == 0) {
     if (info[u].mode == MODE_EVICT) len[u] = info[u].kept;
   }
+  // the one-eviction plan (kv_attn_decode_plan_one), by the head's first query head:
+  // the splits' candidates and, when appended here, the decode token (key 0, the
+  // head's last slot)
+  if (plans) {
+    int n;
+    bool has_new = false;
+    if (nt.k_new) {
+      const int n0 = min(max(nt.n_rec[u], 0), nt.cap);
+      n = incl ? n0 + 1 : n0;
+      has_new = incl;
+    } else {
+      n = min(max(op.len[u], 0), op.cap);
+    }
+    one_plan_head(op, u, n, has_new, 0.0, has_new ? nt.t[u / nt.Hkv] : 0, oc, tid, D, &s_e);
+  }
 }
 
 // ------------------------------------------------------------------ host
-static void launch_merge(const float* part_a, const float* part_ml, int P, int D, float* out,
+// Returns true when the merge also made the one-eviction plan (`one`).
+static bool launch_merge(const float* part_a, const float* part_ml, int P, int D, float* out,
                          float* lse, const UnitInfo* info, int32_t* len, int G, int BH,
                          hipStream_t s, const NewTok* nt = nullptr,
-                         const AsmTail* tail = nullptr) {
+                         const AsmTail* tail = nullptr, const OnePlan* one = nullptr) {
   NewTok none;
   memset(&none, 0, sizeof(none));
   const NewTok& n = nt ? *nt : none;
   AsmTail no_tail;
   memset(&no_tail, 0, sizeof(no_tail));
   const AsmTail& at = tail ? *tail : no_tail;
+  OnePlan no_plan;
+  memset(&no_plan, 0, sizeof(no_plan));
+  const OnePlan& op = one ? *one : no_plan;
   if (P <= 64 && D == 128) {
     hipLaunchKernelGGL(attn_merge_small<128>, dim3(BH), dim3(128), 0, s, part_a, part_ml, P, out,
-                       lse, info, len, G, n, at);
-    return;
+                       lse, info, len, G, n, at, op);
+    return true;
   }
   if (P <= 64 && D == 64) {
     hipLaunchKernelGGL(attn_merge_small<64>, dim3(BH), dim3(64), 0, s, part_a, part_ml, P, out,
-                       lse, info, len, G, n, at);
-    return;
+                       lse, info, len, G, n, at, op);
+    return true;
   }
   if (P > 128)
     hipLaunchKernelGGL(attn_merge<512>, dim3(BH), dim3(512), 0, s, part_a, part_ml, P, D, out,
@@ -1236,6 +1307,7 @@ static void launch_merge(const float* part_a, const float* part_ml, int P, int D
   else
     hipLaunchKernelGGL(attn_merge<256>, dim3(BH), dim3(256), 0, s, part_a, part_ml, P, D, out,
                        lse, info, len, G, n, at);
+  return false;
 }
 
 static bool mfma_supported(const kvb_cache* c, int G) {
@@ -1255,7 +1327,7 @@ static void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
 }
 
 static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s,
-                            const AsmScanArgs* scan = nullptr) {
+                            const AsmScanArgs* scan = nullptr, const OnePlan* one = nullptr) {
   dim3 grid(a.P, c->B * c->Hkv);
   const long long crow_ll = scan ? ((long long)scan->tasks + a.P - 1) / a.P : 0;
   if (scan && c->dtype == KVB_BF16 && c->D == 128 &&
@@ -1282,6 +1354,25 @@ static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s
       hipLaunchKernelGGL(asm_scan_kernel<128>, dim3(scan->tasks), dim3(64), 0, s, *scan);
     else
       hipLaunchKernelGGL(asm_scan_kernel<64>, dim3(scan->tasks), dim3(64), 0, s, *scan);
+  }
+  if (a.cand && c->dtype == KVB_BF16 && c->D == 128 &&
+      (a.G == 1 || a.G == 2 || a.G == 4 || a.G == 8)) {
+    // the splits also find the one-eviction candidates
+#define KVB_SEL_CASE(GG)                                                                   \
+  if (a.G == GG) {                                                                         \
+    const bool lb = c->log_beta != nullptr, vec = vec_bias_loads(c);                      \
+    if (lb && vec) hipLaunchKernelGGL((attn_split_pipe128<GG, true, true, false, true>), grid, dim3(64), 0, s, a);   \
+    else if (lb) hipLaunchKernelGGL((attn_split_pipe128<GG, true, false, false, true>), grid, dim3(64), 0, s, a);   \
+    else if (vec) hipLaunchKernelGGL((attn_split_pipe128<GG, false, true, false, true>), grid, dim3(64), 0, s, a);  \
+    else hipLaunchKernelGGL((attn_split_pipe128<GG, false, false, false, true>), grid, dim3(64), 0, s, a);          \
+    return KVB_OK;                                                                         \
+  }
+    KVB_SEL_CASE(1) KVB_SEL_CASE(2) KVB_SEL_CASE(4) KVB_SEL_CASE(8)
+#undef KVB_SEL_CASE
+  }
+  if (one) {
+    // other kernels: the candidates from a scan of log beta and pos of their own
+    launch_one_scan(c, a.t, *one, s);
   }
   if (mfma_supported(c, a.G)) {
 #define KVB_PIPE_CASE(GG)                                                                  \
@@ -1392,7 +1483,8 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
                                 int32_t num_splits, float* out, float* lse, void* ws,
                                 size_t ws_bytes, hipStream_t stream, const AsmTail* tail,
                                 int32_t* status = nullptr,
-                                const AsmScanArgs* scan = nullptr) {
+                                const AsmScanArgs* scan = nullptr,
+                                const OnePlan* one = nullptr) {
   int32_t st = check_cache(cache, true);
   if (st) return st;
   if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
@@ -1432,6 +1524,7 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
   a.p_off = 0;
   if (!status) status = (int32_t*)ws;
   a.status = status;
+  if (one) a.cand = (OneCand*)one->cand;
 
   // with a decode token: attend over the cached tokens (the splits record each
   // head's len), then the merge adds the token's own state and appends it
@@ -1461,11 +1554,13 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
   }
   {
     TraceScope tr(kTrAttnSplit, s);
-    if ((st = launch_split(cache, a, s, scan))) return st;
+    if ((st = launch_split(cache, a, s, scan, one))) return st;
   }
   TraceScope tr(kTrAttnMerge, s);
-  launch_merge(a.part_a, a.part_ml, P, cache->D, out, lse, nullptr, nullptr, G,
-               cache->B * Hq, s, k_new ? &nt : nullptr, tail);
+  const bool planned = launch_merge(a.part_a, a.part_ml, P, cache->D, out, lse, nullptr,
+                                    nullptr, G, cache->B * Hq, s, k_new ? &nt : nullptr, tail,
+                                    one);
+  if (one && !planned) launch_one_plan(cache, t, *one, s);
   return launch_status();
 }
 
@@ -1476,6 +1571,24 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
                                   size_t ws_bytes, void* stream) {
   return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, num_splits, out,
                           lse, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+extern "C" int32_t kv_attn_decode_plan_one(const kvb_cache* cache, const void* q, int32_t Hq,
+                                           const int32_t* t, float scale, const void* k_new,
+                                           const void* v_new, const float* log_beta_new,
+                                           int32_t num_splits, int32_t fill, float* out,
+                                           float* lse, void* ws, size_t ws_bytes, void* ws_evict,
+                                           size_t ws_evict_bytes, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (num_splits < 0 || num_splits > 4096 || (fill != 0 && fill != 1)) return KVB_EINVAL;
+  if ((long long)cache->B * cache->Hkv > 65535) return KVB_EUNSUPPORTED;
+  const int32_t P = num_splits > 0 ? num_splits : auto_splits(cache);
+  if (!ws_evict || ws_evict_bytes < kv_evict_one_workspace(cache, P)) return KVB_EWORKSPACE;
+  OnePlan op = one_plan_args(cache, P, ws_evict);
+  op.fill = fill;
+  return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, P, out, lse, ws,
+                          ws_bytes, (hipStream_t)stream, nullptr, nullptr, nullptr, &op);
 }
 
 // ------------------------------------------------------------------ no-alloc entry

@@ -182,6 +182,145 @@ EvictView evict_view(const kvb_cache* c, int32_t M, const void* ws);
 // the plan's scratch; must run after kv_evict_plan and before any row is written.
 void launch_fused_stage(const kvb_cache* c, int32_t M, void* ws, hipStream_t s);
 
+// One-eviction planning (kv_attn_decode_plan_one -> kv_evict_one_apply).
+// Candidates: per head and split, the slot (relative to the head's first live slot)
+// with the lowest (retention key, position) among the slots the split attended
+// (positions are distinct, so the order is total); key +inf, position and slot
+// INT32_MAX for a split with no slot.
+struct OneCand {
+  double key;
+  int32_t slot;
+  int32_t pos;
+};
+static_assert(sizeof(OneCand) == 16, "OneCand layout");
+// Per head: the evicted slot e (relative) among n live slots; for a shift its
+// direction (up: rows [0, e) one slot toward the last slot; else rows (e, n) one slot
+// toward the first) and chunk count; fill: the last live row takes slot e instead;
+// the head's first slot.
+struct OneInfo {
+  int32_t e, n, up, nch, s0, fill, pad1, pad2;
+};
+static_assert(sizeof(OneInfo) == 32, "OneInfo layout");
+// What the planner needs: the candidates, where the plan goes (info, and the staged
+// rows: the source row b_c = e -+ (c + 1) R of every shift chunk c with a successor,
+// which chunk c + 1's destinations overwrite), and the cache.
+struct OnePlan {
+  const OneCand* cand;   // [U][P]; null: no planning
+  OneInfo* info;         // [U]
+  unsigned char* scratch;  // [U][SC][srow]: K row, V row, (log beta, pos)
+  const void* k;
+  const void* v;
+  const float* log_beta;
+  const int32_t* pos;
+  const int32_t* start;
+  const int32_t* len;
+  int32_t P, cap, R, SC, srow, row_bytes, fill;
+};
+// Host: the plan arguments of a one-eviction workspace (P candidates per head).
+OnePlan one_plan_args(const kvb_cache* c, int32_t P, void* ws);
+// Candidates by a scan of log beta and pos alone (splits other than the pipelined
+// kernel's): chunk p of each head's live slots gives entry p.
+void launch_one_scan(const kvb_cache* c, const int32_t* t, const OnePlan& p, hipStream_t s);
+// The plan by a kernel of its own (merges that do not plan), after the merge: the
+// candidates and the head's last live slot.
+void launch_one_plan(const kvb_cache* c, const int32_t* t, const OnePlan& p, hipStream_t s);
+
+// Keeps the lower of (bk, bp) and (k, ps) in (key, position) order, with its slot.
+__device__ __forceinline__ void one_better(double& bk, int& bp, int& bs, double k, int ps,
+                                           int s) {
+  if (k < bk || (k == bk && ps < bp)) {
+    bk = k;
+    bp = ps;
+    bs = s;
+  }
+}
+
+// This thread's candidate of head u for one_plan_head (threads below min(P, 64); the
+// others hold no candidate), loaded early so that its latency overlaps other work.
+__device__ __forceinline__ OneCand one_plan_load(const OnePlan& p, int u, int tid) {
+  OneCand c;
+  c.key = __builtin_huge_val();
+  c.slot = 0x7FFFFFFF;
+  c.pos = 0x7FFFFFFF;
+  if (tid < 64 && tid < p.P) c = p.cand[(size_t)u * p.P + tid];
+  return c;
+}
+
+// The plan of head u, by all nthr threads of one workgroup (nthr a multiple of 64,
+// every thread calls it): the lowest (key, position) over the P candidates (own:
+// this thread's one_plan_load) and, with has_last, slot n - 1 with key last_key and
+// position last_pos; then the staged rows (shift only) and the head's OneInfo.
+// s_e: a __shared__ int of the caller.
+__device__ __forceinline__ void one_plan_head(const OnePlan& p, int u, int n, bool has_last,
+                                              double last_key, int last_pos, OneCand own,
+                                              int tid, int nthr, int* s_e) {
+  const int s0 = p.start ? min(max(p.start[u], 0), p.cap - 1) : 0;
+  if (tid < 64) {
+    double bk = own.key;
+    int bp = own.pos, bs = own.slot;
+    for (int i = tid + 64; i < p.P; i += 64) {
+      const OneCand c = p.cand[(size_t)u * p.P + i];
+      one_better(bk, bp, bs, c.key, c.pos, c.slot);
+    }
+    if (tid == 0 && has_last && n > 0) one_better(bk, bp, bs, last_key, last_pos, n - 1);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+      one_better(bk, bp, bs, __shfl_xor(bk, o, 64), __shfl_xor(bp, o, 64), __shfl_xor(bs, o, 64));
+    const int e = n > 0 ? min(max(bs, 0), n - 1) : 0;
+    if (p.fill) {
+      // nothing to stage: the plan is e
+      if (tid == 0) {
+        const OneInfo inf = {e, n, 0, 0, s0, 1, 0, 0};
+        p.info[u] = inf;
+      }
+    } else if (tid == 0) {
+      *s_e = e;
+    }
+  }
+  if (p.fill) return;
+  __syncthreads();
+  const int e = *s_e;
+  const bool up = p.start != nullptr && e < n - 1 - e;
+  const int moved = n > 0 ? (up ? e : n - 1 - e) : 0;
+  const int nch = (moved + p.R - 1) / p.R;
+  const int ppr = p.row_bytes / 16;
+  const int per = 2 * ppr + 1;  // 16-byte pieces of K and V, then (log beta, pos)
+  const int items = nch > 1 ? (nch - 1) * per : 0;
+  const size_t row0 = (size_t)u * p.cap;
+  const unsigned char* kb = (const unsigned char*)p.k + row0 * p.row_bytes;
+  const unsigned char* vb = (const unsigned char*)p.v + row0 * p.row_bytes;
+  unsigned char* sc = p.scratch + (size_t)u * p.SC * p.srow;
+  constexpr int kIn = 4;
+  for (int i0 = 0; i0 < items; i0 += nthr * kIn) {
+    u32x4 x[kIn];
+#pragma unroll
+    for (int q = 0; q < kIn; ++q) {
+      const int it = min(i0 + q * nthr + tid, items - 1);
+      const int c = it / per, pt = it - c * per;
+      int sl = s0 + (up ? e - (c + 1) * p.R : e + (c + 1) * p.R);
+      if (sl >= p.cap) sl -= p.cap;
+      if (pt < 2 * ppr)
+        x[q] = *(const u32x4*)((pt < ppr ? kb : vb) + (size_t)sl * p.row_bytes + 16 * (pt % ppr));
+      else
+        x[q] = u32x4{p.log_beta ? __float_as_uint(p.log_beta[row0 + sl]) : 0u,
+                     (uint32_t)p.pos[row0 + sl], 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < kIn; ++q) {
+      const int it = i0 + q * nthr + tid;
+      if (it >= items) continue;
+      const int c = it / per, pt = it - c * per;
+      *(u32x4*)(sc + (size_t)c * p.srow +
+                (pt < 2 * ppr ? (pt < ppr ? 0 : p.row_bytes) + 16 * (pt % ppr) : 2 * p.row_bytes)) =
+          x[q];
+    }
+  }
+  if (tid == 0) {
+    const OneInfo inf = {e, n, up ? 1 : 0, nch, s0, 0, 0, 0};
+    p.info[u] = inf;
+  }
+}
+
 // Host: 0 if the current device is gfx950, else KVB_EDEVICE (cached per device).
 int32_t check_device();
 
@@ -196,7 +335,7 @@ enum TraceKernel {
   kTrAttnFused = 512, kTrAsmPrefix = 1024, kTrAsmPrefixMerge = 2048, kTrKmAssign = 4096,
   kTrKmUpdate = 8192, kTrAsmAggregate = 16384, kTrAsmVt = 32768,
   kTrLatentAbsorb = 65536, kTrLatentRead = 131072, kTrEvictOne = 262144,
-  kTrEraseSearch = 524288, kTrErasePlan = 1048576
+  kTrEraseSearch = 524288, kTrErasePlan = 1048576, kTrOneShift = 4194304
 };
 struct TraceScope {
   TraceScope(int kernel, hipStream_t s);

@@ -351,3 +351,42 @@ def test_check_cache_rejects_arguments_before_launch():
     assert L.kv_check_cache(ctypes.byref(good), None, None, None, -1, P(8), None) == -1
     assert L.kv_check_cache(ctypes.byref(good), None, None, P(8), 3, P(8), None) == -1  # ranges
     assert L.kv_check_cache(ctypes.byref(_desc(pos=None)), None, None, None, 0, P(8), None) == -1
+
+
+@needs_lib
+def test_plan_one_entries_reject_arguments_before_launch():
+    """kv_attn_decode_plan_one / kv_evict_one_apply: fake pointers; a missing or
+    short eviction workspace, bad splits or budget are refused on the host, and
+    valid arguments without a GPU stop at the device check."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    good = _desc()
+    need = L.kv_evict_one_workspace(ctypes.byref(good), 0)
+    assert need > 256
+    assert L.kv_evict_one_workspace(ctypes.byref(good), 7) > need - 1
+    assert L.kv_evict_one_workspace(ctypes.byref(good), -1) == 0
+    assert L.kv_evict_one_workspace(None, 0) == 0
+    wsa = L.kv_attn_decode_workspace(ctypes.byref(good), 8, 0)
+
+    def plan(ws_e=P(8192), ws_e_bytes=need, splits=0, c=good, fill=0):
+        return L.kv_attn_decode_plan_one(ctypes.byref(c), P(64), 8, P(72), 0.0, None, None,
+                                         None, splits, fill, P(80), P(88), P(4096), wsa, ws_e,
+                                         ws_e_bytes, None)
+    assert plan(ws_e=None) == -4
+    assert plan(ws_e_bytes=need - 1) == -4
+    assert plan(splits=5000) == -1
+    assert plan(fill=2) == -1
+    assert plan(c=_desc(B=300, Hkv=256)) == -2     # B * Hkv above 65535
+
+    def apply(t=P(72), M=5, ws=P(8192), ws_bytes=need, me=0, fill=0):
+        return L.kv_evict_one_apply(ctypes.byref(good), t, M, None, me, None, fill, ws,
+                                    ws_bytes, None)
+    assert apply(t=None) == -1
+    assert apply(M=-1) == -1
+    assert apply(me=-1) == -1
+    assert apply(fill=3) == -1
+    assert apply(ws=None) == -4
+    assert apply(ws_bytes=300) == -4
+    if not _has_gpu():
+        assert plan() == -5
+        assert apply() == -5
