@@ -29,6 +29,22 @@ sys.path.insert(0, ROOT)
 METRIC = "bounded-KV decode attn: KV GB/s vs HBM peak; decode steps/s at 32K ctx"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_qwen3_8b_32k_traffic.json")
+STEADY_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_steady_m4096_traffic.json")
+
+
+def recorded_traffic(path, **match):
+    """HBM bytes per launch recorded from FETCH_SIZE / WRITE_SIZE counters, if they
+    were taken on the attention source as it is now and in the same configuration;
+    else None."""
+    if not os.path.exists(path):
+        return None
+    tr = json.load(open(path))
+    src = os.path.join(ROOT, "bounded_decode_attention_amd", "csrc", "attn_decode.hip")
+    if tr.get("source_sha") != source_digest(src):
+        return None
+    if any(tr.get(k) != v for k, v in match.items()):
+        return None
+    return tr.get("traffic_bytes")
 
 
 def algorithmic_bytes(w, n, moved_rows):
@@ -128,17 +144,18 @@ def steady_bench(args):
     head has a first-slot entry (kvb_cache.start; its slots form a ring) unless
     --no-start, so the compaction moves the shorter side of the evicted slot (the
     rows before it up one slot, or the rows after it down one) instead of always the
-    rows after it.  Default schedule (plan_one): the attention call
-    (kv_attn_decode_plan_one) appends the decode token and plans each head's eviction
-    with fill, so kv_evict_one_apply (on a second stream, beside the next layer's
-    attention) moves one row per head: the decode token into the evicted slot (the
-    slots then hold the live tokens out of position order); --schedule
-    plan_one_shift keeps position order with the shift; fused_append: a separate
-    eviction plan and compaction instead; both_beside: separate append, the plan
-    beside the layer's own attention; deferred: all compactions after the last
-    attention.  Each head's attention is cut into 32 splits (--splits to change;
-    finer splits than the library's default of 16 here share the GPU better with the
-    second stream's compaction).  The whole step is captured once in a HIP graph and
+    rows after it.  Default schedule (fill): one kv_attn_decode_evict_one call per
+    layer, whose splits also select each head's eviction and whose merge writes the
+    decode token into the evicted slot (one row per head; the slots then hold the
+    live tokens out of position order, and the heads need no start array);
+    --schedule plan_one keeps position order: kv_attn_decode_plan_one, then
+    kv_evict_one_apply's shift on a second stream beside the next layer's attention;
+    fused_append: a separate eviction plan and compaction there instead;
+    both_beside: separate append, the plan beside the layer's own attention;
+    deferred: all compactions after the last attention.  Each head's attention is
+    cut into 16 splits with fill, 32 otherwise (--splits to change; finer splits
+    share the GPU better with a second stream's compaction).  The whole step is
+    captured once in a HIP graph and
     replayed (t advances on the device).  A second, eager run of the same steps with
     the library's HIP-event trace gives the per-kernel split."""
     import dataclasses
@@ -154,8 +171,8 @@ def steady_bench(args):
     L, M, B = w.layers, w.budget, w.batch
     print(f"# generating {L} layers of {w.name} with {M} tokens per KV head", file=sys.stderr,
           flush=True)
-    plan1 = args.schedule in (None, "plan_one", "plan_one_shift")
-    fill = args.schedule in (None, "plan_one")  # the default here
+    fill = args.schedule in (None, "fill")  # the default here
+    plan1 = args.schedule == "plan_one"
     # fill moves no rows, so its heads need no first-slot array (and without one the
     # attention reads log beta and pos 16 bytes at a time)
     use_start = not args.no_start and not fill
@@ -169,7 +186,8 @@ def steady_bench(args):
     out = torch.empty((B, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, w.hq), dtype=torch.float32, device="cuda")
     P = args.splits or (16 if fill else 32)
-    ws_a = torch.empty(kvb.kv_attn_decode_workspace(kvs[0], w.hq, P), dtype=torch.uint8,
+    ws_a = torch.empty(kvb.kv_attn_decode_evict_one_workspace(kvs[0], w.hq, P) if fill
+                       else kvb.kv_attn_decode_workspace(kvs[0], w.hq, P), dtype=torch.uint8,
                        device="cuda")
     if plan1:
         ws_e = [torch.empty(kvb.kv_evict_one_workspace(kvs[0], P), dtype=torch.uint8,
@@ -193,17 +211,25 @@ def steady_bench(args):
         for layer in range(L):
             q, kn, vn, lb = qs[layer]
             evl = None if ev is None else ev[layer]
+            if fill:
+                # one call: attention, decode token, eviction (the decode token takes
+                # the evicted slot)
+                kvb.kv_attn_decode_evict_one(kvs[layer], q, t, M, k_new=kn, v_new=vn,
+                                             log_beta_new=lb, num_splits=P, out=out, lse=lse,
+                                             evicted_pos=evl, n_evicted=nev[layer], ws=ws_a,
+                                             stream=main)
+                continue
             if plan1:
-                # the attention call appends the decode token and its splits select
-                # each head's eviction; the layer's apply (select + shift) follows it
-                # on the side stream, beside the next attention
+                # the attention call appends the decode token and plans each head's
+                # eviction; the layer's order-keeping shift follows it on the side
+                # stream, beside the next attention
                 kvb.kv_attn_decode_plan_one(kvs[layer], q, t, ws_e[layer], k_new=kn, v_new=vn,
-                                            log_beta_new=lb, num_splits=P, fill=fill, out=out,
-                                            lse=lse, ws=ws_a, stream=main)
+                                            log_beta_new=lb, num_splits=P, out=out, lse=lse,
+                                            ws=ws_a, stream=main)
                 attended[layer].record(main)
                 side.wait_event(attended[layer])
                 kvb.kv_evict_one_apply(kvs[layer], t, M, ws_e[layer], evicted_pos=evl,
-                                       n_evicted=nev[layer], fill=fill, stream=side)
+                                       n_evicted=nev[layer], stream=side)
                 continue
             if one:
                 # the attention call appends the decode token; the layer's eviction
@@ -272,6 +298,9 @@ def steady_bench(args):
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
+    replay_check = None
+    if not args.no_cpu:
+        replay_check = steady_replay_check(w, kvs[L - 1], qs[L - 1], t, out, lse, g, M, fill)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     nsteps = args.steps
@@ -341,7 +370,7 @@ def steady_bench(args):
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "budget": M, "layers": L, "graph": True,
-                   "schedule": args.schedule or "plan_one",
+                   "schedule": args.schedule or "fill",
                    "layout": "fill (evicted slot takes the decode token)" if fill
                    else "position order (shift)",
                    "head_start": use_start, "kv_splits": P},
@@ -349,16 +378,88 @@ def steady_bench(args):
         "attention_bytes_per_layer": attn_b, "moved_rows_per_step": moved,
         "bytes_per_step": step_b, "kv_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "attn_split_pipe128<G=4> (M + 1 tokens)",
+        "roofline": {"bound": "hbm", "kernel": "attn_split_pipe128<G=4>" +
+                     (" with eviction candidates" if plan1 else "") + " (M + 1 tokens)",
                      "achieved": round(attn_b / (attn_us * 1e-6) / 1e9, 1) if attn_us else None,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_b / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
-                     if attn_us else None, "traffic": None, "bytes_per_launch": attn_b,
+                     if attn_us else None,
+                     "traffic": recorded_traffic(STEADY_TRAFFIC_FILE, splits=P, fill=fill,
+                                                 head_start=use_start),
+                     "bytes_per_launch": attn_b,
                      "avg_launch_ms": round(attn_us / 1000, 5)},
         "cpu_baseline": None}
     if host_units:
         line["cpu_baseline"] = cpu_baseline(w, host_units, M, M, args.cpu_seconds)
+        line["cpu_baseline"]["checked_against_gpu"] = replay_check
     print(json.dumps(line), flush=True)
+
+
+def steady_replay_check(w, c, qd, t, out, lse, graph, M, fill):
+    """One replay of the captured steady step, checked against the oracle on its last
+    layer (which the step's out and lse hold): that layer's heads are copied to the
+    host before the replay; after it, every query head's out and lse must be within
+    2e-3 of the oracle's (append, attend) and every head's live rows, in position
+    order, equal bit for bit to the oracle's layout after the eviction."""
+    import numpy as np
+    import torch
+
+    import oracle
+    bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    torch.cuda.synchronize()
+    q, kn, vn, lb = qd
+    tq = int(t[0].item())
+    B, H, G = w.batch, w.hkv, w.group
+
+    def live(cc):
+        k, v = bits(cc.k), bits(cc.v)
+        lbh, ps, ln = cc.log_beta.cpu().numpy(), cc.pos.cpu().numpy(), cc.length.cpu().numpy()
+        st = cc.start.cpu().numpy() if cc.start is not None else np.zeros((B, H), np.int64)
+        cap = k.shape[2]
+        rows = {}
+        for b in range(B):
+            for g in range(H):
+                n = int(ln[b, g])
+                sl = (int(st[b, g]) + np.arange(n)) % cap
+                order = np.argsort(ps[b, g, sl], kind="stable")
+                sl = sl[order]
+                rows[(b, g)] = (k[b, g, sl], v[b, g, sl], lbh[b, g, sl], ps[b, g, sl], n)
+        return rows
+
+    before = live(c)
+    qh, knh, vnh, lbh = bits(q), bits(kn), bits(vn), lb.cpu().numpy()
+    graph.replay()
+    torch.cuda.synchronize()
+    after = live(c)
+    oh, lh = out.cpu().numpy(), lse.cpu().numpy()
+    worst = 0.0
+    for (b, g), (k, v, lbv, ps, n) in before.items():
+        pad = lambda x: np.concatenate([x, np.zeros_like(x[:1])])[None, None]  # noqa: E731
+        cc = oracle.Cache(pad(k), pad(v), pad(lbv), pad(ps), np.array([[n]], np.int32))
+        oracle.append_tokens(cc, knh[b, g][None, None], vnh[b, g][None, None],
+                             np.array([[lbh[b, g]]], np.float32), np.array([tq]))
+        qv = (qh[b, g * G:(g + 1) * G].astype(np.uint32) << 16).view(np.float32)
+        ro, rl = oracle.decode_attention(cc.values("k"), cc.values("v"), cc.log_beta, cc.pos,
+                                         cc.length, qv.astype(np.float64)[None],
+                                         np.array([tq]))
+        for j in range(G):
+            err = float(np.max(np.abs(oh[b, g * G + j] - ro[0, j])) / np.max(np.abs(ro[0, j])))
+            assert err <= 2e-3 and abs(float(lh[b, g * G + j]) - rl[0, j]) <= 2e-3, \
+                f"steady replay: query head ({b},{g * G + j}) rel err {err:.2e}"
+            worst = max(worst, err)
+        ce, _, _ = oracle.evict_to_budget(cc, np.array([tq]), M)
+        kept = int(ce.length[0, 0])
+        ka, va, la, pa, na = after[(b, g)]
+        assert na == kept, f"steady replay: head ({b},{g}) len {na} vs {kept}"
+        for got, name in ((ka, "k"), (va, "v"), (la, "log_beta"), (pa, "pos")):
+            want = getattr(ce, name)[0, 0, :kept]
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), \
+                f"steady replay: head ({b},{g}) {name} differs from the oracle"
+    return {"what": "one replay of the captured step: the last layer's out/lse within 2e-3 "
+                    "of the oracle (append, attend) and every head's live rows, in position "
+                    "order, equal to the oracle's layout after the eviction",
+            "kv_heads": len(before), "max_rel_err": float(f"{worst:.3e}"),
+            "layout": "fill" if fill else "shift"}
 
 
 def asm_bench(args):
@@ -899,7 +1000,7 @@ def main():
                     help="run each layer's eviction planning on the attention stream (no overlap)")
     ap.add_argument("--schedule", default=None,
                     choices=["plan_beside", "both_beside", "deferred", "deferred_plan",
-                             "fused_append", "evict_one", "plan_one", "plan_one_shift"],
+                             "fused_append", "evict_one", "plan_one", "fill"],
                     help="deferred_plan (default of the 32K step): all layers' eviction "
                          "plans and compactions follow the last attention, each plan running "
                          "beside the previous layer's compaction; deferred: each plan beside "
@@ -909,12 +1010,11 @@ def main():
                          "fused_append (--steady): the attention call appends, each layer's "
                          "plan and compaction beside the next layer's attention; evict_one "
                          "(--steady): the attention call appends, each layer's one-launch "
-                         "eviction (kv_evict_one) beside the next layer's attention; plan_one "
-                         "(--steady default): the attention call appends and plans the "
-                         "eviction (kv_attn_decode_plan_one with fill: the evicted slot takes "
-                         "the decode token), each layer's kv_evict_one_apply beside the next "
-                         "layer's attention; plan_one_shift: the same with the order-keeping "
-                         "shift")
+                         "eviction (kv_evict_one) beside the next layer's attention; fill "
+                         "(--steady default): one kv_attn_decode_evict_one call per layer "
+                         "(the decode token takes the evicted slot); plan_one (--steady): "
+                         "kv_attn_decode_plan_one, each layer's order-keeping "
+                         "kv_evict_one_apply beside the next layer's attention")
     ap.add_argument("--graph", action="store_true",
                     help="ASM step: replay the step as one captured HIP graph (the decode "
                          "step does so unless --eager)")
@@ -1240,13 +1340,7 @@ def main():
         kernel = "attn_split_pipe128<G=4>"
     split_gbps = unit_b / (split_avg * 1e-3) / 1e9
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        src = os.path.join(ROOT, "bounded_decode_attention_amd", "csrc", "attn_decode.hip")
-        if (tr.get("source_sha") == source_digest(src) and tr.get("splits") == splits
-                and tr.get("fused", False) == fused):
-            traffic = tr.get("traffic_bytes")
+    traffic = recorded_traffic(TRAFFIC_FILE, splits=splits, fused=fused)
 
     line = {
         "metric": METRIC, "value": round(1000.0 / ms_per_step, 3), "unit": "decode steps/s",

@@ -61,9 +61,12 @@ def library():
             "kv_evict_apply": (I32, [CP, I32, P, SZ, P]),
             "kv_evict_one": (I32, [CP, P, I32, P, I32, P, P]),
             "kv_evict_one_workspace": (SZ, [CP, I32]),
-            "kv_attn_decode_plan_one": (I32, [CP, P, I32, P, F, P, P, P, I32, I32, P, P, P, SZ,
-                                              P, SZ, P]),
-            "kv_evict_one_apply": (I32, [CP, P, I32, P, I32, P, I32, P, SZ, P]),
+            "kv_attn_decode_plan_one": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P,
+                                              SZ, P]),
+            "kv_evict_one_apply": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
+            "kv_attn_decode_evict_one_workspace": (SZ, [CP, I32, I32]),
+            "kv_attn_decode_evict_one": (I32, [CP, P, I32, P, F, P, P, P, I32, I32, P, P, P, I32,
+                                               P, P, SZ, P]),
             "kv_append": (I32, [CP, P, P, P, P, P, SZ, P]),
             "kv_attn_decode_compact": (I32, [CP, P, I32, P, F, I32, I32, I32, P, P, P, SZ, P, SZ,
                                              P]),
@@ -429,12 +432,54 @@ def kv_evict_one_workspace(cache: KVCache, num_splits: int = 0) -> int:
     return int(library().kv_evict_one_workspace(cache.desc, int(num_splits)))
 
 
+def kv_attn_decode_evict_one_workspace(cache: KVCache, Hq: int, num_splits: int = 0) -> int:
+    return int(library().kv_attn_decode_evict_one_workspace(cache.desc, int(Hq),
+                                                            int(num_splits)))
+
+
+def kv_attn_decode_evict_one(cache: KVCache, q, t, M: int, scale: float = 0.0, k_new=None,
+                             v_new=None, log_beta_new=None, num_splits: int = 0, out=None,
+                             lse=None, evicted_pos=None, n_evicted=None, ws=None, stream=None):
+    """Attention with the decode token, then every head at M + 1 evicts its lowest
+    token and the decode token takes that slot (see kvbound.h).  Returns (out, lse,
+    n_evicted)."""
+    _need(q, "q", cache.k.dtype)
+    _need(t, "t", torch.int32)
+    B, Hq, D = q.shape
+    H = cache.length.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if n_evicted is None:
+        n_evicted = torch.empty((B, H), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _need(n_evicted, "n_evicted", torch.int32)
+    me = 0
+    if evicted_pos is not None:
+        _need(evicted_pos, "evicted_pos", torch.int32)
+        me = evicted_pos.shape[-1]
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x is not None:
+            _need(x, name, cache.k.dtype)
+    if log_beta_new is not None:
+        _need(log_beta_new, "log_beta_new", torch.float32)
+    ws = _ws(ws, kv_attn_decode_evict_one_workspace(cache, Hq, num_splits), q.device)
+    st = library().kv_attn_decode_evict_one(
+        cache.desc, _ptr(q), Hq, _ptr(t), float(scale), _ptr(k_new), _ptr(v_new),
+        _ptr(log_beta_new), int(M), int(num_splits), _ptr(out), _ptr(lse), _ptr(evicted_pos),
+        me, _ptr(n_evicted), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kv_attn_decode_evict_one")
+    return out, lse, n_evicted
+
+
 def kv_attn_decode_plan_one(cache: KVCache, q, t, ws_evict, scale: float = 0.0, k_new=None,
-                            v_new=None, log_beta_new=None, num_splits: int = 0,
-                            fill: bool = False, out=None, lse=None, ws=None, stream=None):
-    """kv_attn_decode that also plans each head's one-token eviction in ws_evict
-    (kv_evict_one_workspace bytes) for kv_evict_one_apply; fill: the evicted slot
-    will take the head's last live row instead of a shift.  Returns (out, lse)."""
+                            v_new=None, log_beta_new=None, num_splits: int = 0, out=None,
+                            lse=None, ws=None, stream=None):
+    """kv_attn_decode that also plans each head's one-token eviction (order-keeping
+    shift) in ws_evict (kv_evict_one_workspace bytes) for kv_evict_one_apply.
+    Returns (out, lse)."""
     _need(q, "q", cache.k.dtype)
     _need(t, "t", torch.int32)
     _need(ws_evict, "ws_evict")
@@ -453,19 +498,17 @@ def kv_attn_decode_plan_one(cache: KVCache, q, t, ws_evict, scale: float = 0.0, 
     ws = _ws(ws, kv_attn_decode_workspace(cache, Hq, num_splits), q.device)
     st = library().kv_attn_decode_plan_one(
         cache.desc, _ptr(q), Hq, _ptr(t), float(scale), _ptr(k_new), _ptr(v_new),
-        _ptr(log_beta_new), int(num_splits), 1 if fill else 0, _ptr(out), _ptr(lse), _ptr(ws),
-        ws.numel(), _ptr(ws_evict), ws_evict.numel() * ws_evict.element_size(),
-        _stream(stream))
+        _ptr(log_beta_new), int(num_splits), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+        _ptr(ws_evict), ws_evict.numel() * ws_evict.element_size(), _stream(stream))
     _check(st, "kv_attn_decode_plan_one")
     return out, lse
 
 
 def kv_evict_one_apply(cache: KVCache, t, M: int, ws_evict, evicted_pos=None, n_evicted=None,
-                       fill: bool = False, stream=None):
+                       stream=None):
     """The eviction kv_attn_decode_plan_one planned (see kvbound.h): heads at M + 1
-    lose their lowest-retention token (fill: the decode token takes its slot; pass
-    the value the plan was made with).  Returns n_evicted [B][Hkv] int32 (1, 0, or
-    -(n - M) for a head left untouched)."""
+    lose their lowest-retention token, the rows keeping position order.  Returns
+    n_evicted [B][Hkv] int32 (1, 0, or -(n - M) for a head left untouched)."""
     _need(t, "t", torch.int32)
     _need(ws_evict, "ws_evict")
     B, H = cache.length.shape
@@ -477,7 +520,7 @@ def kv_evict_one_apply(cache: KVCache, t, M: int, ws_evict, evicted_pos=None, n_
         _need(evicted_pos, "evicted_pos", torch.int32)
         me = evicted_pos.shape[-1]
     st = library().kv_evict_one_apply(cache.desc, _ptr(t), int(M), _ptr(evicted_pos), me,
-                                      _ptr(n_evicted), 1 if fill else 0, _ptr(ws_evict),
+                                      _ptr(n_evicted), _ptr(ws_evict),
                                       ws_evict.numel() * ws_evict.element_size(),
                                       _stream(stream))
     _check(st, "kv_evict_one_apply")

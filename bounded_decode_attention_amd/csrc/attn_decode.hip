@@ -1233,27 +1233,90 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
   }
   out[(size_t)bh * D + tid] = so;
   if (tid == 0) lse[bh] = lse_out;
+  // kv_attn_decode_evict_one: a head with M + 1 live tokens (the decode token
+  // included) loses the lowest (key, position) among the splits' candidates and the
+  // decode token; decided before the decode token is written, since it may take the
+  // evicted slot
+  int ev = -1, n_ev = 0;
+  if (plans && op.fill_M >= 0) {
+    int n0 = 0, n;
+    if (nt.k_new) {
+      n0 = min(max(nt.n_rec[u], 0), nt.cap);
+      n = incl ? n0 + 1 : n0;
+    } else {
+      n = min(max(op.len[u], 0), op.cap);
+    }
+    if (tid < 64) {
+      double bk = oc.key;
+      int bp = oc.pos, bs = oc.slot;
+      if (tid == 0 && nt.k_new && incl) one_better(bk, bp, bs, 0.0, nt.t[u / nt.Hkv], n0);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+        one_better(bk, bp, bs, __shfl_xor(bk, o, 64), __shfl_xor(bp, o, 64),
+                   __shfl_xor(bs, o, 64));
+      if (tid == 0) {
+        int e = -1;
+        if (n == op.fill_M + 1) {
+          e = min(max(bs, 0), n - 1);
+          if (op.evicted_pos && op.max_evict > 0)
+            op.evicted_pos[(size_t)u * op.max_evict] = bp;
+        }
+        if (op.n_evicted)
+          op.n_evicted[u] = e >= 0 ? 1 : (n <= op.fill_M ? 0 : -(n - op.fill_M));
+        s_e = e;
+      }
+    }
+    __syncthreads();
+    ev = s_e;
+    n_ev = n;
+  }
   // append the decode token (first query head of each KV head); every split has
-  // read the old len, and the other merge blocks use the recorded one
+  // read the old len, and the other merge blocks use the recorded one.  With an
+  // eviction above the token goes into the evicted slot (not at all when it is the
+  // evicted one) and len stays.
   if (nt.k_new && bh % G == 0) {
     if (!incl) {
       if (tid == 0) nt.status[0] = KVB_ECAPACITY;
     } else {
       const int n0 = nt.n_rec[u];
-      int s0 = head_start(nt.start, u) + n0;  // slot of the decode token
-      if (s0 >= nt.cap) s0 -= nt.cap;
-      const int words = D * nt.elem / 4;
-      const size_t dst = ((size_t)u * nt.cap + s0) * words;
-      for (int w = tid; w < words; w += D) {
-        ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
-        ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
-      }
-      if (tid == 0) {
-        nt.pos[(size_t)u * nt.cap + s0] = nt.t[u / nt.Hkv];
-        if (nt.log_beta) nt.log_beta[(size_t)u * nt.cap + s0] = nt.lb_new[u];
-        nt.len[u] = n0 + 1;
+      if (ev != n0) {
+        int s0 = head_start(nt.start, u) + (ev >= 0 ? ev : n0);  // slot of the decode token
+        if (s0 >= nt.cap) s0 -= nt.cap;
+        const int words = D * nt.elem / 4;
+        const size_t dst = ((size_t)u * nt.cap + s0) * words;
+        for (int w = tid; w < words; w += D) {
+          ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
+          ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
+        }
+        if (tid == 0) {
+          nt.pos[(size_t)u * nt.cap + s0] = nt.t[u / nt.Hkv];
+          if (nt.log_beta) nt.log_beta[(size_t)u * nt.cap + s0] = nt.lb_new[u];
+          nt.len[u] = ev >= 0 ? n0 : n0 + 1;
+        }
       }
     }
+  }
+  if (ev >= 0 && !(nt.k_new && incl)) {
+    // no decode token written here: the last live row moves into the evicted slot
+    const int n = n_ev;
+    const int s0 = op.start ? min(max(op.start[u], 0), op.cap - 1) : 0;
+    auto slot = [&](int i) { return s0 + i < op.cap ? s0 + i : s0 + i - op.cap; };
+    const size_t row0 = (size_t)u * op.cap;
+    if (ev != n - 1) {
+      const int words = op.row_bytes / 4;
+      const size_t se = (row0 + slot(ev)) * words, sl = (row0 + slot(n - 1)) * words;
+      for (int w = tid; w < words; w += D) {
+        const uint32_t kx = ((const uint32_t*)op.k)[sl + w];
+        const uint32_t vx = ((const uint32_t*)op.v)[sl + w];
+        ((uint32_t*)op.k)[se + w] = kx;
+        ((uint32_t*)op.v)[se + w] = vx;
+      }
+      if (tid == 0) {
+        if (op.log_beta) op.log_beta[row0 + slot(ev)] = op.log_beta[row0 + slot(n - 1)];
+        op.pos[row0 + slot(ev)] = op.pos[row0 + slot(n - 1)];
+      }
+    }
+    if (tid == 0) op.len[u] = n - 1;
   }
   // fused compaction: the head's new length (every split has read the old one)
   if (info && tid == 0 && bh % G == 0) {
@@ -1262,7 +1325,7 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
   // the one-eviction plan (kv_attn_decode_plan_one), by the head's first query head:
   // the splits' candidates and, when appended here, the decode token (key 0, the
   // head's last slot)
-  if (plans) {
+  if (plans && op.fill_M < 0) {
     int n;
     bool has_new = false;
     if (nt.k_new) {
@@ -1576,17 +1639,61 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
 extern "C" int32_t kv_attn_decode_plan_one(const kvb_cache* cache, const void* q, int32_t Hq,
                                            const int32_t* t, float scale, const void* k_new,
                                            const void* v_new, const float* log_beta_new,
-                                           int32_t num_splits, int32_t fill, float* out,
-                                           float* lse, void* ws, size_t ws_bytes, void* ws_evict,
+                                           int32_t num_splits, float* out, float* lse, void* ws,
+                                           size_t ws_bytes, void* ws_evict,
                                            size_t ws_evict_bytes, void* stream) {
   int32_t st = check_cache(cache, true);
   if (st) return st;
-  if (num_splits < 0 || num_splits > 4096 || (fill != 0 && fill != 1)) return KVB_EINVAL;
+  if (num_splits < 0 || num_splits > 4096) return KVB_EINVAL;
   if ((long long)cache->B * cache->Hkv > 65535) return KVB_EUNSUPPORTED;
   const int32_t P = num_splits > 0 ? num_splits : auto_splits(cache);
   if (!ws_evict || ws_evict_bytes < kv_evict_one_workspace(cache, P)) return KVB_EWORKSPACE;
-  OnePlan op = one_plan_args(cache, P, ws_evict);
-  op.fill = fill;
+  const OnePlan op = one_plan_args(cache, P, ws_evict);
+  return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, P, out, lse, ws,
+                          ws_bytes, (hipStream_t)stream, nullptr, nullptr, nullptr, &op);
+}
+
+// kv_attn_decode_evict_one's workspace: the attention's, then the candidates.
+extern "C" size_t kv_attn_decode_evict_one_workspace(const kvb_cache* cache, int32_t Hq,
+                                                     int32_t num_splits) {
+  if (!cache || Hq < 1 || cache->Hkv < 1 || Hq % cache->Hkv != 0) return 0;
+  const size_t a = kv_attn_decode_workspace(cache, Hq, num_splits);
+  if (a == 0 || num_splits < 0 || num_splits > 4096) return 0;
+  const size_t P = num_splits > 0 ? (size_t)num_splits : (size_t)auto_splits(cache);
+  return a + align_up((size_t)cache->B * cache->Hkv * P * sizeof(OneCand), 256);
+}
+
+extern "C" int32_t kv_attn_decode_evict_one(const kvb_cache* cache, const void* q, int32_t Hq,
+                                            const int32_t* t, float scale, const void* k_new,
+                                            const void* v_new, const float* log_beta_new,
+                                            int32_t M, int32_t num_splits, float* out,
+                                            float* lse, int32_t* evicted_pos, int32_t max_evict,
+                                            int32_t* n_evicted, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (num_splits < 0 || num_splits > 4096 || M < 0 || max_evict < 0) return KVB_EINVAL;
+  if ((long long)cache->B * cache->Hkv > 65535) return KVB_EUNSUPPORTED;
+  const int32_t P = num_splits > 0 ? num_splits : auto_splits(cache);
+  const size_t need = kv_attn_decode_evict_one_workspace(cache, Hq, P);
+  if (need == 0) return KVB_EINVAL;
+  if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
+  OnePlan op;
+  memset(&op, 0, sizeof(op));
+  op.cand = (const OneCand*)((char*)ws + kv_attn_decode_workspace(cache, Hq, P));
+  op.k = cache->k;
+  op.v = cache->v;
+  op.log_beta = cache->log_beta;
+  op.pos = cache->pos;
+  op.start = cache->start;
+  op.len = cache->len;
+  op.P = P;
+  op.cap = cache->cap;
+  op.row_bytes = cache->D * (cache->dtype == KVB_BF16 ? 2 : 4);
+  op.fill_M = M;
+  op.evicted_pos = evicted_pos;
+  op.max_evict = max_evict;
+  op.n_evicted = n_evicted;
   return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, P, out, lse, ws,
                           ws_bytes, (hipStream_t)stream, nullptr, nullptr, nullptr, &op);
 }

@@ -193,28 +193,34 @@ struct OneCand {
   int32_t pos;
 };
 static_assert(sizeof(OneCand) == 16, "OneCand layout");
-// Per head: the evicted slot e (relative) among n live slots; for a shift its
-// direction (up: rows [0, e) one slot toward the last slot; else rows (e, n) one slot
-// toward the first) and chunk count; fill: the last live row takes slot e instead;
-// the head's first slot.
+// Per head: the evicted slot e (relative) among n live slots, the direction of the
+// shift (up: rows [0, e) one slot toward the last slot; else rows (e, n) one slot
+// toward the first), its chunk count and the head's first slot.
 struct OneInfo {
-  int32_t e, n, up, nch, s0, fill, pad1, pad2;
+  int32_t e, n, up, nch, s0, pad0, pad1, pad2;
 };
 static_assert(sizeof(OneInfo) == 32, "OneInfo layout");
 // What the planner needs: the candidates, where the plan goes (info, and the staged
 // rows: the source row b_c = e -+ (c + 1) R of every shift chunk c with a successor,
-// which chunk c + 1's destinations overwrite), and the cache.
+// which chunk c + 1's destinations overwrite), and the cache.  With fill_M >= 0
+// (kv_attn_decode_evict_one) there is no plan: a head with fill_M + 1 live tokens
+// evicts at once, the decode token (or the last live row) taking the evicted slot,
+// and the outputs are written.
 struct OnePlan {
   const OneCand* cand;   // [U][P]; null: no planning
   OneInfo* info;         // [U]
   unsigned char* scratch;  // [U][SC][srow]: K row, V row, (log beta, pos)
-  const void* k;
-  const void* v;
-  const float* log_beta;
-  const int32_t* pos;
+  void* k;
+  void* v;
+  float* log_beta;
+  int32_t* pos;
   const int32_t* start;
-  const int32_t* len;
-  int32_t P, cap, R, SC, srow, row_bytes, fill;
+  int32_t* len;
+  int32_t P, cap, R, SC, srow, row_bytes;
+  int32_t fill_M;
+  int32_t* evicted_pos;  // [U][max_evict] or null
+  int32_t max_evict;
+  int32_t* n_evicted;    // [U] or null
 };
 // Host: the plan arguments of a one-eviction workspace (P candidates per head).
 OnePlan one_plan_args(const kvb_cache* c, int32_t P, void* ws);
@@ -222,7 +228,7 @@ OnePlan one_plan_args(const kvb_cache* c, int32_t P, void* ws);
 // kernel's): chunk p of each head's live slots gives entry p.
 void launch_one_scan(const kvb_cache* c, const int32_t* t, const OnePlan& p, hipStream_t s);
 // The plan by a kernel of its own (merges that do not plan), after the merge: the
-// candidates and the head's last live slot.
+// candidates and the head's last live slot; with p.fill_M >= 0 the eviction by fill.
 void launch_one_plan(const kvb_cache* c, const int32_t* t, const OnePlan& p, hipStream_t s);
 
 // Keeps the lower of (bk, bp) and (k, ps) in (key, position) order, with its slot.
@@ -266,18 +272,8 @@ __device__ __forceinline__ void one_plan_head(const OnePlan& p, int u, int n, bo
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
       one_better(bk, bp, bs, __shfl_xor(bk, o, 64), __shfl_xor(bp, o, 64), __shfl_xor(bs, o, 64));
-    const int e = n > 0 ? min(max(bs, 0), n - 1) : 0;
-    if (p.fill) {
-      // nothing to stage: the plan is e
-      if (tid == 0) {
-        const OneInfo inf = {e, n, 0, 0, s0, 1, 0, 0};
-        p.info[u] = inf;
-      }
-    } else if (tid == 0) {
-      *s_e = e;
-    }
+    if (tid == 0) *s_e = n > 0 ? min(max(bs, 0), n - 1) : 0;
   }
-  if (p.fill) return;
   __syncthreads();
   const int e = *s_e;
   const bool up = p.start != nullptr && e < n - 1 - e;

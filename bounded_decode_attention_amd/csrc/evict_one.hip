@@ -1,22 +1,23 @@
 // The steady state of bounded decoding ("Cache What Lasts", section 2.2, inference:
 // each decode step puts one token into a head that holds M, and the token with
-// the lowest retention score beta_i^(t-i) leaves), split between the attention and
-// a one-launch apply so that no pass over the head's keys runs on its own:
+// the lowest retention score beta_i^(t-i) leaves), with the selection folded into
+// the attention so that no pass over the head's keys runs on its own.  The
+// attention's splits find, per head, the attended slot with the lowest (kappa,
+// position), kappa = (t - pos) * log beta exact in double, from the log beta and pos
+// values each split loads for the bias anyway; one candidate per split.  Then:
 //
-//   kv_attn_decode_plan_one  the attention's splits also find, per head, the
-//                 attended slot with the lowest (kappa, slot), kappa = (t - pos) *
-//                 log beta exact in double (one candidate per split, from the log
-//                 beta and pos values the split loads for the bias anyway); its
-//                 merge (one workgroup per head) reduces them to the evicted slot
-//                 e, picks the shorter side (with a start array the rows before e
-//                 move up one slot when there are fewer of them, else the rows
-//                 after e move down one slot) and copies the few rows the shift
-//                 cannot read in place to scratch;
-//   kv_evict_one_apply  one_shift moves the rows, one workgroup per chunk of R rows,
-//                 and sets len, start and the outputs; or, with fill (or for a plan
-//                 made with fill), the head's last live row (the decode token) moves
-//                 into the evicted slot: one row per head (one_fill, one wave per
-//                 head), the slots no longer in position order.
+//   kv_attn_decode_evict_one  the merge (or one_plan after merges that do not
+//                 plan) reduces the candidates and the decode token to the evicted
+//                 slot e and writes the decode token into e instead of appending
+//                 it (fill): nothing else moves, and the live slots are no longer
+//                 in position order;
+//   kv_attn_decode_plan_one + kv_evict_one_apply  the order-keeping form: the
+//                 merge reduces the candidates to e, picks the shorter side (with
+//                 a start array the rows before e move up one slot when there are
+//                 fewer of them, else the rows after e move down one slot) and
+//                 copies the few rows the shift cannot read in place to scratch;
+//                 one_shift moves the rows, one workgroup per chunk of R rows, and
+//                 sets len, start and the outputs.
 //
 // In-place safety of the shift: chunk c of a head moves its R source rows one slot
 // toward e's side.  Its destinations overlap its own sources (read into registers
@@ -26,7 +27,7 @@
 // every chunk c with a successor to scratch, and chunk c reads that row from there.
 //
 // one_scan forms the candidates from log beta and pos alone, for the split kernels
-// that do not produce them; one_plan plans after merges that do not.
+// that do not produce them.
 #include "common.h"
 
 namespace kvb {
@@ -78,7 +79,10 @@ OnePlan one_plan_args(const kvb_cache* c, int32_t P, void* ws) {
   p.SC = L.SC;
   p.srow = L.srow;
   p.row_bytes = L.row_bytes;
-  p.fill = 0;
+  p.fill_M = -1;
+  p.evicted_pos = nullptr;
+  p.max_evict = 0;
+  p.n_evicted = nullptr;
   return p;
 }
 
@@ -130,23 +134,63 @@ void launch_one_scan(const kvb_cache* c, const int32_t* t, const OnePlan& p, hip
 }
 
 // The plan of head blockIdx.x after a merge that does not plan: its candidates and
-// its last live slot (the decode token if the call appended one).
+// its last live slot (the decode token if the call appended one).  With fill_M >= 0
+// the eviction itself: a head with fill_M + 1 live tokens loses the lowest, and its
+// last live row takes that slot.
 __global__ __launch_bounds__(64) void one_plan(OnePlan pl, const int32_t* t, int32_t Hkv) {
   __shared__ int s_e;
-  const int u = blockIdx.x;
+  const int u = blockIdx.x, tid = threadIdx.x;
   const int n = min(max(pl.len[u], 0), pl.cap);
+  const int s0 = pl.start ? min(max(pl.start[u], 0), pl.cap - 1) : 0;
+  auto slot = [&](int i) { return s0 + i < pl.cap ? s0 + i : s0 + i - pl.cap; };
+  const size_t row0 = (size_t)u * pl.cap;
   double lk = 0.0;
   int lp = 0;
   if (n > 0) {
-    const int s0 = pl.start ? min(max(pl.start[u], 0), pl.cap - 1) : 0;
-    int sl = s0 + n - 1;
-    if (sl >= pl.cap) sl -= pl.cap;
-    const size_t i = (size_t)u * pl.cap + sl;
+    const size_t i = row0 + slot(n - 1);
     lp = pl.pos[i];
     lk = one_key(pl.log_beta != nullptr, t[u / Hkv] - lp, pl.log_beta ? pl.log_beta[i] : 0.f);
   }
-  one_plan_head(pl, u, n, true, lk, lp, one_plan_load(pl, u, threadIdx.x), threadIdx.x, 64,
-                &s_e);
+  const OneCand own = one_plan_load(pl, u, tid);
+  if (pl.fill_M < 0) {
+    one_plan_head(pl, u, n, true, lk, lp, own, tid, 64, &s_e);
+    return;
+  }
+  if (n != pl.fill_M + 1) {
+    if (tid == 0 && pl.n_evicted) pl.n_evicted[u] = n <= pl.fill_M ? 0 : -(n - pl.fill_M);
+    return;
+  }
+  double bk = own.key;
+  int bp = own.pos, bs = own.slot;
+  for (int i = tid + 64; i < pl.P; i += 64) {
+    const OneCand c = pl.cand[(size_t)u * pl.P + i];
+    one_better(bk, bp, bs, c.key, c.pos, c.slot);
+  }
+  if (tid == 0) one_better(bk, bp, bs, lk, lp, n - 1);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+    one_better(bk, bp, bs, __shfl_xor(bk, o, 64), __shfl_xor(bp, o, 64), __shfl_xor(bs, o, 64));
+  const int e = min(max(bs, 0), n - 1);
+  // the last live row moves into slot e (nothing moves when e is the last slot)
+  if (e != n - 1) {
+    const int se = slot(e), sl = slot(n - 1);
+    const int ppr = pl.row_bytes / 16;
+    for (int i = tid; i < 2 * ppr; i += 64) {
+      unsigned char* tb = (unsigned char*)(i < ppr ? pl.k : pl.v) + row0 * pl.row_bytes;
+      const int pc = i < ppr ? i : i - ppr;
+      *(u32x4*)(tb + (size_t)se * pl.row_bytes + 16 * pc) =
+          *(const u32x4*)(tb + (size_t)sl * pl.row_bytes + 16 * pc);
+    }
+    if (tid == 0) {
+      if (pl.log_beta) pl.log_beta[row0 + se] = pl.log_beta[row0 + sl];
+      pl.pos[row0 + se] = pl.pos[row0 + sl];
+    }
+  }
+  if (tid == 0) {
+    pl.len[u] = n - 1;
+    if (pl.n_evicted) pl.n_evicted[u] = 1;
+    if (pl.evicted_pos && pl.max_evict > 0) pl.evicted_pos[(size_t)u * pl.max_evict] = bp;
+  }
 }
 
 void launch_one_plan(const kvb_cache* c, const int32_t* t, const OnePlan& p, hipStream_t s) {
@@ -168,46 +212,6 @@ struct ApplyArgs {
   int32_t cap, M, max_evict, row_bytes, srow, R, SC;
 };
 
-// Fill: the head's last live row moves into the evicted slot e (nothing moves when e
-// is the last slot); len, outputs.  By nthr threads of one workgroup.
-__device__ __forceinline__ void fill_head(const ApplyArgs& a, int u, int n, int e, int s0,
-                                          int tid, int nthr) {
-  auto slot = [&](int i) { return s0 + i < a.cap ? s0 + i : s0 + i - a.cap; };
-  const size_t row0 = (size_t)u * a.cap;
-  const int se = slot(e), sl = slot(n - 1);
-  const int32_t epos = a.pos[row0 + se];
-  if (e != n - 1) {
-    const int ppr = a.row_bytes / 16;
-    for (int i = tid; i < 2 * ppr; i += nthr) {
-      unsigned char* tb = (unsigned char*)(i < ppr ? a.k : a.v) + row0 * a.row_bytes;
-      const int pc = i < ppr ? i : i - ppr;
-      *(u32x4*)(tb + (size_t)se * a.row_bytes + 16 * pc) =
-          *(const u32x4*)(tb + (size_t)sl * a.row_bytes + 16 * pc);
-    }
-    if (tid == 0) {
-      if (a.log_beta) a.log_beta[row0 + se] = a.log_beta[row0 + sl];
-      a.pos[row0 + se] = a.pos[row0 + sl];
-    }
-  }
-  if (tid == 0) {
-    a.len[u] = n - 1;
-    if (a.n_out) a.n_out[u] = 1;
-    if (a.evicted_pos && a.max_evict > 0) a.evicted_pos[(size_t)u * a.max_evict] = epos;
-  }
-}
-
-// apply with fill: one wave per head.
-__global__ __launch_bounds__(64) void one_fill(ApplyArgs a) {
-  const int u = blockIdx.x, tid = threadIdx.x;
-  const OneInfo inf = a.info[u];
-  const int n = min(max(inf.n, 0), a.cap);
-  if (n != a.M + 1) {
-    if (tid == 0 && a.n_out) a.n_out[u] = n <= a.M ? 0 : -(n - a.M);
-    return;
-  }
-  fill_head(a, u, n, min(max(inf.e, 0), n - 1), min(max(inf.s0, 0), a.cap - 1), tid, 64);
-}
-
 // Chunk c (blockIdx.x) of head u (blockIdx.y): source rows [lo, hi) move one slot
 // (up: +1, toward the last slot; down: -1).  Thread layout as in compact_move:
 // piece column tid % cols fixed per thread, rows tid / cols + q * rpp.  Chunk 0
@@ -227,11 +231,6 @@ void one_shift(ApplyArgs a) {
   const int s0 = min(max(inf.s0, 0), a.cap - 1);
   auto slot = [&](int i) { return s0 + i < a.cap ? s0 + i : s0 + i - a.cap; };
   const size_t row0 = (size_t)u * a.cap;
-  if (inf.fill) {
-    // a plan made for fill staged nothing: fill (chunk 0 alone)
-    if (c == 0) fill_head(a, u, n, e, s0, tid, kShiftThreads);
-    return;
-  }
   const bool up = a.start != nullptr && e < n - 1 - e;
   const int moved = up ? e : n - 1 - e;
   const int nch = (moved + a.R - 1) / a.R;
@@ -321,11 +320,11 @@ extern "C" size_t kv_evict_one_workspace(const kvb_cache* cache, int32_t num_spl
 
 extern "C" int32_t kv_evict_one_apply(const kvb_cache* cache, const int32_t* t, int32_t M,
                                       int32_t* evicted_pos, int32_t max_evict,
-                                      int32_t* n_evicted, int32_t fill, void* ws,
-                                      size_t ws_bytes, void* stream) {
+                                      int32_t* n_evicted, void* ws, size_t ws_bytes,
+                                      void* stream) {
   int32_t st = check_cache(cache, true);
   if (st) return st;
-  if (!t || M < 0 || max_evict < 0 || (fill != 0 && fill != 1)) return KVB_EINVAL;
+  if (!t || M < 0 || max_evict < 0) return KVB_EINVAL;
   const OneLayout L = one_layout(cache);
   const size_t U = (size_t)cache->B * cache->Hkv;
   if (U > 65535) return KVB_EUNSUPPORTED;
@@ -351,9 +350,6 @@ extern "C" int32_t kv_evict_one_apply(const kvb_cache* cache, const int32_t* t, 
   a.R = L.R;
   a.SC = L.SC;
   TraceScope tr(kTrOneShift, s);
-  if (fill)
-    hipLaunchKernelGGL(one_fill, dim3((unsigned)U), dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(one_shift, dim3(L.X, (unsigned)U), dim3(kShiftThreads), 0, s, a);
+  hipLaunchKernelGGL(one_shift, dim3(L.X, (unsigned)U), dim3(kShiftThreads), 0, s, a);
   return launch_status();
 }

@@ -294,65 +294,76 @@ int32_t kv_evict_one(const kvb_cache* cache, const int32_t* t, int32_t M, int32_
                      int32_t max_evict, int32_t* n_evicted, void* stream);
 
 /*
- * The steady state of bounded decoding in two calls, with the eviction's selection
- * folded into the attention ([TRIM] 2.1 and 2.2, inference: one token in, the
- * lowest-retention token out).
+ * The steady state of bounded decoding, with the eviction's selection folded into
+ * the attention ([TRIM] 2.1 and 2.2, inference: one token in, the lowest-retention
+ * token out).  The attention's KV splits find, per head, the attended slot with the
+ * lowest (kappa, position) (kappa as for kv_evict_to_budget, at t[b]) from the log
+ * beta and pos values they load for the retention bias anyway; the merge reduces
+ * them and the decode token to the head's evicted slot (ties: lower position first).
+ * The attention itself is kv_attn_decode's (same kernels, results bit for bit).
  *
- * kv_attn_decode_plan_one is kv_attn_decode (same arguments, same kernels and
- * results bit for bit, decode token appended the same way) that also plans, per
- * head, the eviction of one token: its KV splits find the attended slot with the
- * lowest (kappa, slot) (kappa as for kv_evict_to_budget, at t[b]) from the log beta
- * and pos values they load for the retention bias anyway, and its merge reduces
- * them (and the appended decode token) to the head's evicted slot (ties: lower
- * position first, as for kv_evict_to_budget), fixes the direction of the shift
- * and copies into ws_evict the few rows the shift cannot read in place.  It writes
- * nothing else of the cache than kv_attn_decode does.
+ * kv_attn_decode_evict_one: one call.  Attention with the decode token as
+ * kv_attn_decode (k_new may be NULL), then every head with n = M + 1 live tokens
+ * (the decode token included) evicts its lowest token, and the decode token is
+ * written into the evicted slot instead of being appended (not written at all when
+ * it is the evicted token itself; without a decode token the head's last live row
+ * moves into the evicted slot): one row per head, len ends at M.  The live tokens
+ * are those kv_evict_to_budget keeps; the slots no longer hold them in position
+ * order.  The eviction rule compares positions, not slots, so a cache kept this way
+ * stays correct for kv_attn_decode, kv_attn_decode_evict_one and kv_append (which
+ * need no order); kv_evict_to_budget, kv_evict_plan/apply, kv_evict_one,
+ * kv_attn_decode_plan_one, kv_erase_ranges and kv_latent_absorb need position order
+ * (kv_check_cache reports KVB_CHECK_POS_ORDER).  Positions must stay distinct.
+ * Heads with n <= M get the plain append (n_evicted 0); heads with n > M + 1 too
+ * (n_evicted -(n - M)).
+ *   M            budget, >= 0
+ *   evicted_pos  [B][Hkv][max_evict] int32 or NULL: the evicted position (first entry)
+ *   n_evicted    [B][Hkv] int32 or NULL
+ *   ws           kv_attn_decode_evict_one_workspace(cache, Hq, num_splits) bytes
+ *                (kv_attn_decode's workspace followed by the candidates)
  *
- * kv_evict_one_apply then carries out the plan in every head with n = M + 1 live
- * tokens (n as planned); len becomes M.  Heads with n <= M are left alone
- * (n_evicted 0); heads with n > M + 1 too (n_evicted -(n - M)).  One launch.
- *   fill = 0  the same evicted slot, direction and layout, bit for bit, as
- *             kv_evict_one / kv_evict_to_budget: with a start array the rows before
- *             the evicted slot move up one slot (start + 1, mod cap) when there are
- *             fewer of them than rows after it, otherwise the rows after it move
- *             down one slot (many workgroups per head).
- *   fill = 1  the head's last live row (the decode token, when the attention call
- *             appended one) moves into the evicted slot: one row per head, and the
- *             live slots hold the same tokens as with fill = 0, no longer in
- *             position order.  The eviction rule compares positions, not slots, so
- *             a cache kept this way stays correct for kv_attn_decode,
- *             kv_attn_decode_plan_one, kv_append and kv_evict_one_apply; the other
- *             eviction, erase and latent-memory calls need position order (which
- *             kv_check_cache reports as KVB_CHECK_POS_ORDER).  Positions must stay
- *             distinct.
- *
- * Between the two calls the cache must not be written; apply may run on another
- * stream once the attention call's work is complete, e.g. beside the next layer's
- * attention.  Using a ws_evict that no kv_attn_decode_plan_one call on this cache
- * filled gives unspecified evictions (every access stays inside the cache and the
- * workspace).
- *   num_splits  as kv_attn_decode (0 = kv_attn_decode_splits())
- *   fill        0 or 1, see above.  The plan made with fill = 0 also stages the rows
- *               the shift needs; one made with fill = 1 does not (less work in the
- *               attention's merge), so apply fills when either call passes fill = 1
- *               and shifts only when both pass 0.  Pass the same value to both.
- *   ws_evict    kv_evict_one_workspace(cache, num_splits) bytes, one per cache
- *               whose apply may still be pending
+ * kv_attn_decode_plan_one + kv_evict_one_apply: the order-keeping form, in two
+ * calls.  kv_attn_decode_plan_one is kv_attn_decode that also plans every head's
+ * eviction into ws_evict: the evicted slot, the direction of the shift, and copies
+ * of the few rows the shift cannot read in place; it writes nothing else of the
+ * cache than kv_attn_decode does.  kv_evict_one_apply then carries out the plan in
+ * every head with n = M + 1 live tokens (n as planned), with the same evicted slot,
+ * direction and layout, bit for bit, as kv_evict_one / kv_evict_to_budget: with a
+ * start array the rows before the evicted slot move up one slot (start + 1, mod
+ * cap) when there are fewer of them than rows after it, otherwise the rows after it
+ * move down one slot; len becomes M.  Heads with n <= M are left alone (n_evicted
+ * 0); heads with n > M + 1 too (n_evicted -(n - M)).  One launch, many workgroups
+ * per head.  Between the two calls the cache must not be written; apply may run on
+ * another stream once the attention call's work is complete, e.g. beside the next
+ * layer's attention.  Using a ws_evict that no kv_attn_decode_plan_one call on this
+ * cache filled gives unspecified evictions (every access stays inside the cache and
+ * the workspace).
+ *   ws_evict    kv_evict_one_workspace(cache, num_splits) bytes, one per cache whose
+ *               apply may still be pending
  *   t, M, evicted_pos, max_evict, n_evicted as kv_evict_one (apply; at most one
  *   position is written per head).
- * Supported for B * Hkv <= 65535.
+ *
+ * Both forms: num_splits as kv_attn_decode (0 = kv_attn_decode_splits()); other
+ * arguments as kv_attn_decode; supported for B * Hkv <= 65535.
  */
+size_t kv_attn_decode_evict_one_workspace(const kvb_cache* cache, int32_t Hq,
+                                          int32_t num_splits);
+int32_t kv_attn_decode_evict_one(const kvb_cache* cache, const void* q, int32_t Hq,
+                                 const int32_t* t, float scale, const void* k_new,
+                                 const void* v_new, const float* log_beta_new, int32_t M,
+                                 int32_t num_splits, float* out, float* lse,
+                                 int32_t* evicted_pos, int32_t max_evict, int32_t* n_evicted,
+                                 void* ws, size_t ws_bytes, void* stream);
 size_t kv_evict_one_workspace(const kvb_cache* cache, int32_t num_splits);
 int32_t kv_attn_decode_plan_one(const kvb_cache* cache, const void* q, int32_t Hq,
                                 const int32_t* t, float scale, const void* k_new,
                                 const void* v_new, const float* log_beta_new,
-                                int32_t num_splits, int32_t fill, float* out, float* lse,
-                                void* ws, size_t ws_bytes, void* ws_evict,
-                                size_t ws_evict_bytes, void* stream);
+                                int32_t num_splits, float* out, float* lse, void* ws,
+                                size_t ws_bytes, void* ws_evict, size_t ws_evict_bytes,
+                                void* stream);
 int32_t kv_evict_one_apply(const kvb_cache* cache, const int32_t* t, int32_t M,
                            int32_t* evicted_pos, int32_t max_evict, int32_t* n_evicted,
-                           int32_t fill, void* ws_evict, size_t ws_evict_bytes,
-                           void* stream);
+                           void* ws_evict, size_t ws_evict_bytes, void* stream);
 
 /*
  * Attention and the planned compaction in one pass over the cache ([TRIM] 2.1 and

@@ -368,25 +368,40 @@ def test_plan_one_entries_reject_arguments_before_launch():
     assert L.kv_evict_one_workspace(None, 0) == 0
     wsa = L.kv_attn_decode_workspace(ctypes.byref(good), 8, 0)
 
-    def plan(ws_e=P(8192), ws_e_bytes=need, splits=0, c=good, fill=0):
+    def plan(ws_e=P(8192), ws_e_bytes=need, splits=0, c=good):
         return L.kv_attn_decode_plan_one(ctypes.byref(c), P(64), 8, P(72), 0.0, None, None,
-                                         None, splits, fill, P(80), P(88), P(4096), wsa, ws_e,
+                                         None, splits, P(80), P(88), P(4096), wsa, ws_e,
                                          ws_e_bytes, None)
     assert plan(ws_e=None) == -4
     assert plan(ws_e_bytes=need - 1) == -4
     assert plan(splits=5000) == -1
-    assert plan(fill=2) == -1
     assert plan(c=_desc(B=300, Hkv=256)) == -2     # B * Hkv above 65535
 
-    def apply(t=P(72), M=5, ws=P(8192), ws_bytes=need, me=0, fill=0):
-        return L.kv_evict_one_apply(ctypes.byref(good), t, M, None, me, None, fill, ws,
-                                    ws_bytes, None)
+    def apply(t=P(72), M=5, ws=P(8192), ws_bytes=need, me=0):
+        return L.kv_evict_one_apply(ctypes.byref(good), t, M, None, me, None, ws, ws_bytes,
+                                    None)
     assert apply(t=None) == -1
     assert apply(M=-1) == -1
     assert apply(me=-1) == -1
-    assert apply(fill=3) == -1
     assert apply(ws=None) == -4
     assert apply(ws_bytes=300) == -4
+    need1 = L.kv_attn_decode_evict_one_workspace(ctypes.byref(good), 8, 0)
+    assert need1 > wsa
+    assert L.kv_attn_decode_evict_one_workspace(ctypes.byref(good), 7, 0) == 0   # Hq % Hkv
+
+    def one(M=5, splits=0, ws=P(4096), ws_bytes=need1, me=0, c=good):
+        # q, Hq, t, scale, k_new, v_new, log_beta_new, M, num_splits, out, lse,
+        # evicted_pos, max_evict, n_evicted, ws, ws_bytes, stream
+        return L.kv_attn_decode_evict_one(ctypes.byref(c), P(64), 8, P(72), 0.0, None, None,
+                                          None, M, splits, P(80), P(88), None, me, None, ws,
+                                          ws_bytes, None)
+    assert one(M=-1) == -1
+    assert one(me=-2) == -1
+    assert one(splits=4097) == -1
+    assert one(ws=None) == -4
+    assert one(ws_bytes=need1 - 1) == -4
+    assert one(c=_desc(B=300, Hkv=256)) == -2
     if not _has_gpu():
         assert plan() == -5
         assert apply() == -5
+        assert one() == -5

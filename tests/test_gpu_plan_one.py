@@ -231,26 +231,28 @@ def _by_position(c: kvb.KVCache):
     return out
 
 
-@pytest.mark.parametrize("dtype,D,Hq", [("bf16", 128, 24), ("bf16", 64, 12), ("f32", 64, 12)])
+@pytest.mark.parametrize("dtype,D,Hq", [("bf16", 128, 24), ("bf16", 128, 48), ("bf16", 64, 12),
+                                        ("f32", 64, 12)])
 @pytest.mark.parametrize("ring", [True, False])
-@pytest.mark.parametrize("P", [0, 7])
-@pytest.mark.parametrize("apply_fill", [True, False])
-def test_plan_one_fill_equals_evict_one(dtype, D, Hq, ring, P, apply_fill):
-    """fill = 1: the decode token takes the evicted slot.  Against kv_attn_decode +
-    kv_evict_one on a copy: out and lse bit for bit, n_evicted, the evicted
-    positions and len equal, start unchanged, and the live rows equal as a set
-    (bit for bit, sorted by position)."""
+@pytest.mark.parametrize("append", [True, False])
+@pytest.mark.parametrize("P", [0, 7, 100])
+def test_evict_one_fill_equals_evict_one(dtype, D, Hq, ring, append, P):
+    """kv_attn_decode_evict_one: the decode token (or, without one, the last live row)
+    takes the evicted slot.  Against kv_attn_decode + kv_evict_one on a copy: out and
+    lse bit for bit, n_evicted, the evicted positions and len equal, start unchanged,
+    and the live rows equal as a set (bit for bit, sorted by position); 100 splits
+    take the merge for many splits and the separate eviction kernel."""
     B, H, M = 2, 6, 300
-    n = M
+    n = M if append else M + 1          # cached slots before the call
     cap = M + 24
     # rows (distinct positions) for the longest head, the others cut to n
-    d = _dense(17 + D + Hq, B, H, n + 2, cap, D, dtype=dtype)
+    d = _dense(17 + D + Hq, B, H, n + 3, cap, D, dtype=dtype)
     d["len"][:] = n
     _special_keys(d, n, M)
-    d["len"][1, 1] = M - 1
+    d["len"][1, 1] = M - (1 if append else 0)        # at M after the call
     d["len"][1, 2] = M - 9
-    d["len"][1, 3] = n + 2
-    t = np.array([n + 3, n + 11], np.int32)
+    d["len"][1, 3] = n + 2                           # further over after the call
+    t = np.array([n + 3 + 3, n + 11], np.int32)
     rng = np.random.default_rng(D + Hq + 1)
     starts = rng.integers(0, cap, (B, H)) if ring else np.zeros((B, H), np.int64)
     c1 = _placed(d, starts, cap, 5)
@@ -258,19 +260,19 @@ def test_plan_one_fill_equals_evict_one(dtype, D, Hq, ring, P, apply_fill):
         c1 = kvb.KVCache(c1.k, c1.v, c1.log_beta, c1.pos, c1.length)
     c2 = _copy_cache(c1)
     q = rng.standard_normal((B, Hq, D))
-    kn = rng.standard_normal((B, H, D))
-    vn = rng.standard_normal((B, H, D))
-    q, kn, vn = ((synth.bf16_bits(x) if dtype == "bf16" else x.astype(np.float32))
-                 for x in (q, kn, vn))
-    lbn = np.log(rng.uniform(0.2, 1.0, (B, H))).astype(np.float32)
-    say("plan_one fill", dtype, D, Hq, "ring", ring, "P", P)
-    ws_e = torch.empty(kvb.kv_evict_one_workspace(c1, P), dtype=torch.uint8, device="cuda")
-    o1, l1 = kvb.kv_attn_decode_plan_one(c1, to_dev(q), to_dev(t), ws_e, k_new=to_dev(kn),
-                                         v_new=to_dev(vn), log_beta_new=to_dev(lbn),
-                                         num_splits=P, fill=True)
+    q = synth.bf16_bits(q) if dtype == "bf16" else q.astype(np.float32)
+    kn = vn = lbn = None
+    if append:
+        kn = rng.standard_normal((B, H, D))
+        vn = rng.standard_normal((B, H, D))
+        kn, vn = ((synth.bf16_bits(x) if dtype == "bf16" else x.astype(np.float32))
+                  for x in (kn, vn))
+        lbn = np.log(rng.uniform(0.2, 1.0, (B, H))).astype(np.float32)
+    say("evict_one fill", dtype, D, Hq, "ring", ring, "append", append, "P", P)
     ev1 = torch.full((B, H, 2), -7, dtype=torch.int32, device="cuda")
-    # apply_fill False: a fill plan is still carried out as a fill
-    n1 = kvb.kv_evict_one_apply(c1, to_dev(t), M, ws_e, evicted_pos=ev1, fill=apply_fill)
+    o1, l1, n1 = kvb.kv_attn_decode_evict_one(c1, to_dev(q), to_dev(t), M, k_new=to_dev(kn),
+                                              v_new=to_dev(vn), log_beta_new=to_dev(lbn),
+                                              num_splits=P, evicted_pos=ev1)
     o2, l2 = kvb.kv_attn_decode(c2, to_dev(q), to_dev(t), k_new=to_dev(kn), v_new=to_dev(vn),
                                 log_beta_new=to_dev(lbn), num_splits=P)
     ev2 = torch.full((B, H, 2), -7, dtype=torch.int32, device="cuda")
@@ -279,14 +281,16 @@ def test_plan_one_fill_equals_evict_one(dtype, D, Hq, ring, P, apply_fill):
     assert torch.equal(o1, o2) and torch.equal(l1, l2), "attention bit for bit"
     assert torch.equal(n1, n2), "n_evicted"
     n1h = to_host(n1)
+    assert n1h[1, 3] == -3 and n1h[1, 1] == 0 and n1h[1, 2] == 0
     assert np.array_equal(to_host(ev1)[n1h == 1][:, 0], to_host(ev2)[n1h == 1][:, 0])
+    assert np.all(to_host(ev1)[n1h != 1] == -7)
     assert torch.equal(c1.length, c2.length), "len"
     if ring:
         assert np.array_equal(to_host(c1.start), starts), "fill keeps every start"
     # the ordered result of kv_evict_one, sorted the same way, equals fill's
     a, b2 = _by_position(c1), _by_position(c2)
+    ln = to_host(c1.length)
     for name in ("k", "v", "pos", "log_beta"):
-        ln = to_host(c1.length)
         for bb in range(B):
             for g in range(H):
                 m = int(ln[bb, g])
@@ -294,12 +298,12 @@ def test_plan_one_fill_equals_evict_one(dtype, D, Hq, ring, P, apply_fill):
 
 
 @pytest.mark.parametrize("ring", [True, False])
-def test_plan_one_fill_steady_loop(ring):
-    """Decode steps at budget M with fill: the slots drift out of position order, so
-    ties among equal keys (one head with every log beta 0, one where the decode
-    tokens carry beta = 1) must be broken by position, not slot.  Each step's output
-    within 2e-3 of the oracle's and the live rows, sorted by position, equal to the
-    oracle's layout after every step."""
+def test_evict_one_fill_steady_loop(ring):
+    """Decode steps at budget M with kv_attn_decode_evict_one: the slots drift out of
+    position order, so ties among equal keys (one head with every log beta 0, one
+    where the decode tokens carry beta = 1) must be broken by position, not slot.
+    Each step's output within 2e-3 of the oracle's and the live rows, sorted by
+    position, equal to the oracle's layout after every step."""
     B, H, Hq, D, M = 2, 3, 12, 128, 200
     cap = M + 4
     d = _dense(47, B, H, M, cap, D)
@@ -309,7 +313,6 @@ def test_plan_one_fill_steady_loop(ring):
                     start=torch.zeros((B, H), dtype=torch.int32, device="cuda") if ring else None)
     ref = oracle.Cache.from_arrays(d)
     rng = np.random.default_rng(9)
-    ws_e = torch.empty(kvb.kv_evict_one_workspace(c, 0), dtype=torch.uint8, device="cuda")
     for s in range(40):
         t = np.full(B, M + 3 * s, np.int32)
         kn = synth.bf16_bits(rng.standard_normal((B, H, D)))
@@ -318,10 +321,8 @@ def test_plan_one_fill_steady_loop(ring):
         lbn[0, 0] = 0.0
         lbn[1, 2] = 0.0
         q = synth.bf16_bits(rng.standard_normal((B, Hq, D)))
-        td = to_dev(t)
-        o, l = kvb.kv_attn_decode_plan_one(c, to_dev(q), td, ws_e, k_new=to_dev(kn),
-                                           v_new=to_dev(vn), log_beta_new=to_dev(lbn), fill=True)
-        ne = kvb.kv_evict_one_apply(c, td, M, ws_e, fill=True)
+        o, l, ne = kvb.kv_attn_decode_evict_one(c, to_dev(q), to_dev(t), M, k_new=to_dev(kn),
+                                                v_new=to_dev(vn), log_beta_new=to_dev(lbn))
         torch.cuda.synchronize()
         assert bool((ne == 1).all()), s
         oracle.append_tokens(ref, kn, vn, lbn, t)
@@ -333,3 +334,37 @@ def test_plan_one_fill_steady_loop(ring):
     pos = to_host(c.pos)
     assert not all(np.all(np.diff(pos[b, g, :M]) > 0) for b in range(B) for g in range(H)), \
         "slots should be out of position order after fill steps"
+
+
+def test_evict_one_fill_full_shape_steps():
+    """kv_attn_decode_evict_one at the 32K workload's model shape (batch 16, 32 query /
+    8 KV heads, D = 128, M = 4096): three steps against kv_attn_decode + kv_evict_one
+    on a copy: the first step's attention bit for bit (same layout), the later ones
+    within 1e-4 (same tokens, other slots), every head's live rows equal as a set."""
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    M = w.budget
+    dc = synth.device_cache(w, 0, n=M, cap=M + 32)
+    B, H = w.batch, w.hkv
+    c1 = kvb.KVCache.from_dict(dc)
+    c2 = _copy_cache(c1)
+    q, kn, vn, lbn = synth.device_queries(w, 0)
+    for s in range(3):
+        t = torch.full((B,), M + s, dtype=torch.int32, device="cuda")
+        say("fill full shape step", s)
+        o1, l1, n1 = kvb.kv_attn_decode_evict_one(c1, q, t, M, k_new=kn, v_new=vn,
+                                                  log_beta_new=lbn, num_splits=16)
+        o2, l2 = kvb.kv_attn_decode(c2, q, t, k_new=kn, v_new=vn, log_beta_new=lbn,
+                                    num_splits=16)
+        n2 = kvb.kv_evict_one(c2, t, M)
+        torch.cuda.synchronize()
+        if s == 0:
+            assert torch.equal(o1, o2) and torch.equal(l1, l2), s
+        else:
+            # the same tokens in other slots: the sums run in another order
+            den = o2.abs().amax(dim=-1)
+            assert bool(((o1 - o2).abs().amax(dim=-1) <= 1e-4 * den).all()), s
+            assert bool(((l1 - l2).abs() <= 1e-4).all()), s
+        assert bool((n1 == 1).all()) and torch.equal(n1, n2), s
+        a, b2 = _by_position(c1), _by_position(c2)
+        for name in ("k", "v", "pos", "log_beta"):
+            assert np.array_equal(a[name][:, :, :M], b2[name][:, :, :M]), (s, name)
