@@ -379,7 +379,8 @@ def steady_bench(args):
         "bytes_per_step": step_b, "kv_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "attn_split_pipe128<G=4>" +
-                     (" with eviction candidates" if plan1 else "") + " (M + 1 tokens)",
+                     (" with eviction candidates" if plan1 or fill else "") +
+                     " (M + 1 tokens)",
                      "achieved": round(attn_b / (attn_us * 1e-6) / 1e9, 1) if attn_us else None,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_b / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
