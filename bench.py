@@ -32,15 +32,31 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_qwen3_8b_32k_traffic.j
 STEADY_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_steady_m4096_traffic.json")
 
 
+ATTN_SRC = os.path.join(ROOT, "bounded_decode_attention_amd", "csrc", "attn_decode.hip")
+KERNEL_BEGIN = "// ------------------------------------------------------------------ MFMA split"
+KERNEL_END = "// The splits plus the ASM lookup's candidate scan in one launch"
+
+
+def kernel_digest(path=ATTN_SRC):
+    """Digest of the split kernels' device code (the attention source between the
+    two markers: the MFMA split kernels, the pipelined kernel and its tile
+    helpers), so that host-side edits elsewhere in the file keep recorded counters
+    valid and any edit of the kernels themselves voids them."""
+    text = open(path).read()
+    i, j = text.find(KERNEL_BEGIN), text.find(KERNEL_END)
+    if i < 0 or j < i:
+        return None
+    return hashlib.sha256(text[i:j].encode()).hexdigest()[:16]
+
+
 def recorded_traffic(path, **match):
     """HBM bytes per launch recorded from FETCH_SIZE / WRITE_SIZE counters, if they
-    were taken on the attention source as it is now and in the same configuration;
-    else None."""
+    were taken on the split kernels' code as it is now and in the same
+    configuration; else None."""
     if not os.path.exists(path):
         return None
     tr = json.load(open(path))
-    src = os.path.join(ROOT, "bounded_decode_attention_amd", "csrc", "attn_decode.hip")
-    if tr.get("source_sha") != source_digest(src):
+    if tr.get("kernel_sha") != kernel_digest():
         return None
     if any(tr.get(k) != v for k, v in match.items()):
         return None
@@ -55,10 +71,6 @@ def algorithmic_bytes(w, n, moved_rows):
     attn = U * n * 2 * D * e + U * n * 8 + w.batch * w.hq * D * e + w.batch * w.hq * (D + 1) * 4
     moves = moved_rows * 2 * (2 * D * e + 8)
     return attn, moves
-
-
-def source_digest(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
 def cpu_baseline(w, host_units, t, M, budget_s=12.0, gpu_res=None):
@@ -677,7 +689,9 @@ def asm_step_bench(args):
                    "head_dim": w.head_dim, "tokens": w.ctx, "codebook": w.codebook,
                    "layers": L, "entry": "kv_attn_decode + asm_lookup_merge" if two_calls
                    else "kv_attn_decode_asm", "launch": "graph" if graph is not None
-                   else "eager", "kv_splits": P or kvb.kv_attn_decode_splits(kvs[0], w.hq)},
+                   else "eager", "kv_splits": P or (
+                       kvb.kv_attn_decode_splits(kvs[0], w.hq) if two_calls
+                       else kvb.kv_attn_decode_asm_splits(kvs[0], w.hq, w.codebook))},
         "bytes_per_step": L * (attn_b + look_b),
         "gbps": round(L * (attn_b + look_b) / (ms * 1e-3) / 1e9, 1),
         "attn_split_us": round(split_ms * 1000, 2),

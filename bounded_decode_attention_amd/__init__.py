@@ -21,7 +21,8 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    asm_prefix_states_workspace,
                    asm_lookup_merge_hier_workspace, asm_lookup_merge_workspace,
                    NOALLOC_SCRATCH_BYTES, kv_append, kv_attn_decode, kv_attn_decode_asm,
-                   kv_attn_decode_asm_workspace, kv_attn_decode_noalloc, workspace_status,
+                   kv_attn_decode_asm_workspace, kv_attn_decode_asm_splits,
+                   kv_attn_decode_noalloc, workspace_status,
                    kv_check_cache, CHECK_BITS,
                    kv_attn_decode_compact, kv_attn_decode_splits, kv_attn_decode_workspace,
                    kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_one,
@@ -40,7 +41,7 @@ __all__ = [
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_evict_one", "kv_attn_decode_compact",
     "kv_attn_decode_plan_one", "kv_evict_one_apply", "kv_evict_one_workspace",
     "kv_attn_decode_evict_one", "kv_attn_decode_evict_one_workspace",
-    "kv_attn_decode_asm", "kv_attn_decode_asm_workspace",
+    "kv_attn_decode_asm", "kv_attn_decode_asm_workspace", "kv_attn_decode_asm_splits",
     "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",
     "kv_latent_absorb", "kv_latent_absorb_workspace", "kv_latent_read",
     "asm_prefix_states", "asm_kmeans", "asm_aggregate_states", "asm_build_memory",

@@ -54,6 +54,7 @@ def library():
             "kv_attn_decode_noalloc": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, P]),
             "kv_check_cache": (I32, [CP, P, P, P, I32, P, P]),
             "kv_attn_decode_asm_workspace": (SZ, [CP, I32, I32, I32]),
+            "kv_attn_decode_asm_splits": (I32, [CP, I32, I32]),
             "kv_attn_decode_asm": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, I32, P, P, P,
                                          P, SZ, P]),
             "kv_evict_to_budget": (I32, [CP, P, I32, P, I32, P, P, SZ, P]),
@@ -278,6 +279,10 @@ def kv_attn_decode_noalloc(cache: KVCache, q, t, out, lse, scale: float = 0.0, k
                        f"{NOALLOC_SCRATCH_BYTES >> 20} MiB device scratch")
     _check(st, "kv_attn_decode_noalloc")
     return out, lse
+
+
+def kv_attn_decode_asm_splits(cache: KVCache, Hq: int, K: int) -> int:
+    return int(library().kv_attn_decode_asm_splits(cache.desc, int(Hq), int(K)))
 
 
 def kv_attn_decode_asm_workspace(cache: KVCache, Hq: int, num_splits: int, K: int) -> int:

@@ -1743,10 +1743,39 @@ extern "C" int32_t kv_attn_decode_noalloc(const kvb_cache* cache, const void* q,
                           status);
 }
 
+// Default split count of kv_attn_decode_asm: where the codebook scan rides in the
+// split launch (bf16, D = 128), its tasks take wave slots of the same round, so the
+// splits get at most what one round of resident waves (2 per SIMD on 256 CUs)
+// leaves, rounded down to a power of two, never more than kv_attn_decode's default.
+// On the ASM workload (512 scan tasks, 256 heads of 2049 tokens): 4 splits per head
+// 507 steps/s, 5: 498, 6 (one full round): 496, 8 (kv_attn_decode's default): 479.
+static int32_t asm_splits(const kvb_cache* c, int32_t Hq, int32_t K) {
+  const int32_t P = auto_splits(c);
+  const int G = Hq / c->Hkv;
+  if (c->dtype != KVB_BF16 || c->D != 128 || (G != 1 && G != 2 && G != 4 && G != 8)) return P;
+  const long long tasks = scan_dims(c->B, Hq, c->Hkv, K).tasks;
+  const long long units = (long long)c->B * c->Hkv;
+  if (tasks >= 2048) return P;
+  long long left = (2048 - tasks) / units;
+  if (left > P) left = P;
+  int32_t p2 = 1;
+  while (2LL * p2 <= left) p2 *= 2;
+  return p2;
+}
+
+extern "C" int32_t kv_attn_decode_asm_splits(const kvb_cache* cache, int32_t Hq, int32_t K) {
+  if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1 || Hq < 1 ||
+      Hq % cache->Hkv || K < 1)
+    return 0;
+  return asm_splits(cache, Hq, K);
+}
+
 extern "C" size_t kv_attn_decode_asm_workspace(const kvb_cache* cache, int32_t Hq,
                                                int32_t num_splits, int32_t K) {
+  if (!cache || cache->Hkv < 1 || Hq < 1 || Hq % cache->Hkv || K < 1) return 0;
+  if (num_splits == 0 && cache->B >= 1 && cache->cap >= 1) num_splits = asm_splits(cache, Hq, K);
   const size_t wa = kv_attn_decode_workspace(cache, Hq, num_splits);
-  if (!wa || K < 1 || cache->Hkv < 1 || Hq % cache->Hkv) return 0;
+  if (!wa) return 0;
   const AsmScanArgs c = scan_dims(cache->B, Hq, cache->Hkv, K);
   const size_t n = (size_t)cache->Hkv * c.QB * 16 * c.KC;
   return align_up(wa, 256) + 2 * align_up(n * 4, 256);
@@ -1766,7 +1795,7 @@ extern "C" int32_t kv_attn_decode_asm(const kvb_cache* cache, const void* q, int
   if (K < 1 || K >= (1 << 24) || Hq < 1 || Hq % cache->Hkv) return KVB_EINVAL;
   if ((long long)cache->B * (Hq / cache->Hkv) > 65536) return KVB_EINVAL;
   if (num_splits < 0 || num_splits > 4096) return KVB_EINVAL;
-  const int P = num_splits > 0 ? num_splits : auto_splits(cache);
+  const int P = num_splits > 0 ? num_splits : asm_splits(cache, Hq, K);
   const size_t need = kv_attn_decode_asm_workspace(cache, Hq, P, K);
   if (!ws || ws_bytes < need) return KVB_EWORKSPACE;
   if ((st = check_device())) return st;

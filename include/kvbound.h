@@ -438,11 +438,17 @@ int32_t asm_lookup_merge(const void* q, int32_t B, int32_t Hq, int32_t Hkv, int3
  * arithmetic); out and lse hold the merged state, idx the chosen entries.
  *   Arguments as kv_attn_decode (bf16 cache, D 128 or 64) and asm_lookup_merge
  *   (centroids, abar [Hkv][K][D] bf16; log_zbar [Hkv][K] f32; 1 <= K < 2^24).
+ *   num_splits 0: kv_attn_decode_asm_splits(): for D = 128 at most what one round
+ *              of resident waves (2048) leaves beside the scan's tasks, per head,
+ *              rounded down to a power of two; otherwise as kv_attn_decode.
  *   ws         workspace of kv_attn_decode_asm_workspace(cache, Hq, num_splits, K)
  *              bytes; the attention's part (and status word) comes first.
  */
 size_t kv_attn_decode_asm_workspace(const kvb_cache* cache, int32_t Hq, int32_t num_splits,
                                     int32_t K);
+/* Number of KV splits kv_attn_decode_asm uses for num_splits == 0 (host only; 0 for
+ * invalid arguments). */
+int32_t kv_attn_decode_asm_splits(const kvb_cache* cache, int32_t Hq, int32_t K);
 int32_t kv_attn_decode_asm(const kvb_cache* cache, const void* q, int32_t Hq, const int32_t* t,
                            float scale, const void* k_new, const void* v_new,
                            const float* log_beta_new, int32_t num_splits,

@@ -292,6 +292,13 @@ def test_fused_asm_entry_rejects_arguments_before_launch():
     assert L.kv_attn_decode_asm(ctypes.byref(_desc(dtype=0, D=64)), *args()) == -2  # f32 cache
     assert L.kv_attn_decode_asm(ctypes.byref(good), *args(ws_bytes=need - 1)) == -4
     assert L.kv_attn_decode_asm_workspace(ctypes.byref(good), 7, 0, 4096) == 0    # Hq % Hkv
+    # default splits: what one round of 2048 waves leaves beside the scan's tasks
+    asm_c = _desc(B=32, Hkv=8, cap=2080)
+    assert L.kv_attn_decode_splits(ctypes.byref(asm_c), 32) == 8
+    assert L.kv_attn_decode_asm_splits(ctypes.byref(asm_c), 32, 4096) == 4
+    assert L.kv_attn_decode_asm_splits(ctypes.byref(asm_c), 31, 4096) == 0
+    assert L.kv_attn_decode_asm_splits(ctypes.byref(_desc(B=32, Hkv=8, cap=2080, D=64)), 32,
+                                       4096) == 8
 
 
 @needs_lib

@@ -107,8 +107,10 @@ def test_asm_small_edges():
 
 def _fused_vs_two_calls(c_two, c_fused, q, t, cent, abar, lz, kn=None, vn=None, splits=0):
     """kv_attn_decode + asm_lookup_merge on one cache, kv_attn_decode_asm on an
-    identical one: every output bit-equal, and the caches (appended rows) too."""
-    so, sl = kvb.kv_attn_decode(c_two, q, t, k_new=kn, v_new=vn, num_splits=splits)
+    identical one: every output bit-equal, and the caches (appended rows) too.  With
+    splits 0 the fused entry takes its own default, which the two calls are given."""
+    two = splits or kvb.kv_attn_decode_asm_splits(c_two, q.shape[1], cent.shape[1])
+    so, sl = kvb.kv_attn_decode(c_two, q, t, k_new=kn, v_new=vn, num_splits=two)
     so_h, sl_h = to_host(so), to_host(sl)
     out2, lse2, idx2 = kvb.asm_lookup_merge(q, cent, abar, lz, so, sl)
     out1, lse1, idx1 = kvb.kv_attn_decode_asm(c_fused, q, t, cent, abar, lz, k_new=kn, v_new=vn,
