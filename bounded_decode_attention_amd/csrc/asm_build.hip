@@ -50,7 +50,9 @@ struct PrefixArgs {
   const uint16_t* k;   // [H][L][D]
   const uint16_t* v;   // [H][L][D]
   uint16_t* vt;        // [H][C][D][Lc]: V^T per chunk in fp16, keys interleaved (vt_prepare)
-  int32_t* status;     // workspace status word (KVB_ERANGE if a value saturated)
+  uint32_t* rmax;      // [H][C][Lc / 64][D]: max |v| per 64-key tile and dimension (bits)
+  int32_t* sexp;       // [H][C][D]: V^T row d of the chunk holds v * 2^-sexp (vt_prepare)
+  int32_t* status;     // workspace status word (KVB_ERANGE for a non-finite v)
   float* out;          // [C][H][N][D]
   float* out_lse;      // [C][H][N]
   int32_t H, N, L, C, csize, Lc;
@@ -65,22 +67,76 @@ __device__ __forceinline__ int vt_position(int kk) {
   return (kk & ~31) + 8 * g + j;
 }
 
+// Per (KV head, chunk, 64-key tile): max |v| of every dimension over the tile's keys
+// (float bits, which order like the values for |v|; NaN above +inf).
+template <int D>
+__global__ __launch_bounds__(256) void vt_range(PrefixArgs p) {
+  __shared__ uint32_t part[256];
+  const int tiles = p.Lc / 64;
+  const int tt = blockIdx.x % tiles, hc = blockIdx.x / tiles;
+  const int c = hc % p.C, h = hc / p.C;
+  const int c0 = c * p.csize, c1 = min(p.L, c0 + p.csize);
+  const int tid = threadIdx.x, d = tid % D, k0 = tid / D;
+  constexpr int KS = 256 / D;  // keys read at a time
+  uint32_t m = 0u;
+  for (int r = k0; r < 64; r += KS) {
+    const int gk = c0 + tt * 64 + r;
+    if (gk < c1) m = max(m, (uint32_t)(p.v[((size_t)h * p.L + gk) * D + d] & 0x7FFFu) << 16);
+  }
+  part[tid] = m;
+  __syncthreads();
+  if (tid < D) {
+    for (int j = 1; j < KS; ++j) m = max(m, part[tid + j * D]);
+    p.rmax[((size_t)hc * tiles + tt) * D + tid] = m;
+  }
+}
+
+// The power-of-two exponent s that brings max |v| = m (float bits) into [2^14, 2^15)
+// (clamped to [-100, 113], the exponents a float multiplier can carry), so v * 2^-s
+// is finite in fp16 and small dimensions keep fp16's full precision; kVtBad for a
+// non-finite m.
+constexpr int kVtBad = 1 << 20;
+__device__ __forceinline__ int vt_exponent(uint32_t m) {
+  const int e = (int)(m >> 23) - 127;  // floor(log2 m) for a normal m
+  if (e >= 128) return kVtBad;
+  return min(max(e - 14, -100), 113);
+}
+
 // V [H][L][D] bf16 -> V^T [H][C][D][Lc] fp16 (chunk-local keys at vt_position, zero
-// past the chunk's end; |v| > 65504 saturates and sets the status word).  One
-// workgroup per (KV head, chunk, 64-key tile).  The tile is staged in LDS with rows
-// of 32 keys and above swapped in 16-byte column pairs (chunk c at c ^ 1): a wave's
-// transposed reads take rows k and k + 32 together, which would otherwise share
-// banks.
+// past the chunk's end).  Row d of a chunk is scaled by 2^-s_d so that the chunk's
+// max |v| in dimension d (vt_range) lies in [2^14, 2^15): every finite bf16 value
+// fits, and a scaling by a power of two changes no significant bit of a bf16 value
+// (the chunk kernel multiplies row d of its output back; inside float32's range the
+// product and its accumulation scale exactly).  A non-finite v saturates and sets
+// the status word.  One workgroup per (KV head,
+// chunk, 64-key tile).  The tile is staged in LDS with rows of 32 keys and above
+// swapped in 16-byte column pairs (chunk c at c ^ 1): a wave's transposed reads
+// take rows k and k + 32 together, which would otherwise share banks.
 template <int D>
 __global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
   constexpr int RP = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t vs[64 * RP];
+  __shared__ float s_mul[D];
+  __shared__ int s_bad;
   const int tiles = p.Lc / 64;
   const int tt = blockIdx.x % tiles, hc = blockIdx.x / tiles;
   const int c = hc % p.C, h = hc / p.C;
   const int c0 = c * p.csize, c1 = min(p.L, c0 + p.csize);
   const int tid = threadIdx.x;
   constexpr int CPR = D / 8;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (tid < D) {
+    uint32_t m = 0u;
+    for (int t2 = 0; t2 < tiles; ++t2) m = max(m, p.rmax[((size_t)hc * tiles + t2) * D + tid]);
+    int e = vt_exponent(m);
+    if (e == kVtBad) {
+      s_bad = 1;
+      e = 0;
+    }
+    s_mul[tid] = __int_as_float((127 - e) << 23);  // 2^-e
+    if (tt == 0) p.sexp[(size_t)hc * D + tid] = e;
+  }
 #pragma unroll
   for (int j = 0; j < 64 * CPR / 256; ++j) {
     const int ci = tid + 256 * j, r = ci / CPR, col = ci % CPR;
@@ -104,12 +160,13 @@ __global__ __launch_bounds__(256) void vt_prepare(PrefixArgs p) {
       const int k1 = (p1 & ~31) + 4 * ((p1 & 31) >> 3) + (p1 & 3) + ((p1 & 4) ? 16 : 0);
       const int c0s = (((d >> 3) ^ ((k0 >> 5) & 1)) << 3) + (d & 7);
       const int c1s = (((d >> 3) ^ ((k1 >> 5) & 1)) << 3) + (d & 7);
-      const float x0 = bf16_bits_to_f32(vs[k0 * RP + c0s]), x1 = bf16_bits_to_f32(vs[k1 * RP + c1s]);
-      sat |= fabsf(x0) > 65504.f || fabsf(x1) > 65504.f;
+      const float x0 = bf16_bits_to_f32(vs[k0 * RP + c0s]) * s_mul[d];
+      const float x1 = bf16_bits_to_f32(vs[k1 * RP + c1s]) * s_mul[d];
+      sat |= !(fabsf(x0) <= 65504.f) || !(fabsf(x1) <= 65504.f);
       w[e / 2] = pack_f16x2(fminf(fmaxf(x0, -65504.f), 65504.f),
                             fminf(fmaxf(x1, -65504.f), 65504.f));
     }
-    if (sat) p.status[0] = KVB_ERANGE;
+    if (sat || (tid == 0 && s_bad)) p.status[0] = KVB_ERANGE;
     *(u32x4*)(dst + (size_t)d * p.Lc + 8 * q) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
@@ -270,8 +327,17 @@ __global__ __launch_bounds__(512) void asm_prefix_chunk(PrefixArgs p) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t row = ((size_t)c * H + h) * p.N + n;
     float* dst = p.out + row * D + 4 * lg;
+    // V^T row d held v * 2^-s_d (vt_prepare): scale output element d back (no V and
+    // no exponents for an empty prefix)
+    const i32x4* se = (const i32x4*)(p.sexp + ((size_t)h * p.C + c) * D + 4 * lg);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *(f32x4*)(dst + dt * 16) = o[dt][qt] * inv;
+    for (int dt = 0; dt < DT; ++dt) {
+      const i32x4 e4 = p.L > 0 ? se[dt * 4] : i32x4{0, 0, 0, 0};
+      f32x4 x = o[dt][qt] * inv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= __int_as_float((127 + e4[i]) << 23);
+      *(f32x4*)(dst + dt * 16) = x;
+    }
     if (lg == 0) p.out_lse[row] = l > 0.f ? m[qt] * kLn2 + logf(l) : kNegInf;
   }
 }
@@ -723,27 +789,34 @@ static bool build_dims_ok(int H, int N, int D) {
 // Workspace of the prefix-state computation: V^T per chunk, then (more than one
 // chunk) the chunk states and their lse.
 static size_t prefix_layout(int H, int N, int D, int L, int chunks, int& C, int& csize, int& Lc,
-                            size_t& o_vt, size_t& o_part, size_t& o_plse) {
+                            size_t& o_vt, size_t& o_part, size_t& o_plse, size_t* o_rmax = nullptr,
+                            size_t* o_sexp = nullptr) {
   C = prefix_chunks(L, chunks, csize);
   Lc = (csize + kPfxKT - 1) / kPfxKT * kPfxKT;
   const size_t rows = (size_t)H * N;
   o_vt = kWsHeader;
   o_part = o_vt + (L > 0 ? align_up((size_t)H * C * D * Lc * 2, 256) : 0);
   o_plse = o_part + (C > 1 ? align_up((size_t)C * rows * D * 4, 256) : 0);
-  return o_plse + (C > 1 ? align_up((size_t)C * rows * 4, 256) : 0);
+  const size_t rm = o_plse + (C > 1 ? align_up((size_t)C * rows * 4, 256) : 0);
+  const size_t se = rm + (L > 0 ? align_up((size_t)H * C * (Lc / kPfxKT) * D * 4, 256) : 0);
+  if (o_rmax) *o_rmax = rm;
+  if (o_sexp) *o_sexp = se;
+  return se + (L > 0 ? align_up((size_t)H * C * D * 4, 256) : 0);
 }
 
 static int32_t launch_prefix(const void* q, int32_t H, int32_t N, int32_t D, const void* k,
                              const void* v, int32_t L, int32_t chunks, float scale, float* a,
                              float* lse, void* ws, int32_t* status, hipStream_t s) {
   int C, csize, Lc;
-  size_t o_vt, o_part, o_plse;
-  prefix_layout(H, N, D, L, chunks, C, csize, Lc, o_vt, o_part, o_plse);
+  size_t o_vt, o_part, o_plse, o_rmax, o_sexp;
+  prefix_layout(H, N, D, L, chunks, C, csize, Lc, o_vt, o_part, o_plse, &o_rmax, &o_sexp);
   PrefixArgs p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
   p.vt = (uint16_t*)((char*)ws + o_vt);
+  p.rmax = (uint32_t*)((char*)ws + o_rmax);
+  p.sexp = (int32_t*)((char*)ws + o_sexp);
   p.status = status;
   p.H = H;
   p.N = N;
@@ -763,10 +836,13 @@ static int32_t launch_prefix(const void* q, int32_t H, int32_t N, int32_t D, con
   if (L > 0) {
     TraceScope tr(kTrAsmVt, s);
     const dim3 g((unsigned)((size_t)H * C * (Lc / kPfxKT)));
-    if (D == 128)
+    if (D == 128) {
+      hipLaunchKernelGGL(vt_range<128>, g, dim3(256), 0, s, p);
       hipLaunchKernelGGL(vt_prepare<128>, g, dim3(256), 0, s, p);
-    else
+    } else {
+      hipLaunchKernelGGL(vt_range<64>, g, dim3(256), 0, s, p);
       hipLaunchKernelGGL(vt_prepare<64>, g, dim3(256), 0, s, p);
+    }
   }
   const dim3 grid(H * ((N + kPfxQB - 1) / kPfxQB), C);
   {

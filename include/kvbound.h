@@ -495,9 +495,10 @@ int32_t asm_lookup_merge_hier(const void* q, int32_t B, int32_t Hq, int32_t Hkv,
  * computed on its own and the states are merged in chunk order with the merge
  * operator.  L == 0 gives a = 0, lse = -inf.  Scores use bf16 MFMA products with
  * float32 accumulation; the value product runs in fp16 (float32 accumulation): the
- * softmax weights rounded to fp16, v converted to fp16 (exact for |v| <= 65504;
- * larger values saturate to +-65504 and the workspace status word, the int32 at
- * byte offset 0, is set to KVB_ERANGE; the call never clears it).
+ * softmax weights rounded to fp16, v converted to fp16 after scaling each chunk's
+ * dimension d by the power of two that brings that dimension's max |v| into
+ * [2^14, 2^15), which the output undoes: every finite bf16 v is carried exactly.  A non-finite v saturates and sets the workspace status word, the int32 at
+ * byte offset 0, to KVB_ERANGE (the call never clears it).
  *   q        [H][N][D] bf16 (the KV head's calibration queries; for GQA the group's
  *            query heads stacked along N)
  *   k, v     [H][L][D] bf16 (may be NULL when L == 0)

@@ -173,8 +173,10 @@ def test_build_entry_points_reject_arguments_before_launch():
     assert call(f, pre, a4=None) == -1        # k with L > 0
     assert call(f, pre, a9=None) == -1        # a
     assert call(f, pre, a12=64) == -4         # workspace too small for 4 chunk states
-    # one chunk: V^T of the 300 tokens (padded to 320 keys) only
-    assert L.asm_prefix_states_workspace(2, 100, 128, 300, 1) == 256 + 2 * 128 * 320 * 2
+    # one chunk: V^T of the 300 tokens (padded to 320 keys), the per-tile (5 tiles of
+    # 64 keys) and per-chunk range words of every dimension
+    assert L.asm_prefix_states_workspace(2, 100, 128, 300, 1) == (256 + 2 * 128 * 320 * 2 +
+                                                                2 * 5 * 128 * 4 + 2 * 128 * 4)
     assert L.asm_prefix_states_workspace(2, 100, 128, 0, 4) == 256
     # 300 tokens in 4 chunks of 75 (V^T padded to 128 keys each): 4 states per query
     assert L.asm_prefix_states_workspace(2, 100, 128, 300, 4) >= (256 + 2 * 4 * 128 * 128 * 2 +
