@@ -181,3 +181,114 @@ def append_tokens(cache: Cache, k_new, v_new, log_beta_new, t):
             cache.pos[b, g, s] = t[b]
             cache.length[b, g] = s + 1
     return cache
+
+
+# ---------------------------------------------------------------- paged form
+# A paged cache keeps each head's tokens in pages of 32 slots.  The page table lists
+# a head's pages in position order; physical page p of a head is slots
+# [32p, 32p + 32) of that head's arrays, and a page holds its live tokens in its first
+# `fill` slots.  The token sequence of a head is its pages' live rows in table order.
+PAGE = 32
+_ROW_ARRAYS = ("k", "v", "pos")
+
+
+@dataclasses.dataclass
+class Pages:
+    """table, fill [B][Hkv][max_pages] int32; n_pages [B][Hkv] int32."""
+    table: np.ndarray
+    fill: np.ndarray
+    n_pages: np.ndarray
+
+    def copy(self):
+        return Pages(self.table.copy(), self.fill.copy(), self.n_pages.copy())
+
+
+def paged_slots(pages: Pages, b: int, g: int):
+    """Slots of head (b, g)'s live tokens, in sequence order."""
+    out = []
+    for i in range(int(pages.n_pages[b, g])):
+        p = int(pages.table[b, g, i])
+        out.extend(range(PAGE * p, PAGE * p + int(pages.fill[b, g, i])))
+    return np.asarray(out, dtype=np.int64)
+
+
+def paged_view(cache: Cache, pages: Pages):
+    """The contiguous cache holding each head's token sequence at slots [0, len)."""
+    out = cache.copy()
+    B, H = cache.length.shape
+    for b in range(B):
+        for g in range(H):
+            idx = paged_slots(pages, b, g)
+            n = idx.shape[0]
+            for name in _ROW_ARRAYS + (() if cache.log_beta is None else ("log_beta",)):
+                getattr(out, name)[b, g, :n] = getattr(cache, name)[b, g][idx]
+            out.length[b, g] = n
+    return out
+
+
+def erase_pages(cache: Cache, pages: Pages, ranges):
+    """MEMENTO erasure on a paged cache, on copies; returns (cache, pages, n_erased).
+
+    The kept tokens are those of erase_plan (position in no range).  Removal is by
+    page: a page with no kept row leaves the table, and a page with some keeps them
+    in order in its first slots (rows of other pages do not move).  The table keeps
+    the remaining pages in order; len is the kept total.
+    """
+    out, pg = cache.copy(), pages.copy()
+    B, H = cache.length.shape
+    n_er = np.zeros((B, H), dtype=np.int32)
+    for b in range(B):
+        for g in range(H):
+            table, fill = [], []
+            before = after = 0
+            for i in range(int(pages.n_pages[b, g])):
+                p, f = int(pages.table[b, g, i]), int(pages.fill[b, g, i])
+                rows = np.arange(PAGE * p, PAGE * p + f)
+                keep = erase_plan(cache.pos[b, g, rows], f, ranges[b])
+                kept = int(keep.sum())
+                before += f
+                after += kept
+                if kept == 0:
+                    continue
+                for arr in (out.k, out.v, out.pos) + (() if out.log_beta is None
+                                                      else (out.log_beta,)):
+                    arr[b, g, PAGE * p:PAGE * p + kept] = arr[b, g, rows[keep]].copy()
+                table.append(p)
+                fill.append(kept)
+            pg.table[b, g, :len(table)] = table
+            pg.fill[b, g, :len(fill)] = fill
+            pg.n_pages[b, g] = len(table)
+            out.length[b, g] = after
+            n_er[b, g] = before - after
+    return out, pg, n_er
+
+
+def paged_append(cache: Cache, pages: Pages, k_new, v_new, log_beta_new, t, spare):
+    """Each head's decode token into its last page when that has a free slot, else
+    into its free page spare[b][g] added to the end of the table (in place).
+    Returns [B][Hkv] bool: stored (False where the head had no room)."""
+    B, H = cache.length.shape
+    max_pages = pages.table.shape[2]
+    stored = np.zeros((B, H), dtype=bool)
+    for b in range(B):
+        for g in range(H):
+            n = int(pages.n_pages[b, g])
+            if n > 0 and pages.fill[b, g, n - 1] < PAGE:
+                p, r = int(pages.table[b, g, n - 1]), int(pages.fill[b, g, n - 1])
+                pages.fill[b, g, n - 1] = r + 1
+            elif spare is not None and spare[b, g] >= 0 and n < max_pages:
+                p, r = int(spare[b, g]), 0
+                pages.table[b, g, n] = p
+                pages.fill[b, g, n] = 1
+                pages.n_pages[b, g] = n + 1
+            else:
+                continue
+            s = PAGE * p + r
+            cache.k[b, g, s] = k_new[b, g]
+            cache.v[b, g, s] = v_new[b, g]
+            if cache.log_beta is not None:
+                cache.log_beta[b, g, s] = log_beta_new[b, g]
+            cache.pos[b, g, s] = t[b]
+            cache.length[b, g] += 1
+            stored[b, g] = True
+    return stored

@@ -687,6 +687,125 @@ def check_decode_loop_order(seed=15):
     assert np.array_equal(final.k[0, 0, :M], kr[[0, 2, 4]])
 
 
+# ---------------------------------------------------------------- P16
+def _paged_case(r, B, H, n_pages_max, spare_pages=2, max_pages=None):
+    """Random paged cache: per head a run of pages with fills 1..32 on distinct
+    physical pages, positions ascending along the table with random gaps."""
+    D = 4
+    max_pages = max_pages or n_pages_max + spare_pages
+    phys = n_pages_max + spare_pages + 3
+    cap = OE.PAGE * phys
+    k = r.integers(0, 1 << 16, size=(B, H, cap, D)).astype(np.uint16)
+    v = r.integers(0, 1 << 16, size=(B, H, cap, D)).astype(np.uint16)
+    lb = r.uniform(-0.1, 0.0, size=(B, H, cap)).astype(np.float32)
+    pos = np.full((B, H, cap), -1, np.int32)
+    table = np.full((B, H, max_pages), -7, np.int32)
+    fill = np.full((B, H, max_pages), -7, np.int32)
+    n_pages = np.zeros((B, H), np.int32)
+    length = np.zeros((B, H), np.int32)
+    for b in range(B):
+        for g in range(H):
+            n = int(r.integers(0, n_pages_max + 1))
+            perm = r.permutation(phys)[:n]
+            p = 0
+            for i in range(n):
+                f = int(r.integers(1, OE.PAGE + 1))
+                for j in range(f):
+                    p += int(r.integers(1, 3))
+                    pos[b, g, OE.PAGE * perm[i] + j] = p
+                table[b, g, i], fill[b, g, i] = perm[i], f
+                length[b, g] += f
+            n_pages[b, g] = n
+    return OE.Cache(k, v, lb, pos, length), OE.Pages(table, fill, n_pages)
+
+
+def check_paged_erase(seed=16):
+    """Block-granular erase: the token sequence it leaves is the contiguous erase's
+    (pinned by the set filter above); page by page, written as loops, a page with
+    no survivor leaves the table, a page untouched keeps its rows bit for bit, and
+    the table keeps its order.  Hand cases fix whole-page drops."""
+    r = _rng(seed)
+    for _ in range(12):
+        c, pg = _paged_case(r, 2, 2, 6)
+        top = int(c.pos.max()) + 5
+        ranges = []
+        for b in range(2):
+            edges = np.sort(r.choice(top, size=2 * int(r.integers(0, 5)), replace=False))
+            ranges.append(edges.reshape(-1, 2).astype(np.int64))
+        c2, pg2, n_er = OE.erase_pages(c, pg, ranges)
+        want, n_want = OE.erase_ranges(OE.paged_view(c, pg), ranges)
+        got = OE.paged_view(c2, pg2)
+        assert np.array_equal(got.length, want.length) and np.array_equal(n_er, n_want)
+        assert np.array_equal(c2.length, want.length), "len is not the kept total"
+        for b in range(2):
+            for g in range(2):
+                n = int(want.length[b, g])
+                for name in ("k", "v", "pos", "log_beta"):
+                    assert np.array_equal(getattr(got, name)[b, g, :n],
+                                          getattr(want, name)[b, g, :n]), name
+                new_i = 0
+                for i in range(int(pg.n_pages[b, g])):
+                    p, f = int(pg.table[b, g, i]), int(pg.fill[b, g, i])
+                    kept = 0
+                    for j in range(f):
+                        x = int(c.pos[b, g, 32 * p + j])
+                        if not any(s <= x < e for s, e in ranges[b]):
+                            kept += 1
+                    if kept == 0:
+                        continue
+                    assert pg2.table[b, g, new_i] == p and pg2.fill[b, g, new_i] == kept
+                    if kept == f:
+                        assert np.array_equal(c2.k[b, g, 32 * p:32 * p + f],
+                                              c.k[b, g, 32 * p:32 * p + f])
+                    new_i += 1
+                assert pg2.n_pages[b, g] == new_i
+    # hand case: pages 3 (positions 0..31) and 1 (32..40); erasing [32, 41) drops
+    # page 1, erasing [0, 32) drops page 3, erasing [30, 34) keeps both, partly
+    pos = np.zeros((1, 1, 128), np.int32)
+    pos[0, 0, 96:128] = np.arange(32)
+    pos[0, 0, 32:41] = np.arange(32, 41)
+    k = np.arange(128 * 2, dtype=np.uint16).reshape(1, 1, 128, 2)
+    c = OE.Cache(k, k.copy(), None, pos, np.array([[41]], np.int32))
+    pg = OE.Pages(np.array([[[3, 1]]], np.int32), np.array([[[32, 9]]], np.int32),
+                  np.array([[2]], np.int32))
+    for rg, tab, fil in (([[32, 41]], [3], [32]), ([[0, 32]], [1], [9]),
+                         ([[30, 34]], [3, 1], [30, 7])):
+        c2, pg2, n_er = OE.erase_pages(c, pg, [np.array(rg)])
+        n = int(pg2.n_pages[0, 0])
+        assert list(pg2.table[0, 0, :n]) == tab and list(pg2.fill[0, 0, :n]) == fil, rg
+        assert n_er[0, 0] == 41 - sum(fil)
+    c2, pg2, _ = OE.erase_pages(c, pg, [np.array([[30, 34]])])
+    assert list(c2.pos[0, 0, 32:39]) == list(range(34, 41))
+    assert np.array_equal(c2.k[0, 0, 32:39], k[0, 0, 34:41])
+
+
+def check_paged_append(seed=17):
+    """Decode token of a paged cache: into the last page's next slot while it has
+    one, else onto the free page given (added to the table), else not stored."""
+    pos = np.zeros((1, 2, 96), np.int32)
+    k = np.zeros((1, 2, 96, 2), np.uint16)
+    c = OE.Cache(k, k.copy(), None, pos, np.array([[5, 32]], np.int32))
+    pg = OE.Pages(np.array([[[2, -1], [0, -1]]], np.int32),
+                  np.array([[[5, 0], [32, 0]]], np.int32), np.array([[1, 1]], np.int32))
+    kn = np.array([[[7, 7], [9, 9]]], np.uint16)
+    st = OE.paged_append(c, pg, kn, kn, None, np.array([50]), np.array([[1, 1]]))
+    assert st.tolist() == [[True, True]]
+    assert c.pos[0, 0, 64 + 5] == 50 and list(c.k[0, 0, 69]) == [7, 7]
+    assert pg.fill[0, 0, 0] == 6 and pg.n_pages[0, 0] == 1, "free page taken while room"
+    assert pg.table[0, 1, 1] == 1 and pg.fill[0, 1, 1] == 1 and pg.n_pages[0, 1] == 2
+    assert c.pos[0, 1, 32] == 50 and list(c.k[0, 1, 32]) == [9, 9]
+    assert c.length.tolist() == [[6, 33]]
+    # no room: a full last page, no free page (or a full table)
+    pg2 = OE.Pages(np.array([[[0, 1], [0, 1]]], np.int32),
+                   np.array([[[32, 32], [32, 0]]], np.int32), np.array([[2, 1]], np.int32))
+    st = OE.paged_append(c, pg2, kn, kn, None, np.array([51]), np.array([[2, -1]]))
+    assert st.tolist() == [[False, False]] and c.length.tolist() == [[6, 33]]
+    # the view walks the table: pages [2, 0] with fills [3, 2] are slots 64-66, 0-1
+    pg3 = OE.Pages(np.array([[[2, 0], [0, 0]]], np.int32),
+                   np.array([[[3, 2], [1, 0]]], np.int32), np.array([[2, 1]], np.int32))
+    assert list(OE.paged_slots(pg3, 0, 0)) == [64, 65, 66, 0, 1]
+
+
 def run_decode(*a, **kw):
     import oracle.decode as OD
     return OD.run_decode_steps(*a, **kw)
@@ -696,4 +815,5 @@ ALL = [check_attention_library, check_bias_closed_form, check_split_merge,
        check_asm_lossless, check_evict_bruteforce, check_evict_sliding_window,
        check_evict_invariants, check_compaction, check_erase_bruteforce,
        check_lookup_bruteforce, check_hier_lookup, check_asm_build, check_latent_memory, check_bytes_model,
-       check_decode_attention_gqa, check_asm_batched, check_decode_loop_order]
+       check_decode_attention_gqa, check_asm_batched, check_decode_loop_order,
+       check_paged_erase, check_paged_append]

@@ -382,6 +382,71 @@ def decode_attend_before_append(*a, **kw):
     return c, steps
 
 
+def _erase_pages_slip(cache, pages, ranges, keep_empty=False, in_place=False):
+    out, pg = cache.copy(), pages.copy()
+    B, H = cache.length.shape
+    n_er = np.zeros((B, H), dtype=np.int32)
+    for b in range(B):
+        for g in range(H):
+            table, fill, before, after = [], [], 0, 0
+            for i in range(int(pages.n_pages[b, g])):
+                p, f = int(pages.table[b, g, i]), int(pages.fill[b, g, i])
+                rows = np.arange(32 * p, 32 * p + f)
+                keep = OE.erase_plan(cache.pos[b, g, rows], f, ranges[b])
+                kept = int(keep.sum())
+                before, after = before + f, after + kept
+                if kept == 0 and not keep_empty:
+                    continue
+                if not in_place:
+                    for name in ("k", "v", "pos", "log_beta"):
+                        a = getattr(out, name)
+                        if a is not None:
+                            a[b, g, 32 * p:32 * p + kept] = a[b, g, rows[keep]].copy()
+                table.append(p)
+                fill.append(kept)
+            pg.table[b, g, :len(table)] = table
+            pg.fill[b, g, :len(fill)] = fill
+            pg.n_pages[b, g] = len(table)
+            out.length[b, g] = after
+            n_er[b, g] = before - after
+    return out, pg, n_er
+
+
+def erase_pages_keeps_empty(cache, pages, ranges):
+    return _erase_pages_slip(cache, pages, ranges, keep_empty=True)
+
+
+def erase_pages_no_compaction(cache, pages, ranges):
+    return _erase_pages_slip(cache, pages, ranges, in_place=True)
+
+
+_orig_paged_append = OE.paged_append
+
+
+def paged_append_prefers_spare(cache, pages, k_new, v_new, log_beta_new, t, spare):
+    full = pages.fill.copy()
+    for b in range(full.shape[0]):
+        for g in range(full.shape[1]):
+            n = int(pages.n_pages[b, g])
+            if spare is not None and spare[b, g] >= 0 and n > 0:
+                pages.fill[b, g, n - 1] = 32
+    st = _orig_paged_append(cache, pages, k_new, v_new, log_beta_new, t, spare)
+    for b in range(full.shape[0]):
+        for g in range(full.shape[1]):
+            n = int(pages.n_pages[b, g])
+            for i in range(n - 1):
+                pages.fill[b, g, i] = full[b, g, i]
+    return st
+
+
+def paged_slots_full_pages(pages, b, g):
+    out = []
+    for i in range(int(pages.n_pages[b, g])):
+        p = int(pages.table[b, g, i])
+        out.extend(range(32 * p, 32 * p + 32))
+    return np.asarray(out, dtype=np.int64)
+
+
 MUTANTS = [
     (OT, "retention_bias", bias_sign_flipped),
     (OT, "retention_bias", bias_dropped),
@@ -427,6 +492,10 @@ MUTANTS = [
     (OA, "asm_lookup_merge_hier", asm_hier_batched_first_head),
     (OD, "run_decode_steps", decode_evict_before_attend),
     (OD, "run_decode_steps", decode_attend_before_append),
+    (OE, "erase_pages", erase_pages_keeps_empty),
+    (OE, "erase_pages", erase_pages_no_compaction),
+    (OE, "paged_append", paged_append_prefers_spare),
+    (OE, "paged_slots", paged_slots_full_pages),
 ]
 
 
