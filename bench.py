@@ -863,7 +863,11 @@ def memento_bench(args):
     nr = torch.tensor([ranges.shape[0]], dtype=torch.int32, device="cuda")
     t = torch.full((1,), w.ctx, dtype=torch.int32, device="cuda")
     ws_er = torch.empty(kvb.kv_erase_workspace(c), dtype=torch.uint8, device="cuda")
-    ws_a = torch.empty(kvb.kv_attn_decode_workspace(c, w.hq, 0), dtype=torch.uint8,
+    # the caller knows the live length after the erase: split count by the library's
+    # rule applied to it (about 2048 / (B * Hkv) splits, at most one per 256 live
+    # slots) instead of to the 1M-slot capacity (512 splits)
+    P_att = max(1, min(2048 // w.units, (kept + 1) // 256))
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(c, w.hq, P_att), dtype=torch.uint8,
                        device="cuda")
     ws_ev = torch.empty(kvb.kv_evict_workspace(c, w.budget), dtype=torch.uint8, device="cuda")
     n_er = torch.empty((1, w.hkv), dtype=torch.int32, device="cuda")
@@ -887,7 +891,8 @@ def memento_bench(args):
         ev[0].record()
         kvb.kv_erase_ranges(c, rg, nr, n_erased=n_er, ws=ws_er)
         ev[1].record()
-        kvb.kv_attn_decode(c, q, t, k_new=kn, v_new=vn, out=out, lse=lse, ws=ws_a)
+        kvb.kv_attn_decode(c, q, t, k_new=kn, v_new=vn, num_splits=P_att, out=out, lse=lse,
+                           ws=ws_a)
         ev[2].record()
         kvb.kv_evict_to_budget(c, t, w.budget, n_evicted=n_ev, ws=ws_ev)
         ev[3].record()
@@ -923,7 +928,8 @@ def memento_bench(args):
         "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": 1, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": D, "slots": w.ctx, "blocks": len(blocks),
-                   "erased_ranges": int(ranges.shape[0]), "kept": kept, "budget": w.budget},
+                   "erased_ranges": int(ranges.shape[0]), "kept": kept, "budget": w.budget,
+                   "attention_splits": P_att},
         "erase_us": {"median": round(float(med[0]), 2), "min": round(float(res[:, 0].min()), 2),
                      "max": round(float(res[:, 0].max()), 2),
                      "bytes": erase_b, "gbps": round(erase_b / (med[0] * 1e-6) / 1e9, 1)},
@@ -931,6 +937,119 @@ def memento_bench(args):
                          "max": round(float(res[:, 1].max()), 2),
                          "bytes": attn_b, "gbps": round(attn_b / (med[1] * 1e-6) / 1e9, 1)},
         "evict_us": {"median": round(float(med[2]), 2)},
+        "kernel_us": {k: round(float(np.median(v)), 1) for k, v in per.items()}}), flush=True)
+
+
+def memento_paged_bench(args):
+    """The MEMENTO trial of memento_bench over a paged cache: the same 1M-token trace
+    laid out in 32-slot pages, every thinking block and every memento starting on a
+    fresh page (its last page partly filled; physical pages in a seeded random
+    order).  The erase drops the completed blocks' pages from each head's page table
+    (no row moves); the decode token goes into the last page (or a free page) and
+    the attention reads the kept pages.  Each trial restores the page arrays and
+    the lengths first (untimed); median over the trials, device times."""
+    import numpy as np
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS["memento_1m"]
+    blocks, ranges = synth.memento_layout(total=w.ctx, seed=w.seed)
+    table, fill, pos0, phys = synth.memento_pages(blocks, w.hkv, seed=w.seed)
+    n = table.shape[1]
+    erased = np.zeros(n, bool)
+    for s0, e0 in ranges:
+        erased |= (pos0 >= s0) & (pos0 < e0)
+    keep = np.nonzero(~erased)[0]
+    kept = int(fill[keep].sum())
+    print(f"# memento_1m paged: {len(blocks)} blocks, {n} pages ({phys} physical), "
+          f"{keep.size} pages and {kept} tokens kept per KV head", file=sys.stderr, flush=True)
+    cap = 32 * phys
+    dc = synth.device_cache(w, layer=0, n=cap, cap=cap)
+    pos = np.zeros((w.hkv, cap), np.int32)
+    for g in range(w.hkv):
+        for i in range(n):
+            pos[g, 32 * table[g, i]:32 * table[g, i] + fill[i]] = pos0[i] + np.arange(fill[i])
+    dc["pos"].copy_(torch.from_numpy(pos[None]))
+    c = kvb.KVCache.from_dict(dc)
+    mp = n + 8
+    tab0 = np.full((1, w.hkv, mp), -1, np.int32)
+    tab0[0, :, :n] = table
+    fil0 = np.zeros((1, w.hkv, mp), np.int32)
+    fil0[0, :, :n] = fill
+    tab0, fil0 = torch.from_numpy(tab0).cuda(), torch.from_numpy(fil0).cuda()
+    pg = kvb.KVPages(tab0.clone(), fil0.clone(),
+                     torch.full((1, w.hkv), n, dtype=torch.int32, device="cuda"))
+    free = [min(set(range(phys)) - set(table[g].tolist())) for g in range(w.hkv)]
+    spare = torch.tensor([free], dtype=torch.int32, device="cuda")
+    q, kn, vn, _ = synth.device_queries(w, 0)
+    rg = torch.from_numpy(ranges[None].copy()).cuda()
+    nr = torch.tensor([ranges.shape[0]], dtype=torch.int32, device="cuda")
+    t = torch.full((1,), w.ctx, dtype=torch.int32, device="cuda")
+    ws_er = torch.empty(kvb.kv_erase_paged_workspace(c, pg), dtype=torch.uint8, device="cuda")
+    # split count by the library's rule applied to the pages left after the erase
+    # (about 2048 / (B * Hkv) splits, at most one per 8 pages)
+    P_att = max(1, min(2048 // w.units, (keep.size + 1) // 8))
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(c, w.hq, P_att), dtype=torch.uint8,
+                       device="cuda")
+    n_er = torch.empty((1, w.hkv), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, w.hq), dtype=torch.float32, device="cuda")
+
+    def restore():
+        pg.table.copy_(tab0)
+        pg.fill.copy_(fil0)
+        pg.n_pages.fill_(n)
+        dc["len"].fill_(int(fill.sum()))
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def trial():
+        restore()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(2_000_000)
+        ev[0].record()
+        kvb.kv_erase_ranges_paged(c, pg, rg, nr, n_erased=n_er, ws=ws_er)
+        ev[1].record()
+        kvb.kv_attn_decode_paged(c, pg, q, t, k_new=kn, v_new=vn, spare=spare,
+                                 num_splits=P_att, out=out, lse=lse, ws=ws_a)
+        ev[2].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(2)]
+
+    for _ in range(args.warmup):
+        trial()
+    trials = max(args.steps, 20)
+    res = np.array([trial() for _ in range(trials)])
+    assert int(n_er.min()) == int(n_er.max()) == w.ctx - kept, "erased count"
+    assert bool((dc["len"] == kept + 1).all()), "kept + decode token"
+    assert bool((pg.n_pages >= keep.size).all()), "pages kept"
+    kvb.trace_enable(8 * trials + 64, ("erase_pages", "attn_split", "attn_merge"))
+    for _ in range(trials):
+        trial()
+    per = {}
+    for name, kms in kvb.trace_read(1 << 16):
+        per.setdefault(name, []).append(kms * 1000.0)
+    kvb.trace_disable()
+    D = w.head_dim
+    attn_b = algorithmic_bytes(w, kept + 1, 0)[0]
+    med = np.median(res, axis=0)
+    print(json.dumps({
+        "metric": "MEMENTO erase + bounded decode attention latency, one layer (1M-token "
+                  "paged cache)",
+        "value": round(float(np.sum(med)), 2), "unit": "us", "n_gpus": 1, "trials": trials,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layout": "paged (32-slot pages, block-aligned)",
+                   "batch": 1, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": D,
+                   "tokens": w.ctx, "pages": n, "pages_kept": int(keep.size),
+                   "erased_ranges": int(ranges.shape[0]), "kept": kept,
+                   "attention_splits": P_att},
+        "erase_us": {"median": round(float(med[0]), 2), "min": round(float(res[:, 0].min()), 2),
+                     "max": round(float(res[:, 0].max()), 2), "rows_moved": 0},
+        "attention_us": {"median": round(float(med[1]), 2), "min": round(float(res[:, 1].min()), 2),
+                         "max": round(float(res[:, 1].max()), 2),
+                         "bytes": attn_b, "gbps": round(attn_b / (med[1] * 1e-6) / 1e9, 1)},
         "kernel_us": {k: round(float(np.median(v)), 1) for k, v in per.items()}}), flush=True)
 
 
@@ -1059,6 +1178,9 @@ def main():
     ap.add_argument("--memento", action="store_true",
                     help="time MEMENTO erasure + attention on the 1M-slot workload instead "
                          "(one JSON line)")
+    ap.add_argument("--paged", action="store_true",
+                    help="--memento: the same trial over a paged cache (block-granular "
+                         "erase, paged attention)")
     ap.add_argument("--latent", action="store_true",
                     help="time the latent memory of evicted tokens (update after the 32K "
                          "eviction, steady-state update, read-out; one JSON line)")
@@ -1084,6 +1206,9 @@ def main():
         return
     if args.latent:
         latent_bench(args)
+        return
+    if args.memento and args.paged:
+        memento_paged_bench(args)
         return
     if args.memento:
         memento_bench(args)

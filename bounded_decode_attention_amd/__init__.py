@@ -10,7 +10,10 @@ Entry points (same names as the C ABI in include/kvbound.h):
 (kv_attn_decode_asm: the first and the last in one call; kv_attn_decode_noalloc:
 the first without a workspace, for callers that cannot allocate;
 kv_attn_decode_evict_one, and kv_attn_decode_plan_one + kv_evict_one_apply: the
-steady state's attention with the one-token eviction selected by its splits), and, for building the memory asm_lookup_merge reads, asm_prefix_states,
+steady state's attention with the one-token eviction selected by its splits;
+kv_attn_decode_paged and kv_erase_ranges_paged: the attention and the
+block-granular erase over a paged cache, ``KVPages``), and, for building the
+memory asm_lookup_merge reads, asm_prefix_states,
 asm_kmeans, asm_aggregate_states, asm_build_memory; and the latent memory of
 evicted tokens, kv_latent_absorb and kv_latent_read;
 plus the workspace-size helpers and ``KVCache``, a holder of one layer's tensors.
@@ -29,6 +32,8 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    kv_evict_plan, kv_attn_decode_plan_one, kv_evict_one_apply,
                    kv_evict_one_workspace, kv_attn_decode_evict_one,
                    kv_attn_decode_evict_one_workspace,
+                   KVPages, kv_attn_decode_paged, kv_erase_paged_workspace,
+                   kv_erase_ranges_paged,
                    kv_latent_absorb, kv_latent_absorb_workspace, kv_latent_read,
                    kv_evict_to_budget,
                    kv_evict_workspace, library, library_path, strerror, trace_disable,
@@ -41,6 +46,7 @@ __all__ = [
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_evict_one", "kv_attn_decode_compact",
     "kv_attn_decode_plan_one", "kv_evict_one_apply", "kv_evict_one_workspace",
     "kv_attn_decode_evict_one", "kv_attn_decode_evict_one_workspace",
+    "KVPages", "kv_attn_decode_paged", "kv_erase_paged_workspace", "kv_erase_ranges_paged",
     "kv_attn_decode_asm", "kv_attn_decode_asm_workspace", "kv_attn_decode_asm_splits",
     "asm_lookup_merge", "asm_lookup_merge_hier", "asm_lookup_merge_hier_workspace",
     "kv_latent_absorb", "kv_latent_absorb_workspace", "kv_latent_read",

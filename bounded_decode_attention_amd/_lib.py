@@ -28,6 +28,11 @@ class _Cache(ctypes.Structure):
                 ("start", ctypes.c_void_p)]
 
 
+class _Pages(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("fill", ctypes.c_void_p),
+                ("n_pages", ctypes.c_void_p), ("max_pages", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -42,6 +47,7 @@ def library():
         L = ctypes.CDLL(_LIB_PATH)
         P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         CP = ctypes.POINTER(_Cache)
+        PP = ctypes.POINTER(_Pages)
         sigs = {
             "kvb_strerror": (ctypes.c_char_p, [I32]),
             "kv_attn_decode_splits": (I32, [CP, I32]),
@@ -72,6 +78,10 @@ def library():
             "kv_attn_decode_compact": (I32, [CP, P, I32, P, F, I32, I32, I32, P, P, P, SZ, P, SZ,
                                              P]),
             "kv_erase_ranges": (I32, [CP, P, P, I32, P, P, SZ, P]),
+            "kv_attn_decode_paged": (I32, [CP, PP, P, I32, P, F, P, P, P, P, I32, P, P, P, SZ,
+                                           P]),
+            "kv_erase_paged_workspace": (SZ, [CP, PP]),
+            "kv_erase_ranges_paged": (I32, [CP, PP, P, P, I32, P, P, SZ, P]),
             "asm_lookup_merge": (I32, [P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, P, P,
                                        SZ, P]),
             "asm_lookup_merge_hier": (I32, [P, I32, I32, I32, I32, P, I32, P, P, P, I32, I32, P,
@@ -175,6 +185,31 @@ class KVCache:
     @classmethod
     def from_dict(cls, d):
         return cls(d["k"], d["v"], d.get("log_beta"), d["pos"], d["len"], d.get("start"))
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+
+class KVPages:
+    """Page table of a paged cache (32-slot pages; see kvb_pages in kvbound.h).
+
+    table    [B][Hkv][max_pages] int32 physical page of each logical page
+    fill     [B][Hkv][max_pages] int32 live slots of each logical page (1..32)
+    n_pages  [B][Hkv] int32 logical pages in use
+    """
+
+    def __init__(self, table, fill, n_pages):
+        _need(table, "table", torch.int32)
+        _need(fill, "fill", torch.int32)
+        _need(n_pages, "n_pages", torch.int32)
+        if table.dim() != 3 or fill.shape != table.shape or \
+                tuple(n_pages.shape) != tuple(table.shape[:2]):
+            raise ValueError("table, fill must be [B][Hkv][max_pages] and n_pages [B][Hkv]")
+        self.table, self.fill, self.n_pages = table, fill, n_pages
+        self.max_pages = table.shape[2]
+        self._desc = _Pages(table.data_ptr(), fill.data_ptr(), n_pages.data_ptr(),
+                            self.max_pages)
 
     @property
     def desc(self):
@@ -570,6 +605,61 @@ def kv_erase_ranges(cache: KVCache, ranges, n_ranges, n_erased=None, ws=None, st
     return n_erased
 
 
+def kv_attn_decode_paged(cache: KVCache, pages: KVPages, q, t, scale: float = 0.0, k_new=None,
+                         v_new=None, log_beta_new=None, spare=None, num_splits: int = 0,
+                         out=None, lse=None, ws=None, stream=None, check_status: bool = False):
+    """kv_attn_decode over a paged cache; the decode token (optional) goes into the
+    last page, or the free page spare [B][Hkv] int32.  Returns (out, lse)."""
+    _need(q, "q", cache.k.dtype)
+    _need(t, "t", torch.int32)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x is not None:
+            _need(x, name, cache.k.dtype)
+    if log_beta_new is not None:
+        _need(log_beta_new, "log_beta_new", torch.float32)
+    if spare is not None:
+        _need(spare, "spare", torch.int32)
+    ws = _ws(ws, kv_attn_decode_workspace(cache, Hq, num_splits), q.device)
+    st = library().kv_attn_decode_paged(cache.desc, pages.desc, _ptr(q), Hq, _ptr(t),
+                                        float(scale), _ptr(k_new), _ptr(v_new),
+                                        _ptr(log_beta_new), _ptr(spare), int(num_splits),
+                                        _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                        _stream(stream))
+    _check(st, "kv_attn_decode_paged")
+    if check_status:
+        _check_ws(ws, stream, "kv_attn_decode_paged (device status)")
+    return out, lse
+
+
+def kv_erase_paged_workspace(cache: KVCache, pages: KVPages) -> int:
+    return int(library().kv_erase_paged_workspace(cache.desc, pages.desc))
+
+
+def kv_erase_ranges_paged(cache: KVCache, pages: KVPages, ranges, n_ranges, n_erased=None,
+                          ws=None, stream=None):
+    """Block-granular erase of half-open position ranges ([B][R][2] int32) over a
+    paged cache: fully erased pages leave the table, partial pages compact in place."""
+    _need(ranges, "ranges", torch.int32)
+    _need(n_ranges, "n_ranges", torch.int32)
+    if ranges.dim() != 3 or ranges.shape[-1] != 2:
+        raise ValueError("ranges must be [B][R][2]")
+    if n_erased is None:
+        n_erased = torch.empty((cache.B, cache.Hkv), dtype=torch.int32, device=ranges.device)
+    ws = _ws(ws, kv_erase_paged_workspace(cache, pages), ranges.device)
+    st = library().kv_erase_ranges_paged(cache.desc, pages.desc, _ptr(ranges), _ptr(n_ranges),
+                                         ranges.shape[1], _ptr(n_erased), _ptr(ws), ws.numel(),
+                                         _stream(stream))
+    _check(st, "kv_erase_ranges_paged")
+    return n_erased
+
+
 def asm_lookup_merge(q, centroids, abar, log_zbar, self_out, self_lse, out=None, out_lse=None,
                      idx=None, ws=None, stream=None):
     """Cosine-argmax codebook lookup + merge with the query's own state.
@@ -607,7 +697,8 @@ TRACE_BITS = {"attn_split": 1, "attn_merge": 2, "append": 4, "evict_select": 8,
               "asm_prefix_merge": 2048, "km_assign": 4096, "km_update": 8192,
               "asm_aggregate": 16384, "asm_vt": 32768, "latent_absorb": 65536,
               "latent_read": 131072, "evict_one": 262144, "erase_search": 524288,
-              "erase_plan": 1048576, "one_shift": 4194304}
+              "erase_plan": 1048576, "one_shift": 4194304,
+              "erase_pages": 8388608}
 
 
 def asm_lookup_merge_hier_workspace(B, Hq, Hkv, K1, m) -> int:

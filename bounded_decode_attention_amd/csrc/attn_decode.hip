@@ -66,6 +66,13 @@ struct AttnArgs {
   int32_t* status = nullptr;
   // one-eviction candidates (kv_attn_decode_plan_one): [U][P] per split; null: none
   OneCand* cand = nullptr;
+  // paged cache (kv_attn_decode_paged): page table, fills, pages in use per head,
+  // the caller's free pages for the decode token
+  const int32_t* pg_table = nullptr;
+  const int32_t* pg_fill = nullptr;
+  const int32_t* pg_n = nullptr;
+  const int32_t* pg_spare = nullptr;
+  int32_t pg_max = 0;
 };
 
 // ------------------------------------------------------------------ append
@@ -772,6 +779,162 @@ void attn_split_asm(AttnArgs a, AsmScanArgs c, int crow) {
   pipe128_split<G, LB, VEC, false>(a, blockIdx.x, (int)blockIdx.y - crow);
 }
 
+// ------------------------------------------------------------------ paged split
+// Loads of one page of a paged cache: physical page rows pr .. pr + 31 of the head,
+// the first fill of them live; rows past fill repeat the last live one (their
+// logits are masked by the caller), so every address stays inside the page.  Log
+// beta and pos are read four at a time (a page starts on a multiple of 32 slots).
+__device__ __forceinline__ void issue_page128(const uint16_t* kb, const uint16_t* vb,
+                                              const float* lbb, const int32_t* pb, int pr,
+                                              int fill, int lane, KTile& t,
+                                              lds_u8* __restrict__ vlds) {
+  const int lg = lane >> 4, lc = lane & 15;
+  const int last = max(fill, 1) - 1;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = pr + min(16 * j + lc, last);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      t.k[j][kk] = *(const u32x4*)(kb + (ptrdiff_t)row * 128 + 32 * kk + 8 * lg);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = pr + min(4 * i + lg, last);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (ptrdiff_t)row * 128 + 8 * lc),
+                                     (lds_void_t*)(vlds + i * kVBlk), 16, 0, kNonTemporal);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rb = pr + 16 * j + 4 * lg;
+    const f32x4 l4 = __builtin_nontemporal_load((const f32x4*)(lbb + rb));
+    const i32x4 p4 = __builtin_nontemporal_load((const i32x4*)(pb + rb));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      t.lb[j][r] = l4[r];
+      t.ps[j][r] = p4[r];
+    }
+  }
+}
+
+// One split (p, head u) of the attention over a paged cache: split p takes the
+// head's logical pages p, p + P, ... (each one 32-slot tile), with the same
+// two-stage pipeline and arithmetic as pipe128_split.  The split's page numbers
+// and fills are loaded 64 at a time (lane i: the split's i-th page) and read per
+// page with a lane read.
+template <int G, bool LB>
+__device__ __forceinline__ void pipe128_paged(const AttnArgs& a, const int p, const int u) {
+  static_assert(2 * G <= 16, "group too large for the hi/lo column split");
+  __shared__ __attribute__((aligned(16))) unsigned char vbufA_[8 * kVBlk];
+  __shared__ __attribute__((aligned(16))) unsigned char vbufB_[8 * kVBlk];
+  lds_u8* vbufA = (lds_u8*)vbufA_;
+  lds_u8* vbufB = (lds_u8*)vbufB_;
+  const int b = u / a.Hkv;
+  const int g = u - b * a.Hkv;
+  const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int lc = lane & 15;
+  const int np = min(max(a.pg_n[u], 0), a.pg_max);
+  const int pages = a.cap / 32;
+  const int32_t* ptab = a.pg_table + (size_t)u * a.pg_max;
+  const int32_t* pfil = a.pg_fill + (size_t)u * a.pg_max;
+  if (a.n_rec && p == 0 && lane == 0) {
+    // the merge appends the decode token: record whether it has room (the last page
+    // has a free slot, or the caller's free page can be appended)
+    const bool room = (np > 0 && pfil[np - 1] < 32) ||
+                      (a.pg_spare && a.pg_spare[u] >= 0 && a.pg_spare[u] < pages && np < a.pg_max);
+    a.n_rec[u] = room ? min(max(a.len[u], 0), a.cap - 1) : a.cap;
+  }
+  if (a.status && p == 0 && u == 0 && lane == 0) a.status[0] = KVB_OK;
+  const size_t head0 = (size_t)u * a.cap;
+
+  const int hcol = lc < G ? lc : (lc < 2 * G ? lc - G : -1);
+  u32x4 qv[4];
+  {
+    const uint16_t* qp =
+        (const uint16_t*)a.q + ((size_t)(b * a.Hq + g * G + (hcol < 0 ? 0 : hcol))) * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qv[kk] = hcol >= 0 ? *(const u32x4*)(qp + 32 * kk + 8 * lg) : z;
+    }
+  }
+  const uint16_t* kb = (const uint16_t*)a.k + head0 * 128;
+  const uint16_t* vb = (const uint16_t*)a.v + head0 * 128;
+  const int32_t* pb = a.pos + head0;
+  const float* lbb = LB ? a.log_beta + head0 : (const float*)pb;
+  const int qpos = a.t[b];
+  const float sc = a.scale_log2;
+
+  float m2 = kNegInf, lsum = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int Pl = gridDim.x;
+  const int ntiles = p < np ? (np - p + Pl - 1) / Pl : 0;
+  int pe = 0, pf = 0;  // lane i: page and fill of the split's tile (64 c + i)
+  auto load_pages = [&](int k0) {
+    const int idx = p + (k0 + lane) * Pl;
+    pe = idx < np ? min(max(ptab[idx], 0), pages - 1) : 0;
+    pf = idx < np ? min(max(pfil[idx], 0), 32) : 0;
+  };
+  auto page_of = [&](int k, int& pr, int& f) {
+    if ((k & 63) == 0 && k > 0) load_pages(k);
+    pr = 32 * __builtin_amdgcn_readlane(pe, k & 63);
+    f = __builtin_amdgcn_readlane(pf, k & 63);
+  };
+  KTile tA, tB;
+  if (ntiles > 0) {
+    load_pages(0);
+    int prA, fA, prB, fB;
+    page_of(0, prA, fA);
+    issue_page128(kb, vb, lbb, pb, prA, fA, lane, tA, vbufA);
+    int k = 0;
+    for (; k + 1 < ntiles; k += 2) {
+      wait_vmem_all();
+      page_of(k + 1, prB, fB);
+      issue_page128(kb, vb, lbb, pb, prB, fB, lane, tB, vbufB);
+      compute_tile128<G>(tA, vbufA, 0, fA, lane, qv, sc, qpos, LB, m2, lsum, acc);
+      wait_vmem_all();
+      if (k + 2 < ntiles) {
+        page_of(k + 2, prA, fA);
+        issue_page128(kb, vb, lbb, pb, prA, fA, lane, tA, vbufA);
+      }
+      compute_tile128<G>(tB, vbufB, 0, fB, lane, qv, sc, qpos, LB, m2, lsum, acc);
+    }
+    if (k < ntiles) {
+      wait_vmem_all();
+      compute_tile128<G>(tA, vbufA, 0, fA, lane, qv, sc, qpos, LB, m2, lsum, acc);
+    }
+  }
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int src = lane + G < 64 ? lane + G : lane;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nb][i] = (acc[nb][i] + __shfl(acc[nb][i], src, 64)) * inv;
+  if (lc < G) {
+    const int h = g * G + lc;
+    const size_t sidx = ((size_t)(b * a.Hq + h)) * a.P + p;
+    float* pa = a.part_a + sidx * 128;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) *(f32x4*)(pa + 16 * nb + 4 * lg) = acc[nb];
+    if (lg == 0) {
+      a.part_ml[2 * sidx] = m2 == kNegInf ? kNegInf : m2 * kLn2;
+      a.part_ml[2 * sidx + 1] = lsum;
+    }
+  }
+}
+
+template <int G, bool LB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_split_paged(AttnArgs a) {
+  pipe128_paged<G, LB>(a, blockIdx.x, blockIdx.y);
+}
+
 // The candidate scan alone (one wave per task), where the splits are not the
 // pipelined kernel.
 template <int D>
@@ -905,10 +1068,46 @@ struct NewTok {
   int32_t* status;
   int32_t cap, Hkv, elem;
   float scale;         // natural-log scale of q.k
+  // paged cache: the token goes into the last page or the caller's free page
+  int32_t* pg_table;
+  int32_t* pg_fill;
+  int32_t* pg_n;
+  const int32_t* pg_spare;
+  int32_t pg_max;
 };
 
 __device__ __forceinline__ float load_elem(const void* p, size_t i, int elem) {
   return elem == 2 ? bf16_bits_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+// The decode token of head u into a paged cache, by the nthr threads of the merge
+// workgroup of the head's first query head (the split kernel found room: the last
+// page has a free slot, or the caller's free page can be appended to the table).
+__device__ __forceinline__ void paged_append(const NewTok& nt, int u, int tid, int nthr) {
+  const int np = min(max(nt.pg_n[u], 0), nt.pg_max);
+  const int lf = np > 0 ? min(max(nt.pg_fill[(size_t)u * nt.pg_max + np - 1], 0), 32) : 32;
+  const bool last = np > 0 && lf < 32;
+  const int page = last ? nt.pg_table[(size_t)u * nt.pg_max + np - 1] : nt.pg_spare[u];
+  const int pages = nt.cap / 32;
+  const int slot = min(max(page, 0), pages - 1) * 32 + (last ? lf : 0);
+  const int words = 128 * nt.elem / 4;
+  const size_t dst = ((size_t)u * nt.cap + slot) * words;
+  for (int w = tid; w < words; w += nthr) {
+    ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
+    ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
+  }
+  if (tid == 0) {
+    nt.pos[(size_t)u * nt.cap + slot] = nt.t[u / nt.Hkv];
+    if (nt.log_beta) nt.log_beta[(size_t)u * nt.cap + slot] = nt.lb_new[u];
+    if (last) {
+      nt.pg_fill[(size_t)u * nt.pg_max + np - 1] = lf + 1;
+    } else {
+      nt.pg_table[(size_t)u * nt.pg_max + np] = page;
+      nt.pg_fill[(size_t)u * nt.pg_max + np] = 1;
+      nt.pg_n[u] = np + 1;
+    }
+    nt.len[u] = nt.n_rec[u] + 1;
+  }
 }
 
 template <int kMergeThreads>
@@ -1058,7 +1257,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
   if (tid == 0) lse[bh] = lse_out;
   // append the decode token (first query head of each KV head); every split has
   // read the old len, and the other merge blocks use the recorded one
-  if (nt.k_new && bh % G == 0) {
+  if (nt.k_new && bh % G == 0 && nt.pg_table) {
+    if (incl) paged_append(nt, u, tid, kMergeThreads);
+    else if (tid == 0) nt.status[0] = KVB_ECAPACITY;
+  } else if (nt.k_new && bh % G == 0) {
     if (!incl) {
       if (tid == 0) nt.status[0] = KVB_ECAPACITY;
     } else {
@@ -1274,7 +1476,10 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
   // read the old len, and the other merge blocks use the recorded one.  With an
   // eviction above the token goes into the evicted slot (not at all when it is the
   // evicted one) and len stays.
-  if (nt.k_new && bh % G == 0) {
+  if (nt.k_new && bh % G == 0 && nt.pg_table) {
+    if (incl) paged_append(nt, u, tid, D);
+    else if (tid == 0) nt.status[0] = KVB_ECAPACITY;
+  } else if (nt.k_new && bh % G == 0) {
     if (!incl) {
       if (tid == 0) nt.status[0] = KVB_ECAPACITY;
     } else {
@@ -1470,6 +1675,20 @@ static int32_t launch_split(const kvb_cache* c, const AttnArgs& a, hipStream_t s
   return KVB_EUNSUPPORTED;
 }
 
+static int32_t launch_paged(const kvb_cache* c, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.P, c->B * c->Hkv);
+  const bool lb = c->log_beta != nullptr;
+#define KVB_PAGED_CASE(GG)                                                                 \
+  if (a.G == GG) {                                                                         \
+    if (lb) hipLaunchKernelGGL((attn_split_paged<GG, true>), grid, dim3(64), 0, s, a);     \
+    else hipLaunchKernelGGL((attn_split_paged<GG, false>), grid, dim3(64), 0, s, a);       \
+    return KVB_OK;                                                                         \
+  }
+  KVB_PAGED_CASE(1) KVB_PAGED_CASE(2) KVB_PAGED_CASE(4) KVB_PAGED_CASE(8)
+#undef KVB_PAGED_CASE
+  return KVB_EUNSUPPORTED;
+}
+
 // Candidate-scan dimensions of kv_attn_decode_asm: QB blocks of 16 query rows per KV
 // head, KC chunks of kScanChunk centroids, one task per (chunk, head, 64 rows).
 static AsmScanArgs scan_dims(int B, int Hq, int Hkv, int K) {
@@ -1547,7 +1766,8 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
                                 size_t ws_bytes, hipStream_t stream, const AsmTail* tail,
                                 int32_t* status = nullptr,
                                 const AsmScanArgs* scan = nullptr,
-                                const OnePlan* one = nullptr) {
+                                const OnePlan* one = nullptr, const kvb_pages* pages = nullptr,
+                                const int32_t* spare = nullptr) {
   int32_t st = check_cache(cache, true);
   if (st) return st;
   if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
@@ -1615,7 +1835,20 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
     nt.elem = cache->dtype == KVB_BF16 ? 2 : 4;
     nt.scale = a.scale_log2 * kLn2;
   }
-  {
+  if (pages) {
+    a.pg_table = pages->table;
+    a.pg_fill = pages->fill;
+    a.pg_n = pages->n_pages;
+    a.pg_spare = spare;
+    a.pg_max = pages->max_pages;
+    nt.pg_table = pages->table;
+    nt.pg_fill = pages->fill;
+    nt.pg_n = pages->n_pages;
+    nt.pg_spare = spare;
+    nt.pg_max = pages->max_pages;
+    TraceScope tr(kTrAttnSplit, s);
+    if ((st = launch_paged(cache, a, s))) return st;
+  } else {
     TraceScope tr(kTrAttnSplit, s);
     if ((st = launch_split(cache, a, s, scan, one))) return st;
   }
@@ -1634,6 +1867,38 @@ extern "C" int32_t kv_attn_decode(const kvb_cache* cache, const void* q, int32_t
                                   size_t ws_bytes, void* stream) {
   return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, num_splits, out,
                           lse, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+// Splits of the paged attention: about 2048 workgroups, at most one per 8 pages a
+// head can hold, never more than kv_attn_decode_workspace's own default.
+static int32_t paged_splits(const kvb_cache* c, const kvb_pages* pg) {
+  const long long units = (long long)c->B * c->Hkv;
+  long long P = (2048 + units - 1) / units;
+  const long long per = pg->max_pages / 8;
+  if (P > per) P = per;
+  if (P > auto_splits(c)) P = auto_splits(c);
+  if (P < 1) P = 1;
+  return (int32_t)P;
+}
+
+extern "C" int32_t kv_attn_decode_paged(const kvb_cache* cache, const kvb_pages* pages,
+                                        const void* q, int32_t Hq, const int32_t* t, float scale,
+                                        const void* k_new, const void* v_new,
+                                        const float* log_beta_new, const int32_t* spare,
+                                        int32_t num_splits, float* out, float* lse, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  int32_t st = check_cache(cache, true);
+  if (st) return st;
+  if (!pages || !pages->table || !pages->fill || !pages->n_pages || pages->max_pages < 1)
+    return KVB_EINVAL;
+  if (cache->start || cache->cap % 32 != 0) return KVB_EINVAL;
+  if (Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
+  if (!mfma_supported(cache, Hq / cache->Hkv) || cache->D != 128) return KVB_EUNSUPPORTED;
+  if (num_splits < 0 || num_splits > 4096) return KVB_EINVAL;
+  const int32_t P = num_splits > 0 ? num_splits : paged_splits(cache, pages);
+  return attn_decode_impl(cache, q, Hq, t, scale, k_new, v_new, log_beta_new, P, out, lse, ws,
+                          ws_bytes, (hipStream_t)stream, nullptr, nullptr, nullptr, nullptr,
+                          pages, spare);
 }
 
 extern "C" int32_t kv_attn_decode_plan_one(const kvb_cache* cache, const void* q, int32_t Hq,

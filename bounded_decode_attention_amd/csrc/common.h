@@ -331,7 +331,8 @@ enum TraceKernel {
   kTrAttnFused = 512, kTrAsmPrefix = 1024, kTrAsmPrefixMerge = 2048, kTrKmAssign = 4096,
   kTrKmUpdate = 8192, kTrAsmAggregate = 16384, kTrAsmVt = 32768,
   kTrLatentAbsorb = 65536, kTrLatentRead = 131072, kTrEvictOne = 262144,
-  kTrEraseSearch = 524288, kTrErasePlan = 1048576, kTrOneShift = 4194304
+  kTrEraseSearch = 524288, kTrErasePlan = 1048576, kTrOneShift = 4194304,
+  kTrErasePages = 8388608
 };
 struct TraceScope {
   TraceScope(int kernel, hipStream_t s);

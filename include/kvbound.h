@@ -95,6 +95,26 @@ typedef struct {
   int32_t* start;
 } kvb_cache;
 
+/*
+ * Paged form of a cache ([MEM] system engineering: entries removed by whole blocks
+ * within one generate call).  A head's live tokens sit in pages of 32 slots; the
+ * page table lists its pages in position order.  Physical page p of head u is slots
+ * [32p, 32p + 32) of that head's cap slots in the kvb_cache arrays; a page holds
+ * its live tokens in its first fill slots, in position order.
+ *   table      [B][Hkv][max_pages] int32 physical page of each logical page
+ *   fill       [B][Hkv][max_pages] int32 live slots of each logical page, 1..32
+ *   n_pages    [B][Hkv] int32 logical pages in use (0..max_pages)
+ *   max_pages  entries per head of table and fill
+ * The kvb_cache's len holds each head's live-token total (the sum of its fills);
+ * its start must be NULL.  Physical pages must lie below cap / 32 and be distinct.
+ */
+typedef struct {
+  int32_t* table;
+  int32_t* fill;
+  int32_t* n_pages;
+  int32_t max_pages;
+} kvb_pages;
+
 /* Violation bits written by kv_check_cache, per KV head. */
 enum {
   KVB_CHECK_LEN = 1,               /* len < 0 or len > cap                                */
@@ -389,6 +409,43 @@ int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q, int32_t Hq
                                float scale, int32_t M, int32_t num_splits, int32_t phase,
                                float* out, float* lse, void* ws, size_t ws_bytes, void* ws_evict,
                                size_t ws_evict_bytes, void* stream);
+
+/*
+ * kv_attn_decode over a paged cache (see kvb_pages; bf16, D = 128, Hq / Hkv in
+ * {1, 2, 4, 8}): the same attention over each head's live tokens, taken page by
+ * page.  A decode token (k_new != NULL) is written into the last page when it has
+ * room, otherwise into the caller's free physical page spare[b][g] (appended to
+ * the table; spare NULL or < 0, or a full table: the token is neither stored nor
+ * attended and the status word becomes KVB_ECAPACITY), with pos = t[b]; len and
+ * the page arrays are updated.
+ *   spare      [B][Hkv] int32 or NULL
+ *   ws         kv_attn_decode_workspace(cache, Hq, num_splits) bytes
+ * Other arguments as kv_attn_decode; num_splits 0 takes about 2048 / (B * Hkv)
+ * splits, at most one per 8 pages of max_pages.
+ */
+int32_t kv_attn_decode_paged(const kvb_cache* cache, const kvb_pages* pages, const void* q,
+                             int32_t Hq, const int32_t* t, float scale, const void* k_new,
+                             const void* v_new, const float* log_beta_new,
+                             const int32_t* spare, int32_t num_splits, float* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_erase_ranges over a paged cache, block-granular ([MEM] blocks and compression;
+ * system engineering): a page whose live positions all lie in the sequence's
+ * ranges leaves the table (its rows are not touched; the page is free for the
+ * caller), a page none of whose positions does stays as it is, and a page with
+ * both keeps its surviving rows, in order, in its first slots (the only rows that
+ * move).  The table keeps the remaining pages in order; n_pages, fill and len are
+ * updated.  A cache whose erased blocks start and end on page boundaries moves no
+ * row at all.
+ *   ranges, n_ranges, R, n_erased  as kv_erase_ranges (at most 4096 ranges per
+ *              sequence)
+ *   ws         kv_erase_paged_workspace(cache, pages) bytes
+ */
+size_t kv_erase_paged_workspace(const kvb_cache* cache, const kvb_pages* pages);
+int32_t kv_erase_ranges_paged(const kvb_cache* cache, const kvb_pages* pages,
+                              const int32_t* ranges, const int32_t* n_ranges, int32_t R,
+                              int32_t* n_erased, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Erase position ranges from every KV head of a sequence and compact in place

@@ -29,7 +29,8 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "bf16_bits", "bf16_to_f64", "f32_bits",
     "host_cache", "host_queries", "host_new_tokens", "host_codebook",
-    "memento_layout", "device_cache", "device_queries", "device_codebook",
+    "memento_layout", "memento_pages", "host_paged", "device_cache", "device_queries",
+    "device_codebook",
 ]
 
 
@@ -316,6 +317,63 @@ def memento_layout(total: int = 1 << 20, seed: int = 1005, memento: int = 200,
         p += L + memento
     ranges = np.array([(s, s + L) for (s, L, mlen) in blocks if mlen > 0], np.int32)
     return blocks, ranges.reshape(-1, 2)
+
+
+def memento_pages(blocks, H: int, seed: int = 1005, page: int = 32, spare: int = 64):
+    """Paged layout of a MEMENTO trace in which every thinking block and every
+    memento starts on a fresh page (its last page is partly filled).
+
+    Physical pages are drawn per head as a seeded permutation of ``n + spare``
+    pages (n: the pages the trace uses), so the table is out of physical order.
+    Returns (table [H][n] int32, fill [n] int32, first position of each page [n]
+    int32, physical pages per head).
+    """
+    fill, pos0 = [], []
+    for (s, L, mlen) in blocks:
+        for (a, m) in ((s, L), (s + L, mlen)):
+            for o in range(0, m, page):
+                fill.append(min(page, m - o))
+                pos0.append(a + o)
+    n = len(fill)
+    phys = n + spare
+    rng = np.random.Generator(np.random.PCG64(seed + 77))
+    table = np.stack([rng.permutation(phys)[:n] for _ in range(H)]).astype(np.int32)
+    return table, np.array(fill, np.int32), np.array(pos0, np.int32), phys
+
+
+def host_paged(rng, B: int, H: int, D: int, n_pages_max: int, max_pages: int,
+               phys: int, retention: bool = True, full_fill: float = 0.5, gap: int = 2):
+    """A small random paged cache: per head a run of pages (count uniform in
+    [0, n_pages_max]) on distinct physical pages out of ``phys``, fills uniform in
+    1..32 (32 with probability ``full_fill``), positions ascending along the table
+    with gaps uniform in [1, gap].  K, V ~ N(0, 1) as bf16 bits over every slot.
+    Returns dict k, v (uint16), log_beta, pos, len, table, fill, n_pages."""
+    cap = 32 * phys
+    k = bf16_bits(rng.standard_normal((B, H, cap, D)))
+    v = bf16_bits(rng.standard_normal((B, H, cap, D)))
+    lb = (_log_sigmoid_f32((rng.standard_normal((B, H, cap)) * 1.5 + 2.0).astype(np.float32))
+          if retention else None)
+    pos = np.zeros((B, H, cap), np.int32)
+    table = np.full((B, H, max_pages), -1, np.int32)
+    fill = np.zeros((B, H, max_pages), np.int32)
+    n_pages = np.zeros((B, H), np.int32)
+    length = np.zeros((B, H), np.int32)
+    for b in range(B):
+        for g in range(H):
+            n = int(rng.integers(0, n_pages_max + 1))
+            perm = rng.permutation(phys)[:n]
+            p = int(rng.integers(0, 50))
+            for i in range(n):
+                f = 32 if rng.random() < full_fill else int(rng.integers(1, 33))
+                steps = rng.integers(1, gap + 1, size=f)
+                pp = p + np.cumsum(steps)
+                pos[b, g, 32 * perm[i]:32 * perm[i] + f] = pp
+                p = int(pp[-1])
+                table[b, g, i], fill[b, g, i] = perm[i], f
+                length[b, g] += f
+            n_pages[b, g] = n
+    return {"k": k, "v": v, "log_beta": lb, "pos": pos, "len": length, "table": table,
+            "fill": fill, "n_pages": n_pages}
 
 
 # --------------------------------------------------------------------------

@@ -414,3 +414,61 @@ def test_plan_one_entries_reject_arguments_before_launch():
         assert plan() == -5
         assert apply() == -5
         assert one() == -5
+
+
+@needs_lib
+def test_paged_entries_reject_arguments_before_launch():
+    """kv_attn_decode_paged / kv_erase_ranges_paged: fake pointers; missing page
+    arrays, a start array, a capacity off the 32-slot pages, unsupported shapes and
+    short workspaces are refused on the host; valid calls without a GPU stop at the
+    device check.  The erase workspace formula."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    good = _desc(cap=128)
+    pages = _lib._Pages(200, 208, 216, 6)
+    no_fill = _lib._Pages(200, None, 216, 6)
+    wsa = L.kv_attn_decode_workspace(ctypes.byref(good), 8, 0)
+
+    def attn(c=good, pg=pages, Hq=8, splits=0, ws_bytes=wsa):
+        # q, Hq, t, scale, k_new, v_new, log_beta_new, spare, num_splits, out, lse, ws
+        return L.kv_attn_decode_paged(ctypes.byref(c), None if pg is None else ctypes.byref(pg),
+                                      P(64), Hq, P(72), 0.0, None, None, None, None, splits,
+                                      P(80), P(88), P(4096), ws_bytes, None)
+    assert attn(pg=None) == -1
+    assert attn(pg=no_fill) == -1
+    assert attn(pg=_lib._Pages(200, 208, 216, 0)) == -1
+    assert attn(c=_desc(cap=100)) == -1                 # not whole pages
+    st = _desc(cap=128)
+    st.start = 32
+    assert attn(c=st) == -1
+    assert attn(Hq=7) == -1
+    assert attn(Hq=32) == -2                            # group of 16
+    assert attn(c=_desc(cap=128, D=64)) == -2
+    assert attn(splits=4097) == -1
+    assert attn(ws_bytes=300) == -4
+    need = L.kv_erase_paged_workspace(ctypes.byref(good), ctypes.byref(pages))
+    U, mp, NB = 4, 6, 1
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert need == 256 + 3 * a256(U * mp * 4) + a256(U * NB * 12)
+    big = _lib._Pages(200, 208, 216, 1000)
+    assert L.kv_erase_paged_workspace(ctypes.byref(good), ctypes.byref(big)) == \
+        256 + 3 * a256(U * 1000 * 4) + a256(U * 4 * 12)
+    assert L.kv_erase_paged_workspace(ctypes.byref(good), None) == 0
+
+    def erase(c=good, pg=pages, R=2, ranges=P(300), nr=P(308), ws=P(4096), ws_bytes=need):
+        return L.kv_erase_ranges_paged(ctypes.byref(c), None if pg is None else ctypes.byref(pg),
+                                       ranges, nr, R, None, ws, ws_bytes, None)
+    assert erase(pg=None) == -1
+    assert erase(pg=no_fill) == -1
+    assert erase(c=_desc(cap=100)) == -1
+    assert erase(c=st) == -1
+    assert erase(R=-1) == -1
+    assert erase(ranges=None) == -1
+    assert erase(nr=None) == -1
+    assert erase(ws=None) == -4
+    assert erase(ws_bytes=need - 1) == -4
+    assert erase(c=_desc(cap=128, B=300, Hkv=256)) == -2   # B * Hkv above 65535
+    if not _has_gpu():
+        assert attn() == -5
+        assert erase() == -5
+        assert erase(R=0, ranges=None) == -5

@@ -1,0 +1,322 @@
+"""Paged cache: kv_attn_decode_paged and kv_erase_ranges_paged against the oracle
+(its page-by-page erase and append, attention over the pages' token sequence)."""
+import numpy as np
+import pytest
+import torch
+
+import bounded_decode_attention_amd as kvb
+import oracle
+import oracle.evict as OE
+import synth
+from gpu_util import check_attention, say, to_dev, to_host, values
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(d):
+    c = kvb.KVCache(to_dev(d["k"]), to_dev(d["v"]), to_dev(d["log_beta"]), to_dev(d["pos"]),
+                    to_dev(d["len"]))
+    pg = kvb.KVPages(to_dev(d["table"]), to_dev(d["fill"]), to_dev(d["n_pages"]))
+    return c, pg
+
+
+def _host(d):
+    c = OE.Cache(d["k"].copy(), d["v"].copy(),
+                 None if d["log_beta"] is None else d["log_beta"].copy(), d["pos"].copy(),
+                 d["len"].copy())
+    return c, OE.Pages(d["table"].copy(), d["fill"].copy(), d["n_pages"].copy())
+
+
+def _check_pages(c, pg, ref, rpg, what):
+    """Page arrays (live entries), len, and every row of the cache arrays bit for bit
+    (rows the oracle leaves alone must be left alone too)."""
+    n = to_host(pg.n_pages)
+    assert np.array_equal(n, rpg.n_pages), f"{what} n_pages {n} vs {rpg.n_pages}"
+    tab, fil = to_host(pg.table), to_host(pg.fill)
+    B, H = n.shape
+    for b in range(B):
+        for g in range(H):
+            m = int(n[b, g])
+            assert np.array_equal(tab[b, g, :m], rpg.table[b, g, :m]), f"{what} table ({b},{g})"
+            assert np.array_equal(fil[b, g, :m], rpg.fill[b, g, :m]), f"{what} fill ({b},{g})"
+    assert np.array_equal(to_host(c.length), ref.length), f"{what} len"
+    for name in ("k", "v", "pos", "log_beta"):
+        a = getattr(ref, name)
+        if a is None:
+            continue
+        got = to_host(getattr(c, name))
+        if not np.array_equal(got.view(np.uint8), a.view(np.uint8)):
+            bad = np.argwhere(np.any((got != a).reshape(B, H, a.shape[2], -1), axis=3))
+            raise AssertionError(f"{what} {name} differs at {bad[:8].tolist()}")
+
+
+def _view_dict(c, pg):
+    v = OE.paged_view(c, pg)
+    return {"k": v.k, "v": v.v, "log_beta": v.log_beta, "pos": v.pos, "len": v.length}
+
+
+def _attend_case(seed, G, retention, n_pages_max, max_pages, phys, num_splits, token,
+                 spare_mode="some", full_fill=0.5):
+    rng = np.random.default_rng(seed)
+    B, H, D = 2, 2, 128
+    d = synth.host_paged(rng, B, H, D, n_pages_max, max_pages, phys, retention, full_fill)
+    say(f"paged attend seed={seed} G={G} lb={retention} pages<={n_pages_max} "
+        f"max={max_pages} phys={phys} P={num_splits} token={token} spare={spare_mode}")
+    q = synth.bf16_bits(rng.standard_normal((B, G * H, D)))
+    t = np.array([int(d["pos"][b].max()) + 3 for b in range(B)], np.int32)
+    c, pg = _dev(d)
+    hc, hpg = _host(d)
+    kw = {}
+    stored = np.ones((B, H), bool)
+    if token:
+        kn = synth.bf16_bits(rng.standard_normal((B, H, D)))
+        vn = synth.bf16_bits(rng.standard_normal((B, H, D)))
+        ln = (rng.uniform(-0.5, 0.0, (B, H)).astype(np.float32) if retention else None)
+        # a free physical page per head: one no page of the head uses, or none
+        spare = np.full((B, H), -1, np.int32)
+        for b in range(B):
+            for g in range(H):
+                used = set(d["table"][b, g, :d["n_pages"][b, g]].tolist())
+                free = [p for p in range(phys) if p not in used]
+                if free and (spare_mode == "all" or (spare_mode == "some" and (b + g) % 3 != 2)):
+                    spare[b, g] = free[int(rng.integers(0, len(free)))]
+        kw = dict(k_new=to_dev(kn), v_new=to_dev(vn), log_beta_new=to_dev(ln),
+                  spare=to_dev(spare))
+        # the oracle attends over the sequence with the token where it was stored
+        stored = OE.paged_append(hc, hpg, kn, vn, ln, t, spare)
+    # a head without room attends over its cached tokens alone (the oracle's append
+    # leaves it as it was)
+    ref = _view_dict(hc, hpg)
+    out, lse = kvb.kv_attn_decode_paged(c, pg, to_dev(q), to_dev(t), num_splits=num_splits, **kw)
+    if token and not stored.all():
+        with pytest.raises(kvb.KVBError):
+            kvb.kv_attn_decode_paged(*_dev(d), to_dev(q), to_dev(t), num_splits=num_splits,
+                                     check_status=True, **kw)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_attention(values(ref["k"]), values(ref["v"]), ref["log_beta"],
+                                     ref["pos"], ref["len"], values(q), t)
+    check_attention(to_host(out), to_host(lse), ro, rl, f"paged seed={seed}")
+    _check_pages(c, pg, hc, hpg, f"paged append seed={seed}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("retention", [True, False])
+def test_paged_attention_vs_oracle(G, retention):
+    _attend_case(100 + G, G, retention, n_pages_max=9, max_pages=12, phys=14, num_splits=3,
+                 token=False)
+    _attend_case(200 + G, G, retention, n_pages_max=9, max_pages=12, phys=14, num_splits=0,
+                 token=True)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 5, 64])
+def test_paged_attention_splits(num_splits):
+    """Splits with no page, one page, and (P = 1) more than 64 pages per split (the
+    page list is reloaded every 64 pages)."""
+    _attend_case(300 + num_splits, 4, True, n_pages_max=150, max_pages=160, phys=170,
+                 num_splits=num_splits, token=True)
+
+
+def test_paged_append_room_cases():
+    """Decode token: into the last page (room), onto the free page (full last page),
+    or refused (no free page): KVB_ECAPACITY and the token not attended."""
+    _attend_case(401, 2, True, n_pages_max=4, max_pages=6, phys=8, num_splits=2, token=True,
+                 spare_mode="some", full_fill=1.0)
+    _attend_case(402, 2, True, n_pages_max=4, max_pages=6, phys=8, num_splits=2, token=True,
+                 spare_mode="all", full_fill=1.0)
+    _attend_case(403, 8, False, n_pages_max=4, max_pages=6, phys=8, num_splits=0, token=True,
+                 spare_mode="all", full_fill=0.0)
+    # a full table: no room even with a free page
+    _attend_case(404, 1, True, n_pages_max=4, max_pages=4, phys=8, num_splits=1, token=True,
+                 spare_mode="all", full_fill=1.0)
+
+
+def _erase_case(seed, n_pages_max, max_pages, phys, n_ranges, retention=True, D=128,
+                aligned=False):
+    rng = np.random.default_rng(seed)
+    B, H = 2, 3
+    d = synth.host_paged(rng, B, H, D, n_pages_max, max_pages, phys, retention)
+    say(f"paged erase seed={seed} pages<={n_pages_max} max={max_pages} ranges={n_ranges} "
+        f"aligned={aligned}")
+    top = int(d["pos"].max()) + 5
+    R = max(n_ranges, 1)
+    ranges = np.zeros((B, R, 2), np.int32)
+    nr = np.zeros(B, np.int32)
+    hr = []
+    for b in range(B):
+        if aligned:
+            # ranges that start and end on page boundaries of head (b, 0)
+            starts = [int(d["pos"][b, 0, 32 * d["table"][b, 0, i]])
+                      for i in range(d["n_pages"][b, 0])] + [top]
+            cut = np.sort(rng.choice(len(starts), size=min(2 * n_ranges, len(starts) // 2 * 2),
+                                     replace=False))
+            edges = np.array([starts[i] for i in cut], np.int64)
+        else:
+            edges = np.sort(rng.choice(top, size=2 * n_ranges, replace=False))
+        rr = edges.reshape(-1, 2).astype(np.int32)
+        ranges[b, :rr.shape[0]] = rr
+        nr[b] = rr.shape[0]
+        hr.append(rr.astype(np.int64))
+    c, pg = _dev(d)
+    hc, hpg = _host(d)
+    n_er = kvb.kv_erase_ranges_paged(c, pg, to_dev(ranges), to_dev(nr))
+    torch.cuda.synchronize()
+    rc, rpg, rn = OE.erase_pages(hc, hpg, hr)
+    assert np.array_equal(to_host(n_er), rn), f"n_erased {to_host(n_er)} vs {rn}"
+    _check_pages(c, pg, rc, rpg, f"paged erase seed={seed}")
+    return d, rc, rpg
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_paged_erase_vs_oracle(seed):
+    _erase_case(500 + seed, n_pages_max=10, max_pages=12, phys=14, n_ranges=4)
+
+
+def test_paged_erase_many_pages_and_ranges():
+    """More than one workgroup of pages per head (the new index of a workgroup's
+    first surviving page sums the ones before it), hundreds of ranges."""
+    _erase_case(601, n_pages_max=700, max_pages=720, phys=740, n_ranges=300)
+    _erase_case(602, n_pages_max=600, max_pages=1030, phys=620, n_ranges=3, retention=False)
+
+
+def test_paged_erase_aligned_moves_nothing():
+    """Ranges on page boundaries drop whole pages: no page survives in part."""
+    d, rc, rpg = _erase_case(701, n_pages_max=40, max_pages=40, phys=44, n_ranges=6,
+                             aligned=True)
+    for b in range(2):
+        old = {int(d["table"][b, 0, i]): int(d["fill"][b, 0, i])
+               for i in range(d["n_pages"][b, 0])}
+        for i in range(rpg.n_pages[b, 0]):
+            assert rpg.fill[b, 0, i] == old[int(rpg.table[b, 0, i])], "a page survived in part"
+
+
+def test_paged_erase_edge_cases():
+    """No ranges (identity), a range over everything (every page leaves), float32
+    rows of D = 64, empty heads."""
+    _erase_case(801, n_pages_max=6, max_pages=8, phys=9, n_ranges=0)
+    rng = np.random.default_rng(802)
+    d = synth.host_paged(rng, 1, 2, 128, 6, 8, 9)
+    c, pg = _dev(d)
+    rg = torch.tensor([[[0, 1 << 30]]], dtype=torch.int32, device="cuda")
+    n_er = kvb.kv_erase_ranges_paged(c, pg, rg, torch.ones(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert to_host(pg.n_pages).tolist() == [[0, 0]] and to_host(c.length).tolist() == [[0, 0]]
+    assert to_host(n_er).tolist() == d["len"].tolist()
+    # float32 rows, D = 64
+    rng = np.random.default_rng(803)
+    d = synth.host_paged(rng, 2, 2, 64, 8, 8, 10)
+    d["k"] = synth.bf16_to_f64(d["k"]).astype(np.float32)
+    d["v"] = synth.bf16_to_f64(d["v"]).astype(np.float32)
+    c, pg = _dev(d)
+    hc, hpg = _host(d)
+    rr = [np.array([[5, 40], [90, 200]], np.int64), np.array([[0, 33]], np.int64)]
+    ranges = np.zeros((2, 2, 2), np.int32)
+    ranges[0] = rr[0]
+    ranges[1, :1] = rr[1]
+    kvb.kv_erase_ranges_paged(c, pg, to_dev(ranges), to_dev(np.array([2, 1], np.int32)))
+    torch.cuda.synchronize()
+    rc, rpg, _ = OE.erase_pages(hc, hpg, rr)
+    _check_pages(c, pg, rc, rpg, "paged erase f32")
+
+
+def test_paged_erase_then_decode_steps():
+    """Erase, then decode steps whose tokens fill the last page and move on to free
+    pages, each step's attention against the oracle's sequence."""
+    d, rc, rpg = _erase_case(901, n_pages_max=8, max_pages=16, phys=20, n_ranges=3)
+    rng = np.random.default_rng(902)
+    B, H, D, G = 2, 3, 128, 2
+    d2 = {"k": rc.k, "v": rc.v, "log_beta": rc.log_beta, "pos": rc.pos, "len": rc.length,
+          "table": rpg.table, "fill": rpg.fill, "n_pages": rpg.n_pages}
+    c, pg = _dev(d2)
+    hc, hpg = _host(d2)
+    t = np.array([int(d["pos"][b].max()) + 1 for b in range(B)], np.int32)
+    for step in range(40):
+        q = synth.bf16_bits(rng.standard_normal((B, G * H, D)))
+        kn = synth.bf16_bits(rng.standard_normal((B, H, D)))
+        vn = synth.bf16_bits(rng.standard_normal((B, H, D)))
+        ln = rng.uniform(-0.5, 0.0, (B, H)).astype(np.float32)
+        spare = np.full((B, H), -1, np.int32)
+        for b in range(B):
+            for g in range(H):
+                used = set(hpg.table[b, g, :hpg.n_pages[b, g]].tolist())
+                spare[b, g] = min(p for p in range(20) if p not in used)
+        stored = OE.paged_append(hc, hpg, kn, vn, ln, t, spare)
+        assert stored.all()
+        out, lse = kvb.kv_attn_decode_paged(c, pg, to_dev(q), to_dev(t), k_new=to_dev(kn),
+                                            v_new=to_dev(vn), log_beta_new=to_dev(ln),
+                                            spare=to_dev(spare), num_splits=2)
+        torch.cuda.synchronize()
+        ref = _view_dict(hc, hpg)
+        ro, rl = oracle.decode_attention(values(ref["k"]), values(ref["v"]), ref["log_beta"],
+                                         ref["pos"], ref["len"], values(q), t)
+        check_attention(to_host(out), to_host(lse), ro, rl, f"paged step {step}")
+        t = t + 1
+    _check_pages(c, pg, hc, hpg, "paged steps")
+
+
+def test_paged_memento_full_size():
+    """The 1M-slot MEMENTO trace laid out with every block and memento on fresh
+    pages: erase the completed blocks (whole pages, no row moves), append the
+    decode token, attend; sampled heads against the oracle."""
+    w = synth.WORKLOADS["memento_1m"]
+    blocks, ranges = synth.memento_layout(total=w.ctx, seed=w.seed)
+    table, fill, pos0, phys = synth.memento_pages(blocks, w.hkv, seed=w.seed)
+    n = table.shape[1]
+    say("paged memento pages", n, "phys", phys, "ranges", ranges.shape)
+    cap = 32 * phys
+    dc = synth.device_cache(w, layer=0, n=cap, cap=cap)
+    pos = np.zeros((w.hkv, cap), np.int32)
+    for g in range(w.hkv):
+        for i in range(n):
+            pos[g, 32 * table[g, i]:32 * table[g, i] + fill[i]] = pos0[i] + np.arange(fill[i])
+    dc["pos"].copy_(torch.from_numpy(pos[None]))
+    dc["len"].fill_(int(fill.sum()))
+    c = kvb.KVCache.from_dict(dc)
+    mp = n + 8
+    tab = np.full((1, w.hkv, mp), -1, np.int32)
+    tab[0, :, :n] = table
+    fil = np.zeros((1, w.hkv, mp), np.int32)
+    fil[0, :, :n] = fill
+    pg = kvb.KVPages(to_dev(tab), to_dev(fil), to_dev(np.full((1, w.hkv), n, np.int32)))
+    # pages that stay: those whose first position lies in no range
+    erased = np.zeros(n, bool)
+    for s, e in ranges:
+        erased |= (pos0 >= s) & (pos0 < e)
+    keep = np.nonzero(~erased)[0]
+    kept = int(fill[keep].sum())
+    k_before = {g: to_host(c.k[0, g]) for g in (0, 5)}
+    rg = torch.from_numpy(ranges[None].copy()).cuda()
+    nr = torch.tensor([ranges.shape[0]], dtype=torch.int32, device="cuda")
+    n_er = kvb.kv_erase_ranges_paged(c, pg, rg, nr)
+    torch.cuda.synchronize()
+    assert (to_host(n_er) == w.ctx - kept).all()
+    assert (to_host(pg.n_pages) == keep.size).all() and (to_host(c.length) == kept).all()
+    th = to_host(pg.table)
+    for g in range(w.hkv):
+        assert np.array_equal(th[0, g, :keep.size], table[g, keep]), f"table g={g}"
+        assert np.array_equal(to_host(pg.fill)[0, g, :keep.size], fill[keep])
+    for g in (0, 5):
+        assert np.array_equal(to_host(c.k[0, g]), k_before[g]), "a whole-page erase moved rows"
+    q, kn, vn, _ = synth.device_queries(w, 0)
+    t = torch.full((1,), w.ctx, dtype=torch.int32, device="cuda")
+    free = [min(set(range(phys)) - set(table[g].tolist())) for g in range(w.hkv)]
+    spare = torch.tensor([free], dtype=torch.int32, device="cuda")
+    out, lse = kvb.kv_attn_decode_paged(c, pg, q, t, k_new=kn, v_new=vn, spare=spare,
+                                        check_status=True)
+    torch.cuda.synchronize()
+    assert (to_host(c.length) == kept + 1).all()
+    G = w.group
+    oh, lh, qh = to_host(out), to_host(lse), to_host(q)
+    knh, vnh = to_host(kn), to_host(vn)
+    for g in (0, 5):
+        rows = np.concatenate([np.arange(32 * table[g, i], 32 * table[g, i] + fill[i])
+                               for i in keep])
+        kk = np.concatenate([k_before[g][rows], knh[0, g][None]])[None, None]
+        vv = np.concatenate([to_host(c.v[0, g])[rows], vnh[0, g][None]])[None, None]
+        pp = np.concatenate([pos[g][rows], [w.ctx]])[None, None]
+        ro, rl = oracle.decode_attention(values(kk), values(vv), None, pp,
+                                         np.array([[kept + 1]]),
+                                         values(qh[:, g * G:(g + 1) * G]), np.array([w.ctx]))
+        check_attention(oh[:, g * G:(g + 1) * G], lh[:, g * G:(g + 1) * G], ro, rl,
+                        f"paged memento attention g={g}")
+    del dc, c
+    torch.cuda.empty_cache()
