@@ -867,6 +867,8 @@ def memento_bench(args):
     # rule applied to it (about 2048 / (B * Hkv) splits, at most one per 256 live
     # slots) instead of to the 1M-slot capacity (512 splits)
     P_att = max(1, min(2048 // w.units, (kept + 1) // 256))
+    if args.splits > 0:
+        P_att = args.splits
     ws_a = torch.empty(kvb.kv_attn_decode_workspace(c, w.hq, P_att), dtype=torch.uint8,
                        device="cuda")
     ws_ev = torch.empty(kvb.kv_evict_workspace(c, w.budget), dtype=torch.uint8, device="cuda")
@@ -991,6 +993,8 @@ def memento_paged_bench(args):
     # split count by the library's rule applied to the pages left after the erase
     # (about 2048 / (B * Hkv) splits, at most one per 8 pages)
     P_att = max(1, min(2048 // w.units, (keep.size + 1) // 8))
+    if args.splits > 0:
+        P_att = args.splits
     ws_a = torch.empty(kvb.kv_attn_decode_workspace(c, w.hq, P_att), dtype=torch.uint8,
                        device="cuda")
     n_er = torch.empty((1, w.hkv), dtype=torch.int32, device="cuda")

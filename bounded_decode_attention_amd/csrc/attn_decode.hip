@@ -1080,10 +1080,26 @@ __device__ __forceinline__ float load_elem(const void* p, size_t i, int elem) {
   return elem == 2 ? bf16_bits_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
 
+// Word tid of head u's decode-token K and V rows, for the merge block that appends
+// it (loaded with the merge's first round of loads; D * elem / 4 <= D words, so
+// every word has a thread).
+__device__ __forceinline__ void token_words(const NewTok& nt, int u, int D, int tid, bool mine,
+                                            uint32_t& kx, uint32_t& vx) {
+  kx = vx = 0u;
+  const int words = D * nt.elem / 4;
+  if (mine && tid < words) {
+    kx = ((const uint32_t*)nt.k_new)[(size_t)u * words + tid];
+    vx = ((const uint32_t*)nt.v_new)[(size_t)u * words + tid];
+  }
+}
+
 // The decode token of head u into a paged cache, by the nthr threads of the merge
 // workgroup of the head's first query head (the split kernel found room: the last
 // page has a free slot, or the caller's free page can be appended to the table).
-__device__ __forceinline__ void paged_append(const NewTok& nt, int u, int tid, int nthr) {
+// kx, vx: word tid of the token's K and V rows (loaded by the caller; every word of
+// the row has a thread).
+__device__ __forceinline__ void paged_append(const NewTok& nt, int u, int tid, uint32_t kx,
+                                             uint32_t vx) {
   const int np = min(max(nt.pg_n[u], 0), nt.pg_max);
   const int lf = np > 0 ? min(max(nt.pg_fill[(size_t)u * nt.pg_max + np - 1], 0), 32) : 32;
   const bool last = np > 0 && lf < 32;
@@ -1092,9 +1108,9 @@ __device__ __forceinline__ void paged_append(const NewTok& nt, int u, int tid, i
   const int slot = min(max(page, 0), pages - 1) * 32 + (last ? lf : 0);
   const int words = 128 * nt.elem / 4;
   const size_t dst = ((size_t)u * nt.cap + slot) * words;
-  for (int w = tid; w < words; w += nthr) {
-    ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
-    ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
+  if (tid < words) {
+    ((uint32_t*)nt.k)[dst + tid] = kx;
+    ((uint32_t*)nt.v)[dst + tid] = vx;
   }
   if (tid == 0) {
     nt.pos[(size_t)u * nt.cap + slot] = nt.t[u / nt.Hkv];
@@ -1110,6 +1126,32 @@ __device__ __forceinline__ void paged_append(const NewTok& nt, int u, int tid, i
   }
 }
 
+// Sum and maximum over a workgroup of NT threads: wave butterflies, then the NT / 64
+// wave results from LDS in wave order (two barriers; `s` may be reused after).
+template <int NT>
+__device__ __forceinline__ float merge_block_sum(float x, float* s) {
+  x = wave_sum(x);
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t += s[i];
+  __syncthreads();
+  return t;
+}
+
+template <int NT>
+__device__ __forceinline__ float merge_block_max(float x, float* s) {
+  x = wave_max(x);
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float t = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t = fmaxf(t, s[i]);
+  __syncthreads();
+  return t;
+}
+
 template <int kMergeThreads>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
                                                             const float* part_ml, int P, int D,
@@ -1118,7 +1160,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
                                                             int G, NewTok nt, AsmTail at) {
   __shared__ float w[kMergeMaxP];
   __shared__ int s_k;  // the lookup's entry (with an ASM tail)
-  __shared__ float red[kMergeThreads];
+  __shared__ float red[kMergeThreads / 64];
   __shared__ float gsum[kMergeThreads];
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
@@ -1135,6 +1177,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
   for (int e = 0; e < kB; ++e) x[e] = p0 + e < p1 ? pa[(size_t)(p0 + e) * D + d] : 0.f;
   // the decode token's logit (when it is appended here)
   const int u = bh / G;
+  uint32_t tkx, tvx;
+  token_words(nt, u, D, tid, nt.k_new && bh % G == 0, tkx, tvx);
   bool incl = false;
   float s_new = kNegInf;
   if (nt.k_new) {
@@ -1143,26 +1187,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     if (incl && tid < D)
       pr = load_elem(nt.q, (size_t)bh * D + tid, nt.elem) *
            load_elem(nt.k_new, (size_t)u * D + tid, nt.elem);
-    red[tid] = pr;
-    __syncthreads();
-    for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
-      if (tid < o) red[tid] += red[tid + o];
-      __syncthreads();
-    }
-    if (incl) s_new = red[0] * nt.scale;
-    __syncthreads();
+    pr = merge_block_sum<kMergeThreads>(pr, red);
+    if (incl) s_new = pr * nt.scale;
   }
   float mx = kNegInf;
   for (int p = tid; p < P; p += kMergeThreads)
     if (ml[2 * p + 1] > 0.f) mx = fmaxf(mx, ml[2 * p]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float M = fmaxf(red[0], s_new);
-  __syncthreads();
+  const float M = fmaxf(merge_block_max<kMergeThreads>(mx, red), s_new);
   float ws = 0.f;
   for (int p = tid; p < P; p += kMergeThreads) {
     const float Zp = ml[2 * p + 1];
@@ -1170,14 +1201,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
     w[p] = wp;
     ws += wp;
   }
-  red[tid] = ws;
-  __syncthreads();
-  for (int o = kMergeThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
+  const float wsum = merge_block_sum<kMergeThreads>(ws, red);  // also orders the w[] stores
   const float w_new = incl ? __expf(s_new - M) : 0.f;
-  const float W = red[0] + w_new;
+  const float W = wsum + w_new;
   float o = 0.f;
 #pragma unroll
   for (int e = 0; e < kB; ++e)
@@ -1258,7 +1284,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
   // append the decode token (first query head of each KV head); every split has
   // read the old len, and the other merge blocks use the recorded one
   if (nt.k_new && bh % G == 0 && nt.pg_table) {
-    if (incl) paged_append(nt, u, tid, kMergeThreads);
+    if (incl) paged_append(nt, u, tid, tkx, tvx);
     else if (tid == 0) nt.status[0] = KVB_ECAPACITY;
   } else if (nt.k_new && bh % G == 0) {
     if (!incl) {
@@ -1269,9 +1295,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
       if (s0 >= nt.cap) s0 -= nt.cap;
       const int words = D * nt.elem / 4;
       const size_t dst = ((size_t)u * nt.cap + s0) * words;
-      for (int w = tid; w < words; w += kMergeThreads) {
-        ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
-        ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
+      if (tid < words) {
+        ((uint32_t*)nt.k)[dst + tid] = tkx;
+        ((uint32_t*)nt.v)[dst + tid] = tvx;
       }
       if (tid == 0) {
         nt.pos[(size_t)u * nt.cap + s0] = nt.t[u / nt.Hkv];
@@ -1292,7 +1318,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* part_a,
 // states, decode token, lookup candidates), a few shuffles, the chosen entry's
 // gather and the stores.  Same arithmetic per output as attn_merge up to the
 // order of the per-dimension sum (here split by split, in order).
-template <int D>
+template <int D, int kB>
 __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const float* part_ml,
                                                       int P, float* out, float* lse,
                                                       const UnitInfo* info, int32_t* len,
@@ -1307,12 +1333,14 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
   const float* ml = part_ml + (size_t)bh * P * 2;
   const float* pa = part_a + (size_t)bh * P * D;
   const int u = bh / G;
-  // every load of the first round: this dimension's split outputs (first 16), the
-  // split (m, Z) in wave 0, the decode token's q.k product terms, the candidates
-  constexpr int kB = 16;
+  // every load of the first round: this dimension's split outputs (the first kB:
+  // all of them when P <= kB), the split (m, Z) in wave 0, the decode token's q.k
+  // product terms and its row, the candidates
   float x[kB];
 #pragma unroll
   for (int e = 0; e < kB; ++e) x[e] = e < P ? pa[(size_t)e * D + tid] : 0.f;
+  uint32_t tkx, tvx;
+  token_words(nt, u, D, tid, nt.k_new && bh % G == 0, tkx, tvx);
   float mp = kNegInf, zp = 0.f;
   if (wave == 0 && lane < P) {
     mp = ml[2 * lane];
@@ -1477,7 +1505,7 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
   // eviction above the token goes into the evicted slot (not at all when it is the
   // evicted one) and len stays.
   if (nt.k_new && bh % G == 0 && nt.pg_table) {
-    if (incl) paged_append(nt, u, tid, D);
+    if (incl) paged_append(nt, u, tid, tkx, tvx);
     else if (tid == 0) nt.status[0] = KVB_ECAPACITY;
   } else if (nt.k_new && bh % G == 0) {
     if (!incl) {
@@ -1489,9 +1517,9 @@ __global__ __launch_bounds__(D) void attn_merge_small(const float* part_a, const
         if (s0 >= nt.cap) s0 -= nt.cap;
         const int words = D * nt.elem / 4;
         const size_t dst = ((size_t)u * nt.cap + s0) * words;
-        for (int w = tid; w < words; w += D) {
-          ((uint32_t*)nt.k)[dst + w] = ((const uint32_t*)nt.k_new)[(size_t)u * words + w];
-          ((uint32_t*)nt.v)[dst + w] = ((const uint32_t*)nt.v_new)[(size_t)u * words + w];
+        if (tid < words) {
+          ((uint32_t*)nt.k)[dst + tid] = tkx;
+          ((uint32_t*)nt.v)[dst + tid] = tvx;
         }
         if (tid == 0) {
           nt.pos[(size_t)u * nt.cap + s0] = nt.t[u / nt.Hkv];
@@ -1559,14 +1587,23 @@ static bool launch_merge(const float* part_a, const float* part_ml, int P, int D
   OnePlan no_plan;
   memset(&no_plan, 0, sizeof(no_plan));
   const OnePlan& op = one ? *one : no_plan;
+  // the small merge loads every split's output in one round (16 or 64 per thread)
   if (P <= 64 && D == 128) {
-    hipLaunchKernelGGL(attn_merge_small<128>, dim3(BH), dim3(128), 0, s, part_a, part_ml, P, out,
-                       lse, info, len, G, n, at, op);
+    if (P <= 16)
+      hipLaunchKernelGGL((attn_merge_small<128, 16>), dim3(BH), dim3(128), 0, s, part_a,
+                         part_ml, P, out, lse, info, len, G, n, at, op);
+    else
+      hipLaunchKernelGGL((attn_merge_small<128, 64>), dim3(BH), dim3(128), 0, s, part_a,
+                         part_ml, P, out, lse, info, len, G, n, at, op);
     return true;
   }
   if (P <= 64 && D == 64) {
-    hipLaunchKernelGGL(attn_merge_small<64>, dim3(BH), dim3(64), 0, s, part_a, part_ml, P, out,
-                       lse, info, len, G, n, at, op);
+    if (P <= 16)
+      hipLaunchKernelGGL((attn_merge_small<64, 16>), dim3(BH), dim3(64), 0, s, part_a, part_ml,
+                         P, out, lse, info, len, G, n, at, op);
+    else
+      hipLaunchKernelGGL((attn_merge_small<64, 64>), dim3(BH), dim3(64), 0, s, part_a, part_ml,
+                         P, out, lse, info, len, G, n, at, op);
     return true;
   }
   if (P > 128)

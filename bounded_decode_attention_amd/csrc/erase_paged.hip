@@ -107,8 +107,35 @@ __device__ __forceinline__ int pg_block_sum(int x, int* s_red) {
   return t;
 }
 
+// Kept rows of one page (count and mask) from its f positions pr[0 .. f).
+__device__ __forceinline__ int page_keep(const int32_t* rg, int nr, const int32_t* pr, int f,
+                                         uint32_t& m) {
+  m = 0u;
+  if (f <= 0) return 0;
+  const int p0 = pr[0], pl = pr[f - 1];
+  int j = range_after(rg, nr, p0);
+  if (j >= nr || rg[2 * j] > pl) {
+    m = f == 32 ? 0xFFFFFFFFu : (1u << f) - 1u;  // no range meets the page's positions
+    return f;
+  }
+  if (rg[2 * j] <= p0 && rg[2 * j + 1] > pl) return 0;  // one range covers them
+  int kc = 0;
+  for (int r = 0; r < f; ++r) {
+    const int p = pr[r];
+    while (j < nr && rg[2 * j + 1] <= p) ++j;
+    if (!(j < nr && rg[2 * j] <= p)) {
+      m |= 1u << r;
+      ++kc;
+    }
+  }
+  return kc;
+}
+
+constexpr int kPgLdsRanges = 1024;  // ranges searched in LDS (more: from global memory)
+
 __global__ __launch_bounds__(kPgThreads) void pg_classify(PgArgs a) {
   __shared__ int s_red[kPgThreads / 64];
+  __shared__ int32_t s_rg[2 * kPgLdsRanges];
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
   const int i = blockIdx.x * kPgThreads + threadIdx.x;
@@ -116,33 +143,23 @@ __global__ __launch_bounds__(kPgThreads) void pg_classify(PgArgs a) {
   const int pages = a.cap / 32;
   const int nr = min(max(a.n_ranges[b], 0), a.R);
   const int32_t* rg = a.ranges + (size_t)b * a.R * 2;
-  int kc = -1, f = 0;
+  const bool in_lds = nr <= kPgLdsRanges;
+  if (in_lds)
+    for (int x = threadIdx.x; x < 2 * nr; x += kPgThreads) s_rg[x] = rg[x];
+  int kc = -1, f = 0, pe = 0;
+  size_t e = 0;
   if (i < a.max_pages) {
-    const size_t e = (size_t)u * a.max_pages + i;
-    const int pe = a.table[e];
+    e = (size_t)u * a.max_pages + i;
+    pe = a.table[e];
+    if (i < np) f = min(max(a.fill[e], 0), 32);
+  }
+  __syncthreads();
+  if (i < a.max_pages) {
     a.tcopy[e] = pe;
     uint32_t m = 0u;
     if (i < np) {
-      f = min(max(a.fill[e], 0), 32);
       const int32_t* pr = a.pos + (size_t)u * a.cap + 32 * (size_t)min(max(pe, 0), pages - 1);
-      kc = 0;
-      if (f > 0) {
-        const int p0 = pr[0], pl = pr[f - 1];
-        int j = range_after(rg, nr, p0);
-        if (j >= nr || rg[2 * j] > pl) {
-          kc = f;  // no range meets the page's positions
-          m = f == 32 ? 0xFFFFFFFFu : (1u << f) - 1u;
-        } else if (!(rg[2 * j] <= p0 && rg[2 * j + 1] > pl)) {
-          for (int r = 0; r < f; ++r) {
-            const int p = pr[r];
-            while (j < nr && rg[2 * j + 1] <= p) ++j;
-            if (!(j < nr && rg[2 * j] <= p)) {
-              m |= 1u << r;
-              ++kc;
-            }
-          }
-        }
-      }
+      kc = in_lds ? page_keep(s_rg, nr, pr, f, m) : page_keep(rg, nr, pr, f, m);
     }
     a.kc[e] = kc;
     a.mask[e] = m;

@@ -176,6 +176,8 @@ def test_paged_erase_many_pages_and_ranges():
     first surviving page sums the ones before it), hundreds of ranges."""
     _erase_case(601, n_pages_max=700, max_pages=720, phys=740, n_ranges=300)
     _erase_case(602, n_pages_max=600, max_pages=1030, phys=620, n_ranges=3, retention=False)
+    # more ranges than the classification keeps in LDS: searched in global memory
+    _erase_case(603, n_pages_max=300, max_pages=300, phys=310, n_ranges=1100)
 
 
 def test_paged_erase_aligned_moves_nothing():
