@@ -94,7 +94,9 @@ __global__ __launch_bounds__(256) void latent_list(LatentArgs a) {
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // 16-byte LDS slot holding token chunk c (8 tokens) of row d (rows of 64 tokens).
-__device__ __forceinline__ int lat_slot(int d, int c) { return c ^ ((d >> 1) & 7); }
+// The operand reads (rows 16T .. 16T + 15, one chunk) hit 16 distinct (row parity,
+// slot) pairs, and the stores (rows e, e + 8, ..., one chunk) all 8 slots, twice.
+__device__ __forceinline__ int lat_slot(int d, int c) { return c ^ (((d >> 1) ^ (d >> 4)) & 7); }
 
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
@@ -113,9 +115,12 @@ void latent_absorb_part(LatentArgs a) {
   if (j0 >= ne || ne <= kLatSmall) return;
   const int j1 = min(ne, j0 + kLatChunk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
-  // each thread: tokens 2qd, 2qd + 1 of the tile x one 16-byte chunk ch, of k and of v
-  const int qd = tid & 31, ch = tid >> 5;
-  const bool act = CPR == 16 || ch < CPR;  // (all threads for D = 128)
+  // each thread: tokens qd and qd + 32 of the tile x one 16-byte chunk ch, of k and
+  // of v; consecutive threads take consecutive chunks of a row, so one wave's load
+  // reads whole rows.  An LDS word holds tokens (qd, qd + 32) of one dimension: the
+  // token order inside a tile is the same for both operands of the product.
+  const int ch = tid % CPR, qd = tid / CPR;
+  const bool act = qd < 32;  // (all threads for D = 128)
   const int32_t* evl = a.ev + (size_t)u * a.cap;
   const size_t uoff = (size_t)u * a.cap * D + (act ? ch : 0) * 8;
 
@@ -136,7 +141,7 @@ void latent_absorb_part(LatentArgs a) {
   u32x4 kr[2][2], vr[2][2];
   auto load_idx = [&](int P, int t0) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) rawi[P][r] = evl[min(t0 + 2 * qd + r, j1 - 1)];
+    for (int r = 0; r < 2; ++r) rawi[P][r] = evl[min(t0 + (act ? qd : 0) + 32 * r, j1 - 1)];
   };
   auto load_rows = [&](int P) {
     if (!act) return;
@@ -154,7 +159,7 @@ void latent_absorb_part(LatentArgs a) {
       float wt[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const int jj = t0 + 2 * qd + r;
+        const int jj = t0 + qd + 32 * r;
         wt[r] = jj < j1 ? exp2_fast((float)(j1 - 1 - jj) * a.log2_lam) : 0.f;
       }
       // one dimension at a time: the 2 tokens' weighted phi(k), split, and v (a
