@@ -46,6 +46,9 @@ int32_t check_cache(const kvb_cache* c, bool need_kv) {
   if (c->B < 1 || c->Hkv < 1 || c->cap < 1 || c->cap >= (1 << 30) || c->D < 1) return KVB_EINVAL;
   if (!c->pos || !c->len) return KVB_EINVAL;
   if (need_kv && (!c->k || !c->v)) return KVB_EINVAL;
+  // rows, positions and log betas are read 16 bytes at a time
+  auto mis = [](const void* p) { return ((uintptr_t)p & 15u) != 0; };
+  if (mis(c->k) || mis(c->v) || mis(c->pos) || mis(c->log_beta)) return KVB_EINVAL;
   if (c->dtype != KVB_F32 && c->dtype != KVB_BF16) return KVB_EUNSUPPORTED;
   if (c->D % 8 != 0 || c->D > 256) return KVB_EUNSUPPORTED;
   if (c->dtype == KVB_BF16 && c->D != 64 && c->D != 128) return KVB_EUNSUPPORTED;

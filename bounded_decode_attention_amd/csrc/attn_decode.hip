@@ -1808,6 +1808,7 @@ static int32_t attn_decode_impl(const kvb_cache* cache, const void* q, int32_t H
   int32_t st = check_cache(cache, true);
   if (st) return st;
   if (!q || !t || !out || !lse || Hq < 1 || Hq % cache->Hkv != 0) return KVB_EINVAL;
+  if (((uintptr_t)q & 15u) != 0) return KVB_EINVAL;  // query rows read 16 bytes at a time
   if ((k_new == nullptr) != (v_new == nullptr)) return KVB_EINVAL;
   if (k_new && cache->log_beta && !log_beta_new) return KVB_EINVAL;
   if (num_splits < 0 || num_splits > 4096) return KVB_EINVAL;

@@ -82,7 +82,9 @@ typedef enum { KVB_F32 = 0, KVB_BF16 = 1 } kvb_dtype;
  *             the decode token goes to slot (start + len) mod cap.  Without one,
  *             head u's live slots are 0 .. len[u] - 1.
  * The caller owns all of it.  Requires 1 <= B, Hkv; 1 <= cap < 2^30;
- * D in {64, 128} for KVB_BF16 (any 1 <= D <= 256 for KVB_F32); D % 8 == 0.
+ * D in {64, 128} for KVB_BF16 (any 1 <= D <= 256 for KVB_F32); D % 8 == 0;
+ * k, v, log_beta and pos 16-byte aligned (KVB_EINVAL otherwise), as is the query
+ * of the attention calls.
  */
 typedef struct {
   void* k;

@@ -51,7 +51,8 @@ def test_strerror():
 
 
 def _desc(**kw):
-    d = dict(k=8, v=8, log_beta=None, pos=16, len=24, B=2, Hkv=2, cap=100, D=128, dtype=1)
+    d = dict(k=4096, v=8192, log_beta=None, pos=12288, len=16384, B=2, Hkv=2, cap=100, D=128,
+             dtype=1)
     d.update(kw)
     return _lib._Cache(d["k"], d["v"], d["log_beta"], d["pos"], d["len"], d["B"], d["Hkv"],
                        d["cap"], d["D"], d["dtype"])
@@ -472,3 +473,20 @@ def test_paged_entries_reject_arguments_before_launch():
         assert attn() == -5
         assert erase() == -5
         assert erase(R=0, ranges=None) == -5
+
+
+@needs_lib
+def test_misaligned_pointers_rejected():
+    """Cache arrays and the query are read 16 bytes at a time: a pointer off a
+    16-byte boundary is refused on the host (KVB_EINVAL) before any launch."""
+    L = kvb.library()
+    P = ctypes.c_void_p
+    ws = P(1 << 20)
+    args = [P(64), 8, P(72), 0.0, None, None, None, 0, P(80), P(88), ws, 1 << 30, None]
+    for kw in (dict(k=4100), dict(v=8196), dict(pos=12292), dict(log_beta=20488)):
+        assert L.kv_attn_decode(ctypes.byref(_desc(**kw)), *args) == -1, kw
+        assert L.kv_evict_to_budget(ctypes.byref(_desc(**kw)), P(8), 5, None, 0, None, ws,
+                                    1 << 30, None) == -1, kw
+    assert L.kv_attn_decode(ctypes.byref(_desc()), P(68), *args[1:]) == -1
+    if not _has_gpu():
+        assert L.kv_attn_decode(ctypes.byref(_desc(log_beta=20480)), *args) == -5
