@@ -322,3 +322,97 @@ def test_paged_memento_full_size():
                         f"paged memento attention g={g}")
     del dc, c
     torch.cuda.empty_cache()
+
+
+def test_paged_erase_and_attention_graph_replay():
+    """The erase and the attention with its decode token captured in one HIP graph
+    on a user stream: every replay (inputs restored eagerly in between, queries
+    redrawn) equals the eager calls bit for bit, page arrays and rows included."""
+    rng = np.random.default_rng(1101)
+    B, H, D, G = 2, 2, 128, 4
+    d = synth.host_paged(rng, B, H, D, 9, 14, 16)
+    top = int(d["pos"].max()) + 5
+    ranges = np.zeros((B, 3, 2), np.int32)
+    for b in range(B):
+        ranges[b] = np.sort(rng.choice(top, size=6, replace=False)).reshape(3, 2)
+    nr = to_dev(np.array([3, 3], np.int32))
+    rg = to_dev(ranges)
+    t = to_dev(np.array([top + 1, top + 2], np.int32))
+    kn = to_dev(synth.bf16_bits(rng.standard_normal((B, H, D))))
+    vn = to_dev(synth.bf16_bits(rng.standard_normal((B, H, D))))
+    ln = to_dev(rng.uniform(-0.5, 0.0, (B, H)).astype(np.float32))
+    spare = np.full((B, H), -1, np.int32)
+    for b in range(B):
+        for g in range(H):
+            used = set(d["table"][b, g, :d["n_pages"][b, g]].tolist())
+            spare[b, g] = min(p for p in range(16) if p not in used)
+    spare = to_dev(spare)
+    c, pg = _dev(d)
+    pristine = {n: x.clone() for n, x in (("k", c.k), ("v", c.v), ("lb", c.log_beta),
+                                          ("pos", c.pos), ("len", c.length), ("tab", pg.table),
+                                          ("fill", pg.fill), ("np", pg.n_pages))}
+    live = {"k": c.k, "v": c.v, "lb": c.log_beta, "pos": c.pos, "len": c.length,
+            "tab": pg.table, "fill": pg.fill, "np": pg.n_pages}
+    q = torch.empty((B, G * H, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, G * H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, G * H), dtype=torch.float32, device="cuda")
+    n_er = torch.empty((B, H), dtype=torch.int32, device="cuda")
+    ws_e = torch.empty(kvb.kv_erase_paged_workspace(c, pg), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(kvb.kv_attn_decode_workspace(c, G * H, 0), dtype=torch.uint8,
+                       device="cuda")
+    user = torch.cuda.Stream()
+
+    def restore():
+        for n, x in live.items():
+            x.copy_(pristine[n])
+
+    def calls():
+        kvb.kv_erase_ranges_paged(c, pg, rg, nr, n_erased=n_er, ws=ws_e, stream=user)
+        kvb.kv_attn_decode_paged(c, pg, q, t, k_new=kn, v_new=vn, log_beta_new=ln, spare=spare,
+                                 out=out, lse=lse, ws=ws_a, stream=user)
+
+    def snapshot():
+        return {n: x.clone() for n, x in live.items()} | {"out": out.clone(), "lse": lse.clone(),
+                                                         "n_er": n_er.clone()}
+
+    def eager():
+        restore()
+        torch.cuda.synchronize()
+        calls()
+        user.synchronize()
+        return snapshot()
+
+    q.copy_(to_dev(synth.bf16_bits(rng.standard_normal((B, G * H, D)))))
+    torch.cuda.synchronize()
+    ref = eager()
+    # the eager result against the oracle (erase, append, attention)
+    hc, hpg = _host(d)
+    rc, rpg, rn = OE.erase_pages(hc, hpg, [ranges[b].astype(np.int64) for b in range(B)])
+    assert np.array_equal(to_host(ref["n_er"]), rn)
+    assert OE.paged_append(rc, rpg, to_host(kn), to_host(vn), to_host(ln), to_host(t),
+                           to_host(spare)).all()
+    v = _view_dict(rc, rpg)
+    ro, rl = oracle.decode_attention(values(v["k"]), values(v["v"]), v["log_beta"], v["pos"],
+                                     v["len"], values(to_host(q)), to_host(t))
+    check_attention(to_host(ref["out"]), to_host(ref["lse"]), ro, rl, "paged graph eager")
+    restore()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(user):
+        with torch.cuda.graph(graph, stream=user):
+            calls()
+    torch.cuda.synchronize()
+    for r in range(3):
+        say("paged graph replay", r)
+        q.copy_(to_dev(synth.bf16_bits(rng.standard_normal((B, G * H, D)))))
+        want = eager()
+        restore()
+        out.fill_(float("nan"))
+        n_er.fill_(-1)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(user):
+            graph.replay()
+        user.synchronize()
+        got = snapshot()
+        for n in want:
+            assert torch.equal(got[n], want[n]), f"replay {r}: {n}"
