@@ -1057,6 +1057,102 @@ def memento_paged_bench(args):
         "kernel_us": {k: round(float(np.median(v)), 1) for k, v in per.items()}}), flush=True)
 
 
+def paged_attn_bench(args):
+    """The 32K workload's attention over a paged cache: each KV head's 32,768 tokens
+    in 1024 full 32-slot pages placed on a seeded random permutation of 1032
+    physical pages, against the same tokens laid out contiguously (gathered page by
+    page on the device).  No decode token; the library's default split counts.
+    Both outputs are compared (within 2e-3); mean time per call over repeated calls
+    (HIP events, the calls queued behind a GPU spin)."""
+    import numpy as np
+    import torch
+
+    import bounded_decode_attention_amd as kvb
+    import synth
+
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    n = w.ctx
+    npg = n // 32
+    phys = npg + 8
+    cap = 32 * phys
+    dc = synth.device_cache(w, layer=0, n=cap, cap=cap)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 91))
+    table = np.stack([rng.permutation(phys)[:npg] for _ in range(w.units)]).astype(np.int32)
+    tab = torch.from_numpy(table).cuda().view(w.batch, w.hkv, npg)
+    # slot of logical token j: 32 * table[j / 32] + j % 32; positions = logical index
+    slot = (tab.long()[..., :, None] * 32 + torch.arange(32, device="cuda")).reshape(
+        w.batch, w.hkv, n)
+    pos = torch.zeros((w.batch, w.hkv, cap), dtype=torch.int32, device="cuda")
+    pos.scatter_(2, slot, torch.arange(n, dtype=torch.int32, device="cuda").expand(
+        w.batch, w.hkv, n).contiguous())
+    dc["pos"].copy_(pos)
+    dc["len"].fill_(n)
+    c = kvb.KVCache.from_dict(dc)
+    pg = kvb.KVPages(tab.contiguous(), torch.full((w.batch, w.hkv, npg), 32, dtype=torch.int32,
+                                                  device="cuda"),
+                     torch.full((w.batch, w.hkv), npg, dtype=torch.int32, device="cuda"))
+    # the same tokens contiguous, in logical order
+    cont = {}
+    for name in ("k", "v", "log_beta"):
+        x = dc[name]
+        if x is None:
+            cont[name] = None
+            continue
+        idx = slot if x.dim() == 3 else slot[..., None].expand(-1, -1, -1, w.head_dim)
+        cont[name] = torch.gather(x, 2, idx).contiguous()
+    cont["pos"] = torch.arange(n, dtype=torch.int32, device="cuda").expand(
+        w.batch, w.hkv, n).contiguous()
+    cont["len"] = torch.full((w.batch, w.hkv), n, dtype=torch.int32, device="cuda")
+    cc = kvb.KVCache.from_dict(cont)
+    q, _, _, _ = synth.device_queries(w, 0)
+    t = torch.full((w.batch,), n, dtype=torch.int32, device="cuda")
+    ws_p = torch.empty(kvb.kv_attn_decode_workspace(c, w.hq, 0), dtype=torch.uint8,
+                       device="cuda")
+    ws_c = torch.empty(kvb.kv_attn_decode_workspace(cc, w.hq, 0), dtype=torch.uint8,
+                       device="cuda")
+    outs = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(2_000_000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1000.0
+
+    def run_paged():
+        outs["p"] = kvb.kv_attn_decode_paged(c, pg, q, t, ws=ws_p)
+
+    def run_cont():
+        outs["c"] = kvb.kv_attn_decode(cc, q, t, ws=ws_c)
+
+    reps = max(args.steps, 20)
+    us_p = timed(run_paged, reps)
+    us_c = timed(run_cont, reps)
+    (op, lp), (oc, lc) = outs["p"], outs["c"]
+    den = oc.abs().amax(dim=-1).clamp_min(1e-30)
+    rel = float(((op - oc).abs().amax(dim=-1) / den).max())
+    dl = float((lp - lc).abs().max())
+    assert rel <= 2e-3 and dl <= 2e-3, (rel, dl)
+    by = algorithmic_bytes(w, n, 0)[0]
+    print(json.dumps({
+        "metric": "paged vs contiguous decode attention, one layer of the 32K workload",
+        "value": round(us_p, 2), "unit": "us", "n_gpus": 1, "reps": reps,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.head_dim, "tokens": n, "pages": npg, "physical_pages": phys},
+        "paged": {"us": round(us_p, 2), "gbps": round(by / (us_p * 1e-6) / 1e9, 1),
+                  "frac": round(by / (us_p * 1e-6) / 8e12, 4)},
+        "contiguous": {"us": round(us_c, 2), "gbps": round(by / (us_c * 1e-6) / 1e9, 1),
+                       "frac": round(by / (us_c * 1e-6) / 8e12, 4)},
+        "bytes": by, "max_rel_err_vs_contiguous": rel, "max_lse_diff": dl}), flush=True)
+
+
 def latent_bench(args):
     """Latent memory of evicted tokens, one layer of the 32K decode workload (batch
     16, 8 KV heads, D = 128): the update after the eviction of 32769 -> 4096 tokens
@@ -1184,7 +1280,8 @@ def main():
                          "(one JSON line)")
     ap.add_argument("--paged", action="store_true",
                     help="--memento: the same trial over a paged cache (block-granular "
-                         "erase, paged attention)")
+                         "erase, paged attention); alone: the 32K workload's attention "
+                         "over a paged cache against the contiguous one (one JSON line)")
     ap.add_argument("--latent", action="store_true",
                     help="time the latent memory of evicted tokens (update after the 32K "
                          "eviction, steady-state update, read-out; one JSON line)")
@@ -1213,6 +1310,9 @@ def main():
         return
     if args.memento and args.paged:
         memento_paged_bench(args)
+        return
+    if args.paged:
+        paged_attn_bench(args)
         return
     if args.memento:
         memento_bench(args)
