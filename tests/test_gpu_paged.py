@@ -416,3 +416,54 @@ def test_paged_erase_and_attention_graph_replay():
         got = snapshot()
         for n in want:
             assert torch.equal(got[n], want[n]), f"replay {r}: {n}"
+
+
+def test_paged_attention_full_size_32k():
+    """The 32K layer in 1024 full pages per head on a random permutation of the
+    physical pages (the launch configuration `bench.py --paged` times): identical
+    to the contiguous attention over the same tokens, and two heads' query groups
+    against the oracle."""
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    n, npg = w.ctx, w.ctx // 32
+    phys = npg + 8
+    cap = 32 * phys
+    dc = synth.device_cache(w, layer=0, n=cap, cap=cap)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 91))
+    table = np.stack([rng.permutation(phys)[:npg] for _ in range(w.units)]).astype(np.int32)
+    tab = torch.from_numpy(table).cuda().view(w.batch, w.hkv, npg)
+    slot = (tab.long()[..., :, None] * 32 + torch.arange(32, device="cuda")).reshape(
+        w.batch, w.hkv, n)
+    pos = torch.zeros((w.batch, w.hkv, cap), dtype=torch.int32, device="cuda")
+    pos.scatter_(2, slot, torch.arange(n, dtype=torch.int32, device="cuda").expand(
+        w.batch, w.hkv, n).contiguous())
+    dc["pos"].copy_(pos)
+    dc["len"].fill_(n)
+    c = kvb.KVCache.from_dict(dc)
+    pg = kvb.KVPages(tab.contiguous(), torch.full((w.batch, w.hkv, npg), 32, dtype=torch.int32,
+                                                  device="cuda"),
+                     torch.full((w.batch, w.hkv), npg, dtype=torch.int32, device="cuda"))
+    cont = {"k": torch.gather(dc["k"], 2, slot[..., None].expand(-1, -1, -1, w.head_dim)),
+            "v": torch.gather(dc["v"], 2, slot[..., None].expand(-1, -1, -1, w.head_dim)),
+            "log_beta": torch.gather(dc["log_beta"], 2, slot),
+            "pos": torch.arange(n, dtype=torch.int32, device="cuda").expand(
+                w.batch, w.hkv, n).contiguous(),
+            "len": torch.full((w.batch, w.hkv), n, dtype=torch.int32, device="cuda")}
+    cc = kvb.KVCache.from_dict({k: v.contiguous() for k, v in cont.items()})
+    q, _, _, _ = synth.device_queries(w, 0)
+    t = torch.full((w.batch,), n, dtype=torch.int32, device="cuda")
+    op, lp = kvb.kv_attn_decode_paged(c, pg, q, t)
+    oc, lc = kvb.kv_attn_decode(cc, q, t)
+    torch.cuda.synchronize()
+    assert torch.equal(op, oc) and torch.equal(lp, lc), "paged != contiguous"
+    G = w.group
+    qh = to_host(q)
+    for b, g in ((0, 0), (11, 5)):
+        ro, rl = oracle.decode_attention(values(to_host(cc.k[b, g]))[None, None],
+                                         values(to_host(cc.v[b, g]))[None, None],
+                                         to_host(cc.log_beta[b, g])[None, None],
+                                         to_host(cc.pos[b, g])[None, None], np.array([[n]]),
+                                         values(qh[b:b + 1, g * G:(g + 1) * G]), np.array([n]))
+        check_attention(to_host(op)[b:b + 1, g * G:(g + 1) * G],
+                        to_host(lp)[b:b + 1, g * G:(g + 1) * G], ro, rl, f"paged 32K ({b},{g})")
+    del dc, c, cont, cc
+    torch.cuda.empty_cache()
