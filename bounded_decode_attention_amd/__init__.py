@@ -26,7 +26,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
                    NOALLOC_SCRATCH_BYTES, kv_append, kv_attn_decode, kv_attn_decode_asm,
                    kv_attn_decode_asm_workspace, kv_attn_decode_asm_splits,
                    kv_attn_decode_noalloc, workspace_status,
-                   kv_check_cache, CHECK_BITS,
+                   kv_check_cache, kv_check_pages, CHECK_BITS,
                    kv_attn_decode_compact, kv_attn_decode_splits, kv_attn_decode_workspace,
                    kv_erase_ranges, kv_erase_workspace, kv_evict_apply, kv_evict_one,
                    kv_evict_plan, kv_attn_decode_plan_one, kv_evict_one_apply,
@@ -42,7 +42,7 @@ from ._lib import (KVBError, KVCache, asm_aggregate_states, asm_build_memory,
 __all__ = [
     "KVBError", "KVCache", "kv_attn_decode", "kv_evict_to_budget", "kv_erase_ranges",
     "kv_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "workspace_status",
-    "kv_check_cache", "CHECK_BITS",
+    "kv_check_cache", "kv_check_pages", "CHECK_BITS",
     "kv_append", "kv_evict_plan", "kv_evict_apply", "kv_evict_one", "kv_attn_decode_compact",
     "kv_attn_decode_plan_one", "kv_evict_one_apply", "kv_evict_one_workspace",
     "kv_attn_decode_evict_one", "kv_attn_decode_evict_one_workspace",

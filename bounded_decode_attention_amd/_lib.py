@@ -59,6 +59,7 @@ def library():
             "kv_attn_decode": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, SZ, P]),
             "kv_attn_decode_noalloc": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, P]),
             "kv_check_cache": (I32, [CP, P, P, P, I32, P, P]),
+            "kv_check_pages": (I32, [CP, PP, P, P, P]),
             "kv_attn_decode_asm_workspace": (SZ, [CP, I32, I32, I32]),
             "kv_attn_decode_asm_splits": (I32, [CP, I32, I32]),
             "kv_attn_decode_asm": (I32, [CP, P, I32, P, F, P, P, P, I32, P, P, P, I32, P, P, P,
@@ -384,7 +385,20 @@ def kv_evict_to_budget(cache: KVCache, t, M: int, evicted_pos=None, n_evicted=No
 
 
 CHECK_BITS = {"len": 1, "start": 2, "pos_order": 4, "pos_after_t": 8, "log_beta_nan": 16,
-              "log_beta_positive": 32, "ranges": 64}
+              "log_beta_positive": 32, "ranges": 64, "pages": 128}
+
+
+def kv_check_pages(cache: KVCache, pages: "KVPages", t=None, flags=None, stream=None):
+    """Device-side precondition check of a paged cache (kv_check_pages in kvbound.h).
+    Returns the [B][Hkv] int32 tensor of violation bits (CHECK_BITS); 0 means none."""
+    if t is not None:
+        _need(t, "t", torch.int32)
+    if flags is None:
+        flags = torch.empty((cache.B, cache.Hkv), dtype=torch.int32, device=cache.pos.device)
+    _need(flags, "flags", torch.int32)
+    st = library().kv_check_pages(cache.desc, pages.desc, _ptr(t), _ptr(flags), _stream(stream))
+    _check(st, "kv_check_pages")
+    return flags
 
 
 def kv_check_cache(cache: KVCache, t=None, ranges=None, n_ranges=None, flags=None,

@@ -125,8 +125,11 @@ enum {
   KVB_CHECK_POS_AFTER_T = 8,       /* a live position above t[b] (negative distance)      */
   KVB_CHECK_LOG_BETA_NAN = 16,     /* a live log beta is NaN                              */
   KVB_CHECK_LOG_BETA_POSITIVE = 32,/* a live log beta above 0 (beta > 1)                  */
-  KVB_CHECK_RANGES = 64            /* the sequence's erase ranges: s >= e, unsorted or
+  KVB_CHECK_RANGES = 64,           /* the sequence's erase ranges: s >= e, unsorted or
                                       overlapping, or n_ranges[b] outside [0, R]          */
+  KVB_CHECK_PAGES = 128            /* kv_check_pages: n_pages outside [0, max_pages], a
+                                      physical page outside [0, cap / 32) or a fill
+                                      outside [1, 32] (the page is then not read)         */
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -238,6 +241,22 @@ int32_t kv_attn_decode_noalloc(const kvb_cache* cache, const void* q, int32_t Hq
  */
 int32_t kv_check_cache(const kvb_cache* cache, const int32_t* t, const int32_t* ranges,
                        const int32_t* n_ranges, int32_t R, int32_t* flags, void* stream);
+
+/*
+ * kv_check_cache for the paged form (see kvb_pages; [MEM] system engineering): per
+ * KV head, the OR of KVB_CHECK_PAGES (malformed table entry, fill or n_pages),
+ * KVB_CHECK_LEN (len differs from the sum of the fills), KVB_CHECK_POS_ORDER
+ * (positions not strictly increasing along the head's pages in table order, which is
+ * also how a physical page listed twice shows), KVB_CHECK_POS_AFTER_T (with t) and
+ * the log beta bits, over the live rows of the well-formed pages.
+ *   t      [B] int32 or NULL;  flags [B][Hkv] int32 (device)
+ * Requires cap % 32 == 0, start == NULL and max_pages <= 2^25 (KVB_EINVAL otherwise;
+ * no head holds more than cap / 32 < 2^25 distinct pages).  Every read stays
+ * inside the arrays: n_pages is clamped to [0, max_pages] and a malformed page is
+ * not read.
+ */
+int32_t kv_check_pages(const kvb_cache* cache, const kvb_pages* pages, const int32_t* t,
+                       int32_t* flags, void* stream);
 
 /*
  * Append one token per KV head: the same append kv_attn_decode performs when

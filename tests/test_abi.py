@@ -490,3 +490,26 @@ def test_misaligned_pointers_rejected():
     assert L.kv_attn_decode(ctypes.byref(_desc()), P(68), *args[1:]) == -1
     if not _has_gpu():
         assert L.kv_attn_decode(ctypes.byref(_desc(log_beta=20480)), *args) == -5
+
+
+@needs_lib
+def test_check_pages_rejects_arguments_before_launch():
+    L = kvb.library()
+    P = ctypes.c_void_p
+    good = _desc(cap=128)
+    pages = _lib._Pages(200, 208, 216, 6)
+
+    def chk(c=good, pg=pages, flags=P(512)):
+        return L.kv_check_pages(ctypes.byref(c), None if pg is None else ctypes.byref(pg),
+                                None, flags, None)
+    assert chk(flags=None) == -1
+    assert chk(pg=None) == -1
+    assert chk(pg=_lib._Pages(200, None, 216, 6)) == -1
+    assert chk(pg=_lib._Pages(200, 208, 216, 0)) == -1
+    assert chk(pg=_lib._Pages(200, 208, 216, (1 << 25) + 1)) == -1
+    assert chk(c=_desc(cap=100)) == -1
+    st = _desc(cap=128)
+    st.start = 32
+    assert chk(c=st) == -1
+    if not _has_gpu():
+        assert chk() == -5

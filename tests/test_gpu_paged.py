@@ -467,3 +467,85 @@ def test_paged_attention_full_size_32k():
                         to_host(lp)[b:b + 1, g * G:(g + 1) * G], ro, rl, f"paged 32K ({b},{g})")
     del dc, c, cont, cc
     torch.cuda.empty_cache()
+
+
+def test_check_pages_each_violation():
+    """kv_check_pages: a clean paged cache has no flags; each planted violation (all
+    values in bounds) sets its bit on exactly the affected head."""
+    bits = kvb.CHECK_BITS
+
+    def base():
+        d = synth.host_paged(np.random.default_rng(1201), 2, 2, 128, 8, 9, 12, full_fill=0.3)
+        # every head with at least three pages
+        for b in range(2):
+            for g in range(2):
+                if d["n_pages"][b, g] < 3:
+                    d2 = synth.host_paged(np.random.default_rng(1300 + 2 * b + g), 1, 1, 128, 8,
+                                          9, 12, full_fill=0.3)
+                    assert d2["n_pages"][0, 0] >= 3
+                    for name in ("k", "v", "log_beta", "pos"):
+                        d[name][b, g] = d2[name][0, 0]
+                    for name in ("table", "fill"):
+                        d[name][b, g] = d2[name][0, 0]
+                    d["n_pages"][b, g] = d2["n_pages"][0, 0]
+                    d["len"][b, g] = d2["len"][0, 0]
+        return d
+
+    def run(d, t=None):
+        c, pg = _dev(d)
+        f = kvb.kv_check_pages(c, pg, t=None if t is None else to_dev(t))
+        torch.cuda.synchronize()
+        return to_host(f)
+
+    d = base()
+    t = np.array([int(d["pos"][b].max()) + 1 for b in range(2)], np.int32)
+    assert not run(d, t).any()
+    cases = []
+    d = base()
+    d["n_pages"][0, 1] = 10                              # above max_pages (9)
+    cases.append(("pages", d, None, (0, 1)))
+    d = base()
+    d["table"][1, 0, 1] = 12                             # physical page past cap / 32
+    cases.append(("pages", d, None, (1, 0)))
+    d = base()
+    d["fill"][1, 1, 2] = 0                               # empty page in the table
+    cases.append(("pages", d, None, (1, 1)))
+    d = base()
+    d["fill"][0, 0, 0] = 33                              # fill past the page
+    cases.append(("pages", d, None, (0, 0)))
+    d = base()
+    d["len"][1, 1] += 1                                  # len is not the sum of the fills
+    cases.append(("len", d, None, (1, 1)))
+    d = base()
+    d["table"][0, 1, 1] = d["table"][0, 1, 0]            # one physical page listed twice
+    d["fill"][0, 1, 1] = d["fill"][0, 1, 0]
+    d["len"][0, 1] = int(d["fill"][0, 1, :d["n_pages"][0, 1]].sum())
+    cases.append(("pos_order", d, None, (0, 1)))
+    d = base()
+    for name in ("table", "fill"):                       # two pages out of order
+        d[name][1, 0, [0, 1]] = d[name][1, 0, [1, 0]]
+    cases.append(("pos_order", d, None, (1, 0)))
+    d = base()
+    i2 = int(np.nonzero(d["fill"][0, 0, :d["n_pages"][0, 0]] >= 2)[0][0])
+    p0 = 32 * d["table"][0, 0, i2]
+    d["pos"][0, 0, p0 + 1] = d["pos"][0, 0, p0]          # repeated position inside a page
+    cases.append(("pos_order", d, None, (0, 0)))
+    d = base()
+    d["log_beta"][1, 1, 32 * d["table"][1, 1, 2]] = np.nan
+    cases.append(("log_beta_nan", d, None, (1, 1)))
+    d = base()
+    d["log_beta"][0, 1, 32 * d["table"][0, 1, 0]] = 0.5
+    cases.append(("log_beta_positive", d, None, (0, 1)))
+    d = base()
+    tt = np.array([int(d["pos"][0].max()) + 1, int(d["pos"][1, 0].max()) - 1], np.int32)
+    both = d["pos"][1, 1].max() > tt[1]                  # head (1, 1) past t as well
+    cases.append(("pos_after_t", d, tt, "b1" if both else (1, 0)))
+    for name, d, tt, where in cases:
+        say("check pages", name, where)
+        f = run(d, tt)
+        for b in range(2):
+            for g in range(2):
+                hit = (where == "b1" and b == 1) or where == (b, g)
+                assert (f[b, g] & bits[name]) == (bits[name] if hit else 0), (name, b, g, f)
+                if not hit:
+                    assert f[b, g] == 0, (name, b, g, f)
