@@ -439,10 +439,12 @@ int32_t kv_attn_decode_compact(const kvb_cache* cache, const void* q, int32_t Hq
  * the table; spare NULL or < 0, or a full table: the token is neither stored nor
  * attended and the status word becomes KVB_ECAPACITY), with pos = t[b]; len and
  * the page arrays are updated.
- *   spare      [B][Hkv] int32 or NULL
+ *   spare      [B][Hkv] int32 or NULL: a physical page the head does not use (not
+ *              checked; kv_check_pages reports a page listed twice)
  *   ws         kv_attn_decode_workspace(cache, Hq, num_splits) bytes
  * Other arguments as kv_attn_decode; num_splits 0 takes about 2048 / (B * Hkv)
- * splits, at most one per 8 pages of max_pages.
+ * splits, at most one per 8 pages of max_pages.  Like kv_attn_decode it allocates
+ * nothing and issues no memset, so it can be captured in a graph.
  */
 int32_t kv_attn_decode_paged(const kvb_cache* cache, const kvb_pages* pages, const void* q,
                              int32_t Hq, const int32_t* t, float scale, const void* k_new,
