@@ -549,3 +549,68 @@ def test_check_pages_each_violation():
                 assert (f[b, g] & bits[name]) == (bits[name] if hit else 0), (name, b, g, f)
                 if not hit:
                     assert f[b, g] == 0, (name, b, g, f)
+
+
+def test_paged_memento_full_size_partial_pages():
+    """The 1M-token MEMENTO trace in full pages (blocks not aligned to pages, so
+    every erased range leaves partly erased pages at both ends): per-head counts in
+    closed form for all heads; head 0's table, fills, positions and moved rows
+    against the oracle's page-by-page erase (run on slot numbers in place of the
+    rows, then the rows compared with the pre-erase rows they name)."""
+    w = synth.WORKLOADS["memento_1m"]
+    blocks, ranges = synth.memento_layout(total=w.ctx, seed=w.seed)
+    n = w.ctx
+    npg = n // 32
+    phys = npg + 8
+    cap = 32 * phys
+    say("paged memento partial pages: pages", npg, "ranges", ranges.shape)
+    dc = synth.device_cache(w, layer=0, n=cap, cap=cap)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 5))
+    table = np.stack([rng.permutation(phys)[:npg] for _ in range(w.hkv)]).astype(np.int32)
+    tab = torch.from_numpy(table).cuda().view(1, w.hkv, npg)
+    slot = (tab.long()[..., :, None] * 32 + torch.arange(32, device="cuda")).reshape(1, w.hkv, n)
+    pos = torch.zeros((1, w.hkv, cap), dtype=torch.int32, device="cuda")
+    pos.scatter_(2, slot, torch.arange(n, dtype=torch.int32, device="cuda").expand(
+        1, w.hkv, n).contiguous())
+    dc["pos"].copy_(pos)
+    dc["len"].fill_(n)
+    c = kvb.KVCache.from_dict(dc)
+    mp = npg + 4
+    tab0 = np.full((1, w.hkv, mp), -1, np.int32)
+    tab0[0, :, :npg] = table
+    fil0 = np.zeros((1, w.hkv, mp), np.int32)
+    fil0[0, :, :npg] = 32
+    pg = kvb.KVPages(to_dev(tab0), to_dev(fil0), to_dev(np.full((1, w.hkv), npg, np.int32)))
+    k_before = c.k[0, 0].clone()
+    v_before = c.v[0, 0].clone()
+    pos_before = to_host(c.pos[0, 0])
+    rg = torch.from_numpy(ranges[None].copy()).cuda()
+    nr = torch.tensor([ranges.shape[0]], dtype=torch.int32, device="cuda")
+    n_er = kvb.kv_erase_ranges_paged(c, pg, rg, nr)
+    torch.cuda.synchronize()
+    # closed form for every head: kept tokens and the pages that keep any
+    keep_tok = oracle.erase_plan(np.arange(n), n, ranges)
+    kept = int(keep_tok.sum())
+    pages_kept = int(keep_tok.reshape(npg, 32).any(axis=1).sum())
+    assert kept == 200 * (len(blocks) - 1) + blocks[-1][1]
+    assert (to_host(n_er) == n - kept).all() and (to_host(c.length) == kept).all()
+    assert (to_host(pg.n_pages) == pages_kept).all()
+    # head 0 against the oracle: rows replaced by their slot numbers
+    hc = OE.Cache(np.arange(cap, dtype=np.int64).reshape(1, 1, cap, 1),
+                  np.arange(cap, dtype=np.int64).reshape(1, 1, cap, 1), None,
+                  pos_before.reshape(1, 1, cap), np.array([[n]], np.int32))
+    hp = OE.Pages(tab0[:, :1].copy(), fil0[:, :1].copy(), np.array([[npg]], np.int32))
+    rc, rp, rn = OE.erase_pages(hc, hp, [ranges.astype(np.int64)])
+    assert rn[0, 0] == n - kept and rp.n_pages[0, 0] == pages_kept
+    m = int(rp.n_pages[0, 0])
+    assert np.array_equal(to_host(pg.table)[0, 0, :m], rp.table[0, 0, :m])
+    assert np.array_equal(to_host(pg.fill)[0, 0, :m], rp.fill[0, 0, :m])
+    live = np.concatenate([np.arange(32 * p, 32 * p + f)
+                           for p, f in zip(rp.table[0, 0, :m], rp.fill[0, 0, :m])])
+    assert np.array_equal(to_host(c.pos[0, 0])[live], rc.pos[0, 0, live])
+    src = torch.from_numpy(rc.k[0, 0, live, 0].copy()).cuda()
+    dst = torch.from_numpy(live.astype(np.int64)).cuda()
+    assert torch.equal(c.k[0, 0].index_select(0, dst), k_before.index_select(0, src))
+    assert torch.equal(c.v[0, 0].index_select(0, dst), v_before.index_select(0, src))
+    del dc, c, k_before, v_before
+    torch.cuda.empty_cache()
