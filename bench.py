@@ -877,10 +877,16 @@ def memento_bench(args):
     out = torch.empty((1, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((1, w.hq), dtype=torch.float32, device="cuda")
 
+    # a one-layer trial re-reads the same ~0.1-0.2 GB, which the 256 MB last-level
+    # cache would otherwise keep between trials: 512 MB are written (untimed) before
+    # each trial, so every trial starts from HBM as a layer of a real step would
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
     def restore():
         for k in ("k", "v", "pos"):
             dc[k][:, :, :keep_slots].copy_(prist[k])
         dc["len"].fill_(w.ctx)
+        flush.fill_(1)
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
@@ -958,13 +964,34 @@ def memento_paged_bench(args):
 
     w = synth.WORKLOADS["memento_1m"]
     blocks, ranges = synth.memento_layout(total=w.ctx, seed=w.seed)
-    table, fill, pos0, phys = synth.memento_pages(blocks, w.hkv, seed=w.seed)
-    n = table.shape[1]
-    erased = np.zeros(n, bool)
-    for s0, e0 in ranges:
-        erased |= (pos0 >= s0) & (pos0 < e0)
-    keep = np.nonzero(~erased)[0]
-    kept = int(fill[keep].sum())
+    full = args.full_pages
+    if full:
+        # the trace in full pages: blocks end inside pages, so each erased range
+        # leaves a partly erased page at both ends (compacted in place)
+        n = w.ctx // 32
+        phys = n + 64
+        prng = np.random.Generator(np.random.PCG64(w.seed + 77))
+        table = np.stack([prng.permutation(phys)[:n] for _ in range(w.hkv)]).astype(np.int32)
+        fill = np.full(n, 32, np.int32)
+        pos0 = (32 * np.arange(n)).astype(np.int32)
+        # a page stays unless one range holds all its 32 positions
+        j = np.searchsorted(ranges[:, 0], pos0, side="right") - 1
+        inside = (j >= 0) & (ranges[np.maximum(j, 0), 1] >= pos0 + 32)
+        keep = np.nonzero(~inside)[0]
+        kept = 200 * (len(blocks) - 1) + blocks[-1][1]
+        tok = np.arange(w.ctx)
+        jt = np.searchsorted(ranges[:, 0], tok, side="right") - 1
+        gone = ((jt >= 0) & (tok < ranges[np.maximum(jt, 0), 1])).reshape(n, 32)
+        n_partial = int((gone.any(axis=1) & ~gone.all(axis=1)).sum())
+    else:
+        table, fill, pos0, phys = synth.memento_pages(blocks, w.hkv, seed=w.seed)
+        n = table.shape[1]
+        n_partial = 0
+        erased = np.zeros(n, bool)
+        for s0, e0 in ranges:
+            erased |= (pos0 >= s0) & (pos0 < e0)
+        keep = np.nonzero(~erased)[0]
+        kept = int(fill[keep].sum())
     print(f"# memento_1m paged: {len(blocks)} blocks, {n} pages ({phys} physical), "
           f"{keep.size} pages and {kept} tokens kept per KV head", file=sys.stderr, flush=True)
     cap = 32 * phys
@@ -975,6 +1002,8 @@ def memento_paged_bench(args):
             pos[g, 32 * table[g, i]:32 * table[g, i] + fill[i]] = pos0[i] + np.arange(fill[i])
     dc["pos"].copy_(torch.from_numpy(pos[None]))
     c = kvb.KVCache.from_dict(dc)
+    # the rows a partly erased page moves, restored before each trial
+    prist = {k: dc[k].clone() for k in ("k", "v", "pos")} if full else None
     mp = n + 8
     tab0 = np.full((1, w.hkv, mp), -1, np.int32)
     tab0[0, :, :n] = table
@@ -1001,11 +1030,19 @@ def memento_paged_bench(args):
     out = torch.empty((1, w.hq, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((1, w.hq), dtype=torch.float32, device="cuda")
 
+    # every trial from HBM: 512 MB written (untimed) before each one, more than the
+    # 256 MB last-level cache holds
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
     def restore():
         pg.table.copy_(tab0)
         pg.fill.copy_(fil0)
         pg.n_pages.fill_(n)
         dc["len"].fill_(int(fill.sum()))
+        if prist is not None:
+            for k in prist:
+                dc[k].copy_(prist[k])
+        flush.fill_(1)
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
 
@@ -1044,13 +1081,16 @@ def memento_paged_bench(args):
                   "paged cache)",
         "value": round(float(np.sum(med)), 2), "unit": "us", "n_gpus": 1, "trials": trials,
         "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "layout": "paged (32-slot pages, block-aligned)",
+        "config": {"workload": w.name,
+                   "layout": ("paged (32-slot pages, full; blocks end inside pages)" if full
+                              else "paged (32-slot pages, block-aligned)"),
                    "batch": 1, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": D,
                    "tokens": w.ctx, "pages": n, "pages_kept": int(keep.size),
                    "erased_ranges": int(ranges.shape[0]), "kept": kept,
                    "attention_splits": P_att},
         "erase_us": {"median": round(float(med[0]), 2), "min": round(float(res[:, 0].min()), 2),
-                     "max": round(float(res[:, 0].max()), 2), "rows_moved": 0},
+                     "max": round(float(res[:, 0].max()), 2),
+                     "partial_pages_per_head": n_partial},
         "attention_us": {"median": round(float(med[1]), 2), "min": round(float(res[:, 1].min()), 2),
                          "max": round(float(res[:, 1].max()), 2),
                          "bytes": attn_b, "gbps": round(attn_b / (med[1] * 1e-6) / 1e9, 1)},
@@ -1282,6 +1322,9 @@ def main():
                     help="--memento: the same trial over a paged cache (block-granular "
                          "erase, paged attention); alone: the 32K workload's attention "
                          "over a paged cache against the contiguous one (one JSON line)")
+    ap.add_argument("--full-pages", action="store_true",
+                    help="--memento --paged: the trace in full pages (blocks not aligned to "
+                         "pages; the erase compacts partly erased pages)")
     ap.add_argument("--latent", action="store_true",
                     help="time the latent memory of evicted tokens (update after the 32K "
                          "eviction, steady-state update, read-out; one JSON line)")
