@@ -41,6 +41,11 @@ int32_t check_device() {
   return ok ? KVB_OK : KVB_EDEVICE;
 }
 
+bool cache_dims_ok(const kvb_cache* c) {
+  return c && c->B >= 1 && c->Hkv >= 1 && c->cap >= 1 && c->cap < (1 << 30) && c->D >= 1 &&
+         c->D <= 256 && (long long)c->B * c->Hkv <= (1 << 20);
+}
+
 int32_t check_cache(const kvb_cache* c, bool need_kv) {
   if (!c) return KVB_EINVAL;
   if (c->B < 1 || c->Hkv < 1 || c->cap < 1 || c->cap >= (1 << 30) || c->D < 1) return KVB_EINVAL;

@@ -571,7 +571,10 @@ using namespace kvb;
 
 extern "C" size_t asm_lookup_merge_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t K) {
   (void)D;
-  if (B < 1 || Hq < 1 || Hkv < 1 || K < 1 || Hq % Hkv) return 0;
+  // the entry's limits: B * G query rows per KV head at most 65536, K below 2^24
+  if (B < 1 || Hq < 1 || Hkv < 1 || K < 1 || K >= (1 << 24) || Hq % Hkv ||
+      (long long)B * (Hq / Hkv) > 65536)
+    return 0;
   int G, QB, KC;
   asm_dims(B, Hq, Hkv, K, G, QB, KC);
   const size_t n = (size_t)Hkv * QB * 16 * KC;
@@ -636,7 +639,8 @@ static size_t hier_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t m, int& NQ
 
 extern "C" size_t asm_lookup_merge_hier_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t K1,
                                                   int32_t m) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || K1 < 1 || K1 > kHierMaxK1 || m < 1 || m > K1)
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || K1 < 1 || K1 > kHierMaxK1 || m < 1 || m > K1 ||
+      (long long)B * (Hq / Hkv) > 65536)
     return 0;
   int NQ;
   size_t a, b;

@@ -775,7 +775,7 @@ static int prefix_chunks(int L, int chunks, int& csize) {
     csize = 1;
     return 1;
   }
-  csize = (L + chunks - 1) / chunks;
+  csize = (int)(((long long)L + chunks - 1) / chunks);
   return (L + csize - 1) / csize;
 }
 

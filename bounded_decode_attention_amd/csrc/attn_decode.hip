@@ -1749,6 +1749,7 @@ static AsmScanArgs scan_dims(int B, int Hq, int Hkv, int K) {
 // splits spend their time in set-up and partial-state writes.
 static int32_t auto_splits(const kvb_cache* c) {
   const long long units = (long long)c->B * c->Hkv;
+  if (units < 1) return 1;
   const long long tiles = c->cap / 256;
   long long P = (2048 + units - 1) / units;
   if (P > tiles) P = tiles;
@@ -1763,12 +1764,12 @@ using namespace kvb;
 
 extern "C" int32_t kv_attn_decode_splits(const kvb_cache* cache, int32_t Hq) {
   (void)Hq;
-  if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1) return 0;
+  if (!cache_dims_ok(cache)) return 0;
   return auto_splits(cache);
 }
 
 extern "C" size_t kv_attn_decode_workspace(const kvb_cache* cache, int32_t Hq, int32_t num_splits) {
-  if (!cache || Hq < 1 || cache->B < 1 || cache->D < 1) return 0;
+  if (!cache_dims_ok(cache) || Hq < 1 || num_splits < 0) return 0;
   const size_t P = num_splits > 0 ? (size_t)num_splits : (size_t)auto_splits(cache);
   const size_t S = (size_t)cache->B * Hq * P;
   return kWsHeader + align_up(S * cache->D * sizeof(float), 256) +
@@ -1959,7 +1960,7 @@ extern "C" int32_t kv_attn_decode_plan_one(const kvb_cache* cache, const void* q
 // kv_attn_decode_evict_one's workspace: the attention's, then the candidates.
 extern "C" size_t kv_attn_decode_evict_one_workspace(const kvb_cache* cache, int32_t Hq,
                                                      int32_t num_splits) {
-  if (!cache || Hq < 1 || cache->Hkv < 1 || Hq % cache->Hkv != 0) return 0;
+  if (!cache_dims_ok(cache) || Hq < 1 || Hq % cache->Hkv != 0) return 0;
   const size_t a = kv_attn_decode_workspace(cache, Hq, num_splits);
   if (a == 0 || num_splits < 0 || num_splits > 4096) return 0;
   const size_t P = num_splits > 0 ? (size_t)num_splits : (size_t)auto_splits(cache);
@@ -2052,6 +2053,12 @@ extern "C" int32_t kv_attn_decode_noalloc(const kvb_cache* cache, const void* q,
 // leaves, rounded down to a power of two, never more than kv_attn_decode's default.
 // On the ASM workload (512 scan tasks, 256 heads of 2049 tokens): 4 splits per head
 // 507 steps/s, 5: 498, 6 (one full round): 496, 8 (kv_attn_decode's default): 479.
+// The size limits kv_attn_decode_asm checks, for its host-only queries.
+static bool asm_dims_ok(const kvb_cache* c, int32_t Hq, int32_t K) {
+  return cache_dims_ok(c) && K >= 1 && K < (1 << 24) && Hq >= 1 && Hq % c->Hkv == 0 &&
+         (long long)c->B * (Hq / c->Hkv) <= 65536;
+}
+
 static int32_t asm_splits(const kvb_cache* c, int32_t Hq, int32_t K) {
   const int32_t P = auto_splits(c);
   const int G = Hq / c->Hkv;
@@ -2067,16 +2074,14 @@ static int32_t asm_splits(const kvb_cache* c, int32_t Hq, int32_t K) {
 }
 
 extern "C" int32_t kv_attn_decode_asm_splits(const kvb_cache* cache, int32_t Hq, int32_t K) {
-  if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1 || Hq < 1 ||
-      Hq % cache->Hkv || K < 1)
-    return 0;
+  if (!asm_dims_ok(cache, Hq, K)) return 0;
   return asm_splits(cache, Hq, K);
 }
 
 extern "C" size_t kv_attn_decode_asm_workspace(const kvb_cache* cache, int32_t Hq,
                                                int32_t num_splits, int32_t K) {
-  if (!cache || cache->Hkv < 1 || Hq < 1 || Hq % cache->Hkv || K < 1) return 0;
-  if (num_splits == 0 && cache->B >= 1 && cache->cap >= 1) num_splits = asm_splits(cache, Hq, K);
+  if (!asm_dims_ok(cache, Hq, K) || num_splits < 0) return 0;
+  if (num_splits == 0) num_splits = asm_splits(cache, Hq, K);
   const size_t wa = kv_attn_decode_workspace(cache, Hq, num_splits);
   if (!wa) return 0;
   const AsmScanArgs c = scan_dims(cache->B, Hq, cache->Hkv, K);

@@ -322,6 +322,9 @@ int32_t check_device();
 
 // Host: validate a cache descriptor (pointers, sizes, dtype/D support).
 int32_t check_cache(const kvb_cache* c, bool need_kv);
+// check_cache's size checks alone (no pointers): what a host-only size query needs
+// before it computes with the descriptor's dimensions.
+bool cache_dims_ok(const kvb_cache* c);
 
 // Kernel-launch tracing (see kvb_trace_enable): records a HIP event pair on the
 // launch stream around each traced kernel while enabled.

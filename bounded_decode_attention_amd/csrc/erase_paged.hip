@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kPgThreads) void pg_apply(PgArgs a) {
 using namespace kvb;
 
 extern "C" size_t kv_erase_paged_workspace(const kvb_cache* cache, const kvb_pages* pages) {
-  if (!cache || !pages || cache->B < 1 || cache->Hkv < 1 || pages->max_pages < 1) return 0;
+  if (!cache_dims_ok(cache) || !pages || pages->max_pages < 1) return 0;
   return pg_layout(cache, pages).total;
 }
 

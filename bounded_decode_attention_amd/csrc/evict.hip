@@ -2249,13 +2249,12 @@ static int32_t evict_validate(const kvb_cache* cache, int32_t M, size_t ws_bytes
 using namespace kvb;
 
 extern "C" size_t kv_evict_workspace(const kvb_cache* cache, int32_t M) {
-  if (!cache || M < 0 || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1 || cache->D < 8)
-    return 0;
+  if (!cache_dims_ok(cache) || M < 0 || cache->D < 8) return 0;
   return compact_layout(cache, M < cache->cap ? M : cache->cap).total;
 }
 
 extern "C" size_t kv_erase_workspace(const kvb_cache* cache) {
-  if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1 || cache->D < 8) return 0;
+  if (!cache_dims_ok(cache) || cache->D < 8) return 0;
   return compact_layout(cache, cache->cap).total;
 }
 

@@ -401,7 +401,7 @@ static size_t latent_layout(const kvb_cache* c, int& S, size_t& o_ev, size_t& o_
 using namespace kvb;
 
 extern "C" size_t kv_latent_absorb_workspace(const kvb_cache* cache) {
-  if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap < 1 || cache->D < 8) return 0;
+  if (!cache_dims_ok(cache) || cache->D < 8) return 0;
   int S;
   size_t a, b, c;
   return latent_layout(cache, S, a, b, c);

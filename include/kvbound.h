@@ -139,7 +139,9 @@ const char* kvb_strerror(int32_t status);
  * 2048 / (B * Hkv), at least one, at most one per 256 slots of capacity. */
 int32_t kv_attn_decode_splits(const kvb_cache* cache, int32_t Hq);
 
-/* Workspace sizes in bytes (host only; no device access). */
+/* Workspace sizes in bytes (host only; no device access).  0 when the dimensions are
+ * ones the matching call rejects (a descriptor outside the kvb_cache limits, a
+ * negative split count, more query rows per KV head than the lookups take). */
 size_t kv_attn_decode_workspace(const kvb_cache* cache, int32_t Hq, int32_t num_splits);
 size_t kv_evict_workspace(const kvb_cache* cache, int32_t M);
 size_t kv_erase_workspace(const kvb_cache* cache);

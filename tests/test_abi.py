@@ -74,6 +74,31 @@ def test_workspace_sizes_host_only():
     assert L.asm_lookup_merge_workspace(1, 3, 2, 128, 16) == 0
 
 
+def test_size_queries_reject_dimensions_the_calls_reject():
+    """Size queries on descriptors the entry points would refuse return 0 instead of
+    dividing by zero or overflowing (found by the sanitizer build of the host code)."""
+    L = kvb.library()
+    for bad in (_desc(Hkv=0), _desc(B=0), _desc(cap=0), _desc(cap=1 << 30),
+                _desc(B=1 << 15, Hkv=1 << 15)):
+        assert L.kv_attn_decode_splits(ctypes.byref(bad), 8) == 0
+        assert L.kv_attn_decode_workspace(ctypes.byref(bad), 8, 0) == 0
+        assert L.kv_attn_decode_asm_workspace(ctypes.byref(bad), 8, 0, 256) == 0
+        assert L.kv_attn_decode_asm_splits(ctypes.byref(bad), 8, 256) == 0
+        assert L.kv_evict_workspace(ctypes.byref(bad), 10) == 0
+        assert L.kv_erase_workspace(ctypes.byref(bad)) == 0
+        assert L.kv_latent_absorb_workspace(ctypes.byref(bad)) == 0
+    c = _desc()
+    assert L.kv_attn_decode_workspace(ctypes.byref(c), 8, -1) == 0
+    # more query rows per KV head than the lookups take (B * G > 65536)
+    assert L.kv_attn_decode_asm_workspace(ctypes.byref(_desc(B=1 << 17, Hkv=1)), 4, 0, 256) == 0
+    assert L.asm_lookup_merge_workspace(1 << 30, 8, 2, 128, 256) == 0
+    assert L.asm_lookup_merge_workspace(1, 8, 2, 128, 1 << 24) == 0
+    assert L.asm_lookup_merge_hier_workspace(1 << 30, 8, 2, 16, 4) == 0
+    # one chunk per token at most, whatever the chunk count asked for
+    assert L.asm_prefix_states_workspace(2, 1024, 128, 512, 2 ** 31 - 1) == \
+        L.asm_prefix_states_workspace(2, 1024, 128, 512, 512)
+
+
 @needs_lib
 def test_invalid_arguments_rejected_before_launch():
     """Fake (never dereferenced) pointers: validation fails first, nothing runs."""
